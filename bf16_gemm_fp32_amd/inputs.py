@@ -1,0 +1,133 @@
+"""Seeded synthetic inputs for the bf16 GEMM workloads.
+
+This module only draws random numbers and stores them as bf16 bit patterns
+(uint16).  It holds none of the GEMM's arithmetic, so the GPU path and the
+CPU oracle can both be fed from it without sharing any of their code.
+
+Recipe (the pages initialise every matrix from a normal distribution with
+mean 0 and standard deviation 1 -- "Outperforming cuBLAS on H100: a worklog",
+section "Experimental setup"):
+
+* operand j of workload i is drawn from numpy's PCG64 generator seeded with
+  ``1000*i + j`` (j = 1: A, 2: B, 3: the initial C, 4: bias);
+* values are float32 standard normals (bias: multiplied by 0.1 in float32,
+  i.e. standard deviation 0.1), rounded to bf16 nearest-even;
+* buffers are filled in storage order: A as M rows of K (row-major), B as N
+  columns of K (column-major), C0 as N columns of M (column-major).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    index: int          # seed block: seeds are 1000*index + operand id
+    M: int
+    N: int
+    K: int
+    alpha: float = 1.0
+    beta: float = 0.0
+    bias: bool = False
+    epilogue: str = "none"
+    bound: str = "mfma"  # which roofline limits it: "mfma" or "hbm"
+    notes: str = field(default="", compare=False)
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Minimum HBM bytes: read A and B once, write C once (read C0 if beta)."""
+        b = 2 * (self.M * self.K + self.K * self.N + self.M * self.N)
+        if self.beta != 0.0:
+            b += 2 * self.M * self.N
+        if self.bias:
+            b += 2 * self.N
+        return b
+
+
+# The five workloads: A row-major, B and C column-major, fp32 accumulation,
+# bf16 output.  The 4096^3 square is the pages' headline shape.
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("square_256", 0, 256, 256, 256,
+                 notes="smallest case; the oracle checks every element"),
+        Workload("square_4096", 1, 4096, 4096, 4096,
+                 notes="headline shape of the worklog"),
+        Workload("square_8192", 2, 8192, 8192, 8192,
+                 notes="large grid: several tiles per compute unit"),
+        Workload("gelu_8192x14336x4096", 3, 8192, 14336, 4096,
+                 alpha=1.0, beta=0.5, bias=True, epilogue="gelu_tanh",
+                 notes="C = GELU_tanh(1.0*A*B + 0.5*C0 + bias[n])"),
+        Workload("skinny_64x8192x8192", 4, 64, 8192, 8192, bound="hbm",
+                 notes="memory-bound: B (128 MiB) is streamed once"),
+    ]
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round finite float32 samples to bf16 bit patterns, nearest-even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("input samples must be finite")
+    u = x.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def normal_bf16(seed: int, numel: int, scale: float = 1.0) -> np.ndarray:
+    """numel i.i.d. N(0, scale^2) samples as bf16 bits (uint16), seeded."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    x = g.standard_normal(numel, dtype=np.float32)
+    if scale != 1.0:
+        x *= np.float32(scale)
+    return f32_to_bf16_bits(x)
+
+
+def operand_seed(index: int, operand: str) -> int:
+    return 1000 * index + {"A": 1, "B": 2, "C0": 3, "bias": 4}[operand]
+
+
+def make_inputs(w: Workload, lda=None, ldb=None, ldc=None) -> dict:
+    """Host buffers (flat uint16, storage order) for workload w.
+
+    With padded leading dimensions the padding elements are filled from the
+    same stream (they must never influence the result).
+    """
+    lda = w.K if lda is None else lda
+    ldb = w.K if ldb is None else ldb
+    ldc = w.M if ldc is None else ldc
+    out = {
+        "A": normal_bf16(operand_seed(w.index, "A"), w.M * lda),
+        "B": normal_bf16(operand_seed(w.index, "B"), w.N * ldb),
+        "lda": lda, "ldb": ldb, "ldc": ldc,
+    }
+    if w.beta != 0.0:
+        out["C0"] = normal_bf16(operand_seed(w.index, "C0"), w.N * ldc)
+    if w.bias:
+        out["bias"] = normal_bf16(operand_seed(w.index, "bias"), w.N, scale=0.1)
+    return out
+
+
+def random_case(seed: int, M: int, N: int, K: int, lda=None, ldb=None, ldc=None,
+                with_c0: bool = False, with_bias: bool = False) -> dict:
+    """Ad-hoc seeded case for tests: same recipe, seeds seed+1..seed+4."""
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    ldc = max(M, 1) if ldc is None else ldc
+    out = {
+        "A": normal_bf16(seed + 1, max(M * lda, 0)),
+        "B": normal_bf16(seed + 2, max(N * ldb, 0)),
+        "lda": max(lda, 1), "ldb": max(ldb, 1), "ldc": ldc,
+    }
+    if with_c0:
+        out["C0"] = normal_bf16(seed + 3, N * ldc)
+    if with_bias:
+        out["bias"] = normal_bf16(seed + 4, N, scale=0.1)
+    return out

@@ -1,0 +1,176 @@
+"""CPU oracle for the bf16 GEMM: plain, slow, fp64-accumulating reference.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the package smoke check and the
+benchmark's CPU-baseline leg may import this module.  The product (the HIP
+library and its Python binding) never imports, links or calls it, and it
+shares no code with the product.
+
+The arithmetic lives in ``gemm_oracle.c`` (compiled with gcc, no fast-math,
+no FP contraction).  This module only marshals numpy arrays into it.
+
+What it computes (see the C file for the sources):
+
+    C_out[m,n] = bf16_rne(epi(alpha * sum_k A[m,k] B[k,n]
+                              + beta * C_in[m,n] + bias[n]))
+
+with A row-major (A[m*lda+k]), B column-major (B[k+n*ldb]) and C
+column-major (C[m+n*ldc]); sums in double with k ascending; one
+round-to-nearest-even to bf16 at the end.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gemm_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+EPI_CODES = {"none": 0, "gelu_tanh": 1}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc into ``oracle/liboracle.so``."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off",
+               "-fno-fast-math", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, u16p, f64 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double
+    lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_f64.restype = f64
+    lib.oracle_bf16_from_f64.argtypes = [f64]
+    lib.oracle_bf16_from_f64.restype = ctypes.c_uint16
+    lib.oracle_gelu_tanh.argtypes = [f64]
+    lib.oracle_gelu_tanh.restype = f64
+    for name in ("oracle_bf16_to_f64_array", "oracle_bf16_from_f64_array",
+                 "oracle_gelu_tanh_array"):
+        getattr(lib, name).argtypes = [ctypes.c_void_p, ctypes.c_void_p, i64]
+        getattr(lib, name).restype = None
+    lib.oracle_gemm.argtypes = [i64, i64, i64, u16p, i64, u16p, i64, u16p, i64,
+                                f64, f64, u16p, ctypes.c_int, u16p,
+                                ctypes.c_void_p, ctypes.c_int]
+    lib.oracle_gemm.restype = ctypes.c_int
+    lib.oracle_gemm_elems.argtypes = [i64, i64, i64, u16p, i64, u16p, i64, u16p, i64,
+                                      f64, f64, u16p, ctypes.c_int, i64,
+                                      ctypes.c_void_p, ctypes.c_void_p, u16p,
+                                      ctypes.c_void_p, ctypes.c_int]
+    lib.oracle_gemm_elems.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u16(a, name):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError(f"{name} must hold raw bf16 bits as uint16, got {a.dtype}")
+    return a.reshape(-1)
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Exact decode of raw bf16 bit patterns (any shape) to float64."""
+    lib = _load()
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(b.shape, dtype=np.float64)
+    lib.oracle_bf16_to_f64_array(_ptr(b), _ptr(out), b.size)
+    return out
+
+
+def bf16_from_f64(x) -> np.ndarray:
+    """Round float64 values (any shape) to bf16 bits, nearest-even, once."""
+    lib = _load()
+    a = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(a.shape, dtype=np.uint16)
+    lib.oracle_bf16_from_f64_array(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def gelu_tanh(x) -> np.ndarray:
+    """GELU, tanh form, in float64 (any shape)."""
+    lib = _load()
+    a = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(a.shape, dtype=np.float64)
+    lib.oracle_gelu_tanh_array(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def gemm(M, N, K, A, lda, B, ldb, C_in=None, ldc=None, alpha=1.0, beta=0.0,
+         bias=None, epilogue="none", nthreads=0, return_pre=False):
+    """Whole-product oracle on flat storage-order buffers of bf16 bits.
+
+    A holds at least (M-1)*lda+K elements (row-major), B at least
+    (N-1)*ldb+K (column-major), C_in (only read if beta != 0) at least
+    (N-1)*ldc+M (column-major).  Returns C_out as a flat uint16 array of
+    N*ldc elements (column-major, leading dimension ldc; padding rows are 0),
+    and with return_pre=True also the pre-rounding float64 values as an
+    (N, M) array (row n holds column n of C).
+    """
+    lib = _load()
+    if ldc is None:
+        ldc = max(1, M)
+    A, B, C_in, bias = _u16(A, "A"), _u16(B, "B"), _u16(C_in, "C_in"), _u16(bias, "bias")
+    if M > 0 and K > 0 and A.size < (M - 1) * lda + K:
+        raise ValueError("A too small")
+    if N > 0 and K > 0 and B.size < (N - 1) * ldb + K:
+        raise ValueError("B too small")
+    if beta != 0.0 and M > 0 and N > 0 and (C_in is None or C_in.size < (N - 1) * ldc + M):
+        raise ValueError("C_in too small")
+    if bias is not None and bias.size < N:
+        raise ValueError("bias too small")
+    out = np.zeros(max(N * ldc, 1), dtype=np.uint16)
+    pre = np.zeros((max(N, 1), max(M, 1)), dtype=np.float64) if return_pre else None
+    rc = lib.oracle_gemm(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C_in), ldc,
+                         float(alpha), float(beta), _ptr(bias), EPI_CODES[epilogue],
+                         _ptr(out), _ptr(pre), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_gemm rejected its arguments")
+    out = out[: N * ldc]
+    if return_pre:
+        return out, pre[:N, :M]
+    return out
+
+
+def gemm_elems(M, N, K, A, lda, B, ldb, ms, ns, C_in=None, ldc=None, alpha=1.0,
+               beta=0.0, bias=None, epilogue="none", nthreads=0, return_pre=False):
+    """The same definition evaluated only at coordinates (ms[i], ns[i])."""
+    lib = _load()
+    if ldc is None:
+        ldc = max(1, M)
+    A, B, C_in, bias = _u16(A, "A"), _u16(B, "B"), _u16(C_in, "C_in"), _u16(bias, "bias")
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    if ms.shape != ns.shape:
+        raise ValueError("ms and ns differ in shape")
+    out = np.zeros(max(ms.size, 1), dtype=np.uint16)
+    pre = np.zeros(max(ms.size, 1), dtype=np.float64) if return_pre else None
+    rc = lib.oracle_gemm_elems(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C_in), ldc,
+                               float(alpha), float(beta), _ptr(bias), EPI_CODES[epilogue],
+                               ms.size, _ptr(ms), _ptr(ns), _ptr(out), _ptr(pre),
+                               int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_gemm_elems rejected its arguments")
+    if return_pre:
+        return out[: ms.size], pre[: ms.size]
+    return out[: ms.size]
