@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X bf16 GEMM library.
+
+One step is one call of gemm_bf16 on the chosen workload (default: the
+4096^3 square, A row-major, B and C column-major, N(0,1) seeded inputs,
+alpha = 1, beta = 0), with inputs already resident in device memory.  The
+protocol follows "Outperforming cuBLAS on H100: a worklog", section
+"Experimental setup": W untimed warm-up launches, then the mean over K timed
+launches, FLOPS = 2*M*N*K / time.  Each launch is bracketed by its own pair
+of HIP events recorded on the stream the kernel runs on.
+
+Prints ONE JSON line (rank 0, one GPU).  With --all it prints one line per
+workload instead.
+
+    python bench.py [--gpus 1] [--steps 8] [--warmup 1] [--workload square_4096]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from bf16_gemm_fp32_amd import inputs  # noqa: E402
+
+METRIC = "bf16 GEMM TFLOP/s at M=N=K=4096 and % of MI355X dense bf16 MFMA peak"
+# MI355X published peaks: dense bf16 MFMA = 256 CU x 4096 flop/clk x 2.4 GHz,
+# HBM3E 8 TB/s.
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_HBM_GBS = 8000.0
+EPI = {"none": 0, "gelu_tanh": 1}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, d, budget_cols=None):
+    """Time the CPU oracle on a bounded sample of the workload: whole output
+    columns (every row m of the first `cols` columns)."""
+    import oracle
+    nthreads = cpu_threads()
+    M, N, K = w.M, w.N, w.K
+    if budget_cols is None:
+        # about 10-20 s on 16 host cores at ~0.18 GMAC/s per core
+        target_macs = 2.0e9 * nthreads
+        budget_cols = int(max(1, min(N, target_macs // max(1, M * K))))
+    cols = budget_cols
+    ms = np.tile(np.arange(M, dtype=np.int64), cols)
+    ns = np.repeat(np.arange(cols, dtype=np.int64), M)
+    t0 = time.perf_counter()
+    oracle.gemm_elems(M, N, K, d["A"], K, d["B"], K, ms, ns, d.get("C0"), M, w.alpha, w.beta,
+                      d.get("bias"), w.epilogue, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * M * cols * K
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": nthreads,
+        "kind": "oracle",
+        "sample": f"{cols} whole columns of C ({M * cols} of {M * N} outputs, {flops:.3e} flop) "
+                  f"in {dt:.2f} s on {cpu_model()}",
+    }
+
+
+def run_workload(w, steps, warmup, cold, with_cpu):
+    import torch
+    import bf16_gemm_fp32_amd as gb
+
+    gb.library()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    log(f"[bench] workload {w.name}: M={w.M} N={w.N} K={w.K} building inputs")
+    d = inputs.make_inputs(w)
+
+    def dev_tensor(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev)
+
+    copies = 4 if cold else 1  # rotate distinct buffers so B is not cache-resident
+    A = [dev_tensor(d["A"]) for _ in range(copies)]
+    B = [dev_tensor(d["B"]) for _ in range(copies)]
+    C = [torch.empty(w.N * w.M, dtype=torch.int16, device=dev) for _ in range(copies)]
+    C0 = dev_tensor(d["C0"]) if "C0" in d else None
+    bias = dev_tensor(d["bias"]) if "bias" in d else None
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    kname = gb.gemm_bf16_kernel_name(w.M, w.N, w.K, A[0].data_ptr(), w.K, B[0].data_ptr(), w.K,
+                                     C[0].data_ptr(), w.M, w.beta, bias.data_ptr() if bias is not None else 0,
+                                     EPI[w.epilogue])
+    log(f"[bench] kernel {kname}; warmup {warmup}, steps {steps}, cold={cold}")
+
+    def launch(i):
+        j = i % copies
+        if C0 is not None:
+            C[j].copy_(C0)  # beta != 0: C is in/out; reset outside the timed pair
+        return j
+
+    def call(j):
+        st = gb.gemm_bf16(w.M, w.N, w.K, A[j].data_ptr(), w.K, B[j].data_ptr(), w.K, C[j].data_ptr(), w.M,
+                          w.alpha, w.beta, bias.data_ptr() if bias is not None else 0, EPI[w.epilogue], sp)
+        if st != 0:
+            raise RuntimeError(f"gemm_bf16 status {st}: {gb.gemm_bf16_status_string(st)}")
+
+    for i in range(warmup):
+        call(launch(i))
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    all0 = torch.cuda.Event(enable_timing=True)
+    all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    all0.record(stream)
+    for i in range(steps):
+        j = launch(warmup + i)
+        ev[i][0].record(stream)
+        call(j)
+        ev[i][1].record(stream)
+    all1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in ev]  # ms
+    mean_ms = statistics.fmean(per)
+    tflops = w.flops / (mean_ms * 1e-3) / 1e12
+    gbs = w.algorithmic_bytes / (mean_ms * 1e-3) / 1e9
+    log(f"[bench] per-launch ms: mean {mean_ms:.4f} min {min(per):.4f} max {max(per):.4f} -> {tflops:.1f} TFLOP/s")
+
+    if w.bound == "hbm":
+        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None}
+    out = {
+        "metric": METRIC if w.name == "square_4096" else f"bf16 GEMM TFLOP/s on {w.name}",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": mean_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha, "beta": w.beta,
+                   "bias": w.bias, "epilogue": w.epilogue, "layout": "A row-major, B/C column-major",
+                   "kernel": kname, "inputs": "N(0,1) seeded (bias N(0,0.1))",
+                   "cache": "cold (4 rotating buffer sets)" if cold else "warm"},
+        "pct_of_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "hbm_gbs_algorithmic": gbs,
+        "per_launch_ms": {"mean": mean_ms, "min": min(per), "median": statistics.median(per),
+                          "max": max(per), "stdev": statistics.pstdev(per)},
+        "timed_region_wall_ms": wall * 1e3,
+        "timed_region_event_ms": all0.elapsed_time(all1),
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if with_cpu:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(w, d)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=8)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="square_4096", choices=list(inputs.WORKLOADS))
+    ap.add_argument("--all", action="store_true", help="one JSON line per workload")
+    ap.add_argument("--cold", choices=["auto", "yes", "no"], default="auto",
+                    help="rotate 4 buffer sets (default: only for the memory-bound workload)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: this build is a single-GPU kernel library "
+              "(multi-GPU sharding is described in the design notes, not implemented).", file=sys.stderr)
+        sys.exit(2)
+
+    names = list(inputs.WORKLOADS) if args.all else [args.workload]
+    for name in names:
+        w = inputs.WORKLOADS[name]
+        cold = (w.bound == "hbm") if args.cold == "auto" else (args.cold == "yes")
+        res = run_workload(w, args.steps, args.warmup, cold,
+                           with_cpu=not args.no_cpu and (name == "square_4096" or not args.all))
+        print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,105 @@
+// device_common.h -- gfx950 building blocks shared by the GEMM kernels:
+// vector types, LDS/wait primitives, buffer resources, bf16 conversion and
+// the fp32 epilogue arithmetic.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gb {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define GB_LDS __attribute__((address_space(3)))
+
+// Epilogue flags (runtime, uniform across the grid).
+enum : uint32_t { kEpiBeta = 1u, kEpiBias = 2u, kEpiGelu = 4u };
+
+struct GemmArgs {
+    int64_t M, N, K;
+    const uint16_t *A;
+    int64_t lda;
+    const uint16_t *B;
+    int64_t ldb;
+    uint16_t *C;
+    int64_t ldc;
+    float alpha, beta;
+    const uint16_t *bias;
+    uint32_t flags;  // kEpi* bits
+};
+
+// ---------------------------------------------------------------- waits ---
+// Explicit waits and barriers as inline asm with a memory clobber: the
+// compiler may not move memory operations across them, and __syncthreads()
+// would force vmcnt(0), draining the load pipeline we keep in flight.
+
+// All LDS reads of this wave have landed, then a workgroup barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// At most N vector-memory operations of this wave still outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// ---------------------------------------------------- buffer resources ---
+// Raw (stride 0) buffer: num_records bytes from base; loads past the end
+// return zero.  Word 3 = 0x00020000 selects the 32-bit data format that
+// untyped buffer loads need on gfx9-family parts.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// 16-byte per lane direct load from a buffer into LDS.  Lane i of the wave
+// writes lds_base + 16*i; lds_base must be wave-uniform.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, GB_LDS void *lds_base,
+                                                  uint32_t voffset, uint32_t soffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_base, 16, voffset, soffset, 0, 0);
+}
+
+// ------------------------------------------------------------ bf16 math ---
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+    return __builtin_bit_cast(float, bits16 << 16);
+}
+
+// Two floats -> two bf16 (round to nearest even) packed low|high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    __bf16 a = (__bf16)lo;
+    __bf16 b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// GELU, tanh form: 0.5 y (1 + tanh(u)), u = sqrt(2/pi) (y + 0.044715 y^3).
+// Uses the identity 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)), evaluated with
+// the hardware base-2 exponential and reciprocal.  Both limits are exact:
+// exp -> inf gives y * 0 (large negative y), exp -> 0 gives y.
+__device__ __forceinline__ float gelu_tanh_f32(float y) {
+    const float kSqrt2OverPi = 0.7978845608028654f;
+    const float kLog2e = 1.4426950408889634f;
+    float u = kSqrt2OverPi * (y + 0.044715f * y * y * y);
+    float e = __builtin_amdgcn_exp2f(-2.0f * kLog2e * u);
+    return y * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// alpha*acc (+ beta*c_in) (+ bias) then the activation, all in fp32.
+__device__ __forceinline__ float epilogue_value(float acc, float c_in, float bias_v, const GemmArgs &a) {
+    float v = a.alpha * acc;
+    if (a.flags & kEpiBeta) v += a.beta * c_in;
+    if (a.flags & kEpiBias) v += bias_v;
+    if (a.flags & kEpiGelu) v = gelu_tanh_f32(v);
+    return v;
+}
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace gb

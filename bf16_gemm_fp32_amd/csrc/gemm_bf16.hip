@@ -1,0 +1,184 @@
+// gemm_bf16.hip -- host side of the library: argument validation, kernel
+// selection and launch behind the C ABI declared in include/gemm_bf16.h.
+#include "gemm_bf16.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+
+#include "device_common.h"
+#include "kernel_generic.h"
+#include "kernel_tile.h"
+#include "tile_schedule.h"
+
+namespace gb {
+
+// Kernel configurations.  256x256 output tiles with four waves of 128x128
+// (256 fp32 accumulators per lane, the AGPR half of the register file at one
+// wave per SIMD) for large grids; 128x128 tiles with four waves of 64x64 when
+// the 256-tiles would leave most compute units idle.
+using CfgLarge = TileConfig<256, 256, 64, 2, 2, 2>;
+using CfgMedium = TileConfig<128, 128, 64, 2, 2, 2>;
+
+enum KernelKind { kNone = 0, kLarge = 1, kMedium = 2, kGeneric = 3 };
+
+static const char *kind_name(int k) {
+    switch (k) {
+    case kLarge: return "tile256x256x64_s2";
+    case kMedium: return "tile128x128x64_s2";
+    case kGeneric: return "generic64x64x32";
+    default: return "none";
+    }
+}
+
+static thread_local int t_last_hip_error = 0;
+
+// Compute-unit count per device, filled on first use (benign race: every
+// thread computes the same value).
+static std::atomic<int> g_cu_count[64];
+
+static int device_cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cached > 0) return cached;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    g_cu_count[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+static int validate(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
+                    const void *C, int64_t ldc, int epilogue) {
+    if (M < 0 || N < 0 || K < 0) return GEMM_ERR_DIM;
+    const int64_t kmin = K > 1 ? K : 1, mmin = M > 1 ? M : 1;
+    if (lda < kmin || ldb < kmin || ldc < mmin) return GEMM_ERR_LD;
+    if ((M > 0 && K > 0 && !A) || (K > 0 && N > 0 && !B) || (M > 0 && N > 0 && !C)) return GEMM_ERR_NULL;
+    if (epilogue != GEMM_EPI_NONE && epilogue != GEMM_EPI_GELU_TANH) return GEMM_ERR_EPILOGUE;
+    return GEMM_OK;
+}
+
+static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+template <class Cfg>
+static bool tile_path_ok(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+                         int64_t ldb, const void *C, int64_t ldc) {
+    if (K <= 0 || M % Cfg::BM || N % Cfg::BN || K % Cfg::BK) return false;
+    if (lda % 8 || ldb % 8 || ldc % 8) return false;
+    if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return false;
+    // 32-bit buffer offsets inside a tile's rows
+    const int64_t lim = (int64_t)1 << 31;
+    if ((Cfg::BM * lda + K) * 2 >= lim || (Cfg::BN * ldb + K) * 2 >= lim) return false;
+    // tile indices held in int
+    if (M / Cfg::BM * (N / Cfg::BN) >= lim) return false;
+    return true;
+}
+
+static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+                         int64_t ldb, const void *C, int64_t ldc, int cus) {
+    if (M == 0 || N == 0) return kNone;
+    const char *force = std::getenv("GEMM_BF16_FORCE_KERNEL");
+    if (force && std::strcmp(force, "generic") == 0) return kGeneric;
+    if (tile_path_ok<CfgLarge>(M, N, K, A, lda, B, ldb, C, ldc)) {
+        const int64_t tiles = (M / CfgLarge::BM) * (N / CfgLarge::BN);
+        if (tiles * 2 >= cus || !tile_path_ok<CfgMedium>(M, N, K, A, lda, B, ldb, C, ldc)) return kLarge;
+    }
+    if (tile_path_ok<CfgMedium>(M, N, K, A, lda, B, ldb, C, ldc)) return kMedium;
+    return kGeneric;
+}
+
+template <class Cfg>
+static hipError_t launch_tile(const GemmArgs &args, int cus, hipStream_t stream) {
+    TileSchedule s{};
+    s.tiles_m = (int)(args.M / Cfg::BM);
+    s.tiles_n = (int)(args.N / Cfg::BN);
+    s.group_m = 4;
+    s.order = kOrderGrouped;
+    s.hilbert_log2 = 0;
+    const int tiles = s.num_tiles();
+    s.grid = tiles < cus ? tiles : cus;
+    hipLaunchKernelGGL(gemm_tile_kernel<Cfg>, dim3(s.grid), dim3(Cfg::kThreads), 0, stream, args, s);
+    return hipGetLastError();
+}
+
+static hipError_t launch_generic(const GemmArgs &args, int cus, hipStream_t stream) {
+    const int64_t tiles_m = (args.M + GenericConfig::BM - 1) / GenericConfig::BM;
+    const int64_t tiles_n = (args.N + GenericConfig::BN - 1) / GenericConfig::BN;
+    const int64_t tiles = tiles_m * tiles_n;
+    const int64_t cap = (int64_t)cus * 8;
+    const int grid = (int)(tiles < cap ? tiles : cap);
+    hipLaunchKernelGGL(gemm_generic_kernel, dim3(grid), dim3(GenericConfig::kThreads), 0, stream, args, tiles_m,
+                       tiles);
+    return hipGetLastError();
+}
+
+}  // namespace gb
+
+extern "C" {
+
+int gemm_bf16(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t lda, const gemm_bf16_t *B,
+              int64_t ldb, gemm_bf16_t *C, int64_t ldc, float alpha, float beta, const gemm_bf16_t *bias,
+              int epilogue, hipStream_t stream) {
+    using namespace gb;
+    const int st = validate(M, N, K, A, lda, B, ldb, C, ldc, epilogue);
+    if (st != GEMM_OK) return st;
+    if (M == 0 || N == 0) return GEMM_OK;
+
+    GemmArgs args;
+    args.M = M;
+    args.N = N;
+    args.K = K;
+    args.A = A;
+    args.lda = lda;
+    args.B = B;
+    args.ldb = ldb;
+    args.C = C;
+    args.ldc = ldc;
+    args.alpha = alpha;
+    args.beta = beta;
+    args.bias = bias;
+    args.flags = (beta != 0.0f ? kEpiBeta : 0u) | (bias ? kEpiBias : 0u) |
+                 (epilogue == GEMM_EPI_GELU_TANH ? kEpiGelu : 0u);
+
+    const int cus = device_cu_count();
+    hipError_t err = hipSuccess;
+    switch (choose_kernel(M, N, K, A, lda, B, ldb, C, ldc, cus)) {
+    case kLarge: err = launch_tile<CfgLarge>(args, cus, stream); break;
+    case kMedium: err = launch_tile<CfgMedium>(args, cus, stream); break;
+    default: err = launch_generic(args, cus, stream); break;
+    }
+    if (err != hipSuccess) {
+        t_last_hip_error = (int)err;
+        return GEMM_ERR_HIP;
+    }
+    return GEMM_OK;
+}
+
+const char *gemm_bf16_status_string(int status) {
+    switch (status) {
+    case GEMM_OK: return "ok";
+    case GEMM_ERR_DIM: return "negative dimension";
+    case GEMM_ERR_LD: return "leading dimension too small";
+    case GEMM_ERR_NULL: return "null pointer for a non-empty operand";
+    case GEMM_ERR_EPILOGUE: return "unknown epilogue";
+    case GEMM_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+int gemm_bf16_last_hip_error(void) { return gb::t_last_hip_error; }
+
+const char *gemm_bf16_kernel_name(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t lda,
+                                  const gemm_bf16_t *B, int64_t ldb, const gemm_bf16_t *C, int64_t ldc,
+                                  float beta, const gemm_bf16_t *bias, int epilogue) {
+    (void)beta;
+    (void)bias;
+    if (gb::validate(M, N, K, A, lda, B, ldb, C, ldc, epilogue) != GEMM_OK) return "none";
+    return gb::kind_name(gb::choose_kernel(M, N, K, A, lda, B, ldb, C, ldc, gb::device_cu_count()));
+}
+
+}  // extern "C"

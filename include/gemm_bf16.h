@@ -1,0 +1,112 @@
+/*
+ * gemm_bf16.h -- C ABI of the MI355X (gfx950) bf16 GEMM library.
+ *
+ *   C[m,n] <- epi( alpha * sum_k A[m,k] * B[k,n] + beta * C[m,n] + bias[n] )
+ *
+ * The product and the layouts (bf16 matrices, A row-major, B and C
+ * column-major) follow "Outperforming cuBLAS on H100: a worklog", sections
+ * "Recap of Simon's blog" and "Experimental setup".  The BLAS form with alpha
+ * and beta, fp32 accumulation of bf16 inputs, and the fused epilogue (bias
+ * first, then the activation, then the write) follow the DeepGEMM kernel-set
+ * article on demingchina.com, sections 1.1, 3.1 and 6.1.
+ *
+ * Numerics: products of bf16 inputs are accumulated in fp32 on the MFMA
+ * units; alpha, beta*C, bias and the activation are applied in fp32; the
+ * result is rounded once to bf16, round-to-nearest-even.
+ *
+ * Every function is thread-safe.  The library keeps no pointer after a call
+ * returns and allocates no device memory.
+ */
+#ifndef GEMM_BF16_H
+#define GEMM_BF16_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Raw bf16 bits (sign, 8-bit exponent, 7-bit mantissa). */
+typedef uint16_t gemm_bf16_t;
+
+/* Epilogue activation, applied last to alpha*AB + beta*C + bias. */
+enum gemm_bf16_epilogue {
+    GEMM_EPI_NONE = 0,
+    /* GELU, tanh form: 0.5x(1 + tanh(sqrt(2/pi)(x + 0.044715x^3))) */
+    GEMM_EPI_GELU_TANH = 1
+};
+
+/* Status codes.  Argument errors are detected on the host, in this order,
+ * before any HIP call is made. */
+enum gemm_bf16_status {
+    GEMM_OK = 0,
+    GEMM_ERR_DIM = -1,       /* M, N or K negative */
+    GEMM_ERR_LD = -2,        /* lda < max(1,K), ldb < max(1,K) or ldc < max(1,M) */
+    GEMM_ERR_NULL = -3,      /* NULL A (M*K>0), NULL B (K*N>0) or NULL C (M*N>0) */
+    GEMM_ERR_EPILOGUE = -4,  /* epilogue not in enum gemm_bf16_epilogue */
+    GEMM_ERR_HIP = -5        /* the HIP runtime reported an error; see
+                                gemm_bf16_last_hip_error() */
+};
+
+/*
+ * gemm_bf16 -- enqueue C <- epi(alpha*A*B + beta*C + bias) on `stream`.
+ *
+ *   M, N, K  problem size (any value >= 0).
+ *   A        device pointer, row-major M x K: element (m,k) at A[m*lda + k].
+ *   B        device pointer, column-major K x N: element (k,n) at B[k + n*ldb].
+ *   C        device pointer, column-major M x N: element (m,n) at C[m + n*ldc].
+ *            In/out: holds the initial C when beta != 0.  When beta == 0 it
+ *            is write-only and is never read (NaN in it cannot propagate).
+ *   alpha, beta  fp32 scalars.
+ *   bias     NULL, or a device pointer to N bf16 values added to column n.
+ *   epilogue one of enum gemm_bf16_epilogue.
+ *   stream   HIP stream (0 = the null stream).  The call is asynchronous: it
+ *            enqueues the work and returns without synchronising.
+ *
+ * Quick returns: M == 0 or N == 0 enqueues nothing.  K == 0 computes
+ * C <- epi(beta*C + bias) (the empty sum contributes nothing).
+ *
+ * Any alignment of the pointers (2-byte bf16 alignment) and any leading
+ * dimensions are accepted.  16-byte aligned pointers with leading dimensions
+ * that are multiples of 8 select the fast kernels; other inputs take a
+ * bounds-checked path that computes the same result more slowly.
+ *
+ * Ownership: all buffers belong to the caller and must stay valid until the
+ * enqueued work has completed.  A, B and bias must not overlap C.
+ *
+ * Returns GEMM_OK or a negative gemm_bf16_status.
+ */
+int gemm_bf16(int64_t M, int64_t N, int64_t K,
+              const gemm_bf16_t *A, int64_t lda,
+              const gemm_bf16_t *B, int64_t ldb,
+              gemm_bf16_t *C, int64_t ldc,
+              float alpha, float beta,
+              const gemm_bf16_t *bias,
+              int epilogue, hipStream_t stream);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char *gemm_bf16_status_string(int status);
+
+/* The hipError_t of the calling thread's most recent GEMM_ERR_HIP, else 0. */
+int gemm_bf16_last_hip_error(void);
+
+/*
+ * gemm_bf16_kernel_name -- name of the kernel configuration gemm_bf16 would
+ * launch for these arguments (static storage), e.g. "tile256x256x64_s2",
+ * or "none" when nothing would be launched or the arguments are invalid.
+ * Makes no HIP call apart from querying the current device's compute-unit
+ * count.  Pointers are only inspected for their alignment.
+ */
+const char *gemm_bf16_kernel_name(int64_t M, int64_t N, int64_t K,
+                                  const gemm_bf16_t *A, int64_t lda,
+                                  const gemm_bf16_t *B, int64_t ldb,
+                                  const gemm_bf16_t *C, int64_t ldc,
+                                  float beta, const gemm_bf16_t *bias,
+                                  int epilogue);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_BF16_H */

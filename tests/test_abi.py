@@ -1,0 +1,100 @@
+"""The C-ABI library loads, exports every function include/gemm_bf16.h
+declares, and rejects bad arguments on the host before any HIP call (these
+calls never reach the device, so they run without a GPU)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import bf16_gemm_fp32_amd as gb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm_bf16.h")
+
+OK, ERR_DIM, ERR_LD, ERR_NULL, ERR_EPI, ERR_HIP = 0, -1, -2, -3, -4, -5
+P = 4096  # a fake non-NULL pointer: never dereferenced on these paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_bf16\w*)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = gb.library()
+    names = declared_functions()
+    assert "gemm_bf16" in names and len(names) >= 4
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in the header but not exported"
+
+
+def test_status_codes_match_header():
+    text = open(HEADER).read()
+    for name, val in [("GEMM_OK", 0), ("GEMM_ERR_DIM", -1), ("GEMM_ERR_LD", -2),
+                      ("GEMM_ERR_NULL", -3), ("GEMM_ERR_EPILOGUE", -4), ("GEMM_ERR_HIP", -5),
+                      ("GEMM_EPI_NONE", 0), ("GEMM_EPI_GELU_TANH", 1)]:
+        assert re.search(rf"\b{name}\s*=\s*{val}\b", text), name
+    assert gb.EPILOGUES == {"none": 0, "gelu_tanh": 1}
+
+
+def call(M, N, K, A=P, lda=None, B=P, ldb=None, C=P, ldc=None, alpha=1.0, beta=0.0, bias=0, epi=0):
+    lda = max(K, 1) if lda is None else lda
+    ldb = max(K, 1) if ldb is None else ldb
+    ldc = max(M, 1) if ldc is None else ldc
+    return gb.gemm_bf16(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, bias, epi, 0)
+
+
+@pytest.mark.parametrize("args,want", [
+    ((-1, 4, 4), ERR_DIM), ((4, -1, 4), ERR_DIM), ((4, 4, -1), ERR_DIM),
+    ((4, 4, 4, P, 3), ERR_LD), ((4, 4, 4, P, 4, P, 3), ERR_LD),
+    ((4, 4, 4, P, 4, P, 4, P, 3), ERR_LD), ((4, 4, 0, P, 0), ERR_LD),
+    ((4, 4, 4, 0), ERR_NULL), ((4, 4, 4, P, 4, 0), ERR_NULL), ((4, 4, 4, P, 4, P, 4, 0), ERR_NULL),
+])
+def test_argument_errors(args, want):
+    assert call(*args) == want
+
+
+def test_error_order_dim_before_ld_before_null_before_epilogue():
+    assert call(-1, 4, 4, 0, 0, 0, 0, 0, 0, epi=9) == ERR_DIM
+    assert call(4, 4, 4, 0, 0, 0, 0, 0, 0, epi=9) == ERR_LD
+    assert call(4, 4, 4, 0, 4, 0, 4, 0, 4, epi=9) == ERR_NULL
+    assert call(4, 4, 4, epi=9) == ERR_EPI
+    assert call(4, 4, 4, epi=-1) == ERR_EPI
+
+
+def test_empty_outputs_are_no_ops_without_device():
+    # M == 0 or N == 0: nothing to compute, no HIP call, NULL operands allowed
+    assert call(0, 5, 7, 0, 7, P, 7, 0, 1) == OK      # B is non-empty, so it must be given
+    assert call(5, 0, 7, P, 7, 0, 7, 0, 5) == OK      # A is non-empty, so it must be given
+    assert call(0, 0, 0, 0, 1, 0, 1, 0, 1) == OK
+
+
+def test_status_strings():
+    for s in (OK, ERR_DIM, ERR_LD, ERR_NULL, ERR_EPI, ERR_HIP, 12345):
+        assert isinstance(gb.gemm_bf16_status_string(s), str) and gb.gemm_bf16_status_string(s)
+    assert gb.gemm_bf16_last_hip_error() == 0
+
+
+def test_kernel_selection_names():
+    # pointer alignment and divisibility decide the path; P is 16-byte aligned
+    name = gb.gemm_bf16_kernel_name
+    assert name(4096, 4096, 4096, P, 4096, P, 4096, P, 4096) == "tile256x256x64_s2"
+    assert name(8192, 14336, 4096, P, 4096, P, 4096, P, 8192) == "tile256x256x64_s2"
+    assert name(256, 256, 256, P, 256, P, 256, P, 256) == "tile128x128x64_s2"
+    assert name(1000, 1000, 1000, P, 1000, P, 1000, P, 1000) == "generic64x64x32"
+    assert name(4096, 4096, 4096, P + 2, 4096, P, 4096, P, 4096) == "generic64x64x32"
+    assert name(4096, 4096, 4100, P, 4100, P, 4100, P, 4096) == "generic64x64x32"
+    assert name(4096, 4096, 0, P, 1, P, 1, P, 4096) == "generic64x64x32"
+    assert name(0, 4096, 4096, P, 4096, P, 4096, P, 1) == "none"
+    assert name(-1, 4096, 4096, P, 4096, P, 4096, P, 1) == "none"
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(gb, "_lib", None)
+    monkeypatch.setattr(gb, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        gb.library()

@@ -1,0 +1,224 @@
+"""GPU parity: the HIP library (called through its C ABI) against the CPU
+oracle on the same seeded inputs, element by element, within
+|gpu - oracle| <= 2 ulp_bf16(oracle) + 1e-3 sqrt(K).
+
+Small and medium shapes are compared in full (several tiles and ragged
+tails); the five benchmark workloads run at full size, in the launch
+configuration the benchmark times, and are compared on sampled elements
+(whole tiles at the corners plus random elements) that the oracle evaluates
+one by one.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from bf16_gemm_fp32_amd import inputs
+from tests.tolerance import assert_within_tolerance, bits_to_f64
+
+torch = pytest.importorskip("torch")
+gb = pytest.importorskip("bf16_gemm_fp32_amd")
+
+pytestmark = pytest.mark.gpu
+
+NAN_BF16 = 0x7FC0
+EPI = {"none": 0, "gelu_tanh": 1}
+
+
+def _threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gb.library()
+    yield
+
+
+def to_dev(bits: np.ndarray, offset: int = 0):
+    """Device copy of a uint16 buffer, optionally starting `offset` elements
+    into a larger allocation (to break 16-byte alignment).  Returns the full
+    tensor and the pointer of the data start."""
+    full = torch.zeros(bits.size + offset + 8, dtype=torch.int16, device="cuda")
+    full[offset:offset + bits.size] = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+    return full, full.data_ptr() + 2 * offset
+
+
+def from_dev(t, offset, n):
+    return t[offset:offset + n].cpu().numpy().view(np.uint16).copy()
+
+
+def run_gpu(M, N, K, A, lda, B, ldb, C_init, ldc, alpha, beta, bias, epilogue, offsets=(0, 0, 0)):
+    a_t, a_p = to_dev(A, offsets[0])
+    b_t, b_p = to_dev(B, offsets[1])
+    c_t, c_p = to_dev(C_init, offsets[2])
+    bias_p = 0
+    if bias is not None:
+        bias_t, bias_p = to_dev(bias)
+    stream = torch.cuda.current_stream().cuda_stream
+    st = gb.gemm_bf16(M, N, K, a_p, lda, b_p, ldb, c_p, ldc, alpha, beta, bias_p, EPI[epilogue], stream)
+    assert st == 0, gb.gemm_bf16_status_string(st)
+    torch.cuda.synchronize()
+    return from_dev(c_t, offsets[2], C_init.size)
+
+
+def check_full(tag, M, N, K, lda=None, ldb=None, ldc=None, alpha=1.0, beta=0.0, use_bias=False,
+               epilogue="none", offsets=(0, 0, 0), seed=0, expect_kernel=None):
+    lda = max(K, 1) if lda is None else lda
+    ldb = max(K, 1) if ldb is None else ldb
+    ldc = max(M, 1) if ldc is None else ldc
+    case = inputs.random_case(seed, M, N, K, lda, ldb, ldc, with_c0=True, with_bias=use_bias)
+    C0 = case["C0"]
+    # beta == 0: C starts as NaN everywhere, which must not leak
+    C_init = C0 if beta != 0.0 else np.full_like(C0, NAN_BF16)
+    bias = case.get("bias") if use_bias else None
+    # the selection only looks at alignment: an aligned stand-in base plus the offsets
+    kname = gb.gemm_bf16_kernel_name(M, N, K, 4096 + 2 * offsets[0], lda, 4096 + 2 * offsets[1], ldb,
+                                     4096 + 2 * offsets[2], ldc)
+    say(f"[parity] {tag}: M={M} N={N} K={K} lda={lda} ldb={ldb} ldc={ldc} alpha={alpha} beta={beta} "
+        f"bias={use_bias} epi={epilogue} offsets={offsets} kernel={kname}")
+    if expect_kernel is not None:
+        assert kname == expect_kernel
+    got = run_gpu(M, N, K, case["A"], lda, case["B"], ldb, C_init, ldc, alpha, beta, bias, epilogue, offsets)
+    ref = oracle.gemm(M, N, K, case["A"], lda, case["B"], ldb, C0, ldc, alpha, beta, bias, epilogue,
+                      nthreads=_threads())
+    g2 = got.reshape(N, ldc)
+    r2 = ref.reshape(N, ldc)
+    rep = assert_within_tolerance(g2[:, :M], r2[:, :M], K, tag)
+    # rows M..ldc-1 of every column are not part of C: untouched
+    if ldc > M:
+        assert np.array_equal(g2[:, M:], C_init.reshape(N, ldc)[:, M:]), f"{tag}: padding written"
+    say(f"[parity] {tag}: ok max_ulp={rep['max_ulp']:.2f} mean_ulp={rep['mean_ulp']:.4f} "
+        f"exact={rep['exact']}/{rep['n']}")
+    return rep
+
+
+# ------------------------------------------------------- tile-path shapes ---
+
+@pytest.mark.parametrize("M,N,K,kernel", [
+    (256, 256, 256, "tile128x128x64_s2"),
+    (512, 384, 192, "tile128x128x64_s2"),     # 3 K-slices (odd)
+    (512, 384, 256, "tile128x128x64_s2"),     # 4 K-slices (even)
+    (4096, 2048, 320, "tile256x256x64_s2"),   # 128 tiles of 256, 5 slices
+    (4096, 2048, 64, "tile256x256x64_s2"),    # a single K-slice
+])
+def test_tile_paths_full(M, N, K, kernel):
+    check_full(f"tile {M}x{N}x{K}", M, N, K, seed=M + N + K, expect_kernel=kernel)
+
+
+def test_tile_path_epilogue_full():
+    check_full("tile256 epilogue", 4096, 2048, 192, alpha=1.0, beta=0.5, use_bias=True,
+               epilogue="gelu_tanh", seed=11, expect_kernel="tile256x256x64_s2")
+    check_full("tile128 epilogue", 512, 512, 128, alpha=-0.75, beta=-1.5, use_bias=True,
+               epilogue="none", seed=12, expect_kernel="tile128x128x64_s2")
+    check_full("tile128 gelu only", 384, 256, 320, alpha=2.0, epilogue="gelu_tanh", seed=13,
+               expect_kernel="tile128x128x64_s2")
+
+
+def test_tile_path_padded_leading_dims():
+    check_full("tile128 padded ld", 512, 256, 256, lda=264, ldb=272, ldc=520, beta=0.25, use_bias=True,
+               seed=14, expect_kernel="tile128x128x64_s2")
+    check_full("tile256 padded ld", 4096, 2048, 128, lda=136, ldb=192, ldc=4104, seed=15,
+               expect_kernel="tile256x256x64_s2")
+
+
+# ---------------------------------------------------- bounds-checked path ---
+
+@pytest.mark.parametrize("M,N,K", [
+    (1, 1, 1), (33, 65, 97), (257, 257, 257), (1000, 1000, 1000), (64, 64, 4097), (1, 4096, 512),
+    (300, 1, 70), (130, 70, 8),
+])
+def test_generic_ragged_full(M, N, K):
+    check_full(f"generic {M}x{N}x{K}", M, N, K, seed=3 * M + N + K, expect_kernel="generic64x64x32")
+
+
+def test_generic_unaligned_and_odd_leading_dims():
+    check_full("unaligned A", 256, 256, 256, offsets=(1, 0, 0), seed=21, expect_kernel="generic64x64x32")
+    check_full("unaligned B C", 128, 192, 64, offsets=(0, 3, 5), beta=0.5, use_bias=True, seed=22,
+               expect_kernel="generic64x64x32")
+    check_full("odd lds", 100, 90, 77, lda=81, ldb=79, ldc=103, beta=2.0, use_bias=True,
+               epilogue="gelu_tanh", seed=23, expect_kernel="generic64x64x32")
+
+
+def test_k_zero_is_epilogue_only():
+    check_full("K=0 beta bias gelu", 200, 150, 0, beta=0.5, use_bias=True, epilogue="gelu_tanh", seed=24,
+               expect_kernel="generic64x64x32")
+    check_full("K=0 beta=0", 64, 64, 0, seed=25, expect_kernel="generic64x64x32")
+
+
+def test_empty_output_touches_nothing():
+    c_t, c_p = to_dev(np.full(16, NAN_BF16, np.uint16))
+    st = gb.gemm_bf16(0, 4, 4, 0, 4, c_p, 4, c_p, 1, 1.0, 0.0, 0, 0, torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert np.all(from_dev(c_t, 0, 16) == NAN_BF16)
+
+
+def test_repeat_launches_bit_identical_and_paths_agree():
+    """Repeated launches of the tile kernel are bit-identical (no race in the
+    LDS ring), and the bounds-checked kernel forced on the same inputs agrees
+    with it within the tolerance."""
+    M, N, K = 512, 512, 512
+    case = inputs.random_case(31, M, N, K)
+    C_init = np.zeros(M * N, np.uint16)
+    r1 = run_gpu(M, N, K, case["A"], K, case["B"], K, C_init, M, 1.0, 0.0, None, "none")
+    r2 = run_gpu(M, N, K, case["A"], K, case["B"], K, C_init, M, 1.0, 0.0, None, "none")
+    assert np.array_equal(r1, r2)
+    os.environ["GEMM_BF16_FORCE_KERNEL"] = "generic"
+    try:
+        r3 = run_gpu(M, N, K, case["A"], K, case["B"], K, C_init, M, 1.0, 0.0, None, "none")
+    finally:
+        del os.environ["GEMM_BF16_FORCE_KERNEL"]
+    assert_within_tolerance(r3, r1, K, "generic vs tile")
+
+
+# ------------------------------------------- the five workloads, full size ---
+
+def sample_coords(M, N, tile, rng, n_random):
+    ms, ns = [], []
+    for (m0, n0) in [(0, 0), (max(M - tile, 0), max(N - tile, 0))]:
+        mm, nn = np.meshgrid(np.arange(m0, min(m0 + tile, M)), np.arange(n0, min(n0 + tile, N)), indexing="ij")
+        ms.append(mm.ravel())
+        ns.append(nn.ravel())
+    ms.append(rng.integers(0, M, n_random))
+    ns.append(rng.integers(0, N, n_random))
+    return np.concatenate(ms), np.concatenate(ns)
+
+
+@pytest.mark.parametrize("name", list(inputs.WORKLOADS))
+def test_workload_full_size_sampled(name):
+    w = inputs.WORKLOADS[name]
+    d = inputs.make_inputs(w)
+    M, N, K = w.M, w.N, w.K
+    C0 = d.get("C0")
+    C_init = C0 if C0 is not None else np.full(N * M, NAN_BF16, np.uint16)
+    bias = d.get("bias")
+    kname = gb.gemm_bf16_kernel_name(M, N, K, 4096, K, 4096, K, 4096, M)
+    say(f"[parity] workload {name}: M={M} N={N} K={K} kernel={kname}")
+    got = run_gpu(M, N, K, d["A"], K, d["B"], K, C_init, M, w.alpha, w.beta, bias, w.epilogue)
+    assert not np.isnan(bits_to_f64(got)).any(), "NaN in the output"
+    if M * N <= 256 * 256:
+        ref = oracle.gemm(M, N, K, d["A"], K, d["B"], K, C0, M, w.alpha, w.beta, bias, w.epilogue,
+                          nthreads=_threads())
+        rep = assert_within_tolerance(got, ref, K, name)
+    else:
+        rng = np.random.Generator(np.random.PCG64(7 + w.index))
+        ms, ns = sample_coords(M, N, 64 if M <= 64 else 256, rng, 20000)
+        ref = oracle.gemm_elems(M, N, K, d["A"], K, d["B"], K, ms, ns, C0, M, w.alpha, w.beta, bias,
+                                w.epilogue, nthreads=_threads())
+        rep = assert_within_tolerance(got[ms + ns * M], ref, K, name)
+    say(f"[parity] workload {name}: ok n={rep['n']} max_ulp={rep['max_ulp']:.2f} "
+        f"mean_ulp={rep['mean_ulp']:.4f} exact={rep['exact']}")
