@@ -189,6 +189,20 @@ def run_workload(w, steps, warmup, cold, with_cpu):
     return out
 
 
+def calibrate_copy(mib):
+    """A plain device-to-device copy of `mib` MiB (torch's copy kernel): the
+    reference for scaling the FETCH_SIZE / WRITE_SIZE counters, which should
+    read `mib` MiB each for it."""
+    import torch
+    n = mib * 1024 * 1024 // 2
+    src = torch.ones(n, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": 2 * n, "bytes_written": 2 * n}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,7 +213,12 @@ def main():
     ap.add_argument("--cold", choices=["auto", "yes", "no"], default="auto",
                     help="rotate 4 buffer sets (default: only for the memory-bound workload)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calibrate-copy", type=int, metavar="MIB", default=0,
+                    help="only run a plain MIB-MiB device copy (counter calibration) and exit")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: this build is a single-GPU kernel library "

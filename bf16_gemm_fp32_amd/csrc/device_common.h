@@ -42,6 +42,9 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// s_waitcnt immediate (gfx9 encoding) that waits for lgkmcnt == 0 only.
+constexpr int kWaitLgkm0 = 0xC07F;
+
 // At most N vector-memory operations of this wave still outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

@@ -19,20 +19,19 @@ namespace gb {
 // Kernel configurations.  256x256 output tiles with four waves of 128x128
 // (256 fp32 accumulators per lane, the AGPR half of the register file at one
 // wave per SIMD) for large grids; 128x128 tiles with four waves of 64x64 when
-// the 256-tiles would leave most compute units idle.
-using CfgLarge = TileConfig<256, 256, 64, 2, 2, 2>;
-using CfgMedium = TileConfig<128, 128, 64, 2, 2, 2>;
+// the 256-tiles would leave most compute units idle.  K-slices of 32 in a
+// 5-deep LDS ring (all 160 KiB) give each slice's loads more than two slices
+// to land; the 4-deep ring is kept for comparison.
+using CfgL32S5 = TileConfig<256, 256, 32, 2, 2, 5>;
+using CfgL32S4 = TileConfig<256, 256, 32, 2, 2, 4>;
+using CfgM64S4 = TileConfig<128, 128, 64, 2, 2, 4>;
 
-enum KernelKind { kNone = 0, kLarge = 1, kMedium = 2, kGeneric = 3 };
+enum KernelKind { kNone = 0, kL32S5, kL32S4, kM64S4, kGeneric, kNumKinds };
 
-static const char *kind_name(int k) {
-    switch (k) {
-    case kLarge: return "tile256x256x64_s2";
-    case kMedium: return "tile128x128x64_s2";
-    case kGeneric: return "generic64x64x32";
-    default: return "none";
-    }
-}
+static const char *const kKindNames[kNumKinds] = {
+    "none", "tile256x256x32_s5", "tile256x256x32_s4", "tile128x128x64_s4", "generic64x64x32"};
+
+static const char *kind_name(int k) { return (k >= 0 && k < kNumKinds) ? kKindNames[k] : "none"; }
 
 static thread_local int t_last_hip_error = 0;
 
@@ -78,16 +77,28 @@ static bool tile_path_ok(int64_t M, int64_t N, int64_t K, const void *A, int64_t
     return true;
 }
 
+// Kernel for a shape.  GEMM_BF16_FORCE_KERNEL=<name> (a kKindNames entry)
+// overrides the choice when that kernel can run the shape; it exists for
+// benchmarking the alternatives.
+// Kernel for a shape.  GEMM_BF16_FORCE_KERNEL=<name> (a kKindNames entry)
+// overrides the choice when that kernel can run the shape; it exists for
+// benchmarking the alternatives.
 static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
                          int64_t ldb, const void *C, int64_t ldc, int cus) {
     if (M == 0 || N == 0) return kNone;
-    const char *force = std::getenv("GEMM_BF16_FORCE_KERNEL");
-    if (force && std::strcmp(force, "generic") == 0) return kGeneric;
-    if (tile_path_ok<CfgLarge>(M, N, K, A, lda, B, ldb, C, ldc)) {
-        const int64_t tiles = (M / CfgLarge::BM) * (N / CfgLarge::BN);
-        if (tiles * 2 >= cus || !tile_path_ok<CfgMedium>(M, N, K, A, lda, B, ldb, C, ldc)) return kLarge;
+    const bool okL = tile_path_ok<CfgL32S5>(M, N, K, A, lda, B, ldb, C, ldc);
+    const bool okM = tile_path_ok<CfgM64S4>(M, N, K, A, lda, B, ldb, C, ldc);
+    if (const char *force = std::getenv("GEMM_BF16_FORCE_KERNEL")) {
+        if (!std::strcmp(force, kKindNames[kGeneric])) return kGeneric;
+        if (!std::strcmp(force, kKindNames[kL32S5]) && okL) return kL32S5;
+        if (!std::strcmp(force, kKindNames[kL32S4]) && okL) return kL32S4;
+        if (!std::strcmp(force, kKindNames[kM64S4]) && okM) return kM64S4;
     }
-    if (tile_path_ok<CfgMedium>(M, N, K, A, lda, B, ldb, C, ldc)) return kMedium;
+    if (okL) {
+        const int64_t tiles = (M / CfgL32S5::BM) * (N / CfgL32S5::BN);
+        if (tiles * 2 >= cus || !okM) return kL32S5;
+    }
+    if (okM) return kM64S4;
     return kGeneric;
 }
 
@@ -147,8 +158,9 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t lda
     const int cus = device_cu_count();
     hipError_t err = hipSuccess;
     switch (choose_kernel(M, N, K, A, lda, B, ldb, C, ldc, cus)) {
-    case kLarge: err = launch_tile<CfgLarge>(args, cus, stream); break;
-    case kMedium: err = launch_tile<CfgMedium>(args, cus, stream); break;
+    case kL32S5: err = launch_tile<CfgL32S5>(args, cus, stream); break;
+    case kL32S4: err = launch_tile<CfgL32S4>(args, cus, stream); break;
+    case kM64S4: err = launch_tile<CfgM64S4>(args, cus, stream); break;
     default: err = launch_generic(args, cus, stream); break;
     }
     if (err != hipSuccess) {

@@ -7,27 +7,41 @@
 //   STAGES buffers (XOR-swizzled rows) --(ds_read_b128)--> VGPR fragments
 //   --(v_mfma_f32_32x32x16_bf16)--> fp32 accumulators in AGPRs
 //
-// and then the fused epilogue writes bf16 C straight from the accumulators.
+// and then the fused epilogue stages the accumulators through LDS and writes
+// bf16 C with 16-byte, column-contiguous stores.
 //
 // The decomposition into tiles, K-slices staged through on-chip memory and
 // register accumulators is the one of "Outperforming cuBLAS on H100: a
 // worklog", section "Recap of Simon's blog", and of the DeepGEMM article
-// (demingchina.com), section 2.1.  The pages' load path (TMA, mbarriers,
-// producer/consumer warpgroups) does not exist on gfx950; here every wave
-// both issues loads and computes, the loads write LDS directly (no VGPR
-// staging), and one workgroup barrier per K-slice orders the ring.
+// (demingchina.com), section 2.1; the multi-slice ring plays the role of its
+// double buffer (section 3.3) and of the worklog's producer/consumer queue
+// ("Kernel 4").  The pages' load path (TMA, mbarriers, producer warpgroups)
+// does not exist on gfx950: every wave both issues loads and computes, the
+// loads write LDS directly (no VGPR staging), and one workgroup barrier per
+// K-slice orders the ring.
 //
-// Operand layout in LDS.  A (row-major) and B (column-major, i.e. rows of
-// K per output column) are both K-contiguous, so both tiles are stored the
-// same way: one 128-byte row per M (or N) index holding BK = 64 bf16, split
-// into eight 16-byte chunks.  Chunk c of row r is stored at position
-// c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1).  A wave's fragment read
-// (32 consecutive rows, one logical chunk) then hits 8 (or 16) distinct
-// bank groups in every group of 8 (or 16) lanes -- the XOR swizzle the
-// DeepGEMM article (section 3.2) uses against shared-memory bank conflicts,
-// redone for 128-byte LDS rows.  The direct-to-LDS load writes a wave's 64
-// lanes to 1 KiB of consecutive LDS bytes, so the swizzle is applied on the
-// global side: lane i fetches the chunk that belongs at its LDS position.
+// Load pacing.  On gfx950 a vector-memory instruction that finds the
+// address/data path busy stalls the issuing wave, and with it that wave's
+// MFMA stream.  Issuing a slice's loads in a burst therefore costs far more
+// than the bytes suggest; spreading them one per four MFMAs and giving each
+// load more than two slices to land keeps the matrix cores busy.  So each
+// slice's loads are split into two halves: the first half goes out right
+// after the barrier that frees its buffer, the second half during the first
+// k-step of the next slice, and data is consumed STAGES-1 slices later.
+//
+// Operand layout in LDS.  A (row-major) and B (column-major, i.e. rows of K
+// per output column) are both K-contiguous, so both tiles are stored the
+// same way: one row of BK bf16 (2*BK bytes) per M (or N) index, split into
+// 16-byte chunks.  Chunk c of row r is stored at position c ^ swz(r):
+//   BK = 64 (8 chunks, 128-byte rows): swz(r) = (r & 7) ^ ((r >> 3) & 1)
+//   BK = 32 (4 chunks,  64-byte rows): swz(r) = ((r >> 1) ^ (r >> 3)) & 3
+// A fragment read (32 consecutive rows, one logical chunk per half-wave) then
+// touches distinct banks in every 8-lane group for 32 four-byte banks and in
+// every 16-lane group for 64 banks -- the XOR swizzle the DeepGEMM article
+// (section 3.2) uses against shared-memory bank conflicts, redone for these
+// row widths.  The direct-to-LDS load writes a wave's 64 lanes to 1 KiB of
+// consecutive LDS bytes, so the swizzle is applied on the global side: lane
+// i fetches the chunk that belongs at its LDS position.
 #pragma once
 
 #include "device_common.h"
@@ -47,109 +61,273 @@ struct TileConfig {
     static constexpr int FN = WTN / 32;
     static constexpr int KSTEPS = BK / 16;    // MFMA k-steps per slice
     static constexpr int kRowBytes = BK * 2;
-    static constexpr int kRowsPerLoad = 8;    // one wave-wide 16 B/lane load = 8 rows
+    static constexpr int kChunks = BK / 8;                 // 16-byte chunks per row
+    static constexpr int kRowsPerLoad = 64 / kChunks;      // rows one 1 KiB wave load fills
     static constexpr int kABytes = BM * kRowBytes;
     static constexpr int kBBytes = BN * kRowBytes;
     static constexpr int kStageBytes = kABytes + kBBytes;
     static constexpr int kLdsBytes = STAGES * kStageBytes;
     static constexpr int kALoads = BM / kRowsPerLoad / kWaves;  // per wave per slice
     static constexpr int kBLoads = BN / kRowsPerLoad / kWaves;
-    static constexpr int kLoadsPerStage = kALoads + kBLoads;
+    static constexpr int kLoads = kALoads + kBLoads;
+    static constexpr int kHalf = kLoads / 2;
+    // epilogue staging: per wave, 32 columns of WTM fp32 rows, padded by 16 B
+    static constexpr int kEpiColBytes = WTM * 4 + 16;
+    static constexpr int kEpiWaveBytes = 32 * kEpiColBytes;
 
-    static_assert(BK == 64, "the swizzle is written for 128-byte LDS rows");
+    static_assert(BK == 32 || BK == 64, "swizzles exist for 64- and 128-byte rows");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must hold whole 32x32 blocks");
     static_assert(BM % (kRowsPerLoad * kWaves) == 0 && BN % (kRowsPerLoad * kWaves) == 0,
                   "tile rows must split evenly over the waves' loads");
-    static_assert(STAGES >= 2, "need at least double buffering");
+    static_assert(kLoads % 2 == 0, "loads are issued in two halves");
+    static_assert(STAGES >= 3, "a slice's loads land STAGES-1 slices after the first half is issued");
+    static_assert((STAGES - 2) * kLoads + kHalf < 64, "vmcnt is a 6-bit counter");
     static_assert(kLdsBytes <= 160 * 1024, "gfx950 has 160 KiB of LDS per compute unit");
-    static_assert(kLoadsPerStage * (STAGES - 2) < 64, "vmcnt limit");
+    static_assert(kWaves * kEpiWaveBytes <= kLdsBytes, "epilogue staging reuses the ring");
+    static_assert(KSTEPS % 2 == 0, "fragment double-buffering alternates per k-step");
+    static_assert((FM * FN) % kHalf == 0 && FM * FN >= FM + FN, "MFMA count paces the loads");
 };
 
-__device__ __forceinline__ int lds_swizzle(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+template <int BK>
+__device__ __forceinline__ int lds_swizzle(int row) {
+    if constexpr (BK == 64)
+        return (row & 7) ^ ((row >> 3) & 1);
+    else
+        return ((row >> 1) ^ (row >> 3)) & 3;
+}
+
+// s_waitcnt vmcnt(n) for a run-time n that is a multiple of kStep, n < 64.
+template <int kStep, int kN = 0>
+__device__ __forceinline__ void wait_vmcnt_rt(int n) {
+    if constexpr (kN + kStep < 64) {
+        if (n > kN) {
+            wait_vmcnt_rt<kStep, kN + kStep>(n);
+            return;
+        }
+    }
+    wait_vmcnt<kN>();
+}
 
 template <class Cfg>
 struct TileKernel {
-    // Issue the loads of K-slice kt into ring buffer buf.  Wave-uniform
-    // arguments only; per-lane offsets come precomputed.
-    __device__ __forceinline__ static void issue_slice(char *smem, int buf, int kt, int wave,
-                                                       __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rB,
-                                                       const uint32_t (&vA)[2], const uint32_t (&vB)[2],
-                                                       uint32_t lda_bytes, uint32_t ldb_bytes) {
+    static constexpr int S = Cfg::STAGES;
+
+    // Per-lane state that stays fixed for the whole launch.
+    struct Lane {
+        uint32_t vA[2], vB[2];            // load voffsets by parity of the row group
+        uint32_t aRow, bRow;              // LDS row offsets of this lane's fragments
+        uint32_t chunk_off[Cfg::KSTEPS];  // swizzled chunk offset per k-step
+        uint32_t lda_bytes, ldb_bytes;
+        int wave;
+    };
+
+    // Loads number LO .. HI-1 of K-slice kt into ring buffer buf.  Loads
+    // 0 .. kALoads-1 fill this wave's row groups of A, the rest those of B.
+    template <int LO, int HI>
+    __device__ __forceinline__ static void issue(char *smem, int buf, int kt, const Lane &L,
+                                                 __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rB) {
         char *sA = smem + buf * Cfg::kStageBytes;
         char *sB = sA + Cfg::kABytes;
         const uint32_t kbytes = (uint32_t)kt * Cfg::BK * 2;
 #pragma unroll
-        for (int j = 0; j < Cfg::kALoads; ++j) {
-            const int q = wave * Cfg::kALoads + j;  // which 8-row group of the tile
-            buffer_load_lds16(rA, (GB_LDS void *)(sA + q * 1024), vA[q & 1],
-                              (uint32_t)(q * 8) * lda_bytes + kbytes);
-        }
-#pragma unroll
-        for (int j = 0; j < Cfg::kBLoads; ++j) {
-            const int q = wave * Cfg::kBLoads + j;
-            buffer_load_lds16(rB, (GB_LDS void *)(sB + q * 1024), vB[q & 1],
-                              (uint32_t)(q * 8) * ldb_bytes + kbytes);
+        for (int idx = LO; idx < HI; ++idx) {
+            if (idx < Cfg::kALoads) {
+                const int q = L.wave * Cfg::kALoads + idx;  // row group of the tile
+                buffer_load_lds16(rA, (GB_LDS void *)(sA + q * 1024), L.vA[q & 1],
+                                  (uint32_t)(q * Cfg::kRowsPerLoad) * L.lda_bytes + kbytes);
+            } else {
+                const int q = L.wave * Cfg::kBLoads + (idx - Cfg::kALoads);
+                buffer_load_lds16(rB, (GB_LDS void *)(sB + q * 1024), L.vB[q & 1],
+                                  (uint32_t)(q * Cfg::kRowsPerLoad) * L.ldb_bytes + kbytes);
+            }
         }
     }
 
-    // MFMAs over one K-slice held in ring buffer buf.
-    __device__ __forceinline__ static void compute_slice(const char *smem, int buf, uint32_t aRow, uint32_t bRow,
-                                                         const uint32_t (&chunk_off)[Cfg::KSTEPS],
-                                                         f32x16 (&acc)[Cfg::FM][Cfg::FN]) {
+    // Fragments of MFMA k-step kk (16 k values) of the slice in ring buffer
+    // buf: FM A blocks and FN B blocks, one ds_read_b128 each.
+    __device__ __forceinline__ static void read_frags(const char *smem, int buf, int kk, const Lane &L,
+                                                      bf16x8 (&a)[Cfg::FM], bf16x8 (&b)[Cfg::FN]) {
         const char *sA = smem + buf * Cfg::kStageBytes;
         const char *sB = sA + Cfg::kABytes;
 #pragma unroll
-        for (int kk = 0; kk < Cfg::KSTEPS; ++kk) {
-            bf16x8 a[Cfg::FM], b[Cfg::FN];
+        for (int i = 0; i < Cfg::FM; ++i)
+            a[i] = *(const GB_LDS bf16x8 *)(sA + L.aRow + i * 32 * Cfg::kRowBytes + L.chunk_off[kk]);
 #pragma unroll
-            for (int i = 0; i < Cfg::FM; ++i)
-                a[i] = *(const GB_LDS bf16x8 *)(sA + aRow + i * 32 * Cfg::kRowBytes + chunk_off[kk]);
+        for (int j = 0; j < Cfg::FN; ++j)
+            b[j] = *(const GB_LDS bf16x8 *)(sB + L.bRow + j * 32 * Cfg::kRowBytes + L.chunk_off[kk]);
+    }
+
+    __device__ __forceinline__ static void mfma_block(const bf16x8 (&a)[Cfg::FM], const bf16x8 (&b)[Cfg::FN],
+                                                      f32x16 (&acc)[Cfg::FM][Cfg::FN]) {
 #pragma unroll
-            for (int j = 0; j < Cfg::FN; ++j)
-                b[j] = *(const GB_LDS bf16x8 *)(sB + bRow + j * 32 * Cfg::kRowBytes + chunk_off[kk]);
+        for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
-            for (int i = 0; i < Cfg::FM; ++i)
+            for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = mfma_32x32x16(a[i], b[j], acc[i][j]);
+    }
+
+    // One k-step: FM groups of FN MFMAs on (a, b).  Before group p go out
+    // (if kRead) the reads of A fragment p and B fragment p of k-step rkk of
+    // ring buffer rbuf into (ra, rb), and (if kLoad) DMA loads number
+    // LO + p*kPer .. of slice lkt into ring buffer lbuf.  Hard scheduling
+    // fences between groups keep this order: each LDS read has a whole k-step
+    // to land, and the loads trickle out at one per FN MFMAs, a rate the
+    // memory pipeline absorbs without stalling the wave.
+    template <bool kRead, bool kLoad, int LO>
+    __device__ __forceinline__ static void kstep(char *smem, const bf16x8 (&a)[Cfg::FM], const bf16x8 (&b)[Cfg::FN],
+                                                 f32x16 (&acc)[Cfg::FM][Cfg::FN], int rbuf, int rkk,
+                                                 bf16x8 (&ra)[Cfg::FM], bf16x8 (&rb)[Cfg::FN], int lbuf, int lkt,
+                                                 const Lane &L, __amdgpu_buffer_rsrc_t rA,
+                                                 __amdgpu_buffer_rsrc_t rB) {
+        static_assert(Cfg::FM >= Cfg::FN, "one A and at most one B read per group");
+        static_assert(Cfg::kHalf % Cfg::FM == 0, "half a slice's loads split over the groups");
+        constexpr int kPer = Cfg::kHalf / Cfg::FM;
+        const char *sA = smem + rbuf * Cfg::kStageBytes;
+        const char *sB = sA + Cfg::kABytes;
 #pragma unroll
-                for (int j = 0; j < Cfg::FN; ++j)
-                    acc[i][j] = mfma_32x32x16(a[i], b[j], acc[i][j]);
+        for (int p = 0; p < Cfg::FM; ++p) {
+            if constexpr (kRead) {
+                ra[p] = *(const GB_LDS bf16x8 *)(sA + L.aRow + p * 32 * Cfg::kRowBytes + L.chunk_off[rkk]);
+                if (p < Cfg::FN)
+                    rb[p] = *(const GB_LDS bf16x8 *)(sB + L.bRow + p * 32 * Cfg::kRowBytes + L.chunk_off[rkk]);
+            }
+            if constexpr (kLoad) issue_range<LO>(smem, lbuf, lkt, L, rA, rB, p * kPer, kPer);
+#pragma unroll
+            for (int j = 0; j < Cfg::FN; ++j) acc[p][j] = mfma_32x32x16(a[p], b[j], acc[p][j]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
-    // Fused epilogue straight from the accumulators.  A 32x32 MFMA result
-    // gives lane l the column j = l % 32 and, in registers 4g..4g+3, the four
-    // consecutive rows 8g + 4(l / 32) + 0..3: with column-major C those are 8
-    // contiguous bytes, written (and, with beta, read) as one 8-byte access.
-    __device__ __forceinline__ static void epilogue(const GemmArgs &args, int64_t m0, int64_t n0, int wm, int wn,
-                                                    int lane, const f32x16 (&acc)[Cfg::FM][Cfg::FN]) {
+    // kCount loads starting at number LO + first (first is a compile-time
+    // constant after unrolling).
+    template <int LO>
+    __device__ __forceinline__ static void issue_range(char *smem, int buf, int kt, const Lane &L,
+                                                       __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rB,
+                                                       int first, int count) {
+        char *sA = smem + buf * Cfg::kStageBytes;
+        char *sB = sA + Cfg::kABytes;
+        const uint32_t kbytes = (uint32_t)kt * Cfg::BK * 2;
+#pragma unroll
+        for (int r = 0; r < count; ++r) {
+            const int idx = LO + first + r;
+            if (idx < Cfg::kALoads) {
+                const int q = L.wave * Cfg::kALoads + idx;
+                buffer_load_lds16(rA, (GB_LDS void *)(sA + q * 1024), L.vA[q & 1],
+                                  (uint32_t)(q * Cfg::kRowsPerLoad) * L.lda_bytes + kbytes);
+            } else {
+                const int q = L.wave * Cfg::kBLoads + (idx - Cfg::kALoads);
+                buffer_load_lds16(rB, (GB_LDS void *)(sB + q * 1024), L.vB[q & 1],
+                                  (uint32_t)(q * Cfg::kRowsPerLoad) * L.ldb_bytes + kbytes);
+            }
+        }
+    }
+
+    // One K-slice kt (in ring buffer cur) of the software pipeline.
+    //   first:  issue the first half of slice kt+S's loads (into cur, once
+    //           the barrier has freed it);
+    //   second: issue the second half of slice kt+S-1's loads (into the
+    //           buffer freed by the previous slice);
+    //   ahead:  loads issued after slice kt+1's, still allowed in flight at
+    //           the barrier;
+    //   kNext:  a slice kt+1 exists.
+    // kSteady: first = second = true and ahead = (S-2) * loads per slice, all
+    // known at compile time; otherwise (the last few slices of a tile) they
+    // are run-time values and the loads of those steps are issued in a burst.
+    // While the MFMAs of k-step kk run, the fragments of kk+1 are read.
+    // Before the last k-step every wave waits for slice kt+1, passes the
+    // barrier (all waves have then finished reading slice kt) and reads
+    // slice kt+1's first fragments during the last k-step's MFMAs.
+    template <bool kSteady, bool kNext>
+    __device__ __forceinline__ static void slice(char *smem, int kt, int cur, bool first, bool second, int ahead,
+                                                 const Lane &L, __amdgpu_buffer_rsrc_t rA,
+                                                 __amdgpu_buffer_rsrc_t rB, bf16x8 (&fa)[2][Cfg::FM],
+                                                 bf16x8 (&fb)[2][Cfg::FN], f32x16 (&acc)[Cfg::FM][Cfg::FN]) {
+        const int prev = (cur == 0) ? S - 1 : cur - 1;
+        const int next = (cur + 1 == S) ? 0 : cur + 1;
+        if (!kSteady && second) issue<Cfg::kHalf, Cfg::kLoads>(smem, prev, kt + S - 1, L, rA, rB);
+#pragma unroll
+        for (int kk = 0; kk < Cfg::KSTEPS - 1; ++kk) {
+            if (kSteady && kk == 0)
+                kstep<true, true, Cfg::kHalf>(smem, fa[0], fb[0], acc, cur, kk + 1, fa[1], fb[1], prev,
+                                               kt + S - 1, L, rA, rB);
+            else
+                kstep<true, false, 0>(smem, fa[kk & 1], fb[kk & 1], acc, cur, kk + 1, fa[(kk + 1) & 1],
+                                      fb[(kk + 1) & 1], 0, 0, L, rA, rB);
+        }
+        constexpr int kLast = (Cfg::KSTEPS - 1) & 1;
+        if constexpr (kNext) {
+            if constexpr (kSteady)
+                wait_vmcnt<(S - 2) * Cfg::kLoads>();
+            else
+                wait_vmcnt_rt<Cfg::kHalf>(ahead);
+            lds_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (kSteady) {
+                kstep<true, true, 0>(smem, fa[kLast], fb[kLast], acc, next, 0, fa[0], fb[0], cur, kt + S, L, rA,
+                                     rB);
+            } else {
+                if (first) issue<0, Cfg::kHalf>(smem, cur, kt + S, L, rA, rB);
+                kstep<true, false, 0>(smem, fa[kLast], fb[kLast], acc, next, 0, fa[0], fb[0], 0, 0, L, rA, rB);
+            }
+        } else {
+            kstep<false, false, 0>(smem, fa[kLast], fb[kLast], acc, 0, 0, fa[0], fb[0], 0, 0, L, rA, rB);
+        }
+    }
+
+    // Fused epilogue.  A 32x32 MFMA result gives lane l the column l % 32 and,
+    // in registers 4g..4g+3, the four consecutive rows 8g + 4(l/32) + 0..3.
+    // Each wave stages 32 columns at a time through its own LDS area as fp32
+    // (column-major, columns padded by 16 bytes against bank conflicts), then
+    // every lane takes 8 consecutive rows of one column: 16 lanes cover a
+    // column's WTM rows, so each store is 16 bytes and a column's bytes are
+    // written contiguously.  alpha, beta*C (read the same way), bias[n] and
+    // the activation are applied in fp32, then one RNE to bf16.
+    __device__ __forceinline__ static void epilogue(char *smem, const GemmArgs &args, int64_t m0, int64_t n0, int wm,
+                                                    int wn, int lane, int wave,
+                                                    const f32x16 (&acc)[Cfg::FM][Cfg::FN]) {
+        char *stage = smem + wave * Cfg::kEpiWaveBytes;
+        constexpr int kColChunks = Cfg::WTM / 8;        // 8-row chunks per column
+        constexpr int kIters = 32 * kColChunks / 64;    // per lane per 32 columns
+        static_assert((32 * kColChunks) % 64 == 0, "column chunks split over the wave");
         const int h = lane >> 5;
 #pragma unroll
         for (int j = 0; j < Cfg::FN; ++j) {
-            const int64_t n = n0 + wn * Cfg::WTN + j * 32 + (lane & 31);
-            float bias_v = 0.f;
-            if (args.flags & kEpiBias) bias_v = bf16_bits_to_f32(args.bias[n]);
-            uint16_t *col = args.C + n * args.ldc;
+            // accumulators -> LDS
 #pragma unroll
-            for (int i = 0; i < Cfg::FM; ++i) {
+            for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const int64_t m = m0 + wm * Cfg::WTM + i * 32 + g * 8 + h * 4;
-                    u32x2 *p = (u32x2 *)(col + m);
-                    float cin[4] = {0.f, 0.f, 0.f, 0.f};
-                    if (args.flags & kEpiBeta) {
-                        const u32x2 raw = *p;
-                        cin[0] = bf16_bits_to_f32(raw.x & 0xFFFFu);
-                        cin[1] = bf16_bits_to_f32(raw.x >> 16);
-                        cin[2] = bf16_bits_to_f32(raw.y & 0xFFFFu);
-                        cin[3] = bf16_bits_to_f32(raw.y >> 16);
-                    }
-                    float v[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) v[q] = epilogue_value(acc[i][j][g * 4 + q], cin[q], bias_v, args);
-                    u32x2 out;
-                    out.x = pack_bf16x2(v[0], v[1]);
-                    out.y = pack_bf16x2(v[2], v[3]);
-                    *p = out;
+                    f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                    const int row = i * 32 + g * 8 + h * 4;
+                    *(GB_LDS f32x4 *)(stage + (lane & 31) * Cfg::kEpiColBytes + row * 4) = v;
                 }
+            // LDS -> 8 consecutive rows of one column per lane -> global
+#pragma unroll
+            for (int t = 0; t < kIters; ++t) {
+                const int idx = t * 64 + lane;
+                const int col = idx / kColChunks;
+                const int q = idx % kColChunks;
+                const f32x4 lo = *(const GB_LDS f32x4 *)(stage + col * Cfg::kEpiColBytes + q * 32);
+                const f32x4 hi = *(const GB_LDS f32x4 *)(stage + col * Cfg::kEpiColBytes + q * 32 + 16);
+                const int64_t n = n0 + wn * Cfg::WTN + j * 32 + col;
+                const int64_t m = m0 + wm * Cfg::WTM + q * 8;
+                uint16_t *p = args.C + n * args.ldc + m;
+                const float bias_v = (args.flags & kEpiBias) ? bf16_bits_to_f32(args.bias[n]) : 0.f;
+                float cin[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                if (args.flags & kEpiBeta) {
+                    const u32x4 raw = *(const u32x4 *)p;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        cin[2 * e] = bf16_bits_to_f32(raw[e] & 0xFFFFu);
+                        cin[2 * e + 1] = bf16_bits_to_f32(raw[e] >> 16);
+                    }
+                }
+                const float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                u32x4 out;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    out[e] = pack_bf16x2(epilogue_value(x[2 * e], cin[2 * e], bias_v, args),
+                                         epilogue_value(x[2 * e + 1], cin[2 * e + 1], bias_v, args));
+                __builtin_nontemporal_store(out, (u32x4 *)p);
             }
         }
     }
@@ -162,33 +340,37 @@ template <class Cfg>
 __global__ void __launch_bounds__(Cfg::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_tile_kernel(const GemmArgs args, const TileSchedule sched) {
     using TK = TileKernel<Cfg>;
+    constexpr int S = Cfg::STAGES;
+    constexpr int L = Cfg::kLoads;
+    constexpr int H = Cfg::kHalf;
     __shared__ __attribute__((aligned(1024))) char smem[Cfg::kLdsBytes];
 
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave / Cfg::WAVES_N;
-    const int wn = wave % Cfg::WAVES_N;
+    typename TK::Lane Ln;
+    Ln.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = Ln.wave / Cfg::WAVES_N;
+    const int wn = Ln.wave % Cfg::WAVES_N;
+    Ln.lda_bytes = (uint32_t)args.lda * 2u;
+    Ln.ldb_bytes = (uint32_t)args.ldb * 2u;
 
-    const uint32_t lda_bytes = (uint32_t)args.lda * 2u;
-    const uint32_t ldb_bytes = (uint32_t)args.ldb * 2u;
-
-    // Load side: in an 8-row group q, lane i covers row 8q + i/8 and LDS
-    // position i%8, which holds logical chunk (i%8) ^ swz(row); swz depends
-    // on the parity of q only, so two offsets per operand suffice.
-    const int lrow = lane >> 3, lpos = lane & 7;
-    const uint32_t vA[2] = {lrow * lda_bytes + (uint32_t)((lpos ^ lrow) << 4),
-                            lrow * lda_bytes + (uint32_t)((lpos ^ lrow ^ 1) << 4)};
-    const uint32_t vB[2] = {lrow * ldb_bytes + (uint32_t)((lpos ^ lrow) << 4),
-                            lrow * ldb_bytes + (uint32_t)((lpos ^ lrow ^ 1) << 4)};
-
+    // Load side: in row group q, lane i covers row q*kRowsPerLoad + i/kChunks
+    // and LDS position i%kChunks, which holds logical chunk (i%kChunks) ^
+    // swz(row).  swz only sees the row's low bits, which the parity of q and
+    // the lane fix, so two offsets per operand suffice.
+    const int lrow = lane / Cfg::kChunks, lpos = lane % Cfg::kChunks;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int c = lpos ^ lds_swizzle<Cfg::BK>(p * Cfg::kRowsPerLoad + lrow);
+        Ln.vA[p] = lrow * Ln.lda_bytes + (uint32_t)(c << 4);
+        Ln.vB[p] = lrow * Ln.ldb_bytes + (uint32_t)(c << 4);
+    }
     // Read side: MFMA operand lane l takes row l % 32 of its 32-row block and
     // 8 consecutive k from logical chunk 2*kk + l/32.
-    const uint32_t aRow = (uint32_t)(wm * Cfg::WTM + (lane & 31)) * Cfg::kRowBytes;
-    const uint32_t bRow = (uint32_t)(wn * Cfg::WTN + (lane & 31)) * Cfg::kRowBytes;
-    uint32_t chunk_off[Cfg::KSTEPS];
+    Ln.aRow = (uint32_t)(wm * Cfg::WTM + (lane & 31)) * Cfg::kRowBytes;
+    Ln.bRow = (uint32_t)(wn * Cfg::WTN + (lane & 31)) * Cfg::kRowBytes;
 #pragma unroll
     for (int kk = 0; kk < Cfg::KSTEPS; ++kk)
-        chunk_off[kk] = (uint32_t)(((2 * kk + (lane >> 5)) ^ lds_swizzle(lane & 31)) << 4);
+        Ln.chunk_off[kk] = (uint32_t)(((2 * kk + (lane >> 5)) ^ lds_swizzle<Cfg::BK>(lane & 31)) << 4);
 
     const int nk = (int)(args.K / Cfg::BK);
     const int num_tiles = sched.num_tiles();
@@ -209,34 +391,42 @@ gemm_tile_kernel(const GemmArgs args, const TileSchedule sched) {
 #pragma unroll
             for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = f32x16{};
 
-        // Prologue: slices 0 .. STAGES-2 in flight.
-#pragma unroll
-        for (int s = 0; s < Cfg::STAGES - 1; ++s)
-            if (s < nk) TK::issue_slice(smem, s, s, wave, rA, rB, vA, vB, lda_bytes, ldb_bytes);
-
-        int buf = 0;
-        for (int kt = 0; kt < nk; ++kt) {
-            // Slice kt has landed once at most (STAGES-2) later slices are
-            // still outstanding; near the end fewer were issued, so drain.
-            if (kt + Cfg::STAGES - 2 < nk)
-                wait_vmcnt<Cfg::kLoadsPerStage * (Cfg::STAGES - 2)>();
-            else
-                wait_vmcnt<0>();
-            // Everyone's slice kt is in LDS, and everyone has finished
-            // reading the buffer that the next load overwrites.
-            lds_barrier();
-            const int next = kt + Cfg::STAGES - 1;
-            if (next < nk) {
-                int nbuf = buf + Cfg::STAGES - 1;
-                if (nbuf >= Cfg::STAGES) nbuf -= Cfg::STAGES;
-                TK::issue_slice(smem, nbuf, next, wave, rA, rB, vA, vB, lda_bytes, ldb_bytes);
-            }
-            TK::compute_slice(smem, buf, aRow, bRow, chunk_off, acc);
-            buf = (buf + 1 == Cfg::STAGES) ? 0 : buf + 1;
-        }
-        // LDS is reused by the next tile's loads.
+        // The previous tile's epilogue is done with LDS.
         lds_barrier();
-        TK::epilogue(args, m0, n0, wm, wn, lane, acc);
+        // Prologue: slices 0 .. S-2 and the first half of slice S-1 in
+        // flight; once slice 0 has landed everywhere its first fragments are
+        // read.
+        bf16x8 fa[2][Cfg::FM], fb[2][Cfg::FN];
+#pragma unroll
+        for (int s = 0; s < S - 1; ++s)
+            if (s < nk) TK::template issue<0, L>(smem, s, s, Ln, rA, rB);
+        if (S - 1 < nk) TK::template issue<0, H>(smem, S - 1, S - 1, Ln, rA, rB);
+        wait_vmcnt_rt<H>((nk - 1 < S - 2 ? nk - 1 : S - 2) * L + (S - 1 < nk ? H : 0));
+        lds_barrier();
+        TK::read_frags(smem, 0, 0, Ln, fa[0], fb[0]);
+        // Drain every LGKM operation once per tile (a real s_waitcnt the
+        // compiler sees), so at the loop head only the pipeline's own LDS
+        // reads are pending and its waits stay exact.
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+
+        int kt = 0, cur = 0;
+        for (; kt + S < nk; ++kt) {
+            TK::template slice<true, true>(smem, kt, cur, true, true, 0, Ln, rA, rB, fa, fb, acc);
+            cur = (cur + 1 == S) ? 0 : cur + 1;
+        }
+        for (; kt + 1 < nk; ++kt) {
+            // loads issued after slice kt+1's: slices kt+2 .. min(kt+S-1, nk-1)
+            const int last = (kt + S - 1 < nk - 1) ? kt + S - 1 : nk - 1;
+            TK::template slice<false, true>(smem, kt, cur, false, kt + S - 1 < nk, (last - (kt + 1)) * L, Ln, rA,
+                                            rB, fa, fb, acc);
+            cur = (cur + 1 == S) ? 0 : cur + 1;
+        }
+        TK::template slice<false, false>(smem, kt, cur, false, false, 0, Ln, rA, rB, fa, fb, acc);
+
+        // Every wave is done reading the ring (all loads landed at the last
+        // wait): its memory now stages the epilogue.
+        lds_barrier();
+        TK::epilogue(smem, args, m0, n0, wm, wn, lane, Ln.wave, acc);
     }
 }
 

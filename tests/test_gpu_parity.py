@@ -109,11 +109,11 @@ def check_full(tag, M, N, K, lda=None, ldb=None, ldc=None, alpha=1.0, beta=0.0, 
 # ------------------------------------------------------- tile-path shapes ---
 
 @pytest.mark.parametrize("M,N,K,kernel", [
-    (256, 256, 256, "tile128x128x64_s2"),
-    (512, 384, 192, "tile128x128x64_s2"),     # 3 K-slices (odd)
-    (512, 384, 256, "tile128x128x64_s2"),     # 4 K-slices (even)
-    (4096, 2048, 320, "tile256x256x64_s2"),   # 128 tiles of 256, 5 slices
-    (4096, 2048, 64, "tile256x256x64_s2"),    # a single K-slice
+    (256, 256, 256, "tile128x128x64_s4"),
+    (512, 384, 192, "tile128x128x64_s4"),     # 3 K-slices (odd)
+    (512, 384, 256, "tile128x128x64_s4"),     # 4 K-slices (even)
+    (4096, 2048, 320, "tile256x256x32_s5"),   # 128 tiles of 256, 5 slices
+    (4096, 2048, 64, "tile256x256x32_s5"),    # a single K-slice
 ])
 def test_tile_paths_full(M, N, K, kernel):
     check_full(f"tile {M}x{N}x{K}", M, N, K, seed=M + N + K, expect_kernel=kernel)
@@ -121,18 +121,36 @@ def test_tile_paths_full(M, N, K, kernel):
 
 def test_tile_path_epilogue_full():
     check_full("tile256 epilogue", 4096, 2048, 192, alpha=1.0, beta=0.5, use_bias=True,
-               epilogue="gelu_tanh", seed=11, expect_kernel="tile256x256x64_s2")
+               epilogue="gelu_tanh", seed=11, expect_kernel="tile256x256x32_s5")
     check_full("tile128 epilogue", 512, 512, 128, alpha=-0.75, beta=-1.5, use_bias=True,
-               epilogue="none", seed=12, expect_kernel="tile128x128x64_s2")
+               epilogue="none", seed=12, expect_kernel="tile128x128x64_s4")
     check_full("tile128 gelu only", 384, 256, 320, alpha=2.0, epilogue="gelu_tanh", seed=13,
-               expect_kernel="tile128x128x64_s2")
+               expect_kernel="tile128x128x64_s4")
 
 
 def test_tile_path_padded_leading_dims():
     check_full("tile128 padded ld", 512, 256, 256, lda=264, ldb=272, ldc=520, beta=0.25, use_bias=True,
-               seed=14, expect_kernel="tile128x128x64_s2")
+               seed=14, expect_kernel="tile128x128x64_s4")
     check_full("tile256 padded ld", 4096, 2048, 128, lda=136, ldb=192, ldc=4104, seed=15,
-               expect_kernel="tile256x256x64_s2")
+               expect_kernel="tile256x256x32_s5")
+
+
+# Every tile kernel forced onto shapes whose K-slice count walks through the
+# pipeline's prologue and tail cases (1 .. 10 slices, fewer and more slices
+# than LDS stages, odd and even counts).
+FORCEABLE = ["tile256x256x32_s5", "tile256x256x32_s4", "tile128x128x64_s4", "generic64x64x32"]
+
+
+@pytest.mark.parametrize("kernel", FORCEABLE)
+@pytest.mark.parametrize("K", [32, 64, 96, 128, 160, 192, 320])
+def test_forced_kernels_all_slice_counts(kernel, K, monkeypatch):
+    M, N = 1024, 512
+    bk = 64 if ("x64_" in kernel or kernel.startswith("generic")) else 32
+    if kernel.startswith("tile") and K % bk:
+        pytest.skip(f"{kernel} needs K % {bk} == 0")
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", kernel)
+    check_full(f"forced {kernel} K={K}", M, N, K, beta=0.5 if K % 64 else 0.0, use_bias=K == 96,
+               seed=K + len(kernel), expect_kernel=kernel)
 
 
 # ---------------------------------------------------- bounds-checked path ---
