@@ -1,12 +1,16 @@
 """Build the HIP library ``libgemm_bf16.so`` in-tree with hipcc for gfx950.
 
 Usage: ``python -m bf16_gemm_fp32_amd.build``.  Cross-compiles without a GPU.
+Each translation unit (host launcher, one per tile configuration) compiles in
+its own process; the objects are then linked into one shared library.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -14,23 +18,35 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libgemm_bf16.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+SOURCES = ["gemm_bf16.hip", "tile_large.hip", "tile_medium.hip", "tile_skinny.hip"]
 
 # Packed-fp32 VALU forms are disabled: the kernels write plain float code.
 HIP_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
 
 
-def build(verbose: bool = False) -> str:
-    src = os.path.join(CSRC, "gemm_bf16.hip")
-    tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp, src]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB_PATH)
+
+
+def build(verbose: bool = False) -> str:
+    with tempfile.TemporaryDirectory(prefix="gemm_bf16_build_") as tmp:
+        objs, cmds = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src.replace(".hip", ".o"))
+            objs.append(obj)
+            cmds.append([HIPCC, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj])
+        with concurrent.futures.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+            for f in [ex.submit(_run, c, verbose) for c in cmds]:
+                f.result()
+        out = LIB_PATH + ".tmp"
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", out, *objs], verbose)
+        os.replace(out, LIB_PATH)
     return LIB_PATH
 
 

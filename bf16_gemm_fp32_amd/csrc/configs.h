@@ -1,0 +1,29 @@
+// configs.h -- the tile-kernel configurations and their launch entry points
+// (each configuration's kernels live in a translation unit of their own so
+// the library builds in parallel).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+
+namespace gb {
+
+// 256x256 output tiles with four waves of 128x128 (256 fp32 accumulators per
+// lane, the AGPR half of the register file at one wave per SIMD) for large
+// grids, K-slices of 32 in a 5-deep LDS ring (all 160 KiB) so every slice's
+// loads have more than two slices to land.  128x128 tiles with four waves of
+// 64x64 when the 256-tiles would leave most compute units idle.
+struct ShapeL { static constexpr int BM = 256, BN = 256, BK = 32; };
+struct ShapeM { static constexpr int BM = 128, BN = 128, BK = 64; };
+
+// Short-and-wide products (M = 64 or 32): one workgroup per 32-column strip
+// streams B once, K-slices of 256.
+struct ShapeSkinny { static constexpr int BN = 32, KS = 256; };
+
+hipError_t launch_tile_large(const GemmArgs &args, int cus, hipStream_t stream);
+hipError_t launch_tile_medium(const GemmArgs &args, int cus, hipStream_t stream);
+hipError_t launch_skinny_m64(const GemmArgs &args, int cus, hipStream_t stream);
+hipError_t launch_skinny_m32(const GemmArgs &args, int cus, hipStream_t stream);
+
+}  // namespace gb

@@ -73,11 +73,14 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
     return __builtin_bit_cast(float, bits16 << 16);
 }
 
-// Two floats -> two bf16 (round to nearest even) packed low|high.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> two bf16 (round to nearest even) packed low|high: a single
+// v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    __bf16 a = (__bf16)lo;
-    __bf16 b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // GELU, tanh form: 0.5 y (1 + tanh(u)), u = sqrt(2/pi) (y + 0.044715 y^3).
@@ -92,8 +95,20 @@ __device__ __forceinline__ float gelu_tanh_f32(float y) {
     return y * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// alpha*acc (+ beta*c_in) (+ bias) then the activation, all in fp32.
-__device__ __forceinline__ float epilogue_value(float acc, float c_in, float bias_v, const GemmArgs &a) {
+// alpha*acc (+ beta*c_in) (+ bias) then the activation, all in fp32, with the
+// epilogue flags known at compile time (the tile kernels are instantiated per
+// flag combination, so the plain product carries no epilogue code at all).
+template <uint32_t kFlags>
+__device__ __forceinline__ float epilogue_value(float acc, float c_in, float bias_v, float alpha, float beta) {
+    float v = alpha * acc;
+    if constexpr ((kFlags & kEpiBeta) != 0) v += beta * c_in;
+    if constexpr ((kFlags & kEpiBias) != 0) v += bias_v;
+    if constexpr ((kFlags & kEpiGelu) != 0) v = gelu_tanh_f32(v);
+    return v;
+}
+
+// The same with run-time flags (the bounds-checked kernel).
+__device__ __forceinline__ float epilogue_value_rt(float acc, float c_in, float bias_v, const GemmArgs &a) {
     float v = a.alpha * acc;
     if (a.flags & kEpiBeta) v += a.beta * c_in;
     if (a.flags & kEpiBias) v += bias_v;

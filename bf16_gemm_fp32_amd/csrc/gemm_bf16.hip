@@ -9,27 +9,16 @@
 #include <cstdlib>
 #include <cstring>
 
+#include "configs.h"
 #include "device_common.h"
 #include "kernel_generic.h"
-#include "kernel_tile.h"
-#include "tile_schedule.h"
 
 namespace gb {
 
-// Kernel configurations.  256x256 output tiles with four waves of 128x128
-// (256 fp32 accumulators per lane, the AGPR half of the register file at one
-// wave per SIMD) for large grids; 128x128 tiles with four waves of 64x64 when
-// the 256-tiles would leave most compute units idle.  K-slices of 32 in a
-// 5-deep LDS ring (all 160 KiB) give each slice's loads more than two slices
-// to land; the 4-deep ring is kept for comparison.
-using CfgL32S5 = TileConfig<256, 256, 32, 2, 2, 5>;
-using CfgL32S4 = TileConfig<256, 256, 32, 2, 2, 4>;
-using CfgM64S4 = TileConfig<128, 128, 64, 2, 2, 4>;
+enum KernelKind { kNone = 0, kLarge, kMedium, kSkinny64, kSkinny32, kGeneric, kNumKinds };
 
-enum KernelKind { kNone = 0, kL32S5, kL32S4, kM64S4, kGeneric, kNumKinds };
-
-static const char *const kKindNames[kNumKinds] = {
-    "none", "tile256x256x32_s5", "tile256x256x32_s4", "tile128x128x64_s4", "generic64x64x32"};
+static const char *const kKindNames[kNumKinds] = {"none",           "tile256x256x32_s5", "tile128x128x64_s4",
+                                                  "skinny64x32x256", "skinny32x32x256",   "generic64x64x32"};
 
 static const char *kind_name(int k) { return (k >= 0 && k < kNumKinds) ? kKindNames[k] : "none"; }
 
@@ -77,43 +66,42 @@ static bool tile_path_ok(int64_t M, int64_t N, int64_t K, const void *A, int64_t
     return true;
 }
 
+static bool skinny_path_ok(int rows, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+                           int64_t ldb, const void *C, int64_t ldc) {
+    if (M != rows || K <= 0 || N % ShapeSkinny::BN || K % ShapeSkinny::KS) return false;
+    if (lda % 8 || ldb % 8 || ldc % 8) return false;
+    if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return false;
+    const int64_t lim = (int64_t)1 << 31;
+    if (((rows - 1) * lda + K) * 2 >= lim || ((ShapeSkinny::BN - 1) * ldb + K) * 2 >= lim) return false;
+    if (N / ShapeSkinny::BN >= lim) return false;
+    return true;
+}
+
 // Kernel for a shape.  GEMM_BF16_FORCE_KERNEL=<name> (a kKindNames entry)
 // overrides the choice when that kernel can run the shape; it exists for
-// benchmarking the alternatives.
-// Kernel for a shape.  GEMM_BF16_FORCE_KERNEL=<name> (a kKindNames entry)
-// overrides the choice when that kernel can run the shape; it exists for
-// benchmarking the alternatives.
+// testing and benchmarking the alternatives.
 static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
                          int64_t ldb, const void *C, int64_t ldc, int cus) {
     if (M == 0 || N == 0) return kNone;
-    const bool okL = tile_path_ok<CfgL32S5>(M, N, K, A, lda, B, ldb, C, ldc);
-    const bool okM = tile_path_ok<CfgM64S4>(M, N, K, A, lda, B, ldb, C, ldc);
+    const bool okL = tile_path_ok<ShapeL>(M, N, K, A, lda, B, ldb, C, ldc);
+    const bool okM = tile_path_ok<ShapeM>(M, N, K, A, lda, B, ldb, C, ldc);
+    const bool okS64 = skinny_path_ok(64, M, N, K, A, lda, B, ldb, C, ldc);
+    const bool okS32 = skinny_path_ok(32, M, N, K, A, lda, B, ldb, C, ldc);
     if (const char *force = std::getenv("GEMM_BF16_FORCE_KERNEL")) {
         if (!std::strcmp(force, kKindNames[kGeneric])) return kGeneric;
-        if (!std::strcmp(force, kKindNames[kL32S5]) && okL) return kL32S5;
-        if (!std::strcmp(force, kKindNames[kL32S4]) && okL) return kL32S4;
-        if (!std::strcmp(force, kKindNames[kM64S4]) && okM) return kM64S4;
+        if (!std::strcmp(force, kKindNames[kLarge]) && okL) return kLarge;
+        if (!std::strcmp(force, kKindNames[kMedium]) && okM) return kMedium;
+        if (!std::strcmp(force, kKindNames[kSkinny64]) && okS64) return kSkinny64;
+        if (!std::strcmp(force, kKindNames[kSkinny32]) && okS32) return kSkinny32;
     }
     if (okL) {
-        const int64_t tiles = (M / CfgL32S5::BM) * (N / CfgL32S5::BN);
-        if (tiles * 2 >= cus || !okM) return kL32S5;
+        const int64_t tiles = (M / ShapeL::BM) * (N / ShapeL::BN);
+        if (tiles * 2 >= cus || !okM) return kLarge;
     }
-    if (okM) return kM64S4;
+    if (okM) return kMedium;
+    if (okS64) return kSkinny64;
+    if (okS32) return kSkinny32;
     return kGeneric;
-}
-
-template <class Cfg>
-static hipError_t launch_tile(const GemmArgs &args, int cus, hipStream_t stream) {
-    TileSchedule s{};
-    s.tiles_m = (int)(args.M / Cfg::BM);
-    s.tiles_n = (int)(args.N / Cfg::BN);
-    s.group_m = 4;
-    s.order = kOrderGrouped;
-    s.hilbert_log2 = 0;
-    const int tiles = s.num_tiles();
-    s.grid = tiles < cus ? tiles : cus;
-    hipLaunchKernelGGL(gemm_tile_kernel<Cfg>, dim3(s.grid), dim3(Cfg::kThreads), 0, stream, args, s);
-    return hipGetLastError();
 }
 
 static hipError_t launch_generic(const GemmArgs &args, int cus, hipStream_t stream) {
@@ -158,9 +146,10 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t lda
     const int cus = device_cu_count();
     hipError_t err = hipSuccess;
     switch (choose_kernel(M, N, K, A, lda, B, ldb, C, ldc, cus)) {
-    case kL32S5: err = launch_tile<CfgL32S5>(args, cus, stream); break;
-    case kL32S4: err = launch_tile<CfgL32S4>(args, cus, stream); break;
-    case kM64S4: err = launch_tile<CfgM64S4>(args, cus, stream); break;
+    case kLarge: err = launch_tile_large(args, cus, stream); break;
+    case kMedium: err = launch_tile_medium(args, cus, stream); break;
+    case kSkinny64: err = launch_skinny_m64(args, cus, stream); break;
+    case kSkinny32: err = launch_skinny_m32(args, cus, stream); break;
     default: err = launch_generic(args, cus, stream); break;
     }
     if (err != hipSuccess) {

@@ -92,7 +92,7 @@ gemm_generic_kernel(const GemmArgs args, int64_t tiles_m, int64_t num_tiles) {
                 const int64_t m = m0 + wm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
                 if (m < args.M) {
                     const float cin = (args.flags & kEpiBeta) ? bf16_bits_to_f32(col[m]) : 0.f;
-                    const float v = epilogue_value(acc[r], cin, bias_v, args);
+                    const float v = epilogue_value_rt(acc[r], cin, bias_v, args);
                     col[m] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFFu);
                 }
             }

@@ -281,6 +281,7 @@ struct TileKernel {
     // column's WTM rows, so each store is 16 bytes and a column's bytes are
     // written contiguously.  alpha, beta*C (read the same way), bias[n] and
     // the activation are applied in fp32, then one RNE to bf16.
+    template <uint32_t kFlags>
     __device__ __forceinline__ static void epilogue(char *smem, const GemmArgs &args, int64_t m0, int64_t n0, int wm,
                                                     int wn, int lane, int wave,
                                                     const f32x16 (&acc)[Cfg::FM][Cfg::FN]) {
@@ -311,9 +312,10 @@ struct TileKernel {
                 const int64_t n = n0 + wn * Cfg::WTN + j * 32 + col;
                 const int64_t m = m0 + wm * Cfg::WTM + q * 8;
                 uint16_t *p = args.C + n * args.ldc + m;
-                const float bias_v = (args.flags & kEpiBias) ? bf16_bits_to_f32(args.bias[n]) : 0.f;
+                float bias_v = 0.f;
+                if constexpr ((kFlags & kEpiBias) != 0) bias_v = bf16_bits_to_f32(args.bias[n]);
                 float cin[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                if (args.flags & kEpiBeta) {
+                if constexpr ((kFlags & kEpiBeta) != 0) {
                     const u32x4 raw = *(const u32x4 *)p;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -325,8 +327,9 @@ struct TileKernel {
                 u32x4 out;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    out[e] = pack_bf16x2(epilogue_value(x[2 * e], cin[2 * e], bias_v, args),
-                                         epilogue_value(x[2 * e + 1], cin[2 * e + 1], bias_v, args));
+                    out[e] = pack_bf16x2(epilogue_value<kFlags>(x[2 * e], cin[2 * e], bias_v, args.alpha, args.beta),
+                                         epilogue_value<kFlags>(x[2 * e + 1], cin[2 * e + 1], bias_v, args.alpha,
+                                                                args.beta));
                 __builtin_nontemporal_store(out, (u32x4 *)p);
             }
         }
@@ -336,7 +339,7 @@ struct TileKernel {
 // Requirements checked by the host before launch: M % BM == 0, N % BN == 0,
 // K % BK == 0, K > 0, A/B/C 16-byte aligned, lda/ldb/ldc multiples of 8, and
 // BM*lda*2 + 2K, BN*ldb*2 + 2K below 2^31 (32-bit buffer offsets).
-template <class Cfg>
+template <class Cfg, uint32_t kFlags>
 __global__ void __launch_bounds__(Cfg::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_tile_kernel(const GemmArgs args, const TileSchedule sched) {
     using TK = TileKernel<Cfg>;
@@ -426,8 +429,35 @@ gemm_tile_kernel(const GemmArgs args, const TileSchedule sched) {
         // Every wave is done reading the ring (all loads landed at the last
         // wait): its memory now stages the epilogue.
         lds_barrier();
-        TK::epilogue(smem, args, m0, n0, wm, wn, lane, Ln.wave, acc);
+        TK::template epilogue<kFlags>(smem, args, m0, n0, wm, wn, lane, Ln.wave, acc);
     }
+}
+
+// Launch the tile kernel of configuration Cfg with the epilogue flags of
+// args baked in.  The grid is min(tiles, compute units): one persistent
+// workgroup per compute unit.
+template <class Cfg>
+hipError_t launch_tile(const GemmArgs &args, int cus, hipStream_t stream) {
+    TileSchedule s{};
+    s.tiles_m = (int)(args.M / Cfg::BM);
+    s.tiles_n = (int)(args.N / Cfg::BN);
+    s.group_m = 4;
+    s.order = kOrderGrouped;
+    s.hilbert_log2 = 0;
+    const int tiles = s.num_tiles();
+    s.grid = tiles < cus ? tiles : cus;
+    const dim3 grid(s.grid), block(Cfg::kThreads);
+    switch (args.flags & 7u) {
+    case 0: hipLaunchKernelGGL((gemm_tile_kernel<Cfg, 0>), grid, block, 0, stream, args, s); break;
+    case 1: hipLaunchKernelGGL((gemm_tile_kernel<Cfg, 1>), grid, block, 0, stream, args, s); break;
+    case 2: hipLaunchKernelGGL((gemm_tile_kernel<Cfg, 2>), grid, block, 0, stream, args, s); break;
+    case 3: hipLaunchKernelGGL((gemm_tile_kernel<Cfg, 3>), grid, block, 0, stream, args, s); break;
+    case 4: hipLaunchKernelGGL((gemm_tile_kernel<Cfg, 4>), grid, block, 0, stream, args, s); break;
+    case 5: hipLaunchKernelGGL((gemm_tile_kernel<Cfg, 5>), grid, block, 0, stream, args, s); break;
+    case 6: hipLaunchKernelGGL((gemm_tile_kernel<Cfg, 6>), grid, block, 0, stream, args, s); break;
+    default: hipLaunchKernelGGL((gemm_tile_kernel<Cfg, 7>), grid, block, 0, stream, args, s); break;
+    }
+    return hipGetLastError();
 }
 
 }  // namespace gb

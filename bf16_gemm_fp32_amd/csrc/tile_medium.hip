@@ -1,0 +1,14 @@
+// tile_medium.hip -- instances of the 128x128x64, 4-stage tile kernel.
+#include "configs.h"
+#include "kernel_tile.h"
+
+namespace gb {
+
+using CfgMedium = TileConfig<128, 128, 64, 2, 2, 4>;
+static_assert(CfgMedium::BM == ShapeM::BM && CfgMedium::BN == ShapeM::BN && CfgMedium::BK == ShapeM::BK);
+
+hipError_t launch_tile_medium(const GemmArgs &args, int cus, hipStream_t stream) {
+    return launch_tile<CfgMedium>(args, cus, stream);
+}
+
+}  // namespace gb

@@ -138,7 +138,7 @@ def test_tile_path_padded_leading_dims():
 # Every tile kernel forced onto shapes whose K-slice count walks through the
 # pipeline's prologue and tail cases (1 .. 10 slices, fewer and more slices
 # than LDS stages, odd and even counts).
-FORCEABLE = ["tile256x256x32_s5", "tile256x256x32_s4", "tile128x128x64_s4", "generic64x64x32"]
+FORCEABLE = ["tile256x256x32_s5", "tile128x128x64_s4", "generic64x64x32"]
 
 
 @pytest.mark.parametrize("kernel", FORCEABLE)
@@ -151,6 +151,36 @@ def test_forced_kernels_all_slice_counts(kernel, K, monkeypatch):
     monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", kernel)
     check_full(f"forced {kernel} K={K}", M, N, K, beta=0.5 if K % 64 else 0.0, use_bias=K == 96,
                seed=K + len(kernel), expect_kernel=kernel)
+
+
+# The tile kernels are compiled once per epilogue combination (beta, bias,
+# GELU): every combination on both tile configurations.
+@pytest.mark.parametrize("kernel,M,N,K", [("tile256x256x32_s5", 2048, 1024, 160),
+                                          ("tile128x128x64_s4", 512, 384, 192)])
+@pytest.mark.parametrize("beta,use_bias,epi", [(b, u, e) for b in (0.0, -0.75) for u in (False, True)
+                                               for e in ("none", "gelu_tanh")])
+def test_tile_epilogue_combinations(kernel, M, N, K, beta, use_bias, epi, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", kernel)
+    check_full(f"{kernel} beta={beta} bias={use_bias} {epi}", M, N, K, alpha=1.25, beta=beta,
+               use_bias=use_bias, epilogue=epi, seed=int(abs(beta) * 4) + 2 * use_bias + len(epi),
+               expect_kernel=kernel)
+
+
+# The streaming kernel for M = 64 / 32: slice counts through its ring
+# prologue and tail (1 .. 10 slices of 256), epilogue combinations, padding.
+@pytest.mark.parametrize("M", [64, 32])
+@pytest.mark.parametrize("K", [256, 512, 768, 1024, 1280, 2560])
+def test_skinny_slice_counts(M, K):
+    check_full(f"skinny M={M} K={K}", M, 1024, K, seed=M + K, expect_kernel=f"skinny{M}x32x256")
+
+
+@pytest.mark.parametrize("beta,use_bias,epi", [(0.5, True, "gelu_tanh"), (0.0, True, "none"),
+                                               (-1.0, False, "gelu_tanh")])
+def test_skinny_epilogues_and_padding(beta, use_bias, epi):
+    check_full(f"skinny epilogue beta={beta} bias={use_bias} {epi}", 64, 2048, 512, alpha=0.5, beta=beta,
+               use_bias=use_bias, epilogue=epi, seed=41, expect_kernel="skinny64x32x256")
+    check_full("skinny padded", 64, 512, 768, lda=776, ldb=1024, ldc=72, beta=beta, use_bias=use_bias,
+               epilogue=epi, seed=42, expect_kernel="skinny64x32x256")
 
 
 # ---------------------------------------------------- bounds-checked path ---
