@@ -34,12 +34,15 @@
 // same way: one row of BK bf16 (2*BK bytes) per M (or N) index, split into
 // 16-byte chunks.  Chunk c of row r is stored at position c ^ swz(r):
 //   BK = 64 (8 chunks, 128-byte rows): swz(r) = (r & 7) ^ ((r >> 3) & 1)
-//   BK = 32 (4 chunks,  64-byte rows): swz(r) = ((r >> 1) ^ (r >> 3)) & 3
-// A fragment read (32 consecutive rows, one logical chunk per half-wave) then
-// touches distinct banks in every 8-lane group for 32 four-byte banks and in
-// every 16-lane group for 64 banks -- the XOR swizzle the DeepGEMM article
-// (section 3.2) uses against shared-memory bank conflicts, redone for these
-// row widths.  The direct-to-LDS load writes a wave's 64 lanes to 1 KiB of
+//   BK = 32 (4 chunks,  64-byte rows): swz(r) = (r >> 2) & 3
+// On gfx950 LDS has 64 four-byte banks and a ds_read_b128 is served in four
+// phases of 16 lanes; lanes 0-31 fall into two phases by the parity of lane
+// bits 2..4 ({0-3, 12-15, 20-27} and {4-11, 16-19, 28-31}), lanes 32-63 the
+// same way (measured with the LDS bank-conflict counter).  A fragment read
+// (32 consecutive rows, one logical chunk per half-wave) then touches 16
+// distinct 16-byte bank groups in every phase -- the XOR swizzle the DeepGEMM
+// article (section 3.2) uses against shared-memory bank conflicts, redone for
+// these row widths and this lane-to-phase map.  The direct-to-LDS load writes a wave's 64 lanes to 1 KiB of
 // consecutive LDS bytes, so the swizzle is applied on the global side: lane
 // i fetches the chunk that belongs at its LDS position.
 #pragma once
@@ -93,7 +96,7 @@ __device__ __forceinline__ int lds_swizzle(int row) {
     if constexpr (BK == 64)
         return (row & 7) ^ ((row >> 3) & 1);
     else
-        return ((row >> 1) ^ (row >> 3)) & 3;
+        return (row >> 2) & 3;
 }
 
 // s_waitcnt vmcnt(n) for a run-time n that is a multiple of kStep, n < 64.
