@@ -12,7 +12,13 @@ of HIP events recorded on the stream the kernel runs on.
 Prints ONE JSON line (rank 0, one GPU).  With --all it prints one line per
 workload instead.
 
-    python bench.py [--gpus 1] [--steps 8] [--warmup 1] [--workload square_4096]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--workload square_4096]
+
+The roofline's "traffic" (HBM bytes per launch) comes from rocprofv3
+FETCH_SIZE / WRITE_SIZE passes recorded in profiles/hbm_traffic.json, each
+counter scaled by what it reads for a plain device copy of known size.  An
+entry is used only if it was recorded for the same kernel, workload and
+library source digest; otherwise traffic is null.
 """
 from __future__ import annotations
 
@@ -36,6 +42,7 @@ METRIC = "bf16 GEMM TFLOP/s at M=N=K=4096 and % of MI355X dense bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
 EPI = {"none": 0, "gelu_tanh": 1}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
 def log(msg):
@@ -68,8 +75,8 @@ def cpu_baseline(w, d, budget_cols=None):
     nthreads = cpu_threads()
     M, N, K = w.M, w.N, w.K
     if budget_cols is None:
-        # about 10-20 s on 16 host cores at ~0.18 GMAC/s per core
-        target_macs = 2.0e9 * nthreads
+        # about 10-20 s on 16 host cores at ~0.37 GMAC/s per core
+        target_macs = 4.0e9 * nthreads
         budget_cols = int(max(1, min(N, target_macs // max(1, M * K))))
     cols = budget_cols
     ms = np.tile(np.arange(M, dtype=np.int64), cols)
@@ -87,6 +94,22 @@ def cpu_baseline(w, d, budget_cols=None):
         "sample": f"{cols} whole columns of C ({M * cols} of {M * N} outputs, {flops:.3e} flop) "
                   f"in {dt:.2f} s on {cpu_model()}",
     }
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch from the recorded counter passes, or None when no
+    record matches this kernel, workload and source digest."""
+    from bf16_gemm_fp32_amd.build import source_digest
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    digest = source_digest()
+    for e in rec.get("entries", []):
+        if e.get("workload") == workload and e.get("kernel") == kernel and e.get("source_digest") == digest:
+            return e.get("hbm_bytes_per_launch")
+    return None
 
 
 def run_workload(w, steps, warmup, cold, with_cpu):
@@ -151,12 +174,16 @@ def run_workload(w, steps, warmup, cold, with_cpu):
     gbs = w.algorithmic_bytes / (mean_ms * 1e-3) / 1e9
     log(f"[bench] per-launch ms: mean {mean_ms:.4f} min {min(per):.4f} max {max(per):.4f} -> {tflops:.1f} TFLOP/s")
 
+    traffic = measured_traffic(w.name, kname)
     if w.bound == "hbm":
         roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
-                "traffic": None}
+                "traffic": traffic}
     else:
         roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None}
+                "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic}
+    roof["traffic_unit"] = "bytes per launch (HBM, counter-measured)"
+    roof["algorithmic_bytes"] = w.algorithmic_bytes
+    roof["traffic_over_algorithmic"] = traffic / w.algorithmic_bytes if traffic else None
     out = {
         "metric": METRIC if w.name == "square_4096" else f"bf16 GEMM TFLOP/s on {w.name}",
         "value": tflops,
@@ -206,8 +233,8 @@ def calibrate_copy(mib):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=8)
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="square_4096", choices=list(inputs.WORKLOADS))
     ap.add_argument("--all", action="store_true", help="one JSON line per workload")
     ap.add_argument("--cold", choices=["auto", "yes", "no"], default="auto",

@@ -7,6 +7,8 @@ its own process; the objects are then linked into one shared library.
 from __future__ import annotations
 
 import concurrent.futures
+import glob
+import hashlib
 import os
 import subprocess
 import sys
@@ -18,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libgemm_bf16.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["gemm_bf16.hip", "tile_large.hip", "tile_medium.hip", "tile_skinny.hip"]
+SOURCES = ["gemm_bf16.hip", "tile_large.hip", "tile_medium.hip", "tile_ring.hip", "tile_skinny.hip"]
 
 # Packed-fp32 VALU forms are disabled: the kernels write plain float code.
 HIP_FLAGS = [
@@ -26,6 +28,27 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
+
+
+def source_files() -> list:
+    """Every file the library is compiled from (kernels, launchers, C header)."""
+    files = glob.glob(os.path.join(CSRC, "*.h")) + glob.glob(os.path.join(CSRC, "*.hip"))
+    files += glob.glob(os.path.join(INCLUDE, "*.h"))
+    return sorted(files)
+
+
+def source_digest() -> str:
+    """Short SHA-256 over the library sources (path and bytes of each file).
+    Hardware-counter results recorded for one digest describe exactly that
+    code; any edit to a kernel, a launcher or the header changes it."""
+    h = hashlib.sha256()
+    for path in source_files():
+        h.update(os.path.relpath(path, ROOT).encode())
+        h.update(b"\0")
+        with open(path, "rb") as f:
+            h.update(f.read())
+        h.update(b"\0")
+    return h.hexdigest()[:16]
 
 
 def _run(cmd, verbose):
@@ -51,4 +74,7 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-q" not in sys.argv))
+    if "--digest" in sys.argv:
+        print(source_digest())
+    else:
+        print(build(verbose="-q" not in sys.argv))

@@ -16,6 +16,9 @@ namespace gb {
 // 64x64 when the 256-tiles would leave most compute units idle.
 struct ShapeL { static constexpr int BM = 256, BN = 256, BK = 32; };
 struct ShapeM { static constexpr int BM = 128, BN = 128, BK = 64; };
+// 256x256 output tiles with K-slices of 64 (full 128-byte operand rows) in
+// a ring of five 32 KiB single-operand units.
+struct ShapeRing { static constexpr int BM = 256, BN = 256, BK = 64; };
 
 // Short-and-wide products (M = 64 or 32): one workgroup per 32-column strip
 // streams B once, K-slices of 256.
@@ -23,6 +26,7 @@ struct ShapeSkinny { static constexpr int BN = 32, KS = 256; };
 
 hipError_t launch_tile_large(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_medium(const GemmArgs &args, int cus, hipStream_t stream);
+hipError_t launch_tile_ring(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_skinny_m64(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_skinny_m32(const GemmArgs &args, int cus, hipStream_t stream);
 

@@ -1,0 +1,73 @@
+// epilogue_tile.h -- the fused epilogue of the 32x32-MFMA tile kernels:
+// accumulators -> alpha, beta*C, bias, activation in fp32 -> bf16 -> C.
+// Cfg supplies the wave tile (WTM x WTN as FM x FN blocks of 32x32) and the
+// per-wave LDS staging area (kEpiColBytes, kEpiWaveBytes).
+#pragma once
+
+#include "device_common.h"
+
+namespace gb {
+
+// A 32x32 MFMA result gives lane l the column l % 32 and, in registers
+// 4g..4g+3, the four consecutive rows 8g + 4(l/32) + 0..3.  Each wave stages
+// 32 columns at a time through its own LDS area as fp32 (column-major,
+// columns padded by 16 bytes against bank conflicts), then every lane takes
+// 8 consecutive rows of one column: 16 lanes cover a column's WTM rows, so
+// each store is 16 bytes and a column's bytes are written contiguously.
+// alpha, beta*C (read the same way), bias[n] and the activation are applied
+// in fp32, then one RNE to bf16.  The caller has made the staging memory
+// free (a barrier after the last LDS read of the main loop).
+template <class Cfg, uint32_t kFlags>
+__device__ __forceinline__ void tile_epilogue(char *smem, const GemmArgs &args, int64_t m0, int64_t n0, int wm,
+                                              int wn, int lane, int wave, const f32x16 (&acc)[Cfg::FM][Cfg::FN]) {
+    char *stage = smem + wave * Cfg::kEpiWaveBytes;
+    constexpr int kColChunks = Cfg::WTM / 8;      // 8-row chunks per column
+    constexpr int kIters = 32 * kColChunks / 64;  // per lane per 32 columns
+    static_assert((32 * kColChunks) % 64 == 0, "column chunks split over the wave");
+    const int h = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+        // accumulators -> LDS
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                const int row = i * 32 + g * 8 + h * 4;
+                *(GB_LDS f32x4 *)(stage + (lane & 31) * Cfg::kEpiColBytes + row * 4) = v;
+            }
+        // LDS -> 8 consecutive rows of one column per lane -> global
+#pragma unroll
+        for (int t = 0; t < kIters; ++t) {
+            const int idx = t * 64 + lane;
+            const int col = idx / kColChunks;
+            const int q = idx % kColChunks;
+            const f32x4 lo = *(const GB_LDS f32x4 *)(stage + col * Cfg::kEpiColBytes + q * 32);
+            const f32x4 hi = *(const GB_LDS f32x4 *)(stage + col * Cfg::kEpiColBytes + q * 32 + 16);
+            const int64_t n = n0 + wn * Cfg::WTN + j * 32 + col;
+            const int64_t m = m0 + wm * Cfg::WTM + q * 8;
+            uint16_t *p = args.C + n * args.ldc + m;
+            float bias_v = 0.f;
+            if constexpr ((kFlags & kEpiBias) != 0) bias_v = bf16_bits_to_f32(args.bias[n]);
+            float cin[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            if constexpr ((kFlags & kEpiBeta) != 0) {
+                const u32x4 raw = *(const u32x4 *)p;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    cin[2 * e] = bf16_bits_to_f32(raw[e] & 0xFFFFu);
+                    cin[2 * e + 1] = bf16_bits_to_f32(raw[e] >> 16);
+                }
+            }
+            const float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            u32x4 out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                out[e] = pack_bf16x2(
+                    epilogue_value<kFlags>(x[2 * e], cin[2 * e], bias_v, args.alpha, args.beta),
+                    epilogue_value<kFlags>(x[2 * e + 1], cin[2 * e + 1], bias_v, args.alpha, args.beta));
+            __builtin_nontemporal_store(out, (u32x4 *)p);
+        }
+    }
+}
+
+}  // namespace gb

@@ -15,10 +15,11 @@
 
 namespace gb {
 
-enum KernelKind { kNone = 0, kLarge, kMedium, kSkinny64, kSkinny32, kGeneric, kNumKinds };
+enum KernelKind { kNone = 0, kLarge, kMedium, kSkinny64, kSkinny32, kGeneric, kRing, kNumKinds };
 
-static const char *const kKindNames[kNumKinds] = {"none",           "tile256x256x32_s5", "tile128x128x64_s4",
-                                                  "skinny64x32x256", "skinny32x32x256",   "generic64x64x32"};
+static const char *const kKindNames[kNumKinds] = {"none",            "tile256x256x32_s5", "tile128x128x64_s4",
+                                                  "skinny64x32x256", "skinny32x32x256",   "generic64x64x32",
+                                                  "ring256x256x64"};
 
 static const char *kind_name(int k) { return (k >= 0 && k < kNumKinds) ? kKindNames[k] : "none"; }
 
@@ -85,18 +86,22 @@ static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t
     if (M == 0 || N == 0) return kNone;
     const bool okL = tile_path_ok<ShapeL>(M, N, K, A, lda, B, ldb, C, ldc);
     const bool okM = tile_path_ok<ShapeM>(M, N, K, A, lda, B, ldb, C, ldc);
+    const bool okR = tile_path_ok<ShapeRing>(M, N, K, A, lda, B, ldb, C, ldc);
     const bool okS64 = skinny_path_ok(64, M, N, K, A, lda, B, ldb, C, ldc);
     const bool okS32 = skinny_path_ok(32, M, N, K, A, lda, B, ldb, C, ldc);
     if (const char *force = std::getenv("GEMM_BF16_FORCE_KERNEL")) {
         if (!std::strcmp(force, kKindNames[kGeneric])) return kGeneric;
         if (!std::strcmp(force, kKindNames[kLarge]) && okL) return kLarge;
         if (!std::strcmp(force, kKindNames[kMedium]) && okM) return kMedium;
+        if (!std::strcmp(force, kKindNames[kRing]) && okR) return kRing;
         if (!std::strcmp(force, kKindNames[kSkinny64]) && okS64) return kSkinny64;
         if (!std::strcmp(force, kKindNames[kSkinny32]) && okS32) return kSkinny32;
     }
-    if (okL) {
+    // 256x256 tiles when they give at least half the compute units a tile:
+    // K-slices of 64 (full-line operand rows) when K allows, else of 32.
+    if (okR || okL) {
         const int64_t tiles = (M / ShapeL::BM) * (N / ShapeL::BN);
-        if (tiles * 2 >= cus || !okM) return kLarge;
+        if (tiles * 2 >= cus || !okM) return okR ? kRing : kLarge;
     }
     if (okM) return kMedium;
     if (okS64) return kSkinny64;
@@ -148,6 +153,7 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t lda
     switch (choose_kernel(M, N, K, A, lda, B, ldb, C, ldc, cus)) {
     case kLarge: err = launch_tile_large(args, cus, stream); break;
     case kMedium: err = launch_tile_medium(args, cus, stream); break;
+    case kRing: err = launch_tile_ring(args, cus, stream); break;
     case kSkinny64: err = launch_skinny_m64(args, cus, stream); break;
     case kSkinny32: err = launch_skinny_m32(args, cus, stream); break;
     default: err = launch_generic(args, cus, stream); break;

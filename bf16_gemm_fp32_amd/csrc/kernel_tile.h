@@ -48,6 +48,7 @@
 #pragma once
 
 #include "device_common.h"
+#include "epilogue_tile.h"
 #include "tile_schedule.h"
 
 namespace gb {
@@ -88,7 +89,7 @@ struct TileConfig {
     static_assert(kLdsBytes <= 160 * 1024, "gfx950 has 160 KiB of LDS per compute unit");
     static_assert(kWaves * kEpiWaveBytes <= kLdsBytes, "epilogue staging reuses the ring");
     static_assert(KSTEPS % 2 == 0, "fragment double-buffering alternates per k-step");
-    static_assert((FM * FN) % kHalf == 0 && FM * FN >= FM + FN, "MFMA count paces the loads");
+    static_assert(FM * FN >= FM + FN && FM * FN >= kHalf, "MFMA count paces the reads and loads");
 };
 
 template <int BK>
@@ -168,34 +169,59 @@ struct TileKernel {
             for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = mfma_32x32x16(a[i], b[j], acc[i][j]);
     }
 
-    // One k-step: FM groups of FN MFMAs on (a, b).  Before group p go out
-    // (if kRead) the reads of A fragment p and B fragment p of k-step rkk of
-    // ring buffer rbuf into (ra, rb), and (if kLoad) DMA loads number
-    // LO + p*kPer .. of slice lkt into ring buffer lbuf.  Hard scheduling
-    // fences between groups keep this order: each LDS read has a whole k-step
-    // to land, and the loads trickle out at one per FN MFMAs, a rate the
-    // memory pipeline absorbs without stalling the wave.
+    // One k-step: the FM x FN MFMAs on (a, b), issued one at a time, with the
+    // other work of the k-step placed in the 32-cycle shadows between them:
+    // after MFMA number s goes out (if kRead) fragment read s of k-step rkk of
+    // ring buffer rbuf (A0, B0, A1, B1, ... into ra, rb: all reads in the
+    // first FM + FN shadows, so they have landed long before the k-step
+    // ends), and (if kLoad) the DMA loads LO .. LO + kHalf - 1 of slice lkt
+    // into ring buffer lbuf, spread evenly over the remaining shadows.  A wave
+    // has one MFMA in flight at a time, so an MFMA shadow that holds more
+    // issue work than the MFMA's own 32 cycles leaves the matrix core idle;
+    // one read or one load per shadow stays under that.  Hard scheduling
+    // fences keep this order.
     template <bool kRead, bool kLoad, int LO>
     __device__ __forceinline__ static void kstep(char *smem, const bf16x8 (&a)[Cfg::FM], const bf16x8 (&b)[Cfg::FN],
                                                  f32x16 (&acc)[Cfg::FM][Cfg::FN], int rbuf, int rkk,
                                                  bf16x8 (&ra)[Cfg::FM], bf16x8 (&rb)[Cfg::FN], int lbuf, int lkt,
                                                  const Lane &L, __amdgpu_buffer_rsrc_t rA,
                                                  __amdgpu_buffer_rsrc_t rB) {
-        static_assert(Cfg::FM >= Cfg::FN, "one A and at most one B read per group");
-        static_assert(Cfg::kHalf % Cfg::FM == 0, "half a slice's loads split over the groups");
-        constexpr int kPer = Cfg::kHalf / Cfg::FM;
+        constexpr int kMf = Cfg::FM * Cfg::FN;
+        constexpr int kReads = Cfg::FM + Cfg::FN;
+        constexpr int kLoadsHere = Cfg::kHalf;
+        static_assert(kReads <= kMf, "one fragment read per MFMA shadow");
+        // first shadow of load l: after the reads if they leave room, else shared with them
+        constexpr int kFree = kMf - kReads;
         const char *sA = smem + rbuf * Cfg::kStageBytes;
         const char *sB = sA + Cfg::kABytes;
 #pragma unroll
-        for (int p = 0; p < Cfg::FM; ++p) {
-            if constexpr (kRead) {
-                ra[p] = *(const GB_LDS bf16x8 *)(sA + L.aRow + p * 32 * Cfg::kRowBytes + L.chunk_off[rkk]);
-                if (p < Cfg::FN)
-                    rb[p] = *(const GB_LDS bf16x8 *)(sB + L.bRow + p * 32 * Cfg::kRowBytes + L.chunk_off[rkk]);
+        for (int s = 0; s < kMf; ++s) {
+            const int p = s / Cfg::FN, j = s % Cfg::FN;
+            acc[p][j] = mfma_32x32x16(a[p], b[j], acc[p][j]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (kRead && s < kReads) {
+                // reads alternate A, B while both remain, then the rest of A
+                const int r = s;
+                const int nb = Cfg::FN;
+                if (r < 2 * nb) {
+                    if ((r & 1) == 0)
+                        ra[r >> 1] = *(const GB_LDS bf16x8 *)(sA + L.aRow + (r >> 1) * 32 * Cfg::kRowBytes +
+                                                             L.chunk_off[rkk]);
+                    else
+                        rb[r >> 1] = *(const GB_LDS bf16x8 *)(sB + L.bRow + (r >> 1) * 32 * Cfg::kRowBytes +
+                                                             L.chunk_off[rkk]);
+                } else {
+                    const int ia = r - nb;
+                    ra[ia] = *(const GB_LDS bf16x8 *)(sA + L.aRow + ia * 32 * Cfg::kRowBytes + L.chunk_off[rkk]);
+                }
             }
-            if constexpr (kLoad) issue_range<LO>(smem, lbuf, lkt, L, rA, rB, p * kPer, kPer);
+            if (kLoad) {
 #pragma unroll
-            for (int j = 0; j < Cfg::FN; ++j) acc[p][j] = mfma_32x32x16(a[p], b[j], acc[p][j]);
+                for (int l = 0; l < kLoadsHere; ++l) {
+                    const int slot = (kFree >= kLoadsHere) ? kReads + l * kFree / kLoadsHere : l * kMf / kLoadsHere;
+                    if (slot == s) issue_range<LO>(smem, lbuf, lkt, L, rA, rB, l, 1);
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -273,68 +299,6 @@ struct TileKernel {
             }
         } else {
             kstep<false, false, 0>(smem, fa[kLast], fb[kLast], acc, 0, 0, fa[0], fb[0], 0, 0, L, rA, rB);
-        }
-    }
-
-    // Fused epilogue.  A 32x32 MFMA result gives lane l the column l % 32 and,
-    // in registers 4g..4g+3, the four consecutive rows 8g + 4(l/32) + 0..3.
-    // Each wave stages 32 columns at a time through its own LDS area as fp32
-    // (column-major, columns padded by 16 bytes against bank conflicts), then
-    // every lane takes 8 consecutive rows of one column: 16 lanes cover a
-    // column's WTM rows, so each store is 16 bytes and a column's bytes are
-    // written contiguously.  alpha, beta*C (read the same way), bias[n] and
-    // the activation are applied in fp32, then one RNE to bf16.
-    template <uint32_t kFlags>
-    __device__ __forceinline__ static void epilogue(char *smem, const GemmArgs &args, int64_t m0, int64_t n0, int wm,
-                                                    int wn, int lane, int wave,
-                                                    const f32x16 (&acc)[Cfg::FM][Cfg::FN]) {
-        char *stage = smem + wave * Cfg::kEpiWaveBytes;
-        constexpr int kColChunks = Cfg::WTM / 8;        // 8-row chunks per column
-        constexpr int kIters = 32 * kColChunks / 64;    // per lane per 32 columns
-        static_assert((32 * kColChunks) % 64 == 0, "column chunks split over the wave");
-        const int h = lane >> 5;
-#pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j) {
-            // accumulators -> LDS
-#pragma unroll
-            for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                    const int row = i * 32 + g * 8 + h * 4;
-                    *(GB_LDS f32x4 *)(stage + (lane & 31) * Cfg::kEpiColBytes + row * 4) = v;
-                }
-            // LDS -> 8 consecutive rows of one column per lane -> global
-#pragma unroll
-            for (int t = 0; t < kIters; ++t) {
-                const int idx = t * 64 + lane;
-                const int col = idx / kColChunks;
-                const int q = idx % kColChunks;
-                const f32x4 lo = *(const GB_LDS f32x4 *)(stage + col * Cfg::kEpiColBytes + q * 32);
-                const f32x4 hi = *(const GB_LDS f32x4 *)(stage + col * Cfg::kEpiColBytes + q * 32 + 16);
-                const int64_t n = n0 + wn * Cfg::WTN + j * 32 + col;
-                const int64_t m = m0 + wm * Cfg::WTM + q * 8;
-                uint16_t *p = args.C + n * args.ldc + m;
-                float bias_v = 0.f;
-                if constexpr ((kFlags & kEpiBias) != 0) bias_v = bf16_bits_to_f32(args.bias[n]);
-                float cin[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                if constexpr ((kFlags & kEpiBeta) != 0) {
-                    const u32x4 raw = *(const u32x4 *)p;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        cin[2 * e] = bf16_bits_to_f32(raw[e] & 0xFFFFu);
-                        cin[2 * e + 1] = bf16_bits_to_f32(raw[e] >> 16);
-                    }
-                }
-                const float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-                u32x4 out;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    out[e] = pack_bf16x2(epilogue_value<kFlags>(x[2 * e], cin[2 * e], bias_v, args.alpha, args.beta),
-                                         epilogue_value<kFlags>(x[2 * e + 1], cin[2 * e + 1], bias_v, args.alpha,
-                                                                args.beta));
-                __builtin_nontemporal_store(out, (u32x4 *)p);
-            }
         }
     }
 };
@@ -432,7 +396,7 @@ gemm_tile_kernel(const GemmArgs args, const TileSchedule sched) {
         // Every wave is done reading the ring (all loads landed at the last
         // wait): its memory now stages the epilogue.
         lds_barrier();
-        TK::template epilogue<kFlags>(smem, args, m0, n0, wm, wn, lane, Ln.wave, acc);
+        tile_epilogue<Cfg, kFlags>(smem, args, m0, n0, wm, wn, lane, Ln.wave, acc);
     }
 }
 

@@ -1,0 +1,13 @@
+// tile_ring.hip -- instances of the 256x256x64 unit-ring tile kernel.
+#include "configs.h"
+#include "kernel_ring.h"
+
+namespace gb {
+
+static_assert(RingConfig::BM == ShapeRing::BM && RingConfig::BN == ShapeRing::BN && RingConfig::BK == ShapeRing::BK);
+
+hipError_t launch_tile_ring(const GemmArgs &args, int cus, hipStream_t stream) {
+    return launch_ring(args, cus, stream);
+}
+
+}  // namespace gb

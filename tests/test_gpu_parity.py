@@ -112,16 +112,20 @@ def check_full(tag, M, N, K, lda=None, ldb=None, ldc=None, alpha=1.0, beta=0.0, 
     (256, 256, 256, "tile128x128x64_s4"),
     (512, 384, 192, "tile128x128x64_s4"),     # 3 K-slices (odd)
     (512, 384, 256, "tile128x128x64_s4"),     # 4 K-slices (even)
-    (4096, 2048, 320, "tile256x256x32_s5"),   # 128 tiles of 256, 5 slices
-    (4096, 2048, 64, "tile256x256x32_s5"),    # a single K-slice
+    (4096, 2048, 320, "ring256x256x64"),      # 128 tiles of 256, 5 slices of 64
+    (4096, 2048, 64, "ring256x256x64"),       # a single K-slice
+    (4096, 2048, 352, "tile256x256x32_s5"),   # K % 64 == 32: 11 slices of 32
+    (4096, 2048, 32, "tile256x256x32_s5"),    # a single K-slice of 32
 ])
 def test_tile_paths_full(M, N, K, kernel):
     check_full(f"tile {M}x{N}x{K}", M, N, K, seed=M + N + K, expect_kernel=kernel)
 
 
 def test_tile_path_epilogue_full():
-    check_full("tile256 epilogue", 4096, 2048, 192, alpha=1.0, beta=0.5, use_bias=True,
-               epilogue="gelu_tanh", seed=11, expect_kernel="tile256x256x32_s5")
+    check_full("ring256 epilogue", 4096, 2048, 192, alpha=1.0, beta=0.5, use_bias=True,
+               epilogue="gelu_tanh", seed=11, expect_kernel="ring256x256x64")
+    check_full("tile256 epilogue", 4096, 2048, 160, alpha=1.0, beta=0.5, use_bias=True,
+               epilogue="gelu_tanh", seed=16, expect_kernel="tile256x256x32_s5")
     check_full("tile128 epilogue", 512, 512, 128, alpha=-0.75, beta=-1.5, use_bias=True,
                epilogue="none", seed=12, expect_kernel="tile128x128x64_s4")
     check_full("tile128 gelu only", 384, 256, 320, alpha=2.0, epilogue="gelu_tanh", seed=13,
@@ -131,22 +135,24 @@ def test_tile_path_epilogue_full():
 def test_tile_path_padded_leading_dims():
     check_full("tile128 padded ld", 512, 256, 256, lda=264, ldb=272, ldc=520, beta=0.25, use_bias=True,
                seed=14, expect_kernel="tile128x128x64_s4")
-    check_full("tile256 padded ld", 4096, 2048, 128, lda=136, ldb=192, ldc=4104, seed=15,
+    check_full("ring256 padded ld", 4096, 2048, 128, lda=136, ldb=192, ldc=4104, seed=15,
+               expect_kernel="ring256x256x64")
+    check_full("tile256 padded ld", 4096, 2048, 96, lda=104, ldb=136, ldc=4112, seed=17,
                expect_kernel="tile256x256x32_s5")
 
 
 # Every tile kernel forced onto shapes whose K-slice count walks through the
 # pipeline's prologue and tail cases (1 .. 10 slices, fewer and more slices
 # than LDS stages, odd and even counts).
-FORCEABLE = ["tile256x256x32_s5", "tile128x128x64_s4", "generic64x64x32"]
+FORCEABLE = {"tile256x256x32_s5": 32, "tile128x128x64_s4": 64, "ring256x256x64": 64, "generic64x64x32": 1}
 
 
-@pytest.mark.parametrize("kernel", FORCEABLE)
-@pytest.mark.parametrize("K", [32, 64, 96, 128, 160, 192, 320])
+@pytest.mark.parametrize("kernel", list(FORCEABLE))
+@pytest.mark.parametrize("K", [32, 64, 96, 128, 160, 192, 256, 320, 448, 640])
 def test_forced_kernels_all_slice_counts(kernel, K, monkeypatch):
     M, N = 1024, 512
-    bk = 64 if ("x64_" in kernel or kernel.startswith("generic")) else 32
-    if kernel.startswith("tile") and K % bk:
+    bk = FORCEABLE[kernel]
+    if K % bk:
         pytest.skip(f"{kernel} needs K % {bk} == 0")
     monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", kernel)
     check_full(f"forced {kernel} K={K}", M, N, K, beta=0.5 if K % 64 else 0.0, use_bias=K == 96,
@@ -154,9 +160,10 @@ def test_forced_kernels_all_slice_counts(kernel, K, monkeypatch):
 
 
 # The tile kernels are compiled once per epilogue combination (beta, bias,
-# GELU): every combination on both tile configurations.
+# GELU): every combination on every tile configuration.
 @pytest.mark.parametrize("kernel,M,N,K", [("tile256x256x32_s5", 2048, 1024, 160),
-                                          ("tile128x128x64_s4", 512, 384, 192)])
+                                          ("tile128x128x64_s4", 512, 384, 192),
+                                          ("ring256x256x64", 2048, 1024, 192)])
 @pytest.mark.parametrize("beta,use_bias,epi", [(b, u, e) for b in (0.0, -0.75) for u in (False, True)
                                                for e in ("none", "gelu_tanh")])
 def test_tile_epilogue_combinations(kernel, M, N, K, beta, use_bias, epi, monkeypatch):
