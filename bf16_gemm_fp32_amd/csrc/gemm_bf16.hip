@@ -15,11 +15,11 @@
 
 namespace gb {
 
-enum KernelKind { kNone = 0, kLarge, kMedium, kSkinny64, kSkinny32, kGeneric, kRing, kNumKinds };
+enum KernelKind { kNone = 0, kLarge, kMedium, kSkinny64, kSkinny32, kGeneric, kRing32, kRing, kNumKinds };
 
 static const char *const kKindNames[kNumKinds] = {"none",            "tile256x256x32_s5", "tile128x128x64_s4",
                                                   "skinny64x32x256", "skinny32x32x256",   "generic64x64x32",
-                                                  "ring256x256x64"};
+                                                  "ring256x256x64_mfma32", "ring256x256x64"};
 
 static const char *kind_name(int k) { return (k >= 0 && k < kNumKinds) ? kKindNames[k] : "none"; }
 
@@ -93,6 +93,7 @@ static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t
         if (!std::strcmp(force, kKindNames[kGeneric])) return kGeneric;
         if (!std::strcmp(force, kKindNames[kLarge]) && okL) return kLarge;
         if (!std::strcmp(force, kKindNames[kMedium]) && okM) return kMedium;
+        if (!std::strcmp(force, kKindNames[kRing32]) && okR) return kRing32;
         if (!std::strcmp(force, kKindNames[kRing]) && okR) return kRing;
         if (!std::strcmp(force, kKindNames[kSkinny64]) && okS64) return kSkinny64;
         if (!std::strcmp(force, kKindNames[kSkinny32]) && okS32) return kSkinny32;
@@ -153,6 +154,7 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t lda
     switch (choose_kernel(M, N, K, A, lda, B, ldb, C, ldc, cus)) {
     case kLarge: err = launch_tile_large(args, cus, stream); break;
     case kMedium: err = launch_tile_medium(args, cus, stream); break;
+    case kRing32: err = launch_tile_ring_mfma32(args, cus, stream); break;
     case kRing: err = launch_tile_ring(args, cus, stream); break;
     case kSkinny64: err = launch_skinny_m64(args, cus, stream); break;
     case kSkinny32: err = launch_skinny_m32(args, cus, stream); break;

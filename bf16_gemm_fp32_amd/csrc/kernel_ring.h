@@ -1,49 +1,56 @@
 // kernel_ring.h -- persistent 256x256 MFMA tile kernel with K-slices of 64:
-// every operand row of a slice is one full 128-byte line, and LDS is a ring
-// of five 32 KiB units, one operand of one slice each.
+// every operand row of a slice is one full 128-byte line, LDS is a ring of
+// five 32 KiB single-operand units, and the products run on
+// v_mfma_f32_16x16x32_bf16.
 //
-// Why a ring of units.  Loading 64-byte row segments (K-slices of 32) makes
+// Why 128-byte rows.  Loading 64-byte row segments (K-slices of 32) makes
 // the L2 deliver whole 128-byte lines for half-line requests: twice the
 // L2->CU traffic, and on a power-limited chip that traffic costs clock.
-// With 128-byte rows one slice of the 256x256 tile is 64 KiB, so 160 KiB of
-// LDS holds two and a half slices.  Splitting a slice into its A unit and
-// its B unit and placing unit u (A of slice j is u = 2j, B is u = 2j+1) in
-// slot u % 5 lets the loads of the next units start as soon as any unit is
-// free:
-//   slice j reads  A(j) in slot 2j%5 and B(j) in slot (2j+1)%5;
-//   while it runs, B(j+1) (second half), A(j+2) and B(j+2) (first half)
-//   are loaded into the slots that A(j-1), B(j-1) and A(j) free.
-// One barrier per slice, placed before its last k-step: every wave has then
-// finished reading slice j (its last fragments are in registers), so A(j)'s
-// slot is free and the next slice's units are published.
+//
+// Why a ring of units.  One 64-wide slice of the 256x256 tile is 64 KiB, so
+// 160 KiB of LDS holds two and a half slices.  Each slice is split into its
+// A unit and its B unit (256 rows x 128 bytes each); A(j) of slice j lives in
+// ring slot (2j) % 5, B(j) in (2j+1) % 5, so loads start as soon as any unit
+// is free.  One barrier per slice, before its last k-step: every wave has
+// then read its last fragments of slice j into registers (A(j)'s and B(j)'s
+// slots are free) and slice j+1's units are published.  Between the barrier
+// of slice j and that of slice j+1 a wave issues B(j+2) (during k-step 1 of
+// slice j, into A(j)'s slot) and A(j+3) (during k-step 0 of slice j+1, into
+// B(j)'s slot); at the barrier of slice j+1 only A(j+3)'s loads may still be
+// in flight.
+//
+// Why 16x16x32 MFMAs.  Per flop the 16x16 form reads and writes half as many
+// accumulator bytes as 32x32x16; on this power-limited part a pure-MFMA loop
+// holds ~2.2 GHz with it against ~1.85 GHz with 32x32x16, and this kernel
+// runs ~7% faster than the same ring on 32x32x16 (kernel_ring_mfma32.h).
 //
 //   HBM/L2 --(buffer_load_dwordx4 ... lds, direct DMA)--> LDS unit slots
 //   LDS --(ds_read_b128, XOR-swizzled 128-byte rows)--> VGPR fragments
-//   fragments --(v_mfma_f32_32x32x16_bf16)--> 256 fp32 accumulators (AGPRs)
+//   fragments --(v_mfma_f32_16x16x32_bf16)--> 256 fp32 accumulators (AGPRs)
 //
-// Within a k-step the 16 MFMAs of a wave go out one at a time; the shadow
-// of each (32 cycles of matrix-core time) carries at most one other
-// instruction: first the 8 fragment reads of the next k-step, then 4 DMA
-// loads.  The matrix core idles only if a shadow's issue work outlasts it.
+// Per wave: a 128x128 tile = 8 x 8 blocks of 16x16, 64 accumulators of 4 fp32;
+// a slice is two k-steps of 32, each 64 MFMAs fed by 8 A and 8 B fragments
+// (ds_read_b128: row l % 16 of the block, k-chunk l / 16 of the k-step).
+// Within a k-step the MFMAs go out one at a time; the 16-cycle shadow after
+// MFMA s carries fragment read s for s < 16 (A0, B0, A1, B1, ...), and the
+// unit's 8 DMA loads sit in shadows 16, 22, ..., 58.
 //
-// Operand layout in LDS (both operands K-contiguous): row r of a unit holds
-// the slice's 64 k values as 8 chunks of 16 bytes, chunk c at position
-// c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1).  On gfx950 a ds_read_b128
-// is served in four 16-lane phases (lanes 0-31 split by the parity of lane
-// bits 2..4); a fragment read -- 32 consecutive rows, one chunk per
-// half-wave -- then touches 16 distinct 16-byte bank groups in every phase.
-// The DMA writes a wave's 64 lanes to 1 KiB of consecutive LDS bytes (8 rows
-// of 128 bytes), so the swizzle is applied on the global side: lane i
-// fetches the chunk that belongs at its LDS position.  This is the XOR
-// swizzle of the DeepGEMM article (section 3.2), redone for this row width
-// and lane-to-phase map.
+// LDS rows (8 chunks of 16 bytes) store chunk c at c ^ swz(r) with
+// swz(r) = (r >> 1) & 7.  On gfx950 a ds_read_b128 is served in four 16-lane
+// phases (lanes 0-31 split by the parity of lane bits 2..4, lanes 32-63 the
+// same way); with this swizzle a fragment read (16 rows x 4 chunks) touches
+// 16 distinct 16-byte bank groups in every phase.  The DMA writes a wave's
+// 64 lanes to 1 KiB of consecutive LDS bytes (8 rows of 128 bytes), so the
+// swizzle is applied on the global side: lane i fetches the chunk that
+// belongs at its LDS position.  This is the XOR swizzle of the DeepGEMM
+// article (section 3.2), redone for this row width and lane-to-phase map.
 #pragma once
 
 #include "device_common.h"
-#include "epilogue_tile.h"
 #include "tile_schedule.h"
 
 namespace gb {
+
 
 struct RingConfig {
     static constexpr int BM = 256, BN = 256, BK = 64;
@@ -51,8 +58,8 @@ struct RingConfig {
     static constexpr int kWaves = WAVES_M * WAVES_N;
     static constexpr int kThreads = 64 * kWaves;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;  // 128 x 128 wave tile
-    static constexpr int FM = WTM / 32, FN = WTN / 32;            // 32x32 MFMA blocks per wave
-    static constexpr int KSTEPS = BK / 16;                        // MFMA k-steps per slice
+    static constexpr int FM = WTM / 16, FN = WTN / 16;            // 16x16 MFMA blocks per wave
+    static constexpr int KSTEPS = BK / 32;                        // MFMA k-steps per slice
     static constexpr int kRowBytes = BK * 2;                      // 128: one cache line
     static constexpr int kUnitBytes = BM * kRowBytes;             // one operand of one slice
     static constexpr int kSlots = 5;
@@ -63,15 +70,19 @@ struct RingConfig {
     static constexpr int kEpiWaveBytes = 32 * kEpiColBytes;
 
     static_assert(BM == BN, "A and B units have the same size");
-    static_assert(KSTEPS == 4 && FM * FN == 16 && kUnitLoads == 8,
-                  "the slice schedule below is written for 4 k-steps of 16 MFMAs and 8 loads per unit");
+    static_assert(KSTEPS == 2 && FM == 8 && FN == 8 && kUnitLoads == 8,
+                  "the slice schedule below is written for 2 k-steps of 64 MFMAs and 8 loads per unit");
     static_assert(kLdsBytes <= 160 * 1024, "gfx950 has 160 KiB of LDS per compute unit");
     static_assert(kWaves * kEpiWaveBytes <= kLdsBytes, "epilogue staging reuses the ring");
 };
 
-__device__ __forceinline__ int ring_swizzle(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int ring_swizzle(int row) { return (row >> 1) & 7; }
 
 __device__ __forceinline__ int ring_slot(int s) { return s >= RingConfig::kSlots ? s - RingConfig::kSlots : s; }
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 
 struct RingKernel {
     using Cfg = RingConfig;
@@ -85,8 +96,7 @@ struct RingKernel {
     };
 
     // DMA load number l (0..7) of this wave for one operand unit: rows
-    // 8q .. 8q+7 of the tile, q = 8 * wave + l, K-slice kt, into the unit
-    // slot at LDS offset slot * kUnitBytes.
+    // 8q .. 8q+7 of the tile, q = 8 * wave + l, K-slice kt, into the slot.
     template <bool kIsA>
     __device__ __forceinline__ static void load(char *smem, int slot, int kt, int l, const Lane &L,
                                                 __amdgpu_buffer_rsrc_t rsrc) {
@@ -97,36 +107,34 @@ struct RingKernel {
                           (uint32_t)(q * Cfg::kRowsPerLoad) * ld + (uint32_t)kt * Cfg::kRowBytes);
     }
 
-    // Loads l0 .. l0+3 of one unit, or none.
     enum : int { kNoLoad = 0, kLoadA = 1, kLoadB = 2 };
 
-    // One k-step: MFMA s = 0..15 on block (s / FN, s % FN) with fragments
-    // (a, b); after MFMA s, if kRead and s < 8, fragment read s of k-step
-    // rkk from the units in slots (rsa, rsb) into (ra, rb), alternating
-    // A0, B0, A1, B1, ...; after MFMAs 8, 10, 12, 14, if kLoad, DMA loads
-    // l0 .. l0+3 of the unit (kLoad's operand) of slice lkt into slot lslot.
+    // One k-step: 64 MFMAs on (a, b), block (s / FN, s % FN) for MFMA s;
+    // after MFMA s < 16 (if kRead) fragment read s of k-step rks from slots
+    // (rsa, rsb) into (ra, rb), alternating A0, B0, A1, B1, ...; after MFMAs
+    // 16, 22, ..., 58 (if kLoad) the 8 DMA loads of the unit (kLoad's operand)
+    // of slice lkt into slot lslot.
     template <bool kRead, int kLoad>
     __device__ __forceinline__ static void kstep(char *smem, const bf16x8 (&a)[Cfg::FM], const bf16x8 (&b)[Cfg::FN],
-                                                 f32x16 (&acc)[Cfg::FM][Cfg::FN], int rsa, int rsb, int rkk,
+                                                 f32x4 (&acc)[Cfg::FM][Cfg::FN], int rsa, int rsb, int rks,
                                                  bf16x8 (&ra)[Cfg::FM], bf16x8 (&rb)[Cfg::FN], int lslot, int lkt,
-                                                 int l0, const Lane &L, __amdgpu_buffer_rsrc_t rA,
-                                                 __amdgpu_buffer_rsrc_t rB) {
+                                                 const Lane &L, __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rB) {
         const char *sA = smem + rsa * Cfg::kUnitBytes;
         const char *sB = smem + rsb * Cfg::kUnitBytes;
 #pragma unroll
         for (int s = 0; s < Cfg::FM * Cfg::FN; ++s) {
-            const int p = s / Cfg::FN, j = s % Cfg::FN;
-            acc[p][j] = mfma_32x32x16(a[p], b[j], acc[p][j]);
+            const int p = s / Cfg::FN, q = s % Cfg::FN;
+            acc[p][q] = mfma_16x16x32(a[p], b[q], acc[p][q]);
             __builtin_amdgcn_sched_barrier(0);
             if (kRead && s < 2 * Cfg::FM) {
                 const int f = s >> 1;
                 if ((s & 1) == 0)
-                    ra[f] = *(const GB_LDS bf16x8 *)(sA + L.aRow + f * 32 * Cfg::kRowBytes + L.chunk_off[rkk]);
+                    ra[f] = *(const GB_LDS bf16x8 *)(sA + L.aRow + f * 16 * Cfg::kRowBytes + L.chunk_off[rks]);
                 else
-                    rb[f] = *(const GB_LDS bf16x8 *)(sB + L.bRow + f * 32 * Cfg::kRowBytes + L.chunk_off[rkk]);
+                    rb[f] = *(const GB_LDS bf16x8 *)(sB + L.bRow + f * 16 * Cfg::kRowBytes + L.chunk_off[rks]);
             }
-            if (kLoad != kNoLoad && s >= 8 && (s & 1) == 0) {
-                const int l = l0 + ((s - 8) >> 1);
+            if (kLoad != kNoLoad && s >= 16 && (s - 16) % 6 == 0 && (s - 16) / 6 < Cfg::kUnitLoads) {
+                const int l = (s - 16) / 6;
                 if (kLoad == kLoadA)
                     load<true>(smem, lslot, lkt, l, L, rA);
                 else
@@ -138,43 +146,92 @@ struct RingKernel {
 
     // Slice j with A(j) in slot sa.  kMode: 0 = steady (j + 2 < nk),
     // 1 = next to last (j + 2 == nk), 2 = last.  On entry (fa[0], fb[0]) hold
-    // k-step 0's fragments of slice j; on exit (modes 0, 1) they hold those
-    // of slice j+1.
-    //   k-step 0: reads k-step 1;  loads B(j+1) 4..7          (modes 0, 1)
-    //   k-step 1: reads k-step 2;  loads A(j+2) 0..3          (mode 0)
-    //   k-step 2: reads k-step 3;  loads A(j+2) 4..7          (mode 0)
-    //   wait for A(j+1), B(j+1); barrier                      (modes 0, 1)
-    //   k-step 3: reads slice j+1's k-step 0;                 (modes 0, 1)
-    //             loads B(j+2) 0..3 into A(j)'s slot          (mode 0)
+    // k-step 0's fragments of slice j; on exit (modes 0, 1) those of j+1.
+    //   k-step 0: reads k-step 1;          loads A(j+2) into B(j-1)'s slot (mode 0)
+    //   wait for A(j+1), B(j+1); barrier   (modes 0, 1)
+    //   k-step 1: reads slice j+1's k-step 0 (modes 0, 1);
+    //             loads B(j+2) into A(j)'s slot (mode 0)
     template <int kMode>
     __device__ __forceinline__ static void slice(char *smem, int j, int sa, const Lane &L,
                                                  __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rB,
                                                  bf16x8 (&fa)[2][Cfg::FM], bf16x8 (&fb)[2][Cfg::FN],
-                                                 f32x16 (&acc)[Cfg::FM][Cfg::FN]) {
+                                                 f32x4 (&acc)[Cfg::FM][Cfg::FN]) {
         const int sb = ring_slot(sa + 1);   // B(j)
         const int san = ring_slot(sa + 2);  // A(j+1)
         const int sbn = ring_slot(sa + 3);  // B(j+1)
         const int sa2 = ring_slot(sa + 4);  // A(j+2)
-        constexpr int kL0 = kMode <= 1 ? kLoadB : kNoLoad;
-        constexpr int kL12 = kMode == 0 ? kLoadA : kNoLoad;
-        constexpr int kL3 = kMode == 0 ? kLoadB : kNoLoad;
-        kstep<true, kL0>(smem, fa[0], fb[0], acc, sa, sb, 1, fa[1], fb[1], sbn, j + 1, 4, L, rA, rB);
-        kstep<true, kL12>(smem, fa[1], fb[1], acc, sa, sb, 2, fa[0], fb[0], sa2, j + 2, 0, L, rA, rB);
-        kstep<true, kL12>(smem, fa[0], fb[0], acc, sa, sb, 3, fa[1], fb[1], sa2, j + 2, 4, L, rA, rB);
+        constexpr int kL0 = kMode == 0 ? kLoadA : kNoLoad;
+        constexpr int kL1 = kMode == 0 ? kLoadB : kNoLoad;
+        kstep<true, kL0>(smem, fa[0], fb[0], acc, sa, sb, 1, fa[1], fb[1], sa2, j + 2, L, rA, rB);
         if constexpr (kMode <= 1) {
-            // A(j+1) and B(j+1) landed; in mode 0 only A(j+2)'s 8 loads may remain
             if constexpr (kMode == 0)
-                wait_vmcnt<8>();
+                wait_vmcnt<Cfg::kUnitLoads>();
             else
                 wait_vmcnt<0>();
             lds_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            kstep<true, kL3>(smem, fa[1], fb[1], acc, san, sbn, 0, fa[0], fb[0], sa, j + 2, 0, L, rA, rB);
+            kstep<true, kL1>(smem, fa[1], fb[1], acc, san, sbn, 0, fa[0], fb[0], sa, j + 2, L, rA, rB);
         } else {
-            kstep<false, kNoLoad>(smem, fa[1], fb[1], acc, 0, 0, 0, fa[0], fb[0], 0, 0, 0, L, rA, rB);
+            kstep<false, kNoLoad>(smem, fa[1], fb[1], acc, 0, 0, 0, fa[0], fb[0], 0, 0, L, rA, rB);
         }
     }
 };
+
+// The fused epilogue for the 16x16 accumulator layout: lane l of block
+// (p, q) holds column 16q + l % 16, rows 16p + 4(l / 16) + 0..3.  Each wave
+// stages 32 columns at a time in LDS as fp32 (column-major, columns padded
+// by 16 bytes), then every lane takes 8 consecutive rows of one column and
+// writes them as one 16-byte store: alpha, beta*C, bias[n] and the
+// activation in fp32, one RNE to bf16.
+template <uint32_t kFlags>
+__device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, int64_t m0, int64_t n0, int wm,
+                                                int wn, int lane, int wave,
+                                                const f32x4 (&acc)[RingConfig::FM][RingConfig::FN]) {
+    using Cfg = RingConfig;
+    char *stage = smem + wave * Cfg::kEpiWaveBytes;
+    constexpr int kColChunks = Cfg::WTM / 8;      // 8-row chunks per column
+    constexpr int kIters = 32 * kColChunks / 64;  // per lane per 32 columns
+    const int c16 = lane & 15, r4 = (lane >> 4) * 4;
+#pragma unroll
+    for (int jj = 0; jj < Cfg::FN / 2; ++jj) {
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+            for (int p = 0; p < Cfg::FM; ++p)
+                *(GB_LDS f32x4 *)(stage + (qq * 16 + c16) * Cfg::kEpiColBytes + (p * 16 + r4) * 4) =
+                    acc[p][2 * jj + qq];
+#pragma unroll
+        for (int t = 0; t < kIters; ++t) {
+            const int idx = t * 64 + lane;
+            const int col = idx / kColChunks;
+            const int q = idx % kColChunks;
+            const f32x4 lo = *(const GB_LDS f32x4 *)(stage + col * Cfg::kEpiColBytes + q * 32);
+            const f32x4 hi = *(const GB_LDS f32x4 *)(stage + col * Cfg::kEpiColBytes + q * 32 + 16);
+            const int64_t n = n0 + wn * Cfg::WTN + jj * 32 + col;
+            const int64_t m = m0 + wm * Cfg::WTM + q * 8;
+            uint16_t *p = args.C + n * args.ldc + m;
+            float bias_v = 0.f;
+            if constexpr ((kFlags & kEpiBias) != 0) bias_v = bf16_bits_to_f32(args.bias[n]);
+            float cin[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            if constexpr ((kFlags & kEpiBeta) != 0) {
+                const u32x4 raw = *(const u32x4 *)p;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    cin[2 * e] = bf16_bits_to_f32(raw[e] & 0xFFFFu);
+                    cin[2 * e + 1] = bf16_bits_to_f32(raw[e] >> 16);
+                }
+            }
+            const float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            u32x4 out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                out[e] = pack_bf16x2(
+                    epilogue_value<kFlags>(x[2 * e], cin[2 * e], bias_v, args.alpha, args.beta),
+                    epilogue_value<kFlags>(x[2 * e + 1], cin[2 * e + 1], bias_v, args.alpha, args.beta));
+            __builtin_nontemporal_store(out, (u32x4 *)p);
+        }
+    }
+}
 
 // Requirements checked by the host before launch: M % 256 == 0,
 // N % 256 == 0, K % 64 == 0, K > 0, A/B/C 16-byte aligned, lda/ldb/ldc
@@ -194,8 +251,8 @@ gemm_ring_kernel(const GemmArgs args, const TileSchedule sched) {
     Ln.lda_bytes = (uint32_t)args.lda * 2u;
     Ln.ldb_bytes = (uint32_t)args.ldb * 2u;
     // Load side: lane i covers row 8q + i/8 of its row group q and LDS
-    // position i%8, which holds logical chunk (i%8) ^ swz(row); swz sees the
-    // row's low 4 bits, fixed by the lane and the parity of q.
+    // position i%8, which holds logical chunk (i%8) ^ swz(row); swz sees row
+    // bits 1..3, fixed by the lane and the parity of q.
     const int lrow = lane >> 3, lpos = lane & 7;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
@@ -203,13 +260,14 @@ gemm_ring_kernel(const GemmArgs args, const TileSchedule sched) {
         Ln.vA[p] = lrow * Ln.lda_bytes + (uint32_t)(c << 4);
         Ln.vB[p] = lrow * Ln.ldb_bytes + (uint32_t)(c << 4);
     }
-    // Read side: MFMA operand lane l takes row l % 32 of its 32-row block and
-    // 8 consecutive k from logical chunk 2*kk + l/32.
-    Ln.aRow = (uint32_t)(wm * Cfg::WTM + (lane & 31)) * Cfg::kRowBytes;
-    Ln.bRow = (uint32_t)(wn * Cfg::WTN + (lane & 31)) * Cfg::kRowBytes;
+    // Read side: operand lane l takes row l % 16 of its 16-row block and 8
+    // consecutive k from logical chunk 4*ks + l/16 (swz sees bits 1..3 of
+    // the row, the same for every 16-row block).
+    Ln.aRow = (uint32_t)(wm * Cfg::WTM + (lane & 15)) * Cfg::kRowBytes;
+    Ln.bRow = (uint32_t)(wn * Cfg::WTN + (lane & 15)) * Cfg::kRowBytes;
 #pragma unroll
-    for (int kk = 0; kk < Cfg::KSTEPS; ++kk)
-        Ln.chunk_off[kk] = (uint32_t)(((2 * kk + (lane >> 5)) ^ ring_swizzle(lane & 31)) << 4);
+    for (int ks = 0; ks < Cfg::KSTEPS; ++ks)
+        Ln.chunk_off[ks] = (uint32_t)(((4 * ks + (lane >> 4)) ^ ring_swizzle(lane & 15)) << 4);
 
     const int nk = (int)(args.K / Cfg::BK);
     const int num_tiles = sched.num_tiles();
@@ -224,16 +282,15 @@ gemm_ring_kernel(const GemmArgs args, const TileSchedule sched) {
         const __amdgpu_buffer_rsrc_t rB =
             make_rsrc(args.B + n0 * args.ldb, (uint32_t)(((Cfg::BN - 1) * args.ldb + args.K) * 2));
 
-        f32x16 acc[Cfg::FM][Cfg::FN];
+        f32x4 acc[Cfg::FM][Cfg::FN];
 #pragma unroll
         for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
-            for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = f32x16{};
+            for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         // The previous tile's epilogue is done with LDS.
         lds_barrier();
-        // Prologue: A(0) -> slot 0, B(0) -> 1, A(1) -> 2, B(1) loads 0..3 -> 3
-        // (slice 0 issues the rest of B(1)).
+        // Prologue: A(0) -> slot 0, B(0) -> 1, A(1) -> 2, B(1) -> 3.
 #pragma unroll
         for (int l = 0; l < Cfg::kUnitLoads; ++l) RK::load<true>(smem, 0, 0, l, Ln, rA);
 #pragma unroll
@@ -242,8 +299,8 @@ gemm_ring_kernel(const GemmArgs args, const TileSchedule sched) {
 #pragma unroll
             for (int l = 0; l < Cfg::kUnitLoads; ++l) RK::load<true>(smem, 2, 1, l, Ln, rA);
 #pragma unroll
-            for (int l = 0; l < Cfg::kUnitLoads / 2; ++l) RK::load<false>(smem, 3, 1, l, Ln, rB);
-            wait_vmcnt<Cfg::kUnitLoads + Cfg::kUnitLoads / 2>();
+            for (int l = 0; l < Cfg::kUnitLoads; ++l) RK::load<false>(smem, 3, 1, l, Ln, rB);
+            wait_vmcnt<2 * Cfg::kUnitLoads>();
         } else {
             wait_vmcnt<0>();
         }
@@ -254,10 +311,10 @@ gemm_ring_kernel(const GemmArgs args, const TileSchedule sched) {
             const char *sB = smem + Cfg::kUnitBytes;
 #pragma unroll
             for (int i = 0; i < Cfg::FM; ++i)
-                fa[0][i] = *(const GB_LDS bf16x8 *)(sA + Ln.aRow + i * 32 * Cfg::kRowBytes + Ln.chunk_off[0]);
+                fa[0][i] = *(const GB_LDS bf16x8 *)(sA + Ln.aRow + i * 16 * Cfg::kRowBytes + Ln.chunk_off[0]);
 #pragma unroll
             for (int i = 0; i < Cfg::FN; ++i)
-                fb[0][i] = *(const GB_LDS bf16x8 *)(sB + Ln.bRow + i * 32 * Cfg::kRowBytes + Ln.chunk_off[0]);
+                fb[0][i] = *(const GB_LDS bf16x8 *)(sB + Ln.bRow + i * 16 * Cfg::kRowBytes + Ln.chunk_off[0]);
         }
         // Drain every LGKM operation once per tile (a real s_waitcnt the
         // compiler sees), so the loop's LDS-read waits stay exact.
@@ -278,7 +335,7 @@ gemm_ring_kernel(const GemmArgs args, const TileSchedule sched) {
         // Every wave is done reading the ring (all loads landed at the last
         // wait): its memory now stages the epilogue.
         lds_barrier();
-        tile_epilogue<Cfg, kFlags>(smem, args, m0, n0, wm, wn, lane, Ln.wave, acc);
+        ring_epilogue<kFlags>(smem, args, m0, n0, wm, wn, lane, Ln.wave, acc);
     }
 }
 
