@@ -145,17 +145,18 @@ struct RingKernel {
     }
 
     // Slice j with A(j) in slot sa.  kMode: 0 = steady (j + 2 < nk),
-    // 1 = next to last (j + 2 == nk), 2 = last.  On entry (fa[0], fb[0]) hold
+    // 1 = next to last (j + 2 == nk), 2 = last (mid() runs before its last
+    // k-step).  On entry (fa[0], fb[0]) hold
     // k-step 0's fragments of slice j; on exit (modes 0, 1) those of j+1.
     //   k-step 0: reads k-step 1;          loads A(j+2) into B(j-1)'s slot (mode 0)
     //   wait for A(j+1), B(j+1); barrier   (modes 0, 1)
     //   k-step 1: reads slice j+1's k-step 0 (modes 0, 1);
     //             loads B(j+2) into A(j)'s slot (mode 0)
-    template <int kMode>
+    template <int kMode, class Mid>
     __device__ __forceinline__ static void slice(char *smem, int j, int sa, const Lane &L,
                                                  __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rB,
                                                  bf16x8 (&fa)[2][Cfg::FM], bf16x8 (&fb)[2][Cfg::FN],
-                                                 f32x4 (&acc)[Cfg::FM][Cfg::FN]) {
+                                                 f32x4 (&acc)[Cfg::FM][Cfg::FN], Mid &&mid) {
         const int sb = ring_slot(sa + 1);   // B(j)
         const int san = ring_slot(sa + 2);  // A(j+1)
         const int sbn = ring_slot(sa + 3);  // B(j+1)
@@ -172,6 +173,9 @@ struct RingKernel {
             __builtin_amdgcn_sched_barrier(0);
             kstep<true, kL1>(smem, fa[1], fb[1], acc, san, sbn, 0, fa[0], fb[0], sa, j + 2, L, rA, rB);
         } else {
+            // k-step 0's fragments are dead: their registers take mid()'s loads
+            mid();
+            __builtin_amdgcn_sched_barrier(0);
             kstep<false, kNoLoad>(smem, fa[1], fb[1], acc, 0, 0, 0, fa[0], fb[0], 0, 0, L, rA, rB);
         }
     }
@@ -179,21 +183,50 @@ struct RingKernel {
 
 // The fused epilogue for the 16x16 accumulator layout: lane l of block
 // (p, q) holds column 16q + l % 16, rows 16p + 4(l / 16) + 0..3.  Each wave
-// stages 32 columns at a time in LDS as fp32 (column-major, columns padded
-// by 16 bytes), then every lane takes 8 consecutive rows of one column and
-// writes them as one 16-byte store: alpha, beta*C, bias[n] and the
-// activation in fp32, one RNE to bf16.
+// works through its 128 columns in four groups of 32: it stages a group in
+// LDS as fp32 (column-major, columns padded by 16 bytes), then every lane
+// takes 8 consecutive rows of one column, 8 times, and writes each as one
+// 16-byte store: alpha, beta*C, bias[n] and the activation in fp32, one RNE
+// to bf16.  The C and bias values a group needs are loaded one group ahead
+// (the first group's before the tile's last K-slice), so their latency hides
+// behind the previous group's work instead of stalling every store.
+struct RingEpiInputs {
+    u32x4 c[8];    // C (beta != 0): 8 consecutive rows of one column per iteration
+    uint32_t b[8]; // bias bits (bias != NULL), one column per iteration
+};
+
+template <uint32_t kFlags>
+__device__ __forceinline__ void ring_epi_load(RingEpiInputs &in, const GemmArgs &args, int64_t m0, int64_t n0,
+                                              int wm, int wn, int lane, int jj) {
+    using Cfg = RingConfig;
+    constexpr int kColChunks = Cfg::WTM / 8;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int idx = t * 64 + lane;
+        const int col = idx / kColChunks;
+        const int q = idx % kColChunks;
+        const int64_t n = n0 + wn * Cfg::WTN + jj * 32 + col;
+        const int64_t m = m0 + wm * Cfg::WTM + q * 8;
+        if constexpr ((kFlags & kEpiBeta) != 0) in.c[t] = *(const u32x4 *)(args.C + n * args.ldc + m);
+        if constexpr ((kFlags & kEpiBias) != 0) in.b[t] = args.bias[n];
+    }
+}
+
 template <uint32_t kFlags>
 __device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, int64_t m0, int64_t n0, int wm,
-                                                int wn, int lane, int wave,
-                                                const f32x4 (&acc)[RingConfig::FM][RingConfig::FN]) {
+                                              int wn, int lane, int wave,
+                                              const f32x4 (&acc)[RingConfig::FM][RingConfig::FN],
+                                              RingEpiInputs &in) {
     using Cfg = RingConfig;
     char *stage = smem + wave * Cfg::kEpiWaveBytes;
     constexpr int kColChunks = Cfg::WTM / 8;      // 8-row chunks per column
     constexpr int kIters = 32 * kColChunks / 64;  // per lane per 32 columns
+    static_assert(kIters == 8, "RingEpiInputs holds one group's 8 iterations");
     const int c16 = lane & 15, r4 = (lane >> 4) * 4;
 #pragma unroll
     for (int jj = 0; jj < Cfg::FN / 2; ++jj) {
+        RingEpiInputs next;
+        if (jj + 1 < Cfg::FN / 2) ring_epi_load<kFlags>(next, args, m0, n0, wm, wn, lane, jj + 1);
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
@@ -209,16 +242,14 @@ __device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, 
             const f32x4 hi = *(const GB_LDS f32x4 *)(stage + col * Cfg::kEpiColBytes + q * 32 + 16);
             const int64_t n = n0 + wn * Cfg::WTN + jj * 32 + col;
             const int64_t m = m0 + wm * Cfg::WTM + q * 8;
-            uint16_t *p = args.C + n * args.ldc + m;
             float bias_v = 0.f;
-            if constexpr ((kFlags & kEpiBias) != 0) bias_v = bf16_bits_to_f32(args.bias[n]);
+            if constexpr ((kFlags & kEpiBias) != 0) bias_v = bf16_bits_to_f32(in.b[t]);
             float cin[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             if constexpr ((kFlags & kEpiBeta) != 0) {
-                const u32x4 raw = *(const u32x4 *)p;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    cin[2 * e] = bf16_bits_to_f32(raw[e] & 0xFFFFu);
-                    cin[2 * e + 1] = bf16_bits_to_f32(raw[e] >> 16);
+                    cin[2 * e] = bf16_bits_to_f32(in.c[t][e] & 0xFFFFu);
+                    cin[2 * e + 1] = bf16_bits_to_f32(in.c[t][e] >> 16);
                 }
             }
             const float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -228,8 +259,9 @@ __device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, 
                 out[e] = pack_bf16x2(
                     epilogue_value<kFlags>(x[2 * e], cin[2 * e], bias_v, args.alpha, args.beta),
                     epilogue_value<kFlags>(x[2 * e + 1], cin[2 * e + 1], bias_v, args.alpha, args.beta));
-            __builtin_nontemporal_store(out, (u32x4 *)p);
+            __builtin_nontemporal_store(out, (u32x4 *)(args.C + n * args.ldc + m));
         }
+        if (jj + 1 < Cfg::FN / 2) in = next;
     }
 }
 
@@ -322,20 +354,25 @@ gemm_ring_kernel(const GemmArgs args, const TileSchedule sched) {
 
         int j = 0, sa = 0;
         for (; j + 2 < nk; ++j) {
-            RK::slice<0>(smem, j, sa, Ln, rA, rB, fa, fb, acc);
+            RK::slice<0>(smem, j, sa, Ln, rA, rB, fa, fb, acc, [] {});
             sa = ring_slot(sa + 2);
         }
         if (j + 1 < nk) {
-            RK::slice<1>(smem, j, sa, Ln, rA, rB, fa, fb, acc);
+            RK::slice<1>(smem, j, sa, Ln, rA, rB, fa, fb, acc, [] {});
             ++j;
             sa = ring_slot(sa + 2);
         }
-        RK::slice<2>(smem, j, sa, Ln, rA, rB, fa, fb, acc);
+        // The epilogue's first C / bias values load during the last k-step.
+        RingEpiInputs epi_in;
+        RK::slice<2>(smem, j, sa, Ln, rA, rB, fa, fb, acc, [&] {
+            if constexpr ((kFlags & (kEpiBeta | kEpiBias)) != 0)
+                ring_epi_load<kFlags>(epi_in, args, m0, n0, wm, wn, lane, 0);
+        });
 
         // Every wave is done reading the ring (all loads landed at the last
         // wait): its memory now stages the epilogue.
         lds_barrier();
-        ring_epilogue<kFlags>(smem, args, m0, n0, wm, wn, lane, Ln.wave, acc);
+        ring_epilogue<kFlags>(smem, args, m0, n0, wm, wn, lane, Ln.wave, acc, epi_in);
     }
 }
 
