@@ -61,6 +61,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
                                              0x00020000);
 }
 
+// A buffer offset past every resource this library builds (their sizes and
+// offsets stay below 2^31, checked on the host): a load from it is out of
+// range and returns zeros -- also into LDS for the direct-to-LDS form.
+constexpr uint32_t kOobOffset = 0x80000000u;
+
 // 16-byte per lane direct load from a buffer into LDS.  Lane i of the wave
 // writes lds_base + 16*i; lds_base must be wave-uniform.
 __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, GB_LDS void *lds_base,

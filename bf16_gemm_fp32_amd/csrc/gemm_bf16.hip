@@ -15,11 +15,14 @@
 
 namespace gb {
 
-enum KernelKind { kNone = 0, kLarge, kMedium, kSkinny64, kSkinny32, kGeneric, kRing32, kRing, kNumKinds };
+enum KernelKind {
+    kNone = 0, kLarge, kMedium, kSkinny64, kSkinny32, kGeneric, kRing32, kRing, kRingMasked, kNumKinds
+};
 
 static const char *const kKindNames[kNumKinds] = {"none",            "tile256x256x32_s5", "tile128x128x64_s4",
                                                   "skinny64x32x256", "skinny32x32x256",   "generic64x64x32",
-                                                  "ring256x256x64_mfma32", "ring256x256x64"};
+                                                  "ring256x256x64_mfma32", "ring256x256x64",
+                                                  "ring256x256x64_masked"};
 
 static const char *kind_name(int k) { return (k >= 0 && k < kNumKinds) ? kKindNames[k] : "none"; }
 
@@ -67,6 +70,21 @@ static bool tile_path_ok(int64_t M, int64_t N, int64_t K, const void *A, int64_t
     return true;
 }
 
+// The masked ring kernel: any M, N >= 1; K and the leading dimensions
+// multiples of 8 (16-byte operand chunks and C columns), 16-byte aligned
+// pointers, 32-bit buffer offsets within a tile's rows.
+static bool ring_masked_ok(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+                           int64_t ldb, const void *C, int64_t ldc) {
+    if (M <= 0 || N <= 0 || K <= 0 || K % 8) return false;
+    if (lda % 8 || ldb % 8 || ldc % 8) return false;
+    if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return false;
+    const int64_t lim = (int64_t)1 << 31;
+    if ((ShapeRing::BM * lda + K) * 2 >= lim || (ShapeRing::BN * ldb + K) * 2 >= lim) return false;
+    if (K + ShapeRing::BK >= lim) return false;
+    const int64_t tiles = ((M + ShapeRing::BM - 1) / ShapeRing::BM) * ((N + ShapeRing::BN - 1) / ShapeRing::BN);
+    return tiles < lim;
+}
+
 static bool skinny_path_ok(int rows, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
                            int64_t ldb, const void *C, int64_t ldc) {
     if (M != rows || K <= 0 || N % ShapeSkinny::BN || K % ShapeSkinny::KS) return false;
@@ -87,6 +105,7 @@ static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t
     const bool okL = tile_path_ok<ShapeL>(M, N, K, A, lda, B, ldb, C, ldc);
     const bool okM = tile_path_ok<ShapeM>(M, N, K, A, lda, B, ldb, C, ldc);
     const bool okR = tile_path_ok<ShapeRing>(M, N, K, A, lda, B, ldb, C, ldc);
+    const bool okRM = ring_masked_ok(M, N, K, A, lda, B, ldb, C, ldc);
     const bool okS64 = skinny_path_ok(64, M, N, K, A, lda, B, ldb, C, ldc);
     const bool okS32 = skinny_path_ok(32, M, N, K, A, lda, B, ldb, C, ldc);
     if (const char *force = std::getenv("GEMM_BF16_FORCE_KERNEL")) {
@@ -95,14 +114,20 @@ static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t
         if (!std::strcmp(force, kKindNames[kMedium]) && okM) return kMedium;
         if (!std::strcmp(force, kKindNames[kRing32]) && okR) return kRing32;
         if (!std::strcmp(force, kKindNames[kRing]) && okR) return kRing;
+        if (!std::strcmp(force, kKindNames[kRingMasked]) && okRM) return kRingMasked;
         if (!std::strcmp(force, kKindNames[kSkinny64]) && okS64) return kSkinny64;
         if (!std::strcmp(force, kKindNames[kSkinny32]) && okS32) return kSkinny32;
     }
     // 256x256 tiles when they give at least half the compute units a tile:
-    // K-slices of 64 (full-line operand rows) when K allows, else of 32.
-    if (okR || okL) {
+    // exact multiples take the unmasked ring kernel, shapes with tails the
+    // masked one.
+    if (okRM) {
+        const int64_t tiles = ((M + ShapeRing::BM - 1) / ShapeRing::BM) * ((N + ShapeRing::BN - 1) / ShapeRing::BN);
+        if (tiles * 2 >= cus || (!okM && okR)) return okR ? kRing : kRingMasked;
+    }
+    if (okL) {
         const int64_t tiles = (M / ShapeL::BM) * (N / ShapeL::BN);
-        if (tiles * 2 >= cus || !okM) return okR ? kRing : kLarge;
+        if (tiles * 2 >= cus || !okM) return kLarge;
     }
     if (okM) return kMedium;
     if (okS64) return kSkinny64;
@@ -156,6 +181,7 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t lda
     case kMedium: err = launch_tile_medium(args, cus, stream); break;
     case kRing32: err = launch_tile_ring_mfma32(args, cus, stream); break;
     case kRing: err = launch_tile_ring(args, cus, stream); break;
+    case kRingMasked: err = launch_tile_ring_masked(args, cus, stream); break;
     case kSkinny64: err = launch_skinny_m64(args, cus, stream); break;
     case kSkinny32: err = launch_skinny_m32(args, cus, stream); break;
     default: err = launch_generic(args, cus, stream); break;

@@ -84,6 +84,14 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(const bf16x8 &a, const bf16x8 &b,
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// kMasked: the shape has tails (M or N not a multiple of 256, or K not a
+// multiple of 64; K and the leading dimensions are multiples of 8).  Every
+// 16-byte operand chunk outside the matrix -- row or column past the end,
+// or k >= K -- is loaded from an out-of-range buffer offset, which the DMA
+// turns into zeros (the zero-fill of the DeepGEMM article, sections 4.2-4.3),
+// and the epilogue masks its loads and stores.  Unmasked instances carry no
+// such code.
+template <bool kMasked>
 struct RingKernel {
     using Cfg = RingConfig;
 
@@ -93,6 +101,10 @@ struct RingKernel {
         uint32_t chunk_off[Cfg::KSTEPS];
         uint32_t lda_bytes, ldb_bytes;
         int wave;
+        // masking only: this lane's row within a load's 8 rows, its logical
+        // chunk by parity of the row group, and the tile's valid extents
+        int lrow, lchunk[2];
+        int rowsA, rowsB, kmax;
     };
 
     // DMA load number l (0..7) of this wave for one operand unit: rows
@@ -102,8 +114,13 @@ struct RingKernel {
                                                 __amdgpu_buffer_rsrc_t rsrc) {
         const int q = L.wave * Cfg::kUnitLoads + l;
         const uint32_t ld = kIsA ? L.lda_bytes : L.ldb_bytes;
-        buffer_load_lds16(rsrc, (GB_LDS void *)(smem + slot * Cfg::kUnitBytes + q * 1024),
-                          kIsA ? L.vA[q & 1] : L.vB[q & 1],
+        uint32_t voff = kIsA ? L.vA[q & 1] : L.vB[q & 1];
+        if constexpr (kMasked) {
+            const int row = q * Cfg::kRowsPerLoad + L.lrow;
+            const int k = kt * Cfg::BK + L.lchunk[q & 1] * 8;
+            if (!(row < (kIsA ? L.rowsA : L.rowsB) && k < L.kmax)) voff = kOobOffset;
+        }
+        buffer_load_lds16(rsrc, (GB_LDS void *)(smem + slot * Cfg::kUnitBytes + q * 1024), voff,
                           (uint32_t)(q * Cfg::kRowsPerLoad) * ld + (uint32_t)kt * Cfg::kRowBytes);
     }
 
@@ -195,7 +212,10 @@ struct RingEpiInputs {
     uint32_t b[8]; // bias bits (bias != NULL), one column per iteration
 };
 
-template <uint32_t kFlags>
+// Rows m .. m+7 of column n of C: full when m + 8 <= M; with masking, a
+// chunk that straddles M is read and written element by element, and
+// chunks past M or columns past N are skipped.
+template <uint32_t kFlags, bool kMasked>
 __device__ __forceinline__ void ring_epi_load(RingEpiInputs &in, const GemmArgs &args, int64_t m0, int64_t n0,
                                               int wm, int wn, int lane, int jj) {
     using Cfg = RingConfig;
@@ -207,12 +227,29 @@ __device__ __forceinline__ void ring_epi_load(RingEpiInputs &in, const GemmArgs 
         const int q = idx % kColChunks;
         const int64_t n = n0 + wn * Cfg::WTN + jj * 32 + col;
         const int64_t m = m0 + wm * Cfg::WTM + q * 8;
-        if constexpr ((kFlags & kEpiBeta) != 0) in.c[t] = *(const u32x4 *)(args.C + n * args.ldc + m);
-        if constexpr ((kFlags & kEpiBias) != 0) in.b[t] = args.bias[n];
+        if constexpr (kMasked) {
+            in.c[t] = u32x4{0u, 0u, 0u, 0u};
+            in.b[t] = 0u;
+            if (n >= args.N) continue;
+            if constexpr ((kFlags & kEpiBias) != 0) in.b[t] = args.bias[n];
+            if constexpr ((kFlags & kEpiBeta) != 0) {
+                const uint16_t *p = args.C + n * args.ldc + m;
+                if (m + 8 <= args.M) {
+                    in.c[t] = *(const u32x4 *)p;
+                } else if (m < args.M) {
+                    uint32_t w[4] = {0u, 0u, 0u, 0u};
+                    for (int e = 0; e < 8 && m + e < args.M; ++e) w[e >> 1] |= (uint32_t)p[e] << ((e & 1) * 16);
+                    in.c[t] = u32x4{w[0], w[1], w[2], w[3]};
+                }
+            }
+        } else {
+            if constexpr ((kFlags & kEpiBeta) != 0) in.c[t] = *(const u32x4 *)(args.C + n * args.ldc + m);
+            if constexpr ((kFlags & kEpiBias) != 0) in.b[t] = args.bias[n];
+        }
     }
 }
 
-template <uint32_t kFlags>
+template <uint32_t kFlags, bool kMasked>
 __device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, int64_t m0, int64_t n0, int wm,
                                               int wn, int lane, int wave,
                                               const f32x4 (&acc)[RingConfig::FM][RingConfig::FN],
@@ -226,7 +263,7 @@ __device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, 
 #pragma unroll
     for (int jj = 0; jj < Cfg::FN / 2; ++jj) {
         RingEpiInputs next;
-        if (jj + 1 < Cfg::FN / 2) ring_epi_load<kFlags>(next, args, m0, n0, wm, wn, lane, jj + 1);
+        if (jj + 1 < Cfg::FN / 2) ring_epi_load<kFlags, kMasked>(next, args, m0, n0, wm, wn, lane, jj + 1);
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
@@ -259,7 +296,19 @@ __device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, 
                 out[e] = pack_bf16x2(
                     epilogue_value<kFlags>(x[2 * e], cin[2 * e], bias_v, args.alpha, args.beta),
                     epilogue_value<kFlags>(x[2 * e + 1], cin[2 * e + 1], bias_v, args.alpha, args.beta));
-            __builtin_nontemporal_store(out, (u32x4 *)(args.C + n * args.ldc + m));
+            uint16_t *p = args.C + n * args.ldc + m;
+            if constexpr (kMasked) {
+                if (n < args.N) {
+                    if (m + 8 <= args.M) {
+                        __builtin_nontemporal_store(out, (u32x4 *)p);
+                    } else {
+                        for (int e = 0; e < 8 && m + e < args.M; ++e)
+                            p[e] = (uint16_t)(out[e >> 1] >> ((e & 1) * 16));
+                    }
+                }
+            } else {
+                __builtin_nontemporal_store(out, (u32x4 *)p);
+            }
         }
         if (jj + 1 < Cfg::FN / 2) in = next;
     }
@@ -268,15 +317,15 @@ __device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, 
 // Requirements checked by the host before launch: M % 256 == 0,
 // N % 256 == 0, K % 64 == 0, K > 0, A/B/C 16-byte aligned, lda/ldb/ldc
 // multiples of 8, and 256*lda*2 + 2K, 256*ldb*2 + 2K below 2^31.
-template <uint32_t kFlags>
+template <uint32_t kFlags, bool kMasked>
 __global__ void __launch_bounds__(RingConfig::kThreads)
 gemm_ring_kernel(const GemmArgs args, const TileSchedule sched) {
     using Cfg = RingConfig;
-    using RK = RingKernel;
+    using RK = RingKernel<kMasked>;
     __shared__ __attribute__((aligned(1024))) char smem[Cfg::kLdsBytes];
 
     const int lane = threadIdx.x & 63;
-    RK::Lane Ln;
+    typename RK::Lane Ln;
     Ln.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = Ln.wave / Cfg::WAVES_N;
     const int wn = Ln.wave % Cfg::WAVES_N;
@@ -291,7 +340,10 @@ gemm_ring_kernel(const GemmArgs args, const TileSchedule sched) {
         const int c = lpos ^ ring_swizzle(p * Cfg::kRowsPerLoad + lrow);
         Ln.vA[p] = lrow * Ln.lda_bytes + (uint32_t)(c << 4);
         Ln.vB[p] = lrow * Ln.ldb_bytes + (uint32_t)(c << 4);
+        Ln.lchunk[p] = c;
     }
+    Ln.lrow = lrow;
+    Ln.kmax = (int)args.K;
     // Read side: operand lane l takes row l % 16 of its 16-row block and 8
     // consecutive k from logical chunk 4*ks + l/16 (swz sees bits 1..3 of
     // the row, the same for every 16-row block).
@@ -301,7 +353,7 @@ gemm_ring_kernel(const GemmArgs args, const TileSchedule sched) {
     for (int ks = 0; ks < Cfg::KSTEPS; ++ks)
         Ln.chunk_off[ks] = (uint32_t)(((4 * ks + (lane >> 4)) ^ ring_swizzle(lane & 15)) << 4);
 
-    const int nk = (int)(args.K / Cfg::BK);
+    const int nk = (int)((args.K + Cfg::BK - 1) / Cfg::BK);
     const int num_tiles = sched.num_tiles();
 
     for (int t = sched.slot(blockIdx.x); t < num_tiles; t += sched.grid) {
@@ -309,6 +361,10 @@ gemm_ring_kernel(const GemmArgs args, const TileSchedule sched) {
         sched.tile(t, tm, tn);
         const int64_t m0 = (int64_t)tm * Cfg::BM;
         const int64_t n0 = (int64_t)tn * Cfg::BN;
+        if constexpr (kMasked) {
+            Ln.rowsA = (int)(args.M - m0 < Cfg::BM ? args.M - m0 : Cfg::BM);
+            Ln.rowsB = (int)(args.N - n0 < Cfg::BN ? args.N - n0 : Cfg::BN);
+        }
         const __amdgpu_buffer_rsrc_t rA =
             make_rsrc(args.A + m0 * args.lda, (uint32_t)(((Cfg::BM - 1) * args.lda + args.K) * 2));
         const __amdgpu_buffer_rsrc_t rB =
@@ -324,14 +380,14 @@ gemm_ring_kernel(const GemmArgs args, const TileSchedule sched) {
         lds_barrier();
         // Prologue: A(0) -> slot 0, B(0) -> 1, A(1) -> 2, B(1) -> 3.
 #pragma unroll
-        for (int l = 0; l < Cfg::kUnitLoads; ++l) RK::load<true>(smem, 0, 0, l, Ln, rA);
+        for (int l = 0; l < Cfg::kUnitLoads; ++l) RK::template load<true>(smem, 0, 0, l, Ln, rA);
 #pragma unroll
-        for (int l = 0; l < Cfg::kUnitLoads; ++l) RK::load<false>(smem, 1, 0, l, Ln, rB);
+        for (int l = 0; l < Cfg::kUnitLoads; ++l) RK::template load<false>(smem, 1, 0, l, Ln, rB);
         if (nk >= 2) {
 #pragma unroll
-            for (int l = 0; l < Cfg::kUnitLoads; ++l) RK::load<true>(smem, 2, 1, l, Ln, rA);
+            for (int l = 0; l < Cfg::kUnitLoads; ++l) RK::template load<true>(smem, 2, 1, l, Ln, rA);
 #pragma unroll
-            for (int l = 0; l < Cfg::kUnitLoads; ++l) RK::load<false>(smem, 3, 1, l, Ln, rB);
+            for (int l = 0; l < Cfg::kUnitLoads; ++l) RK::template load<false>(smem, 3, 1, l, Ln, rB);
             wait_vmcnt<2 * Cfg::kUnitLoads>();
         } else {
             wait_vmcnt<0>();
@@ -354,51 +410,57 @@ gemm_ring_kernel(const GemmArgs args, const TileSchedule sched) {
 
         int j = 0, sa = 0;
         for (; j + 2 < nk; ++j) {
-            RK::slice<0>(smem, j, sa, Ln, rA, rB, fa, fb, acc, [] {});
+            RK::template slice<0>(smem, j, sa, Ln, rA, rB, fa, fb, acc, [] {});
             sa = ring_slot(sa + 2);
         }
         if (j + 1 < nk) {
-            RK::slice<1>(smem, j, sa, Ln, rA, rB, fa, fb, acc, [] {});
+            RK::template slice<1>(smem, j, sa, Ln, rA, rB, fa, fb, acc, [] {});
             ++j;
             sa = ring_slot(sa + 2);
         }
         // The epilogue's first C / bias values load during the last k-step.
         RingEpiInputs epi_in;
-        RK::slice<2>(smem, j, sa, Ln, rA, rB, fa, fb, acc, [&] {
+        RK::template slice<2>(smem, j, sa, Ln, rA, rB, fa, fb, acc, [&] {
             if constexpr ((kFlags & (kEpiBeta | kEpiBias)) != 0)
-                ring_epi_load<kFlags>(epi_in, args, m0, n0, wm, wn, lane, 0);
+                ring_epi_load<kFlags, kMasked>(epi_in, args, m0, n0, wm, wn, lane, 0);
         });
 
         // Every wave is done reading the ring (all loads landed at the last
         // wait): its memory now stages the epilogue.
         lds_barrier();
-        ring_epilogue<kFlags>(smem, args, m0, n0, wm, wn, lane, Ln.wave, acc, epi_in);
+        ring_epilogue<kFlags, kMasked>(smem, args, m0, n0, wm, wn, lane, Ln.wave, acc, epi_in);
     }
 }
 
 // Launch with the epilogue flags of args baked in; grid = min(tiles, CUs),
-// one persistent workgroup per compute unit.
-inline hipError_t launch_ring(const GemmArgs &args, int cus, hipStream_t stream) {
+// one persistent workgroup per compute unit.  The masked instances run when
+// the shape has tails.
+template <bool kMasked>
+hipError_t launch_ring_t(const GemmArgs &args, const TileSchedule &s, hipStream_t stream) {
+    const dim3 grid(s.grid), block(RingConfig::kThreads);
+    switch (args.flags & 7u) {
+    case 0: hipLaunchKernelGGL((gemm_ring_kernel<0, kMasked>), grid, block, 0, stream, args, s); break;
+    case 1: hipLaunchKernelGGL((gemm_ring_kernel<1, kMasked>), grid, block, 0, stream, args, s); break;
+    case 2: hipLaunchKernelGGL((gemm_ring_kernel<2, kMasked>), grid, block, 0, stream, args, s); break;
+    case 3: hipLaunchKernelGGL((gemm_ring_kernel<3, kMasked>), grid, block, 0, stream, args, s); break;
+    case 4: hipLaunchKernelGGL((gemm_ring_kernel<4, kMasked>), grid, block, 0, stream, args, s); break;
+    case 5: hipLaunchKernelGGL((gemm_ring_kernel<5, kMasked>), grid, block, 0, stream, args, s); break;
+    case 6: hipLaunchKernelGGL((gemm_ring_kernel<6, kMasked>), grid, block, 0, stream, args, s); break;
+    default: hipLaunchKernelGGL((gemm_ring_kernel<7, kMasked>), grid, block, 0, stream, args, s); break;
+    }
+    return hipGetLastError();
+}
+
+inline TileSchedule ring_schedule(const GemmArgs &args, int cus) {
     TileSchedule s{};
-    s.tiles_m = (int)(args.M / RingConfig::BM);
-    s.tiles_n = (int)(args.N / RingConfig::BN);
+    s.tiles_m = (int)((args.M + RingConfig::BM - 1) / RingConfig::BM);
+    s.tiles_n = (int)((args.N + RingConfig::BN - 1) / RingConfig::BN);
     s.group_m = 4;
     s.order = kOrderGrouped;
     s.hilbert_log2 = 0;
     const int tiles = s.num_tiles();
     s.grid = tiles < cus ? tiles : cus;
-    const dim3 grid(s.grid), block(RingConfig::kThreads);
-    switch (args.flags & 7u) {
-    case 0: hipLaunchKernelGGL((gemm_ring_kernel<0>), grid, block, 0, stream, args, s); break;
-    case 1: hipLaunchKernelGGL((gemm_ring_kernel<1>), grid, block, 0, stream, args, s); break;
-    case 2: hipLaunchKernelGGL((gemm_ring_kernel<2>), grid, block, 0, stream, args, s); break;
-    case 3: hipLaunchKernelGGL((gemm_ring_kernel<3>), grid, block, 0, stream, args, s); break;
-    case 4: hipLaunchKernelGGL((gemm_ring_kernel<4>), grid, block, 0, stream, args, s); break;
-    case 5: hipLaunchKernelGGL((gemm_ring_kernel<5>), grid, block, 0, stream, args, s); break;
-    case 6: hipLaunchKernelGGL((gemm_ring_kernel<6>), grid, block, 0, stream, args, s); break;
-    default: hipLaunchKernelGGL((gemm_ring_kernel<7>), grid, block, 0, stream, args, s); break;
-    }
-    return hipGetLastError();
+    return s;
 }
 
 }  // namespace gb

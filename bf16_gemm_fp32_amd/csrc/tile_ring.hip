@@ -1,5 +1,5 @@
-// tile_ring16.hip -- instances of the 256x256x64 unit-ring tile kernel on
-// 16x16x32 MFMAs.
+// tile_ring.hip -- instances of the 256x256x64 unit-ring tile kernel for
+// shapes without tails (M, N multiples of 256, K a multiple of 64).
 #include "configs.h"
 #include "kernel_ring.h"
 
@@ -9,7 +9,7 @@ static_assert(RingConfig::BM == ShapeRing::BM && RingConfig::BN == ShapeRing::BN
               RingConfig::BK == ShapeRing::BK);
 
 hipError_t launch_tile_ring(const GemmArgs &args, int cus, hipStream_t stream) {
-    return launch_ring(args, cus, stream);
+    return launch_ring_t<false>(args, ring_schedule(args, cus), stream);
 }
 
 }  // namespace gb

@@ -67,6 +67,10 @@ WORKLOADS = {
                  notes="C = GELU_tanh(1.0*A*B + 0.5*C0 + bias[n])"),
         Workload("skinny_64x8192x8192", 4, 64, 8192, 8192, bound="hbm",
                  notes="memory-bound: B (128 MiB) is streamed once"),
+        # beyond the five: a shape with tails in M, N and K (tiles of 256 and
+        # K-slices of 64 do not divide it), for the masked fast path
+        Workload("ragged_4000x4000x4000", 5, 4000, 4000, 4000,
+                 notes="tails in every dimension: 4000 = 15*256 + 160 = 62*64 + 32"),
     ]
 }
 

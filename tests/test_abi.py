@@ -84,8 +84,10 @@ def test_kernel_selection_names():
     name = gb.gemm_bf16_kernel_name
     assert name(4096, 4096, 4096, P, 4096, P, 4096, P, 4096) == "ring256x256x64"
     assert name(8192, 14336, 4096, P, 4096, P, 4096, P, 8192) == "ring256x256x64"
-    # K a multiple of 32 but not of 64: K-slices of 32
-    assert name(4096, 4096, 4064, P, 4064, P, 4064, P, 4096) == "tile256x256x32_s5"
+    # tails (K not a multiple of 64, M or N not of 256): the masked ring kernel
+    assert name(4096, 4096, 4064, P, 4064, P, 4064, P, 4096) == "ring256x256x64_masked"
+    assert name(4000, 4000, 4000, P, 4000, P, 4000, P, 4000) == "ring256x256x64_masked"
+    assert name(4000, 2000, 1000, P, 1000, P, 1000, P, 4000) == "ring256x256x64_masked"
     assert name(256, 256, 256, P, 256, P, 256, P, 256) == "tile128x128x64_s4"
     assert name(1000, 1000, 1000, P, 1000, P, 1000, P, 1000) == "generic64x64x32"
     assert name(64, 8192, 8192, P, 8192, P, 8192, P, 64) == "skinny64x32x256"

@@ -76,11 +76,17 @@ def run_gpu(M, N, K, A, lda, B, ldb, C_init, ldc, alpha, beta, bias, epilogue, o
 
 
 def check_full(tag, M, N, K, lda=None, ldb=None, ldc=None, alpha=1.0, beta=0.0, use_bias=False,
-               epilogue="none", offsets=(0, 0, 0), seed=0, expect_kernel=None):
+               epilogue="none", offsets=(0, 0, 0), seed=0, expect_kernel=None, poison_pad=False):
     lda = max(K, 1) if lda is None else lda
     ldb = max(K, 1) if ldb is None else ldb
     ldc = max(M, 1) if ldc is None else ldc
     case = inputs.random_case(seed, M, N, K, lda, ldb, ldc, with_c0=True, with_bias=use_bias)
+    if poison_pad:
+        # operand padding (k >= K within a row of A / a column of B) is NaN:
+        # a kernel that reads it produces NaN
+        for key, ld, rows in (("A", lda, M), ("B", ldb, N)):
+            if ld > K:
+                case[key].reshape(rows, ld)[:, K:] = NAN_BF16
     C0 = case["C0"]
     # beta == 0: C starts as NaN everywhere, which must not leak
     C_init = C0 if beta != 0.0 else np.full_like(C0, NAN_BF16)
@@ -114,8 +120,8 @@ def check_full(tag, M, N, K, lda=None, ldb=None, ldc=None, alpha=1.0, beta=0.0, 
     (512, 384, 256, "tile128x128x64_s4"),     # 4 K-slices (even)
     (4096, 2048, 320, "ring256x256x64"),      # 128 tiles of 256, 5 slices of 64
     (4096, 2048, 64, "ring256x256x64"),       # a single K-slice
-    (4096, 2048, 352, "tile256x256x32_s5"),   # K % 64 == 32: 11 slices of 32
-    (4096, 2048, 32, "tile256x256x32_s5"),    # a single K-slice of 32
+    (4096, 2048, 352, "ring256x256x64_masked"),  # K % 64 == 32: a half-empty last slice
+    (4096, 2048, 32, "ring256x256x64_masked"),   # a single half-empty K-slice
 ])
 def test_tile_paths_full(M, N, K, kernel):
     check_full(f"tile {M}x{N}x{K}", M, N, K, seed=M + N + K, expect_kernel=kernel)
@@ -124,8 +130,8 @@ def test_tile_paths_full(M, N, K, kernel):
 def test_tile_path_epilogue_full():
     check_full("ring256 epilogue", 4096, 2048, 192, alpha=1.0, beta=0.5, use_bias=True,
                epilogue="gelu_tanh", seed=11, expect_kernel="ring256x256x64")
-    check_full("tile256 epilogue", 4096, 2048, 160, alpha=1.0, beta=0.5, use_bias=True,
-               epilogue="gelu_tanh", seed=16, expect_kernel="tile256x256x32_s5")
+    check_full("masked ring epilogue", 4096, 2048, 160, alpha=1.0, beta=0.5, use_bias=True,
+               epilogue="gelu_tanh", seed=16, expect_kernel="ring256x256x64_masked")
     check_full("tile128 epilogue", 512, 512, 128, alpha=-0.75, beta=-1.5, use_bias=True,
                epilogue="none", seed=12, expect_kernel="tile128x128x64_s4")
     check_full("tile128 gelu only", 384, 256, 320, alpha=2.0, epilogue="gelu_tanh", seed=13,
@@ -137,15 +143,15 @@ def test_tile_path_padded_leading_dims():
                seed=14, expect_kernel="tile128x128x64_s4")
     check_full("ring256 padded ld", 4096, 2048, 128, lda=136, ldb=192, ldc=4104, seed=15,
                expect_kernel="ring256x256x64")
-    check_full("tile256 padded ld", 4096, 2048, 96, lda=104, ldb=136, ldc=4112, seed=17,
-               expect_kernel="tile256x256x32_s5")
+    check_full("masked ring padded ld", 4096, 2048, 96, lda=104, ldb=136, ldc=4112, seed=17,
+               expect_kernel="ring256x256x64_masked")
 
 
 # Every tile kernel forced onto shapes whose K-slice count walks through the
 # pipeline's prologue and tail cases (1 .. 10 slices, fewer and more slices
 # than LDS stages, odd and even counts).
 FORCEABLE = {"tile256x256x32_s5": 32, "tile128x128x64_s4": 64, "ring256x256x64": 64,
-             "ring256x256x64_mfma32": 64, "generic64x64x32": 1}
+             "ring256x256x64_mfma32": 64, "ring256x256x64_masked": 8, "generic64x64x32": 1}
 
 
 @pytest.mark.parametrize("kernel", list(FORCEABLE))
@@ -173,6 +179,43 @@ def test_tile_epilogue_combinations(kernel, M, N, K, beta, use_bias, epi, monkey
     check_full(f"{kernel} beta={beta} bias={use_bias} {epi}", M, N, K, alpha=1.25, beta=beta,
                use_bias=use_bias, epilogue=epi, seed=int(abs(beta) * 4) + 2 * use_bias + len(epi),
                expect_kernel=kernel)
+
+
+# The masked ring kernel (shapes with tails): M and N tails of every size
+# class (1 row/column, less than a wave's 128, straddling 8-row chunks), K
+# tails down to a single 8-wide chunk, padded leading dimensions whose
+# padding is NaN, and every epilogue combination.
+MASKED = "ring256x256x64_masked"
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc", [
+    (300, 260, 72, 72, 72, 304),      # one full + one 8-wide K chunk past a slice
+    (257, 513, 8, 16, 24, 264),        # a single 8-wide K chunk, 1-row / 1-column tails
+    (1000, 600, 1000, 1000, 1008, 1000),
+    (1001, 777, 200, 208, 200, 1008),  # M % 8 == 1: the last 8-row chunk straddles M
+    (255, 1, 136, 136, 144, 256),      # N = 1
+    (1, 255, 64, 64, 64, 8),           # M = 1
+    (520, 264, 4040, 4048, 4040, 528), # 63 full slices and a 8-wide K tail
+    (512, 512, 4096, 4096, 4096, 512), # no tails at all through the masked path
+])
+def test_masked_ring_tails(M, N, K, lda, ldb, ldc, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", MASKED)
+    check_full(f"masked {M}x{N}x{K}", M, N, K, lda=lda, ldb=ldb, ldc=ldc, beta=0.0, seed=M + N + K,
+               expect_kernel=MASKED, poison_pad=True)
+
+
+@pytest.mark.parametrize("beta,use_bias,epi", [(b, u, e) for b in (0.0, -0.75) for u in (False, True)
+                                               for e in ("none", "gelu_tanh")])
+def test_masked_ring_epilogue_combinations(beta, use_bias, epi, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", MASKED)
+    check_full(f"masked beta={beta} bias={use_bias} {epi}", 777, 300, 200, ldc=784, alpha=1.25, beta=beta,
+               use_bias=use_bias, epilogue=epi, seed=7 + int(abs(beta) * 4) + 2 * use_bias + len(epi),
+               expect_kernel=MASKED, poison_pad=True)
+
+
+def test_masked_ring_is_the_default_for_large_ragged_shapes():
+    check_full("ragged default", 4000, 2000, 1000, beta=0.5, use_bias=True, epilogue="gelu_tanh", seed=51,
+               expect_kernel=MASKED)
 
 
 # The streaming kernel for M = 64 / 32: slice counts through its ring
