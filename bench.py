@@ -6,8 +6,14 @@ One step is one call of gemm_bf16 on the chosen workload (default: the
 alpha = 1, beta = 0), with inputs already resident in device memory.  The
 protocol follows "Outperforming cuBLAS on H100: a worklog", section
 "Experimental setup": W untimed warm-up launches, then the mean over K timed
-launches, FLOPS = 2*M*N*K / time.  Each launch is bracketed by its own pair
-of HIP events recorded on the stream the kernel runs on.
+launches, FLOPS = 2*M*N*K / time.  The K launches run back to back between
+one pair of HIP events recorded on the stream the kernel runs on (synchronized
+on both sides); their mean is `value` and the roofline's achieved rate.  A
+second pass of K launches, each between its own event pair, gives the
+per-launch spread (min / median / max); a per-launch pair also times the
+command processor's dispatch of the kernel, a few microseconds that matter
+for the short memory-bound launch.  When beta != 0 C is in/out: every launch
+reads the previous launch's output as C0 (same bytes, same work).
 
 Prints ONE JSON line (rank 0, one GPU).  With --all it prints one line per
 workload instead.
@@ -41,7 +47,7 @@ METRIC = "bf16 GEMM TFLOP/s at M=N=K=4096 and % of MI355X dense bf16 MFMA peak"
 # HBM3E 8 TB/s.
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
-EPI = {"none": 0, "gelu_tanh": 1}
+EPI = {"none": 0, "gelu_tanh": 1, "relu": 2}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
@@ -82,8 +88,10 @@ def cpu_baseline(w, d, budget_cols=None):
     ms = np.tile(np.arange(M, dtype=np.int64), cols)
     ns = np.repeat(np.arange(cols, dtype=np.int64), M)
     t0 = time.perf_counter()
-    oracle.gemm_elems(M, N, K, d["A"], K, d["B"], K, ms, ns, d.get("C0"), M, w.alpha, w.beta,
-                      d.get("bias"), w.epilogue, nthreads=nthreads)
+    _, y = oracle.gemm_elems(M, N, K, d["A"], K, d["B"], K, ms, ns, d.get("C0"), M, w.alpha, w.beta,
+                             d.get("bias"), w.epilogue, nthreads=nthreads, return_pre=True)
+    if w.out == "int8":
+        oracle.quantize_i8_array(y, d["scale"][ms], w.zero_point)
     dt = time.perf_counter() - t0
     flops = 2.0 * M * cols * K
     return {
@@ -126,27 +134,40 @@ def run_workload(w, steps, warmup, cold, with_cpu):
         return torch.from_numpy(bits.view(np.int16)).to(dev)
 
     copies = 4 if cold else 1  # rotate distinct buffers so B is not cache-resident
+    q8 = w.out == "int8"
     A = [dev_tensor(d["A"]) for _ in range(copies)]
     B = [dev_tensor(d["B"]) for _ in range(copies)]
-    C = [torch.empty(w.N * w.M, dtype=torch.int16, device=dev) for _ in range(copies)]
+    C = [torch.empty(w.N * w.M, dtype=torch.int8 if q8 else torch.int16, device=dev) for _ in range(copies)]
     C0 = dev_tensor(d["C0"]) if "C0" in d else None
     bias = dev_tensor(d["bias"]) if "bias" in d else None
+    scale = torch.from_numpy(d["scale"]).to(dev) if q8 else None
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
-    kname = gb.gemm_bf16_kernel_name(w.M, w.N, w.K, A[0].data_ptr(), w.K, B[0].data_ptr(), w.K,
-                                     C[0].data_ptr(), w.M, w.beta, bias.data_ptr() if bias is not None else 0,
-                                     EPI[w.epilogue])
+    bias_p = bias.data_ptr() if bias is not None else 0
+    if q8:
+        c0_p = C0.data_ptr() if C0 is not None else 0
+        kname = gb.gemm_bf16_q8_kernel_name(w.M, w.N, w.K, A[0].data_ptr(), w.K, B[0].data_ptr(), w.K, c0_p, w.M,
+                                            C[0].data_ptr(), w.M, w.beta, scale.data_ptr(), EPI[w.epilogue])
+    else:
+        kname = gb.gemm_bf16_kernel_name(w.M, w.N, w.K, A[0].data_ptr(), w.K, B[0].data_ptr(), w.K,
+                                         C[0].data_ptr(), w.M, w.beta, bias_p, EPI[w.epilogue])
     log(f"[bench] kernel {kname}; warmup {warmup}, steps {steps}, cold={cold}")
 
+    if C0 is not None and not q8:
+        for c in C:
+            c.copy_(C0)  # beta != 0: C starts as C0 and stays in/out
+
     def launch(i):
-        j = i % copies
-        if C0 is not None:
-            C[j].copy_(C0)  # beta != 0: C is in/out; reset outside the timed pair
-        return j
+        return i % copies
 
     def call(j):
-        st = gb.gemm_bf16(w.M, w.N, w.K, A[j].data_ptr(), w.K, B[j].data_ptr(), w.K, C[j].data_ptr(), w.M,
-                          w.alpha, w.beta, bias.data_ptr() if bias is not None else 0, EPI[w.epilogue], sp)
+        if q8:
+            st = gb.gemm_bf16_q8(w.M, w.N, w.K, A[j].data_ptr(), w.K, B[j].data_ptr(), w.K, c0_p, w.M,
+                                 C[j].data_ptr(), w.M, w.alpha, w.beta, bias_p, EPI[w.epilogue], scale.data_ptr(),
+                                 w.zero_point, sp)
+        else:
+            st = gb.gemm_bf16(w.M, w.N, w.K, A[j].data_ptr(), w.K, B[j].data_ptr(), w.K, C[j].data_ptr(), w.M,
+                              w.alpha, w.beta, bias_p, EPI[w.epilogue], sp)
         if st != 0:
             raise RuntimeError(f"gemm_bf16 status {st}: {gb.gemm_bf16_status_string(st)}")
 
@@ -154,25 +175,35 @@ def run_workload(w, steps, warmup, cold, with_cpu):
         call(launch(i))
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    # timed region: K launches back to back between one event pair
     all0 = torch.cuda.Event(enable_timing=True)
     all1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     all0.record(stream)
     for i in range(steps):
-        j = launch(warmup + i)
-        ev[i][0].record(stream)
-        call(j)
-        ev[i][1].record(stream)
+        call(launch(warmup + i))
     all1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [a.elapsed_time(b) for a, b in ev]  # ms
-    mean_ms = statistics.fmean(per)
+    region_ms = all0.elapsed_time(all1)
+    mean_ms = region_ms / steps
     tflops = w.flops / (mean_ms * 1e-3) / 1e12
     gbs = w.algorithmic_bytes / (mean_ms * 1e-3) / 1e9
-    log(f"[bench] per-launch ms: mean {mean_ms:.4f} min {min(per):.4f} max {max(per):.4f} -> {tflops:.1f} TFLOP/s")
+    log(f"[bench] timed region: {steps} launches in {region_ms:.3f} ms -> {mean_ms * 1e3:.2f} us per launch, "
+        f"{tflops:.1f} TFLOP/s, {gbs:.0f} GB/s algorithmic")
+
+    # spread: the same K launches again, each between its own event pair
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        j = launch(warmup + steps + i)
+        ev[i][0].record(stream)
+        call(j)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in ev]  # ms
+    log(f"[bench] per-launch event pairs ms: mean {statistics.fmean(per):.4f} min {min(per):.4f} "
+        f"median {statistics.median(per):.4f} max {max(per):.4f}")
 
     traffic = measured_traffic(w.name, kname)
     if w.bound == "hbm":
@@ -199,14 +230,15 @@ def run_workload(w, steps, warmup, cold, with_cpu):
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha, "beta": w.beta,
                    "bias": w.bias, "epilogue": w.epilogue, "layout": "A row-major, B/C column-major",
-                   "kernel": kname, "inputs": "N(0,1) seeded (bias N(0,0.1))",
+                   "kernel": kname, "inputs": "N(0,1) seeded (bias N(0,0.1))", "output": w.out,
                    "cache": "cold (4 rotating buffer sets)" if cold else "warm"},
         "pct_of_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "hbm_gbs_algorithmic": gbs,
-        "per_launch_ms": {"mean": mean_ms, "min": min(per), "median": statistics.median(per),
-                          "max": max(per), "stdev": statistics.pstdev(per)},
+        "per_launch_event_pairs_ms": {"mean": statistics.fmean(per), "min": min(per),
+                                      "median": statistics.median(per), "max": max(per),
+                                      "stdev": statistics.pstdev(per)},
         "timed_region_wall_ms": wall * 1e3,
-        "timed_region_event_ms": all0.elapsed_time(all1),
+        "timed_region_event_ms": region_ms,
         "roofline": roof,
         "cpu_baseline": None,
     }

@@ -15,12 +15,13 @@ import os
 
 __all__ = [
     "EPILOGUES", "GemmError", "LIB_PATH", "gemm", "gemm_bf16", "gemm_bf16_kernel_name",
-    "gemm_bf16_last_hip_error", "gemm_bf16_status_string", "library",
+    "gemm_bf16_last_hip_error", "gemm_bf16_q8", "gemm_bf16_q8_kernel_name", "gemm_bf16_status_string",
+    "gemm_q8", "library",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemm_bf16.so")
 
-EPILOGUES = {"none": 0, "gelu_tanh": 1}
+EPILOGUES = {"none": 0, "gelu_tanh": 1, "relu": 2}
 GEMM_OK = 0
 
 _lib = None
@@ -51,6 +52,11 @@ def library() -> ctypes.CDLL:
     lib.gemm_bf16_last_hip_error.restype = i32
     lib.gemm_bf16_kernel_name.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, f32, vp, i32]
     lib.gemm_bf16_kernel_name.restype = ctypes.c_char_p
+    lib.gemm_bf16_q8.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, f32, f32, vp, i32, vp,
+                                 ctypes.c_int32, vp]
+    lib.gemm_bf16_q8.restype = i32
+    lib.gemm_bf16_q8_kernel_name.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, f32, vp, i32]
+    lib.gemm_bf16_q8_kernel_name.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -59,6 +65,20 @@ def gemm_bf16(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, bias, epilogue, stre
     """Raw C-ABI call; pointers and the stream are integers (0 / None = NULL)."""
     return library().gemm_bf16(M, N, K, A or None, lda, B or None, ldb, C or None, ldc,
                                alpha, beta, bias or None, epilogue, stream or None)
+
+
+def gemm_bf16_q8(M, N, K, A, lda, B, ldb, C, ldc, Q, ldq, alpha, beta, bias, epilogue, scale,
+                 zero_point, stream) -> int:
+    """Raw C-ABI call of the int8-output entry point (pointers as integers)."""
+    return library().gemm_bf16_q8(M, N, K, A or None, lda, B or None, ldb, C or None, ldc, Q or None, ldq,
+                                  alpha, beta, bias or None, epilogue, scale or None, int(zero_point),
+                                  stream or None)
+
+
+def gemm_bf16_q8_kernel_name(M, N, K, A, lda, B, ldb, C, ldc, Q, ldq, beta=0.0, scale=None,
+                             epilogue=0) -> str:
+    return library().gemm_bf16_q8_kernel_name(M, N, K, A or None, lda, B or None, ldb, C or None, ldc,
+                                              Q or None, ldq, beta, scale or None, epilogue).decode()
 
 
 def gemm_bf16_status_string(status: int) -> str:
@@ -120,3 +140,40 @@ def gemm(A, Bt, Ct, alpha: float = 1.0, beta: float = 0.0, bias=None, epilogue: 
             msg += f" (hipError {gemm_bf16_last_hip_error()})"
         raise GemmError(status, msg)
     return Ct
+
+
+def gemm_q8(A, Bt, Qt, scale, zero_point: int = 0, alpha: float = 1.0, beta: float = 0.0, Ct=None,
+            bias=None, epilogue: str = "none", stream=None):
+    """Qt <- sat8(rne(epi(alpha*A*B + beta*C + bias) * scale[m] + zero_point)).
+
+    A, Bt, bias as in gemm; Qt: (N, M) int8 with contiguous rows (column-major
+    Q, ldq = Qt.stride(0)); scale: (M,) contiguous float32; Ct: (N, M) bf16
+    input C0, only needed when beta != 0.  Returns Qt.
+    """
+    import torch
+    M, K = A.shape
+    N = Bt.shape[0]
+    a_ptr, lda = _operand(A, "A", M, K)
+    b_ptr, ldb = _operand(Bt, "Bt", N, K)
+    c_ptr, ldc = (0, max(M, 1)) if Ct is None else _operand(Ct, "Ct", N, M)
+    if Qt.dtype != torch.int8 or tuple(Qt.shape) != (N, M) or (M > 1 and Qt.stride(1) != 1) or not Qt.is_cuda:
+        raise ValueError("Qt must be an (N, M) int8 device tensor with contiguous rows")
+    ldq = max(Qt.stride(0) if N > 1 else M, M, 1)
+    if scale.dtype != torch.float32 or scale.numel() != M or not scale.is_contiguous() or not scale.is_cuda:
+        raise ValueError("scale must be a contiguous float32 device tensor of M elements")
+    bias_ptr = 0
+    if bias is not None:
+        if bias.dtype != torch.bfloat16 or bias.numel() != N or not bias.is_contiguous() or not bias.is_cuda:
+            raise ValueError("bias must be a contiguous bf16 device tensor of N elements")
+        bias_ptr = bias.data_ptr()
+    if stream is None:
+        stream = torch.cuda.current_stream(Qt.device)
+    st = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    status = gemm_bf16_q8(M, N, K, a_ptr, lda, b_ptr, ldb, c_ptr, ldc, Qt.data_ptr(), ldq, float(alpha),
+                          float(beta), bias_ptr, EPILOGUES[epilogue], scale.data_ptr(), int(zero_point), st)
+    if status != GEMM_OK:
+        msg = gemm_bf16_status_string(status)
+        if status == -5:
+            msg += f" (hipError {gemm_bf16_last_hip_error()})"
+        raise GemmError(status, msg)
+    return Qt

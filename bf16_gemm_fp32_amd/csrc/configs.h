@@ -29,6 +29,7 @@ hipError_t launch_tile_medium(const GemmArgs &args, int cus, hipStream_t stream)
 hipError_t launch_tile_ring_mfma32(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_ring(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_ring_masked(const GemmArgs &args, int cus, hipStream_t stream);
+hipError_t launch_tile_ring_q8(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_skinny_m64(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_skinny_m32(const GemmArgs &args, int cus, hipStream_t stream);
 

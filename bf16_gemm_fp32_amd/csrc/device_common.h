@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace gb {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -16,8 +18,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define GB_LDS __attribute__((address_space(3)))
 
-// Epilogue flags (runtime, uniform across the grid).
-enum : uint32_t { kEpiBeta = 1u, kEpiBias = 2u, kEpiGelu = 4u };
+// Epilogue flags (uniform across the grid).  GELU and ReLU exclude each
+// other, so twelve combinations exist.
+enum : uint32_t { kEpiBeta = 1u, kEpiBias = 2u, kEpiGelu = 4u, kEpiRelu = 8u };
 
 struct GemmArgs {
     int64_t M, N, K;
@@ -30,7 +33,33 @@ struct GemmArgs {
     float alpha, beta;
     const uint16_t *bias;
     uint32_t flags;  // kEpi* bits
+    // int8 output (the quantizing entry point only): Q[m + n*ldq] =
+    // sat8(rne(fma(v, scale[m], zp))); unused by the bf16 kernels.
+    int8_t *Q;
+    int64_t ldq;
+    const float *scale;
+    float zp;
 };
+
+// Call f(std::integral_constant<uint32_t, flags>) for the run-time flag word,
+// so each launcher instantiates its kernel once per valid combination.
+template <class F>
+__host__ inline void dispatch_flags(uint32_t flags, F &&f) {
+    switch (flags) {
+    case 0: f(std::integral_constant<uint32_t, 0>{}); break;
+    case 1: f(std::integral_constant<uint32_t, 1>{}); break;
+    case 2: f(std::integral_constant<uint32_t, 2>{}); break;
+    case 3: f(std::integral_constant<uint32_t, 3>{}); break;
+    case 4: f(std::integral_constant<uint32_t, 4>{}); break;
+    case 5: f(std::integral_constant<uint32_t, 5>{}); break;
+    case 6: f(std::integral_constant<uint32_t, 6>{}); break;
+    case 7: f(std::integral_constant<uint32_t, 7>{}); break;
+    case 8: f(std::integral_constant<uint32_t, 8>{}); break;
+    case 9: f(std::integral_constant<uint32_t, 9>{}); break;
+    case 10: f(std::integral_constant<uint32_t, 10>{}); break;
+    default: f(std::integral_constant<uint32_t, 11>{}); break;
+    }
+}
 
 // ---------------------------------------------------------------- waits ---
 // Explicit waits and barriers as inline asm with a memory clobber: the
@@ -100,6 +129,10 @@ __device__ __forceinline__ float gelu_tanh_f32(float y) {
     return y * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// ReLU: negative values become 0; NaN passes through (a compare-select, not
+// v_max_f32, which would return 0 for NaN).
+__device__ __forceinline__ float relu_f32(float y) { return y < 0.f ? 0.f : y; }
+
 // alpha*acc (+ beta*c_in) (+ bias) then the activation, all in fp32, with the
 // epilogue flags known at compile time (the tile kernels are instantiated per
 // flag combination, so the plain product carries no epilogue code at all).
@@ -109,6 +142,7 @@ __device__ __forceinline__ float epilogue_value(float acc, float c_in, float bia
     if constexpr ((kFlags & kEpiBeta) != 0) v += beta * c_in;
     if constexpr ((kFlags & kEpiBias) != 0) v += bias_v;
     if constexpr ((kFlags & kEpiGelu) != 0) v = gelu_tanh_f32(v);
+    if constexpr ((kFlags & kEpiRelu) != 0) v = relu_f32(v);
     return v;
 }
 
@@ -118,7 +152,19 @@ __device__ __forceinline__ float epilogue_value_rt(float acc, float c_in, float 
     if (a.flags & kEpiBeta) v += a.beta * c_in;
     if (a.flags & kEpiBias) v += bias_v;
     if (a.flags & kEpiGelu) v = gelu_tanh_f32(v);
+    if (a.flags & kEpiRelu) v = relu_f32(v);
     return v;
+}
+
+// Per-row int8 quantization of an epilogue value: one fused multiply-add in
+// fp32, round to nearest even, saturate to [-128, 127]; NaN gives 0 (the
+// DeepGEMM article, section 6.2: y = round(x * scale + zero_point), one
+// scale per row).
+__device__ __forceinline__ int32_t quantize_i8(float v, float scale, float zp) {
+    const float t = __builtin_fmaf(v, scale, zp);
+    if (!(t == t)) return 0;
+    const float r = __builtin_rintf(t);
+    return (int32_t)(r < -128.f ? -128.f : (r > 127.f ? 127.f : r));
 }
 
 __device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {

@@ -16,13 +16,13 @@
 namespace gb {
 
 enum KernelKind {
-    kNone = 0, kLarge, kMedium, kSkinny64, kSkinny32, kGeneric, kRing32, kRing, kRingMasked, kNumKinds
+    kNone = 0, kLarge, kMedium, kSkinny64, kSkinny32, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kNumKinds
 };
 
 static const char *const kKindNames[kNumKinds] = {"none",            "tile256x256x32_s5", "tile128x128x64_s4",
                                                   "skinny64x32x256", "skinny32x32x256",   "generic64x64x32",
                                                   "ring256x256x64_mfma32", "ring256x256x64",
-                                                  "ring256x256x64_masked"};
+                                                  "ring256x256x64_masked", "ring256x256x64_q8"};
 
 static const char *kind_name(int k) { return (k >= 0 && k < kNumKinds) ? kKindNames[k] : "none"; }
 
@@ -44,13 +44,38 @@ static int device_cu_count() {
     return cus;
 }
 
+static bool epilogue_ok(int epilogue) {
+    return epilogue == GEMM_EPI_NONE || epilogue == GEMM_EPI_GELU_TANH || epilogue == GEMM_EPI_RELU;
+}
+
+static uint32_t epilogue_flags(float beta, const void *bias, int epilogue) {
+    return (beta != 0.0f ? kEpiBeta : 0u) | (bias ? kEpiBias : 0u) |
+           (epilogue == GEMM_EPI_GELU_TANH ? kEpiGelu : 0u) | (epilogue == GEMM_EPI_RELU ? kEpiRelu : 0u);
+}
+
 static int validate(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
                     const void *C, int64_t ldc, int epilogue) {
     if (M < 0 || N < 0 || K < 0) return GEMM_ERR_DIM;
     const int64_t kmin = K > 1 ? K : 1, mmin = M > 1 ? M : 1;
     if (lda < kmin || ldb < kmin || ldc < mmin) return GEMM_ERR_LD;
     if ((M > 0 && K > 0 && !A) || (K > 0 && N > 0 && !B) || (M > 0 && N > 0 && !C)) return GEMM_ERR_NULL;
-    if (epilogue != GEMM_EPI_NONE && epilogue != GEMM_EPI_GELU_TANH) return GEMM_ERR_EPILOGUE;
+    if (!epilogue_ok(epilogue)) return GEMM_ERR_EPILOGUE;
+    return GEMM_OK;
+}
+
+// The quantizing entry point: C (the bf16 C0) is only needed when beta != 0;
+// Q (M x N int8, ldq >= M) and scale (M floats) always.
+static int validate_q8(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
+                       const void *C, int64_t ldc, const void *Q, int64_t ldq, float beta, const void *scale,
+                       int epilogue) {
+    if (M < 0 || N < 0 || K < 0) return GEMM_ERR_DIM;
+    const int64_t kmin = K > 1 ? K : 1, mmin = M > 1 ? M : 1;
+    if (lda < kmin || ldb < kmin || ldq < mmin || (beta != 0.0f && ldc < mmin)) return GEMM_ERR_LD;
+    const bool out = M > 0 && N > 0;
+    if ((M > 0 && K > 0 && !A) || (K > 0 && N > 0 && !B) || (out && beta != 0.0f && !C) || (out && !Q) ||
+        (out && !scale))
+        return GEMM_ERR_NULL;
+    if (!epilogue_ok(epilogue)) return GEMM_ERR_EPILOGUE;
     return GEMM_OK;
 }
 
@@ -135,6 +160,26 @@ static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t
     return kGeneric;
 }
 
+// The quantizing path: the masked ring kernel when its requirements hold
+// (also for Q, scale and ldq) and its 256x256 tiles give at least half the
+// compute units a tile, else the bounds-checked kernel.
+static int choose_kernel_q8(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+                            int64_t ldb, const void *C, int64_t ldc, float beta, const void *Q, int64_t ldq,
+                            const void *scale, int cus) {
+    if (M == 0 || N == 0) return kNone;
+    const void *c_probe = beta != 0.0f ? C : A;  // C is not read when beta == 0
+    const int64_t ldc_probe = beta != 0.0f ? ldc : 8;
+    const bool ok = ring_masked_ok(M, N, K, A, lda, B, ldb, c_probe, ldc_probe) && aligned16(Q) &&
+                    aligned16(scale) && ldq % 8 == 0;
+    if (ok) {
+        const int64_t tiles = ((M + ShapeRing::BM - 1) / ShapeRing::BM) * ((N + ShapeRing::BN - 1) / ShapeRing::BN);
+        const char *force = std::getenv("GEMM_BF16_FORCE_KERNEL");
+        const bool forced = force && !std::strcmp(force, kKindNames[kRingQ8]);
+        if (tiles * 2 >= cus || forced) return kRingQ8;
+    }
+    return kGeneric;
+}
+
 static hipError_t launch_generic(const GemmArgs &args, int cus, hipStream_t stream) {
     const int64_t tiles_m = (args.M + GenericConfig::BM - 1) / GenericConfig::BM;
     const int64_t tiles_n = (args.N + GenericConfig::BN - 1) / GenericConfig::BN;
@@ -171,8 +216,11 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t lda
     args.alpha = alpha;
     args.beta = beta;
     args.bias = bias;
-    args.flags = (beta != 0.0f ? kEpiBeta : 0u) | (bias ? kEpiBias : 0u) |
-                 (epilogue == GEMM_EPI_GELU_TANH ? kEpiGelu : 0u);
+    args.flags = epilogue_flags(beta, bias, epilogue);
+    args.Q = nullptr;
+    args.ldq = 0;
+    args.scale = nullptr;
+    args.zp = 0.f;
 
     const int cus = device_cu_count();
     hipError_t err = hipSuccess;
@@ -191,6 +239,56 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t lda
         return GEMM_ERR_HIP;
     }
     return GEMM_OK;
+}
+
+int gemm_bf16_q8(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t lda, const gemm_bf16_t *B,
+                 int64_t ldb, const gemm_bf16_t *C, int64_t ldc, int8_t *Q, int64_t ldq, float alpha, float beta,
+                 const gemm_bf16_t *bias, int epilogue, const float *scale, int32_t zero_point,
+                 hipStream_t stream) {
+    using namespace gb;
+    const int st = validate_q8(M, N, K, A, lda, B, ldb, C, ldc, Q, ldq, beta, scale, epilogue);
+    if (st != GEMM_OK) return st;
+    if (M == 0 || N == 0) return GEMM_OK;
+
+    GemmArgs args;
+    args.M = M;
+    args.N = N;
+    args.K = K;
+    args.A = A;
+    args.lda = lda;
+    args.B = B;
+    args.ldb = ldb;
+    args.C = const_cast<gemm_bf16_t *>(C);  // read only (beta != 0); never written on this path
+    args.ldc = beta != 0.0f ? ldc : 1;
+    args.alpha = alpha;
+    args.beta = beta;
+    args.bias = bias;
+    args.flags = epilogue_flags(beta, bias, epilogue);
+    args.Q = Q;
+    args.ldq = ldq;
+    args.scale = scale;
+    args.zp = (float)zero_point;
+
+    const int cus = device_cu_count();
+    hipError_t err = hipSuccess;
+    if (choose_kernel_q8(M, N, K, A, lda, B, ldb, C, ldc, beta, Q, ldq, scale, cus) == kRingQ8)
+        err = launch_tile_ring_q8(args, cus, stream);
+    else
+        err = launch_generic(args, cus, stream);
+    if (err != hipSuccess) {
+        t_last_hip_error = (int)err;
+        return GEMM_ERR_HIP;
+    }
+    return GEMM_OK;
+}
+
+const char *gemm_bf16_q8_kernel_name(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t lda,
+                                     const gemm_bf16_t *B, int64_t ldb, const gemm_bf16_t *C, int64_t ldc,
+                                     const int8_t *Q, int64_t ldq, float beta, const float *scale,
+                                     int epilogue) {
+    if (gb::validate_q8(M, N, K, A, lda, B, ldb, C, ldc, Q, ldq, beta, scale, epilogue) != GEMM_OK) return "none";
+    return gb::kind_name(
+        gb::choose_kernel_q8(M, N, K, A, lda, B, ldb, C, ldc, beta, Q, ldq, scale, gb::device_cu_count()));
 }
 
 const char *gemm_bf16_status_string(int status) {

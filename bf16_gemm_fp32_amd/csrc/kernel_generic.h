@@ -82,18 +82,22 @@ gemm_generic_kernel(const GemmArgs args, int64_t tiles_m, int64_t num_tiles) {
             lds_barrier();
         }
 
-        // lane: column n, rows 8g + 4h + 0..3 of the wave's 32x32 block
+        // lane: column n, rows 8g + 4h + 0..3 of the wave's 32x32 block.
+        // With args.Q set the output is int8 (quantizing entry point) and C,
+        // if read at all, is the separate bf16 input C0.
         const int64_t n = n0 + wn * 32 + (lane & 31);
         if (n < args.N) {
             const float bias_v = (args.flags & kEpiBias) ? bf16_bits_to_f32(args.bias[n]) : 0.f;
-            uint16_t *col = args.C + n * args.ldc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t m = m0 + wm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
                 if (m < args.M) {
-                    const float cin = (args.flags & kEpiBeta) ? bf16_bits_to_f32(col[m]) : 0.f;
+                    const float cin = (args.flags & kEpiBeta) ? bf16_bits_to_f32(args.C[n * args.ldc + m]) : 0.f;
                     const float v = epilogue_value_rt(acc[r], cin, bias_v, args);
-                    col[m] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFFu);
+                    if (args.Q)
+                        args.Q[n * args.ldq + m] = (int8_t)quantize_i8(v, args.scale[m], args.zp);
+                    else
+                        args.C[n * args.ldc + m] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFFu);
                 }
             }
         }

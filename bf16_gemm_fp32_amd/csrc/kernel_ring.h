@@ -126,11 +126,18 @@ struct RingKernel {
 
     enum : int { kNoLoad = 0, kLoadA = 1, kLoadB = 2 };
 
+    // Shadow schedule of a k-step: the fragment read (0..15, A0, B0, A1, B1,
+    // ...) and the DMA load (0..7) that follow MFMA s, or -1.
+    __host__ __device__ static constexpr int read_at(int s) { return s < 2 * Cfg::FM ? s : -1; }
+    __host__ __device__ static constexpr int load_at(int s) {
+        return (s >= 16 && (s - 16) % 6 == 0 && (s - 16) / 6 < Cfg::kUnitLoads) ? (s - 16) / 6 : -1;
+    }
+
     // One k-step: 64 MFMAs on (a, b), block (s / FN, s % FN) for MFMA s;
-    // after MFMA s < 16 (if kRead) fragment read s of k-step rks from slots
-    // (rsa, rsb) into (ra, rb), alternating A0, B0, A1, B1, ...; after MFMAs
-    // 16, 22, ..., 58 (if kLoad) the 8 DMA loads of the unit (kLoad's operand)
-    // of slice lkt into slot lslot.
+    // (if kRead) the 16 fragment reads of k-step rks from slots (rsa, rsb)
+    // into (ra, rb) and (if kLoad) the 8 DMA loads of the unit (kLoad's
+    // operand) of slice lkt into slot lslot, each in the MFMA shadow that
+    // read_at / load_at assign it.
     template <bool kRead, int kLoad>
     __device__ __forceinline__ static void kstep(char *smem, const bf16x8 (&a)[Cfg::FM], const bf16x8 (&b)[Cfg::FN],
                                                  f32x4 (&acc)[Cfg::FM][Cfg::FN], int rsa, int rsb, int rks,
@@ -143,15 +150,16 @@ struct RingKernel {
             const int p = s / Cfg::FN, q = s % Cfg::FN;
             acc[p][q] = mfma_16x16x32(a[p], b[q], acc[p][q]);
             __builtin_amdgcn_sched_barrier(0);
-            if (kRead && s < 2 * Cfg::FM) {
-                const int f = s >> 1;
-                if ((s & 1) == 0)
+            const int r = read_at(s);
+            if (kRead && r >= 0) {
+                const int f = r >> 1;
+                if ((r & 1) == 0)
                     ra[f] = *(const GB_LDS bf16x8 *)(sA + L.aRow + f * 16 * Cfg::kRowBytes + L.chunk_off[rks]);
                 else
                     rb[f] = *(const GB_LDS bf16x8 *)(sB + L.bRow + f * 16 * Cfg::kRowBytes + L.chunk_off[rks]);
             }
-            if (kLoad != kNoLoad && s >= 16 && (s - 16) % 6 == 0 && (s - 16) / 6 < Cfg::kUnitLoads) {
-                const int l = (s - 16) / 6;
+            const int l = load_at(s);
+            if (kLoad != kNoLoad && l >= 0) {
                 if (kLoad == kLoadA)
                     load<true>(smem, lslot, lkt, l, L, rA);
                 else
@@ -249,7 +257,10 @@ __device__ __forceinline__ void ring_epi_load(RingEpiInputs &in, const GemmArgs 
     }
 }
 
-template <uint32_t kFlags, bool kMasked>
+// kQ8: the quantizing output -- each value becomes one int8 byte of Q,
+// sat8(rne(v * scale[m] + zp)); a lane's 8 rows are fixed for the whole tile
+// (its 8-row chunk is lane % 16), so their scales are loaded once.
+template <uint32_t kFlags, bool kMasked, bool kQ8>
 __device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, int64_t m0, int64_t n0, int wm,
                                               int wn, int lane, int wave,
                                               const f32x4 (&acc)[RingConfig::FM][RingConfig::FN],
@@ -259,7 +270,20 @@ __device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, 
     constexpr int kColChunks = Cfg::WTM / 8;      // 8-row chunks per column
     constexpr int kIters = 32 * kColChunks / 64;  // per lane per 32 columns
     static_assert(kIters == 8, "RingEpiInputs holds one group's 8 iterations");
+    static_assert(64 % kColChunks == 0, "a lane's row chunk is the same in every iteration");
     const int c16 = lane & 15, r4 = (lane >> 4) * 4;
+    float sc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if constexpr (kQ8) {
+        const int64_t m = m0 + wm * Cfg::WTM + (lane % kColChunks) * 8;
+        if (!kMasked || m + 8 <= args.M) {
+            const f32x4 lo = *(const f32x4 *)(args.scale + m);
+            const f32x4 hi = *(const f32x4 *)(args.scale + m + 4);
+            sc[0] = lo.x; sc[1] = lo.y; sc[2] = lo.z; sc[3] = lo.w;
+            sc[4] = hi.x; sc[5] = hi.y; sc[6] = hi.z; sc[7] = hi.w;
+        } else {
+            for (int e = 0; e < 8 && m + e < args.M; ++e) sc[e] = args.scale[m + e];
+        }
+    }
 #pragma unroll
     for (int jj = 0; jj < Cfg::FN / 2; ++jj) {
         RingEpiInputs next;
@@ -290,6 +314,21 @@ __device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, 
                 }
             }
             const float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            if constexpr (kQ8) {
+                u32x2 qw = {0u, 0u};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float v = epilogue_value<kFlags>(x[e], cin[e], bias_v, args.alpha, args.beta);
+                    qw[e >> 2] |= ((uint32_t)quantize_i8(v, sc[e], args.zp) & 0xFFu) << ((e & 3) * 8);
+                }
+                int8_t *qp = args.Q + n * args.ldq + m;
+                if (!kMasked || (n < args.N && m + 8 <= args.M)) {
+                    __builtin_nontemporal_store(qw, (u32x2 *)qp);
+                } else if (n < args.N) {
+                    for (int e = 0; e < 8 && m + e < args.M; ++e) qp[e] = (int8_t)(qw[e >> 2] >> ((e & 3) * 8));
+                }
+                continue;
+            }
             u32x4 out;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -315,9 +354,11 @@ __device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, 
 }
 
 // Requirements checked by the host before launch: M % 256 == 0,
-// N % 256 == 0, K % 64 == 0, K > 0, A/B/C 16-byte aligned, lda/ldb/ldc
-// multiples of 8, and 256*lda*2 + 2K, 256*ldb*2 + 2K below 2^31.
-template <uint32_t kFlags, bool kMasked>
+// N % 256 == 0, K % 64 == 0 (masked: any M, N >= 1 and K % 8 == 0), K > 0,
+// A/B/C 16-byte aligned, lda/ldb/ldc multiples of 8, and 256*lda*2 + 2K,
+// 256*ldb*2 + 2K below 2^31; for kQ8 also Q and scale 16-byte aligned and
+// ldq a multiple of 8.
+template <uint32_t kFlags, bool kMasked, bool kQ8>
 __global__ void __launch_bounds__(RingConfig::kThreads)
 gemm_ring_kernel(const GemmArgs args, const TileSchedule sched) {
     using Cfg = RingConfig;
@@ -428,26 +469,20 @@ gemm_ring_kernel(const GemmArgs args, const TileSchedule sched) {
         // Every wave is done reading the ring (all loads landed at the last
         // wait): its memory now stages the epilogue.
         lds_barrier();
-        ring_epilogue<kFlags, kMasked>(smem, args, m0, n0, wm, wn, lane, Ln.wave, acc, epi_in);
+        ring_epilogue<kFlags, kMasked, kQ8>(smem, args, m0, n0, wm, wn, lane, Ln.wave, acc, epi_in);
     }
 }
 
 // Launch with the epilogue flags of args baked in; grid = min(tiles, CUs),
 // one persistent workgroup per compute unit.  The masked instances run when
 // the shape has tails.
-template <bool kMasked>
+template <bool kMasked, bool kQ8 = false>
 hipError_t launch_ring_t(const GemmArgs &args, const TileSchedule &s, hipStream_t stream) {
+    static_assert(kMasked || !kQ8, "the quantizing output is built on the masked instance");
     const dim3 grid(s.grid), block(RingConfig::kThreads);
-    switch (args.flags & 7u) {
-    case 0: hipLaunchKernelGGL((gemm_ring_kernel<0, kMasked>), grid, block, 0, stream, args, s); break;
-    case 1: hipLaunchKernelGGL((gemm_ring_kernel<1, kMasked>), grid, block, 0, stream, args, s); break;
-    case 2: hipLaunchKernelGGL((gemm_ring_kernel<2, kMasked>), grid, block, 0, stream, args, s); break;
-    case 3: hipLaunchKernelGGL((gemm_ring_kernel<3, kMasked>), grid, block, 0, stream, args, s); break;
-    case 4: hipLaunchKernelGGL((gemm_ring_kernel<4, kMasked>), grid, block, 0, stream, args, s); break;
-    case 5: hipLaunchKernelGGL((gemm_ring_kernel<5, kMasked>), grid, block, 0, stream, args, s); break;
-    case 6: hipLaunchKernelGGL((gemm_ring_kernel<6, kMasked>), grid, block, 0, stream, args, s); break;
-    default: hipLaunchKernelGGL((gemm_ring_kernel<7, kMasked>), grid, block, 0, stream, args, s); break;
-    }
+    dispatch_flags(args.flags, [&](auto f) {
+        hipLaunchKernelGGL((gemm_ring_kernel<decltype(f)::value, kMasked, kQ8>), grid, block, 0, stream, args, s);
+    });
     return hipGetLastError();
 }
 

@@ -270,16 +270,9 @@ inline hipError_t launch_ring32(const GemmArgs &args, int cus, hipStream_t strea
     const int tiles = s.num_tiles();
     s.grid = tiles < cus ? tiles : cus;
     const dim3 grid(s.grid), block(Ring32Config::kThreads);
-    switch (args.flags & 7u) {
-    case 0: hipLaunchKernelGGL((gemm_ring32_kernel<0>), grid, block, 0, stream, args, s); break;
-    case 1: hipLaunchKernelGGL((gemm_ring32_kernel<1>), grid, block, 0, stream, args, s); break;
-    case 2: hipLaunchKernelGGL((gemm_ring32_kernel<2>), grid, block, 0, stream, args, s); break;
-    case 3: hipLaunchKernelGGL((gemm_ring32_kernel<3>), grid, block, 0, stream, args, s); break;
-    case 4: hipLaunchKernelGGL((gemm_ring32_kernel<4>), grid, block, 0, stream, args, s); break;
-    case 5: hipLaunchKernelGGL((gemm_ring32_kernel<5>), grid, block, 0, stream, args, s); break;
-    case 6: hipLaunchKernelGGL((gemm_ring32_kernel<6>), grid, block, 0, stream, args, s); break;
-    default: hipLaunchKernelGGL((gemm_ring32_kernel<7>), grid, block, 0, stream, args, s); break;
-    }
+    dispatch_flags(args.flags, [&](auto f) {
+        hipLaunchKernelGGL((gemm_ring32_kernel<decltype(f)::value>), grid, block, 0, stream, args, s);
+    });
     return hipGetLastError();
 }
 

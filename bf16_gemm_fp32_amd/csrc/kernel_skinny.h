@@ -238,16 +238,9 @@ template <class Cfg>
 hipError_t launch_skinny(const GemmArgs &args, int cus, hipStream_t stream) {
     const int strips = (int)(args.N / Cfg::BN);
     const dim3 grid(strips < cus ? strips : cus), block(Cfg::kThreads);
-    switch (args.flags & 7u) {
-    case 0: hipLaunchKernelGGL((gemm_skinny_kernel<Cfg, 0>), grid, block, 0, stream, args, strips); break;
-    case 1: hipLaunchKernelGGL((gemm_skinny_kernel<Cfg, 1>), grid, block, 0, stream, args, strips); break;
-    case 2: hipLaunchKernelGGL((gemm_skinny_kernel<Cfg, 2>), grid, block, 0, stream, args, strips); break;
-    case 3: hipLaunchKernelGGL((gemm_skinny_kernel<Cfg, 3>), grid, block, 0, stream, args, strips); break;
-    case 4: hipLaunchKernelGGL((gemm_skinny_kernel<Cfg, 4>), grid, block, 0, stream, args, strips); break;
-    case 5: hipLaunchKernelGGL((gemm_skinny_kernel<Cfg, 5>), grid, block, 0, stream, args, strips); break;
-    case 6: hipLaunchKernelGGL((gemm_skinny_kernel<Cfg, 6>), grid, block, 0, stream, args, strips); break;
-    default: hipLaunchKernelGGL((gemm_skinny_kernel<Cfg, 7>), grid, block, 0, stream, args, strips); break;
-    }
+    dispatch_flags(args.flags, [&](auto f) {
+        hipLaunchKernelGGL((gemm_skinny_kernel<Cfg, decltype(f)::value>), grid, block, 0, stream, args, strips);
+    });
     return hipGetLastError();
 }
 

@@ -414,16 +414,9 @@ hipError_t launch_tile(const GemmArgs &args, int cus, hipStream_t stream) {
     const int tiles = s.num_tiles();
     s.grid = tiles < cus ? tiles : cus;
     const dim3 grid(s.grid), block(Cfg::kThreads);
-    switch (args.flags & 7u) {
-    case 0: hipLaunchKernelGGL((gemm_tile_kernel<Cfg, 0>), grid, block, 0, stream, args, s); break;
-    case 1: hipLaunchKernelGGL((gemm_tile_kernel<Cfg, 1>), grid, block, 0, stream, args, s); break;
-    case 2: hipLaunchKernelGGL((gemm_tile_kernel<Cfg, 2>), grid, block, 0, stream, args, s); break;
-    case 3: hipLaunchKernelGGL((gemm_tile_kernel<Cfg, 3>), grid, block, 0, stream, args, s); break;
-    case 4: hipLaunchKernelGGL((gemm_tile_kernel<Cfg, 4>), grid, block, 0, stream, args, s); break;
-    case 5: hipLaunchKernelGGL((gemm_tile_kernel<Cfg, 5>), grid, block, 0, stream, args, s); break;
-    case 6: hipLaunchKernelGGL((gemm_tile_kernel<Cfg, 6>), grid, block, 0, stream, args, s); break;
-    default: hipLaunchKernelGGL((gemm_tile_kernel<Cfg, 7>), grid, block, 0, stream, args, s); break;
-    }
+    dispatch_flags(args.flags, [&](auto f) {
+        hipLaunchKernelGGL((gemm_tile_kernel<Cfg, decltype(f)::value>), grid, block, 0, stream, args, s);
+    });
     return hipGetLastError();
 }
 

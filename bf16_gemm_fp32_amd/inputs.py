@@ -13,7 +13,9 @@ section "Experimental setup"):
 * values are float32 standard normals (bias: multiplied by 0.1 in float32,
   i.e. standard deviation 0.1), rounded to bf16 nearest-even;
 * buffers are filled in storage order: A as M rows of K (row-major), B as N
-  columns of K (column-major), C0 as N columns of M (column-major).
+  columns of K (column-major), C0 as N columns of M (column-major);
+* int8-output workloads also draw one float32 scale per row (operand j = 5),
+  uniform in [lo, hi), and use a fixed zero point.
 """
 from __future__ import annotations
 
@@ -34,6 +36,9 @@ class Workload:
     bias: bool = False
     epilogue: str = "none"
     bound: str = "mfma"  # which roofline limits it: "mfma" or "hbm"
+    out: str = "bf16"    # "bf16", or "int8" (per-row quantized output)
+    scale_range: tuple = (0.25, 0.75)  # int8 output: per-row scales, uniform
+    zero_point: int = 0                # int8 output: zero point
     notes: str = field(default="", compare=False)
 
     @property
@@ -42,12 +47,16 @@ class Workload:
 
     @property
     def algorithmic_bytes(self) -> int:
-        """Minimum HBM bytes: read A and B once, write C once (read C0 if beta)."""
-        b = 2 * (self.M * self.K + self.K * self.N + self.M * self.N)
+        """Minimum HBM bytes: read A and B once, write C once (read C0 if
+        beta); an int8 output writes 1 byte per element and reads M scales."""
+        b = 2 * (self.M * self.K + self.K * self.N)
+        b += (1 if self.out == "int8" else 2) * self.M * self.N
         if self.beta != 0.0:
             b += 2 * self.M * self.N
         if self.bias:
             b += 2 * self.N
+        if self.out == "int8":
+            b += 4 * self.M
         return b
 
 
@@ -71,6 +80,11 @@ WORKLOADS = {
         # K-slices of 64 do not divide it), for the masked fast path
         Workload("ragged_4000x4000x4000", 5, 4000, 4000, 4000,
                  notes="tails in every dimension: 4000 = 15*256 + 160 = 62*64 + 32"),
+        # the fused quantizing epilogue of the DeepGEMM article (section
+        # 6.2) on the epilogue case's shape: bias, ReLU, per-row int8
+        Workload("q8relu_8192x14336x4096", 6, 8192, 14336, 4096, bias=True, epilogue="relu",
+                 out="int8", zero_point=-20,
+                 notes="Q = sat8(rne(relu(A*B + bias[n]) * scale[m] - 20))"),
     ]
 }
 
@@ -95,7 +109,13 @@ def normal_bf16(seed: int, numel: int, scale: float = 1.0) -> np.ndarray:
 
 
 def operand_seed(index: int, operand: str) -> int:
-    return 1000 * index + {"A": 1, "B": 2, "C0": 3, "bias": 4}[operand]
+    return 1000 * index + {"A": 1, "B": 2, "C0": 3, "bias": 4, "scale": 5}[operand]
+
+
+def uniform_f32(seed: int, numel: int, lo: float, hi: float) -> np.ndarray:
+    """numel i.i.d. float32 samples, uniform in [lo, hi), seeded."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    return (np.float32(lo) + g.random(numel, dtype=np.float32) * np.float32(hi - lo)).astype(np.float32)
 
 
 def make_inputs(w: Workload, lda=None, ldb=None, ldc=None) -> dict:
@@ -116,6 +136,8 @@ def make_inputs(w: Workload, lda=None, ldb=None, ldc=None) -> dict:
         out["C0"] = normal_bf16(operand_seed(w.index, "C0"), w.N * ldc)
     if w.bias:
         out["bias"] = normal_bf16(operand_seed(w.index, "bias"), w.N, scale=0.1)
+    if w.out == "int8":
+        out["scale"] = uniform_f32(operand_seed(w.index, "scale"), w.M, *w.scale_range)
     return out
 
 

@@ -14,6 +14,9 @@
  * units; alpha, beta*C, bias and the activation are applied in fp32; the
  * result is rounded once to bf16, round-to-nearest-even.
  *
+ * gemm_bf16_q8 writes int8 instead: the same fp32 epilogue value, then a
+ * per-row quantization (section 6.2 of the same article).
+ *
  * Every function is thread-safe.  The library keeps no pointer after a call
  * returns and allocates no device memory.
  */
@@ -30,11 +33,14 @@ extern "C" {
 /* Raw bf16 bits (sign, 8-bit exponent, 7-bit mantissa). */
 typedef uint16_t gemm_bf16_t;
 
-/* Epilogue activation, applied last to alpha*AB + beta*C + bias. */
+/* Epilogue activation, applied last to alpha*AB + beta*C + bias (the
+ * DeepGEMM article, section 6.1: bias first, then ReLU or GELU). */
 enum gemm_bf16_epilogue {
     GEMM_EPI_NONE = 0,
     /* GELU, tanh form: 0.5x(1 + tanh(sqrt(2/pi)(x + 0.044715x^3))) */
-    GEMM_EPI_GELU_TANH = 1
+    GEMM_EPI_GELU_TANH = 1,
+    /* ReLU: x < 0 ? 0 : x (NaN passes through) */
+    GEMM_EPI_RELU = 2
 };
 
 /* Status codes.  Argument errors are detected on the host, in this order,
@@ -85,6 +91,42 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K,
               const gemm_bf16_t *bias,
               int epilogue, hipStream_t stream);
 
+/*
+ * gemm_bf16_q8 -- enqueue the same product and epilogue with an int8 output
+ * quantized per row (per token): the DeepGEMM article (demingchina.com),
+ * section 6.2, y = round(x * scale + zero_point) with one scale per row.
+ *
+ *   Q[m + n*ldq] = sat8( rne( fma( v[m,n], scale[m], zero_point ) ) )
+ *   v[m,n]       = epi( alpha * sum_k A[m,k]*B[k,n] + beta*C[m,n] + bias[n] )
+ *
+ * v is the fp32 value gemm_bf16 would round to bf16; the multiply-add is one
+ * fp32 fused operation, rne rounds to the nearest integer with ties to even,
+ * sat8 clamps to [-128, 127], and a NaN v gives 0.
+ *
+ *   A, lda, B, ldb, alpha, beta, bias, epilogue, stream: as in gemm_bf16.
+ *   C        device pointer, column-major M x N bf16 input C0 (element (m,n)
+ *            at C[m + n*ldc]), read only when beta != 0; may be NULL (and
+ *            ldc anything) when beta == 0.  Never written.
+ *   Q        device pointer, column-major M x N int8 output, element (m,n)
+ *            at Q[m + n*ldq], ldq >= max(1, M).  Rows M..ldq-1 untouched.
+ *   scale    device pointer to M fp32 scales, one per row m.
+ *   zero_point  added after the scaling (converted to fp32).
+ *
+ * Errors as gemm_bf16, with these differences: GEMM_ERR_LD also when
+ * ldq < max(1,M), and ldc is only checked when beta != 0; GEMM_ERR_NULL also
+ * for a NULL Q or scale (M*N > 0), and for a NULL C only when beta != 0.
+ * Q must not overlap A, B, C, bias or scale.
+ */
+int gemm_bf16_q8(int64_t M, int64_t N, int64_t K,
+                 const gemm_bf16_t *A, int64_t lda,
+                 const gemm_bf16_t *B, int64_t ldb,
+                 const gemm_bf16_t *C, int64_t ldc,
+                 int8_t *Q, int64_t ldq,
+                 float alpha, float beta,
+                 const gemm_bf16_t *bias, int epilogue,
+                 const float *scale, int32_t zero_point,
+                 hipStream_t stream);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char *gemm_bf16_status_string(int status);
 
@@ -104,6 +146,16 @@ const char *gemm_bf16_kernel_name(int64_t M, int64_t N, int64_t K,
                                   const gemm_bf16_t *C, int64_t ldc,
                                   float beta, const gemm_bf16_t *bias,
                                   int epilogue);
+
+/* The kernel configuration gemm_bf16_q8 would launch (as
+ * gemm_bf16_kernel_name). */
+const char *gemm_bf16_q8_kernel_name(int64_t M, int64_t N, int64_t K,
+                                     const gemm_bf16_t *A, int64_t lda,
+                                     const gemm_bf16_t *B, int64_t ldb,
+                                     const gemm_bf16_t *C, int64_t ldc,
+                                     const int8_t *Q, int64_t ldq,
+                                     float beta, const float *scale,
+                                     int epilogue);
 
 #ifdef __cplusplus
 }

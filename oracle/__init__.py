@@ -29,7 +29,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gemm_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-EPI_CODES = {"none": 0, "gelu_tanh": 1}
+EPI_CODES = {"none": 0, "gelu_tanh": 1, "relu": 2}
 
 _lib = None
 
@@ -72,6 +72,17 @@ def _load():
                                       ctypes.c_void_p, ctypes.c_void_p, u16p,
                                       ctypes.c_void_p, ctypes.c_int]
     lib.oracle_gemm_elems.restype = ctypes.c_int
+    lib.oracle_relu.argtypes = [f64]
+    lib.oracle_relu.restype = f64
+    lib.oracle_quantize_i8.argtypes = [f64, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]
+    lib.oracle_quantize_i8.restype = ctypes.c_int
+    lib.oracle_gemm_q8.argtypes = [i64, i64, i64, u16p, i64, u16p, i64, u16p, i64, f64, f64, u16p,
+                                   ctypes.c_int, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, i64,
+                                   ctypes.c_void_p, ctypes.c_int]
+    lib.oracle_gemm_q8.restype = ctypes.c_int
+    lib.oracle_quantize_i8_array.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                             ctypes.c_void_p, ctypes.c_void_p, i64]
+    lib.oracle_quantize_i8_array.restype = None
     _lib = lib
     return lib
 
@@ -174,3 +185,56 @@ def gemm_elems(M, N, K, A, lda, B, ldb, ms, ns, C_in=None, ldc=None, alpha=1.0,
     if return_pre:
         return out[: ms.size], pre[: ms.size]
     return out[: ms.size]
+
+
+def relu(y: float) -> float:
+    """ReLU of one value, in float64 (NaN passes through)."""
+    return _load().oracle_relu(float(y))
+
+
+def quantize_i8(y: float, scale: float, zero_point: int):
+    """(code, t_exact): the int8 code of one epilogue value and y*scale+zp in double."""
+    t = ctypes.c_double()
+    q = _load().oracle_quantize_i8(float(y), float(scale), int(zero_point), ctypes.byref(t))
+    return q, t.value
+
+
+def gemm_q8(M, N, K, A, lda, B, ldb, scale, zero_point=0, C_in=None, ldc=None, ldq=None, alpha=1.0,
+            beta=0.0, bias=None, epilogue="none", nthreads=0):
+    """Int8-output oracle: returns (Q, t_exact).
+
+    Q is a flat int8 array of N*ldq elements (column-major, leading dimension
+    ldq; padding rows are 0); t_exact is the (N, M) float64 array of
+    y*scale[m] + zero_point before the fp32 decision.  scale holds M float32.
+    """
+    lib = _load()
+    if ldc is None:
+        ldc = max(1, M)
+    if ldq is None:
+        ldq = max(1, M)
+    A, B, C_in, bias = _u16(A, "A"), _u16(B, "B"), _u16(C_in, "C_in"), _u16(bias, "bias")
+    scale = np.ascontiguousarray(scale, dtype=np.float32).reshape(-1)
+    if scale.size < M:
+        raise ValueError("scale too small")
+    Q = np.zeros(max(N * ldq, 1), dtype=np.int8)
+    t = np.zeros((max(N, 1), max(M, 1)), dtype=np.float64)
+    rc = lib.oracle_gemm_q8(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C_in), ldc, float(alpha), float(beta),
+                            _ptr(bias), EPI_CODES[epilogue], _ptr(scale), int(zero_point), _ptr(Q), ldq,
+                            _ptr(t), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_gemm_q8 rejected its arguments")
+    return Q[: N * ldq], t[:N, :M]
+
+
+def quantize_i8_array(y, scale, zero_point):
+    """Vector form of quantize_i8: y (float64) and per-element scales (float32)
+    of the same length; returns (codes int8, t_exact float64)."""
+    lib = _load()
+    y = np.ascontiguousarray(y, dtype=np.float64).reshape(-1)
+    s = np.ascontiguousarray(scale, dtype=np.float32).reshape(-1)
+    if s.size != y.size:
+        raise ValueError("y and scale differ in length")
+    q = np.zeros(max(y.size, 1), dtype=np.int8)
+    t = np.zeros(max(y.size, 1), dtype=np.float64)
+    lib.oracle_quantize_i8_array(_ptr(y), _ptr(s), int(zero_point), _ptr(q), _ptr(t), y.size)
+    return q[: y.size], t[: y.size]

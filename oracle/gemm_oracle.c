@@ -22,11 +22,19 @@
  *  - DeepGEMM kernel-set article (demingchina.com), section 1.1: the BLAS
  *    form C = alpha*A*B + beta*C; section 3.1: low-precision inputs with
  *    high-precision accumulation; section 6.1: bias is added first, then the
- *    activation (ReLU/GELU) is applied, then the result is written.
+ *    activation (ReLU/GELU) is applied, then the result is written;
+ *    section 6.2: an int8 output quantized per token (per row of C),
+ *    y = round(x * scale + zero_point), with x the fp32 GEMM output.
  *
  * Readings where the pages are silent (each listed in the design notes):
  *  - GELU is the tanh form 0.5*y*(1+tanh(sqrt(2/pi)*(y+0.044715*y^3))),
  *    applied to the whole pre-activation sum (alpha*AB + beta*C + bias).
+ *  - ReLU is y < 0 ? 0 : y (NaN passes through).
+ *  - Quantization: x is the epilogue value rounded once to fp32 (the page's
+ *    "FP32 output"); the code is decided in fp32 as the page's formula
+ *    reads, t = fma(x, scale[m], zero_point) (one rounding), then rounded to
+ *    the nearest integer with ties to even, then saturated to [-128, 127];
+ *    a NaN t gives 0.  "Per token" is read as one scale per row m of C.
  *  - bias is indexed by the output column n (length N).
  *  - beta == 0 means C_in is not read at all (BLAS convention).
  *  - Accumulation is in double; every bf16*bf16 product is exact in double
@@ -50,6 +58,7 @@
 
 #define ORACLE_EPI_NONE 0
 #define ORACLE_EPI_GELU_TANH 1
+#define ORACLE_EPI_RELU 2
 #define ORACLE_PI 3.14159265358979323846264338327950288
 
 /* Exact decode: bf16 is the upper half of an IEEE binary32. */
@@ -104,6 +113,43 @@ double oracle_gelu_tanh(double y)
     return 0.5 * y * (1.0 + tanh(c * (y + 0.044715 * y * y * y)));
 }
 
+/* ReLU: negative values to 0, everything else (NaN included) unchanged. */
+double oracle_relu(double y)
+{
+    return y < 0.0 ? 0.0 : y;
+}
+
+/*
+ * The int8 code of one epilogue value y for a row with scale s and zero
+ * point zp, decided in fp32: x = (float)y, t = fmaf(x, s, zp), round half to
+ * even (rintf in the default rounding mode), saturate.  *t_exact (if not
+ * NULL) receives y*s + zp in double, the value the decision approximates.
+ */
+int oracle_quantize_i8(double y, float s, int32_t zp, double *t_exact)
+{
+    if (t_exact)
+        *t_exact = y * (double)s + (double)zp;
+    float x = (float)y;
+    float t = fmaf(x, s, (float)zp);
+    if (isnan(t))
+        return 0;
+    float r = rintf(t);
+    if (r < -128.0f)
+        return -128;
+    if (r > 127.0f)
+        return 127;
+    return (int)r;
+}
+
+/* oracle_quantize_i8 over n values with their own scales (for sampled
+ * elements); t_exact may be NULL. */
+void oracle_quantize_i8_array(const double *y, const float *s, int32_t zp, int8_t *q, double *t_exact,
+                              int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        q[i] = (int8_t)oracle_quantize_i8(y[i], s[i], zp, t_exact ? &t_exact[i] : NULL);
+}
+
 /* Element-wise array forms of the two conversions (n elements). */
 void oracle_bf16_to_f64_array(const uint16_t *in, double *out, int64_t n)
 {
@@ -143,7 +189,14 @@ static double epilogue(double s, double alpha, double beta, const uint16_t *c_in
         y += oracle_bf16_to_f64(bias[n]);
     if (epi == ORACLE_EPI_GELU_TANH)
         y = oracle_gelu_tanh(y);
+    else if (epi == ORACLE_EPI_RELU)
+        y = oracle_relu(y);
     return y;
+}
+
+static int epi_ok(int epi)
+{
+    return epi == ORACLE_EPI_NONE || epi == ORACLE_EPI_GELU_TANH || epi == ORACLE_EPI_RELU;
 }
 
 /*
@@ -164,7 +217,7 @@ int oracle_gemm(int64_t M, int64_t N, int64_t K,
         return -1;
     if (lda < (K > 1 ? K : 1) || ldb < (K > 1 ? K : 1) || ldc < (M > 1 ? M : 1))
         return -1;
-    if (epi != ORACLE_EPI_NONE && epi != ORACLE_EPI_GELU_TANH)
+    if (!epi_ok(epi))
         return -1;
     if (beta != 0.0 && !C_in)
         return -1;
@@ -200,7 +253,7 @@ int oracle_gemm_elems(int64_t M, int64_t N, int64_t K,
         return -1;
     if (lda < (K > 1 ? K : 1) || ldb < (K > 1 ? K : 1) || ldc < (M > 1 ? M : 1))
         return -1;
-    if (epi != ORACLE_EPI_NONE && epi != ORACLE_EPI_GELU_TANH)
+    if (!epi_ok(epi))
         return -1;
     if (beta != 0.0 && !C_in)
         return -1;
@@ -217,6 +270,42 @@ int oracle_gemm_elems(int64_t M, int64_t N, int64_t K,
         if (pre)
             pre[i] = y;
         out[i] = oracle_bf16_from_f64(y);
+    }
+    return 0;
+}
+
+/*
+ * The quantizing product: Q[m + n*ldq] = oracle_quantize_i8(y[m,n], scale[m],
+ * zp) with y the epilogue value of oracle_gemm (before any bf16 rounding).
+ * C_in is read only when beta != 0.  If `t_exact` is not NULL it receives
+ * y*scale[m] + zp in double, column-major with leading dimension M.
+ */
+int oracle_gemm_q8(int64_t M, int64_t N, int64_t K,
+                   const uint16_t *A, int64_t lda,
+                   const uint16_t *B, int64_t ldb,
+                   const uint16_t *C_in, int64_t ldc,
+                   double alpha, double beta,
+                   const uint16_t *bias, int epi,
+                   const float *scale, int32_t zp,
+                   int8_t *Q, int64_t ldq, double *t_exact, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return -1;
+    if (lda < (K > 1 ? K : 1) || ldb < (K > 1 ? K : 1) || ldq < (M > 1 ? M : 1))
+        return -1;
+    if (beta != 0.0 && (!C_in || ldc < (M > 1 ? M : 1)))
+        return -1;
+    if (!epi_ok(epi) || (M > 0 && !scale))
+        return -1;
+    if (nthreads < 1)
+        nthreads = omp_get_max_threads();
+    int64_t total = M * N;
+#pragma omp parallel for schedule(dynamic, 64) num_threads(nthreads)
+    for (int64_t idx = 0; idx < total; ++idx) {
+        int64_t n = idx / M, m = idx % M;
+        double s = dot_row_col(A + m * lda, B + n * ldb, K);
+        double y = epilogue(s, alpha, beta, beta != 0.0 ? C_in + m + n * ldc : NULL, bias, n, epi);
+        Q[m + n * ldq] = (int8_t)oracle_quantize_i8(y, scale[m], zp, t_exact ? &t_exact[m + n * M] : NULL);
     }
     return 0;
 }

@@ -36,9 +36,9 @@ def test_status_codes_match_header():
     text = open(HEADER).read()
     for name, val in [("GEMM_OK", 0), ("GEMM_ERR_DIM", -1), ("GEMM_ERR_LD", -2),
                       ("GEMM_ERR_NULL", -3), ("GEMM_ERR_EPILOGUE", -4), ("GEMM_ERR_HIP", -5),
-                      ("GEMM_EPI_NONE", 0), ("GEMM_EPI_GELU_TANH", 1)]:
+                      ("GEMM_EPI_NONE", 0), ("GEMM_EPI_GELU_TANH", 1), ("GEMM_EPI_RELU", 2)]:
         assert re.search(rf"\b{name}\s*=\s*{val}\b", text), name
-    assert gb.EPILOGUES == {"none": 0, "gelu_tanh": 1}
+    assert gb.EPILOGUES == {"none": 0, "gelu_tanh": 1, "relu": 2}
 
 
 def call(M, N, K, A=P, lda=None, B=P, ldb=None, C=P, ldc=None, alpha=1.0, beta=0.0, bias=0, epi=0):
@@ -56,6 +56,39 @@ def call(M, N, K, A=P, lda=None, B=P, ldb=None, C=P, ldc=None, alpha=1.0, beta=0
 ])
 def test_argument_errors(args, want):
     assert call(*args) == want
+
+
+def call_q8(M, N, K, A=P, lda=None, B=P, ldb=None, C=0, ldc=None, Q=P, ldq=None, alpha=1.0, beta=0.0,
+            bias=0, epi=0, scale=P, zp=0):
+    lda = max(K, 1) if lda is None else lda
+    ldb = max(K, 1) if ldb is None else ldb
+    ldc = max(M, 1) if ldc is None else ldc
+    ldq = max(M, 1) if ldq is None else ldq
+    return gb.gemm_bf16_q8(M, N, K, A, lda, B, ldb, C, ldc, Q, ldq, alpha, beta, bias, epi, scale, zp, 0)
+
+
+def test_q8_argument_errors():
+    assert call_q8(-1, 4, 4) == ERR_DIM
+    assert call_q8(4, 4, 4, ldq=3) == ERR_LD
+    assert call_q8(4, 4, 4, beta=0.5, C=P, ldc=3) == ERR_LD
+    assert call_q8(4, 4, 4, Q=0) == ERR_NULL
+    assert call_q8(4, 4, 4, scale=0) == ERR_NULL
+    assert call_q8(4, 4, 4, beta=0.5, C=0) == ERR_NULL
+    assert call_q8(4, 4, 4, epi=3) == ERR_EPI
+    # beta == 0: C and ldc are not looked at; empty outputs launch nothing
+    assert call_q8(0, 4, 4, Q=0, scale=0) == OK
+    name = gb.gemm_bf16_q8_kernel_name
+    assert name(4096, 4096, 4096, P, 4096, P, 4096, 0, 1, P, 4096, 0.0, P, 2) == "ring256x256x64_q8"
+    assert name(4000, 4000, 1000, P, 1000, P, 1000, P, 4000, P, 4000, 0.5, P, 1) == "ring256x256x64_q8"
+    assert name(4096, 4096, 4096, P, 4096, P, 4096, 0, 1, P + 8, 4096, 0.0, P, 0) == "generic64x64x32"
+    assert name(4096, 4096, 4096, P, 4096, P, 4096, 0, 1, P, 4100, 0.0, P, 0) == "generic64x64x32"
+    assert name(100, 100, 64, P, 64, P, 64, 0, 1, P, 112, 0.0, P, 0) == "generic64x64x32"
+
+
+def test_relu_is_accepted():
+    # M == 0: nothing to launch, so the status is decided by validation alone
+    assert call(0, 4, 4, A=0, C=0, epi=2) == OK
+    assert call(0, 4, 4, A=0, C=0, epi=3) == ERR_EPI
 
 
 def test_error_order_dim_before_ld_before_null_before_epilogue():

@@ -17,7 +17,7 @@ import pytest
 
 import oracle
 from bf16_gemm_fp32_amd import inputs
-from tests.tolerance import assert_within_tolerance, bits_to_f64
+from tests.tolerance import assert_q8_within_tolerance, assert_within_tolerance, bits_to_f64
 
 torch = pytest.importorskip("torch")
 gb = pytest.importorskip("bf16_gemm_fp32_amd")
@@ -25,7 +25,8 @@ gb = pytest.importorskip("bf16_gemm_fp32_amd")
 pytestmark = pytest.mark.gpu
 
 NAN_BF16 = 0x7FC0
-EPI = {"none": 0, "gelu_tanh": 1}
+EPI = {"none": 0, "gelu_tanh": 1, "relu": 2}
+Q8_POISON = 0x55  # int8 padding rows must keep it
 
 
 def _threads():
@@ -173,7 +174,7 @@ def test_forced_kernels_all_slice_counts(kernel, K, monkeypatch):
                                           ("ring256x256x64", 2048, 1024, 192),
                                           ("ring256x256x64_mfma32", 2048, 1024, 192)])
 @pytest.mark.parametrize("beta,use_bias,epi", [(b, u, e) for b in (0.0, -0.75) for u in (False, True)
-                                               for e in ("none", "gelu_tanh")])
+                                               for e in ("none", "gelu_tanh", "relu")])
 def test_tile_epilogue_combinations(kernel, M, N, K, beta, use_bias, epi, monkeypatch):
     monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", kernel)
     check_full(f"{kernel} beta={beta} bias={use_bias} {epi}", M, N, K, alpha=1.25, beta=beta,
@@ -205,7 +206,7 @@ def test_masked_ring_tails(M, N, K, lda, ldb, ldc, monkeypatch):
 
 
 @pytest.mark.parametrize("beta,use_bias,epi", [(b, u, e) for b in (0.0, -0.75) for u in (False, True)
-                                               for e in ("none", "gelu_tanh")])
+                                               for e in ("none", "gelu_tanh", "relu")])
 def test_masked_ring_epilogue_combinations(beta, use_bias, epi, monkeypatch):
     monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", MASKED)
     check_full(f"masked beta={beta} bias={use_bias} {epi}", 777, 300, 200, ldc=784, alpha=1.25, beta=beta,
@@ -227,7 +228,7 @@ def test_skinny_slice_counts(M, K):
 
 
 @pytest.mark.parametrize("beta,use_bias,epi", [(0.5, True, "gelu_tanh"), (0.0, True, "none"),
-                                               (-1.0, False, "gelu_tanh")])
+                                               (-1.0, False, "gelu_tanh"), (0.25, True, "relu")])
 def test_skinny_epilogues_and_padding(beta, use_bias, epi):
     check_full(f"skinny epilogue beta={beta} bias={use_bias} {epi}", 64, 2048, 512, alpha=0.5, beta=beta,
                use_bias=use_bias, epilogue=epi, seed=41, expect_kernel="skinny64x32x256")
@@ -251,6 +252,8 @@ def test_generic_unaligned_and_odd_leading_dims():
                expect_kernel="generic64x64x32")
     check_full("odd lds", 100, 90, 77, lda=81, ldb=79, ldc=103, beta=2.0, use_bias=True,
                epilogue="gelu_tanh", seed=23, expect_kernel="generic64x64x32")
+    check_full("odd lds relu", 100, 90, 77, lda=81, ldb=79, ldc=103, beta=-0.5, use_bias=True,
+               epilogue="relu", seed=26, expect_kernel="generic64x64x32")
 
 
 def test_k_zero_is_epilogue_only():
@@ -285,6 +288,99 @@ def test_repeat_launches_bit_identical_and_paths_agree():
     assert_within_tolerance(r3, r1, K, "generic vs tile")
 
 
+# ------------------------------------------------------- int8 output ---
+
+def run_gpu_q8(M, N, K, A, lda, B, ldb, C0, ldc, Q_init, ldq, alpha, beta, bias, epilogue, scale, zp,
+               q_offset=0):
+    a_t, a_p = to_dev(A)
+    b_t, b_p = to_dev(B)
+    c_p = 0
+    if beta != 0.0:
+        c_t, c_p = to_dev(C0)
+    q_t = torch.zeros(Q_init.size + q_offset + 16, dtype=torch.int8, device="cuda")
+    q_t[q_offset:q_offset + Q_init.size] = torch.from_numpy(np.ascontiguousarray(Q_init)).cuda()
+    s_t = torch.from_numpy(np.ascontiguousarray(scale, dtype=np.float32)).cuda()
+    bias_p = 0
+    if bias is not None:
+        bias_t, bias_p = to_dev(bias)
+    stream = torch.cuda.current_stream().cuda_stream
+    st = gb.gemm_bf16_q8(M, N, K, a_p, lda, b_p, ldb, c_p, ldc, q_t.data_ptr() + q_offset, ldq, alpha, beta,
+                         bias_p, EPI[epilogue], s_t.data_ptr(), zp, stream)
+    assert st == 0, gb.gemm_bf16_status_string(st)
+    torch.cuda.synchronize()
+    return q_t[q_offset:q_offset + Q_init.size].cpu().numpy().copy()
+
+
+def check_q8(tag, M, N, K, ldq=None, ldc=None, alpha=1.0, beta=0.0, use_bias=False, epilogue="none", zp=0,
+             scale_range=(0.25, 0.75), q_offset=0, seed=0, expect_kernel=None):
+    ldq = max(M, 1) if ldq is None else ldq
+    ldc = max(M, 1) if ldc is None else ldc
+    case = inputs.random_case(seed, M, N, K, ldc=ldc, with_c0=True, with_bias=use_bias)
+    scale = inputs.uniform_f32(seed + 5, M, *scale_range)
+    bias = case.get("bias") if use_bias else None
+    Q_init = np.full(N * ldq, Q8_POISON, np.int8)
+    kld = max(K, 1)
+    kname = gb.gemm_bf16_q8_kernel_name(M, N, K, 4096, kld, 4096, kld, 4096 if beta != 0.0 else 0, ldc,
+                                        4096 + q_offset, ldq, beta, 4096, EPI[epilogue])
+    say(f"[parity-q8] {tag}: M={M} N={N} K={K} ldc={ldc} ldq={ldq} alpha={alpha} beta={beta} bias={use_bias} "
+        f"epi={epilogue} zp={zp} scales={scale_range} q_offset={q_offset} kernel={kname}")
+    if expect_kernel is not None:
+        assert kname == expect_kernel
+    got = run_gpu_q8(M, N, K, case["A"], kld, case["B"], kld, case["C0"], ldc, Q_init, ldq, alpha, beta, bias,
+                     epilogue, scale, zp, q_offset)
+    ref, t = oracle.gemm_q8(M, N, K, case["A"], kld, case["B"], kld, scale, zp, C_in=case["C0"], ldc=ldc, ldq=ldq,
+                            alpha=alpha, beta=beta, bias=bias, epilogue=epilogue, nthreads=_threads())
+    g2, r2 = got.reshape(N, ldq), ref.reshape(N, ldq)
+    rep = assert_q8_within_tolerance(g2[:, :M], r2[:, :M], t, np.broadcast_to(scale[None, :], (N, M)), zp, K,
+                                     tag)
+    if ldq > M:
+        assert np.all(g2[:, M:] == Q8_POISON), f"{tag}: padding rows written"
+    say(f"[parity-q8] {tag}: ok exact={rep['exact']}/{rep['n']} near_boundary={rep['near_boundary']} "
+        f"saturated={int(np.count_nonzero(np.abs(r2[:, :M].astype(np.int64) + 0.5) > 127))}")
+    return rep
+
+
+RQ8 = "ring256x256x64_q8"
+
+
+def test_q8_ring_is_the_default_for_large_shapes():
+    check_q8("q8 ring default", 4096, 2048, 192, use_bias=True, epilogue="relu", zp=-20, seed=61,
+             expect_kernel=RQ8)
+
+
+@pytest.mark.parametrize("M,N,K,ldq", [
+    (1001, 777, 200, 1008), (257, 513, 8, 264), (1, 255, 64, 8), (300, 260, 72, 304), (512, 512, 256, 512),
+])
+def test_q8_ring_tails(M, N, K, ldq, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", RQ8)
+    check_q8(f"q8 ring {M}x{N}x{K}", M, N, K, ldq=ldq, zp=3, seed=M + N, expect_kernel=RQ8)
+
+
+@pytest.mark.parametrize("beta,use_bias,epi", [(b, u, e) for b in (0.0, -0.75) for u in (False, True)
+                                               for e in ("none", "gelu_tanh", "relu")])
+def test_q8_ring_epilogue_combinations(beta, use_bias, epi, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", RQ8)
+    check_q8(f"q8 ring beta={beta} bias={use_bias} {epi}", 777, 300, 200, ldq=784, ldc=792, alpha=1.25, beta=beta,
+             use_bias=use_bias, epilogue=epi, zp=-5, seed=70 + int(abs(beta) * 4) + 2 * use_bias + len(epi),
+             expect_kernel=RQ8)
+
+
+def test_q8_saturation_both_paths(monkeypatch):
+    # scales of 4..8 on values of std ~16: most codes saturate at -128 / 127
+    check_q8("q8 saturating generic", 200, 150, 256, scale_range=(4.0, 8.0), zp=7, seed=81,
+             expect_kernel="generic64x64x32")
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", RQ8)
+    check_q8("q8 saturating ring", 512, 256, 256, scale_range=(4.0, 8.0), zp=7, seed=82, expect_kernel=RQ8)
+
+
+def test_q8_generic_paths():
+    check_q8("q8 generic odd ldq", 100, 90, 77, ldq=103, beta=0.5, use_bias=True, epilogue="gelu_tanh", seed=83,
+             expect_kernel="generic64x64x32")
+    check_q8("q8 generic unaligned Q", 4096, 512, 64, q_offset=3, zp=-1, seed=84, expect_kernel="generic64x64x32")
+    check_q8("q8 K=0", 70, 50, 0, beta=2.0, use_bias=True, epilogue="relu", zp=1, seed=85,
+             expect_kernel="generic64x64x32")
+
+
 # ------------------------------------------- the five workloads, full size ---
 
 def sample_coords(M, N, tile, rng, n_random):
@@ -302,6 +398,8 @@ def sample_coords(M, N, tile, rng, n_random):
 def test_workload_full_size_sampled(name):
     w = inputs.WORKLOADS[name]
     d = inputs.make_inputs(w)
+    if w.out == "int8":
+        return _workload_q8_sampled(w, d)
     M, N, K = w.M, w.N, w.K
     C0 = d.get("C0")
     C_init = C0 if C0 is not None else np.full(N * M, NAN_BF16, np.uint16)
@@ -322,3 +420,21 @@ def test_workload_full_size_sampled(name):
         rep = assert_within_tolerance(got[ms + ns * M], ref, K, name)
     say(f"[parity] workload {name}: ok n={rep['n']} max_ulp={rep['max_ulp']:.2f} "
         f"mean_ulp={rep['mean_ulp']:.4f} exact={rep['exact']}")
+
+
+def _workload_q8_sampled(w, d):
+    M, N, K = w.M, w.N, w.K
+    C0, bias, scale = d.get("C0"), d.get("bias"), d["scale"]
+    kname = gb.gemm_bf16_q8_kernel_name(M, N, K, 4096, K, 4096, K, 4096 if C0 is not None else 0, M, 4096, M,
+                                        w.beta, 4096, EPI[w.epilogue])
+    say(f"[parity-q8] workload {w.name}: M={M} N={N} K={K} kernel={kname}")
+    Q_init = np.full(N * M, Q8_POISON, np.int8)
+    got = run_gpu_q8(M, N, K, d["A"], K, d["B"], K, C0, M, Q_init, M, w.alpha, w.beta, bias, w.epilogue, scale,
+                     w.zero_point)
+    rng = np.random.Generator(np.random.PCG64(7 + w.index))
+    ms, ns = sample_coords(M, N, 256, rng, 20000)
+    _, y = oracle.gemm_elems(M, N, K, d["A"], K, d["B"], K, ms, ns, C0, M, w.alpha, w.beta, bias, w.epilogue,
+                             nthreads=_threads(), return_pre=True)
+    ref, t = oracle.quantize_i8_array(y, scale[ms], w.zero_point)
+    rep = assert_q8_within_tolerance(got[ms + ns * M], ref, t, scale[ms], w.zero_point, K, w.name)
+    say(f"[parity-q8] workload {w.name}: ok exact={rep['exact']}/{rep['n']} near_boundary={rep['near_boundary']}")

@@ -422,3 +422,156 @@ def test_p10_tolerance_hand_cases():
     assert tolerance_report(nan, nan, 1)["fail"] == 0
     assert tolerance_report(one, nan, 1)["fail"] == 1
     assert tolerance_report(nan, one, 1)["fail"] == 1
+
+
+# ---------------------------------------------------------------- P11 ReLU ---
+
+def test_p11_relu_in_the_gemm_matches_torch_after_bias():
+    """K = 1: the pre-activation a*b + bias is exact in double; the output is
+    torch's ReLU of it, rounded (the P2-pinned rounding)."""
+    M, N = 23, 17
+    a = inputs.normal_bf16(41, M)
+    b = inputs.normal_bf16(42, N)
+    bias = inputs.normal_bf16(43, N, scale=0.5)
+    got, pre = oracle.gemm(M, N, 1, a, 1, b, 1, bias=bias, epilogue="relu", return_pre=True)
+    y = np.outer(bits_to_f64(b), bits_to_f64(a)) + bits_to_f64(bias)[:, None]
+    ref = torch.relu(torch.from_numpy(y)).numpy()
+    assert np.array_equal(pre, ref)
+    assert np.all(same_value(got.reshape(N, M), oracle.bf16_from_f64(ref)))
+    assert np.count_nonzero(ref == 0) > 50 and np.count_nonzero(ref > 0) > 50
+
+
+def test_p11_relu_odd_part_identity_and_nan():
+    """relu(y) - relu(-y) = y: negating A and bias negates the pre-activation
+    exactly.  NaN (inf * 0) passes through ReLU, as in torch."""
+    M, N, K = 30, 22, 40
+    case = inputs.random_case(44, M, N, K, with_bias=True)
+    neg = lambda bits: (np.asarray(bits, np.uint16) ^ np.uint16(0x8000)).astype(np.uint16)
+    _, p1 = oracle.gemm(M, N, K, case["A"], K, case["B"], K, bias=case["bias"], epilogue="relu", return_pre=True)
+    _, p2 = oracle.gemm(M, N, K, neg(case["A"]), K, case["B"], K, bias=neg(case["bias"]), epilogue="relu",
+                        return_pre=True)
+    _, p0 = oracle.gemm(M, N, K, case["A"], K, case["B"], K, bias=case["bias"], return_pre=True)
+    assert np.array_equal(p1 - p2, p0)
+    inf, zero = np.array([0x7F80], np.uint16), np.array([0], np.uint16)
+    out = oracle.gemm(1, 1, 1, inf, 1, zero, 1, epilogue="relu")
+    assert np.isnan(bits_to_f64(out)[0]) and np.isnan(torch.relu(torch.tensor([np.nan])).item())
+
+
+# ------------------------------------------------------- P12 int8 output ---
+
+def round_fraction_to_f32(q: Fraction) -> Fraction:
+    """Nearest binary32 value to the exact rational q, ties to even (normal
+    range only; enough for the values here)."""
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    if Fraction(2) ** (e + 1) <= a:
+        e += 1
+    unit = Fraction(2) ** (e - 23)
+    return sign * round(a / unit) * unit  # Python's round() on a Fraction ties to even
+
+
+def q8_code_by_hand(y: Fraction, s: float, zp: int) -> int:
+    """The decision the pages' formula describes, taken in fp32 exactly:
+    x = f32(y), t = f32(x*s + zp) (one rounding), ties-to-even integer,
+    saturated."""
+    x = round_fraction_to_f32(y)
+    t = round_fraction_to_f32(x * Fraction(s) + zp)
+    return max(-128, min(127, round(t)))
+
+
+def test_p12_quantize_hand_table():
+    """Worked by hand: scale 1, zero point 0, exact K = 1 products."""
+    f = inputs.f32_to_bf16_bits
+    cases = [(2.5, 2), (3.5, 4), (-2.5, -2), (0.5, 0), (1.5, 2), (-0.5, 0), (126.5, 126), (127.5, 127),
+             (300.0, 127), (-300.0, -128), (0.75, 1), (-0.75, -1)]
+    vals = np.array([v for v, _ in cases], np.float32)
+    A = f(vals)
+    B = f(np.array([1.0], np.float32))
+    Q, t = oracle.gemm_q8(len(cases), 1, 1, A, 1, B, 1, np.ones(len(cases), np.float32), 0)
+    assert Q.tolist() == [c for _, c in cases]
+    assert np.array_equal(t[0], vals.astype(np.float64))
+    # zero point 10 and scale 1/4: 2.5*... -> rint(v/4 + 10)
+    Q2, _ = oracle.gemm_q8(len(cases), 1, 1, A, 1, B, 1, np.full(len(cases), 0.25, np.float32), 10)
+    assert Q2.tolist() == [max(-128, min(127, round(Fraction(float(v)) / 4 + 10))) for v in vals]
+    # zero point -128: -128.5 -> -128 (even), -129.5 -> -130 -> saturates, -127.5 -> -128, -126.5 -> -126
+    Q3, _ = oracle.gemm_q8(4, 1, 1, f(np.array([-0.5, -1.5, 0.5, 1.5], np.float32)), 1, B, 1,
+                           np.ones(4, np.float32), -128)
+    assert Q3.tolist() == [-128, -128, -128, -126]
+    # NaN (inf * 0) gives 0
+    Qn, tn = oracle.gemm_q8(1, 1, 1, np.array([0x7F80], np.uint16), 1, np.array([0], np.uint16), 1,
+                            np.ones(1, np.float32), 5)
+    assert Qn.tolist() == [0] and np.isnan(tn[0, 0])
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_p12_quantize_exact_rational_bruteforce(seed):
+    """Tiny random products with per-row scales, a zero point, alpha, beta,
+    bias and each activation but GELU: exact rational epilogue value, then the
+    fp32 decision worked by hand -- identical codes."""
+    g = np.random.Generator(np.random.PCG64(7000 + seed))
+    M, N, K = (int(v) for v in g.integers(1, 9, 3))
+    case = inputs.random_case(7100 + seed, M, N, K, with_c0=True, with_bias=True)
+    scale = (g.random(M) * 8 + 0.5).astype(np.float32) * np.float32(g.choice([-1, 1]))
+    zp = int(g.integers(-20, 21))
+    alpha, beta = 1.25, -0.5
+    epi = ["none", "relu"][seed % 2]
+    Q, _ = oracle.gemm_q8(M, N, K, case["A"], K, case["B"], K, scale, zp, C_in=case["C0"], ldc=M,
+                          alpha=alpha, beta=beta, bias=case["bias"], epilogue=epi)
+    A, B = dense(case, M, N, K)
+    C0 = bits_to_f64(case["C0"]).reshape(N, M)
+    bias = bits_to_f64(case["bias"])
+    for n in range(N):
+        for m in range(M):
+            s = sum(Fraction(A[m, k]) * Fraction(B[k, n]) for k in range(K))
+            y = Fraction(alpha) * s + Fraction(beta) * Fraction(C0[n, m]) + Fraction(bias[n])
+            if epi == "relu" and y < 0:
+                y = Fraction(0)
+            assert Q[m + n * M] == q8_code_by_hand(y, float(scale[m]), zp), (m, n)
+
+
+def test_p12_quantize_rows_use_their_own_scale_and_layout():
+    """M != N, padded ldq: row m uses scale[m] (indexing by n would fail),
+    codes land at Q[m + n*ldq] and the padding stays 0."""
+    M, N, K, ldq = 12, 7, 5, 16
+    case = inputs.random_case(7200, M, N, K)
+    scale = np.arange(1, M + 1, dtype=np.float32)
+    Q, t = oracle.gemm_q8(M, N, K, case["A"], K, case["B"], K, scale, 3, ldq=ldq)
+    _, pre = oracle.gemm(M, N, K, case["A"], K, case["B"], K, return_pre=True)
+    assert np.allclose(t, pre * scale[None, :] + 3, rtol=0, atol=1e-12 * (1 + np.abs(t)).max())
+    Q2 = Q.reshape(N, ldq)
+    assert np.all(Q2[:, M:] == 0)
+    for n in range(N):
+        for m in range(M):
+            assert Q2[n, m] == q8_code_by_hand(Fraction(pre[n, m]), float(scale[m]), 3)
+
+
+def test_p13_q8_tolerance_hand_cases():
+    from tests.tolerance import q8_report
+    # exact agreement passes; a code one off passes only next to a boundary
+    assert q8_report([3], [3], [3.2], [1.0], 0, 64)["fail"] == 0
+    assert q8_report([4], [3], [3.2], [1.0], 0, 64)["fail"] == 1
+    assert q8_report([4], [3], [3.4999], [1.0], 0, 64)["fail"] == 0   # delta = 0.008 covers 1e-4
+    assert q8_report([5], [3], [3.4999], [1.0], 0, 64)["fail"] == 1
+    assert q8_report([0], [0], [np.nan], [1.0], 0, 64)["fail"] == 0
+    assert q8_report([1], [0], [np.nan], [1.0], 0, 64)["fail"] == 1
+
+
+def test_p12_quantize_array_agrees_with_whole_product():
+    """The sampled-element form (epilogue values, then codes) reproduces the
+    whole-product codes at every coordinate."""
+    M, N, K = 40, 30, 50
+    case = inputs.random_case(7300, M, N, K, with_c0=True, with_bias=True)
+    scale = inputs.uniform_f32(7305, M, 0.25, 4.0)
+    Q, t = oracle.gemm_q8(M, N, K, case["A"], K, case["B"], K, scale, -7, C_in=case["C0"], ldc=M, alpha=0.75,
+                          beta=0.5, bias=case["bias"], epilogue="gelu_tanh")
+    g = np.random.Generator(np.random.PCG64(7306))
+    ms, ns = g.integers(0, M, 400), g.integers(0, N, 400)
+    _, y = oracle.gemm_elems(M, N, K, case["A"], K, case["B"], K, ms, ns, case["C0"], M, 0.75, 0.5,
+                             case["bias"], "gelu_tanh", return_pre=True)
+    q2, t2 = oracle.quantize_i8_array(y, scale[ms], -7)
+    assert np.array_equal(q2, Q[ms + ns * M]) and np.array_equal(t2, t[ns, ms])

@@ -58,3 +58,38 @@ def assert_within_tolerance(gpu_bits, ref_bits, K: int, what: str = "") -> dict:
     rep = tolerance_report(gpu_bits, ref_bits, K)
     assert rep["fail"] == 0, f"{what}: {rep['fail']} of {rep['n']} elements outside tolerance: {rep}"
     return rep
+
+
+def q8_report(q_gpu, q_ref, t_exact, scale_per_elem, zp: int, K: int) -> dict:
+    """Acceptance test for int8 codes against the oracle.
+
+    The oracle decides each code from the exact epilogue value; the kernel
+    from its fp32 accumulation, which may differ by about 1e-3*sqrt(K) in
+    absolute terms and 2^-16 relative (the bf16 tolerance's fp32 error
+    model).  So a code must equal the oracle's exactly unless the oracle's
+    exact t = y*scale + zp lies within
+        delta = |scale|*1e-3*sqrt(K) + 2^-16*|t - zp| + 2^-22*|t|
+    of a rounding boundary (a half-integer), where the neighbouring code is
+    also accepted.  Saturated codes have no boundary at the clamp (both
+    sides of +-127.5 / -128.5 give the same code).  A NaN t must give 0.
+    """
+    g = np.asarray(q_gpu, dtype=np.int64).reshape(-1)
+    r = np.asarray(q_ref, dtype=np.int64).reshape(-1)
+    t = np.asarray(t_exact, dtype=np.float64).reshape(-1)
+    s = np.abs(np.asarray(scale_per_elem, dtype=np.float64).reshape(-1))
+    delta = s * 1e-3 * np.sqrt(max(K, 0)) + 2.0 ** -16 * np.abs(t - zp) + 2.0 ** -22 * np.abs(t)
+    frac_dist = np.abs(t - (np.floor(t) + 0.5))
+    near = np.isfinite(t) & (frac_dist <= delta)
+    nan = np.isnan(t)
+    ok = (g == r) | (near & (np.abs(g - r) <= 1))
+    ok &= ~nan | ((g == 0) & (r == 0))
+    bad = np.flatnonzero(~ok)
+    return {"n": int(r.size), "fail": int(bad.size), "first_bad": bad[:8].tolist(),
+            "exact": int(np.count_nonzero(g == r)), "near_boundary": int(np.count_nonzero(near)),
+            "max_code_diff": int(np.abs(g - r).max()) if r.size else 0}
+
+
+def assert_q8_within_tolerance(q_gpu, q_ref, t_exact, scale_per_elem, zp, K, what="") -> dict:
+    rep = q8_report(q_gpu, q_ref, t_exact, scale_per_elem, zp, K)
+    assert rep["fail"] == 0, f"{what}: {rep['fail']} of {rep['n']} int8 codes outside tolerance: {rep}"
+    return rep
