@@ -20,9 +20,12 @@ struct ShapeM { static constexpr int BM = 128, BN = 128, BK = 64; };
 // a ring of five 32 KiB single-operand units.
 struct ShapeRing { static constexpr int BM = 256, BN = 256, BK = 64; };
 
-// Short-and-wide products (M = 64 or 32): one workgroup per 32-column strip
-// streams B once, K-slices of 256.
-struct ShapeSkinny { static constexpr int BN = 32, KS = 256; };
+// Short-and-wide products (at most 64 rows): one workgroup per strip of 32,
+// 64 or 128 columns and range of K (split-K) streams B once; K-slices of 256
+// for 32-column strips, 128 for the wider ones.
+struct ShapeSkinny { static constexpr int KS_N32 = 256, KS_WIDE = 128; };
+
+struct SkinnyWork;
 
 hipError_t launch_tile_large(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_medium(const GemmArgs &args, int cus, hipStream_t stream);
@@ -30,7 +33,8 @@ hipError_t launch_tile_ring_mfma32(const GemmArgs &args, int cus, hipStream_t st
 hipError_t launch_tile_ring(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_ring_masked(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_ring_q8(const GemmArgs &args, int cus, hipStream_t stream);
-hipError_t launch_skinny_m64(const GemmArgs &args, int cus, hipStream_t stream);
-hipError_t launch_skinny_m32(const GemmArgs &args, int cus, hipStream_t stream);
+// rows: 32 or 64 (the kernel's row block, M <= rows); cols: strip width
+hipError_t launch_skinny(int rows, int cols, const GemmArgs &args, const SkinnyWork &work, int cus,
+                         hipStream_t stream);
 
 }  // namespace gb

@@ -8,19 +8,23 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "configs.h"
 #include "device_common.h"
 #include "kernel_generic.h"
+#include "kernel_skinny.h"
 
 namespace gb {
 
 enum KernelKind {
-    kNone = 0, kLarge, kMedium, kSkinny64, kSkinny32, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kNumKinds
+    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kNumKinds
 };
 
 static const char *const kKindNames[kNumKinds] = {"none",            "tile256x256x32_s5", "tile128x128x64_s4",
-                                                  "skinny64x32x256", "skinny32x32x256",   "generic64x64x32",
+                                                  "skinny",          "generic64x64x32",
                                                   "ring256x256x64_mfma32", "ring256x256x64",
                                                   "ring256x256x64_masked", "ring256x256x64_q8"};
 
@@ -110,15 +114,118 @@ static bool ring_masked_ok(int64_t M, int64_t N, int64_t K, const void *A, int64
     return tiles < lim;
 }
 
-static bool skinny_path_ok(int rows, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+// The streaming kernel for short products: 1 <= M <= 64, K a multiple of 8,
+// lda and ldb multiples of 8, A and B 16-byte aligned (C may have any ldc:
+// its accesses go element by element unless C is aligned and ldc % 8 == 0),
+// 32-bit buffer offsets within a strip's rows (strips are at most 128
+// columns).
+static bool skinny_path_ok(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
                            int64_t ldb, const void *C, int64_t ldc) {
-    if (M != rows || K <= 0 || N % ShapeSkinny::BN || K % ShapeSkinny::KS) return false;
-    if (lda % 8 || ldb % 8 || ldc % 8) return false;
-    if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return false;
+    (void)C;
+    (void)ldc;
+    if (M <= 0 || M > 64 || N <= 0 || K <= 0 || K % 8) return false;
+    if (lda % 8 || ldb % 8) return false;
+    if (!aligned16(A) || !aligned16(B)) return false;
     const int64_t lim = (int64_t)1 << 31;
-    if (((rows - 1) * lda + K) * 2 >= lim || ((ShapeSkinny::BN - 1) * ldb + K) * 2 >= lim) return false;
-    if (N / ShapeSkinny::BN >= lim) return false;
+    if ((64 * lda + K + 256) * 2 >= lim || (128 * ldb + K + 256) * 2 >= lim) return false;
+    if (N / 32 + 1 >= lim / 64) return false;
     return true;
+}
+
+// How the streaming kernel covers a short product: its row block (32 or
+// 64), strip width, and the K split.  32-column strips measured fastest at
+// every size tried (the wider ones exist for experiments).  K is split only
+// when the strips alone would leave more than half of the compute units
+// idle: then up to one unit per compute unit, each split keeping at least 4
+// K-slices so the rings have something to overlap.  (At 64 x 1024 x 16384 a
+// split of 8 runs 2.3x faster than none; at 64 x 4096 x 4096, with 128
+// strips, a split of 2 is 10% slower than none.)
+struct SkinnyPlan {
+    int rows, cols, strips, splits, spp;
+};
+
+static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int cus) {
+    SkinnyPlan p{};
+    p.rows = M <= 32 ? 32 : 64;
+    int width = 32;
+    if (const char *env = std::getenv("GEMM_BF16_SKINNY_COLS")) {  // tuning knob: 32, 64 or 128
+        const int w = std::atoi(env);
+        if (w == 32 || w == 64 || w == 128) width = w;
+    }
+    p.cols = width;
+    const int ks = width == 32 ? ShapeSkinny::KS_N32 : ShapeSkinny::KS_WIDE;
+    const int64_t nk = (K + ks - 1) / ks;
+    p.strips = (int)((N + width - 1) / width);
+    int64_t splits = p.strips * 2 >= cus ? 1 : cus / p.strips;
+    if (const char *env = std::getenv("GEMM_BF16_SKINNY_SPLITS")) {  // tuning knob
+        const int s = std::atoi(env);
+        if (s >= 1) splits = s;
+    }
+    const int64_t max_splits = nk / 4 > 1 ? nk / 4 : 1;
+    if (splits > max_splits) splits = max_splits;
+    if (splits < 1) splits = 1;
+    p.spp = (int)((nk + splits - 1) / splits);
+    p.splits = (int)((nk + p.spp - 1) / p.spp);  // no empty split
+    return p;
+}
+
+// Per-(device, stream) workspace of the split-K reductions: one uint32
+// counter per strip (zero at allocation; the last unit of a strip resets its
+// counter) followed by the fp32 partials.  Calls on one stream are ordered,
+// so they can share it; a call on another stream gets its own.  It grows on
+// demand (after draining the stream, whose work may still use the old one)
+// and lives until the process ends.
+struct Workspace {
+    char *base = nullptr;
+    size_t counter_bytes = 0, partial_bytes = 0;
+};
+static std::mutex g_ws_mutex;
+static std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+static hipError_t get_workspace(hipStream_t stream, size_t counters, size_t partial_floats, uint32_t **cnt,
+                                float **partials) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    const size_t need_c = (counters * 4 + 255) / 256 * 256, need_p = partial_floats * 4;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace &w = g_ws[std::make_pair(dev, stream)];
+    if (w.base == nullptr || w.counter_bytes < need_c || w.partial_bytes < need_p) {
+        const size_t nc = need_c > w.counter_bytes ? need_c : w.counter_bytes;
+        const size_t np = need_p > w.partial_bytes ? need_p : w.partial_bytes;
+        if (w.base != nullptr) {
+            if ((err = hipStreamSynchronize(stream)) != hipSuccess) return err;
+            if ((err = hipFree(w.base)) != hipSuccess) return err;
+            w = Workspace{};
+        }
+        char *p = nullptr;
+        if ((err = hipMalloc(&p, nc + np)) != hipSuccess) return err;
+        if ((err = hipMemsetAsync(p, 0, nc, stream)) != hipSuccess) {
+            (void)hipFree(p);
+            return err;
+        }
+        w.base = p;
+        w.counter_bytes = nc;
+        w.partial_bytes = np;
+    }
+    *cnt = reinterpret_cast<uint32_t *>(w.base);
+    *partials = reinterpret_cast<float *>(w.base + w.counter_bytes);
+    return hipSuccess;
+}
+
+static hipError_t launch_skinny_plan(const GemmArgs &args, int cus, hipStream_t stream) {
+    const SkinnyPlan p = plan_skinny(args.M, args.N, args.K, cus);
+    SkinnyWork work{};
+    work.num_strips = p.strips;
+    work.splits = p.splits;
+    work.spp = p.spp;
+    work.c_vector = aligned16(args.C) && args.ldc % 8 == 0;
+    if (p.splits > 1) {
+        const size_t floats = (size_t)p.strips * p.splits * p.cols * p.rows;
+        hipError_t err = get_workspace(stream, (size_t)p.strips, floats, &work.counters, &work.partials);
+        if (err != hipSuccess) return err;
+    }
+    return launch_skinny(p.rows, p.cols, args, work, cus, stream);
 }
 
 // Kernel for a shape.  GEMM_BF16_FORCE_KERNEL=<name> (a kKindNames entry)
@@ -131,8 +238,7 @@ static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t
     const bool okM = tile_path_ok<ShapeM>(M, N, K, A, lda, B, ldb, C, ldc);
     const bool okR = tile_path_ok<ShapeRing>(M, N, K, A, lda, B, ldb, C, ldc);
     const bool okRM = ring_masked_ok(M, N, K, A, lda, B, ldb, C, ldc);
-    const bool okS64 = skinny_path_ok(64, M, N, K, A, lda, B, ldb, C, ldc);
-    const bool okS32 = skinny_path_ok(32, M, N, K, A, lda, B, ldb, C, ldc);
+    const bool okS = skinny_path_ok(M, N, K, A, lda, B, ldb, C, ldc);
     if (const char *force = std::getenv("GEMM_BF16_FORCE_KERNEL")) {
         if (!std::strcmp(force, kKindNames[kGeneric])) return kGeneric;
         if (!std::strcmp(force, kKindNames[kLarge]) && okL) return kLarge;
@@ -140,9 +246,11 @@ static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t
         if (!std::strcmp(force, kKindNames[kRing32]) && okR) return kRing32;
         if (!std::strcmp(force, kKindNames[kRing]) && okR) return kRing;
         if (!std::strcmp(force, kKindNames[kRingMasked]) && okRM) return kRingMasked;
-        if (!std::strcmp(force, kKindNames[kSkinny64]) && okS64) return kSkinny64;
-        if (!std::strcmp(force, kKindNames[kSkinny32]) && okS32) return kSkinny32;
+        if (!std::strcmp(force, kKindNames[kSkinny]) && okS) return kSkinny;
     }
+    // At most 64 rows: the streaming kernel (a 256- or 128-row tile would be
+    // mostly empty).
+    if (okS) return kSkinny;
     // 256x256 tiles when they give at least half the compute units a tile:
     // exact multiples take the unmasked ring kernel, shapes with tails the
     // masked one.
@@ -155,8 +263,6 @@ static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t
         if (tiles * 2 >= cus || !okM) return kLarge;
     }
     if (okM) return kMedium;
-    if (okS64) return kSkinny64;
-    if (okS32) return kSkinny32;
     return kGeneric;
 }
 
@@ -230,8 +336,7 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t lda
     case kRing32: err = launch_tile_ring_mfma32(args, cus, stream); break;
     case kRing: err = launch_tile_ring(args, cus, stream); break;
     case kRingMasked: err = launch_tile_ring_masked(args, cus, stream); break;
-    case kSkinny64: err = launch_skinny_m64(args, cus, stream); break;
-    case kSkinny32: err = launch_skinny_m32(args, cus, stream); break;
+    case kSkinny: err = launch_skinny_plan(args, cus, stream); break;
     default: err = launch_generic(args, cus, stream); break;
     }
     if (err != hipSuccess) {

@@ -1,5 +1,5 @@
-// kernel_skinny.h -- streaming kernel for short-and-wide products (M = 32 or
-// 64 rows of C) whose cost is reading B once from HBM.
+// kernel_skinny.h -- streaming kernel for short-and-wide products (at most 64
+// rows of C) whose cost is reading B once from HBM.
 //
 // With M this small the product is memory-bound: at M = 64, N = K = 8192 the
 // kernel moves 136 MB for 8.6 GFLOP (63 flop/byte, against a machine balance
@@ -7,25 +7,41 @@
 // HBM bandwidth (small M "lacks data reuse, memory loads become the
 // bottleneck" -- DeepGEMM article, demingchina.com, section 5.1; small N is
 // bandwidth-bound in "Outperforming cuBLAS on H100: a worklog", section
-// "Conclusion").
+// "Conclusion").  Decode-sized products (M = 1..16) take the same path.
 //
-// Work split.  One workgroup (four waves) per 32-column strip of C, looping
-// over strips (persistent).  The strip's B columns (K-contiguous) and all of
-// A are walked in K-slices of 256: each slice is DMA-loaded into LDS with
-// coalesced 16 B/lane loads (two 512-byte rows per wave load), and the four
-// waves split the slice's 16 MFMA k-steps, each keeping a private fp32
-// accumulator of the whole 64 x 32 (or 32 x 32) strip.  At the end the four
-// partial strips are summed through LDS and the fused epilogue writes bf16
-// C with 16-byte, column-contiguous stores.
+// Work split.  A work unit is one strip of BN columns of C over one range of
+// K (split-K: the K-slices are divided into `splits` contiguous ranges).
+// One workgroup (four waves) per unit, looping over units (persistent).  The
+// unit's B columns (K-contiguous) and all rows of A are walked in K-slices
+// of KS: each slice is DMA-loaded into LDS with 16 B/lane loads, and the
+// four waves split the slice's MFMA k-steps, each keeping a private fp32
+// accumulator of the whole strip.  The four partial strips are then summed
+// through LDS.  With one split the fused epilogue writes bf16 C directly;
+// otherwise the unit's fp32 partial goes to a workspace and the last unit of
+// the strip to arrive (an atomic counter per strip) adds the partials in
+// split order -- the same order whichever unit is last, so the result is
+// deterministic -- and runs the epilogue.
 //
-// Rings.  A (M x 256 per slice) is re-read from L2 by every strip and
-// arrives quickly, B (32 x 256 per slice) comes from HBM once, so B is
-// prefetched further ahead: A and B rings of SA and SB slices (SA * 32 KiB +
-// SB * 16 KiB <= 160 KiB), with SA-1 and SB-1 slices in flight.
+// Why split K.  Every unit reads all M rows of A for its K range, so without
+// a split each of 256 compute units pulls the whole of A through its load
+// path: at M = 64, N = 8192, K = 8192 that is twice the B traffic per unit,
+// and it (not HBM) is what limits a 32-column strip.  Wider strips with a
+// split keep the unit count while dividing the A traffic per unit.
 //
-// LDS rows are 512 bytes (256 bf16, 32 chunks of 16 B); chunk c of row r is
-// stored at c ^ (r & 15), which makes the 32-row fragment reads hit distinct
-// banks in every 8- and 16-lane group.
+// Tails.  Rows of A past M, columns of B past N and K-chunks past K are
+// loaded from an out-of-range buffer offset, which the DMA turns into zeros
+// (the zero-fill of the DeepGEMM article, sections 4.2-4.3); the epilogue
+// masks its loads and stores.  K must be a multiple of 8 (whole 16-byte
+// chunks).
+//
+// Rings.  A (BMr x KS per slice) is re-read from L2 by every unit and
+// arrives quickly, B (BN x KS per slice) comes from HBM once, so B is
+// prefetched further ahead: rings of SA and SB slices, with SA-1 and SB-1
+// slices in flight.
+//
+// LDS rows are KS*2 bytes; chunk c of row r is stored at c ^ (r & 15) (r & 15
+// limited to the row's chunk count), which keeps the 32-row fragment reads
+// on distinct banks in every 8- and 16-lane group.
 #pragma once
 
 #include "device_common.h"
@@ -33,9 +49,9 @@
 
 namespace gb {
 
-template <int FM_, int SA_ = 3, int SB_ = 4, int FN_ = 1, int KS_ = 256>
+template <int FM_, int FN_ = 1, int KS_ = 256, int SA_ = 3, int SB_ = 4>
 struct SkinnyConfig {
-    static constexpr int FM = FM_;                 // 32-row MFMA blocks: M = 32 * FM
+    static constexpr int FM = FM_;                 // 32-row MFMA blocks: up to 32 * FM rows
     static constexpr int FN = FN_;                 // 32-column MFMA blocks per strip
     static constexpr int BMr = 32 * FM;            // rows of C
     static constexpr int BN = 32 * FN;             // columns per strip
@@ -44,6 +60,7 @@ struct SkinnyConfig {
     static constexpr int kThreads = 256;
     static constexpr int kRowBytes = KS * 2;       // 512 for KS = 256
     static constexpr int kChunks = kRowBytes / 16; // 16-byte chunks per row
+    static constexpr int kSwzMask = kChunks >= 16 ? 15 : kChunks - 1;
     static constexpr int kRowsPerLoad = 1024 / kRowBytes;
     static constexpr int kABytes = BMr * kRowBytes;
     static constexpr int kBBytes = BN * kRowBytes;
@@ -52,22 +69,41 @@ struct SkinnyConfig {
     static constexpr int kALoads = BMr / kRowsPerLoad / kWaves;  // 1 KiB wave loads
     static constexpr int kBLoads = BN / kRowsPerLoad / kWaves;
     static constexpr int kStepsPerWave = KS / 16 / kWaves;
-    static_assert(FM == 1 || FM == 2, "32 or 64 rows");
+    // partial-sum staging: fp32, column-major, columns padded by 16 bytes
+    static constexpr int kColBytes = BMr * 4 + 16;
+    static constexpr int kPartBytes = BN * kColBytes;
+    static constexpr int kFlagOffset = kLdsBytes - 16;  // the "last unit" flag word
+    static_assert(FM == 1 || FM == 2, "up to 32 or 64 rows");
+    static_assert(FN == 1 || FN == 2 || FN == 4, "strips of 32, 64 or 128 columns");
     static_assert(KS == 128 || KS == 256, "rows of 256 or 512 bytes");
     static_assert(BMr % (kRowsPerLoad * kWaves) == 0 && BN % (kRowsPerLoad * kWaves) == 0, "loads split");
     static_assert((KS / 16) % kWaves == 0, "k-steps split over the waves");
     static_assert(kLdsBytes <= 160 * 1024, "gfx950 has 160 KiB of LDS per compute unit");
     static_assert(SA >= 2 && SB > SA, "B is prefetched further ahead than A");
     static_assert((SA - 1) * kALoads + (SB - 1) * kBLoads < 64, "vmcnt is a 6-bit counter");
-    static_assert(kWaves * BMr * BN * 4 <= kLdsBytes, "partial sums reuse the rings");
+    static_assert(kWaves * kPartBytes + 16 <= kLdsBytes, "partial sums and the flag reuse the rings");
 };
 
-// Requirements checked by the host: M == 32 * FM, N % 32 == 0, K % 256 == 0,
-// K > 0, A/B/C 16-byte aligned, lda/ldb/ldc multiples of 8, and the byte
-// offsets of one strip ((BMr-1)*lda + K, (BN-1)*ldb + K, times 2) below 2^31.
+// The unit decomposition and the split-K workspace (unused with splits == 1):
+// partials[unit * BN * BMr + col * BMr + row] in fp32 (unit = strip * splits
+// + split) and one uint32 counter per strip, zero between calls.
+struct SkinnyWork {
+    int num_strips;
+    int splits;
+    int spp;       // K-slices per split (the last split may have fewer)
+    int c_vector;  // C 16-byte aligned and ldc % 8 == 0: 8-row chunks move as one 16-byte access
+    float *partials;
+    uint32_t *counters;
+};
+
+// Requirements checked by the host: 1 <= M <= BMr, N >= 1, K >= 8 and
+// K % 8 == 0, A/B 16-byte aligned, lda/ldb multiples of 8 (C: any ldc >= M,
+// element-wise accesses unless work.c_vector), the byte
+// offsets of one unit ((BMr-1)*lda + K + KS, (BN-1)*ldb + K + KS, times 2)
+// below 2^31, and every split owning at least one K-slice.
 template <class Cfg, uint32_t kFlags>
 __global__ void __launch_bounds__(Cfg::kThreads)
-gemm_skinny_kernel(const GemmArgs args, int num_strips) {
+gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
     __shared__ __attribute__((aligned(1024))) char smem[Cfg::kLdsBytes];
     char *const ringA = smem;
     char *const ringB = smem + Cfg::SA * Cfg::kABytes;
@@ -76,43 +112,92 @@ gemm_skinny_kernel(const GemmArgs args, int num_strips) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lda_bytes = (uint32_t)args.lda * 2u, ldb_bytes = (uint32_t)args.ldb * 2u;
 
-    // Load side: a wave load covers rows 2q, 2q+1; lane i takes row 2q + i/32
-    // and LDS chunk position i%32, holding logical chunk (i%32) ^ (row & 15).
-    // row & 15 = (2q & 15) + i/32: fold the q-part into a per-load XOR.
+    // Load side: a wave load covers rows kRowsPerLoad*q ..; lane i takes row
+    // kRowsPerLoad*q + i/kChunks and LDS chunk position i%kChunks, holding
+    // logical chunk (i%kChunks) ^ (row & kSwzMask).
     const int lrow = lane / Cfg::kChunks, lpos = lane % Cfg::kChunks;
     // Fragment side: lane l reads row l%32 (+32i) at logical chunk 2s + l/32.
     const uint32_t fragRow = (uint32_t)(lane & 31) * Cfg::kRowBytes;
-    const int fragSw = lane & 15 & (Cfg::kChunks - 1);
+    const int fragSw = lane & Cfg::kSwzMask;
 
-    const int nk = (int)(args.K / Cfg::KS);
-
-    for (int strip = blockIdx.x; strip < num_strips; strip += gridDim.x) {
-        const int64_t n0 = (int64_t)strip * Cfg::BN;
-        const __amdgpu_buffer_rsrc_t rA = make_rsrc(args.A, (uint32_t)(((Cfg::BMr - 1) * args.lda + args.K) * 2));
-        const __amdgpu_buffer_rsrc_t rB =
-            make_rsrc(args.B + n0 * args.ldb, (uint32_t)(((Cfg::BN - 1) * args.ldb + args.K) * 2));
-
-        // Slice j of this strip's order (K-slice ks) into its ring buffer.
-        auto issueA = [&](int j, int ks) {
-            char *dst = ringA + (j % Cfg::SA) * Cfg::kABytes;
+    // Per-lane row, chunk and byte offset (row * ld + chunk * 16) of each of
+    // this wave's loads -- the same for every slice and unit, so a load only
+    // adds the slice's K offset (one scalar).
+    int rA_[Cfg::kALoads], rB_[Cfg::kBLoads], cA[Cfg::kALoads], cB[Cfg::kBLoads];
+    uint32_t vA[Cfg::kALoads], vB[Cfg::kBLoads];
 #pragma unroll
-            for (int j = 0; j < Cfg::kALoads; ++j) {
-                const int q = wave * Cfg::kALoads + j;
-                const int row = Cfg::kRowsPerLoad * q + lrow;
-                const uint32_t chunk = (uint32_t)(lpos ^ (row & 15 & (Cfg::kChunks - 1)));
-                buffer_load_lds16(rA, (GB_LDS void *)(dst + q * 1024), lrow * lda_bytes + chunk * 16,
-                                  (uint32_t)(Cfg::kRowsPerLoad * q) * lda_bytes + (uint32_t)ks * Cfg::kRowBytes);
+    for (int i = 0; i < Cfg::kALoads; ++i) {
+        rA_[i] = Cfg::kRowsPerLoad * (wave * Cfg::kALoads + i) + lrow;
+        cA[i] = lpos ^ (rA_[i] & Cfg::kSwzMask);
+        vA[i] = (uint32_t)rA_[i] * lda_bytes + (uint32_t)cA[i] * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg::kBLoads; ++i) {
+        rB_[i] = Cfg::kRowsPerLoad * (wave * Cfg::kBLoads + i) + lrow;
+        cB[i] = lpos ^ (rB_[i] & Cfg::kSwzMask);
+        vB[i] = (uint32_t)rB_[i] * ldb_bytes + (uint32_t)cB[i] * 16;
+    }
+
+    const int nk = (int)((args.K + Cfg::KS - 1) / Cfg::KS);
+    const int rowsA = (int)(args.M < Cfg::BMr ? args.M : Cfg::BMr);
+    const int kmax = (int)args.K;
+    const int num_units = work.num_strips * work.splits;
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(args.A, (uint32_t)(((rowsA - 1) * args.lda + args.K) * 2));
+
+    for (int unit = blockIdx.x; unit < num_units; unit += gridDim.x) {
+        const int strip = unit / work.splits;
+        const int split = unit % work.splits;
+        const int64_t n0 = (int64_t)strip * Cfg::BN;
+        const int colsB = (int)(args.N - n0 < Cfg::BN ? args.N - n0 : Cfg::BN);
+        const int s0 = split * work.spp;
+        const int ns = (nk - s0 < work.spp ? nk - s0 : work.spp);  // >= 1, checked by the host
+        const __amdgpu_buffer_rsrc_t rB =
+            make_rsrc(args.B + n0 * args.ldb, (uint32_t)(((colsB - 1) * args.ldb + args.K) * 2));
+
+        // Slice j of this unit's order into its ring buffer.  Slices are
+        // issued in order (A and B each), walking the unit's K range from a
+        // rotated start (strip index within its XCD, so the workgroups
+        // sharing an L2 do not all request the same A lines at once).  A
+        // chunk outside the matrix (row past M or N, k past K) is loaded from
+        // the out-of-range offset; slices of full strips take a branch-free
+        // path.
+        const bool allA = rowsA == Cfg::BMr, allB = colsB == Cfg::BN;
+        const int s_end = s0 + ns;
+        int ksA = s0 + (strip / kNumXcds) % ns, ksB = ksA;
+        auto issueA = [&](int j) {
+            char *dst = ringA + (j % Cfg::SA) * Cfg::kABytes;
+            const int ks = ksA;
+            ksA = ksA + 1 == s_end ? s0 : ksA + 1;
+            const uint32_t soff = (uint32_t)ks * Cfg::kRowBytes;
+            if (allA && (ks + 1) * Cfg::KS <= kmax) {
+#pragma unroll
+                for (int i = 0; i < Cfg::kALoads; ++i)
+                    buffer_load_lds16(rA, (GB_LDS void *)(dst + (wave * Cfg::kALoads + i) * 1024), vA[i], soff);
+            } else {
+#pragma unroll
+                for (int i = 0; i < Cfg::kALoads; ++i) {
+                    const bool ok = rA_[i] < rowsA && ks * Cfg::KS + cA[i] * 8 < kmax;
+                    buffer_load_lds16(rA, (GB_LDS void *)(dst + (wave * Cfg::kALoads + i) * 1024),
+                                      ok ? vA[i] : kOobOffset, soff);
+                }
             }
         };
-        auto issueB = [&](int j, int ks) {
+        auto issueB = [&](int j) {
             char *dst = ringB + (j % Cfg::SB) * Cfg::kBBytes;
+            const int ks = ksB;
+            ksB = ksB + 1 == s_end ? s0 : ksB + 1;
+            const uint32_t soff = (uint32_t)ks * Cfg::kRowBytes;
+            if (allB && (ks + 1) * Cfg::KS <= kmax) {
 #pragma unroll
-            for (int j = 0; j < Cfg::kBLoads; ++j) {
-                const int q = wave * Cfg::kBLoads + j;
-                const int row = Cfg::kRowsPerLoad * q + lrow;
-                const uint32_t chunk = (uint32_t)(lpos ^ (row & 15 & (Cfg::kChunks - 1)));
-                buffer_load_lds16(rB, (GB_LDS void *)(dst + q * 1024), lrow * ldb_bytes + chunk * 16,
-                                  (uint32_t)(Cfg::kRowsPerLoad * q) * ldb_bytes + (uint32_t)ks * Cfg::kRowBytes);
+                for (int i = 0; i < Cfg::kBLoads; ++i)
+                    buffer_load_lds16(rB, (GB_LDS void *)(dst + (wave * Cfg::kBLoads + i) * 1024), vB[i], soff);
+            } else {
+#pragma unroll
+                for (int i = 0; i < Cfg::kBLoads; ++i) {
+                    const bool ok = rB_[i] < colsB && ks * Cfg::KS + cB[i] * 8 < kmax;
+                    buffer_load_lds16(rB, (GB_LDS void *)(dst + (wave * Cfg::kBLoads + i) * 1024),
+                                      ok ? vB[i] : kOobOffset, soff);
+                }
             }
         };
 
@@ -122,36 +207,31 @@ gemm_skinny_kernel(const GemmArgs args, int num_strips) {
 #pragma unroll
             for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = f32x16{};
 
-        // Previous strip's partial-sum reduction is done with LDS.
+        // Previous unit's partial-sum reduction is done with LDS.
         lds_barrier();
-        // Slice order: strips start at different K-slices (rotation by the
-        // strip's index within its XCD), so the workgroups sharing an L2 do
-        // not all request the same A lines at the same moment.
-        const int rot = (strip / kNumXcds) % nk;
-        auto slice_of = [&](int j) { return (j + rot) % nk; };
         // Prologue: the steady state issues A(j + SA-1), then B(j + SB-1), at
         // slice j's barrier; the prologue replays that order for the virtual
         // barriers j = -(SB-1) .. -1, leaving A(0 .. SA-2) and B(0 .. SB-2)
         // in flight.
         for (int j = -(Cfg::SB - 1); j < 0; ++j) {
             const int a = j + Cfg::SA - 1, b = j + Cfg::SB - 1;
-            if (a >= 0 && a < nk) issueA(a, slice_of(a));
-            if (b < nk) issueB(b, slice_of(b));
+            if (a >= 0 && a < ns) issueA(a);
+            if (b < ns) issueB(b);
         }
 
-        for (int kt = 0; kt < nk; ++kt) {
+        for (int kt = 0; kt < ns; ++kt) {
             // Slice kt's A and B have landed once only the loads issued after
             // A(kt) are outstanding (B(kt) went out before A(kt) since SB >
             // SA): when every slice up to kt+SB-2 exists these are A(kt+1 ..
-            // kt+SA-2) and B(kt+SB-SA .. kt+SB-2); near the end of K the
-            // pipeline simply drains.
-            if (kt + Cfg::SB - 1 <= nk)
+            // kt+SA-2) and B(kt+SB-SA .. kt+SB-2); near the end of the range
+            // the pipeline simply drains.
+            if (kt + Cfg::SB - 1 <= ns)
                 wait_vmcnt<(Cfg::SA - 2) * Cfg::kALoads + (Cfg::SA - 1) * Cfg::kBLoads>();
             else
                 wait_vmcnt<0>();
             lds_barrier();  // everyone's loads landed; slice kt-1 fully read
-            if (kt + Cfg::SA - 1 < nk) issueA(kt + Cfg::SA - 1, slice_of(kt + Cfg::SA - 1));
-            if (kt + Cfg::SB - 1 < nk) issueB(kt + Cfg::SB - 1, slice_of(kt + Cfg::SB - 1));
+            if (kt + Cfg::SA - 1 < ns) issueA(kt + Cfg::SA - 1);
+            if (kt + Cfg::SB - 1 < ns) issueB(kt + Cfg::SB - 1);
 
             const char *sA = ringA + (kt % Cfg::SA) * Cfg::kABytes;
             const char *sB = ringB + (kt % Cfg::SB) * Cfg::kBBytes;
@@ -176,11 +256,8 @@ gemm_skinny_kernel(const GemmArgs args, int num_strips) {
         // fp32, column-major (column stride BMr*4 + 16 bytes), then each lane
         // sums 8 consecutive rows of one column over the four copies.
         lds_barrier();
-        constexpr int kColBytes = Cfg::BMr * 4 + 16;
-        constexpr int kPartBytes = Cfg::BN * kColBytes;
-        static_assert(Cfg::kWaves * kPartBytes <= Cfg::kLdsBytes, "partials fit");
         {
-            char *part = smem + wave * kPartBytes;
+            char *part = smem + wave * Cfg::kPartBytes;
             const int h = lane >> 5;
 #pragma unroll
             for (int j = 0; j < Cfg::FN; ++j)
@@ -190,36 +267,50 @@ gemm_skinny_kernel(const GemmArgs args, int num_strips) {
                     for (int g = 0; g < 4; ++g) {
                         const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                                          acc[i][j][4 * g + 3]};
-                        *(GB_LDS f32x4 *)(part + (j * 32 + (lane & 31)) * kColBytes + (i * 32 + g * 8 + h * 4) * 4) =
-                            v;
+                        *(GB_LDS f32x4 *)(part + (j * 32 + (lane & 31)) * Cfg::kColBytes +
+                                          (i * 32 + g * 8 + h * 4) * 4) = v;
                     }
         }
         lds_barrier();
         constexpr int kChunksPerCol = Cfg::BMr / 8;
         constexpr int kChunks = Cfg::BN * kChunksPerCol;  // 8-row pieces of the strip
-        for (int idx = threadIdx.x; idx < kChunks; idx += Cfg::kThreads) {
+
+        // The four waves' sum of one 8-row chunk (column idx / kChunksPerCol).
+        auto wave_sum = [&](int idx, float (&x)[8]) {
             const int col = idx / kChunksPerCol, q = idx % kChunksPerCol;
-            float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = 0.f;
 #pragma unroll
             for (int w = 0; w < Cfg::kWaves; ++w) {
-                const char *p = smem + w * kPartBytes + col * kColBytes + q * 32;
+                const char *p = smem + w * Cfg::kPartBytes + col * Cfg::kColBytes + q * 32;
                 const f32x4 lo = *(const GB_LDS f32x4 *)p;
                 const f32x4 hi = *(const GB_LDS f32x4 *)(p + 16);
                 x[0] += lo.x; x[1] += lo.y; x[2] += lo.z; x[3] += lo.w;
                 x[4] += hi.x; x[5] += hi.y; x[6] += hi.z; x[7] += hi.w;
             }
+        };
+        // The fused epilogue on one 8-row chunk of the strip's sum x: bf16 C
+        // with a 16-byte store, element by element where the chunk straddles M.
+        auto finish = [&](int idx, const float (&x)[8]) {
+            const int col = idx / kChunksPerCol, q = idx % kChunksPerCol;
             const int64_t n = n0 + col;
             const int64_t m = (int64_t)q * 8;
+            if (n >= args.N || m >= args.M) return;
             uint16_t *cp = args.C + n * args.ldc + m;
+            const bool full = m + 8 <= args.M && work.c_vector;
             float bias_v = 0.f;
             if constexpr ((kFlags & kEpiBias) != 0) bias_v = bf16_bits_to_f32(args.bias[n]);
             float cin[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             if constexpr ((kFlags & kEpiBeta) != 0) {
-                const u32x4 raw = *(const u32x4 *)cp;
+                if (full) {
+                    const u32x4 raw = *(const u32x4 *)cp;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    cin[2 * e] = bf16_bits_to_f32(raw[e] & 0xFFFFu);
-                    cin[2 * e + 1] = bf16_bits_to_f32(raw[e] >> 16);
+                    for (int e = 0; e < 4; ++e) {
+                        cin[2 * e] = bf16_bits_to_f32(raw[e] & 0xFFFFu);
+                        cin[2 * e + 1] = bf16_bits_to_f32(raw[e] >> 16);
+                    }
+                } else {
+                    for (int e = 0; e < 8 && m + e < args.M; ++e) cin[e] = bf16_bits_to_f32(cp[e]);
                 }
             }
             u32x4 out;
@@ -228,18 +319,79 @@ gemm_skinny_kernel(const GemmArgs args, int num_strips) {
                 out[e] = pack_bf16x2(epilogue_value<kFlags>(x[2 * e], cin[2 * e], bias_v, args.alpha, args.beta),
                                      epilogue_value<kFlags>(x[2 * e + 1], cin[2 * e + 1], bias_v, args.alpha,
                                                             args.beta));
-            __builtin_nontemporal_store(out, (u32x4 *)cp);
+            if (full) {
+                __builtin_nontemporal_store(out, (u32x4 *)cp);
+            } else {
+                for (int e = 0; e < 8 && m + e < args.M; ++e) cp[e] = (uint16_t)(out[e >> 1] >> ((e & 1) * 16));
+            }
+        };
+
+        if (work.splits == 1) {
+            for (int idx = threadIdx.x; idx < kChunks; idx += Cfg::kThreads) {
+                float x[8];
+                wave_sum(idx, x);
+                finish(idx, x);
+            }
+            continue;
         }
+
+        // Split K: publish this unit's partial, then count arrivals per
+        // strip.  The XCDs' L2 caches are not coherent with each other, and a
+        // cache-wide write-back / invalidate (an agent-scope fence) costs
+        // tens of microseconds when every unit issues one.  The partials are
+        // small, so they move through agent-scope atomic read-modify-writes
+        // instead, which the hardware performs coherently for the whole
+        // device (as it does the arrival counter): each unit swaps its values
+        // in, waits for those atomics to complete, then counts; the last unit
+        // reads every partial back with an atomic OR of 0.
+        unsigned long long *mine =
+            (unsigned long long *)(work.partials + (int64_t)unit * (Cfg::BN * Cfg::BMr));
+        for (int idx = threadIdx.x; idx < kChunks; idx += Cfg::kThreads) {
+            float x[8];
+            wave_sum(idx, x);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const unsigned long long bits = (unsigned long long)__builtin_bit_cast(uint32_t, x[2 * e]) |
+                                                ((unsigned long long)__builtin_bit_cast(uint32_t, x[2 * e + 1]) << 32);
+                __hip_atomic_exchange(mine + idx * 4 + e, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        wait_vmcnt<0>();
+        __syncthreads();
+        uint32_t *flag = (uint32_t *)(smem + Cfg::kFlagOffset);
+        if (threadIdx.x == 0)
+            *flag = atomicAdd(work.counters + strip, 1u) == (uint32_t)(work.splits - 1) ? 1u : 0u;
+        __syncthreads();
+        const bool last = *flag != 0u;
+        if (!last) continue;
+        unsigned long long *base =
+            (unsigned long long *)(work.partials + (int64_t)strip * work.splits * (Cfg::BN * Cfg::BMr));
+        for (int idx = threadIdx.x; idx < kChunks; idx += Cfg::kThreads) {
+            float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int sp = 0; sp < work.splits; ++sp) {  // split order: the same sum whoever is last
+                unsigned long long *src = base + (int64_t)sp * (Cfg::BN * Cfg::BMr / 2) + idx * 4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const unsigned long long bits =
+                        __hip_atomic_fetch_or(src + e, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    x[2 * e] += __builtin_bit_cast(float, (uint32_t)bits);
+                    x[2 * e + 1] += __builtin_bit_cast(float, (uint32_t)(bits >> 32));
+                }
+            }
+            finish(idx, x);
+        }
+        // ready for the next call on this workspace (an atomic, like the adds)
+        if (threadIdx.x == 0) atomicExch(work.counters + strip, 0u);
     }
 }
 
-// One workgroup per compute unit (at most one per strip).
+// One workgroup per compute unit (at most one per work unit).
 template <class Cfg>
-hipError_t launch_skinny(const GemmArgs &args, int cus, hipStream_t stream) {
-    const int strips = (int)(args.N / Cfg::BN);
-    const dim3 grid(strips < cus ? strips : cus), block(Cfg::kThreads);
+hipError_t launch_skinny(const GemmArgs &args, const SkinnyWork &work, int cus, hipStream_t stream) {
+    const int units = work.num_strips * work.splits;
+    const dim3 grid(units < cus ? units : cus), block(Cfg::kThreads);
     dispatch_flags(args.flags, [&](auto f) {
-        hipLaunchKernelGGL((gemm_skinny_kernel<Cfg, decltype(f)::value>), grid, block, 0, stream, args, strips);
+        hipLaunchKernelGGL((gemm_skinny_kernel<Cfg, decltype(f)::value>), grid, block, 0, stream, args, work);
     });
     return hipGetLastError();
 }

@@ -1,17 +1,33 @@
-// tile_skinny.hip -- instances of the streaming kernel for M = 64 and M = 32
-// (32-column strips, K-slices of 256, A/B rings of 3/4 slices; wider strips
-// and shorter slices measured slower on the 64 x 8192 x 8192 product).
+// tile_skinny.hip -- instances of the streaming kernel for at most 64 rows:
+// 32-column strips with K-slices of 256 in A/B rings of 3/4 slices, and 64-
+// or 128-column strips (for split-K) with K-slices of 128.
 #include "configs.h"
 #include "kernel_skinny.h"
 
 namespace gb {
 
-hipError_t launch_skinny_m64(const GemmArgs &args, int cus, hipStream_t stream) {
-    return launch_skinny<SkinnyConfig<2>>(args, cus, stream);
-}
+using SkinnyM64N32 = SkinnyConfig<2, 1, 256, 3, 4>;
+using SkinnyM64N64 = SkinnyConfig<2, 2, 128, 3, 7>;
+using SkinnyM64N128 = SkinnyConfig<2, 4, 128, 2, 4>;
+using SkinnyM32N32 = SkinnyConfig<1, 1, 256, 3, 6>;
+using SkinnyM32N64 = SkinnyConfig<1, 2, 128, 3, 8>;
+using SkinnyM32N128 = SkinnyConfig<1, 4, 128, 2, 4>;
 
-hipError_t launch_skinny_m32(const GemmArgs &args, int cus, hipStream_t stream) {
-    return launch_skinny<SkinnyConfig<1>>(args, cus, stream);
+static_assert(SkinnyM64N32::KS == ShapeSkinny::KS_N32 && SkinnyM64N64::KS == ShapeSkinny::KS_WIDE &&
+                  SkinnyM64N128::KS == ShapeSkinny::KS_WIDE && SkinnyM32N32::KS == ShapeSkinny::KS_N32 &&
+                  SkinnyM32N64::KS == ShapeSkinny::KS_WIDE && SkinnyM32N128::KS == ShapeSkinny::KS_WIDE,
+              "the host plans splits with these slice lengths");
+
+hipError_t launch_skinny(int rows, int cols, const GemmArgs &args, const SkinnyWork &work, int cus,
+                         hipStream_t stream) {
+    if (rows == 64) {
+        if (cols == 32) return launch_skinny<SkinnyM64N32>(args, work, cus, stream);
+        if (cols == 64) return launch_skinny<SkinnyM64N64>(args, work, cus, stream);
+        return launch_skinny<SkinnyM64N128>(args, work, cus, stream);
+    }
+    if (cols == 32) return launch_skinny<SkinnyM32N32>(args, work, cus, stream);
+    if (cols == 64) return launch_skinny<SkinnyM32N64>(args, work, cus, stream);
+    return launch_skinny<SkinnyM32N128>(args, work, cus, stream);
 }
 
 }  // namespace gb

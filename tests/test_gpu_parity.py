@@ -219,21 +219,83 @@ def test_masked_ring_is_the_default_for_large_ragged_shapes():
                expect_kernel=MASKED)
 
 
-# The streaming kernel for M = 64 / 32: slice counts through its ring
-# prologue and tail (1 .. 10 slices of 256), epilogue combinations, padding.
+# The streaming kernel for at most 64 rows: slice counts through its ring
+# prologue and tail, every strip width, K splits (the split-K reduction),
+# row / column / K tails, epilogue combinations, padding.
+SK = "skinny"
+
+
 @pytest.mark.parametrize("M", [64, 32])
 @pytest.mark.parametrize("K", [256, 512, 768, 1024, 1280, 2560])
-def test_skinny_slice_counts(M, K):
-    check_full(f"skinny M={M} K={K}", M, 1024, K, seed=M + K, expect_kernel=f"skinny{M}x32x256")
+def test_skinny_slice_counts(M, K, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_SKINNY_SPLITS", "1")
+    check_full(f"skinny M={M} K={K}", M, 1024, K, seed=M + K, expect_kernel=SK)
+
+
+@pytest.mark.parametrize("cols", ["32", "64", "128"])
+@pytest.mark.parametrize("splits", ["1", "2", "3", "7"])
+def test_skinny_widths_and_splits(cols, splits, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_SKINNY_COLS", cols)
+    monkeypatch.setenv("GEMM_BF16_SKINNY_SPLITS", splits)
+    check_full(f"skinny cols={cols} splits={splits}", 64, 1024, 4096, beta=0.5, use_bias=True, epilogue="gelu_tanh",
+               seed=int(cols) + int(splits), expect_kernel=SK)
+    check_full(f"skinny M=32 cols={cols} splits={splits}", 32, 512, 2048, seed=3 * int(cols) + int(splits),
+               expect_kernel=SK)
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc", [
+    (1, 4096, 4096, 4096, 4096, 8),      # decode: one row
+    (7, 1000, 1032, 1032, 1040, 8),      # 7 rows, N and K tails
+    (16, 333, 8, 8, 8, 16),              # a single 8-wide K chunk
+    (33, 96, 520, 528, 520, 40),         # just over one 32-row block
+    (48, 4096, 1024, 1024, 1024, 48),
+    (63, 129, 4104, 4104, 4112, 64),     # every tail at once
+    (64, 1, 256, 256, 256, 64),          # one column
+    (1, 4096, 4096, 4096, 4096, 1),      # decode with the natural ldc = 1
+    (7, 512, 2048, 2048, 2048, 7),       # ldc not a multiple of 8
+    (12, 300, 1024, 1024, 1032, 13),
+])
+@pytest.mark.parametrize("splits", ["1", "3"])
+def test_skinny_tails(M, N, K, lda, ldb, ldc, splits, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_SKINNY_SPLITS", splits)
+    check_full(f"skinny tails {M}x{N}x{K} splits={splits}", M, N, K, lda=lda, ldb=ldb, ldc=ldc, beta=0.0,
+               seed=M + N + K, expect_kernel=SK, poison_pad=True)
+
+
+def test_skinny_unaligned_c_with_beta():
+    check_full("skinny unaligned C", 40, 1000, 1024, ldc=41, beta=-0.5, use_bias=True, epilogue="relu",
+               offsets=(0, 0, 3), seed=92, expect_kernel=SK)
 
 
 @pytest.mark.parametrize("beta,use_bias,epi", [(0.5, True, "gelu_tanh"), (0.0, True, "none"),
                                                (-1.0, False, "gelu_tanh"), (0.25, True, "relu")])
-def test_skinny_epilogues_and_padding(beta, use_bias, epi):
-    check_full(f"skinny epilogue beta={beta} bias={use_bias} {epi}", 64, 2048, 512, alpha=0.5, beta=beta,
-               use_bias=use_bias, epilogue=epi, seed=41, expect_kernel="skinny64x32x256")
-    check_full("skinny padded", 64, 512, 768, lda=776, ldb=1024, ldc=72, beta=beta, use_bias=use_bias,
-               epilogue=epi, seed=42, expect_kernel="skinny64x32x256")
+@pytest.mark.parametrize("splits", ["1", "4"])
+def test_skinny_epilogues_and_padding(beta, use_bias, epi, splits, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_SKINNY_SPLITS", splits)
+    check_full(f"skinny epilogue beta={beta} bias={use_bias} {epi}", 64, 2048, 4096, alpha=0.5, beta=beta,
+               use_bias=use_bias, epilogue=epi, seed=41, expect_kernel=SK)
+    check_full("skinny padded", 61, 512, 4096, lda=4104, ldb=4160, ldc=72, beta=beta, use_bias=use_bias,
+               epilogue=epi, seed=42, expect_kernel=SK, poison_pad=True)
+
+
+def test_skinny_split_k_is_deterministic_across_launches(monkeypatch):
+    """Split-K: the last unit adds the partials in split order, whichever
+    unit arrives last, and resets the strip counters -- repeated launches on
+    one stream are bit-identical and match the unsplit kernel within the
+    tolerance."""
+    M, N, K = 64, 2048, 8192
+    case = inputs.random_case(91, M, N, K)
+    C_init = np.zeros(M * N, np.uint16)
+    monkeypatch.setenv("GEMM_BF16_SKINNY_COLS", "64")
+    monkeypatch.setenv("GEMM_BF16_SKINNY_SPLITS", "8")
+    runs = [run_gpu(M, N, K, case["A"], K, case["B"], K, C_init, M, 1.0, 0.0, None, "none") for _ in range(4)]
+    for r in runs[1:]:
+        assert np.array_equal(runs[0], r)
+    monkeypatch.setenv("GEMM_BF16_SKINNY_SPLITS", "1")
+    single = run_gpu(M, N, K, case["A"], K, case["B"], K, C_init, M, 1.0, 0.0, None, "none")
+    assert_within_tolerance(runs[0], single, K, "split vs unsplit")
+    ref = oracle.gemm(M, N, K, case["A"], K, case["B"], K, nthreads=_threads())
+    assert_within_tolerance(runs[0], ref, K, "split vs oracle")
 
 
 # ---------------------------------------------------- bounds-checked path ---
@@ -242,7 +304,9 @@ def test_skinny_epilogues_and_padding(beta, use_bias, epi):
     (1, 1, 1), (33, 65, 97), (257, 257, 257), (1000, 1000, 1000), (64, 64, 4097), (1, 4096, 512),
     (300, 1, 70), (130, 70, 8),
 ])
-def test_generic_ragged_full(M, N, K):
+def test_generic_ragged_full(M, N, K, monkeypatch):
+    # forced: some of these shapes have a fast path (1 x 4096 x 512 streams)
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", "generic64x64x32")
     check_full(f"generic {M}x{N}x{K}", M, N, K, seed=3 * M + N + K, expect_kernel="generic64x64x32")
 
 
