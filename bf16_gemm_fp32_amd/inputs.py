@@ -15,7 +15,11 @@ section "Experimental setup"):
 * buffers are filled in storage order: A as M rows of K (row-major), B as N
   columns of K (column-major), C0 as N columns of M (column-major);
 * int8-output workloads also draw one float32 scale per row (operand j = 5),
-  uniform in [lo, hi), and use a fixed zero point.
+  uniform in [lo, hi), and use a fixed zero point;
+* fp8-input workloads round the same float32 normals to OCP FP8 E4M3 (torch's
+  float8_e4m3fn conversion, nearest-even; N(0,1) samples never reach its
+  range limit of 448) and draw per-row and per-column float32 scales
+  (operands j = 6 and 7), uniform in [0.5, 2).
 """
 from __future__ import annotations
 
@@ -37,6 +41,7 @@ class Workload:
     epilogue: str = "none"
     bound: str = "mfma"  # which roofline limits it: "mfma" or "hbm"
     out: str = "bf16"    # "bf16", or "int8" (per-row quantized output)
+    inp: str = "bf16"    # "bf16", or "fp8" (E4M3 operands with per-row / per-column scales)
     scale_range: tuple = (0.25, 0.75)  # int8 output: per-row scales, uniform
     zero_point: int = 0                # int8 output: zero point
     notes: str = field(default="", compare=False)
@@ -46,11 +51,17 @@ class Workload:
         return 2 * self.M * self.N * self.K
 
     @property
+    def in_bytes(self) -> int:
+        return 1 if self.inp == "fp8" else 2
+
+    @property
     def algorithmic_bytes(self) -> int:
         """Minimum HBM bytes: read A and B once, write C once (read C0 if
         beta); an int8 output writes 1 byte per element and reads M scales."""
-        b = 2 * (self.M * self.K + self.K * self.N)
+        b = self.in_bytes * (self.M * self.K + self.K * self.N)
         b += (1 if self.out == "int8" else 2) * self.M * self.N
+        if self.inp == "fp8":
+            b += 4 * (self.M + self.N)
         if self.beta != 0.0:
             b += 2 * self.M * self.N
         if self.bias:
@@ -85,6 +96,16 @@ WORKLOADS = {
         Workload("q8relu_8192x14336x4096", 6, 8192, 14336, 4096, bias=True, epilogue="relu",
                  out="int8", zero_point=-20,
                  notes="Q = sat8(rne(relu(A*B + bias[n]) * scale[m] - 20))"),
+        # the DeepGEMM article's small shapes (section 5.1): one-row decode
+        # (memory-bound: B is read once) and a small square-ish product
+        Workload("decode_1x4096x4096", 7, 1, 4096, 4096, bound="hbm",
+                 notes="M = 1: a matrix-vector product, B (32 MiB) streamed once"),
+        Workload("mid_1024x1024x4096", 8, 1024, 1024, 4096,
+                 notes="64 tiles of 128x128 for 256 compute units"),
+        # FP8 inputs (the DeepGEMM article, sections 1.2 and 6.3) on the
+        # headline shape: E4M3 operands, per-row / per-column scales
+        Workload("fp8_4096", 9, 4096, 4096, 4096, inp="fp8",
+                 notes="C = sa[m] sb[n] (A*B), A and B in OCP FP8 E4M3"),
     ]
 }
 
@@ -109,7 +130,19 @@ def normal_bf16(seed: int, numel: int, scale: float = 1.0) -> np.ndarray:
 
 
 def operand_seed(index: int, operand: str) -> int:
-    return 1000 * index + {"A": 1, "B": 2, "C0": 3, "bias": 4, "scale": 5}[operand]
+    return 1000 * index + {"A": 1, "B": 2, "C0": 3, "bias": 4, "scale": 5, "scale_a": 6, "scale_b": 7}[operand]
+
+
+def normal_fp8(seed: int, numel: int, scale: float = 1.0) -> np.ndarray:
+    """numel i.i.d. N(0, scale^2) samples as OCP FP8 E4M3 bytes (uint8), seeded."""
+    import torch
+    g = np.random.Generator(np.random.PCG64(seed))
+    x = g.standard_normal(numel, dtype=np.float32)
+    if scale != 1.0:
+        x *= np.float32(scale)
+    if numel and float(np.abs(x).max()) >= 448.0:
+        raise ValueError("sample outside the E4M3 range")
+    return torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
 
 
 def uniform_f32(seed: int, numel: int, lo: float, hi: float) -> np.ndarray:
@@ -127,11 +160,15 @@ def make_inputs(w: Workload, lda=None, ldb=None, ldc=None) -> dict:
     lda = w.K if lda is None else lda
     ldb = w.K if ldb is None else ldb
     ldc = w.M if ldc is None else ldc
+    draw = normal_fp8 if w.inp == "fp8" else normal_bf16
     out = {
-        "A": normal_bf16(operand_seed(w.index, "A"), w.M * lda),
-        "B": normal_bf16(operand_seed(w.index, "B"), w.N * ldb),
+        "A": draw(operand_seed(w.index, "A"), w.M * lda),
+        "B": draw(operand_seed(w.index, "B"), w.N * ldb),
         "lda": lda, "ldb": ldb, "ldc": ldc,
     }
+    if w.inp == "fp8":
+        out["scale_a"] = uniform_f32(operand_seed(w.index, "scale_a"), w.M, 0.5, 2.0)
+        out["scale_b"] = uniform_f32(operand_seed(w.index, "scale_b"), w.N, 0.5, 2.0)
     if w.beta != 0.0:
         out["C0"] = normal_bf16(operand_seed(w.index, "C0"), w.N * ldc)
     if w.bias:

@@ -83,6 +83,14 @@ def _load():
     lib.oracle_quantize_i8_array.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                              ctypes.c_void_p, ctypes.c_void_p, i64]
     lib.oracle_quantize_i8_array.restype = None
+    lib.oracle_fp8_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+    lib.oracle_fp8_e4m3_to_f64.restype = f64
+    lib.oracle_fp8_e4m3_to_f64_array.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i64]
+    lib.oracle_fp8_e4m3_to_f64_array.restype = None
+    lib.oracle_gemm_fp8.argtypes = [i64, i64, i64, ctypes.c_void_p, i64, ctypes.c_void_p, i64, u16p, i64,
+                                    f64, f64, ctypes.c_void_p, ctypes.c_void_p, u16p, ctypes.c_int, u16p,
+                                    ctypes.c_void_p, ctypes.c_int]
+    lib.oracle_gemm_fp8.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -238,3 +246,44 @@ def quantize_i8_array(y, scale, zero_point):
     t = np.zeros(max(y.size, 1), dtype=np.float64)
     lib.oracle_quantize_i8_array(_ptr(y), _ptr(s), int(zero_point), _ptr(q), _ptr(t), y.size)
     return q[: y.size], t[: y.size]
+
+
+def fp8_to_f64(bits) -> np.ndarray:
+    """Exact decode of OCP FP8 E4M3 bytes (any shape) to float64."""
+    lib = _load()
+    b = np.ascontiguousarray(bits, dtype=np.uint8)
+    out = np.empty(b.shape, dtype=np.float64)
+    lib.oracle_fp8_e4m3_to_f64_array(_ptr(b), _ptr(out), b.size)
+    return out
+
+
+def gemm_fp8(M, N, K, A, lda, B, ldb, C_in=None, ldc=None, alpha=1.0, beta=0.0, scale_a=None,
+             scale_b=None, bias=None, epilogue="none", nthreads=0, return_pre=False):
+    """fp8 (E4M3) input oracle: A, B flat uint8 buffers (A row-major, B
+    column-major), optional per-row scale_a (M floats) and per-column
+    scale_b (N floats); returns C_out as gemm() does."""
+    lib = _load()
+    if ldc is None:
+        ldc = max(1, M)
+    A = np.ascontiguousarray(A, dtype=np.uint8).reshape(-1)
+    B = np.ascontiguousarray(B, dtype=np.uint8).reshape(-1)
+    C_in, bias = _u16(C_in, "C_in"), _u16(bias, "bias")
+    sa = None if scale_a is None else np.ascontiguousarray(scale_a, dtype=np.float32).reshape(-1)
+    sb = None if scale_b is None else np.ascontiguousarray(scale_b, dtype=np.float32).reshape(-1)
+    if M > 0 and K > 0 and A.size < (M - 1) * lda + K:
+        raise ValueError("A too small")
+    if N > 0 and K > 0 and B.size < (N - 1) * ldb + K:
+        raise ValueError("B too small")
+    if (sa is not None and sa.size < M) or (sb is not None and sb.size < N):
+        raise ValueError("scales too small")
+    out = np.zeros(max(N * ldc, 1), dtype=np.uint16)
+    pre = np.zeros((max(N, 1), max(M, 1)), dtype=np.float64) if return_pre else None
+    rc = lib.oracle_gemm_fp8(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C_in), ldc, float(alpha), float(beta),
+                             _ptr(sa), _ptr(sb), _ptr(bias), EPI_CODES[epilogue], _ptr(out), _ptr(pre),
+                             int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_gemm_fp8 rejected its arguments")
+    out = out[: N * ldc]
+    if return_pre:
+        return out, pre[:N, :M]
+    return out

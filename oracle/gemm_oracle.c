@@ -19,6 +19,10 @@
  *    "Recap of Simon's blog": the product C[m,n] = A[m,k] x B[k,n];
  *    section "Experimental setup": bf16 matrices, A row-major, B and C
  *    column-major.
+ *  - The same article, sections 1.2 and 6.3: low-precision FP8 inputs; the
+ *    fp8 product below takes OCP FP8 E4M3 operands (4 exponent bits, bias 7,
+ *    3 mantissa bits, no infinities, S.1111.111 = NaN) with optional
+ *    per-row scales of A and per-column scales of B.
  *  - DeepGEMM kernel-set article (demingchina.com), section 1.1: the BLAS
  *    form C = alpha*A*B + beta*C; section 3.1: low-precision inputs with
  *    high-precision accumulation; section 6.1: bias is added first, then the
@@ -148,6 +152,26 @@ void oracle_quantize_i8_array(const double *y, const float *s, int32_t zp, int8_
 {
     for (int64_t i = 0; i < n; ++i)
         q[i] = (int8_t)oracle_quantize_i8(y[i], s[i], zp, t_exact ? &t_exact[i] : NULL);
+}
+
+/*
+ * Exact decode of an OCP FP8 E4M3 value: (-1)^s * 2^(e-7) * (1 + m/8) for
+ * exponent field e >= 1, (-1)^s * 2^-6 * m/8 for e == 0, NaN for e == 15 and
+ * m == 7 (the format has no infinities).
+ */
+double oracle_fp8_e4m3_to_f64(uint8_t bits)
+{
+    int s = (bits >> 7) & 1, e = (bits >> 3) & 15, m = bits & 7;
+    if (e == 15 && m == 7)
+        return NAN;
+    double mag = e == 0 ? ldexp((double)m, -9) : ldexp(8.0 + m, e - 10);
+    return s ? -mag : mag;
+}
+
+void oracle_fp8_e4m3_to_f64_array(const uint8_t *in, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_fp8_e4m3_to_f64(in[i]);
 }
 
 /* Element-wise array forms of the two conversions (n elements). */
@@ -306,6 +330,52 @@ int oracle_gemm_q8(int64_t M, int64_t N, int64_t K,
         double s = dot_row_col(A + m * lda, B + n * ldb, K);
         double y = epilogue(s, alpha, beta, beta != 0.0 ? C_in + m + n * ldc : NULL, bias, n, epi);
         Q[m + n * ldq] = (int8_t)oracle_quantize_i8(y, scale[m], zp, t_exact ? &t_exact[m + n * M] : NULL);
+    }
+    return 0;
+}
+
+/*
+ * The fp8-input product: C_out[m,n] = bf16_rne(epi(alpha * sa[m] * sb[n] *
+ * sum_k A[m,k]*B[k,n] + beta*C_in[m,n] + bias[n])), A and B OCP FP8 E4M3
+ * bytes in the same layouts as the bf16 product (A[m*lda + k], B[k + n*ldb]),
+ * sa / sb per-row / per-column fp32 scales or NULL (1).  Products of two
+ * E4M3 values are exact in double and summed with k ascending; the scale
+ * factors multiply the exact sum in double.  `pre` (if not NULL) receives
+ * the value before rounding, column-major with leading dimension M.
+ */
+int oracle_gemm_fp8(int64_t M, int64_t N, int64_t K,
+                    const uint8_t *A, int64_t lda,
+                    const uint8_t *B, int64_t ldb,
+                    const uint16_t *C_in, int64_t ldc,
+                    double alpha, double beta,
+                    const float *sa, const float *sb,
+                    const uint16_t *bias, int epi,
+                    uint16_t *C_out, double *pre, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return -1;
+    if (lda < (K > 1 ? K : 1) || ldb < (K > 1 ? K : 1) || ldc < (M > 1 ? M : 1))
+        return -1;
+    if (!epi_ok(epi) || (beta != 0.0 && !C_in))
+        return -1;
+    if (nthreads < 1)
+        nthreads = omp_get_max_threads();
+    int64_t total = M * N;
+#pragma omp parallel for schedule(dynamic, 64) num_threads(nthreads)
+    for (int64_t idx = 0; idx < total; ++idx) {
+        int64_t n = idx / M, m = idx % M;
+        const uint8_t *a = A + m * lda, *b = B + n * ldb;
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            s += oracle_fp8_e4m3_to_f64(a[k]) * oracle_fp8_e4m3_to_f64(b[k]);
+        if (sa)
+            s *= (double)sa[m];
+        if (sb)
+            s *= (double)sb[n];
+        double y = epilogue(s, alpha, beta, beta != 0.0 ? C_in + m + n * ldc : NULL, bias, n, epi);
+        if (pre)
+            pre[m + n * M] = y;
+        C_out[m + n * ldc] = oracle_bf16_from_f64(y);
     }
     return 0;
 }

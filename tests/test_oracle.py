@@ -575,3 +575,80 @@ def test_p12_quantize_array_agrees_with_whole_product():
                              case["bias"], "gelu_tanh", return_pre=True)
     q2, t2 = oracle.quantize_i8_array(y, scale[ms], -7)
     assert np.array_equal(q2, Q[ms + ns * M]) and np.array_equal(t2, t[ns, ms])
+
+
+# ------------------------------------------------------ P14-P17 fp8 input ---
+
+def test_p14_fp8_decode_exhaustive_matches_torch():
+    bits = np.arange(256, dtype=np.uint16).astype(np.uint8)
+    ours = oracle.fp8_to_f64(bits)
+    ref = torch.from_numpy(bits.copy()).view(torch.float8_e4m3fn).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan) and nan.sum() == 2     # 0x7F and 0xFF
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))  # -0 at 0x80
+    assert ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9 and ours[0x08] == 2.0 ** -6
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_p15_fp8_exact_rational_bruteforce_tiny(seed):
+    """Tiny fp8 products (random bytes, subnormals included), per-row and
+    per-column scales, alpha, beta, bias, ReLU: exact rational result rounded
+    by brute force -- bit-identical."""
+    g = np.random.Generator(np.random.PCG64(8000 + seed))
+    M, N, K = (int(v) for v in g.integers(1, 9, 3))
+    lda, ldb = K + int(g.integers(0, 3)), K + int(g.integers(0, 3))
+    A = g.integers(0, 256, M * lda).astype(np.uint8)
+    B = g.integers(0, 256, N * ldb).astype(np.uint8)
+    A[(A & 0x7F) == 0x7F] = 0x3C   # no NaN operands here
+    B[(B & 0x7F) == 0x7F] = 0xB4
+    sa = (g.random(M) * 2 + 0.25).astype(np.float32)
+    sb = (g.random(N) * 2 + 0.25).astype(np.float32)
+    C0 = inputs.normal_bf16(8100 + seed, N * M)
+    bias = inputs.normal_bf16(8200 + seed, N, scale=0.5)
+    alpha, beta = 0.75, -1.5
+    epi = ["none", "relu"][seed % 2]
+    got = oracle.gemm_fp8(M, N, K, A, lda, B, ldb, C0, M, alpha, beta, sa, sb, bias, epi)
+    dA = oracle.fp8_to_f64(A).reshape(M, lda)
+    dB = oracle.fp8_to_f64(B).reshape(N, ldb)
+    torch_a = torch.from_numpy(A.copy()).view(torch.float8_e4m3fn).double().numpy().reshape(M, lda)
+    assert np.array_equal(dA, torch_a)
+    c0 = bits_to_f64(C0).reshape(N, M)
+    bb = bits_to_f64(bias)
+    for n in range(N):
+        for m in range(M):
+            s = sum(Fraction(dA[m, k]) * Fraction(dB[n, k]) for k in range(K))
+            y = Fraction(alpha) * Fraction(float(sa[m])) * Fraction(float(sb[n])) * s
+            y += Fraction(beta) * Fraction(c0[n, m]) + Fraction(bb[n])
+            if epi == "relu" and y < 0:
+                y = Fraction(0)
+            want = round_fraction_to_bf16(y)
+            assert same_value(got[m + n * M], want), (m, n)
+
+
+def test_p16_fp8_matches_numpy_float64_matmul():
+    M, N, K = 96, 80, 1000
+    A = inputs.normal_fp8(8301, M * K)
+    B = inputs.normal_fp8(8302, N * K)
+    sa = inputs.uniform_f32(8303, M, 0.5, 2.0)
+    sb = inputs.uniform_f32(8304, N, 0.5, 2.0)
+    _, pre = oracle.gemm_fp8(M, N, K, A, K, B, K, scale_a=sa, scale_b=sb, return_pre=True)
+    dA = oracle.fp8_to_f64(A).reshape(M, K)
+    dB = oracle.fp8_to_f64(B).reshape(N, K)
+    ref = (dA @ dB.T) * sa.astype(np.float64)[:, None] * sb.astype(np.float64)[None, :]
+    assert np.max(np.abs(pre.T - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_p17_fp8_identity_and_scale_axes():
+    """A = I (fp8 1.0 is 0x38): C[m,n] = sa[m] * sb[n] * B[m,n] exactly after
+    rounding (M != N, so swapped scale axes would fail)."""
+    M, N = 24, 10
+    A = np.zeros(M * M, np.uint8)
+    A[np.arange(M) * M + np.arange(M)] = 0x38
+    B = inputs.normal_fp8(8401, N * M)
+    sa = np.exp2(np.arange(M) % 5 - 2).astype(np.float32)      # powers of two: exact products
+    sb = np.exp2(np.arange(N) % 3 - 1).astype(np.float32)
+    got = oracle.gemm_fp8(M, N, M, A, M, B, M, scale_a=sa, scale_b=sb).reshape(N, M)
+    want = oracle.fp8_to_f64(B).reshape(N, M) * sa[None, :] * sb[:, None]
+    assert np.all(same_value(got, oracle.bf16_from_f64(want)))
+    assert oracle.fp8_to_f64(np.array([0x38], np.uint8))[0] == 1.0
