@@ -18,7 +18,7 @@ reads the previous launch's output as C0 (same bytes, same work).
 Prints ONE JSON line (rank 0, one GPU).  With --all it prints one line per
 workload instead.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--workload square_4096]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 300] [--workload square_4096]
 
 The roofline's "traffic" (HBM bytes per launch) comes from rocprofv3
 FETCH_SIZE / WRITE_SIZE passes recorded in profiles/hbm_traffic.json, each
@@ -46,6 +46,7 @@ METRIC = "bf16 GEMM TFLOP/s at M=N=K=4096 and % of MI355X dense bf16 MFMA peak"
 # MI355X published peaks: dense bf16 MFMA = 256 CU x 4096 flop/clk x 2.4 GHz,
 # HBM3E 8 TB/s.
 PEAK_BF16_TFLOPS = 2516.6
+PEAK_FP8_TFLOPS = 5033.2  # dense fp8 MFMA: twice the bf16 rate
 PEAK_HBM_GBS = 8000.0
 EPI = {"none": 0, "gelu_tanh": 1, "relu": 2}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -88,10 +89,14 @@ def cpu_baseline(w, d, budget_cols=None):
     ms = np.tile(np.arange(M, dtype=np.int64), cols)
     ns = np.repeat(np.arange(cols, dtype=np.int64), M)
     t0 = time.perf_counter()
-    _, y = oracle.gemm_elems(M, N, K, d["A"], K, d["B"], K, ms, ns, d.get("C0"), M, w.alpha, w.beta,
-                             d.get("bias"), w.epilogue, nthreads=nthreads, return_pre=True)
-    if w.out == "int8":
-        oracle.quantize_i8_array(y, d["scale"][ms], w.zero_point)
+    if w.inp == "fp8":
+        oracle.gemm_fp8_elems(M, N, K, d["A"], K, d["B"], K, ms, ns, d.get("C0"), M, w.alpha, w.beta,
+                              d["scale_a"], d["scale_b"], d.get("bias"), w.epilogue, nthreads=nthreads)
+    else:
+        _, y = oracle.gemm_elems(M, N, K, d["A"], K, d["B"], K, ms, ns, d.get("C0"), M, w.alpha, w.beta,
+                                 d.get("bias"), w.epilogue, nthreads=nthreads, return_pre=True)
+        if w.out == "int8":
+            oracle.quantize_i8_array(y, d["scale"][ms], w.zero_point)
     dt = time.perf_counter() - t0
     flops = 2.0 * M * cols * K
     return {
@@ -131,9 +136,14 @@ def run_workload(w, steps, warmup, cold, with_cpu):
     d = inputs.make_inputs(w)
 
     def dev_tensor(bits):
+        if bits.dtype == np.uint8:
+            return torch.from_numpy(bits).to(dev)
         return torch.from_numpy(bits.view(np.int16)).to(dev)
 
-    copies = 4 if cold else 1  # rotate distinct buffers so B is not cache-resident
+    # rotate distinct buffer sets (>= 512 MiB in all, twice the 256 MB
+    # Infinity Cache) so the memory-bound workloads read B from HBM
+    in_bytes = w.in_bytes * (w.M * w.K + w.K * w.N)
+    copies = max(4, -(-512 * 2 ** 20 // max(in_bytes, 1))) if cold else 1
     q8 = w.out == "int8"
     A = [dev_tensor(d["A"]) for _ in range(copies)]
     B = [dev_tensor(d["B"]) for _ in range(copies)]
@@ -141,10 +151,16 @@ def run_workload(w, steps, warmup, cold, with_cpu):
     C0 = dev_tensor(d["C0"]) if "C0" in d else None
     bias = dev_tensor(d["bias"]) if "bias" in d else None
     scale = torch.from_numpy(d["scale"]).to(dev) if q8 else None
+    fp8 = w.inp == "fp8"
+    sa = torch.from_numpy(d["scale_a"]).to(dev) if fp8 else None
+    sb = torch.from_numpy(d["scale_b"]).to(dev) if fp8 else None
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     bias_p = bias.data_ptr() if bias is not None else 0
-    if q8:
+    if fp8:
+        kname = gb.gemm_fp8_kernel_name(w.M, w.N, w.K, A[0].data_ptr(), w.K, B[0].data_ptr(), w.K, C[0].data_ptr(),
+                                        w.M, EPI[w.epilogue])
+    elif q8:
         c0_p = C0.data_ptr() if C0 is not None else 0
         kname = gb.gemm_bf16_q8_kernel_name(w.M, w.N, w.K, A[0].data_ptr(), w.K, B[0].data_ptr(), w.K, c0_p, w.M,
                                             C[0].data_ptr(), w.M, w.beta, scale.data_ptr(), EPI[w.epilogue])
@@ -161,7 +177,10 @@ def run_workload(w, steps, warmup, cold, with_cpu):
         return i % copies
 
     def call(j):
-        if q8:
+        if fp8:
+            st = gb.gemm_fp8(w.M, w.N, w.K, A[j].data_ptr(), w.K, B[j].data_ptr(), w.K, C[j].data_ptr(), w.M,
+                             w.alpha, w.beta, sa.data_ptr(), sb.data_ptr(), bias_p, EPI[w.epilogue], sp)
+        elif q8:
             st = gb.gemm_bf16_q8(w.M, w.N, w.K, A[j].data_ptr(), w.K, B[j].data_ptr(), w.K, c0_p, w.M,
                                  C[j].data_ptr(), w.M, w.alpha, w.beta, bias_p, EPI[w.epilogue], scale.data_ptr(),
                                  w.zero_point, sp)
@@ -210,8 +229,9 @@ def run_workload(w, steps, warmup, cold, with_cpu):
         roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                 "traffic": traffic}
     else:
-        roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic}
+        peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
+        roof = {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+                "frac": tflops / peak, "traffic": traffic}
     roof["traffic_unit"] = "bytes per launch (HBM, counter-measured)"
     roof["algorithmic_bytes"] = w.algorithmic_bytes
     roof["traffic_over_algorithmic"] = traffic / w.algorithmic_bytes if traffic else None
@@ -226,13 +246,13 @@ def run_workload(w, steps, warmup, cold, with_cpu):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8_e4m3" if fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha, "beta": w.beta,
                    "bias": w.bias, "epilogue": w.epilogue, "layout": "A row-major, B/C column-major",
                    "kernel": kname, "inputs": "N(0,1) seeded (bias N(0,0.1))", "output": w.out,
-                   "cache": "cold (4 rotating buffer sets)" if cold else "warm"},
-        "pct_of_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+                   "cache": f"cold ({copies} rotating buffer sets)" if cold else "warm"},
+        "pct_of_peak": 100.0 * tflops / (PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS),
         "hbm_gbs_algorithmic": gbs,
         "per_launch_event_pairs_ms": {"mean": statistics.fmean(per), "min": min(per),
                                       "median": statistics.median(per), "max": max(per),
@@ -265,8 +285,11 @@ def calibrate_copy(mib):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
+    # The part's clocks settle only after some 20-30 ms of sustained load
+    # (the first ~200 launches at 4096^3 run ~20% slower, and again after an
+    # idle second), so the default warm-up is 300 launches.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="square_4096", choices=list(inputs.WORKLOADS))
     ap.add_argument("--all", action="store_true", help="one JSON line per workload")
     ap.add_argument("--cold", choices=["auto", "yes", "no"], default="auto",

@@ -16,7 +16,7 @@ import os
 __all__ = [
     "EPILOGUES", "GemmError", "LIB_PATH", "gemm", "gemm_bf16", "gemm_bf16_kernel_name",
     "gemm_bf16_last_hip_error", "gemm_bf16_q8", "gemm_bf16_q8_kernel_name", "gemm_bf16_status_string",
-    "gemm_q8", "library",
+    "gemm_fp8", "gemm_fp8_kernel_name", "gemm_q8", "library",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemm_bf16.so")
@@ -57,6 +57,10 @@ def library() -> ctypes.CDLL:
     lib.gemm_bf16_q8.restype = i32
     lib.gemm_bf16_q8_kernel_name.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, f32, vp, i32]
     lib.gemm_bf16_q8_kernel_name.restype = ctypes.c_char_p
+    lib.gemm_fp8.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, f32, f32, vp, vp, vp, i32, vp]
+    lib.gemm_fp8.restype = i32
+    lib.gemm_fp8_kernel_name.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, i32]
+    lib.gemm_fp8_kernel_name.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -79,6 +83,17 @@ def gemm_bf16_q8_kernel_name(M, N, K, A, lda, B, ldb, C, ldc, Q, ldq, beta=0.0, 
                              epilogue=0) -> str:
     return library().gemm_bf16_q8_kernel_name(M, N, K, A or None, lda, B or None, ldb, C or None, ldc,
                                               Q or None, ldq, beta, scale or None, epilogue).decode()
+
+
+def gemm_fp8(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, scale_a, scale_b, bias, epilogue, stream) -> int:
+    """Raw C-ABI call of the FP8 (E4M3) input entry point (pointers as integers)."""
+    return library().gemm_fp8(M, N, K, A or None, lda, B or None, ldb, C or None, ldc, alpha, beta,
+                              scale_a or None, scale_b or None, bias or None, epilogue, stream or None)
+
+
+def gemm_fp8_kernel_name(M, N, K, A, lda, B, ldb, C, ldc, epilogue=0) -> str:
+    return library().gemm_fp8_kernel_name(M, N, K, A or None, lda, B or None, ldb, C or None, ldc,
+                                          epilogue).decode()
 
 
 def gemm_bf16_status_string(status: int) -> str:

@@ -27,12 +27,17 @@ struct ShapeSkinny { static constexpr int KS_N32 = 256, KS_WIDE = 128; };
 
 struct SkinnyWork;
 
+// FP8 (E4M3) operands: 256x256 output tiles, K-slices of 128 fp8 (one
+// 128-byte line per operand row).
+struct ShapeFp8 { static constexpr int BM = 256, BN = 256, BK = 128; };
+
 hipError_t launch_tile_large(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_medium(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_ring_mfma32(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_ring(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_ring_masked(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_ring_q8(const GemmArgs &args, int cus, hipStream_t stream);
+hipError_t launch_tile_fp8(const GemmArgs &args, int cus, hipStream_t stream);
 // rows: 32 or 64 (the kernel's row block, M <= rows); cols: strip width
 hipError_t launch_skinny(int rows, int cols, const GemmArgs &args, const SkinnyWork &work, int cus,
                          hipStream_t stream);

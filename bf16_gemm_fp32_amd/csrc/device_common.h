@@ -39,6 +39,11 @@ struct GemmArgs {
     int64_t ldq;
     const float *scale;
     float zp;
+    // fp8 inputs (the fp8 entry point only): A and B hold OCP FP8 E4M3 bytes
+    // (lda, ldb in bytes) and the product is scaled by scale_a[m] and
+    // scale_b[n] when given.
+    const float *scale_a;
+    const float *scale_b;
 };
 
 // Call f(std::integral_constant<uint32_t, flags>) for the run-time flag word,
@@ -127,6 +132,17 @@ __device__ __forceinline__ float gelu_tanh_f32(float y) {
     float u = kSqrt2OverPi * (y + 0.044715f * y * y * y);
     float e = __builtin_amdgcn_exp2f(-2.0f * kLog2e * u);
     return y * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// OCP FP8 E4M3 byte -> bf16 bits, exactly (every E4M3 value is a bf16
+// value): normal values re-bias the exponent (7 -> 127), subnormals m * 2^-9
+// go through an exact fp32 product, S.1111.111 is NaN.
+__device__ __forceinline__ uint32_t fp8_e4m3_to_bf16_bits(uint32_t b) {
+    const uint32_t s = (b & 0x80u) << 8;
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    if (e == 15u && m == 7u) return s | 0x7FC0u;
+    if (e != 0u) return s | ((e + 120u) << 7) | (m << 4);
+    return s | (__builtin_bit_cast(uint32_t, (float)m * 0x1p-9f) >> 16);
 }
 
 // ReLU: negative values become 0; NaN passes through (a compare-select, not

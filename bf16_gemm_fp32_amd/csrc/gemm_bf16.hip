@@ -20,13 +20,14 @@
 namespace gb {
 
 enum KernelKind {
-    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kNumKinds
+    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8, kNumKinds
 };
 
 static const char *const kKindNames[kNumKinds] = {"none",            "tile256x256x32_s5", "tile128x128x64_s4",
                                                   "skinny",          "generic64x64x32",
                                                   "ring256x256x64_mfma32", "ring256x256x64",
-                                                  "ring256x256x64_masked", "ring256x256x64_q8"};
+                                                  "ring256x256x64_masked", "ring256x256x64_q8",
+                                                  "fp8_256x256x128"};
 
 static const char *kind_name(int k) { return (k >= 0 && k < kNumKinds) ? kKindNames[k] : "none"; }
 
@@ -286,15 +287,34 @@ static int choose_kernel_q8(int64_t M, int64_t N, int64_t K, const void *A, int6
     return kGeneric;
 }
 
-static hipError_t launch_generic(const GemmArgs &args, int cus, hipStream_t stream) {
+static hipError_t launch_generic(const GemmArgs &args, int cus, hipStream_t stream, bool fp8 = false) {
     const int64_t tiles_m = (args.M + GenericConfig::BM - 1) / GenericConfig::BM;
     const int64_t tiles_n = (args.N + GenericConfig::BN - 1) / GenericConfig::BN;
     const int64_t tiles = tiles_m * tiles_n;
     const int64_t cap = (int64_t)cus * 8;
     const int grid = (int)(tiles < cap ? tiles : cap);
-    hipLaunchKernelGGL(gemm_generic_kernel, dim3(grid), dim3(GenericConfig::kThreads), 0, stream, args, tiles_m,
-                       tiles);
+    if (fp8)
+        hipLaunchKernelGGL(gemm_generic_kernel<true>, dim3(grid), dim3(GenericConfig::kThreads), 0, stream, args,
+                           tiles_m, tiles);
+    else
+        hipLaunchKernelGGL(gemm_generic_kernel<false>, dim3(grid), dim3(GenericConfig::kThreads), 0, stream, args,
+                           tiles_m, tiles);
     return hipGetLastError();
+}
+
+// The fp8 product: the 256x256 FP8 tile kernel for exact tile multiples
+// (M, N % 256, K % 128) with 16-byte aligned rows, else the bounds-checked
+// kernel (which converts the bytes to bf16 on their way into LDS).
+static int choose_kernel_fp8(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+                             int64_t ldb, const void *C, int64_t ldc) {
+    if (M == 0 || N == 0) return kNone;
+    const char *force = std::getenv("GEMM_BF16_FORCE_KERNEL");
+    if (force && !std::strcmp(force, kKindNames[kGeneric])) return kGeneric;
+    bool ok = K > 0 && M % ShapeFp8::BM == 0 && N % ShapeFp8::BN == 0 && K % ShapeFp8::BK == 0;
+    ok = ok && lda % 16 == 0 && ldb % 16 == 0 && ldc % 8 == 0 && aligned16(A) && aligned16(B) && aligned16(C);
+    const int64_t lim = (int64_t)1 << 31;
+    ok = ok && ShapeFp8::BM * lda + K < lim && ShapeFp8::BN * ldb + K < lim && (M / 256) * (N / 256) < lim;
+    return ok ? kFp8 : kGeneric;
 }
 
 }  // namespace gb
@@ -309,7 +329,7 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t lda
     if (st != GEMM_OK) return st;
     if (M == 0 || N == 0) return GEMM_OK;
 
-    GemmArgs args;
+    GemmArgs args{};
     args.M = M;
     args.N = N;
     args.K = K;
@@ -355,7 +375,7 @@ int gemm_bf16_q8(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t 
     if (st != GEMM_OK) return st;
     if (M == 0 || N == 0) return GEMM_OK;
 
-    GemmArgs args;
+    GemmArgs args{};
     args.M = M;
     args.N = N;
     args.K = K;
@@ -394,6 +414,51 @@ const char *gemm_bf16_q8_kernel_name(int64_t M, int64_t N, int64_t K, const gemm
     if (gb::validate_q8(M, N, K, A, lda, B, ldb, C, ldc, Q, ldq, beta, scale, epilogue) != GEMM_OK) return "none";
     return gb::kind_name(
         gb::choose_kernel_q8(M, N, K, A, lda, B, ldb, C, ldc, beta, Q, ldq, scale, gb::device_cu_count()));
+}
+
+int gemm_fp8(int64_t M, int64_t N, int64_t K, const gemm_fp8_t *A, int64_t lda, const gemm_fp8_t *B,
+             int64_t ldb, gemm_bf16_t *C, int64_t ldc, float alpha, float beta, const float *scale_a,
+             const float *scale_b, const gemm_bf16_t *bias, int epilogue, hipStream_t stream) {
+    using namespace gb;
+    const int st = validate(M, N, K, A, lda, B, ldb, C, ldc, epilogue);
+    if (st != GEMM_OK) return st;
+    if (M == 0 || N == 0) return GEMM_OK;
+
+    GemmArgs args{};
+    args.M = M;
+    args.N = N;
+    args.K = K;
+    args.A = reinterpret_cast<const uint16_t *>(A);  // bytes; the fp8 kernels read them as such
+    args.lda = lda;
+    args.B = reinterpret_cast<const uint16_t *>(B);
+    args.ldb = ldb;
+    args.C = C;
+    args.ldc = ldc;
+    args.alpha = alpha;
+    args.beta = beta;
+    args.bias = bias;
+    args.flags = epilogue_flags(beta, bias, epilogue);
+    args.scale_a = scale_a;
+    args.scale_b = scale_b;
+
+    const int cus = device_cu_count();
+    hipError_t err = hipSuccess;
+    if (choose_kernel_fp8(M, N, K, A, lda, B, ldb, C, ldc) == kFp8)
+        err = launch_tile_fp8(args, cus, stream);
+    else
+        err = launch_generic(args, cus, stream, true);
+    if (err != hipSuccess) {
+        t_last_hip_error = (int)err;
+        return GEMM_ERR_HIP;
+    }
+    return GEMM_OK;
+}
+
+const char *gemm_fp8_kernel_name(int64_t M, int64_t N, int64_t K, const gemm_fp8_t *A, int64_t lda,
+                                 const gemm_fp8_t *B, int64_t ldb, const gemm_bf16_t *C, int64_t ldc,
+                                 int epilogue) {
+    if (gb::validate(M, N, K, A, lda, B, ldb, C, ldc, epilogue) != GEMM_OK) return "none";
+    return gb::kind_name(gb::choose_kernel_fp8(M, N, K, A, lda, B, ldb, C, ldc));
 }
 
 const char *gemm_bf16_status_string(int status) {

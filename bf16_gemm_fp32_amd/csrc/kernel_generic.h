@@ -44,6 +44,27 @@ __device__ __forceinline__ u32x4 load_row_chunk(const uint16_t *row, bool row_ok
     return v;
 }
 
+// Eight consecutive OCP FP8 E4M3 bytes of one K-contiguous row as eight
+// bf16 values (exact), elements with k >= K (or a row outside the matrix)
+// read as zero.
+__device__ __forceinline__ u32x4 load_row_chunk_fp8(const uint8_t *row, bool row_ok, int64_t k, int64_t K) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (!row_ok) return v;
+    const uint8_t *p = row + k;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        if (k + e < K) w[e >> 1] |= fp8_e4m3_to_bf16_bits(p[e]) << ((e & 1) * 16);
+    v.x = w[0];
+    v.y = w[1];
+    v.z = w[2];
+    v.w = w[3];
+    return v;
+}
+
+// kFp8: A and B hold E4M3 bytes (lda, ldb in bytes), converted to bf16 on
+// their way into LDS, and the product is scaled by scale_a[m] * scale_b[n].
+template <bool kFp8>
 __global__ void __launch_bounds__(GenericConfig::kThreads)
 gemm_generic_kernel(const GemmArgs args, int64_t tiles_m, int64_t num_tiles) {
     using G = GenericConfig;
@@ -62,13 +83,17 @@ gemm_generic_kernel(const GemmArgs args, int64_t tiles_m, int64_t num_tiles) {
         const int64_t n0 = (tile / tiles_m) * G::BN;
         const bool a_ok = m0 + lr < args.M;
         const bool b_ok = n0 + lr < args.N;
-        const uint16_t *a_row = args.A + (a_ok ? (m0 + lr) * args.lda : 0);
-        const uint16_t *b_row = args.B + (b_ok ? (n0 + lr) * args.ldb : 0);
+        const uint16_t *a_row = args.A + (a_ok && !kFp8 ? (m0 + lr) * args.lda : 0);
+        const uint16_t *b_row = args.B + (b_ok && !kFp8 ? (n0 + lr) * args.ldb : 0);
+        const uint8_t *a_row8 = reinterpret_cast<const uint8_t *>(args.A) + (a_ok ? (m0 + lr) * args.lda : 0);
+        const uint8_t *b_row8 = reinterpret_cast<const uint8_t *>(args.B) + (b_ok ? (n0 + lr) * args.ldb : 0);
 
         f32x16 acc = {};
         for (int64_t k0 = 0; k0 < args.K; k0 += G::BK) {
-            const u32x4 va = load_row_chunk(a_row, a_ok, k0 + lc * 8, args.K);
-            const u32x4 vb = load_row_chunk(b_row, b_ok, k0 + lc * 8, args.K);
+            const u32x4 va = kFp8 ? load_row_chunk_fp8(a_row8, a_ok, k0 + lc * 8, args.K)
+                                  : load_row_chunk(a_row, a_ok, k0 + lc * 8, args.K);
+            const u32x4 vb = kFp8 ? load_row_chunk_fp8(b_row8, b_ok, k0 + lc * 8, args.K)
+                                  : load_row_chunk(b_row, b_ok, k0 + lc * 8, args.K);
             *(GB_LDS u32x4 *)(sA + lr * G::kRowBytes + lc * 16) = va;
             *(GB_LDS u32x4 *)(sB + lr * G::kRowBytes + lc * 16) = vb;
             lds_barrier();
@@ -88,12 +113,15 @@ gemm_generic_kernel(const GemmArgs args, int64_t tiles_m, int64_t num_tiles) {
         const int64_t n = n0 + wn * 32 + (lane & 31);
         if (n < args.N) {
             const float bias_v = (args.flags & kEpiBias) ? bf16_bits_to_f32(args.bias[n]) : 0.f;
+            const float sb = (kFp8 && args.scale_b) ? args.scale_b[n] : 1.f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t m = m0 + wm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
                 if (m < args.M) {
                     const float cin = (args.flags & kEpiBeta) ? bf16_bits_to_f32(args.C[n * args.ldc + m]) : 0.f;
-                    const float v = epilogue_value_rt(acc[r], cin, bias_v, args);
+                    float x = acc[r];
+                    if (kFp8) x = x * (args.scale_a ? args.scale_a[m] : 1.f) * sb;
+                    const float v = epilogue_value_rt(x, cin, bias_v, args);
                     if (args.Q)
                         args.Q[n * args.ldq + m] = (int8_t)quantize_i8(v, args.scale[m], args.zp);
                     else

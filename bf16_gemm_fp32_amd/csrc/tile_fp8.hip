@@ -1,0 +1,13 @@
+// tile_fp8.hip -- instances of the 256x256 FP8 (E4M3) tile kernel.
+#include "configs.h"
+#include "kernel_fp8.h"
+
+namespace gb {
+
+static_assert(Fp8Config::BM == ShapeFp8::BM && Fp8Config::BN == ShapeFp8::BN && Fp8Config::BK == ShapeFp8::BK);
+
+hipError_t launch_tile_fp8(const GemmArgs &args, int cus, hipStream_t stream) {
+    return launch_fp8_ring(args, cus, stream);
+}
+
+}  // namespace gb

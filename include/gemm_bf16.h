@@ -33,6 +33,10 @@ extern "C" {
 /* Raw bf16 bits (sign, 8-bit exponent, 7-bit mantissa). */
 typedef uint16_t gemm_bf16_t;
 
+/* Raw OCP FP8 E4M3 bits (sign, 4-bit exponent with bias 7, 3-bit mantissa;
+ * no infinities, S.1111.111 is NaN). */
+typedef uint8_t gemm_fp8_t;
+
 /* Epilogue activation, applied last to alpha*AB + beta*C + bias (the
  * DeepGEMM article, section 6.1: bias first, then ReLU or GELU). */
 enum gemm_bf16_epilogue {
@@ -127,6 +131,36 @@ int gemm_bf16_q8(int64_t M, int64_t N, int64_t K,
                  const float *scale, int32_t zero_point,
                  hipStream_t stream);
 
+/*
+ * gemm_fp8 -- enqueue the product of FP8 operands, the FP8 input path of the
+ * DeepGEMM article (demingchina.com), sections 1.2 and 6.3:
+ *
+ *   C[m,n] <- epi( alpha * sa[m] * sb[n] * sum_k A[m,k]*B[k,n]
+ *                  + beta * C[m,n] + bias[n] )
+ *
+ * with A and B OCP FP8 E4M3 values (exact products, fp32 accumulation), the
+ * scales, alpha, beta*C, bias and the activation in fp32, one RNE to bf16.
+ *
+ *   A        device pointer, row-major M x K bytes: A[m*lda + k], lda >= K.
+ *   B        device pointer, column-major K x N bytes: B[k + n*ldb], ldb >= K.
+ *   C, ldc, alpha, beta, bias, epilogue, stream: as in gemm_bf16.
+ *   scale_a  NULL (all 1), or a device pointer to M fp32 per-row scales.
+ *   scale_b  NULL (all 1), or a device pointer to N fp32 per-column scales.
+ *
+ * Errors and quick returns as gemm_bf16.  16-byte aligned A, B and C with
+ * lda, ldb multiples of 16, ldc a multiple of 8, M and N multiples of 256
+ * and K a multiple of 128 select the FP8 MFMA kernel; other inputs take the
+ * bounds-checked path (same result).
+ */
+int gemm_fp8(int64_t M, int64_t N, int64_t K,
+             const gemm_fp8_t *A, int64_t lda,
+             const gemm_fp8_t *B, int64_t ldb,
+             gemm_bf16_t *C, int64_t ldc,
+             float alpha, float beta,
+             const float *scale_a, const float *scale_b,
+             const gemm_bf16_t *bias, int epilogue,
+             hipStream_t stream);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char *gemm_bf16_status_string(int status);
 
@@ -156,6 +190,13 @@ const char *gemm_bf16_q8_kernel_name(int64_t M, int64_t N, int64_t K,
                                      const int8_t *Q, int64_t ldq,
                                      float beta, const float *scale,
                                      int epilogue);
+
+/* The kernel configuration gemm_fp8 would launch (as gemm_bf16_kernel_name). */
+const char *gemm_fp8_kernel_name(int64_t M, int64_t N, int64_t K,
+                                 const gemm_fp8_t *A, int64_t lda,
+                                 const gemm_fp8_t *B, int64_t ldb,
+                                 const gemm_bf16_t *C, int64_t ldc,
+                                 int epilogue);
 
 #ifdef __cplusplus
 }

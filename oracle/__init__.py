@@ -91,6 +91,10 @@ def _load():
                                     f64, f64, ctypes.c_void_p, ctypes.c_void_p, u16p, ctypes.c_int, u16p,
                                     ctypes.c_void_p, ctypes.c_int]
     lib.oracle_gemm_fp8.restype = ctypes.c_int
+    lib.oracle_gemm_fp8_elems.argtypes = [i64, i64, i64, ctypes.c_void_p, i64, ctypes.c_void_p, i64, u16p, i64,
+                                          f64, f64, ctypes.c_void_p, ctypes.c_void_p, u16p, ctypes.c_int, i64,
+                                          ctypes.c_void_p, ctypes.c_void_p, u16p, ctypes.c_int]
+    lib.oracle_gemm_fp8_elems.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -287,3 +291,25 @@ def gemm_fp8(M, N, K, A, lda, B, ldb, C_in=None, ldc=None, alpha=1.0, beta=0.0, 
     if return_pre:
         return out, pre[:N, :M]
     return out
+
+
+def gemm_fp8_elems(M, N, K, A, lda, B, ldb, ms, ns, C_in=None, ldc=None, alpha=1.0, beta=0.0, scale_a=None,
+                   scale_b=None, bias=None, epilogue="none", nthreads=0):
+    """The fp8 definition evaluated only at coordinates (ms[i], ns[i])."""
+    lib = _load()
+    if ldc is None:
+        ldc = max(1, M)
+    A = np.ascontiguousarray(A, dtype=np.uint8).reshape(-1)
+    B = np.ascontiguousarray(B, dtype=np.uint8).reshape(-1)
+    C_in, bias = _u16(C_in, "C_in"), _u16(bias, "bias")
+    sa = None if scale_a is None else np.ascontiguousarray(scale_a, dtype=np.float32).reshape(-1)
+    sb = None if scale_b is None else np.ascontiguousarray(scale_b, dtype=np.float32).reshape(-1)
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    out = np.zeros(max(ms.size, 1), dtype=np.uint16)
+    rc = lib.oracle_gemm_fp8_elems(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C_in), ldc, float(alpha),
+                                   float(beta), _ptr(sa), _ptr(sb), _ptr(bias), EPI_CODES[epilogue], ms.size,
+                                   _ptr(ms), _ptr(ns), _ptr(out), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_gemm_fp8_elems rejected its arguments")
+    return out[: ms.size]

@@ -379,3 +379,42 @@ int oracle_gemm_fp8(int64_t M, int64_t N, int64_t K,
     }
     return 0;
 }
+
+/* The fp8 definition above on a list of output coordinates only. */
+int oracle_gemm_fp8_elems(int64_t M, int64_t N, int64_t K,
+                          const uint8_t *A, int64_t lda,
+                          const uint8_t *B, int64_t ldb,
+                          const uint16_t *C_in, int64_t ldc,
+                          double alpha, double beta,
+                          const float *sa, const float *sb,
+                          const uint16_t *bias, int epi,
+                          int64_t count, const int64_t *ms, const int64_t *ns,
+                          uint16_t *out, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0 || count < 0)
+        return -1;
+    if (lda < (K > 1 ? K : 1) || ldb < (K > 1 ? K : 1) || ldc < (M > 1 ? M : 1))
+        return -1;
+    if (!epi_ok(epi) || (beta != 0.0 && !C_in))
+        return -1;
+    for (int64_t i = 0; i < count; ++i)
+        if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N)
+            return -1;
+    if (nthreads < 1)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 16) num_threads(nthreads)
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t m = ms[i], n = ns[i];
+        const uint8_t *a = A + m * lda, *b = B + n * ldb;
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            s += oracle_fp8_e4m3_to_f64(a[k]) * oracle_fp8_e4m3_to_f64(b[k]);
+        if (sa)
+            s *= (double)sa[m];
+        if (sb)
+            s *= (double)sb[n];
+        double y = epilogue(s, alpha, beta, beta != 0.0 ? C_in + m + n * ldc : NULL, bias, n, epi);
+        out[i] = oracle_bf16_from_f64(y);
+    }
+    return 0;
+}

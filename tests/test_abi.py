@@ -85,6 +85,20 @@ def test_q8_argument_errors():
     assert name(100, 100, 64, P, 64, P, 64, 0, 1, P, 112, 0.0, P, 0) == "generic64x64x32"
 
 
+def test_fp8_argument_errors_and_names():
+    f = gb.gemm_fp8
+    assert f(-1, 4, 4, P, 4, P, 4, P, 4, 1.0, 0.0, 0, 0, 0, 0, 0) == ERR_DIM
+    assert f(4, 4, 4, P, 3, P, 4, P, 4, 1.0, 0.0, 0, 0, 0, 0, 0) == ERR_LD
+    assert f(4, 4, 4, 0, 4, P, 4, P, 4, 1.0, 0.0, 0, 0, 0, 0, 0) == ERR_NULL
+    assert f(4, 4, 4, P, 4, P, 4, P, 4, 1.0, 0.0, 0, 0, 0, 7, 0) == ERR_EPI
+    assert f(0, 4, 4, 0, 4, P, 4, 0, 1, 1.0, 0.0, 0, 0, 0, 2, 0) == OK
+    name = gb.gemm_fp8_kernel_name
+    assert name(4096, 4096, 4096, P, 4096, P, 4096, P, 4096) == "fp8_256x256x128"
+    assert name(4096, 4096, 4032, P, 4032, P, 4032, P, 4096) == "generic64x64x32"   # K % 128 != 0
+    assert name(4096, 4096, 4096, P + 8, 4096, P, 4096, P, 4096) == "generic64x64x32"  # unaligned A
+    assert name(4000, 4096, 4096, P, 4096, P, 4096, P, 4000) == "generic64x64x32"
+
+
 def test_relu_is_accepted():
     # M == 0: nothing to launch, so the status is decided by validation alone
     assert call(0, 4, 4, A=0, C=0, epi=2) == OK

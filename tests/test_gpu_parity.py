@@ -445,6 +445,89 @@ def test_q8_generic_paths():
              expect_kernel="generic64x64x32")
 
 
+# ----------------------------------------------------------- fp8 inputs ---
+
+FP8R = "fp8_256x256x128"
+
+
+def to_dev_u8(bits: np.ndarray, offset: int = 0):
+    full = torch.zeros(bits.size + offset + 16, dtype=torch.uint8, device="cuda")
+    full[offset:offset + bits.size] = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint8)).cuda()
+    return full, full.data_ptr() + offset
+
+
+def check_fp8(tag, M, N, K, lda=None, ldb=None, ldc=None, alpha=1.0, beta=0.0, use_bias=False,
+              epilogue="none", scales=True, offsets=(0, 0, 0), seed=0, expect_kernel=None):
+    lda = max(K, 1) if lda is None else lda
+    ldb = max(K, 1) if ldb is None else ldb
+    ldc = max(M, 1) if ldc is None else ldc
+    A = inputs.normal_fp8(seed + 1, M * lda)
+    B = inputs.normal_fp8(seed + 2, N * ldb)
+    C0 = inputs.normal_bf16(seed + 3, N * ldc)
+    bias = inputs.normal_bf16(seed + 4, N, scale=0.1) if use_bias else None
+    sa = inputs.uniform_f32(seed + 6, M, 0.5, 2.0) if scales else None
+    sb = inputs.uniform_f32(seed + 7, N, 0.5, 2.0) if scales else None
+    C_init = C0 if beta != 0.0 else np.full_like(C0, NAN_BF16)
+    kname = gb.gemm_fp8_kernel_name(M, N, K, 4096 + offsets[0], lda, 4096 + offsets[1], ldb,
+                                    4096 + 2 * offsets[2], ldc, EPI[epilogue])
+    say(f"[parity-fp8] {tag}: M={M} N={N} K={K} lda={lda} ldb={ldb} ldc={ldc} alpha={alpha} beta={beta} "
+        f"bias={use_bias} epi={epilogue} scales={scales} offsets={offsets} kernel={kname}")
+    if expect_kernel is not None:
+        assert kname == expect_kernel
+    a_t, a_p = to_dev_u8(A, offsets[0])
+    b_t, b_p = to_dev_u8(B, offsets[1])
+    c_t, c_p = to_dev(C_init, offsets[2])
+    bias_p = 0
+    if bias is not None:
+        bias_t, bias_p = to_dev(bias)
+    sa_t = torch.from_numpy(sa).cuda() if scales else None
+    sb_t = torch.from_numpy(sb).cuda() if scales else None
+    st = gb.gemm_fp8(M, N, K, a_p, lda, b_p, ldb, c_p, ldc, alpha, beta, sa_t.data_ptr() if scales else 0,
+                     sb_t.data_ptr() if scales else 0, bias_p, EPI[epilogue], torch.cuda.current_stream().cuda_stream)
+    assert st == 0, gb.gemm_bf16_status_string(st)
+    torch.cuda.synchronize()
+    got = from_dev(c_t, offsets[2], C_init.size)
+    ref = oracle.gemm_fp8(M, N, K, A, lda, B, ldb, C0, ldc, alpha, beta, sa, sb, bias, epilogue,
+                          nthreads=_threads())
+    g2, r2 = got.reshape(N, ldc), ref.reshape(N, ldc)
+    rep = assert_within_tolerance(g2[:, :M], r2[:, :M], K, tag)
+    if ldc > M:
+        assert np.array_equal(g2[:, M:], C_init.reshape(N, ldc)[:, M:]), f"{tag}: padding written"
+    say(f"[parity-fp8] {tag}: ok max_ulp={rep['max_ulp']:.2f} mean_ulp={rep['mean_ulp']:.4f} "
+        f"exact={rep['exact']}/{rep['n']}")
+    return rep
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 512, 128), (512, 256, 256), (1024, 512, 640), (4096, 2048, 1280)])
+def test_fp8_ring_slice_counts(M, N, K):
+    check_fp8(f"fp8 ring {M}x{N}x{K}", M, N, K, seed=M + N + K, expect_kernel=FP8R)
+
+
+@pytest.mark.parametrize("beta,use_bias,epi,scales", [(b, u, e, sc) for b in (0.0, -0.75) for u in (False, True)
+                                                      for e in ("none", "gelu_tanh", "relu") for sc in (True, False)
+                                                      if not (u and not sc and e == "relu")])
+def test_fp8_ring_epilogue_combinations(beta, use_bias, epi, scales):
+    check_fp8(f"fp8 ring beta={beta} bias={use_bias} {epi} scales={scales}", 1024, 512, 384, alpha=1.25,
+              beta=beta, use_bias=use_bias, epilogue=epi, scales=scales,
+              seed=int(abs(beta) * 4) + 2 * use_bias + len(epi) + 7 * scales, expect_kernel=FP8R)
+
+
+def test_fp8_ring_padded_leading_dims():
+    check_fp8("fp8 ring padded", 512, 768, 512, lda=528, ldb=640, ldc=520, beta=0.5, use_bias=True, seed=95,
+              expect_kernel=FP8R)
+
+
+def test_fp8_generic_paths(monkeypatch):
+    check_fp8("fp8 generic ragged", 300, 200, 77, beta=0.5, use_bias=True, epilogue="gelu_tanh", seed=96,
+              expect_kernel="generic64x64x32")
+    check_fp8("fp8 generic unaligned", 256, 256, 256, offsets=(3, 5, 1), lda=259, ldb=261, ldc=257, seed=97,
+              expect_kernel="generic64x64x32")
+    check_fp8("fp8 K=0", 70, 50, 0, beta=2.0, use_bias=True, epilogue="relu", seed=98,
+              expect_kernel="generic64x64x32")
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", "generic64x64x32")
+    check_fp8("fp8 generic forced on a tile shape", 512, 512, 256, seed=99, expect_kernel="generic64x64x32")
+
+
 # ------------------------------------------- the five workloads, full size ---
 
 def sample_coords(M, N, tile, rng, n_random):
@@ -464,6 +547,8 @@ def test_workload_full_size_sampled(name):
     d = inputs.make_inputs(w)
     if w.out == "int8":
         return _workload_q8_sampled(w, d)
+    if w.inp == "fp8":
+        return _workload_fp8_sampled(w, d)
     M, N, K = w.M, w.N, w.K
     C0 = d.get("C0")
     C_init = C0 if C0 is not None else np.full(N * M, NAN_BF16, np.uint16)
@@ -502,3 +587,25 @@ def _workload_q8_sampled(w, d):
     ref, t = oracle.quantize_i8_array(y, scale[ms], w.zero_point)
     rep = assert_q8_within_tolerance(got[ms + ns * M], ref, t, scale[ms], w.zero_point, K, w.name)
     say(f"[parity-q8] workload {w.name}: ok exact={rep['exact']}/{rep['n']} near_boundary={rep['near_boundary']}")
+
+
+def _workload_fp8_sampled(w, d):
+    M, N, K = w.M, w.N, w.K
+    kname = gb.gemm_fp8_kernel_name(M, N, K, 4096, K, 4096, K, 4096, M, EPI[w.epilogue])
+    say(f"[parity-fp8] workload {w.name}: M={M} N={N} K={K} kernel={kname}")
+    a_t, a_p = to_dev_u8(d["A"])
+    b_t, b_p = to_dev_u8(d["B"])
+    c_t, c_p = to_dev(np.full(N * M, NAN_BF16, np.uint16))
+    sa_t = torch.from_numpy(d["scale_a"]).cuda()
+    sb_t = torch.from_numpy(d["scale_b"]).cuda()
+    st = gb.gemm_fp8(M, N, K, a_p, K, b_p, K, c_p, M, w.alpha, w.beta, sa_t.data_ptr(), sb_t.data_ptr(), 0,
+                     EPI[w.epilogue], torch.cuda.current_stream().cuda_stream)
+    assert st == 0, gb.gemm_bf16_status_string(st)
+    torch.cuda.synchronize()
+    got = from_dev(c_t, 0, N * M)
+    rng = np.random.Generator(np.random.PCG64(7 + w.index))
+    ms, ns = sample_coords(M, N, 256, rng, 20000)
+    ref_bits = oracle.gemm_fp8_elems(M, N, K, d["A"], K, d["B"], K, ms, ns, scale_a=d["scale_a"],
+                                     scale_b=d["scale_b"], epilogue=w.epilogue, nthreads=_threads())
+    rep = assert_within_tolerance(got[ms + ns * M], ref_bits, K, w.name)
+    say(f"[parity-fp8] workload {w.name}: ok n={rep['n']} max_ulp={rep['max_ulp']:.2f} exact={rep['exact']}")

@@ -652,3 +652,18 @@ def test_p17_fp8_identity_and_scale_axes():
     want = oracle.fp8_to_f64(B).reshape(N, M) * sa[None, :] * sb[:, None]
     assert np.all(same_value(got, oracle.bf16_from_f64(want)))
     assert oracle.fp8_to_f64(np.array([0x38], np.uint8))[0] == 1.0
+
+
+def test_p16_fp8_elems_agree_with_whole_product():
+    M, N, K = 40, 30, 300
+    A = inputs.normal_fp8(8501, M * K)
+    B = inputs.normal_fp8(8502, N * K)
+    sa = inputs.uniform_f32(8503, M, 0.5, 2.0)
+    sb = inputs.uniform_f32(8504, N, 0.5, 2.0)
+    C0 = inputs.normal_bf16(8505, N * M)
+    bias = inputs.normal_bf16(8506, N, scale=0.1)
+    full = oracle.gemm_fp8(M, N, K, A, K, B, K, C0, M, 1.5, 0.25, sa, sb, bias, "gelu_tanh")
+    g = np.random.Generator(np.random.PCG64(8507))
+    ms, ns = g.integers(0, M, 300), g.integers(0, N, 300)
+    el = oracle.gemm_fp8_elems(M, N, K, A, K, B, K, ms, ns, C0, M, 1.5, 0.25, sa, sb, bias, "gelu_tanh")
+    assert np.array_equal(el, full[ms + ns * M])
