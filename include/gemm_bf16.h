@@ -17,8 +17,14 @@
  * gemm_bf16_q8 writes int8 instead: the same fp32 epilogue value, then a
  * per-row quantization (section 6.2 of the same article).
  *
- * Every function is thread-safe.  The library keeps no pointer after a call
- * returns and allocates no device memory.
+ * Every function is thread-safe.  The library keeps no pointer to caller
+ * buffers after a call returns.  Its one device allocation is the split-K
+ * workspace of the short-product kernel (1 <= M <= 64 with few columns):
+ * a per-(device, stream) buffer of fp32 partial sums and per-strip counters,
+ * allocated with hipMalloc and zeroed with hipMemsetAsync on the first call
+ * that needs it, grown (after synchronising that stream) when a later call
+ * needs more, and kept until the process ends.  Calls whose shape needs no
+ * split, and every other kernel, allocate nothing.
  */
 #ifndef GEMM_BF16_H
 #define GEMM_BF16_H
@@ -83,7 +89,9 @@ enum gemm_bf16_status {
  * bounds-checked path that computes the same result more slowly.
  *
  * Ownership: all buffers belong to the caller and must stay valid until the
- * enqueued work has completed.  A, B and bias must not overlap C.
+ * enqueued work has completed.  A, B and bias must not overlap C.  The
+ * split-K workspace (see above) is shared by the calls on one stream, which
+ * run in order; calls on different streams use different workspaces.
  *
  * Returns GEMM_OK or a negative gemm_bf16_status.
  */
@@ -169,7 +177,7 @@ int gemm_bf16_last_hip_error(void);
 
 /*
  * gemm_bf16_kernel_name -- name of the kernel configuration gemm_bf16 would
- * launch for these arguments (static storage), e.g. "tile256x256x64_s2",
+ * launch for these arguments (static storage), e.g. "ring256x256x64",
  * or "none" when nothing would be launched or the arguments are invalid.
  * Makes no HIP call apart from querying the current device's compute-unit
  * count.  Pointers are only inspected for their alignment.

@@ -19,11 +19,12 @@
  *    "Recap of Simon's blog": the product C[m,n] = A[m,k] x B[k,n];
  *    section "Experimental setup": bf16 matrices, A row-major, B and C
  *    column-major.
- *  - The same article, sections 1.2 and 6.3: low-precision FP8 inputs; the
- *    fp8 product below takes OCP FP8 E4M3 operands (4 exponent bits, bias 7,
- *    3 mantissa bits, no infinities, S.1111.111 = NaN) with optional
- *    per-row scales of A and per-column scales of B.
- *  - DeepGEMM kernel-set article (demingchina.com), section 1.1: the BLAS
+ *  - DeepGEMM kernel-set article (demingchina.com), sections 1.2 and 6.3:
+ *    low-precision FP8 inputs; the fp8 product below takes OCP FP8 E4M3
+ *    operands (4 exponent bits, bias 7, 3 mantissa bits, no infinities,
+ *    S.1111.111 = NaN) with optional per-row scales of A and per-column
+ *    scales of B.
+ *  - The same DeepGEMM article, section 1.1: the BLAS
  *    form C = alpha*A*B + beta*C; section 3.1: low-precision inputs with
  *    high-precision accumulation; section 6.1: bias is added first, then the
  *    activation (ReLU/GELU) is applied, then the result is written;
