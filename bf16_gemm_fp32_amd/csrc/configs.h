@@ -33,11 +33,15 @@ struct ShapeFp8 { static constexpr int BM = 256, BN = 256, BK = 128; };
 
 hipError_t launch_tile_large(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_medium(const GemmArgs &args, int cus, hipStream_t stream);
+// split-K on the 128x128 tiles (split.P: splits * M * N floats of workspace)
+hipError_t launch_tile_medium_splitk(const GemmArgs &args, const TileSplit &split, int cus, hipStream_t stream);
 hipError_t launch_tile_ring_mfma32(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_ring(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_ring_masked(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_ring_q8(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_fp8(const GemmArgs &args, int cus, hipStream_t stream);
+// matrix-vector products: 1 <= M <= 4
+hipError_t launch_gemv(const GemmArgs &args, hipStream_t stream);
 // rows: 32 or 64 (the kernel's row block, M <= rows); cols: strip width
 hipError_t launch_skinny(int rows, int cols, const GemmArgs &args, const SkinnyWork &work, int cus,
                          hipStream_t stream);

@@ -46,6 +46,15 @@ struct GemmArgs {
     const float *scale_b;
 };
 
+// The K split of the tile kernel: `splits` ranges of `kper` K-slices (the
+// last may be shorter, none is empty); partial s of the element (m, n) is
+// P[s * pstride + n * ldp + m].
+struct TileSplit {
+    float *P;
+    int64_t ldp, pstride;
+    int splits, kper;
+};
+
 // Call f(std::integral_constant<uint32_t, flags>) for the run-time flag word,
 // so each launcher instantiates its kernel once per valid combination.
 template <class F>

@@ -20,14 +20,14 @@
 namespace gb {
 
 enum KernelKind {
-    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8, kNumKinds
+    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8, kSplitK, kGemv, kNumKinds
 };
 
 static const char *const kKindNames[kNumKinds] = {"none",            "tile256x256x32_s5", "tile128x128x64_s4",
                                                   "skinny",          "generic64x64x32",
                                                   "ring256x256x64_mfma32", "ring256x256x64",
                                                   "ring256x256x64_masked", "ring256x256x64_q8",
-                                                  "fp8_256x256x128"};
+                                                  "fp8_256x256x128",  "splitk128x128x64", "gemv"};
 
 static const char *kind_name(int k) { return (k >= 0 && k < kNumKinds) ? kKindNames[k] : "none"; }
 
@@ -133,6 +133,19 @@ static bool skinny_path_ok(int64_t M, int64_t N, int64_t K, const void *A, int64
     return true;
 }
 
+// The matrix-vector kernel: 1 <= M <= 4, K a multiple of 8, lda and ldb
+// multiples of 8, A and B 16-byte aligned, 32-bit byte offsets within four
+// rows of A and four columns of B (C may have any ldc).
+static bool gemv_path_ok(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+                         int64_t ldb) {
+    if (M <= 0 || M > 4 || N <= 0 || K <= 0 || K % 8) return false;
+    if (lda % 8 || ldb % 8) return false;
+    if (!aligned16(A) || !aligned16(B)) return false;
+    const int64_t lim = (int64_t)1 << 31;
+    if ((4 * lda + K) * 2 >= lim || (4 * ldb + K) * 2 >= lim) return false;
+    return true;
+}
+
 // How the streaming kernel covers a short product: its row block (32 or
 // 64), strip width, and the K split.  32-column strips measured fastest at
 // every size tried (the wider ones exist for experiments).  K is split only
@@ -229,6 +242,44 @@ static hipError_t launch_skinny_plan(const GemmArgs &args, int cus, hipStream_t 
     return launch_skinny(p.rows, p.cols, args, work, cus, stream);
 }
 
+// Split-K on the 128x128 tiles: used when those tiles alone would leave more
+// than half of the compute units idle.  The K-slices (64 wide) are cut into
+// up to CUs / tiles ranges of at least kMinSlices slices each, so every
+// range still runs a pipelined loop; partials take splits * M * N floats of
+// workspace (at most 4M floats: splits * tiles <= CUs and a tile is 16K
+// elements).  Returns 1 when no split applies.
+constexpr int kSplitMinSlices = 8;
+
+static TileSplit plan_splitk(int64_t M, int64_t N, int64_t K, int cus) {
+    TileSplit p{};
+    p.splits = 1;
+    const int64_t tiles = (M / ShapeM::BM) * (N / ShapeM::BN);
+    const int64_t nk = K / ShapeM::BK;
+    if (tiles <= 0 || tiles * 2 >= cus) return p;
+    int64_t splits = cus / tiles;
+    if (const char *env = std::getenv("GEMM_BF16_SPLITK_SPLITS")) {  // tuning knob
+        const int v = std::atoi(env);
+        if (v >= 1) splits = v;
+    }
+    const int64_t max_splits = nk / kSplitMinSlices;
+    if (splits > max_splits) splits = max_splits;
+    if (splits < 2) return p;
+    p.kper = (int)((nk + splits - 1) / splits);
+    p.splits = (int)((nk + p.kper - 1) / p.kper);  // no empty range
+    p.ldp = M;
+    p.pstride = M * N;
+    return p;
+}
+
+static hipError_t launch_splitk_plan(const GemmArgs &args, int cus, hipStream_t stream) {
+    TileSplit p = plan_splitk(args.M, args.N, args.K, cus);
+    if (p.splits < 2) return launch_tile_medium(args, cus, stream);
+    uint32_t *unused = nullptr;
+    hipError_t err = get_workspace(stream, 0, (size_t)p.splits * (size_t)args.M * (size_t)args.N, &unused, &p.P);
+    if (err != hipSuccess) return err;
+    return launch_tile_medium_splitk(args, p, cus, stream);
+}
+
 // Kernel for a shape.  GEMM_BF16_FORCE_KERNEL=<name> (a kKindNames entry)
 // overrides the choice when that kernel can run the shape; it exists for
 // testing and benchmarking the alternatives.
@@ -240,15 +291,21 @@ static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t
     const bool okR = tile_path_ok<ShapeRing>(M, N, K, A, lda, B, ldb, C, ldc);
     const bool okRM = ring_masked_ok(M, N, K, A, lda, B, ldb, C, ldc);
     const bool okS = skinny_path_ok(M, N, K, A, lda, B, ldb, C, ldc);
+    const bool okV = gemv_path_ok(M, N, K, A, lda, B, ldb);
     if (const char *force = std::getenv("GEMM_BF16_FORCE_KERNEL")) {
         if (!std::strcmp(force, kKindNames[kGeneric])) return kGeneric;
         if (!std::strcmp(force, kKindNames[kLarge]) && okL) return kLarge;
         if (!std::strcmp(force, kKindNames[kMedium]) && okM) return kMedium;
+        if (!std::strcmp(force, kKindNames[kSplitK]) && okM && plan_splitk(M, N, K, cus).splits >= 2)
+            return kSplitK;
         if (!std::strcmp(force, kKindNames[kRing32]) && okR) return kRing32;
         if (!std::strcmp(force, kKindNames[kRing]) && okR) return kRing;
         if (!std::strcmp(force, kKindNames[kRingMasked]) && okRM) return kRingMasked;
         if (!std::strcmp(force, kKindNames[kSkinny]) && okS) return kSkinny;
+        if (!std::strcmp(force, kKindNames[kGemv]) && okV) return kGemv;
     }
+    // One to four rows: the matrix-vector kernel.
+    if (okV) return kGemv;
     // At most 64 rows: the streaming kernel (a 256- or 128-row tile would be
     // mostly empty).
     if (okS) return kSkinny;
@@ -263,7 +320,7 @@ static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t
         const int64_t tiles = (M / ShapeL::BM) * (N / ShapeL::BN);
         if (tiles * 2 >= cus || !okM) return kLarge;
     }
-    if (okM) return kMedium;
+    if (okM) return plan_splitk(M, N, K, cus).splits >= 2 ? kSplitK : kMedium;
     return kGeneric;
 }
 
@@ -353,6 +410,8 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t lda
     switch (choose_kernel(M, N, K, A, lda, B, ldb, C, ldc, cus)) {
     case kLarge: err = launch_tile_large(args, cus, stream); break;
     case kMedium: err = launch_tile_medium(args, cus, stream); break;
+    case kSplitK: err = launch_splitk_plan(args, cus, stream); break;
+    case kGemv: err = launch_gemv(args, stream); break;
     case kRing32: err = launch_tile_ring_mfma32(args, cus, stream); break;
     case kRing: err = launch_tile_ring(args, cus, stream); break;
     case kRingMasked: err = launch_tile_ring_masked(args, cus, stream); break;

@@ -45,6 +45,18 @@
 // these row widths and this lane-to-phase map.  The direct-to-LDS load writes a wave's 64 lanes to 1 KiB of
 // consecutive LDS bytes, so the swizzle is applied on the global side: lane
 // i fetches the chunk that belongs at its LDS position.
+//
+// Split-K.  When the tiles alone would leave most compute units idle (a
+// 1024 x 1024 output is 64 tiles of 128x128 for 256 compute units), the
+// K-slices are cut into `splits` contiguous ranges and a work unit is one
+// (range, tile) pair: unit u = s * tiles + t, so the units of one range run
+// side by side and the compute units of one XCD share their A rows and B
+// columns in L2.  A unit stores its fp32 partial tile to a workspace instead
+// of running the epilogue; splitk_reduce_kernel then adds the partials of
+// each element in range order (the same order on every run, so results are
+// deterministic) and applies the fused epilogue.  The partials cross XCDs,
+// whose L2s are not coherent with each other, so the reduction is a second
+// kernel on the same stream: the kernel boundary makes the partials visible.
 #pragma once
 
 #include "device_common.h"
@@ -306,9 +318,32 @@ struct TileKernel {
 // Requirements checked by the host before launch: M % BM == 0, N % BN == 0,
 // K % BK == 0, K > 0, A/B/C 16-byte aligned, lda/ldb/ldc multiples of 8, and
 // BM*lda*2 + 2K, BN*ldb*2 + 2K below 2^31 (32-bit buffer offsets).
-template <class Cfg, uint32_t kFlags>
+// Store a wave's accumulators as fp32 partial sums: a 32x32 MFMA result
+// gives lane l column l % 32 and, in registers 4g..4g+3, rows
+// 8g + 4(l/32) + 0..3, one 16-byte store each.
+template <class Cfg>
+__device__ __forceinline__ void tile_store_partial(const TileSplit &split, int s, int64_t m0, int64_t n0, int wm,
+                                                   int wn, int lane, const f32x16 (&acc)[Cfg::FM][Cfg::FN]) {
+    float *base = split.P + (int64_t)s * split.pstride;
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+        const int64_t n = n0 + wn * Cfg::WTN + j * 32 + (lane & 31);
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int64_t m = m0 + wm * Cfg::WTM + i * 32 + g * 8 + (lane >> 5) * 4;
+                const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                *(f32x4 *)(base + n * split.ldp + m) = v;
+            }
+    }
+}
+
+// kSplit: the units are (K range, tile) pairs and each stores its partial
+// (kFlags is then unused: the reduction applies the epilogue).
+template <class Cfg, uint32_t kFlags, bool kSplit = false>
 __global__ void __launch_bounds__(Cfg::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-gemm_tile_kernel(const GemmArgs args, const TileSchedule sched) {
+gemm_tile_kernel(const GemmArgs args, const TileSchedule sched, const TileSplit split) {
     using TK = TileKernel<Cfg>;
     constexpr int S = Cfg::STAGES;
     constexpr int L = Cfg::kLoads;
@@ -342,18 +377,28 @@ gemm_tile_kernel(const GemmArgs args, const TileSchedule sched) {
     for (int kk = 0; kk < Cfg::KSTEPS; ++kk)
         Ln.chunk_off[kk] = (uint32_t)(((2 * kk + (lane >> 5)) ^ lds_swizzle<Cfg::BK>(lane & 31)) << 4);
 
-    const int nk = (int)(args.K / Cfg::BK);
+    const int nk_all = (int)(args.K / Cfg::BK);
     const int num_tiles = sched.num_tiles();
+    const int num_units = kSplit ? num_tiles * split.splits : num_tiles;
 
-    for (int t = sched.slot(blockIdx.x); t < num_tiles; t += sched.grid) {
+    for (int u = sched.slot(blockIdx.x); u < num_units; u += sched.grid) {
+        int t = u, s = 0, nk = nk_all;
+        if constexpr (kSplit) {
+            s = u / num_tiles;
+            t = u - s * num_tiles;
+            const int rest = nk_all - s * split.kper;
+            nk = rest < split.kper ? rest : split.kper;
+        }
         int tm, tn;
         sched.tile(t, tm, tn);
         const int64_t m0 = (int64_t)tm * Cfg::BM;
         const int64_t n0 = (int64_t)tn * Cfg::BN;
+        const int64_t k0 = kSplit ? (int64_t)s * split.kper * Cfg::BK : 0;
+        const int64_t kn = (int64_t)nk * Cfg::BK;
         const __amdgpu_buffer_rsrc_t rA =
-            make_rsrc(args.A + m0 * args.lda, (uint32_t)(((Cfg::BM - 1) * args.lda + args.K) * 2));
+            make_rsrc(args.A + m0 * args.lda + k0, (uint32_t)(((Cfg::BM - 1) * args.lda + kn) * 2));
         const __amdgpu_buffer_rsrc_t rB =
-            make_rsrc(args.B + n0 * args.ldb, (uint32_t)(((Cfg::BN - 1) * args.ldb + args.K) * 2));
+            make_rsrc(args.B + n0 * args.ldb + k0, (uint32_t)(((Cfg::BN - 1) * args.ldb + kn) * 2));
 
         f32x16 acc[Cfg::FM][Cfg::FN];
 #pragma unroll
@@ -393,10 +438,69 @@ gemm_tile_kernel(const GemmArgs args, const TileSchedule sched) {
         }
         TK::template slice<false, false>(smem, kt, cur, false, false, 0, Ln, rA, rB, fa, fb, acc);
 
-        // Every wave is done reading the ring (all loads landed at the last
-        // wait): its memory now stages the epilogue.
-        lds_barrier();
-        tile_epilogue<Cfg, kFlags>(smem, args, m0, n0, wm, wn, lane, Ln.wave, acc);
+        if constexpr (kSplit) {
+            tile_store_partial<Cfg>(split, s, m0, n0, wm, wn, lane, acc);
+        } else {
+            // Every wave is done reading the ring (all loads landed at the
+            // last wait): its memory now stages the epilogue.
+            lds_barrier();
+            tile_epilogue<Cfg, kFlags>(smem, args, m0, n0, wm, wn, lane, Ln.wave, acc);
+        }
+    }
+}
+
+// The split-K reduction: thread i takes 8 consecutive rows of one column,
+// adds the splits' partials in range order, applies alpha, beta*C, bias and
+// the activation in fp32 and writes one 16-byte run of bf16 C.  Requires
+// M % 8 == 0, C 16-byte aligned and ldc % 8 == 0 (true on the tile path).
+template <uint32_t kFlags>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs args, const TileSplit split) {
+    const int64_t chunks_m = args.M / 8;
+    const int64_t total = chunks_m * args.N;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
+        const int64_t n = idx / chunks_m;
+        const int64_t m = (idx - n * chunks_m) * 8;
+        // Loads of four ranges go out before their sums, so the memory
+        // latency is paid once per four ranges; the adds keep range order.
+        const float *p = split.P + n * split.ldp + m;
+        f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+        int s = 0;
+        for (; s + 4 <= split.splits; s += 4) {
+            f32x4 l[4], h[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                l[u] = *(const f32x4 *)(p + (int64_t)(s + u) * split.pstride);
+                h[u] = *(const f32x4 *)(p + (int64_t)(s + u) * split.pstride + 4);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                lo += l[u];
+                hi += h[u];
+            }
+        }
+        for (; s < split.splits; ++s) {
+            lo += *(const f32x4 *)(p + (int64_t)s * split.pstride);
+            hi += *(const f32x4 *)(p + (int64_t)s * split.pstride + 4);
+        }
+        uint16_t *c = args.C + n * args.ldc + m;
+        float bias_v = 0.f;
+        if constexpr ((kFlags & kEpiBias) != 0) bias_v = bf16_bits_to_f32(args.bias[n]);
+        float cin[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if constexpr ((kFlags & kEpiBeta) != 0) {
+            const u32x4 raw = *(const u32x4 *)c;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                cin[2 * e] = bf16_bits_to_f32(raw[e] & 0xFFFFu);
+                cin[2 * e + 1] = bf16_bits_to_f32(raw[e] >> 16);
+            }
+        }
+        const float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        u32x4 out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            out[e] = pack_bf16x2(epilogue_value<kFlags>(x[2 * e], cin[2 * e], bias_v, args.alpha, args.beta),
+                                 epilogue_value<kFlags>(x[2 * e + 1], cin[2 * e + 1], bias_v, args.alpha, args.beta));
+        __builtin_nontemporal_store(out, (u32x4 *)c);
     }
 }
 
@@ -414,8 +518,38 @@ hipError_t launch_tile(const GemmArgs &args, int cus, hipStream_t stream) {
     const int tiles = s.num_tiles();
     s.grid = tiles < cus ? tiles : cus;
     const dim3 grid(s.grid), block(Cfg::kThreads);
+    const TileSplit none{};
     dispatch_flags(args.flags, [&](auto f) {
-        hipLaunchKernelGGL((gemm_tile_kernel<Cfg, decltype(f)::value>), grid, block, 0, stream, args, s);
+        hipLaunchKernelGGL((gemm_tile_kernel<Cfg, decltype(f)::value>), grid, block, 0, stream, args, s, none);
+    });
+    return hipGetLastError();
+}
+
+// Split-K launch: the tile kernel over (range, tile) units into the
+// workspace split.P, then the reduction with the epilogue flags baked in.
+// The host has checked the tile-path requirements, split.splits >= 2, every
+// range non-empty, and that split.P holds splits * M * N floats (ldp = M,
+// pstride = M * N).
+template <class Cfg>
+hipError_t launch_tile_splitk(const GemmArgs &args, const TileSplit &split, int cus, hipStream_t stream) {
+    TileSchedule s{};
+    s.tiles_m = (int)(args.M / Cfg::BM);
+    s.tiles_n = (int)(args.N / Cfg::BN);
+    s.group_m = 4;
+    s.order = kOrderGrouped;
+    s.hilbert_log2 = 0;
+    const int units = s.num_tiles() * split.splits;
+    s.grid = units < cus ? units : cus;
+    hipLaunchKernelGGL((gemm_tile_kernel<Cfg, 0u, true>), dim3(s.grid), dim3(Cfg::kThreads), 0, stream, args, s,
+                       split);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t threads = args.M / 8 * args.N;
+    const int64_t blocks = (threads + 255) / 256;
+    const int64_t cap = (int64_t)cus * 8;
+    const dim3 rgrid((unsigned)(blocks < cap ? blocks : cap));
+    dispatch_flags(args.flags, [&](auto f) {
+        hipLaunchKernelGGL((splitk_reduce_kernel<decltype(f)::value>), rgrid, dim3(256), 0, stream, args, split);
     });
     return hipGetLastError();
 }

@@ -1,4 +1,5 @@
-// tile_medium.hip -- instances of the 128x128x64, 4-stage tile kernel.
+// tile_medium.hip -- instances of the 128x128x64, 4-stage tile kernel (whole
+// K, and split-K with its reduction).
 #include "configs.h"
 #include "kernel_tile.h"
 
@@ -9,6 +10,10 @@ static_assert(CfgMedium::BM == ShapeM::BM && CfgMedium::BN == ShapeM::BN && CfgM
 
 hipError_t launch_tile_medium(const GemmArgs &args, int cus, hipStream_t stream) {
     return launch_tile<CfgMedium>(args, cus, stream);
+}
+
+hipError_t launch_tile_medium_splitk(const GemmArgs &args, const TileSplit &split, int cus, hipStream_t stream) {
+    return launch_tile_splitk<CfgMedium>(args, split, cus, stream);
 }
 
 }  // namespace gb

@@ -136,11 +136,19 @@ def test_kernel_selection_names():
     assert name(4000, 4000, 4000, P, 4000, P, 4000, P, 4000) == "ring256x256x64_masked"
     assert name(4000, 2000, 1000, P, 1000, P, 1000, P, 4000) == "ring256x256x64_masked"
     assert name(256, 256, 256, P, 256, P, 256, P, 256) == "tile128x128x64_s4"
+    # small grids of 128-tiles with enough K-slices: split-K
+    assert name(1024, 1024, 4096, P, 4096, P, 4096, P, 1024) == "splitk128x128x64"
+    assert name(512, 512, 8192, P, 8192, P, 8192, P, 512) == "splitk128x128x64"
+    assert name(512, 512, 512, P, 512, P, 512, P, 512) == "tile128x128x64_s4"   # 8 slices: no split
+    assert name(2048, 2048, 4096, P, 4096, P, 4096, P, 2048) == "tile128x128x64_s4"  # 256 tiles
     assert name(1000, 1000, 1000, P, 1000, P, 1000, P, 1000) == "generic64x64x32"
     assert name(64, 8192, 8192, P, 8192, P, 8192, P, 64) == "skinny"
     assert name(32, 4096, 1024, P, 1024, P, 1024, P, 32) == "skinny"
     assert name(48, 4096, 1024, P, 1024, P, 1024, P, 48) == "skinny"
-    assert name(1, 4096, 4096, P, 4096, P, 4096, P, 8) == "skinny"
+    assert name(1, 4096, 4096, P, 4096, P, 4096, P, 8) == "gemv"
+    assert name(4, 4096, 4096, P, 4096, P, 4096, P, 4) == "gemv"
+    assert name(5, 4096, 4096, P, 4096, P, 4096, P, 8) == "skinny"
+    assert name(1, 4096, 4100, P, 4100, P, 4100, P, 1) == "generic64x64x32"   # K % 8 != 0
     assert name(48, 4096, 1020, P, 1020, P, 1020, P, 48) == "generic64x64x32"
     assert name(65, 4096, 1024, P, 1024, P, 1024, P, 72) != "skinny"
     assert name(4096, 4096, 4096, P + 2, 4096, P, 4096, P, 4096) == "generic64x64x32"

@@ -148,6 +148,53 @@ def test_tile_path_padded_leading_dims():
                expect_kernel="ring256x256x64_masked")
 
 
+# Split-K on the 128x128 tiles (small grids): the K-slices are cut into
+# ranges whose fp32 partials a second kernel adds in range order, then runs
+# the epilogue.  Shapes with 2, 3 (uneven: 9, 9, 7 slices), 4, 8 and 16
+# ranges, padded leading dimensions, every epilogue combination, forced
+# split counts, and run-to-run bit equality.
+SPLITK = "splitk128x128x64"
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (512, 512, 1024),    # 16 tiles, 16 slices: 2 ranges
+    (256, 256, 1600),    # 4 tiles, 25 slices: 3 ranges of 9, 9, 7
+    (256, 384, 2048),    # 6 tiles: 4 ranges
+    (512, 256, 4096),    # 8 tiles: 8 ranges
+    (128, 128, 8192),    # 1 tile: 16 ranges
+])
+def test_splitk_full(M, N, K):
+    check_full(f"splitk {M}x{N}x{K}", M, N, K, seed=M + 3 * N + K, expect_kernel=SPLITK)
+
+
+@pytest.mark.parametrize("beta,use_bias,epi", [(b, u, e) for b in (0.0, -0.75) for u in (False, True)
+                                               for e in ("none", "gelu_tanh", "relu")])
+def test_splitk_epilogue_combinations(beta, use_bias, epi):
+    check_full(f"splitk beta={beta} bias={use_bias} {epi}", 256, 384, 1024, alpha=1.25, beta=beta,
+               use_bias=use_bias, epilogue=epi, seed=40 + int(abs(beta) * 4) + 2 * use_bias + len(epi),
+               expect_kernel=SPLITK)
+
+
+def test_splitk_padded_leading_dims():
+    check_full("splitk padded ld", 512, 256, 2048, lda=2056, ldb=2064, ldc=520, beta=0.5, use_bias=True,
+               epilogue="gelu_tanh", seed=51, expect_kernel=SPLITK)
+
+
+@pytest.mark.parametrize("splits", [2, 3, 5, 7])
+def test_splitk_forced_split_counts(splits, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_SPLITK_SPLITS", str(splits))
+    check_full(f"splitk forced {splits} ranges", 384, 256, 3840, beta=0.25, use_bias=True, seed=60 + splits,
+               expect_kernel=SPLITK)
+
+
+def test_splitk_deterministic():
+    M, N, K = 512, 256, 4096
+    case = inputs.random_case(70, M, N, K, with_c0=False, with_bias=False)
+    C_init = np.full(N * M, NAN_BF16, np.uint16)
+    runs = [run_gpu(M, N, K, case["A"], K, case["B"], K, C_init, M, 1.0, 0.0, None, "none") for _ in range(3)]
+    assert np.array_equal(runs[0], runs[1]) and np.array_equal(runs[0], runs[2]), "split-K results vary"
+
+
 # Every tile kernel forced onto shapes whose K-slice count walks through the
 # pipeline's prologue and tail cases (1 .. 10 slices, fewer and more slices
 # than LDS stages, odd and even counts).
@@ -258,8 +305,43 @@ def test_skinny_widths_and_splits(cols, splits, monkeypatch):
 @pytest.mark.parametrize("splits", ["1", "3"])
 def test_skinny_tails(M, N, K, lda, ldb, ldc, splits, monkeypatch):
     monkeypatch.setenv("GEMM_BF16_SKINNY_SPLITS", splits)
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", SK)  # M <= 4 would take the matrix-vector kernel
     check_full(f"skinny tails {M}x{N}x{K} splits={splits}", M, N, K, lda=lda, ldb=ldb, ldc=ldc, beta=0.0,
                seed=M + N + K, expect_kernel=SK, poison_pad=True)
+
+
+# The matrix-vector kernel (1 to 4 rows): several K blocks with tails, N
+# tails inside a wave's columns, NaN padding, any ldc and C alignment,
+# every epilogue combination.
+GV = "gemv"
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc", [
+    (1, 4096, 4096, 4096, 4096, 1),      # decode: one full K block
+    (2, 1000, 1032, 1032, 1040, 2),      # N % 4 == 0, K tail inside the block
+    (3, 333, 8, 8, 8, 3),                # a single 8-wide K chunk; an odd N leaves a 1-column wave
+    (4, 129, 4104, 4104, 4112, 4),       # whole blocks and an 8-wide last block
+    (1, 1, 8, 8, 8, 1),                  # the smallest product
+    (4, 4097, 8200, 8200, 8200, 8),      # two blocks and a tail; a 1-column last wave
+    (1, 5, 12296, 12304, 12296, 1),      # three blocks and a tail
+    (3, 2050, 4096, 4096, 4104, 5),      # ldc > M
+])
+def test_gemv_shapes(M, N, K, lda, ldb, ldc):
+    check_full(f"gemv {M}x{N}x{K}", M, N, K, lda=lda, ldb=ldb, ldc=ldc, beta=0.0, seed=M + N + K + 5,
+               expect_kernel=GV, poison_pad=True)
+
+
+@pytest.mark.parametrize("beta,use_bias,epi", [(b, u, e) for b in (0.0, -0.75) for u in (False, True)
+                                               for e in ("none", "gelu_tanh", "relu")])
+def test_gemv_epilogue_combinations(beta, use_bias, epi):
+    check_full(f"gemv beta={beta} bias={use_bias} {epi}", 3, 515, 1000, ldc=3, alpha=1.25, beta=beta,
+               use_bias=use_bias, epilogue=epi, seed=80 + int(abs(beta) * 4) + 2 * use_bias + len(epi),
+               expect_kernel=GV)
+
+
+def test_gemv_unaligned_c_with_beta():
+    check_full("gemv unaligned C", 2, 777, 520, ldc=3, beta=0.5, use_bias=True, epilogue="gelu_tanh",
+               offsets=(0, 0, 1), seed=93, expect_kernel=GV)
 
 
 def test_skinny_unaligned_c_with_beta():
