@@ -19,12 +19,15 @@
  *
  * Every function is thread-safe.  The library keeps no pointer to caller
  * buffers after a call returns.  Its one device allocation is the split-K
- * workspace of the short-product kernel (1 <= M <= 64 with few columns):
- * a per-(device, stream) buffer of fp32 partial sums and per-strip counters,
- * allocated with hipMalloc and zeroed with hipMemsetAsync on the first call
- * that needs it, grown (after synchronising that stream) when a later call
- * needs more, and kept until the process ends.  Calls whose shape needs no
- * split, and every other kernel, allocate nothing.
+ * workspace (fp32 partial sums, and counters for the short-product kernel)
+ * used by two kinds of shape: 5 <= M <= 64 with few columns, and products
+ * whose 128x128 tiles would leave most compute units idle (for example
+ * 1024 x 1024 x 4096).  It is one buffer per (device, stream), allocated
+ * with hipMalloc and its counters zeroed with hipMemsetAsync on the first
+ * call that needs it, grown (after synchronising that stream) when a later
+ * call needs more, and kept until the process ends; it holds at most about
+ * 16 MiB on a 256-CU device.  Calls whose shape needs no split allocate
+ * nothing.
  */
 #ifndef GEMM_BF16_H
 #define GEMM_BF16_H
