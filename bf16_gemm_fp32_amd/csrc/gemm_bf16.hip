@@ -188,7 +188,9 @@ static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int cus) {
 // counter) followed by the fp32 partials.  Calls on one stream are ordered,
 // so they can share it; a call on another stream gets its own.  It grows on
 // demand (after draining the stream, whose work may still use the old one)
-// and lives until the process ends.
+// and lives until the process ends.  The caller holds g_ws_mutex from the
+// lookup until its kernels are enqueued, so a growth started by another
+// thread on the same stream cannot free the buffer in between.
 struct Workspace {
     char *base = nullptr;
     size_t counter_bytes = 0, partial_bytes = 0;
@@ -202,7 +204,6 @@ static hipError_t get_workspace(hipStream_t stream, size_t counters, size_t part
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
     const size_t need_c = (counters * 4 + 255) / 256 * 256, need_p = partial_floats * 4;
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace &w = g_ws[std::make_pair(dev, stream)];
     if (w.base == nullptr || w.counter_bytes < need_c || w.partial_bytes < need_p) {
         const size_t nc = need_c > w.counter_bytes ? need_c : w.counter_bytes;
@@ -236,8 +237,10 @@ static hipError_t launch_skinny_plan(const GemmArgs &args, int cus, hipStream_t 
     work.c_vector = aligned16(args.C) && args.ldc % 8 == 0;
     if (p.splits > 1) {
         const size_t floats = (size_t)p.strips * p.splits * p.cols * p.rows;
+        std::lock_guard<std::mutex> lock(g_ws_mutex);
         hipError_t err = get_workspace(stream, (size_t)p.strips, floats, &work.counters, &work.partials);
         if (err != hipSuccess) return err;
+        return launch_skinny(p.rows, p.cols, args, work, cus, stream);
     }
     return launch_skinny(p.rows, p.cols, args, work, cus, stream);
 }
@@ -275,6 +278,7 @@ static hipError_t launch_splitk_plan(const GemmArgs &args, int cus, hipStream_t 
     TileSplit p = plan_splitk(args.M, args.N, args.K, cus);
     if (p.splits < 2) return launch_tile_medium(args, cus, stream);
     uint32_t *unused = nullptr;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
     hipError_t err = get_workspace(stream, 0, (size_t)p.splits * (size_t)args.M * (size_t)args.N, &unused, &p.P);
     if (err != hipSuccess) return err;
     return launch_tile_medium_splitk(args, p, cus, stream);
