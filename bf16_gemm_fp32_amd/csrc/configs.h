@@ -35,6 +35,9 @@ hipError_t launch_tile_large(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_medium(const GemmArgs &args, int cus, hipStream_t stream);
 // split-K on the 128x128 tiles (split.P: splits * M * N floats of workspace)
 hipError_t launch_tile_medium_splitk(const GemmArgs &args, const TileSplit &split, int cus, hipStream_t stream);
+// the same with int8 output (the reduction quantizes per row)
+hipError_t launch_tile_medium_splitk_q8(const GemmArgs &args, const TileSplit &split, int cus,
+                                        hipStream_t stream);
 hipError_t launch_tile_ring_mfma32(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_ring(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_ring_masked(const GemmArgs &args, int cus, hipStream_t stream);

@@ -20,14 +20,15 @@
 namespace gb {
 
 enum KernelKind {
-    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8, kSplitK, kGemv, kNumKinds
+    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8, kSplitK, kGemv, kSplitKQ8, kNumKinds
 };
 
 static const char *const kKindNames[kNumKinds] = {"none",            "tile256x256x32_s5", "tile128x128x64_s4",
                                                   "skinny",          "generic64x64x32",
                                                   "ring256x256x64_mfma32", "ring256x256x64",
                                                   "ring256x256x64_masked", "ring256x256x64_q8",
-                                                  "fp8_256x256x128",  "splitk128x128x64", "gemv"};
+                                                  "fp8_256x256x128",  "splitk128x128x64", "gemv",
+                                                  "splitk128x128x64_q8"};
 
 static const char *kind_name(int k) { return (k >= 0 && k < kNumKinds) ? kKindNames[k] : "none"; }
 
@@ -274,14 +275,16 @@ static TileSplit plan_splitk(int64_t M, int64_t N, int64_t K, int cus) {
     return p;
 }
 
-static hipError_t launch_splitk_plan(const GemmArgs &args, int cus, hipStream_t stream) {
+// kQ8: the quantizing output (the host chose this path only when the plan
+// splits).
+static hipError_t launch_splitk_plan(const GemmArgs &args, int cus, hipStream_t stream, bool q8 = false) {
     TileSplit p = plan_splitk(args.M, args.N, args.K, cus);
-    if (p.splits < 2) return launch_tile_medium(args, cus, stream);
+    if (p.splits < 2) return q8 ? hipErrorInvalidValue : launch_tile_medium(args, cus, stream);
     uint32_t *unused = nullptr;
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     hipError_t err = get_workspace(stream, 0, (size_t)p.splits * (size_t)args.M * (size_t)args.N, &unused, &p.P);
     if (err != hipSuccess) return err;
-    return launch_tile_medium_splitk(args, p, cus, stream);
+    return q8 ? launch_tile_medium_splitk_q8(args, p, cus, stream) : launch_tile_medium_splitk(args, p, cus, stream);
 }
 
 // Kernel for a shape.  GEMM_BF16_FORCE_KERNEL=<name> (a kKindNames entry)
@@ -330,7 +333,8 @@ static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t
 
 // The quantizing path: the masked ring kernel when its requirements hold
 // (also for Q, scale and ldq) and its 256x256 tiles give at least half the
-// compute units a tile, else the bounds-checked kernel.
+// compute units a tile; on smaller grids split-K on 128x128 tiles when the
+// shape allows it (its reduction quantizes); else the bounds-checked kernel.
 static int choose_kernel_q8(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
                             int64_t ldb, const void *C, int64_t ldc, float beta, const void *Q, int64_t ldq,
                             const void *scale, int cus) {
@@ -344,6 +348,9 @@ static int choose_kernel_q8(int64_t M, int64_t N, int64_t K, const void *A, int6
         const char *force = std::getenv("GEMM_BF16_FORCE_KERNEL");
         const bool forced = force && !std::strcmp(force, kKindNames[kRingQ8]);
         if (tiles * 2 >= cus || forced) return kRingQ8;
+        if (tile_path_ok<ShapeM>(M, N, K, A, lda, B, ldb, c_probe, ldc_probe) &&
+            plan_splitk(M, N, K, cus).splits >= 2)
+            return kSplitKQ8;
     }
     return kGeneric;
 }
@@ -459,10 +466,11 @@ int gemm_bf16_q8(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t 
 
     const int cus = device_cu_count();
     hipError_t err = hipSuccess;
-    if (choose_kernel_q8(M, N, K, A, lda, B, ldb, C, ldc, beta, Q, ldq, scale, cus) == kRingQ8)
-        err = launch_tile_ring_q8(args, cus, stream);
-    else
-        err = launch_generic(args, cus, stream);
+    switch (choose_kernel_q8(M, N, K, A, lda, B, ldb, C, ldc, beta, Q, ldq, scale, cus)) {
+    case kRingQ8: err = launch_tile_ring_q8(args, cus, stream); break;
+    case kSplitKQ8: err = launch_splitk_plan(args, cus, stream, true); break;
+    default: err = launch_generic(args, cus, stream); break;
+    }
     if (err != hipSuccess) {
         t_last_hip_error = (int)err;
         return GEMM_ERR_HIP;

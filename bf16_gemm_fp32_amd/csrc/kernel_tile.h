@@ -451,9 +451,12 @@ gemm_tile_kernel(const GemmArgs args, const TileSchedule sched, const TileSplit 
 
 // The split-K reduction: thread i takes 8 consecutive rows of one column,
 // adds the splits' partials in range order, applies alpha, beta*C, bias and
-// the activation in fp32 and writes one 16-byte run of bf16 C.  Requires
-// M % 8 == 0, C 16-byte aligned and ldc % 8 == 0 (true on the tile path).
-template <uint32_t kFlags>
+// the activation in fp32 and writes one 16-byte run of bf16 C -- or, with
+// kQ8, quantizes the 8 values with their rows' scales and writes 8 bytes of
+// int8 Q.  Requires M % 8 == 0, C 16-byte aligned and ldc % 8 == 0 (when C
+// is read or written), and for kQ8 Q and scale 16-byte aligned and
+// ldq % 8 == 0 (checked on the host).
+template <uint32_t kFlags, bool kQ8 = false>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs args, const TileSplit split) {
     const int64_t chunks_m = args.M / 8;
     const int64_t total = chunks_m * args.N;
@@ -495,12 +498,26 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs args,
             }
         }
         const float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        u32x4 out;
+        if constexpr (kQ8) {
+            const f32x4 s_lo = *(const f32x4 *)(args.scale + m);
+            const f32x4 s_hi = *(const f32x4 *)(args.scale + m + 4);
+            const float sc[8] = {s_lo.x, s_lo.y, s_lo.z, s_lo.w, s_hi.x, s_hi.y, s_hi.z, s_hi.w};
+            u32x2 qw = {0u, 0u};
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            out[e] = pack_bf16x2(epilogue_value<kFlags>(x[2 * e], cin[2 * e], bias_v, args.alpha, args.beta),
-                                 epilogue_value<kFlags>(x[2 * e + 1], cin[2 * e + 1], bias_v, args.alpha, args.beta));
-        __builtin_nontemporal_store(out, (u32x4 *)c);
+            for (int e = 0; e < 8; ++e) {
+                const float v = epilogue_value<kFlags>(x[e], cin[e], bias_v, args.alpha, args.beta);
+                qw[e >> 2] |= ((uint32_t)quantize_i8(v, sc[e], args.zp) & 0xFFu) << ((e & 3) * 8);
+            }
+            __builtin_nontemporal_store(qw, (u32x2 *)(args.Q + n * args.ldq + m));
+        } else {
+            u32x4 out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                out[e] = pack_bf16x2(
+                    epilogue_value<kFlags>(x[2 * e], cin[2 * e], bias_v, args.alpha, args.beta),
+                    epilogue_value<kFlags>(x[2 * e + 1], cin[2 * e + 1], bias_v, args.alpha, args.beta));
+            __builtin_nontemporal_store(out, (u32x4 *)c);
+        }
     }
 }
 
@@ -526,11 +543,11 @@ hipError_t launch_tile(const GemmArgs &args, int cus, hipStream_t stream) {
 }
 
 // Split-K launch: the tile kernel over (range, tile) units into the
-// workspace split.P, then the reduction with the epilogue flags baked in.
-// The host has checked the tile-path requirements, split.splits >= 2, every
-// range non-empty, and that split.P holds splits * M * N floats (ldp = M,
-// pstride = M * N).
-template <class Cfg>
+// workspace split.P, then the reduction with the epilogue flags baked in
+// (kQ8: writing int8 Q).  The host has checked the tile-path requirements,
+// split.splits >= 2, every range non-empty, and that split.P holds
+// splits * M * N floats (ldp = M, pstride = M * N).
+template <class Cfg, bool kQ8 = false>
 hipError_t launch_tile_splitk(const GemmArgs &args, const TileSplit &split, int cus, hipStream_t stream) {
     TileSchedule s{};
     s.tiles_m = (int)(args.M / Cfg::BM);
@@ -549,7 +566,8 @@ hipError_t launch_tile_splitk(const GemmArgs &args, const TileSplit &split, int 
     const int64_t cap = (int64_t)cus * 8;
     const dim3 rgrid((unsigned)(blocks < cap ? blocks : cap));
     dispatch_flags(args.flags, [&](auto f) {
-        hipLaunchKernelGGL((splitk_reduce_kernel<decltype(f)::value>), rgrid, dim3(256), 0, stream, args, split);
+        hipLaunchKernelGGL((splitk_reduce_kernel<decltype(f)::value, kQ8>), rgrid, dim3(256), 0, stream, args,
+                           split);
     });
     return hipGetLastError();
 }

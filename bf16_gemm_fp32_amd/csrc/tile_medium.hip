@@ -16,4 +16,9 @@ hipError_t launch_tile_medium_splitk(const GemmArgs &args, const TileSplit &spli
     return launch_tile_splitk<CfgMedium>(args, split, cus, stream);
 }
 
+hipError_t launch_tile_medium_splitk_q8(const GemmArgs &args, const TileSplit &split, int cus,
+                                        hipStream_t stream) {
+    return launch_tile_splitk<CfgMedium, true>(args, split, cus, stream);
+}
+
 }  // namespace gb

@@ -83,6 +83,10 @@ def test_q8_argument_errors():
     assert name(4096, 4096, 4096, P, 4096, P, 4096, 0, 1, P + 8, 4096, 0.0, P, 0) == "generic64x64x32"
     assert name(4096, 4096, 4096, P, 4096, P, 4096, 0, 1, P, 4100, 0.0, P, 0) == "generic64x64x32"
     assert name(100, 100, 64, P, 64, P, 64, 0, 1, P, 112, 0.0, P, 0) == "generic64x64x32"
+    # small grids of 128-tiles with enough K-slices: split-K, the reduction quantizing
+    assert name(1024, 1024, 4096, P, 4096, P, 4096, 0, 1, P, 1024, 0.0, P, 2) == "splitk128x128x64_q8"
+    assert name(1024, 1024, 4096, P, 4096, P, 4096, 0, 1, P, 1028, 0.0, P, 2) == "generic64x64x32"
+    assert name(1024, 1024, 512, P, 512, P, 512, 0, 1, P, 1024, 0.0, P, 2) == "generic64x64x32"  # 8 slices
 
 
 def test_fp8_argument_errors_and_names():

@@ -487,6 +487,18 @@ def check_q8(tag, M, N, K, ldq=None, ldc=None, alpha=1.0, beta=0.0, use_bias=Fal
 
 
 RQ8 = "ring256x256x64_q8"
+SQ8 = "splitk128x128x64_q8"
+
+
+# Small grids: split-K on 128x128 tiles, the reduction quantizing per row.
+@pytest.mark.parametrize("M,N,K,ldq,beta,use_bias,epi,zp", [
+    (1024, 512, 2048, 1024, 0.0, True, "relu", -20),   # 32 tiles, 4 ranges
+    (256, 256, 4096, 264, 0.5, True, "gelu_tanh", 3),  # 4 tiles, 8 ranges, padded ldq, C0 read
+    (512, 384, 1600, 520, -0.75, False, "none", 0),    # uneven ranges
+])
+def test_q8_splitk(M, N, K, ldq, beta, use_bias, epi, zp):
+    check_q8(f"q8 splitk {M}x{N}x{K}", M, N, K, ldq=ldq, alpha=1.25, beta=beta, use_bias=use_bias, epilogue=epi,
+             zp=zp, seed=M + N + K, expect_kernel=SQ8)
 
 
 def test_q8_ring_is_the_default_for_large_shapes():
