@@ -43,6 +43,7 @@ hipError_t launch_tile_ring(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_ring_masked(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_ring_q8(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_fp8(const GemmArgs &args, int cus, hipStream_t stream);
+hipError_t launch_tile_fp8_masked(const GemmArgs &args, int cus, hipStream_t stream);
 // matrix-vector products: 1 <= M <= 4
 hipError_t launch_gemv(const GemmArgs &args, hipStream_t stream);
 // rows: 32 or 64 (the kernel's row block, M <= rows); cols: strip width

@@ -20,7 +20,7 @@
 namespace gb {
 
 enum KernelKind {
-    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8, kSplitK, kGemv, kSplitKQ8, kNumKinds
+    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8, kSplitK, kGemv, kSplitKQ8, kFp8Masked, kNumKinds
 };
 
 static const char *const kKindNames[kNumKinds] = {"none",            "tile256x256x32_s5", "tile128x128x64_s4",
@@ -28,7 +28,7 @@ static const char *const kKindNames[kNumKinds] = {"none",            "tile256x25
                                                   "ring256x256x64_mfma32", "ring256x256x64",
                                                   "ring256x256x64_masked", "ring256x256x64_q8",
                                                   "fp8_256x256x128",  "splitk128x128x64", "gemv",
-                                                  "splitk128x128x64_q8"};
+                                                  "splitk128x128x64_q8", "fp8_256x256x128_masked"};
 
 static const char *kind_name(int k) { return (k >= 0 && k < kNumKinds) ? kKindNames[k] : "none"; }
 
@@ -370,19 +370,25 @@ static hipError_t launch_generic(const GemmArgs &args, int cus, hipStream_t stre
     return hipGetLastError();
 }
 
-// The fp8 product: the 256x256 FP8 tile kernel for exact tile multiples
-// (M, N % 256, K % 128) with 16-byte aligned rows, else the bounds-checked
-// kernel (which converts the bytes to bf16 on their way into LDS).
+// The fp8 product: the 256x256 FP8 tile kernel with 16-byte aligned rows
+// (lda, ldb % 16, K % 16, ldc % 8) -- its unmasked instance for exact tile
+// multiples (M, N % 256, K % 128), the masked one for shapes with tails --
+// else the bounds-checked kernel (which converts the bytes to bf16 on their
+// way into LDS).
 static int choose_kernel_fp8(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
                              int64_t ldb, const void *C, int64_t ldc) {
     if (M == 0 || N == 0) return kNone;
     const char *force = std::getenv("GEMM_BF16_FORCE_KERNEL");
     if (force && !std::strcmp(force, kKindNames[kGeneric])) return kGeneric;
-    bool ok = K > 0 && M % ShapeFp8::BM == 0 && N % ShapeFp8::BN == 0 && K % ShapeFp8::BK == 0;
+    bool ok = K > 0 && K % 16 == 0;
     ok = ok && lda % 16 == 0 && ldb % 16 == 0 && ldc % 8 == 0 && aligned16(A) && aligned16(B) && aligned16(C);
     const int64_t lim = (int64_t)1 << 31;
-    ok = ok && ShapeFp8::BM * lda + K < lim && ShapeFp8::BN * ldb + K < lim && (M / 256) * (N / 256) < lim;
-    return ok ? kFp8 : kGeneric;
+    ok = ok && ShapeFp8::BM * lda + K + ShapeFp8::BK < lim && ShapeFp8::BN * ldb + K + ShapeFp8::BK < lim;
+    ok = ok && ((M + 255) / 256) * ((N + 255) / 256) < lim;
+    if (!ok) return kGeneric;
+    const bool exact = M % ShapeFp8::BM == 0 && N % ShapeFp8::BN == 0 && K % ShapeFp8::BK == 0;
+    if (force && !std::strcmp(force, kKindNames[kFp8Masked])) return kFp8Masked;
+    return exact ? kFp8 : kFp8Masked;
 }
 
 }  // namespace gb
@@ -514,10 +520,11 @@ int gemm_fp8(int64_t M, int64_t N, int64_t K, const gemm_fp8_t *A, int64_t lda, 
 
     const int cus = device_cu_count();
     hipError_t err = hipSuccess;
-    if (choose_kernel_fp8(M, N, K, A, lda, B, ldb, C, ldc) == kFp8)
-        err = launch_tile_fp8(args, cus, stream);
-    else
-        err = launch_generic(args, cus, stream, true);
+    switch (choose_kernel_fp8(M, N, K, A, lda, B, ldb, C, ldc)) {
+    case kFp8: err = launch_tile_fp8(args, cus, stream); break;
+    case kFp8Masked: err = launch_tile_fp8_masked(args, cus, stream); break;
+    default: err = launch_generic(args, cus, stream, true); break;
+    }
     if (err != hipSuccess) {
         t_last_hip_error = (int)err;
         return GEMM_ERR_HIP;

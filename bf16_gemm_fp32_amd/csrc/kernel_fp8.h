@@ -25,6 +25,12 @@
 // Shadows: after MFMA r of a k-step (r < 16) comes fragment read r of the
 // next k-step (A0 lo, B0 lo, A0 hi, B0 hi, A1 lo, ...), after MFMA 2l+1 DMA
 // load l of the unit the k-step loads.
+//
+// Tails (kMasked): rows past M or N and 16-byte chunks past K are loaded
+// from an out-of-range buffer offset, which the DMA turns into zeros (the
+// zero-fill of the DeepGEMM article, sections 4.2-4.3); the epilogue skips
+// columns past N and 8-row chunks past M and writes a chunk that straddles
+// M element by element.  K must be a multiple of 16.
 #pragma once
 
 #include "device_common.h"
@@ -69,6 +75,7 @@ __device__ __forceinline__ f32x16 mfma_fp8_32x32x64(const i32x8 &a, const i32x8 
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+template <bool kMasked>
 struct Fp8Kernel {
     using Cfg = Fp8Config;
 
@@ -78,6 +85,10 @@ struct Fp8Kernel {
         uint32_t lo_off[Cfg::KSTEPS], hi_off[Cfg::KSTEPS];
         uint32_t lda_bytes, ldb_bytes;
         int wave;
+        // masking only: this lane's row within a load's 8 rows, its logical
+        // chunk by parity of the row group, and the tile's valid extents
+        int lrow, lchunk[2];
+        int rowsA, rowsB, kmax;
     };
 
     // DMA load number l (0..7) of this wave for one operand unit: rows
@@ -87,8 +98,13 @@ struct Fp8Kernel {
                                                 __amdgpu_buffer_rsrc_t rsrc) {
         const int q = L.wave * Cfg::kUnitLoads + l;
         const uint32_t ld = kIsA ? L.lda_bytes : L.ldb_bytes;
-        buffer_load_lds16(rsrc, (GB_LDS void *)(smem + slot * Cfg::kUnitBytes + q * 1024),
-                          kIsA ? L.vA[q & 1] : L.vB[q & 1],
+        uint32_t voff = kIsA ? L.vA[q & 1] : L.vB[q & 1];
+        if constexpr (kMasked) {
+            const int row = q * Cfg::kRowsPerLoad + L.lrow;
+            const int k = kt * Cfg::BK + L.lchunk[q & 1] * 16;
+            if (!(row < (kIsA ? L.rowsA : L.rowsB) && k < L.kmax)) voff = kOobOffset;
+        }
+        buffer_load_lds16(rsrc, (GB_LDS void *)(smem + slot * Cfg::kUnitBytes + q * 1024), voff,
                           (uint32_t)(q * Cfg::kRowsPerLoad) * ld + (uint32_t)kt * Cfg::kRowBytes);
     }
 
@@ -179,7 +195,7 @@ struct Fp8Kernel {
 // consecutive rows of one column -- the same rows throughout (its 8-row
 // chunk is lane % 16), so their row scales load once -- and writes
 // epi(alpha * sa[m] * sb[n] * acc + beta*C + bias[n]) as one 16-byte store.
-template <uint32_t kFlags>
+template <uint32_t kFlags, bool kMasked>
 __device__ __forceinline__ void fp8_epilogue(char *smem, const GemmArgs &args, int64_t m0, int64_t n0, int wm,
                                              int wn, int lane, int wave,
                                              const f32x16 (&acc)[Fp8Config::FM][Fp8Config::FN]) {
@@ -193,7 +209,8 @@ __device__ __forceinline__ void fp8_epilogue(char *smem, const GemmArgs &args, i
     float sa[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
     if (args.scale_a) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sa[e] = args.scale_a[mrow + e];
+        for (int e = 0; e < 8; ++e)
+            if (!kMasked || mrow + e < args.M) sa[e] = args.scale_a[mrow + e];
     }
 #pragma unroll
     for (int j = 0; j < Cfg::FN; ++j) {
@@ -214,17 +231,23 @@ __device__ __forceinline__ void fp8_epilogue(char *smem, const GemmArgs &args, i
             const f32x4 hi = *(const GB_LDS f32x4 *)(stage + col * Cfg::kEpiColBytes + q * 32 + 16);
             const int64_t n = n0 + wn * Cfg::WTN + j * 32 + col;
             const int64_t m = m0 + wm * Cfg::WTM + q * 8;
+            if (kMasked && (n >= args.N || m >= args.M)) continue;
+            const bool full = !kMasked || m + 8 <= args.M;
             uint16_t *p = args.C + n * args.ldc + m;
             const float sb = args.scale_b ? args.scale_b[n] : 1.f;
             float bias_v = 0.f;
             if constexpr ((kFlags & kEpiBias) != 0) bias_v = bf16_bits_to_f32(args.bias[n]);
             float cin[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             if constexpr ((kFlags & kEpiBeta) != 0) {
-                const u32x4 raw = *(const u32x4 *)p;
+                if (full) {
+                    const u32x4 raw = *(const u32x4 *)p;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    cin[2 * e] = bf16_bits_to_f32(raw[e] & 0xFFFFu);
-                    cin[2 * e + 1] = bf16_bits_to_f32(raw[e] >> 16);
+                    for (int e = 0; e < 4; ++e) {
+                        cin[2 * e] = bf16_bits_to_f32(raw[e] & 0xFFFFu);
+                        cin[2 * e + 1] = bf16_bits_to_f32(raw[e] >> 16);
+                    }
+                } else {
+                    for (int e = 0; e < 8 && m + e < args.M; ++e) cin[e] = bf16_bits_to_f32(p[e]);
                 }
             }
             const float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -235,26 +258,30 @@ __device__ __forceinline__ void fp8_epilogue(char *smem, const GemmArgs &args, i
                     epilogue_value<kFlags>(x[2 * e] * sa[2 * e] * sb, cin[2 * e], bias_v, args.alpha, args.beta),
                     epilogue_value<kFlags>(x[2 * e + 1] * sa[2 * e + 1] * sb, cin[2 * e + 1], bias_v, args.alpha,
                                            args.beta));
-            __builtin_nontemporal_store(out, (u32x4 *)p);
+            if (full) {
+                __builtin_nontemporal_store(out, (u32x4 *)p);
+            } else {
+                for (int e = 0; e < 8 && m + e < args.M; ++e) p[e] = (uint16_t)(out[e >> 1] >> ((e & 1) * 16));
+            }
         }
     }
 }
 
 // Requirements checked by the host before launch: M % 256 == 0,
-// N % 256 == 0, K % 128 == 0, K > 0, A/B/C 16-byte aligned, lda/ldb
-// multiples of 16, ldc a multiple of 8, and 256*lda + K, 256*ldb + K (bytes)
-// below 2^31.
-template <uint32_t kFlags>
+// N % 256 == 0, K % 128 == 0 (masked: any M, N >= 1 and K % 16 == 0),
+// K > 0, A/B/C 16-byte aligned, lda/ldb multiples of 16, ldc a multiple of
+// 8, and 256*lda + K + 128, 256*ldb + K + 128 (bytes) below 2^31.
+template <uint32_t kFlags, bool kMasked>
 __global__ void __launch_bounds__(Fp8Config::kThreads)
 gemm_fp8_kernel(const GemmArgs args, const TileSchedule sched) {
     using Cfg = Fp8Config;
-    using RK = Fp8Kernel;
+    using RK = Fp8Kernel<kMasked>;
     __shared__ __attribute__((aligned(1024))) char smem[Cfg::kLdsBytes];
     const uint8_t *A8 = reinterpret_cast<const uint8_t *>(args.A);
     const uint8_t *B8 = reinterpret_cast<const uint8_t *>(args.B);
 
     const int lane = threadIdx.x & 63;
-    RK::Lane Ln;
+    typename RK::Lane Ln;
     Ln.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = Ln.wave / Cfg::WAVES_N;
     const int wn = Ln.wave % Cfg::WAVES_N;
@@ -269,7 +296,10 @@ gemm_fp8_kernel(const GemmArgs args, const TileSchedule sched) {
         const int c = lpos ^ fp8_swizzle(p * Cfg::kRowsPerLoad + lrow);
         Ln.vA[p] = lrow * Ln.lda_bytes + (uint32_t)(c << 4);
         Ln.vB[p] = lrow * Ln.ldb_bytes + (uint32_t)(c << 4);
+        Ln.lchunk[p] = c;
     }
+    Ln.lrow = lrow;
+    Ln.kmax = (int)args.K;
     // Read side: lane l takes row l % 32 of its 32-row block; in k-step ks its
     // fragment's low 16 bytes are logical chunk 4ks + l/32, its high 16 bytes
     // chunk 4ks + 2 + l/32.
@@ -282,7 +312,7 @@ gemm_fp8_kernel(const GemmArgs args, const TileSchedule sched) {
         Ln.hi_off[ks] = (uint32_t)(((4 * ks + 2 + h) ^ swz) << 4);
     }
 
-    const int nk = (int)(args.K / Cfg::BK);
+    const int nk = (int)((args.K + Cfg::BK - 1) / Cfg::BK);
     const int num_tiles = sched.num_tiles();
 
     for (int t = sched.slot(blockIdx.x); t < num_tiles; t += sched.grid) {
@@ -290,6 +320,10 @@ gemm_fp8_kernel(const GemmArgs args, const TileSchedule sched) {
         sched.tile(t, tm, tn);
         const int64_t m0 = (int64_t)tm * Cfg::BM;
         const int64_t n0 = (int64_t)tn * Cfg::BN;
+        if constexpr (kMasked) {
+            Ln.rowsA = (int)(args.M - m0 < Cfg::BM ? args.M - m0 : Cfg::BM);
+            Ln.rowsB = (int)(args.N - n0 < Cfg::BN ? args.N - n0 : Cfg::BN);
+        }
         const __amdgpu_buffer_rsrc_t rA =
             make_rsrc(A8 + m0 * args.lda, (uint32_t)((Cfg::BM - 1) * args.lda + args.K));
         const __amdgpu_buffer_rsrc_t rB =
@@ -305,14 +339,14 @@ gemm_fp8_kernel(const GemmArgs args, const TileSchedule sched) {
         lds_barrier();
         // Prologue: A(0) -> slot 0, B(0) -> 1, A(1) -> 2, B(1) -> 3.
 #pragma unroll
-        for (int l = 0; l < Cfg::kUnitLoads; ++l) RK::load<true>(smem, 0, 0, l, Ln, rA);
+        for (int l = 0; l < Cfg::kUnitLoads; ++l) RK::template load<true>(smem, 0, 0, l, Ln, rA);
 #pragma unroll
-        for (int l = 0; l < Cfg::kUnitLoads; ++l) RK::load<false>(smem, 1, 0, l, Ln, rB);
+        for (int l = 0; l < Cfg::kUnitLoads; ++l) RK::template load<false>(smem, 1, 0, l, Ln, rB);
         if (nk >= 2) {
 #pragma unroll
-            for (int l = 0; l < Cfg::kUnitLoads; ++l) RK::load<true>(smem, 2, 1, l, Ln, rA);
+            for (int l = 0; l < Cfg::kUnitLoads; ++l) RK::template load<true>(smem, 2, 1, l, Ln, rA);
 #pragma unroll
-            for (int l = 0; l < Cfg::kUnitLoads; ++l) RK::load<false>(smem, 3, 1, l, Ln, rB);
+            for (int l = 0; l < Cfg::kUnitLoads; ++l) RK::template load<false>(smem, 3, 1, l, Ln, rB);
             wait_vmcnt<2 * Cfg::kUnitLoads>();
         } else {
             wait_vmcnt<0>();
@@ -339,27 +373,28 @@ gemm_fp8_kernel(const GemmArgs args, const TileSchedule sched) {
 
         int j = 0, sa = 0;
         for (; j + 2 < nk; ++j) {
-            RK::slice<0>(smem, j, sa, Ln, rA, rB, fa, fb, acc);
+            RK::template slice<0>(smem, j, sa, Ln, rA, rB, fa, fb, acc);
             sa = fp8_slot(sa + 2);
         }
         if (j + 1 < nk) {
-            RK::slice<1>(smem, j, sa, Ln, rA, rB, fa, fb, acc);
+            RK::template slice<1>(smem, j, sa, Ln, rA, rB, fa, fb, acc);
             ++j;
             sa = fp8_slot(sa + 2);
         }
-        RK::slice<2>(smem, j, sa, Ln, rA, rB, fa, fb, acc);
+        RK::template slice<2>(smem, j, sa, Ln, rA, rB, fa, fb, acc);
 
         // Every wave is done reading the ring (all loads landed at the last
         // wait): its memory now stages the epilogue.
         lds_barrier();
-        fp8_epilogue<kFlags>(smem, args, m0, n0, wm, wn, lane, Ln.wave, acc);
+        fp8_epilogue<kFlags, kMasked>(smem, args, m0, n0, wm, wn, lane, Ln.wave, acc);
     }
 }
 
-inline hipError_t launch_fp8_ring(const GemmArgs &args, int cus, hipStream_t stream) {
+template <bool kMasked>
+hipError_t launch_fp8_ring(const GemmArgs &args, int cus, hipStream_t stream) {
     TileSchedule s{};
-    s.tiles_m = (int)(args.M / Fp8Config::BM);
-    s.tiles_n = (int)(args.N / Fp8Config::BN);
+    s.tiles_m = (int)((args.M + Fp8Config::BM - 1) / Fp8Config::BM);
+    s.tiles_n = (int)((args.N + Fp8Config::BN - 1) / Fp8Config::BN);
     s.group_m = 4;
     s.order = kOrderGrouped;
     s.hilbert_log2 = 0;
@@ -367,7 +402,7 @@ inline hipError_t launch_fp8_ring(const GemmArgs &args, int cus, hipStream_t str
     s.grid = tiles < cus ? tiles : cus;
     const dim3 grid(s.grid), block(Fp8Config::kThreads);
     dispatch_flags(args.flags, [&](auto f) {
-        hipLaunchKernelGGL((gemm_fp8_kernel<decltype(f)::value>), grid, block, 0, stream, args, s);
+        hipLaunchKernelGGL((gemm_fp8_kernel<decltype(f)::value, kMasked>), grid, block, 0, stream, args, s);
     });
     return hipGetLastError();
 }

@@ -7,7 +7,7 @@ namespace gb {
 static_assert(Fp8Config::BM == ShapeFp8::BM && Fp8Config::BN == ShapeFp8::BN && Fp8Config::BK == ShapeFp8::BK);
 
 hipError_t launch_tile_fp8(const GemmArgs &args, int cus, hipStream_t stream) {
-    return launch_fp8_ring(args, cus, stream);
+    return launch_fp8_ring<false>(args, cus, stream);
 }
 
 }  // namespace gb

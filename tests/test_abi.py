@@ -98,9 +98,12 @@ def test_fp8_argument_errors_and_names():
     assert f(0, 4, 4, 0, 4, P, 4, 0, 1, 1.0, 0.0, 0, 0, 0, 2, 0) == OK
     name = gb.gemm_fp8_kernel_name
     assert name(4096, 4096, 4096, P, 4096, P, 4096, P, 4096) == "fp8_256x256x128"
-    assert name(4096, 4096, 4032, P, 4032, P, 4032, P, 4096) == "generic64x64x32"   # K % 128 != 0
+    # tails: the masked instance (K a multiple of 16)
+    assert name(4096, 4096, 4032, P, 4032, P, 4032, P, 4096) == "fp8_256x256x128_masked"  # K % 128 != 0
+    assert name(4000, 4096, 4096, P, 4096, P, 4096, P, 4000) == "fp8_256x256x128_masked"
+    assert name(4096, 4096, 4040, P, 4048, P, 4048, P, 4096) == "generic64x64x32"   # K % 16 != 0
     assert name(4096, 4096, 4096, P + 8, 4096, P, 4096, P, 4096) == "generic64x64x32"  # unaligned A
-    assert name(4000, 4096, 4096, P, 4096, P, 4096, P, 4000) == "generic64x64x32"
+    assert name(4000, 4096, 4096, P, 4096, P, 4096, P, 4004) == "generic64x64x32"      # ldc % 8 != 0
 
 
 def test_relu_is_accepted():

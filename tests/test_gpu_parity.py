@@ -611,6 +611,38 @@ def test_fp8_ring_padded_leading_dims():
               expect_kernel=FP8R)
 
 
+# The masked FP8 instance: M and N tails of every size class, K tails down
+# to a single 16-byte chunk, padded leading dimensions, epilogue
+# combinations, and exact tile multiples forced through it.
+FP8M = "fp8_256x256x128_masked"
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc", [
+    (300, 260, 144, 144, 144, 304),      # one full slice and a 16-wide K chunk
+    (257, 513, 16, 32, 48, 264),         # a single 16-wide K chunk, 1-row / 1-column tails
+    (1001, 777, 208, 224, 208, 1008),    # M % 8 == 1: the last 8-row chunk straddles M
+    (255, 1, 128, 128, 144, 256),        # N = 1
+    (1, 255, 64, 64, 64, 8),             # M = 1
+    (520, 264, 4048, 4064, 4048, 528),   # 31 full slices and a 80-wide K tail
+])
+def test_fp8_masked_tails(M, N, K, lda, ldb, ldc):
+    check_fp8(f"fp8 masked {M}x{N}x{K}", M, N, K, lda=lda, ldb=ldb, ldc=ldc, seed=M + N + K + 11,
+              expect_kernel=FP8M)
+
+
+@pytest.mark.parametrize("beta,use_bias,epi", [(b, u, e) for b in (0.0, -0.75) for u in (False, True)
+                                               for e in ("none", "gelu_tanh", "relu")])
+def test_fp8_masked_epilogue_combinations(beta, use_bias, epi):
+    check_fp8(f"fp8 masked beta={beta} bias={use_bias} {epi}", 777, 300, 208, ldc=784, alpha=1.25, beta=beta,
+              use_bias=use_bias, epilogue=epi, seed=17 + int(abs(beta) * 4) + 2 * use_bias + len(epi),
+              expect_kernel=FP8M)
+
+
+def test_fp8_masked_forced_on_tile_multiples(monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", FP8M)
+    check_fp8("fp8 masked forced", 512, 512, 384, beta=0.5, use_bias=True, seed=18, expect_kernel=FP8M)
+
+
 def test_fp8_generic_paths(monkeypatch):
     check_fp8("fp8 generic ragged", 300, 200, 77, beta=0.5, use_bias=True, epilogue="gelu_tanh", seed=96,
               expect_kernel="generic64x64x32")
