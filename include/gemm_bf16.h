@@ -159,9 +159,9 @@ int gemm_bf16_q8(int64_t M, int64_t N, int64_t K,
  *   scale_b  NULL (all 1), or a device pointer to N fp32 per-column scales.
  *
  * Errors and quick returns as gemm_bf16.  16-byte aligned A, B and C with
- * lda, ldb multiples of 16, ldc a multiple of 8, M and N multiples of 256
- * and K a multiple of 128 select the FP8 MFMA kernel; other inputs take the
- * bounds-checked path (same result).
+ * lda, ldb multiples of 16 and ldc a multiple of 8 select the FP8 MFMA
+ * kernel (any M and N, K a multiple of 16; tails are masked); other inputs
+ * take the bounds-checked path (same result).
  */
 int gemm_fp8(int64_t M, int64_t N, int64_t K,
              const gemm_fp8_t *A, int64_t lda,
