@@ -162,6 +162,16 @@ def test_kernel_selection_names():
     assert name(4096, 4096, 4100, P, 4100, P, 4100, P, 4096) == "generic64x64x32"
     assert name(4096, 4096, 0, P, 1, P, 1, P, 4096) == "generic64x64x32"
     assert name(0, 4096, 4096, P, 4096, P, 4096, P, 1) == "none"
+    # maximum sizes: the fast kernels address a tile's rows with 32-bit byte
+    # offsets; leading dimensions too large for that take the next kernel
+    # whose offsets still fit, down to the bounds-checked one (64-bit indexing)
+    big = 1 << 22   # 256 rows * 2^22 elements * 2 bytes = 2^31
+    assert name(4096, 4096, 4096, P, big, P, 4096, P, 4096) == "tile128x128x64_s4"
+    assert name(4096, 4096, 4096, P, 2 * big, P, 4096, P, 4096) == "generic64x64x32"
+    assert name(64, 8192, 8192, P, big * 2, P, 8192, P, 64) == "skinny"      # 64 rows: 2^30 bytes
+    assert name(64, 8192, 8192, P, big * 4, P, 8192, P, 64) == "generic64x64x32"
+    assert name(1, 4096, 4096, P, 4096, P, big * 32, P, 1) == "gemv"          # 4 columns: 2^30 bytes
+    assert name(1, 4096, 4096, P, 4096, P, big * 64, P, 1) == "generic64x64x32"
     assert name(-1, 4096, 4096, P, 4096, P, 4096, P, 1) == "none"
 
 
