@@ -44,8 +44,8 @@ hipError_t launch_tile_ring_masked(const GemmArgs &args, int cus, hipStream_t st
 hipError_t launch_tile_ring_q8(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_fp8(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_fp8_masked(const GemmArgs &args, int cus, hipStream_t stream);
-// matrix-vector products: 1 <= M <= 4
-hipError_t launch_gemv(const GemmArgs &args, hipStream_t stream);
+// matrix-vector products: 1 <= M <= 4 (fp8: E4M3 operands)
+hipError_t launch_gemv(const GemmArgs &args, hipStream_t stream, bool fp8 = false);
 // rows: 32 or 64 (the kernel's row block, M <= rows); cols: strip width
 hipError_t launch_skinny(int rows, int cols, const GemmArgs &args, const SkinnyWork &work, int cus,
                          hipStream_t stream);

@@ -20,7 +20,7 @@
 namespace gb {
 
 enum KernelKind {
-    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8, kSplitK, kGemv, kSplitKQ8, kFp8Masked, kNumKinds
+    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8, kSplitK, kGemv, kSplitKQ8, kFp8Masked, kGemvFp8, kNumKinds
 };
 
 static const char *const kKindNames[kNumKinds] = {"none",            "tile256x256x32_s5", "tile128x128x64_s4",
@@ -28,7 +28,8 @@ static const char *const kKindNames[kNumKinds] = {"none",            "tile256x25
                                                   "ring256x256x64_mfma32", "ring256x256x64",
                                                   "ring256x256x64_masked", "ring256x256x64_q8",
                                                   "fp8_256x256x128",  "splitk128x128x64", "gemv",
-                                                  "splitk128x128x64_q8", "fp8_256x256x128_masked"};
+                                                  "splitk128x128x64_q8", "fp8_256x256x128_masked",
+                                                  "gemv_fp8"};
 
 static const char *kind_name(int k) { return (k >= 0 && k < kNumKinds) ? kKindNames[k] : "none"; }
 
@@ -370,7 +371,8 @@ static hipError_t launch_generic(const GemmArgs &args, int cus, hipStream_t stre
     return hipGetLastError();
 }
 
-// The fp8 product: the 256x256 FP8 tile kernel with 16-byte aligned rows
+// The fp8 product: one to four rows on the matrix-vector kernel; else the
+// 256x256 FP8 tile kernel with 16-byte aligned rows
 // (lda, ldb % 16, K % 16, ldc % 8) -- its unmasked instance for exact tile
 // multiples (M, N % 256, K % 128), the masked one for shapes with tails --
 // else the bounds-checked kernel (which converts the bytes to bf16 on their
@@ -380,9 +382,13 @@ static int choose_kernel_fp8(int64_t M, int64_t N, int64_t K, const void *A, int
     if (M == 0 || N == 0) return kNone;
     const char *force = std::getenv("GEMM_BF16_FORCE_KERNEL");
     if (force && !std::strcmp(force, kKindNames[kGeneric])) return kGeneric;
+    // One to four rows: the matrix-vector kernel (16-byte chunks of 16 values).
+    const int64_t lim = (int64_t)1 << 31;
+    if (M <= 4 && K > 0 && K % 16 == 0 && lda % 16 == 0 && ldb % 16 == 0 && aligned16(A) && aligned16(B) &&
+        4 * lda + K < lim && 4 * ldb + K < lim)
+        return kGemvFp8;
     bool ok = K > 0 && K % 16 == 0;
     ok = ok && lda % 16 == 0 && ldb % 16 == 0 && ldc % 8 == 0 && aligned16(A) && aligned16(B) && aligned16(C);
-    const int64_t lim = (int64_t)1 << 31;
     ok = ok && ShapeFp8::BM * lda + K + ShapeFp8::BK < lim && ShapeFp8::BN * ldb + K + ShapeFp8::BK < lim;
     ok = ok && ((M + 255) / 256) * ((N + 255) / 256) < lim;
     if (!ok) return kGeneric;
@@ -523,6 +529,7 @@ int gemm_fp8(int64_t M, int64_t N, int64_t K, const gemm_fp8_t *A, int64_t lda, 
     switch (choose_kernel_fp8(M, N, K, A, lda, B, ldb, C, ldc)) {
     case kFp8: err = launch_tile_fp8(args, cus, stream); break;
     case kFp8Masked: err = launch_tile_fp8_masked(args, cus, stream); break;
+    case kGemvFp8: err = launch_gemv(args, stream, true); break;
     default: err = launch_generic(args, cus, stream, true); break;
     }
     if (err != hipSuccess) {

@@ -158,10 +158,11 @@ int gemm_bf16_q8(int64_t M, int64_t N, int64_t K,
  *   scale_a  NULL (all 1), or a device pointer to M fp32 per-row scales.
  *   scale_b  NULL (all 1), or a device pointer to N fp32 per-column scales.
  *
- * Errors and quick returns as gemm_bf16.  16-byte aligned A, B and C with
- * lda, ldb multiples of 16 and ldc a multiple of 8 select the FP8 MFMA
- * kernel (any M and N, K a multiple of 16; tails are masked); other inputs
- * take the bounds-checked path (same result).
+ * Errors and quick returns as gemm_bf16.  With K, lda and ldb multiples of
+ * 16 and A, B 16-byte aligned: 1 <= M <= 4 takes a matrix-vector kernel
+ * (any ldc); larger M the FP8 MFMA kernel when C is 16-byte aligned and ldc
+ * a multiple of 8 (any M and N; tails are masked).  Other inputs take the
+ * bounds-checked path (same result).
  */
 int gemm_fp8(int64_t M, int64_t N, int64_t K,
              const gemm_fp8_t *A, int64_t lda,

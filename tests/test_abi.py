@@ -104,6 +104,11 @@ def test_fp8_argument_errors_and_names():
     assert name(4096, 4096, 4040, P, 4048, P, 4048, P, 4096) == "generic64x64x32"   # K % 16 != 0
     assert name(4096, 4096, 4096, P + 8, 4096, P, 4096, P, 4096) == "generic64x64x32"  # unaligned A
     assert name(4000, 4096, 4096, P, 4096, P, 4096, P, 4004) == "generic64x64x32"      # ldc % 8 != 0
+    # one to four rows: the matrix-vector kernel (any ldc)
+    assert name(1, 4096, 4096, P, 4096, P, 4096, P, 1) == "gemv_fp8"
+    assert name(4, 4096, 4096, P, 4096, P, 4096, P + 2, 5) == "gemv_fp8"
+    assert name(5, 4096, 4096, P, 4096, P, 4096, P, 8) == "fp8_256x256x128_masked"
+    assert name(1, 4096, 4040, P, 4048, P, 4048, P, 1) == "generic64x64x32"          # K % 16 != 0
 
 
 def test_relu_is_accepted():

@@ -622,7 +622,7 @@ FP8M = "fp8_256x256x128_masked"
     (257, 513, 16, 32, 48, 264),         # a single 16-wide K chunk, 1-row / 1-column tails
     (1001, 777, 208, 224, 208, 1008),    # M % 8 == 1: the last 8-row chunk straddles M
     (255, 1, 128, 128, 144, 256),        # N = 1
-    (1, 255, 64, 64, 64, 8),             # M = 1
+    (5, 255, 64, 64, 64, 8),             # M = 5 (1 to 4 rows take the matrix-vector kernel)
     (520, 264, 4048, 4064, 4048, 528),   # 31 full slices and a 80-wide K tail
 ])
 def test_fp8_masked_tails(M, N, K, lda, ldb, ldc):
@@ -636,6 +636,33 @@ def test_fp8_masked_epilogue_combinations(beta, use_bias, epi):
     check_fp8(f"fp8 masked beta={beta} bias={use_bias} {epi}", 777, 300, 208, ldc=784, alpha=1.25, beta=beta,
               use_bias=use_bias, epilogue=epi, seed=17 + int(abs(beta) * 4) + 2 * use_bias + len(epi),
               expect_kernel=FP8M)
+
+
+# FP8 on the matrix-vector kernel (1 to 4 rows): 16 values per 16-byte
+# chunk, K blocks of 4096 with tails, N tails, scales on and off.
+GVF = "gemv_fp8"
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc", [
+    (1, 4096, 4096, 4096, 4096, 1),      # decode: one full K block
+    (2, 1000, 1040, 1040, 1056, 2),      # K tail inside the block
+    (3, 333, 16, 16, 16, 3),             # a single 16-wide K chunk
+    (4, 129, 4112, 4112, 4128, 4),       # a full block and a 16-wide second block
+    (1, 5, 12304, 12304, 12304, 1),      # three blocks and a tail
+    (4, 4097, 8208, 8208, 8224, 8),      # a 1-column last wave
+])
+def test_fp8_gemv_shapes(M, N, K, lda, ldb, ldc):
+    check_fp8(f"fp8 gemv {M}x{N}x{K}", M, N, K, lda=lda, ldb=ldb, ldc=ldc, seed=M + N + K + 23,
+              expect_kernel=GVF)
+
+
+@pytest.mark.parametrize("beta,use_bias,epi,scales", [(b, u, e, sc) for b in (0.0, -0.75) for u in (False, True)
+                                                      for e in ("none", "gelu_tanh", "relu") for sc in (True, False)
+                                                      if not (u and not sc and e == "relu")])
+def test_fp8_gemv_epilogue_combinations(beta, use_bias, epi, scales):
+    check_fp8(f"fp8 gemv beta={beta} bias={use_bias} {epi} scales={scales}", 3, 515, 1008, ldc=3, alpha=1.25,
+              beta=beta, use_bias=use_bias, epilogue=epi, scales=scales,
+              seed=29 + int(abs(beta) * 4) + 2 * use_bias + len(epi) + 7 * scales, expect_kernel=GVF)
 
 
 def test_fp8_masked_forced_on_tile_multiples(monkeypatch):
