@@ -22,8 +22,9 @@ struct ShapeRing { static constexpr int BM = 256, BN = 256, BK = 64; };
 
 // Short-and-wide products (at most 64 rows): one workgroup per strip of 32,
 // 64 or 128 columns and range of K (split-K) streams B once; K-slices of 256
-// for 32-column strips, 128 for the wider ones.
-struct ShapeSkinny { static constexpr int KS_N32 = 256, KS_WIDE = 128; };
+// for 32-column strips, 128 for the wider ones, 512 FP8 values (the same
+// 512 bytes) for FP8 operands.
+struct ShapeSkinny { static constexpr int KS_N32 = 256, KS_WIDE = 128, KS_FP8 = 512; };
 
 struct SkinnyWork;
 
@@ -49,5 +50,7 @@ hipError_t launch_gemv(const GemmArgs &args, hipStream_t stream, bool fp8 = fals
 // rows: 32 or 64 (the kernel's row block, M <= rows); cols: strip width
 hipError_t launch_skinny(int rows, int cols, const GemmArgs &args, const SkinnyWork &work, int cus,
                          hipStream_t stream);
+// FP8 (E4M3) operands, 32-column strips with slices of KS_FP8 values
+hipError_t launch_skinny_fp8(int rows, const GemmArgs &args, const SkinnyWork &work, int cus, hipStream_t stream);
 
 }  // namespace gb

@@ -196,4 +196,15 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8 &a, const bf16x8 &b
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// E4M3 x E4M3 block, fp32 accumulate: format selectors 0 / 0 (FP8 E4M3 for
+// both operands) and unit block scales (E8M0 exponent 127 = 2^0).  Each lane
+// supplies 32 bytes (32 values) of its row of A and of its column of B;
+// which 32 of the block's 64 k a lane holds is free as long as A and B agree.
+__device__ __forceinline__ f32x16 mfma_fp8_32x32x64(const i32x8 &a, const i32x8 &b, const f32x16 &c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
 }  // namespace gb

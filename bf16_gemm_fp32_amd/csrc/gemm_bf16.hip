@@ -20,7 +20,7 @@
 namespace gb {
 
 enum KernelKind {
-    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8, kSplitK, kGemv, kSplitKQ8, kFp8Masked, kGemvFp8, kNumKinds
+    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8, kSplitK, kGemv, kSplitKQ8, kFp8Masked, kGemvFp8, kSkinnyFp8, kNumKinds
 };
 
 static const char *const kKindNames[kNumKinds] = {"none",            "tile256x256x32_s5", "tile128x128x64_s4",
@@ -29,7 +29,7 @@ static const char *const kKindNames[kNumKinds] = {"none",            "tile256x25
                                                   "ring256x256x64_masked", "ring256x256x64_q8",
                                                   "fp8_256x256x128",  "splitk128x128x64", "gemv",
                                                   "splitk128x128x64_q8", "fp8_256x256x128_masked",
-                                                  "gemv_fp8"};
+                                                  "gemv_fp8",          "skinny_fp8"};
 
 static const char *kind_name(int k) { return (k >= 0 && k < kNumKinds) ? kKindNames[k] : "none"; }
 
@@ -160,7 +160,7 @@ struct SkinnyPlan {
     int rows, cols, strips, splits, spp;
 };
 
-static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int cus) {
+static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int cus, bool fp8 = false) {
     SkinnyPlan p{};
     p.rows = M <= 32 ? 32 : 64;
     int width = 32;
@@ -168,8 +168,9 @@ static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int cus) {
         const int w = std::atoi(env);
         if (w == 32 || w == 64 || w == 128) width = w;
     }
+    if (fp8) width = 32;  // the FP8 instances are built for 32-column strips
     p.cols = width;
-    const int ks = width == 32 ? ShapeSkinny::KS_N32 : ShapeSkinny::KS_WIDE;
+    const int ks = fp8 ? ShapeSkinny::KS_FP8 : (width == 32 ? ShapeSkinny::KS_N32 : ShapeSkinny::KS_WIDE);
     const int64_t nk = (K + ks - 1) / ks;
     p.strips = (int)((N + width - 1) / width);
     int64_t splits = p.strips * 2 >= cus ? 1 : cus / p.strips;
@@ -230,8 +231,8 @@ static hipError_t get_workspace(hipStream_t stream, size_t counters, size_t part
     return hipSuccess;
 }
 
-static hipError_t launch_skinny_plan(const GemmArgs &args, int cus, hipStream_t stream) {
-    const SkinnyPlan p = plan_skinny(args.M, args.N, args.K, cus);
+static hipError_t launch_skinny_plan(const GemmArgs &args, int cus, hipStream_t stream, bool fp8 = false) {
+    const SkinnyPlan p = plan_skinny(args.M, args.N, args.K, cus, fp8);
     SkinnyWork work{};
     work.num_strips = p.strips;
     work.splits = p.splits;
@@ -242,9 +243,11 @@ static hipError_t launch_skinny_plan(const GemmArgs &args, int cus, hipStream_t 
         std::lock_guard<std::mutex> lock(g_ws_mutex);
         hipError_t err = get_workspace(stream, (size_t)p.strips, floats, &work.counters, &work.partials);
         if (err != hipSuccess) return err;
-        return launch_skinny(p.rows, p.cols, args, work, cus, stream);
+        return fp8 ? launch_skinny_fp8(p.rows, args, work, cus, stream)
+                   : launch_skinny(p.rows, p.cols, args, work, cus, stream);
     }
-    return launch_skinny(p.rows, p.cols, args, work, cus, stream);
+    return fp8 ? launch_skinny_fp8(p.rows, args, work, cus, stream)
+               : launch_skinny(p.rows, p.cols, args, work, cus, stream);
 }
 
 // Split-K on the 128x128 tiles: used when those tiles alone would leave more
@@ -371,7 +374,8 @@ static hipError_t launch_generic(const GemmArgs &args, int cus, hipStream_t stre
     return hipGetLastError();
 }
 
-// The fp8 product: one to four rows on the matrix-vector kernel; else the
+// The fp8 product: one to four rows on the matrix-vector kernel, up to 64
+// on the streaming kernel; else the
 // 256x256 FP8 tile kernel with 16-byte aligned rows
 // (lda, ldb % 16, K % 16, ldc % 8) -- its unmasked instance for exact tile
 // multiples (M, N % 256, K % 128), the masked one for shapes with tails --
@@ -387,6 +391,11 @@ static int choose_kernel_fp8(int64_t M, int64_t N, int64_t K, const void *A, int
     if (M <= 4 && K > 0 && K % 16 == 0 && lda % 16 == 0 && ldb % 16 == 0 && aligned16(A) && aligned16(B) &&
         4 * lda + K < lim && 4 * ldb + K < lim)
         return kGemvFp8;
+    // Up to 64 rows: the streaming kernel (slices of 512 bytes; C any ldc).
+    if (M <= 64 && K > 0 && K % 16 == 0 && lda % 16 == 0 && ldb % 16 == 0 && aligned16(A) && aligned16(B) &&
+        64 * lda + K + ShapeSkinny::KS_FP8 < lim && 128 * ldb + K + ShapeSkinny::KS_FP8 < lim &&
+        N / 32 + 1 < lim / 64)
+        return kSkinnyFp8;
     bool ok = K > 0 && K % 16 == 0;
     ok = ok && lda % 16 == 0 && ldb % 16 == 0 && ldc % 8 == 0 && aligned16(A) && aligned16(B) && aligned16(C);
     ok = ok && ShapeFp8::BM * lda + K + ShapeFp8::BK < lim && ShapeFp8::BN * ldb + K + ShapeFp8::BK < lim;
@@ -530,6 +539,7 @@ int gemm_fp8(int64_t M, int64_t N, int64_t K, const gemm_fp8_t *A, int64_t lda, 
     case kFp8: err = launch_tile_fp8(args, cus, stream); break;
     case kFp8Masked: err = launch_tile_fp8_masked(args, cus, stream); break;
     case kGemvFp8: err = launch_gemv(args, stream, true); break;
+    case kSkinnyFp8: err = launch_skinny_plan(args, cus, stream, true); break;
     default: err = launch_generic(args, cus, stream, true); break;
     }
     if (err != hipSuccess) {

@@ -38,8 +38,6 @@
 
 namespace gb {
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 struct Fp8Config {
     static constexpr int BM = 256, BN = 256, BK = 128;  // BK in fp8 elements = bytes
@@ -69,11 +67,6 @@ __device__ __forceinline__ int fp8_swizzle(int row) { return (row & 7) ^ ((row >
 
 __device__ __forceinline__ int fp8_slot(int s) { return s >= Fp8Config::kSlots ? s - Fp8Config::kSlots : s; }
 
-// E4M3 x E4M3 block, fp32 accumulate: format selectors 0 / 0 (FP8 E4M3 for
-// both operands) and unit block scales (E8M0 exponent 127 = 2^0).
-__device__ __forceinline__ f32x16 mfma_fp8_32x32x64(const i32x8 &a, const i32x8 &b, const f32x16 &c) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
-}
 
 template <bool kMasked>
 struct Fp8Kernel {

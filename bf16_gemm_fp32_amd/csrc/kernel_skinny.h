@@ -42,6 +42,14 @@
 // LDS rows are KS*2 bytes; chunk c of row r is stored at c ^ (r & 15) (r & 15
 // limited to the row's chunk count), which keeps the 32-row fragment reads
 // on distinct banks in every 8- and 16-lane group.
+//
+// kFp8: A and B hold OCP FP8 E4M3 bytes (the FP8 input path of the DeepGEMM
+// article, sections 1.2 and 6.3).  The byte layout is unchanged -- a slice
+// row is still KS*2 bytes, now 2*KS values, and a 16-byte chunk 16 values --
+// and the k-steps run on 32x32x64 FP8 MFMAs: lane l's 32 bytes of a k-step
+// are chunks 4s + l/32 and 4s + 2 + l/32 (the same for A and B, which is all
+// the MFMA needs).  The epilogue scales the sum by scale_a[m] and
+// scale_b[n].
 #pragma once
 
 #include "device_common.h"
@@ -96,21 +104,25 @@ struct SkinnyWork {
     uint32_t *counters;
 };
 
-// Requirements checked by the host: 1 <= M <= BMr, N >= 1, K >= 8 and
-// K % 8 == 0, A/B 16-byte aligned, lda/ldb multiples of 8 (C: any ldc >= M,
-// element-wise accesses unless work.c_vector), the byte
-// offsets of one unit ((BMr-1)*lda + K + KS, (BN-1)*ldb + K + KS, times 2)
-// below 2^31, and every split owning at least one K-slice.
-template <class Cfg, uint32_t kFlags>
+// Requirements checked by the host: 1 <= M <= BMr, N >= 1, K a multiple of
+// one 16-byte chunk (8 values, 16 with kFp8), A/B 16-byte aligned, lda/ldb
+// multiples of a chunk (C: any ldc >= M, element-wise accesses unless
+// work.c_vector), the byte offsets of one unit ((BMr-1)*lda + K + a slice,
+// (BN-1)*ldb + K + a slice) below 2^31, and every split owning at least one
+// K-slice.
+template <class Cfg, uint32_t kFlags, bool kFp8 = false>
 __global__ void __launch_bounds__(Cfg::kThreads)
 gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
     __shared__ __attribute__((aligned(1024))) char smem[Cfg::kLdsBytes];
     char *const ringA = smem;
     char *const ringB = smem + Cfg::SA * Cfg::kABytes;
+    constexpr int kElem = kFp8 ? 1 : 2;                       // bytes per value
+    constexpr int kSliceVals = Cfg::kRowBytes / kElem;        // values per slice row
+    constexpr int kChunkVals = 16 / kElem;                    // values per 16-byte chunk
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t lda_bytes = (uint32_t)args.lda * 2u, ldb_bytes = (uint32_t)args.ldb * 2u;
+    const uint32_t lda_bytes = (uint32_t)(args.lda * kElem), ldb_bytes = (uint32_t)(args.ldb * kElem);
 
     // Load side: a wave load covers rows kRowsPerLoad*q ..; lane i takes row
     // kRowsPerLoad*q + i/kChunks and LDS chunk position i%kChunks, holding
@@ -138,11 +150,13 @@ gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
         vB[i] = (uint32_t)rB_[i] * ldb_bytes + (uint32_t)cB[i] * 16;
     }
 
-    const int nk = (int)((args.K + Cfg::KS - 1) / Cfg::KS);
+    const int nk = (int)((args.K + kSliceVals - 1) / kSliceVals);
     const int rowsA = (int)(args.M < Cfg::BMr ? args.M : Cfg::BMr);
     const int kmax = (int)args.K;
     const int num_units = work.num_strips * work.splits;
-    const __amdgpu_buffer_rsrc_t rA = make_rsrc(args.A, (uint32_t)(((rowsA - 1) * args.lda + args.K) * 2));
+    const char *A8 = reinterpret_cast<const char *>(args.A);
+    const char *B8 = reinterpret_cast<const char *>(args.B);
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(A8, (uint32_t)(((rowsA - 1) * args.lda + args.K) * kElem));
 
     for (int unit = blockIdx.x; unit < num_units; unit += gridDim.x) {
         const int strip = unit / work.splits;
@@ -152,7 +166,7 @@ gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
         const int s0 = split * work.spp;
         const int ns = (nk - s0 < work.spp ? nk - s0 : work.spp);  // >= 1, checked by the host
         const __amdgpu_buffer_rsrc_t rB =
-            make_rsrc(args.B + n0 * args.ldb, (uint32_t)(((colsB - 1) * args.ldb + args.K) * 2));
+            make_rsrc(B8 + n0 * args.ldb * kElem, (uint32_t)(((colsB - 1) * args.ldb + args.K) * kElem));
 
         // Slice j of this unit's order into its ring buffer.  Slices are
         // issued in order (A and B each), walking the unit's K range from a
@@ -169,14 +183,14 @@ gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
             const int ks = ksA;
             ksA = ksA + 1 == s_end ? s0 : ksA + 1;
             const uint32_t soff = (uint32_t)ks * Cfg::kRowBytes;
-            if (allA && (ks + 1) * Cfg::KS <= kmax) {
+            if (allA && (ks + 1) * kSliceVals <= kmax) {
 #pragma unroll
                 for (int i = 0; i < Cfg::kALoads; ++i)
                     buffer_load_lds16(rA, (GB_LDS void *)(dst + (wave * Cfg::kALoads + i) * 1024), vA[i], soff);
             } else {
 #pragma unroll
                 for (int i = 0; i < Cfg::kALoads; ++i) {
-                    const bool ok = rA_[i] < rowsA && ks * Cfg::KS + cA[i] * 8 < kmax;
+                    const bool ok = rA_[i] < rowsA && ks * kSliceVals + cA[i] * kChunkVals < kmax;
                     buffer_load_lds16(rA, (GB_LDS void *)(dst + (wave * Cfg::kALoads + i) * 1024),
                                       ok ? vA[i] : kOobOffset, soff);
                 }
@@ -187,14 +201,14 @@ gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
             const int ks = ksB;
             ksB = ksB + 1 == s_end ? s0 : ksB + 1;
             const uint32_t soff = (uint32_t)ks * Cfg::kRowBytes;
-            if (allB && (ks + 1) * Cfg::KS <= kmax) {
+            if (allB && (ks + 1) * kSliceVals <= kmax) {
 #pragma unroll
                 for (int i = 0; i < Cfg::kBLoads; ++i)
                     buffer_load_lds16(rB, (GB_LDS void *)(dst + (wave * Cfg::kBLoads + i) * 1024), vB[i], soff);
             } else {
 #pragma unroll
                 for (int i = 0; i < Cfg::kBLoads; ++i) {
-                    const bool ok = rB_[i] < colsB && ks * Cfg::KS + cB[i] * 8 < kmax;
+                    const bool ok = rB_[i] < colsB && ks * kSliceVals + cB[i] * kChunkVals < kmax;
                     buffer_load_lds16(rB, (GB_LDS void *)(dst + (wave * Cfg::kBLoads + i) * 1024),
                                       ok ? vB[i] : kOobOffset, soff);
                 }
@@ -235,6 +249,30 @@ gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
 
             const char *sA = ringA + (kt % Cfg::SA) * Cfg::kABytes;
             const char *sB = ringB + (kt % Cfg::SB) * Cfg::kBBytes;
+            if constexpr (kFp8) {
+                // 64-byte k-steps: Cfg::kStepsPerWave / 2 per wave
+#pragma unroll
+                for (int st = 0; st < Cfg::kStepsPerWave / 2; ++st) {
+                    const int s = wave * (Cfg::kStepsPerWave / 2) + st;
+                    const uint32_t clo = (uint32_t)(((4 * s + (lane >> 5)) ^ fragSw) << 4);
+                    const uint32_t chi = (uint32_t)(((4 * s + 2 + (lane >> 5)) ^ fragSw) << 4);
+                    i32x8 b[Cfg::FN];
+#pragma unroll
+                    for (int j = 0; j < Cfg::FN; ++j) {
+                        b[j].lo = *(const GB_LDS i32x4 *)(sB + j * 32 * Cfg::kRowBytes + fragRow + clo);
+                        b[j].hi = *(const GB_LDS i32x4 *)(sB + j * 32 * Cfg::kRowBytes + fragRow + chi);
+                    }
+#pragma unroll
+                    for (int i = 0; i < Cfg::FM; ++i) {
+                        i32x8 a;
+                        a.lo = *(const GB_LDS i32x4 *)(sA + i * 32 * Cfg::kRowBytes + fragRow + clo);
+                        a.hi = *(const GB_LDS i32x4 *)(sA + i * 32 * Cfg::kRowBytes + fragRow + chi);
+#pragma unroll
+                        for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = mfma_fp8_32x32x64(a, b[j], acc[i][j]);
+                    }
+                }
+                continue;
+            }
 #pragma unroll
             for (int st = 0; st < Cfg::kStepsPerWave; ++st) {
                 const int s = wave * Cfg::kStepsPerWave + st;
@@ -298,6 +336,17 @@ gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
             if (n >= args.N || m >= args.M) return;
             uint16_t *cp = args.C + n * args.ldc + m;
             const bool full = m + 8 <= args.M && work.c_vector;
+            float xs[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xs[e] = x[e];
+            if constexpr (kFp8) {
+                const float sb = args.scale_b ? args.scale_b[n] : 1.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float sa = (args.scale_a && m + e < args.M) ? args.scale_a[m + e] : 1.f;
+                    xs[e] = x[e] * sa * sb;
+                }
+            }
             float bias_v = 0.f;
             if constexpr ((kFlags & kEpiBias) != 0) bias_v = bf16_bits_to_f32(args.bias[n]);
             float cin[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -316,8 +365,8 @@ gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
             u32x4 out;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                out[e] = pack_bf16x2(epilogue_value<kFlags>(x[2 * e], cin[2 * e], bias_v, args.alpha, args.beta),
-                                     epilogue_value<kFlags>(x[2 * e + 1], cin[2 * e + 1], bias_v, args.alpha,
+                out[e] = pack_bf16x2(epilogue_value<kFlags>(xs[2 * e], cin[2 * e], bias_v, args.alpha, args.beta),
+                                     epilogue_value<kFlags>(xs[2 * e + 1], cin[2 * e + 1], bias_v, args.alpha,
                                                             args.beta));
             if (full) {
                 __builtin_nontemporal_store(out, (u32x4 *)cp);
@@ -386,12 +435,13 @@ gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
 }
 
 // One workgroup per compute unit (at most one per work unit).
-template <class Cfg>
+template <class Cfg, bool kFp8 = false>
 hipError_t launch_skinny(const GemmArgs &args, const SkinnyWork &work, int cus, hipStream_t stream) {
     const int units = work.num_strips * work.splits;
     const dim3 grid(units < cus ? units : cus), block(Cfg::kThreads);
     dispatch_flags(args.flags, [&](auto f) {
-        hipLaunchKernelGGL((gemm_skinny_kernel<Cfg, decltype(f)::value>), grid, block, 0, stream, args, work);
+        hipLaunchKernelGGL((gemm_skinny_kernel<Cfg, decltype(f)::value, kFp8>), grid, block, 0, stream, args,
+                           work);
     });
     return hipGetLastError();
 }

@@ -160,9 +160,10 @@ int gemm_bf16_q8(int64_t M, int64_t N, int64_t K,
  *
  * Errors and quick returns as gemm_bf16.  With K, lda and ldb multiples of
  * 16 and A, B 16-byte aligned: 1 <= M <= 4 takes a matrix-vector kernel
- * (any ldc); larger M the FP8 MFMA kernel when C is 16-byte aligned and ldc
- * a multiple of 8 (any M and N; tails are masked).  Other inputs take the
- * bounds-checked path (same result).
+ * and 5 <= M <= 64 a streaming FP8 MFMA kernel (any ldc); larger M the
+ * 256x256 FP8 MFMA kernel when C is 16-byte aligned and ldc a multiple of 8
+ * (any M and N; tails are masked).  Other inputs take the bounds-checked
+ * path (same result).
  */
 int gemm_fp8(int64_t M, int64_t N, int64_t K,
              const gemm_fp8_t *A, int64_t lda,

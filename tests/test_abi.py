@@ -107,7 +107,9 @@ def test_fp8_argument_errors_and_names():
     # one to four rows: the matrix-vector kernel (any ldc)
     assert name(1, 4096, 4096, P, 4096, P, 4096, P, 1) == "gemv_fp8"
     assert name(4, 4096, 4096, P, 4096, P, 4096, P + 2, 5) == "gemv_fp8"
-    assert name(5, 4096, 4096, P, 4096, P, 4096, P, 8) == "fp8_256x256x128_masked"
+    assert name(5, 4096, 4096, P, 4096, P, 4096, P, 8) == "skinny_fp8"
+    assert name(64, 8192, 8192, P, 8192, P, 8192, P, 64) == "skinny_fp8"
+    assert name(65, 4096, 4096, P, 4096, P, 4096, P, 72) == "fp8_256x256x128_masked"
     assert name(1, 4096, 4040, P, 4048, P, 4048, P, 1) == "generic64x64x32"          # K % 16 != 0
 
 

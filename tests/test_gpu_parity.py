@@ -622,7 +622,7 @@ FP8M = "fp8_256x256x128_masked"
     (257, 513, 16, 32, 48, 264),         # a single 16-wide K chunk, 1-row / 1-column tails
     (1001, 777, 208, 224, 208, 1008),    # M % 8 == 1: the last 8-row chunk straddles M
     (255, 1, 128, 128, 144, 256),        # N = 1
-    (5, 255, 64, 64, 64, 8),             # M = 5 (1 to 4 rows take the matrix-vector kernel)
+    (65, 255, 64, 64, 64, 72),           # M = 65 (up to 64 rows take the streaming kernels)
     (520, 264, 4048, 4064, 4048, 528),   # 31 full slices and a 80-wide K tail
 ])
 def test_fp8_masked_tails(M, N, K, lda, ldb, ldc):
@@ -663,6 +663,36 @@ def test_fp8_gemv_epilogue_combinations(beta, use_bias, epi, scales):
     check_fp8(f"fp8 gemv beta={beta} bias={use_bias} {epi} scales={scales}", 3, 515, 1008, ldc=3, alpha=1.25,
               beta=beta, use_bias=use_bias, epilogue=epi, scales=scales,
               seed=29 + int(abs(beta) * 4) + 2 * use_bias + len(epi) + 7 * scales, expect_kernel=GVF)
+
+
+# FP8 on the streaming kernel (5 to 64 rows): 512-value slices with K
+# tails, row / column tails, split-K, epilogue combinations with scales.
+SKF = "skinny_fp8"
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc", [
+    (64, 1024, 4096, 4096, 4096, 64),    # 8 slices
+    (33, 96, 528, 544, 528, 40),         # just over one 32-row block, a 16-wide K tail
+    (7, 1000, 1040, 1040, 1056, 8),      # 7 rows, N and K tails
+    (48, 4096, 1024, 1024, 1024, 48),
+    (63, 129, 4112, 4112, 4128, 64),     # every tail at once
+    (64, 1, 512, 512, 512, 64),          # one column, one slice
+    (5, 300, 16, 16, 16, 5),             # a single 16-wide K chunk, ldc not a multiple of 8
+])
+@pytest.mark.parametrize("splits", ["1", "3"])
+def test_fp8_skinny_shapes(M, N, K, lda, ldb, ldc, splits, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_SKINNY_SPLITS", splits)
+    check_fp8(f"fp8 skinny {M}x{N}x{K} splits={splits}", M, N, K, lda=lda, ldb=ldb, ldc=ldc,
+              seed=M + N + K + 31, expect_kernel=SKF)
+
+
+@pytest.mark.parametrize("beta,use_bias,epi,scales", [(b, u, e, sc) for b in (0.0, -0.75) for u in (False, True)
+                                                      for e in ("none", "gelu_tanh", "relu") for sc in (True, False)
+                                                      if not (u and not sc and e == "relu")])
+def test_fp8_skinny_epilogue_combinations(beta, use_bias, epi, scales):
+    check_fp8(f"fp8 skinny beta={beta} bias={use_bias} {epi} scales={scales}", 40, 515, 2048, ldc=41, alpha=1.25,
+              beta=beta, use_bias=use_bias, epilogue=epi, scales=scales,
+              seed=37 + int(abs(beta) * 4) + 2 * use_bias + len(epi) + 7 * scales, expect_kernel=SKF)
 
 
 def test_fp8_masked_forced_on_tile_multiples(monkeypatch):
