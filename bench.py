@@ -236,7 +236,7 @@ def run_workload(w, steps, warmup, cold, with_cpu):
     roof["algorithmic_bytes"] = w.algorithmic_bytes
     roof["traffic_over_algorithmic"] = traffic / w.algorithmic_bytes if traffic else None
     out = {
-        "metric": METRIC if w.name == "square_4096" else f"bf16 GEMM TFLOP/s on {w.name}",
+        "metric": METRIC if w.name == "square_4096" else f"{'fp8' if fp8 else 'bf16'} GEMM TFLOP/s on {w.name}",
         "value": tflops,
         "unit": "TFLOP/s",
         "n_gpus": 1,

@@ -106,6 +106,9 @@ WORKLOADS = {
         # headline shape: E4M3 operands, per-row / per-column scales
         Workload("fp8_4096", 9, 4096, 4096, 4096, inp="fp8",
                  notes="C = sa[m] sb[n] (A*B), A and B in OCP FP8 E4M3"),
+        # the memory-bound case with FP8 operands: B (64 MiB) streamed once
+        Workload("fp8_skinny_64x8192x8192", 10, 64, 8192, 8192, inp="fp8", bound="hbm",
+                 notes="C = sa[m] sb[n] (A*B), E4M3 operands, 64 rows"),
     ]
 }
 
