@@ -315,8 +315,12 @@ static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t
         if (!std::strcmp(force, kKindNames[kSkinny]) && okS) return kSkinny;
         if (!std::strcmp(force, kKindNames[kGemv]) && okV) return kGemv;
     }
-    // One to four rows: the matrix-vector kernel.
-    if (okV) return kGemv;
+    // One to four rows: the matrix-vector kernel.  Each of its waves reads
+    // every row of A for two columns of B, so at three and four rows on a
+    // large B (N * K >= 2^26) the streaming kernel, which shares A across a
+    // 32-column strip, is faster (8192 x 8192: 25.0 us against 27.8 us at
+    // three rows and 29.2 us at four).
+    if (okV && (M <= 2 || N * K < ((int64_t)1 << 26) || !okS)) return kGemv;
     // At most 64 rows: the streaming kernel (a 256- or 128-row tile would be
     // mostly empty).
     if (okS) return kSkinny;

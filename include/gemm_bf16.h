@@ -20,7 +20,7 @@
  * Every function is thread-safe.  The library keeps no pointer to caller
  * buffers after a call returns.  Its one device allocation is the split-K
  * workspace (fp32 partial sums, and counters for the short-product kernel)
- * used by two kinds of shape: 5 <= M <= 64 with few columns, and products
+ * used by two kinds of shape: 3 <= M <= 64 with few columns, and products
  * whose 128x128 tiles would leave most compute units idle (for example
  * 1024 x 1024 x 4096).  It is one buffer per (device, stream), allocated
  * with hipMalloc and its counters zeroed with hipMemsetAsync on the first

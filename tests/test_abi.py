@@ -161,6 +161,10 @@ def test_kernel_selection_names():
     assert name(48, 4096, 1024, P, 1024, P, 1024, P, 48) == "skinny"
     assert name(1, 4096, 4096, P, 4096, P, 4096, P, 8) == "gemv"
     assert name(4, 4096, 4096, P, 4096, P, 4096, P, 4) == "gemv"
+    assert name(2, 8192, 8192, P, 8192, P, 8192, P, 2) == "gemv"
+    assert name(3, 8192, 8192, P, 8192, P, 8192, P, 3) == "skinny"   # large B: A shared per strip
+    assert name(4, 16384, 4096, P, 4096, P, 4096, P, 4) == "skinny"
+    assert name(4, 4096, 16376, P, 16376, P, 16376, P, 4) == "gemv"    # N * K just below 2^26
     assert name(5, 4096, 4096, P, 4096, P, 4096, P, 8) == "skinny"
     assert name(1, 4096, 4100, P, 4100, P, 4100, P, 1) == "generic64x64x32"   # K % 8 != 0
     assert name(48, 4096, 1020, P, 1020, P, 1020, P, 48) == "generic64x64x32"

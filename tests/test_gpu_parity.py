@@ -339,6 +339,12 @@ def test_gemv_epilogue_combinations(beta, use_bias, epi):
                expect_kernel=GV)
 
 
+@pytest.mark.parametrize("M,N,K,ldc", [(3, 8192, 8192, 3), (4, 16384, 4096, 8)])
+def test_three_and_four_rows_on_large_b_take_the_streaming_kernel(M, N, K, ldc):
+    check_full(f"rows {M} large B", M, N, K, ldc=ldc, beta=0.5, use_bias=True, epilogue="gelu_tanh",
+               seed=M * 7 + 3, expect_kernel="skinny")
+
+
 def test_gemv_unaligned_c_with_beta():
     check_full("gemv unaligned C", 2, 777, 520, ldc=3, beta=0.5, use_bias=True, epilogue="gelu_tanh",
                offsets=(0, 0, 1), seed=93, expect_kernel=GV)
