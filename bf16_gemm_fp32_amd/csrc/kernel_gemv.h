@@ -86,7 +86,11 @@ __global__ void __launch_bounds__(GemvConfig::kThreads) gemm_gemv_kernel(const G
     constexpr int kElem = kFp8 ? 1 : 2;        // bytes per value
     constexpr int kPerChunk = 16 / kElem;      // values per 16-byte chunk
     const int lane = threadIdx.x & 63;
-    const int64_t wave = (int64_t)blockIdx.x * Cfg::kWaves + (threadIdx.x >> 6);
+    // The wave index through readfirstlane: the compiler then knows n0, and
+    // the B buffer descriptor built from it, to be wave-uniform and keeps
+    // them in scalar registers (a descriptor it must assume divergent costs
+    // a readfirstlane loop around every load).
+    const int64_t wave = (int64_t)blockIdx.x * Cfg::kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t n0 = wave * Cfg::kCols;
     if (n0 >= args.N) return;  // whole wave past the last column (wave-uniform)
     const int cols = (int)(args.N - n0 < Cfg::kCols ? args.N - n0 : Cfg::kCols);
