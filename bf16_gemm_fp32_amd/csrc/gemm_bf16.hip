@@ -279,6 +279,20 @@ static TileSplit plan_splitk(int64_t M, int64_t N, int64_t K, int cus) {
     return p;
 }
 
+// Whether splitting K beats the unsplit 128x128 kernel on a small grid.
+// Measured: the unsplit kernel takes about 4.3 us plus 0.31 us per 64-wide
+// K-slice whatever the tile count (up to 64 tiles), while the split pays a
+// reduction kernel and runs more, busier compute units; it wins from about
+// 26 slices at 16 tiles, 33 at 32 tiles and 46 at 64 tiles (1024 x 1024 x
+// 1024: 15.2 us split against 9.4 us unsplit; 1024 x 1024 x 4096: 23.4 us
+// against 25.0 us).  The quantizing output has no unsplit small-grid kernel
+// and splits whenever the plan allows.
+static bool splitk_pays(int64_t M, int64_t N, int64_t K) {
+    const int64_t tiles = (M / ShapeM::BM) * (N / ShapeM::BN);
+    const int64_t nk = K / ShapeM::BK;
+    return 5 * nk >= 100 + 2 * tiles;
+}
+
 // kQ8: the quantizing output (the host chose this path only when the plan
 // splits).
 static hipError_t launch_splitk_plan(const GemmArgs &args, int cus, hipStream_t stream, bool q8 = false) {
@@ -335,7 +349,7 @@ static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t
         const int64_t tiles = (M / ShapeL::BM) * (N / ShapeL::BN);
         if (tiles * 2 >= cus || !okM) return kLarge;
     }
-    if (okM) return plan_splitk(M, N, K, cus).splits >= 2 ? kSplitK : kMedium;
+    if (okM) return plan_splitk(M, N, K, cus).splits >= 2 && splitk_pays(M, N, K) ? kSplitK : kMedium;
     return kGeneric;
 }
 

@@ -153,6 +153,9 @@ def test_kernel_selection_names():
     # small grids of 128-tiles with enough K-slices: split-K
     assert name(1024, 1024, 4096, P, 4096, P, 4096, P, 1024) == "splitk128x128x64"
     assert name(512, 512, 8192, P, 8192, P, 8192, P, 512) == "splitk128x128x64"
+    assert name(512, 512, 2048, P, 2048, P, 2048, P, 512) == "splitk128x128x64"     # 16 tiles, 32 slices
+    assert name(1024, 1024, 2048, P, 2048, P, 2048, P, 1024) == "tile128x128x64_s4"  # 64 tiles: K too short to split
+    assert name(1024, 1024, 1024, P, 1024, P, 1024, P, 1024) == "tile128x128x64_s4"
     assert name(512, 512, 512, P, 512, P, 512, P, 512) == "tile128x128x64_s4"   # 8 slices: no split
     assert name(2048, 2048, 4096, P, 4096, P, 4096, P, 2048) == "tile128x128x64_s4"  # 256 tiles
     assert name(1000, 1000, 1000, P, 1000, P, 1000, P, 1000) == "generic64x64x32"

@@ -157,8 +157,9 @@ SPLITK = "splitk128x128x64"
 
 
 @pytest.mark.parametrize("M,N,K", [
-    (512, 512, 1024),    # 16 tiles, 16 slices: 2 ranges
+    (1536, 1024, 4096),  # 96 tiles, 64 slices: 2 ranges
     (256, 256, 1600),    # 4 tiles, 25 slices: 3 ranges of 9, 9, 7
+    (512, 512, 2048),    # 16 tiles, 32 slices: 4 ranges
     (256, 384, 2048),    # 6 tiles: 4 ranges
     (512, 256, 4096),    # 8 tiles: 8 ranges
     (128, 128, 8192),    # 1 tile: 16 ranges
@@ -170,7 +171,7 @@ def test_splitk_full(M, N, K):
 @pytest.mark.parametrize("beta,use_bias,epi", [(b, u, e) for b in (0.0, -0.75) for u in (False, True)
                                                for e in ("none", "gelu_tanh", "relu")])
 def test_splitk_epilogue_combinations(beta, use_bias, epi):
-    check_full(f"splitk beta={beta} bias={use_bias} {epi}", 256, 384, 1024, alpha=1.25, beta=beta,
+    check_full(f"splitk beta={beta} bias={use_bias} {epi}", 256, 384, 2048, alpha=1.25, beta=beta,
                use_bias=use_bias, epilogue=epi, seed=40 + int(abs(beta) * 4) + 2 * use_bias + len(epi),
                expect_kernel=SPLITK)
 
@@ -185,6 +186,12 @@ def test_splitk_forced_split_counts(splits, monkeypatch):
     monkeypatch.setenv("GEMM_BF16_SPLITK_SPLITS", str(splits))
     check_full(f"splitk forced {splits} ranges", 384, 256, 3840, beta=0.25, use_bias=True, seed=60 + splits,
                expect_kernel=SPLITK)
+
+
+@pytest.mark.parametrize("M,N,K", [(1024, 1024, 1024), (512, 512, 1024), (256, 384, 1024)])
+def test_short_k_small_grids_stay_unsplit(M, N, K):
+    check_full(f"unsplit {M}x{N}x{K}", M, N, K, beta=0.5, use_bias=True, epilogue="gelu_tanh", seed=M + N + K,
+               expect_kernel="tile128x128x64_s4")
 
 
 def test_splitk_deterministic():
