@@ -119,8 +119,9 @@ def check_full(tag, M, N, K, lda=None, ldb=None, ldc=None, alpha=1.0, beta=0.0, 
     (256, 256, 256, "tile128x128x64_s4"),
     (512, 384, 192, "tile128x128x64_s4"),     # 3 K-slices (odd)
     (512, 384, 256, "tile128x128x64_s4"),     # 4 K-slices (even)
-    (4096, 2048, 320, "ring256x256x64"),      # 128 tiles of 256, 5 slices of 64
-    (4096, 2048, 64, "ring256x256x64"),       # a single K-slice
+    (4608, 2048, 320, "ring256x256x64"),      # 144 tiles of 256, 5 slices of 64
+    (4608, 2048, 64, "ring256x256x64"),       # a single K-slice
+    (4096, 2048, 320, "tile128x128x64_s4"),   # 128 ring tiles, half the CUs: 128x128 tiles, two per CU
     (4096, 2048, 352, "ring256x256x64_masked"),  # K % 64 == 32: a half-empty last slice
     (4096, 2048, 32, "ring256x256x64_masked"),   # a single half-empty K-slice
 ])
@@ -129,7 +130,7 @@ def test_tile_paths_full(M, N, K, kernel):
 
 
 def test_tile_path_epilogue_full():
-    check_full("ring256 epilogue", 4096, 2048, 192, alpha=1.0, beta=0.5, use_bias=True,
+    check_full("ring256 epilogue", 4608, 2048, 192, alpha=1.0, beta=0.5, use_bias=True,
                epilogue="gelu_tanh", seed=11, expect_kernel="ring256x256x64")
     check_full("masked ring epilogue", 4096, 2048, 160, alpha=1.0, beta=0.5, use_bias=True,
                epilogue="gelu_tanh", seed=16, expect_kernel="ring256x256x64_masked")
@@ -142,7 +143,7 @@ def test_tile_path_epilogue_full():
 def test_tile_path_padded_leading_dims():
     check_full("tile128 padded ld", 512, 256, 256, lda=264, ldb=272, ldc=520, beta=0.25, use_bias=True,
                seed=14, expect_kernel="tile128x128x64_s4")
-    check_full("ring256 padded ld", 4096, 2048, 128, lda=136, ldb=192, ldc=4104, seed=15,
+    check_full("ring256 padded ld", 4608, 2048, 128, lda=136, ldb=192, ldc=4616, seed=15,
                expect_kernel="ring256x256x64")
     check_full("masked ring padded ld", 4096, 2048, 96, lda=104, ldb=136, ldc=4112, seed=17,
                expect_kernel="ring256x256x64_masked")
