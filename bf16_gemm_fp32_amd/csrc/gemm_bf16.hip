@@ -20,7 +20,7 @@
 namespace gb {
 
 enum KernelKind {
-    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8, kSplitK, kGemv, kSplitKQ8, kFp8Masked, kGemvFp8, kSkinnyFp8, kNumKinds
+    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8, kSplitK, kGemv, kSplitKQ8, kFp8Masked, kGemvFp8, kSkinnyFp8, kFp8SplitK, kNumKinds
 };
 
 static const char *const kKindNames[kNumKinds] = {"none",            "tile256x256x32_s5", "tile128x128x64_s4",
@@ -29,7 +29,8 @@ static const char *const kKindNames[kNumKinds] = {"none",            "tile256x25
                                                   "ring256x256x64_masked", "ring256x256x64_q8",
                                                   "fp8_256x256x128",  "splitk128x128x64", "gemv",
                                                   "splitk128x128x64_q8", "fp8_256x256x128_masked",
-                                                  "gemv_fp8",          "skinny_fp8"};
+                                                  "gemv_fp8",          "skinny_fp8",
+                                                  "splitk_fp8_256x256x128"};
 
 static const char *kind_name(int k) { return (k >= 0 && k < kNumKinds) ? kKindNames[k] : "none"; }
 
@@ -293,6 +294,43 @@ static bool splitk_pays(int64_t M, int64_t N, int64_t K) {
     return 5 * nk >= 100 + 2 * tiles;
 }
 
+// Split-K for the FP8 tiles on small grids (the fp8 path has no smaller
+// tile): when the 256x256 tiles fill less than half of the compute units,
+// up to CUs / tiles ranges of at least 4 slices of 128, at most 8, and at
+// most 4M floats of partials (16 MiB).  Returns 1 when no split applies.
+static TileSplit plan_splitk_fp8(int64_t M, int64_t N, int64_t K, int cus) {
+    TileSplit p{};
+    p.splits = 1;
+    const int64_t tiles = (M / ShapeFp8::BM) * (N / ShapeFp8::BN);
+    const int64_t nk = K / ShapeFp8::BK;
+    if (tiles <= 0 || tiles * 2 >= cus) return p;
+    int64_t splits = cus / tiles;
+    if (const char *env = std::getenv("GEMM_BF16_FP8_SPLITS")) {  // tuning knob
+        const int v = std::atoi(env);
+        if (v >= 1) splits = v;
+    }
+    if (splits > nk / 4) splits = nk / 4;
+    if (splits > 8) splits = 8;
+    const int64_t cap = ((int64_t)4 << 20) / (M * N);
+    if (splits > cap) splits = cap;
+    if (splits < 2) return p;
+    p.kper = (int)((nk + splits - 1) / splits);
+    p.splits = (int)((nk + p.kper - 1) / p.kper);  // no empty range
+    p.ldp = M;
+    p.pstride = M * N;
+    return p;
+}
+
+static hipError_t launch_fp8_splitk_plan(const GemmArgs &args, int cus, hipStream_t stream) {
+    TileSplit p = plan_splitk_fp8(args.M, args.N, args.K, cus);
+    if (p.splits < 2) return launch_tile_fp8(args, cus, stream);
+    uint32_t *unused = nullptr;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    hipError_t err = get_workspace(stream, 0, (size_t)p.splits * (size_t)args.M * (size_t)args.N, &unused, &p.P);
+    if (err != hipSuccess) return err;
+    return launch_tile_fp8_splitk(args, p, cus, stream);
+}
+
 // kQ8: the quantizing output (the host chose this path only when the plan
 // splits).
 static hipError_t launch_splitk_plan(const GemmArgs &args, int cus, hipStream_t stream, bool q8 = false) {
@@ -427,6 +465,9 @@ static int choose_kernel_fp8(int64_t M, int64_t N, int64_t K, const void *A, int
     if (!ok) return kGeneric;
     const bool exact = M % ShapeFp8::BM == 0 && N % ShapeFp8::BN == 0 && K % ShapeFp8::BK == 0;
     if (force && !std::strcmp(force, kKindNames[kFp8Masked])) return kFp8Masked;
+    if (force && !std::strcmp(force, kKindNames[kFp8])) return exact ? kFp8 : kFp8Masked;
+    // small grids of exact tiles: split K (the reduction needs C aligned, ldc % 8, M % 8: all implied)
+    if (exact && plan_splitk_fp8(M, N, K, device_cu_count()).splits >= 2) return kFp8SplitK;
     return exact ? kFp8 : kFp8Masked;
 }
 
@@ -561,6 +602,7 @@ int gemm_fp8(int64_t M, int64_t N, int64_t K, const gemm_fp8_t *A, int64_t lda, 
     hipError_t err = hipSuccess;
     switch (choose_kernel_fp8(M, N, K, A, lda, B, ldb, C, ldc)) {
     case kFp8: err = launch_tile_fp8(args, cus, stream); break;
+    case kFp8SplitK: err = launch_fp8_splitk_plan(args, cus, stream); break;
     case kFp8Masked: err = launch_tile_fp8_masked(args, cus, stream); break;
     case kGemvFp8: err = launch_gemv(args, stream, true); break;
     case kSkinnyFp8: err = launch_skinny_plan(args, cus, stream, true); break;

@@ -34,6 +34,7 @@
 #pragma once
 
 #include "device_common.h"
+#include "kernel_tile.h"
 #include "tile_schedule.h"
 
 namespace gb {
@@ -264,9 +265,14 @@ __device__ __forceinline__ void fp8_epilogue(char *smem, const GemmArgs &args, i
 // N % 256 == 0, K % 128 == 0 (masked: any M, N >= 1 and K % 16 == 0),
 // K > 0, A/B/C 16-byte aligned, lda/ldb multiples of 16, ldc a multiple of
 // 8, and 256*lda + K + 128, 256*ldb + K + 128 (bytes) below 2^31.
-template <uint32_t kFlags, bool kMasked>
+// kSplit (unmasked only): the units are (K range, tile) pairs -- unit u =
+// s * tiles + t covers slices s * kper .. of tile t -- and each stores its
+// unscaled fp32 partial to split.P; splitk_reduce_kernel then adds them in
+// range order and applies the scales and the epilogue (kFlags is unused).
+template <uint32_t kFlags, bool kMasked, bool kSplit = false>
 __global__ void __launch_bounds__(Fp8Config::kThreads)
-gemm_fp8_kernel(const GemmArgs args, const TileSchedule sched) {
+gemm_fp8_kernel(const GemmArgs args, const TileSchedule sched, const TileSplit split) {
+    static_assert(!(kSplit && kMasked), "split-K runs on exact tile multiples");
     using Cfg = Fp8Config;
     using RK = Fp8Kernel<kMasked>;
     __shared__ __attribute__((aligned(1024))) char smem[Cfg::kLdsBytes];
@@ -305,22 +311,33 @@ gemm_fp8_kernel(const GemmArgs args, const TileSchedule sched) {
         Ln.hi_off[ks] = (uint32_t)(((4 * ks + 2 + h) ^ swz) << 4);
     }
 
-    const int nk = (int)((args.K + Cfg::BK - 1) / Cfg::BK);
+    const int nk_all = (int)((args.K + Cfg::BK - 1) / Cfg::BK);
     const int num_tiles = sched.num_tiles();
+    const int num_units = kSplit ? num_tiles * split.splits : num_tiles;
 
-    for (int t = sched.slot(blockIdx.x); t < num_tiles; t += sched.grid) {
+    for (int u = sched.slot(blockIdx.x); u < num_units; u += sched.grid) {
+        int t = u, sp = 0, nk = nk_all;
+        if constexpr (kSplit) {
+            sp = u / num_tiles;
+            t = u - sp * num_tiles;
+            const int rest = nk_all - sp * split.kper;
+            nk = rest < split.kper ? rest : split.kper;
+        }
         int tm, tn;
         sched.tile(t, tm, tn);
         const int64_t m0 = (int64_t)tm * Cfg::BM;
         const int64_t n0 = (int64_t)tn * Cfg::BN;
+        // the unit's K range starts k0 bytes into every row (one byte per value)
+        const int64_t k0 = kSplit ? (int64_t)sp * split.kper * Cfg::BK : 0;
+        const int64_t kn = kSplit ? (int64_t)nk * Cfg::BK : args.K;
         if constexpr (kMasked) {
             Ln.rowsA = (int)(args.M - m0 < Cfg::BM ? args.M - m0 : Cfg::BM);
             Ln.rowsB = (int)(args.N - n0 < Cfg::BN ? args.N - n0 : Cfg::BN);
         }
         const __amdgpu_buffer_rsrc_t rA =
-            make_rsrc(A8 + m0 * args.lda, (uint32_t)((Cfg::BM - 1) * args.lda + args.K));
+            make_rsrc(A8 + m0 * args.lda + k0, (uint32_t)((Cfg::BM - 1) * args.lda + kn));
         const __amdgpu_buffer_rsrc_t rB =
-            make_rsrc(B8 + n0 * args.ldb, (uint32_t)((Cfg::BN - 1) * args.ldb + args.K));
+            make_rsrc(B8 + n0 * args.ldb + k0, (uint32_t)((Cfg::BN - 1) * args.ldb + kn));
 
         f32x16 acc[Cfg::FM][Cfg::FN];
 #pragma unroll
@@ -376,10 +393,15 @@ gemm_fp8_kernel(const GemmArgs args, const TileSchedule sched) {
         }
         RK::template slice<2>(smem, j, sa, Ln, rA, rB, fa, fb, acc);
 
-        // Every wave is done reading the ring (all loads landed at the last
-        // wait): its memory now stages the epilogue.
-        lds_barrier();
-        fp8_epilogue<kFlags, kMasked>(smem, args, m0, n0, wm, wn, lane, Ln.wave, acc);
+        if constexpr (kSplit) {
+            // no LDS use: the next unit's first barrier orders the ring
+            tile_store_partial<Cfg>(split, sp, m0, n0, wm, wn, lane, acc);
+        } else {
+            // Every wave is done reading the ring (all loads landed at the
+            // last wait): its memory now stages the epilogue.
+            lds_barrier();
+            fp8_epilogue<kFlags, kMasked>(smem, args, m0, n0, wm, wn, lane, Ln.wave, acc);
+        }
     }
 }
 
@@ -394,8 +416,38 @@ hipError_t launch_fp8_ring(const GemmArgs &args, int cus, hipStream_t stream) {
     const int tiles = s.num_tiles();
     s.grid = tiles < cus ? tiles : cus;
     const dim3 grid(s.grid), block(Fp8Config::kThreads);
+    const TileSplit none{};
     dispatch_flags(args.flags, [&](auto f) {
-        hipLaunchKernelGGL((gemm_fp8_kernel<decltype(f)::value, kMasked>), grid, block, 0, stream, args, s);
+        hipLaunchKernelGGL((gemm_fp8_kernel<decltype(f)::value, kMasked>), grid, block, 0, stream, args, s, none);
+    });
+    return hipGetLastError();
+}
+
+// Split-K on small grids: the tile kernel over (range, tile) units into the
+// workspace split.P, then the reduction (which applies the scales and the
+// epilogue).  The host has checked the exact-tile requirements, M % 8 == 0,
+// split.splits >= 2, every range non-empty, and that split.P holds
+// splits * M * N floats (ldp = M, pstride = M * N).
+inline hipError_t launch_fp8_splitk(const GemmArgs &args, const TileSplit &split, int cus, hipStream_t stream) {
+    TileSchedule s{};
+    s.tiles_m = (int)(args.M / Fp8Config::BM);
+    s.tiles_n = (int)(args.N / Fp8Config::BN);
+    s.group_m = 4;
+    s.order = kOrderGrouped;
+    s.hilbert_log2 = 0;
+    const int units = s.num_tiles() * split.splits;
+    s.grid = units < cus ? units : cus;
+    hipLaunchKernelGGL((gemm_fp8_kernel<0u, false, true>), dim3(s.grid), dim3(Fp8Config::kThreads), 0, stream, args,
+                       s, split);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t threads = args.M / 8 * args.N;
+    const int64_t blocks = (threads + 255) / 256;
+    const int64_t cap = (int64_t)cus * 8;
+    const dim3 rgrid((unsigned)(blocks < cap ? blocks : cap));
+    dispatch_flags(args.flags, [&](auto f) {
+        hipLaunchKernelGGL((splitk_reduce_kernel<decltype(f)::value, false>), rgrid, dim3(256), 0, stream, args,
+                           split);
     });
     return hipGetLastError();
 }

@@ -450,7 +450,8 @@ gemm_tile_kernel(const GemmArgs args, const TileSchedule sched, const TileSplit 
 }
 
 // The split-K reduction: thread i takes 8 consecutive rows of one column,
-// adds the splits' partials in range order, applies alpha, beta*C, bias and
+// adds the splits' partials in range order, multiplies by the fp8 scales
+// when the call has them, applies alpha, beta*C, bias and
 // the activation in fp32 and writes one 16-byte run of bf16 C -- or, with
 // kQ8, quantizes the 8 values with their rows' scales and writes 8 bytes of
 // int8 Q.  Requires M % 8 == 0, C 16-byte aligned and ldc % 8 == 0 (when C
@@ -497,7 +498,18 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs args,
                 cin[2 * e + 1] = bf16_bits_to_f32(raw[e] >> 16);
             }
         }
-        const float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        // fp8 inputs: the sum times scale_a[m] and scale_b[n] (NULL = 1), as
+        // in the fp8 tile kernel's own epilogue
+        if (args.scale_a) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = x[e] * args.scale_a[m + e];
+        }
+        if (args.scale_b) {
+            const float sb = args.scale_b[n];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = x[e] * sb;
+        }
         if constexpr (kQ8) {
             const f32x4 s_lo = *(const f32x4 *)(args.scale + m);
             const f32x4 s_hi = *(const f32x4 *)(args.scale + m + 4);

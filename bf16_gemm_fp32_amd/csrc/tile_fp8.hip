@@ -1,4 +1,5 @@
-// tile_fp8.hip -- instances of the 256x256 FP8 (E4M3) tile kernel.
+// tile_fp8.hip -- instances of the 256x256 FP8 (E4M3) tile kernel, whole-K
+// and split-K (with its reduction).
 #include "configs.h"
 #include "kernel_fp8.h"
 
@@ -8,6 +9,10 @@ static_assert(Fp8Config::BM == ShapeFp8::BM && Fp8Config::BN == ShapeFp8::BN && 
 
 hipError_t launch_tile_fp8(const GemmArgs &args, int cus, hipStream_t stream) {
     return launch_fp8_ring<false>(args, cus, stream);
+}
+
+hipError_t launch_tile_fp8_splitk(const GemmArgs &args, const TileSplit &split, int cus, hipStream_t stream) {
+    return launch_fp8_splitk(args, split, cus, stream);
 }
 
 }  // namespace gb

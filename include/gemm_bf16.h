@@ -20,9 +20,9 @@
  * Every function is thread-safe.  The library keeps no pointer to caller
  * buffers after a call returns.  Its one device allocation is the split-K
  * workspace (fp32 partial sums, and counters for the short-product kernel)
- * used by two kinds of shape: 3 <= M <= 64 with few columns, and products
+ * used by three kinds of shape: 3 <= M <= 64 with few columns, products
  * whose 128x128 tiles would leave most compute units idle (for example
- * 1024 x 1024 x 4096).  It is one buffer per (device, stream), allocated
+ * 1024 x 1024 x 4096), and FP8 products whose 256x256 tiles would.  It is one buffer per (device, stream), allocated
  * with hipMalloc and its counters zeroed with hipMemsetAsync on the first
  * call that needs it, grown (after synchronising that stream) when a later
  * call needs more, and kept until the process ends; it holds at most about
@@ -162,8 +162,11 @@ int gemm_bf16_q8(int64_t M, int64_t N, int64_t K,
  * 16 and A, B 16-byte aligned: 1 <= M <= 4 takes a matrix-vector kernel
  * and 5 <= M <= 64 a streaming FP8 MFMA kernel (any ldc); larger M the
  * 256x256 FP8 MFMA kernel when C is 16-byte aligned and ldc a multiple of 8
- * (any M and N; tails are masked).  Other inputs take the bounds-checked
- * path (same result).
+ * (any M and N; tails are masked).  When those tiles are exact multiples
+ * and would fill less than half of the compute units, K is split over up to
+ * eight ranges (fp32 partials in the split-K workspace, at most 16 MiB,
+ * then an ordered reduction that applies the scales and the epilogue).
+ * Other inputs take the bounds-checked path (same result).
  */
 int gemm_fp8(int64_t M, int64_t N, int64_t K,
              const gemm_fp8_t *A, int64_t lda,

@@ -106,6 +106,12 @@ def test_fp8_argument_errors_and_names():
     assert name(4000, 4096, 4096, P, 4096, P, 4096, P, 4004) == "generic64x64x32"      # ldc % 8 != 0
     # one to four rows: the matrix-vector kernel (any ldc)
     assert name(1, 4096, 4096, P, 4096, P, 4096, P, 1) == "gemv_fp8"
+    # small grids of exact FP8 tiles split K; larger grids and short K do not
+    assert name(1024, 1024, 4096, P, 4096, P, 4096, P, 1024) == "splitk_fp8_256x256x128"
+    assert name(512, 512, 8192, P, 8192, P, 8192, P, 512) == "splitk_fp8_256x256x128"
+    assert name(1024, 1024, 384, P, 384, P, 384, P, 1024) == "fp8_256x256x128"     # 3 slices
+    assert name(2048, 4096, 4096, P, 4096, P, 4096, P, 2048) == "fp8_256x256x128"  # 128 tiles
+    assert name(2048, 2048, 4096, P, 4096, P, 4096, P, 2048) == "fp8_256x256x128"  # 4M outputs: partials capped
     assert name(4, 4096, 4096, P, 4096, P, 4096, P + 2, 5) == "gemv_fp8"
     assert name(5, 4096, 4096, P, 4096, P, 4096, P, 8) == "skinny_fp8"
     assert name(64, 8192, 8192, P, 8192, P, 8192, P, 64) == "skinny_fp8"

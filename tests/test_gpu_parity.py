@@ -625,6 +625,61 @@ def test_fp8_ring_padded_leading_dims():
               expect_kernel=FP8R)
 
 
+# Split-K on the FP8 tiles for small grids: ranges of unequal length, the
+# scales applied by the reduction, every epilogue combination, forced range
+# counts, run-to-run bit equality.
+FP8S = "splitk_fp8_256x256x128"
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1024, 1024, 4096),   # 16 tiles, 32 slices: 4 ranges
+    (512, 512, 8192),     # 4 tiles, 64 slices: 8 ranges
+    (256, 768, 1664),     # 3 tiles, 13 slices: ranges of 5, 5, 3
+    (512, 256, 1024),     # 2 tiles, 8 slices: 2 ranges
+])
+def test_fp8_splitk_shapes(M, N, K):
+    check_fp8(f"fp8 splitk {M}x{N}x{K}", M, N, K, beta=0.5, use_bias=True, epilogue="gelu_tanh",
+              seed=M + 2 * N + K, expect_kernel=FP8S)
+
+
+@pytest.mark.parametrize("beta,use_bias,epi,scales", [(b, u, e, sc) for b in (0.0, -0.75) for u in (False, True)
+                                                      for e in ("none", "gelu_tanh", "relu") for sc in (True, False)
+                                                      if not (u and not sc and e == "relu")])
+def test_fp8_splitk_epilogue_combinations(beta, use_bias, epi, scales):
+    check_fp8(f"fp8 splitk beta={beta} bias={use_bias} {epi} scales={scales}", 512, 256, 1024, alpha=1.25,
+              beta=beta, use_bias=use_bias, epilogue=epi, scales=scales,
+              seed=100 + int(abs(beta) * 4) + 2 * use_bias + len(epi) + 7 * scales, expect_kernel=FP8S)
+
+
+def test_fp8_splitk_padded_leading_dims():
+    check_fp8("fp8 splitk padded", 512, 512, 2048, lda=2064, ldb=2080, ldc=520, beta=0.5, use_bias=True,
+              seed=131, expect_kernel=FP8S)
+
+
+@pytest.mark.parametrize("splits", ["2", "3", "5"])
+def test_fp8_splitk_forced_range_counts(splits, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FP8_SPLITS", splits)
+    check_fp8(f"fp8 splitk {splits} ranges", 256, 512, 2560, beta=0.25, use_bias=True, seed=140 + int(splits),
+              expect_kernel=FP8S)
+
+
+def test_fp8_splitk_deterministic():
+    M, N, K = 512, 512, 4096
+    A, B = inputs.normal_fp8(150, M * K), inputs.normal_fp8(151, N * K)
+    a_t, a_p = to_dev_u8(A)
+    b_t, b_p = to_dev_u8(B)
+    assert gb.gemm_fp8_kernel_name(M, N, K, a_p, K, b_p, K, a_p, M) == FP8S
+    outs = []
+    for _ in range(3):
+        c = torch.full((M * N,), -1, dtype=torch.int16, device="cuda")
+        st = gb.gemm_fp8(M, N, K, a_p, K, b_p, K, c.data_ptr(), M, 1.0, 0.0, 0, 0, 0, 0,
+                         torch.cuda.current_stream().cuda_stream)
+        assert st == 0
+        torch.cuda.synchronize()
+        outs.append(c.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2]), "fp8 split-K results vary"
+
+
 # The masked FP8 instance: M and N tails of every size class, K tails down
 # to a single 16-byte chunk, padded leading dimensions, epilogue
 # combinations, and exact tile multiples forced through it.
