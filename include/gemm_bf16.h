@@ -159,8 +159,9 @@ int gemm_bf16_q8(int64_t M, int64_t N, int64_t K,
  *   scale_b  NULL (all 1), or a device pointer to N fp32 per-column scales.
  *
  * Errors and quick returns as gemm_bf16.  With K, lda and ldb multiples of
- * 16 and A, B 16-byte aligned: 1 <= M <= 4 takes a matrix-vector kernel
- * and 5 <= M <= 64 a streaming FP8 MFMA kernel (any ldc); larger M the
+ * 16 and A, B 16-byte aligned: 1 <= M <= 2 (and 3 <= M <= 4 when
+ * N * K < 2^26) takes a matrix-vector kernel and the other M <= 64 a
+ * streaming FP8 MFMA kernel (any ldc); larger M the
  * 256x256 FP8 MFMA kernel when C is 16-byte aligned and ldc a multiple of 8
  * (any M and N; tails are masked).  When those tiles are exact multiples
  * and would fill less than half of the compute units, K is split over up to

@@ -106,6 +106,9 @@ def test_fp8_argument_errors_and_names():
     assert name(4000, 4096, 4096, P, 4096, P, 4096, P, 4004) == "generic64x64x32"      # ldc % 8 != 0
     # one to four rows: the matrix-vector kernel (any ldc)
     assert name(1, 4096, 4096, P, 4096, P, 4096, P, 1) == "gemv_fp8"
+    assert name(2, 8192, 8192, P, 8192, P, 8192, P, 2) == "gemv_fp8"
+    assert name(3, 8192, 8192, P, 8192, P, 8192, P, 3) == "skinny_fp8"   # large B: A shared per strip
+    assert name(4, 16384, 4096, P, 4096, P, 4096, P, 4) == "skinny_fp8"
     # small grids of exact FP8 tiles split K; larger grids and short K do not
     assert name(1024, 1024, 4096, P, 4096, P, 4096, P, 1024) == "splitk_fp8_256x256x128"
     assert name(512, 512, 8192, P, 8192, P, 8192, P, 512) == "splitk_fp8_256x256x128"

@@ -625,6 +625,12 @@ def test_fp8_ring_padded_leading_dims():
               expect_kernel=FP8R)
 
 
+@pytest.mark.parametrize("M,N,K,ldc", [(3, 8192, 8192, 3), (4, 16384, 4096, 8)])
+def test_fp8_three_and_four_rows_on_large_b_take_the_streaming_kernel(M, N, K, ldc):
+    check_fp8(f"fp8 rows {M} large B", M, N, K, ldc=ldc, beta=0.5, use_bias=True, epilogue="gelu_tanh",
+              seed=M * 11 + 5, expect_kernel="skinny_fp8")
+
+
 # Split-K on the FP8 tiles for small grids: ranges of unequal length, the
 # scales applied by the reduction, every epilogue combination, forced range
 # counts, run-to-run bit equality.
