@@ -42,7 +42,9 @@ hipError_t launch_tile_medium_splitk_q8(const GemmArgs &args, const TileSplit &s
 hipError_t launch_tile_ring_mfma32(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_ring(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_ring_masked(const GemmArgs &args, int cus, hipStream_t stream);
+// int8 output: exact tile multiples, and shapes with tails (masked)
 hipError_t launch_tile_ring_q8(const GemmArgs &args, int cus, hipStream_t stream);
+hipError_t launch_tile_ring_q8_masked(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_fp8(const GemmArgs &args, int cus, hipStream_t stream);
 // split-K on the FP8 tiles (split.P: splits * M * N floats of workspace)
 hipError_t launch_tile_fp8_splitk(const GemmArgs &args, const TileSplit &split, int cus, hipStream_t stream);

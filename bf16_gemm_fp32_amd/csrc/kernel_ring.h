@@ -478,7 +478,6 @@ gemm_ring_kernel(const GemmArgs args, const TileSchedule sched) {
 // the shape has tails.
 template <bool kMasked, bool kQ8 = false>
 hipError_t launch_ring_t(const GemmArgs &args, const TileSchedule &s, hipStream_t stream) {
-    static_assert(kMasked || !kQ8, "the quantizing output is built on the masked instance");
     const dim3 grid(s.grid), block(RingConfig::kThreads);
     dispatch_flags(args.flags, [&](auto f) {
         hipLaunchKernelGGL((gemm_ring_kernel<decltype(f)::value, kMasked, kQ8>), grid, block, 0, stream, args, s);

@@ -79,7 +79,7 @@ def test_q8_argument_errors():
     assert call_q8(0, 4, 4, Q=0, scale=0) == OK
     name = gb.gemm_bf16_q8_kernel_name
     assert name(4096, 4096, 4096, P, 4096, P, 4096, 0, 1, P, 4096, 0.0, P, 2) == "ring256x256x64_q8"
-    assert name(4000, 4000, 1000, P, 1000, P, 1000, P, 4000, P, 4000, 0.5, P, 1) == "ring256x256x64_q8"
+    assert name(4000, 4000, 1000, P, 1000, P, 1000, P, 4000, P, 4000, 0.5, P, 1) == "ring256x256x64_q8_masked"
     assert name(4096, 4096, 4096, P, 4096, P, 4096, 0, 1, P + 8, 4096, 0.0, P, 0) == "generic64x64x32"
     assert name(4096, 4096, 4096, P, 4096, P, 4096, 0, 1, P, 4100, 0.0, P, 0) == "generic64x64x32"
     assert name(100, 100, 64, P, 64, P, 64, 0, 1, P, 112, 0.0, P, 0) == "generic64x64x32"

@@ -501,6 +501,7 @@ def check_q8(tag, M, N, K, ldq=None, ldc=None, alpha=1.0, beta=0.0, use_bias=Fal
 
 
 RQ8 = "ring256x256x64_q8"
+RQ8M = "ring256x256x64_q8_masked"
 SQ8 = "splitk128x128x64_q8"
 
 
@@ -524,17 +525,33 @@ def test_q8_ring_is_the_default_for_large_shapes():
     (1001, 777, 200, 1008), (257, 513, 8, 264), (1, 255, 64, 8), (300, 260, 72, 304), (512, 512, 256, 512),
 ])
 def test_q8_ring_tails(M, N, K, ldq, monkeypatch):
-    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", RQ8)
-    check_q8(f"q8 ring {M}x{N}x{K}", M, N, K, ldq=ldq, zp=3, seed=M + N, expect_kernel=RQ8)
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", RQ8M)
+    check_q8(f"q8 ring {M}x{N}x{K}", M, N, K, ldq=ldq, zp=3, seed=M + N, expect_kernel=RQ8M)
 
 
 @pytest.mark.parametrize("beta,use_bias,epi", [(b, u, e) for b in (0.0, -0.75) for u in (False, True)
                                                for e in ("none", "gelu_tanh", "relu")])
 def test_q8_ring_epilogue_combinations(beta, use_bias, epi, monkeypatch):
-    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", RQ8)
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", RQ8M)
     check_q8(f"q8 ring beta={beta} bias={use_bias} {epi}", 777, 300, 200, ldq=784, ldc=792, alpha=1.25, beta=beta,
              use_bias=use_bias, epilogue=epi, zp=-5, seed=70 + int(abs(beta) * 4) + 2 * use_bias + len(epi),
-             expect_kernel=RQ8)
+             expect_kernel=RQ8M)
+
+
+# The unmasked int8 instance (exact tile multiples): every epilogue
+# combination, padded leading dimensions, several tiles per compute unit.
+@pytest.mark.parametrize("beta,use_bias,epi", [(b, u, e) for b in (0.0, -0.75) for u in (False, True)
+                                               for e in ("none", "gelu_tanh", "relu")])
+def test_q8_exact_ring_epilogue_combinations(beta, use_bias, epi, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", RQ8)
+    check_q8(f"q8 exact ring beta={beta} bias={use_bias} {epi}", 768, 512, 320, ldq=776, ldc=784, alpha=0.75,
+             beta=beta, use_bias=use_bias, epilogue=epi, zp=4,
+             seed=170 + int(abs(beta) * 4) + 2 * use_bias + len(epi), expect_kernel=RQ8)
+
+
+def test_q8_exact_ring_many_tiles():
+    check_q8("q8 exact ring 4608x2048", 4608, 2048, 256, beta=0.5, use_bias=True, epilogue="gelu_tanh", zp=-3,
+             seed=190, expect_kernel=RQ8)
 
 
 def test_q8_saturation_both_paths(monkeypatch):
