@@ -20,7 +20,7 @@
 namespace gb {
 
 enum KernelKind {
-    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8, kSplitK, kGemv, kSplitKQ8, kFp8Masked, kGemvFp8, kSkinnyFp8, kFp8SplitK, kRingQ8Masked, kNumKinds
+    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8, kSplitK, kGemv, kSplitKQ8, kFp8Masked, kGemvFp8, kSkinnyFp8, kFp8SplitK, kRingQ8Masked, kSkinnyQ8, kNumKinds
 };
 
 static const char *const kKindNames[kNumKinds] = {"none",            "tile256x256x32_s5", "tile128x128x64_s4",
@@ -30,7 +30,8 @@ static const char *const kKindNames[kNumKinds] = {"none",            "tile256x25
                                                   "fp8_256x256x128",  "splitk128x128x64", "gemv",
                                                   "splitk128x128x64_q8", "fp8_256x256x128_masked",
                                                   "gemv_fp8",          "skinny_fp8",
-                                                  "splitk_fp8_256x256x128", "ring256x256x64_q8_masked"};
+                                                  "splitk_fp8_256x256x128", "ring256x256x64_q8_masked",
+                                                  "skinny_q8"};
 
 static const char *kind_name(int k) { return (k >= 0 && k < kNumKinds) ? kKindNames[k] : "none"; }
 
@@ -161,7 +162,7 @@ struct SkinnyPlan {
     int rows, cols, strips, splits, spp;
 };
 
-static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int cus, bool fp8 = false) {
+static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int cus, bool fp8 = false, bool q8 = false) {
     SkinnyPlan p{};
     p.rows = M <= 32 ? 32 : 64;
     int width = 32;
@@ -169,7 +170,7 @@ static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int cus, bool fp8
         const int w = std::atoi(env);
         if (w == 32 || w == 64 || w == 128) width = w;
     }
-    if (fp8) width = 32;  // the FP8 instances are built for 32-column strips
+    if (fp8 || q8) width = 32;  // the FP8 and int8-output instances are built for 32-column strips
     p.cols = width;
     const int ks = fp8 ? ShapeSkinny::KS_FP8 : (width == 32 ? ShapeSkinny::KS_N32 : ShapeSkinny::KS_WIDE);
     const int64_t nk = (K + ks - 1) / ks;
@@ -232,21 +233,25 @@ static hipError_t get_workspace(hipStream_t stream, size_t counters, size_t part
     return hipSuccess;
 }
 
-static hipError_t launch_skinny_plan(const GemmArgs &args, int cus, hipStream_t stream, bool fp8 = false) {
-    const SkinnyPlan p = plan_skinny(args.M, args.N, args.K, cus, fp8);
+static hipError_t launch_skinny_plan(const GemmArgs &args, int cus, hipStream_t stream, bool fp8 = false,
+                                     bool q8 = false) {
+    const SkinnyPlan p = plan_skinny(args.M, args.N, args.K, cus, fp8, q8);
     SkinnyWork work{};
     work.num_strips = p.strips;
     work.splits = p.splits;
     work.spp = p.spp;
     work.c_vector = aligned16(args.C) && args.ldc % 8 == 0;
+    work.q_vector = q8 && (reinterpret_cast<uintptr_t>(args.Q) & 7u) == 0 && args.ldq % 8 == 0;
     if (p.splits > 1) {
         const size_t floats = (size_t)p.strips * p.splits * p.cols * p.rows;
         std::lock_guard<std::mutex> lock(g_ws_mutex);
         hipError_t err = get_workspace(stream, (size_t)p.strips, floats, &work.counters, &work.partials);
         if (err != hipSuccess) return err;
+        if (q8) return launch_skinny_q8(p.rows, args, work, cus, stream);
         return fp8 ? launch_skinny_fp8(p.rows, args, work, cus, stream)
                    : launch_skinny(p.rows, p.cols, args, work, cus, stream);
     }
+    if (q8) return launch_skinny_q8(p.rows, args, work, cus, stream);
     return fp8 ? launch_skinny_fp8(p.rows, args, work, cus, stream)
                : launch_skinny(p.rows, p.cols, args, work, cus, stream);
 }
@@ -405,6 +410,15 @@ static int choose_kernel_q8(int64_t M, int64_t N, int64_t K, const void *A, int6
                             int64_t ldb, const void *C, int64_t ldc, float beta, const void *Q, int64_t ldq,
                             const void *scale, int cus) {
     if (M == 0 || N == 0) return kNone;
+    // At most 64 rows: the streaming kernel with the int8 epilogue (any ldc
+    // and ldq; 8-row chunks of Q go out as one store when Q allows it).
+    {
+        const char *force = std::getenv("GEMM_BF16_FORCE_KERNEL");
+        const bool forced_other = force && (!std::strcmp(force, kKindNames[kGeneric]) ||
+                                            !std::strcmp(force, kKindNames[kRingQ8]) ||
+                                            !std::strcmp(force, kKindNames[kRingQ8Masked]));
+        if (!forced_other && skinny_path_ok(M, N, K, A, lda, B, ldb, C, ldc)) return kSkinnyQ8;
+    }
     const void *c_probe = beta != 0.0f ? C : A;  // C is not read when beta == 0
     const int64_t ldc_probe = beta != 0.0f ? ldc : 8;
     const bool ok = ring_masked_ok(M, N, K, A, lda, B, ldb, c_probe, ldc_probe) && aligned16(Q) &&
@@ -563,6 +577,7 @@ int gemm_bf16_q8(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t 
     switch (choose_kernel_q8(M, N, K, A, lda, B, ldb, C, ldc, beta, Q, ldq, scale, cus)) {
     case kRingQ8: err = launch_tile_ring_q8(args, cus, stream); break;
     case kRingQ8Masked: err = launch_tile_ring_q8_masked(args, cus, stream); break;
+    case kSkinnyQ8: err = launch_skinny_plan(args, cus, stream, false, true); break;
     case kSplitKQ8: err = launch_splitk_plan(args, cus, stream, true); break;
     default: err = launch_generic(args, cus, stream); break;
     }

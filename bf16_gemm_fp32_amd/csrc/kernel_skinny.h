@@ -100,6 +100,7 @@ struct SkinnyWork {
     int splits;
     int spp;       // K-slices per split (the last split may have fewer)
     int c_vector;  // C 16-byte aligned and ldc % 8 == 0: 8-row chunks move as one 16-byte access
+    int q_vector;  // int8 output: Q 8-byte aligned and ldq % 8 == 0 (8-row chunks as one 8-byte store)
     float *partials;
     uint32_t *counters;
 };
@@ -110,9 +111,13 @@ struct SkinnyWork {
 // work.c_vector), the byte offsets of one unit ((BMr-1)*lda + K + a slice,
 // (BN-1)*ldb + K + a slice) below 2^31, and every split owning at least one
 // K-slice.
-template <class Cfg, uint32_t kFlags, bool kFp8 = false>
+// kQ8: the int8 output of the quantizing entry point -- the epilogue value
+// of row m becomes sat8(rne(fma(v, scale[m], zp))) in Q (C is then only
+// read, when beta != 0).
+template <class Cfg, uint32_t kFlags, bool kFp8 = false, bool kQ8 = false>
 __global__ void __launch_bounds__(Cfg::kThreads)
 gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
+    static_assert(!(kFp8 && kQ8), "int8 output is built for bf16 inputs");
     __shared__ __attribute__((aligned(1024))) char smem[Cfg::kLdsBytes];
     char *const ringA = smem;
     char *const ringB = smem + Cfg::SA * Cfg::kABytes;
@@ -362,6 +367,23 @@ gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
                     for (int e = 0; e < 8 && m + e < args.M; ++e) cin[e] = bf16_bits_to_f32(cp[e]);
                 }
             }
+            if constexpr (kQ8) {
+                // rows past M get scale 0 and are never stored
+                u32x2 qw = {0u, 0u};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float v = epilogue_value<kFlags>(xs[e], cin[e], bias_v, args.alpha, args.beta);
+                    const float sc = m + e < args.M ? args.scale[m + e] : 0.f;
+                    qw[e >> 2] |= ((uint32_t)quantize_i8(v, sc, args.zp) & 0xFFu) << ((e & 3) * 8);
+                }
+                int8_t *qp = args.Q + n * args.ldq + m;
+                if (m + 8 <= args.M && work.q_vector) {
+                    __builtin_nontemporal_store(qw, (u32x2 *)qp);
+                } else {
+                    for (int e = 0; e < 8 && m + e < args.M; ++e) qp[e] = (int8_t)(qw[e >> 2] >> ((e & 3) * 8));
+                }
+                return;
+            }
             u32x4 out;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -435,15 +457,20 @@ gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
 }
 
 // One workgroup per compute unit (at most one per work unit).
-template <class Cfg, bool kFp8 = false>
+template <class Cfg, bool kFp8 = false, bool kQ8 = false>
 hipError_t launch_skinny(const GemmArgs &args, const SkinnyWork &work, int cus, hipStream_t stream) {
     const int units = work.num_strips * work.splits;
     const dim3 grid(units < cus ? units : cus), block(Cfg::kThreads);
     dispatch_flags(args.flags, [&](auto f) {
-        hipLaunchKernelGGL((gemm_skinny_kernel<Cfg, decltype(f)::value, kFp8>), grid, block, 0, stream, args,
+        hipLaunchKernelGGL((gemm_skinny_kernel<Cfg, decltype(f)::value, kFp8, kQ8>), grid, block, 0, stream, args,
                            work);
     });
     return hipGetLastError();
 }
+
+// The 32-column configurations the host plans with: rows of 64 (or 32),
+// K-slices of 256 in A/B rings of 3 and 4 (6 for 32 rows) slices.
+using SkinnyM64N32 = SkinnyConfig<2, 1, 256, 3, 4>;
+using SkinnyM32N32 = SkinnyConfig<1, 1, 256, 3, 6>;
 
 }  // namespace gb

@@ -6,10 +6,8 @@
 
 namespace gb {
 
-using SkinnyM64N32 = SkinnyConfig<2, 1, 256, 3, 4>;
 using SkinnyM64N64 = SkinnyConfig<2, 2, 128, 3, 7>;
 using SkinnyM64N128 = SkinnyConfig<2, 4, 128, 2, 4>;
-using SkinnyM32N32 = SkinnyConfig<1, 1, 256, 3, 6>;
 using SkinnyM32N64 = SkinnyConfig<1, 2, 128, 3, 8>;
 using SkinnyM32N128 = SkinnyConfig<1, 4, 128, 2, 4>;
 

@@ -131,6 +131,13 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K,
  * ldq < max(1,M), and ldc is only checked when beta != 0; GEMM_ERR_NULL also
  * for a NULL Q or scale (M*N > 0), and for a NULL C only when beta != 0.
  * Q must not overlap A, B, C, bias or scale.
+ *
+ * Kernels: 1 <= M <= 64 (K, lda, ldb multiples of 8, A and B 16-byte
+ * aligned; any ldc, ldq and Q alignment) the streaming kernel, splitting K
+ * through the split-K workspace when the strips are few; large grids the
+ * 256x256 ring kernel (Q, scale 16-byte aligned, ldq % 8 == 0); small grids
+ * of 128x128 tiles split-K with a quantizing reduction; else the
+ * bounds-checked kernel.  All give the same result.
  */
 int gemm_bf16_q8(int64_t M, int64_t N, int64_t K,
                  const gemm_bf16_t *A, int64_t lda,

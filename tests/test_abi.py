@@ -80,6 +80,9 @@ def test_q8_argument_errors():
     name = gb.gemm_bf16_q8_kernel_name
     assert name(4096, 4096, 4096, P, 4096, P, 4096, 0, 1, P, 4096, 0.0, P, 2) == "ring256x256x64_q8"
     assert name(4000, 4000, 1000, P, 1000, P, 1000, P, 4000, P, 4000, 0.5, P, 1) == "ring256x256x64_q8_masked"
+    assert name(1, 4096, 4096, P, 4096, P, 4096, 0, 1, P + 3, 1, 0.0, P, 2) == "skinny_q8"    # any Q alignment
+    assert name(64, 8192, 8192, P, 8192, P, 8192, 0, 64, P, 64, 0.0, P, 0) == "skinny_q8"
+    assert name(65, 8192, 8192, P, 8192, P, 8192, 0, 72, P, 72, 0.0, P, 0) != "skinny_q8"
     assert name(4096, 4096, 4096, P, 4096, P, 4096, 0, 1, P + 8, 4096, 0.0, P, 0) == "generic64x64x32"
     assert name(4096, 4096, 4096, P, 4096, P, 4096, 0, 1, P, 4100, 0.0, P, 0) == "generic64x64x32"
     assert name(100, 100, 64, P, 64, P, 64, 0, 1, P, 112, 0.0, P, 0) == "generic64x64x32"

@@ -562,6 +562,41 @@ def test_q8_saturation_both_paths(monkeypatch):
     check_q8("q8 saturating ring", 512, 256, 256, scale_range=(4.0, 8.0), zp=7, seed=82, expect_kernel=RQ8)
 
 
+# Int8 output on the streaming kernel (1 to 64 rows): row tails inside the
+# 32- and 64-row blocks, K tails, padded and unaligned Q (element-wise
+# stores), the split-K path (few strips), every epilogue combination.
+SQ8K = "skinny_q8"
+
+
+@pytest.mark.parametrize("M,N,K,ldq,ldc,q_offset", [
+    (1, 4096, 4096, 1, 1, 0),        # decode
+    (3, 1000, 520, 3, 3, 0),         # a K tail inside the last slice
+    (17, 777, 1032, 24, 17, 0),      # padded ldq
+    (32, 2048, 2048, 32, 32, 0),     # a full 32-row block
+    (33, 515, 264, 40, 40, 3),       # 64-row block, unaligned Q
+    (64, 8192, 2048, 64, 64, 0),     # 256 strips, no split
+    (64, 256, 8192, 64, 64, 0),      # 8 strips: split K
+])
+def test_q8_skinny_shapes(M, N, K, ldq, ldc, q_offset):
+    check_q8(f"q8 skinny {M}x{N}x{K}", M, N, K, ldq=ldq, ldc=ldc, use_bias=True, epilogue="relu", zp=-7,
+             q_offset=q_offset, seed=200 + M + K, expect_kernel=SQ8K)
+
+
+@pytest.mark.parametrize("beta,use_bias,epi", [(b, u, e) for b in (0.0, -0.75) for u in (False, True)
+                                               for e in ("none", "gelu_tanh", "relu")])
+def test_q8_skinny_epilogue_combinations(beta, use_bias, epi):
+    check_q8(f"q8 skinny beta={beta} bias={use_bias} {epi}", 48, 640, 768, ldq=56, ldc=52, alpha=1.25, beta=beta,
+             use_bias=use_bias, epilogue=epi, zp=3, seed=220 + int(abs(beta) * 4) + 2 * use_bias + len(epi),
+             expect_kernel=SQ8K)
+
+
+@pytest.mark.parametrize("splits", ["2", "3", "7"])
+def test_q8_skinny_forced_splits(splits, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_SKINNY_SPLITS", splits)
+    check_q8(f"q8 skinny {splits} splits", 40, 512, 4096, beta=0.5, use_bias=True, epilogue="gelu_tanh", zp=1,
+             seed=240 + int(splits), expect_kernel=SQ8K)
+
+
 def test_q8_generic_paths():
     check_q8("q8 generic odd ldq", 100, 90, 77, ldq=103, beta=0.5, use_bias=True, epilogue="gelu_tanh", seed=83,
              expect_kernel="generic64x64x32")
