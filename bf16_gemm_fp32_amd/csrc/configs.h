@@ -39,6 +39,11 @@ hipError_t launch_tile_medium_splitk(const GemmArgs &args, const TileSplit &spli
 // the same with int8 output (the reduction quantizes per row)
 hipError_t launch_tile_medium_splitk_q8(const GemmArgs &args, const TileSplit &split, int cus,
                                         hipStream_t stream);
+// the same with tails (zero-filled loads, masked epilogue; split.P padded
+// to tile multiples)
+hipError_t launch_tile_medium_masked(const GemmArgs &args, int cus, hipStream_t stream);
+hipError_t launch_tile_medium_splitk_masked(const GemmArgs &args, const TileSplit &split, int cus,
+                                            hipStream_t stream);
 hipError_t launch_tile_ring_mfma32(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_ring(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_ring_masked(const GemmArgs &args, int cus, hipStream_t stream);

@@ -16,8 +16,11 @@ namespace gb {
 // each store is 16 bytes and a column's bytes are written contiguously.
 // alpha, beta*C (read the same way), bias[n] and the activation are applied
 // in fp32, then one RNE to bf16.  The caller has made the staging memory
-// free (a barrier after the last LDS read of the main loop).
-template <class Cfg, uint32_t kFlags>
+// free (a barrier after the last LDS read of the main loop).  kMasked:
+// columns past N and 8-row chunks past M are skipped, and a chunk that
+// straddles M -- or every chunk, when ldc % 8 != 0 or C is not 16-byte
+// aligned -- is read and written element by element.
+template <class Cfg, uint32_t kFlags, bool kMasked = false>
 __device__ __forceinline__ void tile_epilogue(char *smem, const GemmArgs &args, int64_t m0, int64_t n0, int wm,
                                               int wn, int lane, int wave, const f32x16 (&acc)[Cfg::FM][Cfg::FN]) {
     char *stage = smem + wave * Cfg::kEpiWaveBytes;
@@ -25,6 +28,7 @@ __device__ __forceinline__ void tile_epilogue(char *smem, const GemmArgs &args, 
     constexpr int kIters = 32 * kColChunks / 64;  // per lane per 32 columns
     static_assert((32 * kColChunks) % 64 == 0, "column chunks split over the wave");
     const int h = lane >> 5;
+    const bool cvec = !kMasked || ((args.ldc & 7) == 0 && (reinterpret_cast<uintptr_t>(args.C) & 15) == 0);
 #pragma unroll
     for (int j = 0; j < Cfg::FN; ++j) {
         // accumulators -> LDS
@@ -46,16 +50,22 @@ __device__ __forceinline__ void tile_epilogue(char *smem, const GemmArgs &args, 
             const f32x4 hi = *(const GB_LDS f32x4 *)(stage + col * Cfg::kEpiColBytes + q * 32 + 16);
             const int64_t n = n0 + wn * Cfg::WTN + j * 32 + col;
             const int64_t m = m0 + wm * Cfg::WTM + q * 8;
+            if (kMasked && (n >= args.N || m >= args.M)) continue;
+            const bool full = !kMasked || (m + 8 <= args.M && cvec);
             uint16_t *p = args.C + n * args.ldc + m;
             float bias_v = 0.f;
             if constexpr ((kFlags & kEpiBias) != 0) bias_v = bf16_bits_to_f32(args.bias[n]);
             float cin[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             if constexpr ((kFlags & kEpiBeta) != 0) {
-                const u32x4 raw = *(const u32x4 *)p;
+                if (full) {
+                    const u32x4 raw = *(const u32x4 *)p;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    cin[2 * e] = bf16_bits_to_f32(raw[e] & 0xFFFFu);
-                    cin[2 * e + 1] = bf16_bits_to_f32(raw[e] >> 16);
+                    for (int e = 0; e < 4; ++e) {
+                        cin[2 * e] = bf16_bits_to_f32(raw[e] & 0xFFFFu);
+                        cin[2 * e + 1] = bf16_bits_to_f32(raw[e] >> 16);
+                    }
+                } else {
+                    for (int e = 0; e < 8 && m + e < args.M; ++e) cin[e] = bf16_bits_to_f32(p[e]);
                 }
             }
             const float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -65,7 +75,11 @@ __device__ __forceinline__ void tile_epilogue(char *smem, const GemmArgs &args, 
                 out[e] = pack_bf16x2(
                     epilogue_value<kFlags>(x[2 * e], cin[2 * e], bias_v, args.alpha, args.beta),
                     epilogue_value<kFlags>(x[2 * e + 1], cin[2 * e + 1], bias_v, args.alpha, args.beta));
-            __builtin_nontemporal_store(out, (u32x4 *)p);
+            if (full) {
+                __builtin_nontemporal_store(out, (u32x4 *)p);
+            } else {
+                for (int e = 0; e < 8 && m + e < args.M; ++e) p[e] = (uint16_t)(out[e >> 1] >> ((e & 1) * 16));
+            }
         }
     }
 }

@@ -124,18 +124,43 @@ __device__ __forceinline__ void wait_vmcnt_rt(int n) {
     wait_vmcnt<kN>();
 }
 
-template <class Cfg>
+// kMasked: the shape has tails (M or N not a multiple of the tile, or K not
+// a multiple of BK; K and the leading dimensions multiples of 8).  Every
+// 16-byte operand chunk outside the matrix -- row or column past the end,
+// or k at or past the unit's K -- is loaded from an out-of-range buffer
+// offset, which the DMA turns into zeros (the zero-fill of the DeepGEMM
+// article, sections 4.2-4.3), and the epilogue masks its accesses.
+template <class Cfg, bool kMasked = false>
 struct TileKernel {
     static constexpr int S = Cfg::STAGES;
 
-    // Per-lane state that stays fixed for the whole launch.
+    // Per-lane state that stays fixed for the whole launch (the masking
+    // fields per tile).
     struct Lane {
         uint32_t vA[2], vB[2];            // load voffsets by parity of the row group
         uint32_t aRow, bRow;              // LDS row offsets of this lane's fragments
         uint32_t chunk_off[Cfg::KSTEPS];  // swizzled chunk offset per k-step
         uint32_t lda_bytes, ldb_bytes;
         int wave;
+        // masking only: this lane's row within a load's rows, its logical
+        // chunk by parity of the row group, the tile's valid rows of A and
+        // B and the unit's K
+        int lrow, lchunk[2];
+        int rowsA, rowsB, kmax;
     };
+
+    // The voffset of this lane's chunk in load q (row group q) of slice kt:
+    // the precomputed one, or the out-of-range offset outside the matrix.
+    template <bool kIsA>
+    __device__ __forceinline__ static uint32_t voff(int q, int kt, const Lane &L) {
+        uint32_t v = kIsA ? L.vA[q & 1] : L.vB[q & 1];
+        if constexpr (kMasked) {
+            const int row = q * Cfg::kRowsPerLoad + L.lrow;
+            const int k = kt * Cfg::BK + L.lchunk[q & 1] * 8;
+            if (!(row < (kIsA ? L.rowsA : L.rowsB) && k < L.kmax)) v = kOobOffset;
+        }
+        return v;
+    }
 
     // Loads number LO .. HI-1 of K-slice kt into ring buffer buf.  Loads
     // 0 .. kALoads-1 fill this wave's row groups of A, the rest those of B.
@@ -149,11 +174,11 @@ struct TileKernel {
         for (int idx = LO; idx < HI; ++idx) {
             if (idx < Cfg::kALoads) {
                 const int q = L.wave * Cfg::kALoads + idx;  // row group of the tile
-                buffer_load_lds16(rA, (GB_LDS void *)(sA + q * 1024), L.vA[q & 1],
+                buffer_load_lds16(rA, (GB_LDS void *)(sA + q * 1024), voff<true>(q, kt, L),
                                   (uint32_t)(q * Cfg::kRowsPerLoad) * L.lda_bytes + kbytes);
             } else {
                 const int q = L.wave * Cfg::kBLoads + (idx - Cfg::kALoads);
-                buffer_load_lds16(rB, (GB_LDS void *)(sB + q * 1024), L.vB[q & 1],
+                buffer_load_lds16(rB, (GB_LDS void *)(sB + q * 1024), voff<false>(q, kt, L),
                                   (uint32_t)(q * Cfg::kRowsPerLoad) * L.ldb_bytes + kbytes);
             }
         }
@@ -252,11 +277,11 @@ struct TileKernel {
             const int idx = LO + first + r;
             if (idx < Cfg::kALoads) {
                 const int q = L.wave * Cfg::kALoads + idx;
-                buffer_load_lds16(rA, (GB_LDS void *)(sA + q * 1024), L.vA[q & 1],
+                buffer_load_lds16(rA, (GB_LDS void *)(sA + q * 1024), voff<true>(q, kt, L),
                                   (uint32_t)(q * Cfg::kRowsPerLoad) * L.lda_bytes + kbytes);
             } else {
                 const int q = L.wave * Cfg::kBLoads + (idx - Cfg::kALoads);
-                buffer_load_lds16(rB, (GB_LDS void *)(sB + q * 1024), L.vB[q & 1],
+                buffer_load_lds16(rB, (GB_LDS void *)(sB + q * 1024), voff<false>(q, kt, L),
                                   (uint32_t)(q * Cfg::kRowsPerLoad) * L.ldb_bytes + kbytes);
             }
         }
@@ -340,11 +365,15 @@ __device__ __forceinline__ void tile_store_partial(const TileSplit &split, int s
 }
 
 // kSplit: the units are (K range, tile) pairs and each stores its partial
-// (kFlags is then unused: the reduction applies the epilogue).
-template <class Cfg, uint32_t kFlags, bool kSplit = false>
+// (kFlags is then unused: the reduction applies the epilogue).  kMasked:
+// any M, N >= 1 and K % 8 == 0 (tails zero-filled and masked); a masked
+// split stores whole tiles into a workspace padded to tile multiples
+// (split.ldp, split.pstride), the rows and columns past the matrix holding
+// zeros.
+template <class Cfg, uint32_t kFlags, bool kSplit = false, bool kMasked = false>
 __global__ void __launch_bounds__(Cfg::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_tile_kernel(const GemmArgs args, const TileSchedule sched, const TileSplit split) {
-    using TK = TileKernel<Cfg>;
+    using TK = TileKernel<Cfg, kMasked>;
     constexpr int S = Cfg::STAGES;
     constexpr int L = Cfg::kLoads;
     constexpr int H = Cfg::kHalf;
@@ -368,7 +397,10 @@ gemm_tile_kernel(const GemmArgs args, const TileSchedule sched, const TileSplit 
         const int c = lpos ^ lds_swizzle<Cfg::BK>(p * Cfg::kRowsPerLoad + lrow);
         Ln.vA[p] = lrow * Ln.lda_bytes + (uint32_t)(c << 4);
         Ln.vB[p] = lrow * Ln.ldb_bytes + (uint32_t)(c << 4);
+        Ln.lchunk[p] = c;
     }
+    Ln.lrow = lrow;
+    Ln.rowsA = Ln.rowsB = Ln.kmax = 0;
     // Read side: MFMA operand lane l takes row l % 32 of its 32-row block and
     // 8 consecutive k from logical chunk 2*kk + l/32.
     Ln.aRow = (uint32_t)(wm * Cfg::WTM + (lane & 31)) * Cfg::kRowBytes;
@@ -377,7 +409,7 @@ gemm_tile_kernel(const GemmArgs args, const TileSchedule sched, const TileSplit 
     for (int kk = 0; kk < Cfg::KSTEPS; ++kk)
         Ln.chunk_off[kk] = (uint32_t)(((2 * kk + (lane >> 5)) ^ lds_swizzle<Cfg::BK>(lane & 31)) << 4);
 
-    const int nk_all = (int)(args.K / Cfg::BK);
+    const int nk_all = (int)((args.K + Cfg::BK - 1) / Cfg::BK);
     const int num_tiles = sched.num_tiles();
     const int num_units = kSplit ? num_tiles * split.splits : num_tiles;
 
@@ -395,6 +427,11 @@ gemm_tile_kernel(const GemmArgs args, const TileSchedule sched, const TileSplit 
         const int64_t n0 = (int64_t)tn * Cfg::BN;
         const int64_t k0 = kSplit ? (int64_t)s * split.kper * Cfg::BK : 0;
         const int64_t kn = (int64_t)nk * Cfg::BK;
+        if constexpr (kMasked) {
+            Ln.rowsA = (int)(args.M - m0 < Cfg::BM ? args.M - m0 : Cfg::BM);
+            Ln.rowsB = (int)(args.N - n0 < Cfg::BN ? args.N - n0 : Cfg::BN);
+            Ln.kmax = (int)(args.K - k0);  // the unit's K: chunks at or past it are zeros
+        }
         const __amdgpu_buffer_rsrc_t rA =
             make_rsrc(args.A + m0 * args.lda + k0, (uint32_t)(((Cfg::BM - 1) * args.lda + kn) * 2));
         const __amdgpu_buffer_rsrc_t rB =
@@ -444,7 +481,7 @@ gemm_tile_kernel(const GemmArgs args, const TileSchedule sched, const TileSplit 
             // Every wave is done reading the ring (all loads landed at the
             // last wait): its memory now stages the epilogue.
             lds_barrier();
-            tile_epilogue<Cfg, kFlags>(smem, args, m0, n0, wm, wn, lane, Ln.wave, acc);
+            tile_epilogue<Cfg, kFlags, kMasked>(smem, args, m0, n0, wm, wn, lane, Ln.wave, acc);
         }
     }
 }
@@ -459,7 +496,7 @@ gemm_tile_kernel(const GemmArgs args, const TileSchedule sched, const TileSplit 
 // ldq % 8 == 0 (checked on the host).
 template <uint32_t kFlags, bool kQ8 = false>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs args, const TileSplit split) {
-    const int64_t chunks_m = args.M / 8;
+    const int64_t chunks_m = (args.M + 7) / 8;
     const int64_t total = chunks_m * args.N;
     for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
         const int64_t n = idx / chunks_m;
@@ -486,16 +523,24 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs args,
             lo += *(const f32x4 *)(p + (int64_t)s * split.pstride);
             hi += *(const f32x4 *)(p + (int64_t)s * split.pstride + 4);
         }
+        // a chunk that straddles M, or any chunk when ldc % 8 != 0 or C is
+        // not 16-byte aligned (masked splits only), is read and written
+        // element by element; partials past M are zeros in the padding
+        const bool full = m + 8 <= args.M && (args.ldc & 7) == 0 && (reinterpret_cast<uintptr_t>(args.C) & 15) == 0;
         uint16_t *c = args.C + n * args.ldc + m;
         float bias_v = 0.f;
         if constexpr ((kFlags & kEpiBias) != 0) bias_v = bf16_bits_to_f32(args.bias[n]);
         float cin[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         if constexpr ((kFlags & kEpiBeta) != 0) {
-            const u32x4 raw = *(const u32x4 *)c;
+            if (full) {
+                const u32x4 raw = *(const u32x4 *)c;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                cin[2 * e] = bf16_bits_to_f32(raw[e] & 0xFFFFu);
-                cin[2 * e + 1] = bf16_bits_to_f32(raw[e] >> 16);
+                for (int e = 0; e < 4; ++e) {
+                    cin[2 * e] = bf16_bits_to_f32(raw[e] & 0xFFFFu);
+                    cin[2 * e + 1] = bf16_bits_to_f32(raw[e] >> 16);
+                }
+            } else {
+                for (int e = 0; e < 8 && m + e < args.M; ++e) cin[e] = bf16_bits_to_f32(c[e]);
             }
         }
         float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -503,7 +548,7 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs args,
         // in the fp8 tile kernel's own epilogue
         if (args.scale_a) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = x[e] * args.scale_a[m + e];
+            for (int e = 0; e < 8; ++e) x[e] = x[e] * (m + e < args.M ? args.scale_a[m + e] : 0.f);
         }
         if (args.scale_b) {
             const float sb = args.scale_b[n];
@@ -511,6 +556,7 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs args,
             for (int e = 0; e < 8; ++e) x[e] = x[e] * sb;
         }
         if constexpr (kQ8) {
+            // the quantizing reduction runs on exact tile multiples only
             const f32x4 s_lo = *(const f32x4 *)(args.scale + m);
             const f32x4 s_hi = *(const f32x4 *)(args.scale + m + 4);
             const float sc[8] = {s_lo.x, s_lo.y, s_lo.z, s_lo.w, s_hi.x, s_hi.y, s_hi.z, s_hi.w};
@@ -528,7 +574,11 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs args,
                 out[e] = pack_bf16x2(
                     epilogue_value<kFlags>(x[2 * e], cin[2 * e], bias_v, args.alpha, args.beta),
                     epilogue_value<kFlags>(x[2 * e + 1], cin[2 * e + 1], bias_v, args.alpha, args.beta));
-            __builtin_nontemporal_store(out, (u32x4 *)c);
+            if (full) {
+                __builtin_nontemporal_store(out, (u32x4 *)c);
+            } else {
+                for (int e = 0; e < 8 && m + e < args.M; ++e) c[e] = (uint16_t)(out[e >> 1] >> ((e & 1) * 16));
+            }
         }
     }
 }
@@ -536,11 +586,11 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs args,
 // Launch the tile kernel of configuration Cfg with the epilogue flags of
 // args baked in.  The grid is min(tiles, compute units): one persistent
 // workgroup per compute unit.
-template <class Cfg>
+template <class Cfg, bool kMasked = false>
 hipError_t launch_tile(const GemmArgs &args, int cus, hipStream_t stream) {
     TileSchedule s{};
-    s.tiles_m = (int)(args.M / Cfg::BM);
-    s.tiles_n = (int)(args.N / Cfg::BN);
+    s.tiles_m = (int)((args.M + Cfg::BM - 1) / Cfg::BM);
+    s.tiles_n = (int)((args.N + Cfg::BN - 1) / Cfg::BN);
     s.group_m = 4;
     s.order = kOrderGrouped;
     s.hilbert_log2 = 0;
@@ -549,7 +599,8 @@ hipError_t launch_tile(const GemmArgs &args, int cus, hipStream_t stream) {
     const dim3 grid(s.grid), block(Cfg::kThreads);
     const TileSplit none{};
     dispatch_flags(args.flags, [&](auto f) {
-        hipLaunchKernelGGL((gemm_tile_kernel<Cfg, decltype(f)::value>), grid, block, 0, stream, args, s, none);
+        hipLaunchKernelGGL((gemm_tile_kernel<Cfg, decltype(f)::value, false, kMasked>), grid, block, 0, stream, args,
+                           s, none);
     });
     return hipGetLastError();
 }
@@ -558,22 +609,24 @@ hipError_t launch_tile(const GemmArgs &args, int cus, hipStream_t stream) {
 // workspace split.P, then the reduction with the epilogue flags baked in
 // (kQ8: writing int8 Q).  The host has checked the tile-path requirements,
 // split.splits >= 2, every range non-empty, and that split.P holds
-// splits * M * N floats (ldp = M, pstride = M * N).
-template <class Cfg, bool kQ8 = false>
+// splits * pstride floats (ldp = M rounded up to BM, pstride = ldp times N
+// rounded up to BN; exact shapes: M and M * N).
+template <class Cfg, bool kQ8 = false, bool kMasked = false>
 hipError_t launch_tile_splitk(const GemmArgs &args, const TileSplit &split, int cus, hipStream_t stream) {
+    static_assert(!(kQ8 && kMasked), "the quantizing reduction runs on exact tile multiples");
     TileSchedule s{};
-    s.tiles_m = (int)(args.M / Cfg::BM);
-    s.tiles_n = (int)(args.N / Cfg::BN);
+    s.tiles_m = (int)((args.M + Cfg::BM - 1) / Cfg::BM);
+    s.tiles_n = (int)((args.N + Cfg::BN - 1) / Cfg::BN);
     s.group_m = 4;
     s.order = kOrderGrouped;
     s.hilbert_log2 = 0;
     const int units = s.num_tiles() * split.splits;
     s.grid = units < cus ? units : cus;
-    hipLaunchKernelGGL((gemm_tile_kernel<Cfg, 0u, true>), dim3(s.grid), dim3(Cfg::kThreads), 0, stream, args, s,
-                       split);
+    hipLaunchKernelGGL((gemm_tile_kernel<Cfg, 0u, true, kMasked>), dim3(s.grid), dim3(Cfg::kThreads), 0, stream, args,
+                       s, split);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const int64_t threads = args.M / 8 * args.N;
+    const int64_t threads = (args.M + 7) / 8 * args.N;
     const int64_t blocks = (threads + 255) / 256;
     const int64_t cap = (int64_t)cus * 8;
     const dim3 rgrid((unsigned)(blocks < cap ? blocks : cap));

@@ -22,7 +22,8 @@
  * workspace (fp32 partial sums, and counters for the short-product kernel)
  * used by three kinds of shape: 3 <= M <= 64 with few columns, products
  * whose 128x128 tiles would leave most compute units idle (for example
- * 1024 x 1024 x 4096), and FP8 products whose 256x256 tiles would.  It is one buffer per (device, stream), allocated
+ * 1024 x 1024 x 4096; with tails the partials are padded to whole tiles),
+ * and FP8 products whose 256x256 tiles would.  It is one buffer per (device, stream), allocated
  * with hipMalloc and its counters zeroed with hipMemsetAsync on the first
  * call that needs it, grown (after synchronising that stream) when a later
  * call needs more, and kept until the process ends; it holds at most about
@@ -87,9 +88,11 @@ enum gemm_bf16_status {
  * C <- epi(beta*C + bias) (the empty sum contributes nothing).
  *
  * Any alignment of the pointers (2-byte bf16 alignment) and any leading
- * dimensions are accepted.  16-byte aligned pointers with leading dimensions
- * that are multiples of 8 select the fast kernels; other inputs take a
- * bounds-checked path that computes the same result more slowly.
+ * dimensions are accepted.  The fast kernels need K, lda and ldb multiples
+ * of 8 and A, B 16-byte aligned (the large-grid ones also C aligned and
+ * ldc % 8 == 0; the 128x128 kernel for shapes with tails takes any C);
+ * other inputs take a bounds-checked path that computes the same result
+ * more slowly.
  *
  * Ownership: all buffers belong to the caller and must stay valid until the
  * enqueued work has completed.  A, B and bias must not overlap C.  The

@@ -172,7 +172,9 @@ def test_kernel_selection_names():
     assert name(1024, 1024, 1024, P, 1024, P, 1024, P, 1024) == "tile128x128x64_s4"
     assert name(512, 512, 512, P, 512, P, 512, P, 512) == "tile128x128x64_s4"   # 8 slices: no split
     assert name(2048, 2048, 4096, P, 4096, P, 4096, P, 2048) == "tile128x128x64_s4"  # 256 tiles
-    assert name(1000, 1000, 1000, P, 1000, P, 1000, P, 1000) == "generic64x64x32"
+    assert name(1000, 1000, 1000, P, 1000, P, 1000, P, 1000) == "tile128x128x64_s4_masked"
+    assert name(1000, 1000, 4096, P, 4096, P, 4096, P, 1000) == "splitk128x128x64_masked"
+    assert name(1000, 1000, 1004, P, 1004, P, 1004, P, 1000) == "generic64x64x32"   # K % 8 != 0
     assert name(64, 8192, 8192, P, 8192, P, 8192, P, 64) == "skinny"
     assert name(32, 4096, 1024, P, 1024, P, 1024, P, 32) == "skinny"
     assert name(48, 4096, 1024, P, 1024, P, 1024, P, 48) == "skinny"

@@ -207,7 +207,8 @@ def test_splitk_deterministic():
 # pipeline's prologue and tail cases (1 .. 10 slices, fewer and more slices
 # than LDS stages, odd and even counts).
 FORCEABLE = {"tile256x256x32_s5": 32, "tile128x128x64_s4": 64, "ring256x256x64": 64,
-             "ring256x256x64_mfma32": 64, "ring256x256x64_masked": 8, "generic64x64x32": 1}
+             "ring256x256x64_mfma32": 64, "ring256x256x64_masked": 8, "generic64x64x32": 1,
+             "tile128x128x64_s4_masked": 8}
 
 
 @pytest.mark.parametrize("kernel", list(FORCEABLE))
@@ -220,6 +221,52 @@ def test_forced_kernels_all_slice_counts(kernel, K, monkeypatch):
     monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", kernel)
     check_full(f"forced {kernel} K={K}", M, N, K, beta=0.5 if K % 64 else 0.0, use_bias=K == 96,
                seed=K + len(kernel), expect_kernel=kernel)
+
+
+# Tails on small and mid-sized grids: the masked 128x128 kernel (whole K)
+# and its split-K (whole tiles into a padded workspace; the reduction writes
+# a chunk that straddles M element by element).
+T128M = "tile128x128x64_s4_masked"
+SPLITKM = "splitk128x128x64_masked"
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc,kernel", [
+    (1000, 1000, 1000, 1000, 1000, 1000, T128M),   # 64 tiles, K tail in the last slice
+    (2000, 2000, 2000, 2000, 2000, 2000, T128M),   # 256 tiles
+    (1001, 999, 1000, 1008, 1000, 1008, T128M),    # M % 8 == 1, N tail, padded lda / ldc
+    (130, 70, 520, 520, 528, 136, T128M),          # one row / one column past a tile
+    (1000, 1000, 4096, 4096, 4096, 1000, SPLITKM),  # 64 tiles: split K
+    (1001, 520, 8200, 8200, 8208, 1008, SPLITKM),  # M % 8 == 1 in the reduction, K tail
+    (250, 130, 3000, 3000, 3000, 256, SPLITKM),    # 4 tiles, a K tail in the last range
+    (1500, 700, 1000, 1000, 1000, 1500, T128M),    # ldc % 8 != 0: element-wise C
+    (1001, 777, 4000, 4000, 4000, 1003, SPLITKM),  # ldc % 8 != 0 in the reduction
+])
+def test_masked_small_grid_shapes(M, N, K, lda, ldb, ldc, kernel):
+    check_full(f"masked small grid {M}x{N}x{K}", M, N, K, lda=lda, ldb=ldb, ldc=ldc, beta=0.5, use_bias=True,
+               epilogue="gelu_tanh", seed=M + N + K + 300, expect_kernel=kernel, poison_pad=True)
+
+
+@pytest.mark.parametrize("beta,use_bias,epi", [(b, u, e) for b in (0.0, -0.75) for u in (False, True)
+                                               for e in ("none", "gelu_tanh", "relu")])
+@pytest.mark.parametrize("M,N,K,ldc,kernel", [(999, 555, 320, 1000, T128M), (1000, 500, 4000, 1000, SPLITKM)])
+def test_masked_small_grid_epilogue_combinations(M, N, K, ldc, kernel, beta, use_bias, epi):
+    check_full(f"{kernel} beta={beta} bias={use_bias} {epi}", M, N, K, ldc=ldc, alpha=1.25, beta=beta,
+               use_bias=use_bias, epilogue=epi, seed=310 + int(abs(beta) * 4) + 2 * use_bias + len(epi),
+               expect_kernel=kernel)
+
+
+def test_masked_small_grid_unaligned_c():
+    check_full("masked medium unaligned C", 520, 300, 640, ldc=521, offsets=(0, 0, 3), beta=0.5, use_bias=True,
+               epilogue="relu", seed=340, expect_kernel=T128M)
+    check_full("masked splitk unaligned C", 520, 300, 4000, ldc=523, offsets=(0, 0, 5), beta=-0.5, use_bias=True,
+               epilogue="gelu_tanh", seed=341, expect_kernel=SPLITKM)
+
+
+@pytest.mark.parametrize("splits", [2, 3, 5])
+def test_masked_splitk_forced_split_counts(splits, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_SPLITK_SPLITS", str(splits))
+    check_full(f"masked splitk forced {splits}", 377, 250, 2000, ldc=384, beta=0.25, use_bias=True,
+               seed=330 + splits, expect_kernel=SPLITKM)
 
 
 # The tile kernels are compiled once per epilogue combination (beta, bias,
