@@ -53,6 +53,8 @@ hipError_t launch_tile_ring_q8_masked(const GemmArgs &args, int cus, hipStream_t
 hipError_t launch_tile_fp8(const GemmArgs &args, int cus, hipStream_t stream);
 // split-K on the FP8 tiles (split.P: splits * M * N floats of workspace)
 hipError_t launch_tile_fp8_splitk(const GemmArgs &args, const TileSplit &split, int cus, hipStream_t stream);
+hipError_t launch_tile_fp8_splitk_masked(const GemmArgs &args, const TileSplit &split, int cus,
+                                         hipStream_t stream);
 hipError_t launch_tile_fp8_masked(const GemmArgs &args, int cus, hipStream_t stream);
 // matrix-vector products: 1 <= M <= 4 (fp8: E4M3 operands)
 hipError_t launch_gemv(const GemmArgs &args, hipStream_t stream, bool fp8 = false);

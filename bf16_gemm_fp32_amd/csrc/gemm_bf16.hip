@@ -20,7 +20,7 @@
 namespace gb {
 
 enum KernelKind {
-    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8, kSplitK, kGemv, kSplitKQ8, kFp8Masked, kGemvFp8, kSkinnyFp8, kFp8SplitK, kRingQ8Masked, kSkinnyQ8, kMediumMasked, kSplitKMasked, kNumKinds
+    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8, kSplitK, kGemv, kSplitKQ8, kFp8Masked, kGemvFp8, kSkinnyFp8, kFp8SplitK, kRingQ8Masked, kSkinnyQ8, kMediumMasked, kSplitKMasked, kFp8SplitKMasked, kNumKinds
 };
 
 static const char *const kKindNames[kNumKinds] = {"none",            "tile256x256x32_s5", "tile128x128x64_s4",
@@ -32,7 +32,7 @@ static const char *const kKindNames[kNumKinds] = {"none",            "tile256x25
                                                   "gemv_fp8",          "skinny_fp8",
                                                   "splitk_fp8_256x256x128", "ring256x256x64_q8_masked",
                                                   "skinny_q8", "tile128x128x64_s4_masked",
-                                                  "splitk128x128x64_masked"};
+                                                  "splitk128x128x64_masked", "splitk_fp8_256x256x128_masked"};
 
 static const char *kind_name(int k) { return (k >= 0 && k < kNumKinds) ? kKindNames[k] : "none"; }
 
@@ -326,8 +326,12 @@ static bool splitk_pays(int64_t M, int64_t N, int64_t K) {
 static TileSplit plan_splitk_fp8(int64_t M, int64_t N, int64_t K, int cus) {
     TileSplit p{};
     p.splits = 1;
-    const int64_t tiles = (M / ShapeFp8::BM) * (N / ShapeFp8::BN);
-    const int64_t nk = K / ShapeFp8::BK;
+    // tiles and slices rounded up (shapes with tails run the masked kernel,
+    // whose partials are whole tiles in a padded workspace)
+    const int64_t mp = (M + ShapeFp8::BM - 1) / ShapeFp8::BM * ShapeFp8::BM;
+    const int64_t np = (N + ShapeFp8::BN - 1) / ShapeFp8::BN * ShapeFp8::BN;
+    const int64_t tiles = (mp / ShapeFp8::BM) * (np / ShapeFp8::BN);
+    const int64_t nk = (K + ShapeFp8::BK - 1) / ShapeFp8::BK;
     if (tiles <= 0 || tiles * 2 >= cus) return p;
     int64_t splits = cus / tiles;
     if (const char *env = std::getenv("GEMM_BF16_FP8_SPLITS")) {  // tuning knob
@@ -336,24 +340,24 @@ static TileSplit plan_splitk_fp8(int64_t M, int64_t N, int64_t K, int cus) {
     }
     if (splits > nk / 4) splits = nk / 4;
     if (splits > 8) splits = 8;
-    const int64_t cap = ((int64_t)4 << 20) / (M * N);
+    const int64_t cap = ((int64_t)4 << 20) / (mp * np);
     if (splits > cap) splits = cap;
     if (splits < 2) return p;
     p.kper = (int)((nk + splits - 1) / splits);
     p.splits = (int)((nk + p.kper - 1) / p.kper);  // no empty range
-    p.ldp = M;
-    p.pstride = M * N;
+    p.ldp = mp;
+    p.pstride = mp * np;
     return p;
 }
 
-static hipError_t launch_fp8_splitk_plan(const GemmArgs &args, int cus, hipStream_t stream) {
+static hipError_t launch_fp8_splitk_plan(const GemmArgs &args, int cus, hipStream_t stream, bool masked) {
     TileSplit p = plan_splitk_fp8(args.M, args.N, args.K, cus);
-    if (p.splits < 2) return launch_tile_fp8(args, cus, stream);
+    if (p.splits < 2) return masked ? launch_tile_fp8_masked(args, cus, stream) : launch_tile_fp8(args, cus, stream);
     uint32_t *unused = nullptr;
     std::lock_guard<std::mutex> lock(g_ws_mutex);
-    hipError_t err = get_workspace(stream, 0, (size_t)p.splits * (size_t)args.M * (size_t)args.N, &unused, &p.P);
+    hipError_t err = get_workspace(stream, 0, (size_t)p.splits * (size_t)p.pstride, &unused, &p.P);
     if (err != hipSuccess) return err;
-    return launch_tile_fp8_splitk(args, p, cus, stream);
+    return masked ? launch_tile_fp8_splitk_masked(args, p, cus, stream) : launch_tile_fp8_splitk(args, p, cus, stream);
 }
 
 // kQ8: the quantizing output (the host chose this path only when the plan
@@ -516,15 +520,19 @@ static int choose_kernel_fp8(int64_t M, int64_t N, int64_t K, const void *A, int
     if (okV && (M <= 2 || N * K < ((int64_t)1 << 26) || !okS)) return kGemvFp8;
     if (okS) return kSkinnyFp8;
     bool ok = K > 0 && K % 16 == 0;
-    ok = ok && lda % 16 == 0 && ldb % 16 == 0 && ldc % 8 == 0 && aligned16(A) && aligned16(B) && aligned16(C);
+    ok = ok && lda % 16 == 0 && ldb % 16 == 0 && aligned16(A) && aligned16(B);
     ok = ok && ShapeFp8::BM * lda + K + ShapeFp8::BK < lim && ShapeFp8::BN * ldb + K + ShapeFp8::BK < lim;
     ok = ok && ((M + 255) / 256) * ((N + 255) / 256) < lim;
     if (!ok) return kGeneric;
-    const bool exact = M % ShapeFp8::BM == 0 && N % ShapeFp8::BN == 0 && K % ShapeFp8::BK == 0;
+    // the unmasked instance stores C in 16-byte runs; the masked one takes any
+    // C (element by element where ldc % 8 != 0 or C is unaligned)
+    const bool exact = M % ShapeFp8::BM == 0 && N % ShapeFp8::BN == 0 && K % ShapeFp8::BK == 0 && ldc % 8 == 0 &&
+                       aligned16(C);
     if (force && !std::strcmp(force, kKindNames[kFp8Masked])) return kFp8Masked;
     if (force && !std::strcmp(force, kKindNames[kFp8])) return exact ? kFp8 : kFp8Masked;
-    // small grids of exact tiles: split K (the reduction needs C aligned, ldc % 8, M % 8: all implied)
-    if (exact && plan_splitk_fp8(M, N, K, device_cu_count()).splits >= 2) return kFp8SplitK;
+    // small grids: split K (the reduction needs C aligned and ldc % 8, both
+    // implied; it writes a chunk that straddles M element by element)
+    if (plan_splitk_fp8(M, N, K, device_cu_count()).splits >= 2) return exact ? kFp8SplitK : kFp8SplitKMasked;
     return exact ? kFp8 : kFp8Masked;
 }
 
@@ -663,7 +671,8 @@ int gemm_fp8(int64_t M, int64_t N, int64_t K, const gemm_fp8_t *A, int64_t lda, 
     hipError_t err = hipSuccess;
     switch (choose_kernel_fp8(M, N, K, A, lda, B, ldb, C, ldc)) {
     case kFp8: err = launch_tile_fp8(args, cus, stream); break;
-    case kFp8SplitK: err = launch_fp8_splitk_plan(args, cus, stream); break;
+    case kFp8SplitK: err = launch_fp8_splitk_plan(args, cus, stream, false); break;
+    case kFp8SplitKMasked: err = launch_fp8_splitk_plan(args, cus, stream, true); break;
     case kFp8Masked: err = launch_tile_fp8_masked(args, cus, stream); break;
     case kGemvFp8: err = launch_gemv(args, stream, true); break;
     case kSkinnyFp8: err = launch_skinny_plan(args, cus, stream, true); break;

@@ -30,7 +30,8 @@
 // from an out-of-range buffer offset, which the DMA turns into zeros (the
 // zero-fill of the DeepGEMM article, sections 4.2-4.3); the epilogue skips
 // columns past N and 8-row chunks past M and writes a chunk that straddles
-// M element by element.  K must be a multiple of 16.
+// M -- or every chunk, when ldc % 8 != 0 or C is unaligned -- element by
+// element.  K must be a multiple of 16.
 #pragma once
 
 #include "device_common.h"
@@ -199,6 +200,7 @@ __device__ __forceinline__ void fp8_epilogue(char *smem, const GemmArgs &args, i
     constexpr int kIters = 32 * kColChunks / 64;  // per lane per 32 columns
     static_assert(64 % kColChunks == 0, "a lane's row chunk is the same in every iteration");
     const int h = lane >> 5;
+    const bool cvec = !kMasked || ((args.ldc & 7) == 0 && (reinterpret_cast<uintptr_t>(args.C) & 15) == 0);
     const int64_t mrow = m0 + wm * Cfg::WTM + (lane % kColChunks) * 8;
     float sa[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
     if (args.scale_a) {
@@ -226,7 +228,7 @@ __device__ __forceinline__ void fp8_epilogue(char *smem, const GemmArgs &args, i
             const int64_t n = n0 + wn * Cfg::WTN + j * 32 + col;
             const int64_t m = m0 + wm * Cfg::WTM + q * 8;
             if (kMasked && (n >= args.N || m >= args.M)) continue;
-            const bool full = !kMasked || m + 8 <= args.M;
+            const bool full = !kMasked || (m + 8 <= args.M && cvec);
             uint16_t *p = args.C + n * args.ldc + m;
             const float sb = args.scale_b ? args.scale_b[n] : 1.f;
             float bias_v = 0.f;
@@ -265,14 +267,15 @@ __device__ __forceinline__ void fp8_epilogue(char *smem, const GemmArgs &args, i
 // N % 256 == 0, K % 128 == 0 (masked: any M, N >= 1 and K % 16 == 0),
 // K > 0, A/B/C 16-byte aligned, lda/ldb multiples of 16, ldc a multiple of
 // 8, and 256*lda + K + 128, 256*ldb + K + 128 (bytes) below 2^31.
-// kSplit (unmasked only): the units are (K range, tile) pairs -- unit u =
-// s * tiles + t covers slices s * kper .. of tile t -- and each stores its
-// unscaled fp32 partial to split.P; splitk_reduce_kernel then adds them in
-// range order and applies the scales and the epilogue (kFlags is unused).
+// kSplit: the units are (K range, tile) pairs -- unit u = s * tiles + t
+// covers slices s * kper .. of tile t -- and each stores its unscaled fp32
+// partial tile to split.P (padded to tile multiples when masked: rows and
+// columns past the matrix hold zeros); splitk_reduce_kernel then adds them
+// in range order and applies the scales and the epilogue (kFlags is
+// unused).
 template <uint32_t kFlags, bool kMasked, bool kSplit = false>
 __global__ void __launch_bounds__(Fp8Config::kThreads)
 gemm_fp8_kernel(const GemmArgs args, const TileSchedule sched, const TileSplit split) {
-    static_assert(!(kSplit && kMasked), "split-K runs on exact tile multiples");
     using Cfg = Fp8Config;
     using RK = Fp8Kernel<kMasked>;
     __shared__ __attribute__((aligned(1024))) char smem[Cfg::kLdsBytes];
@@ -330,6 +333,7 @@ gemm_fp8_kernel(const GemmArgs args, const TileSchedule sched, const TileSplit s
         // the unit's K range starts k0 bytes into every row (one byte per value)
         const int64_t k0 = kSplit ? (int64_t)sp * split.kper * Cfg::BK : 0;
         const int64_t kn = kSplit ? (int64_t)nk * Cfg::BK : args.K;
+        if constexpr (kSplit && kMasked) Ln.kmax = (int)(args.K - k0);  // the unit's K
         if constexpr (kMasked) {
             Ln.rowsA = (int)(args.M - m0 < Cfg::BM ? args.M - m0 : Cfg::BM);
             Ln.rowsB = (int)(args.N - n0 < Cfg::BN ? args.N - n0 : Cfg::BN);
@@ -425,23 +429,25 @@ hipError_t launch_fp8_ring(const GemmArgs &args, int cus, hipStream_t stream) {
 
 // Split-K on small grids: the tile kernel over (range, tile) units into the
 // workspace split.P, then the reduction (which applies the scales and the
-// epilogue).  The host has checked the exact-tile requirements, M % 8 == 0,
-// split.splits >= 2, every range non-empty, and that split.P holds
-// splits * M * N floats (ldp = M, pstride = M * N).
-inline hipError_t launch_fp8_splitk(const GemmArgs &args, const TileSplit &split, int cus, hipStream_t stream) {
+// epilogue).  The host has checked the tile requirements (exact multiples,
+// or the masked ones), split.splits >= 2, every range non-empty, and that
+// split.P holds splits * pstride floats (ldp = M rounded up to 256, pstride
+// = ldp times N rounded up to 256).
+template <bool kMasked>
+hipError_t launch_fp8_splitk(const GemmArgs &args, const TileSplit &split, int cus, hipStream_t stream) {
     TileSchedule s{};
-    s.tiles_m = (int)(args.M / Fp8Config::BM);
-    s.tiles_n = (int)(args.N / Fp8Config::BN);
+    s.tiles_m = (int)((args.M + Fp8Config::BM - 1) / Fp8Config::BM);
+    s.tiles_n = (int)((args.N + Fp8Config::BN - 1) / Fp8Config::BN);
     s.group_m = 4;
     s.order = kOrderGrouped;
     s.hilbert_log2 = 0;
     const int units = s.num_tiles() * split.splits;
     s.grid = units < cus ? units : cus;
-    hipLaunchKernelGGL((gemm_fp8_kernel<0u, false, true>), dim3(s.grid), dim3(Fp8Config::kThreads), 0, stream, args,
-                       s, split);
+    hipLaunchKernelGGL((gemm_fp8_kernel<0u, kMasked, true>), dim3(s.grid), dim3(Fp8Config::kThreads), 0, stream,
+                       args, s, split);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const int64_t threads = args.M / 8 * args.N;
+    const int64_t threads = (args.M + 7) / 8 * args.N;
     const int64_t blocks = (threads + 255) / 256;
     const int64_t cap = (int64_t)cus * 8;
     const dim3 rgrid((unsigned)(blocks < cap ? blocks : cap));

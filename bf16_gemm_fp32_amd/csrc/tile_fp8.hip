@@ -12,7 +12,7 @@ hipError_t launch_tile_fp8(const GemmArgs &args, int cus, hipStream_t stream) {
 }
 
 hipError_t launch_tile_fp8_splitk(const GemmArgs &args, const TileSplit &split, int cus, hipStream_t stream) {
-    return launch_fp8_splitk(args, split, cus, stream);
+    return launch_fp8_splitk<false>(args, split, cus, stream);
 }
 
 }  // namespace gb

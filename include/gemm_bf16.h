@@ -172,10 +172,11 @@ int gemm_bf16_q8(int64_t M, int64_t N, int64_t K,
  * 16 and A, B 16-byte aligned: 1 <= M <= 2 (and 3 <= M <= 4 when
  * N * K < 2^26) takes a matrix-vector kernel and the other M <= 64 a
  * streaming FP8 MFMA kernel (any ldc); larger M the
- * 256x256 FP8 MFMA kernel when C is 16-byte aligned and ldc a multiple of 8
- * (any M and N; tails are masked).  When those tiles are exact multiples
- * and would fill less than half of the compute units, K is split over up to
- * eight ranges (fp32 partials in the split-K workspace, at most 16 MiB,
+ * 256x256 FP8 MFMA kernel (any M and N: tails are masked; exact tile
+ * multiples with C 16-byte aligned and ldc % 8 == 0 run unmasked, anything
+ * else accesses C element by element where it must).  When those tiles
+ * would fill less than half of the compute units, K is split over up to
+ * eight ranges (fp32 partial tiles in the split-K workspace, at most 16 MiB,
  * then an ordered reduction that applies the scales and the epilogue).
  * Other inputs take the bounds-checked path (same result).
  */

@@ -106,7 +106,8 @@ def test_fp8_argument_errors_and_names():
     assert name(4000, 4096, 4096, P, 4096, P, 4096, P, 4000) == "fp8_256x256x128_masked"
     assert name(4096, 4096, 4040, P, 4048, P, 4048, P, 4096) == "generic64x64x32"   # K % 16 != 0
     assert name(4096, 4096, 4096, P + 8, 4096, P, 4096, P, 4096) == "generic64x64x32"  # unaligned A
-    assert name(4000, 4096, 4096, P, 4096, P, 4096, P, 4004) == "generic64x64x32"      # ldc % 8 != 0
+    assert name(4000, 4096, 4096, P, 4096, P, 4096, P, 4004) == "fp8_256x256x128_masked"  # ldc % 8 != 0: element-wise C
+    assert name(4096, 4096, 4096, P, 4096, P, 4096, P, 4100) == "fp8_256x256x128_masked"  # exact tiles, odd ldc
     # one to four rows: the matrix-vector kernel (any ldc)
     assert name(1, 4096, 4096, P, 4096, P, 4096, P, 1) == "gemv_fp8"
     assert name(2, 8192, 8192, P, 8192, P, 8192, P, 2) == "gemv_fp8"
@@ -116,12 +117,14 @@ def test_fp8_argument_errors_and_names():
     assert name(1024, 1024, 4096, P, 4096, P, 4096, P, 1024) == "splitk_fp8_256x256x128"
     assert name(512, 512, 8192, P, 8192, P, 8192, P, 512) == "splitk_fp8_256x256x128"
     assert name(1024, 1024, 384, P, 384, P, 384, P, 1024) == "fp8_256x256x128"     # 3 slices
+    assert name(1000, 1000, 4096, P, 4096, P, 4096, P, 1000) == "splitk_fp8_256x256x128_masked"
+    assert name(1000, 1000, 208, P, 208, P, 208, P, 1000) == "fp8_256x256x128_masked"
     assert name(2048, 4096, 4096, P, 4096, P, 4096, P, 2048) == "fp8_256x256x128"  # 128 tiles
     assert name(2048, 2048, 4096, P, 4096, P, 4096, P, 2048) == "fp8_256x256x128"  # 4M outputs: partials capped
     assert name(4, 4096, 4096, P, 4096, P, 4096, P + 2, 5) == "gemv_fp8"
     assert name(5, 4096, 4096, P, 4096, P, 4096, P, 8) == "skinny_fp8"
     assert name(64, 8192, 8192, P, 8192, P, 8192, P, 64) == "skinny_fp8"
-    assert name(65, 4096, 4096, P, 4096, P, 4096, P, 72) == "fp8_256x256x128_masked"
+    assert name(65, 4096, 4096, P, 4096, P, 4096, P, 72) == "splitk_fp8_256x256x128_masked"  # 16 tiles: split
     assert name(1, 4096, 4040, P, 4048, P, 4048, P, 1) == "generic64x64x32"          # K % 16 != 0
 
 

@@ -791,17 +791,50 @@ def test_fp8_splitk_deterministic():
 FP8M = "fp8_256x256x128_masked"
 
 
+def test_fp8_masked_odd_ldc():
+    check_fp8("fp8 masked odd ldc", 1001, 777, 208, lda=224, ldb=208, ldc=1003, beta=0.5, use_bias=True,
+              epilogue="relu", seed=420, expect_kernel=FP8M)
+    check_fp8("fp8 masked unaligned C", 512, 512, 256, ldc=520, offsets=(0, 0, 3), beta=-0.5, seed=421,
+              expect_kernel=FP8M)
+
+
 @pytest.mark.parametrize("M,N,K,lda,ldb,ldc", [
     (300, 260, 144, 144, 144, 304),      # one full slice and a 16-wide K chunk
     (257, 513, 16, 32, 48, 264),         # a single 16-wide K chunk, 1-row / 1-column tails
     (1001, 777, 208, 224, 208, 1008),    # M % 8 == 1: the last 8-row chunk straddles M
     (255, 1, 128, 128, 144, 256),        # N = 1
     (65, 255, 64, 64, 64, 72),           # M = 65 (up to 64 rows take the streaming kernels)
-    (520, 264, 4048, 4064, 4048, 528),   # 31 full slices and a 80-wide K tail
+    (520, 264, 4048, 4064, 4048, 528),   # 31 full slices and a 80-wide K tail (forced unsplit)
 ])
-def test_fp8_masked_tails(M, N, K, lda, ldb, ldc):
+def test_fp8_masked_tails(M, N, K, lda, ldb, ldc, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", FP8M)
     check_fp8(f"fp8 masked {M}x{N}x{K}", M, N, K, lda=lda, ldb=ldb, ldc=ldc, seed=M + N + K + 11,
               expect_kernel=FP8M)
+
+
+# Split-K on the masked FP8 kernel (tails on small grids): whole tiles into a
+# padded workspace, K tails in the last range, M % 8 != 0 in the reduction.
+FP8SM = "splitk_fp8_256x256x128_masked"
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc", [
+    (520, 264, 4048, 4064, 4048, 528),   # 6 tiles, 32 slices: 8 ranges, an 80-wide K tail
+    (1001, 777, 4000, 4000, 4016, 1008), # M % 8 == 1, N tail
+    (300, 260, 2064, 2064, 2064, 304),   # 4 tiles, 17 slices: 4 ranges, a 16-wide K tail
+    (1001, 777, 4000, 4000, 4000, 1001), # ldc % 8 != 0: element-wise C in the reduction
+])
+def test_fp8_masked_splitk_shapes(M, N, K, lda, ldb, ldc):
+    check_fp8(f"fp8 masked splitk {M}x{N}x{K}", M, N, K, lda=lda, ldb=ldb, ldc=ldc, beta=0.5, use_bias=True,
+              epilogue="gelu_tanh", seed=M + N + K + 400, expect_kernel=FP8SM)
+
+
+@pytest.mark.parametrize("beta,use_bias,epi,scales", [(b, u, e, sc) for b in (0.0, -0.75) for u in (False, True)
+                                                      for e in ("none", "gelu_tanh", "relu") for sc in (True, False)
+                                                      if not (u and not sc and e == "relu")])
+def test_fp8_masked_splitk_epilogue_combinations(beta, use_bias, epi, scales):
+    check_fp8(f"fp8 masked splitk beta={beta} bias={use_bias} {epi} scales={scales}", 777, 300, 2000, ldc=784,
+              alpha=1.25, beta=beta, use_bias=use_bias, epilogue=epi, scales=scales,
+              seed=410 + int(abs(beta) * 4) + 2 * use_bias + len(epi) + 7 * scales, expect_kernel=FP8SM)
 
 
 @pytest.mark.parametrize("beta,use_bias,epi", [(b, u, e) for b in (0.0, -0.75) for u in (False, True)
