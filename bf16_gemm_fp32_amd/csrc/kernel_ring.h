@@ -221,8 +221,9 @@ struct RingEpiInputs {
 };
 
 // Rows m .. m+7 of column n of C: full when m + 8 <= M; with masking, a
-// chunk that straddles M is read and written element by element, and
-// chunks past M or columns past N are skipped.
+// chunk that straddles M -- or every chunk, when ldc % 8 != 0 or C is not
+// 16-byte aligned -- is read and written element by element, and chunks
+// past M or columns past N are skipped.
 template <uint32_t kFlags, bool kMasked>
 __device__ __forceinline__ void ring_epi_load(RingEpiInputs &in, const GemmArgs &args, int64_t m0, int64_t n0,
                                               int wm, int wn, int lane, int jj) {
@@ -242,7 +243,8 @@ __device__ __forceinline__ void ring_epi_load(RingEpiInputs &in, const GemmArgs 
             if constexpr ((kFlags & kEpiBias) != 0) in.b[t] = args.bias[n];
             if constexpr ((kFlags & kEpiBeta) != 0) {
                 const uint16_t *p = args.C + n * args.ldc + m;
-                if (m + 8 <= args.M) {
+                const bool cvec = (args.ldc & 7) == 0 && (reinterpret_cast<uintptr_t>(args.C) & 15) == 0;
+                if (m + 8 <= args.M && cvec) {
                     in.c[t] = *(const u32x4 *)p;
                 } else if (m < args.M) {
                     uint32_t w[4] = {0u, 0u, 0u, 0u};
@@ -338,7 +340,7 @@ __device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, 
             uint16_t *p = args.C + n * args.ldc + m;
             if constexpr (kMasked) {
                 if (n < args.N) {
-                    if (m + 8 <= args.M) {
+                    if (m + 8 <= args.M && (args.ldc & 7) == 0 && (reinterpret_cast<uintptr_t>(args.C) & 15) == 0) {
                         __builtin_nontemporal_store(out, (u32x4 *)p);
                     } else {
                         for (int e = 0; e < 8 && m + e < args.M; ++e)
@@ -354,8 +356,9 @@ __device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, 
 }
 
 // Requirements checked by the host before launch: M % 256 == 0,
-// N % 256 == 0, K % 64 == 0 (masked: any M, N >= 1 and K % 8 == 0), K > 0,
-// A/B/C 16-byte aligned, lda/ldb/ldc multiples of 8, and 256*lda*2 + 2K,
+// N % 256 == 0, K % 64 == 0 (masked: any M, N >= 1 and K % 8 == 0, any C
+// alignment and ldc), K > 0, A/B (and unmasked C) 16-byte aligned,
+// lda/ldb (and unmasked ldc) multiples of 8, and 256*lda*2 + 2K,
 // 256*ldb*2 + 2K below 2^31; for kQ8 also Q and scale 16-byte aligned and
 // ldq a multiple of 8.
 template <uint32_t kFlags, bool kMasked, bool kQ8>

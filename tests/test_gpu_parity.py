@@ -316,6 +316,18 @@ def test_masked_ring_epilogue_combinations(beta, use_bias, epi, monkeypatch):
                expect_kernel=MASKED, poison_pad=True)
 
 
+def test_masked_ring_any_ldc_and_c_alignment():
+    check_full("masked ring odd ldc", 4000, 2000, 320, ldc=4001, beta=0.5, use_bias=True, epilogue="gelu_tanh",
+               seed=350, expect_kernel="ring256x256x64_masked")
+    check_full("masked ring unaligned C", 4096, 2304, 256, ldc=4104, offsets=(0, 0, 3), beta=-0.5, seed=351,
+               expect_kernel="ring256x256x64_masked")
+
+
+def test_q8_exact_ring_unaligned_c0_takes_the_masked_instance():
+    check_q8("q8 ring unaligned C0", 4096, 2048, 192, ldc=4100, beta=0.5, use_bias=True, epilogue="relu", zp=2,
+             seed=352, expect_kernel="ring256x256x64_q8_masked")
+
+
 def test_masked_ring_is_the_default_for_large_ragged_shapes():
     check_full("ragged default", 4000, 2000, 1000, beta=0.5, use_bias=True, epilogue="gelu_tanh", seed=51,
                expect_kernel=MASKED)
