@@ -50,12 +50,16 @@ hipError_t launch_tile_ring_masked(const GemmArgs &args, int cus, hipStream_t st
 // int8 output: exact tile multiples, and shapes with tails (masked)
 hipError_t launch_tile_ring_q8(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_ring_q8_masked(const GemmArgs &args, int cus, hipStream_t stream);
+// FP8 tiles on 16x16x128 MFMAs: exact multiples, and shapes with tails
 hipError_t launch_tile_fp8(const GemmArgs &args, int cus, hipStream_t stream);
-// split-K on the FP8 tiles (split.P: splits * M * N floats of workspace)
+hipError_t launch_tile_fp8_masked(const GemmArgs &args, int cus, hipStream_t stream);
+// the same tiles on 32x32x64 MFMAs (chosen only when forced)
+hipError_t launch_tile_fp8_mfma32(const GemmArgs &args, int cus, hipStream_t stream);
+hipError_t launch_tile_fp8_mfma32_masked(const GemmArgs &args, int cus, hipStream_t stream);
+// split-K on the 32x32x64 FP8 tiles (split.P: splits * M * N floats of workspace)
 hipError_t launch_tile_fp8_splitk(const GemmArgs &args, const TileSplit &split, int cus, hipStream_t stream);
 hipError_t launch_tile_fp8_splitk_masked(const GemmArgs &args, const TileSplit &split, int cus,
                                          hipStream_t stream);
-hipError_t launch_tile_fp8_masked(const GemmArgs &args, int cus, hipStream_t stream);
 // matrix-vector products: 1 <= M <= 4 (fp8: E4M3 operands)
 hipError_t launch_gemv(const GemmArgs &args, hipStream_t stream, bool fp8 = false);
 // rows: 32 or 64 (the kernel's row block, M <= rows); cols: strip width

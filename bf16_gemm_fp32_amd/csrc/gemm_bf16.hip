@@ -20,19 +20,20 @@
 namespace gb {
 
 enum KernelKind {
-    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8, kSplitK, kGemv, kSplitKQ8, kFp8Masked, kGemvFp8, kSkinnyFp8, kFp8SplitK, kRingQ8Masked, kSkinnyQ8, kMediumMasked, kSplitKMasked, kFp8SplitKMasked, kNumKinds
+    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8Mfma32, kSplitK, kGemv, kSplitKQ8, kFp8Mfma32Masked, kGemvFp8, kSkinnyFp8, kFp8SplitK, kRingQ8Masked, kSkinnyQ8, kMediumMasked, kSplitKMasked, kFp8SplitKMasked, kFp8, kFp8Masked, kNumKinds
 };
 
 static const char *const kKindNames[kNumKinds] = {"none",            "tile256x256x32_s5", "tile128x128x64_s4",
                                                   "skinny",          "generic64x64x32",
                                                   "ring256x256x64_mfma32", "ring256x256x64",
                                                   "ring256x256x64_masked", "ring256x256x64_q8",
-                                                  "fp8_256x256x128",  "splitk128x128x64", "gemv",
-                                                  "splitk128x128x64_q8", "fp8_256x256x128_masked",
+                                                  "fp8_256x256x128_mfma32", "splitk128x128x64", "gemv",
+                                                  "splitk128x128x64_q8", "fp8_256x256x128_mfma32_masked",
                                                   "gemv_fp8",          "skinny_fp8",
                                                   "splitk_fp8_256x256x128", "ring256x256x64_q8_masked",
                                                   "skinny_q8", "tile128x128x64_s4_masked",
-                                                  "splitk128x128x64_masked", "splitk_fp8_256x256x128_masked"};
+                                                  "splitk128x128x64_masked", "splitk_fp8_256x256x128_masked",
+                                                  "fp8_256x256x128", "fp8_256x256x128_masked"};
 
 static const char *kind_name(int k) { return (k >= 0 && k < kNumKinds) ? kKindNames[k] : "none"; }
 
@@ -326,6 +327,18 @@ static bool splitk_pays(int64_t M, int64_t N, int64_t K) {
 // tile): when the 256x256 tiles fill less than half of the compute units,
 // up to CUs / tiles ranges of at least 4 slices of 128, at most 8, and at
 // most 4M floats of partials (16 MiB).  Returns 1 when no split applies.
+// Whether splitting K over the 256x256 FP8 tiles beats the unsplit kernel:
+// measured on gfx950, the split (tile kernel, then the reduction) wins from
+// about 15 slices of 128 at 8 tiles, 24 at 16 tiles and 33 at 32 tiles
+// (16 tiles: 16 slices unsplit 23.1 us against 28.0 split, 32 slices 37.6
+// against 31.7; 32 tiles: 24 slices 30.8 against 35.5, 40 slices 46.5
+// against 40.1).
+static bool fp8_splitk_pays(int64_t M, int64_t N, int64_t K) {
+    const int64_t tiles = ((M + ShapeFp8::BM - 1) / ShapeFp8::BM) * ((N + ShapeFp8::BN - 1) / ShapeFp8::BN);
+    const int64_t nk = (K + ShapeFp8::BK - 1) / ShapeFp8::BK;
+    return 8 * nk >= 88 + 5 * tiles;
+}
+
 static TileSplit plan_splitk_fp8(int64_t M, int64_t N, int64_t K, int cus) {
     TileSplit p{};
     p.splits = 1;
@@ -535,9 +548,15 @@ static int choose_kernel_fp8(int64_t M, int64_t N, int64_t K, const void *A, int
                        aligned16(C);
     if (force && !std::strcmp(force, kKindNames[kFp8Masked])) return kFp8Masked;
     if (force && !std::strcmp(force, kKindNames[kFp8])) return exact ? kFp8 : kFp8Masked;
+    if (force && !std::strcmp(force, kKindNames[kFp8Mfma32Masked])) return kFp8Mfma32Masked;
+    if (force && !std::strcmp(force, kKindNames[kFp8Mfma32])) return exact ? kFp8Mfma32 : kFp8Mfma32Masked;
     // small grids: split K (the reduction needs C aligned and ldc % 8, both
     // implied; it writes a chunk that straddles M element by element)
-    if (plan_splitk_fp8(M, N, K, device_cu_count()).splits >= 2) return exact ? kFp8SplitK : kFp8SplitKMasked;
+    const bool can_split = plan_splitk_fp8(M, N, K, device_cu_count()).splits >= 2;
+    if (force && can_split &&
+        (!std::strcmp(force, kKindNames[kFp8SplitK]) || !std::strcmp(force, kKindNames[kFp8SplitKMasked])))
+        return exact ? kFp8SplitK : kFp8SplitKMasked;
+    if (can_split && fp8_splitk_pays(M, N, K)) return exact ? kFp8SplitK : kFp8SplitKMasked;
     return exact ? kFp8 : kFp8Masked;
 }
 
@@ -679,6 +698,8 @@ int gemm_fp8(int64_t M, int64_t N, int64_t K, const gemm_fp8_t *A, int64_t lda, 
     case kFp8SplitK: err = launch_fp8_splitk_plan(args, cus, stream, false); break;
     case kFp8SplitKMasked: err = launch_fp8_splitk_plan(args, cus, stream, true); break;
     case kFp8Masked: err = launch_tile_fp8_masked(args, cus, stream); break;
+    case kFp8Mfma32: err = launch_tile_fp8_mfma32(args, cus, stream); break;
+    case kFp8Mfma32Masked: err = launch_tile_fp8_mfma32_masked(args, cus, stream); break;
     case kGemvFp8: err = launch_gemv(args, stream, true); break;
     case kSkinnyFp8: err = launch_skinny_plan(args, cus, stream, true); break;
     default: err = launch_generic(args, cus, stream, true); break;

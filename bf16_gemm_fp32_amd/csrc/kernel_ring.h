@@ -218,13 +218,14 @@ struct RingKernel {
 struct RingEpiInputs {
     u32x4 c[8];    // C (beta != 0): 8 consecutive rows of one column per iteration
     uint32_t b[8]; // bias bits (bias != NULL), one column per iteration
+    float s[8];    // kScaled: the column's scale_b[n] (1 without scale_b)
 };
 
 // Rows m .. m+7 of column n of C: full when m + 8 <= M; with masking, a
 // chunk that straddles M -- or every chunk, when ldc % 8 != 0 or C is not
 // 16-byte aligned -- is read and written element by element, and chunks
-// past M or columns past N are skipped.
-template <uint32_t kFlags, bool kMasked>
+// past M or columns past N are skipped.  kScaled: also the column scales.
+template <uint32_t kFlags, bool kMasked, bool kScaled = false>
 __device__ __forceinline__ void ring_epi_load(RingEpiInputs &in, const GemmArgs &args, int64_t m0, int64_t n0,
                                               int wm, int wn, int lane, int jj) {
     using Cfg = RingConfig;
@@ -236,6 +237,7 @@ __device__ __forceinline__ void ring_epi_load(RingEpiInputs &in, const GemmArgs 
         const int q = idx % kColChunks;
         const int64_t n = n0 + wn * Cfg::WTN + jj * 32 + col;
         const int64_t m = m0 + wm * Cfg::WTM + q * 8;
+        if constexpr (kScaled) in.s[t] = (args.scale_b && (!kMasked || n < args.N)) ? args.scale_b[n] : 1.f;
         if constexpr (kMasked) {
             in.c[t] = u32x4{0u, 0u, 0u, 0u};
             in.b[t] = 0u;
@@ -262,7 +264,10 @@ __device__ __forceinline__ void ring_epi_load(RingEpiInputs &in, const GemmArgs 
 // kQ8: the quantizing output -- each value becomes one int8 byte of Q,
 // sat8(rne(v * scale[m] + zp)); a lane's 8 rows are fixed for the whole tile
 // (its 8-row chunk is lane % 16), so their scales are loaded once.
-template <uint32_t kFlags, bool kMasked, bool kQ8>
+// kScaled: the FP8 input scales -- the product is acc * scale_a[m] *
+// scale_b[n] (a missing scale is 1) before alpha, beta*C, bias and the
+// activation; the row scales likewise load once per tile.
+template <uint32_t kFlags, bool kMasked, bool kQ8, bool kScaled = false>
 __device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, int64_t m0, int64_t n0, int wm,
                                               int wn, int lane, int wave,
                                               const f32x4 (&acc)[RingConfig::FM][RingConfig::FN],
@@ -286,10 +291,20 @@ __device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, 
             for (int e = 0; e < 8 && m + e < args.M; ++e) sc[e] = args.scale[m + e];
         }
     }
+    float sa[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+    if constexpr (kScaled) {
+        const int64_t m = m0 + wm * Cfg::WTM + (lane % kColChunks) * 8;
+        if (args.scale_a) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (!kMasked || m + e < args.M) sa[e] = args.scale_a[m + e];
+        }
+    }
 #pragma unroll
     for (int jj = 0; jj < Cfg::FN / 2; ++jj) {
         RingEpiInputs next;
-        if (jj + 1 < Cfg::FN / 2) ring_epi_load<kFlags, kMasked>(next, args, m0, n0, wm, wn, lane, jj + 1);
+        if (jj + 1 < Cfg::FN / 2)
+            ring_epi_load<kFlags, kMasked, kScaled>(next, args, m0, n0, wm, wn, lane, jj + 1);
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
@@ -315,7 +330,11 @@ __device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, 
                     cin[2 * e + 1] = bf16_bits_to_f32(in.c[t][e] >> 16);
                 }
             }
-            const float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            if constexpr (kScaled) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = x[e] * sa[e] * in.s[t];
+            }
             if constexpr (kQ8) {
                 u32x2 qw = {0u, 0u};
 #pragma unroll

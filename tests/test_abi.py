@@ -125,7 +125,25 @@ def test_fp8_argument_errors_and_names():
     assert name(5, 4096, 4096, P, 4096, P, 4096, P, 8) == "skinny_fp8"
     assert name(64, 8192, 8192, P, 8192, P, 8192, P, 64) == "skinny_fp8"
     assert name(65, 4096, 4096, P, 4096, P, 4096, P, 72) == "splitk_fp8_256x256x128_masked"  # 16 tiles: split
+    # the split must pay for its reduction: few slices on 16 or more tiles run unsplit
+    assert name(1024, 1024, 2048, P, 2048, P, 2048, P, 1024) == "fp8_256x256x128"      # 16 tiles, 16 slices
+    assert name(1024, 1024, 3072, P, 3072, P, 3072, P, 1024) == "splitk_fp8_256x256x128"  # 16 tiles, 24 slices
+    assert name(2048, 1024, 3072, P, 3072, P, 3072, P, 2048) == "fp8_256x256x128"      # 32 tiles, 24 slices
+    assert name(2048, 1024, 4096, P, 4096, P, 4096, P, 2048) == "splitk_fp8_256x256x128"  # 32 tiles, 32 slices
+    assert name(512, 512, 2048, P, 2048, P, 2048, P, 512) == "splitk_fp8_256x256x128"  # 4 tiles, 16 slices
     assert name(1, 4096, 4040, P, 4048, P, 4048, P, 1) == "generic64x64x32"          # K % 16 != 0
+
+
+def test_fp8_forced_mfma32_names(monkeypatch):
+    # the 32x32x64 FP8 tiles run only when forced (their split mode serves split-K)
+    name = gb.gemm_fp8_kernel_name
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", "fp8_256x256x128_mfma32")
+    assert name(4096, 4096, 4096, P, 4096, P, 4096, P, 4096) == "fp8_256x256x128_mfma32"
+    assert name(4000, 4096, 4096, P, 4096, P, 4096, P, 4000) == "fp8_256x256x128_mfma32_masked"
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", "fp8_256x256x128_mfma32_masked")
+    assert name(4096, 4096, 4096, P, 4096, P, 4096, P, 4096) == "fp8_256x256x128_mfma32_masked"
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", "fp8_256x256x128")
+    assert name(1024, 1024, 4096, P, 4096, P, 4096, P, 1024) == "fp8_256x256x128"  # unsplit when forced
 
 
 def test_relu_is_accepted():

@@ -752,7 +752,7 @@ FP8S = "splitk_fp8_256x256x128"
     (1024, 1024, 4096),   # 16 tiles, 32 slices: 4 ranges
     (512, 512, 8192),     # 4 tiles, 64 slices: 8 ranges
     (256, 768, 1664),     # 3 tiles, 13 slices: ranges of 5, 5, 3
-    (512, 256, 1024),     # 2 tiles, 8 slices: 2 ranges
+    (512, 256, 2048),     # 2 tiles, 16 slices: 4 ranges
 ])
 def test_fp8_splitk_shapes(M, N, K):
     check_fp8(f"fp8 splitk {M}x{N}x{K}", M, N, K, beta=0.5, use_bias=True, epilogue="gelu_tanh",
@@ -763,7 +763,7 @@ def test_fp8_splitk_shapes(M, N, K):
                                                       for e in ("none", "gelu_tanh", "relu") for sc in (True, False)
                                                       if not (u and not sc and e == "relu")])
 def test_fp8_splitk_epilogue_combinations(beta, use_bias, epi, scales):
-    check_fp8(f"fp8 splitk beta={beta} bias={use_bias} {epi} scales={scales}", 512, 256, 1024, alpha=1.25,
+    check_fp8(f"fp8 splitk beta={beta} bias={use_bias} {epi} scales={scales}", 512, 256, 2048, alpha=1.25,
               beta=beta, use_bias=use_bias, epilogue=epi, scales=scales,
               seed=100 + int(abs(beta) * 4) + 2 * use_bias + len(epi) + 7 * scales, expect_kernel=FP8S)
 
@@ -795,6 +795,60 @@ def test_fp8_splitk_deterministic():
         torch.cuda.synchronize()
         outs.append(c.cpu().numpy())
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2]), "fp8 split-K results vary"
+
+
+# The FP8 tile kernel on 32x32x64 MFMAs (forced; its split mode serves
+# split-K): 1 to 10 K-slices, two tiles per CU, epilogue combinations with
+# scales on and off, padded leading dimensions, and its masked instance on
+# tails.
+FP8R32 = "fp8_256x256x128_mfma32"
+FP8R32M = "fp8_256x256x128_mfma32_masked"
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (512, 256, 256), (512, 512, 384), (256, 512, 512),
+                                   (1024, 512, 640), (256, 768, 1152), (4096, 2048, 1280), (8192, 4096, 128)])
+def test_fp8_mfma32_slice_counts(M, N, K, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", FP8R32)
+    check_fp8(f"fp8 mfma32 {M}x{N}x{K}", M, N, K, seed=M + N + K + 500, expect_kernel=FP8R32)
+
+
+@pytest.mark.parametrize("beta,use_bias,epi,scales", [(b, u, e, sc) for b in (0.0, -0.75) for u in (False, True)
+                                                      for e in ("none", "gelu_tanh", "relu") for sc in (True, False)
+                                                      if not (u and not sc and e == "relu")])
+def test_fp8_mfma32_epilogue_combinations(beta, use_bias, epi, scales, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", FP8R32)
+    check_fp8(f"fp8 mfma32 beta={beta} bias={use_bias} {epi} scales={scales}", 1024, 512, 384, alpha=1.25,
+              beta=beta, use_bias=use_bias, epilogue=epi, scales=scales,
+              seed=510 + int(abs(beta) * 4) + 2 * use_bias + len(epi) + 7 * scales, expect_kernel=FP8R32)
+
+
+def test_fp8_mfma32_padded_leading_dims(monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", FP8R32)
+    check_fp8("fp8 mfma32 padded", 512, 768, 512, lda=528, ldb=640, ldc=520, beta=0.5, use_bias=True, seed=530,
+              expect_kernel=FP8R32)
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc", [
+    (300, 260, 144, 144, 144, 304),      # one full slice and a 16-wide K chunk
+    (257, 513, 16, 32, 48, 264),         # a single 16-wide K chunk, 1-row / 1-column tails
+    (1001, 777, 208, 224, 208, 1008),    # M % 8 == 1: the last 8-row chunk straddles M
+    (255, 1, 128, 128, 144, 256),        # N = 1
+    (520, 264, 4048, 4064, 4048, 528),   # 31 full slices and a 80-wide K tail
+    (1001, 777, 400, 400, 416, 1003),    # ldc % 8 != 0: element-wise C
+])
+def test_fp8_mfma32_masked_tails(M, N, K, lda, ldb, ldc, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", FP8R32M)
+    check_fp8(f"fp8 mfma32 masked {M}x{N}x{K}", M, N, K, lda=lda, ldb=ldb, ldc=ldc, beta=0.5, use_bias=True,
+              epilogue="relu", seed=M + N + K + 540, expect_kernel=FP8R32M)
+
+
+@pytest.mark.parametrize("beta,use_bias,epi,scales", [(0.0, False, "none", True), (-0.75, True, "gelu_tanh", False),
+                                                      (0.5, False, "relu", True), (0.0, True, "none", False)])
+def test_fp8_mfma32_masked_epilogue_combinations(beta, use_bias, epi, scales, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", FP8R32M)
+    check_fp8(f"fp8 mfma32 masked beta={beta} bias={use_bias} {epi} scales={scales}", 777, 300, 208, ldc=784,
+              alpha=1.25, beta=beta, use_bias=use_bias, epilogue=epi, scales=scales,
+              seed=560 + int(abs(beta) * 4) + 2 * use_bias + len(epi) + 7 * scales, expect_kernel=FP8R32M)
 
 
 # The masked FP8 instance: M and N tails of every size class, K tails down
