@@ -50,12 +50,14 @@ hipError_t launch_tile_ring_masked(const GemmArgs &args, int cus, hipStream_t st
 // int8 output: exact tile multiples, and shapes with tails (masked)
 hipError_t launch_tile_ring_q8(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_ring_q8_masked(const GemmArgs &args, int cus, hipStream_t stream);
-// FP8 tiles on 16x16x128 MFMAs: exact multiples, and shapes with tails
+// FP8 tiles on 16x16x128 MFMAs: exact multiples (the default), and shapes
+// with tails (chosen only when forced)
 hipError_t launch_tile_fp8(const GemmArgs &args, int cus, hipStream_t stream);
-hipError_t launch_tile_fp8_masked(const GemmArgs &args, int cus, hipStream_t stream);
-// the same tiles on 32x32x64 MFMAs (chosen only when forced)
-hipError_t launch_tile_fp8_mfma32(const GemmArgs &args, int cus, hipStream_t stream);
+hipError_t launch_tile_fp8_mfma16_masked(const GemmArgs &args, int cus, hipStream_t stream);
+// the same tiles on 32x32x64 MFMAs: shapes with tails (the default), and
+// exact multiples (chosen only when forced)
 hipError_t launch_tile_fp8_mfma32_masked(const GemmArgs &args, int cus, hipStream_t stream);
+hipError_t launch_tile_fp8_mfma32(const GemmArgs &args, int cus, hipStream_t stream);
 // split-K on the 32x32x64 FP8 tiles (split.P: splits * M * N floats of workspace)
 hipError_t launch_tile_fp8_splitk(const GemmArgs &args, const TileSplit &split, int cus, hipStream_t stream);
 hipError_t launch_tile_fp8_splitk_masked(const GemmArgs &args, const TileSplit &split, int cus,

@@ -20,7 +20,7 @@
 namespace gb {
 
 enum KernelKind {
-    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8Mfma32, kSplitK, kGemv, kSplitKQ8, kFp8Mfma32Masked, kGemvFp8, kSkinnyFp8, kFp8SplitK, kRingQ8Masked, kSkinnyQ8, kMediumMasked, kSplitKMasked, kFp8SplitKMasked, kFp8, kFp8Masked, kNumKinds
+    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8Mfma32, kSplitK, kGemv, kSplitKQ8, kFp8Masked, kGemvFp8, kSkinnyFp8, kFp8SplitK, kRingQ8Masked, kSkinnyQ8, kMediumMasked, kSplitKMasked, kFp8SplitKMasked, kFp8, kFp8Mfma16Masked, kNumKinds
 };
 
 static const char *const kKindNames[kNumKinds] = {"none",            "tile256x256x32_s5", "tile128x128x64_s4",
@@ -28,12 +28,12 @@ static const char *const kKindNames[kNumKinds] = {"none",            "tile256x25
                                                   "ring256x256x64_mfma32", "ring256x256x64",
                                                   "ring256x256x64_masked", "ring256x256x64_q8",
                                                   "fp8_256x256x128_mfma32", "splitk128x128x64", "gemv",
-                                                  "splitk128x128x64_q8", "fp8_256x256x128_mfma32_masked",
+                                                  "splitk128x128x64_q8", "fp8_256x256x128_masked",
                                                   "gemv_fp8",          "skinny_fp8",
                                                   "splitk_fp8_256x256x128", "ring256x256x64_q8_masked",
                                                   "skinny_q8", "tile128x128x64_s4_masked",
                                                   "splitk128x128x64_masked", "splitk_fp8_256x256x128_masked",
-                                                  "fp8_256x256x128", "fp8_256x256x128_masked"};
+                                                  "fp8_256x256x128", "fp8_256x256x128_mfma16_masked"};
 
 static const char *kind_name(int k) { return (k >= 0 && k < kNumKinds) ? kKindNames[k] : "none"; }
 
@@ -368,7 +368,7 @@ static TileSplit plan_splitk_fp8(int64_t M, int64_t N, int64_t K, int cus) {
 
 static hipError_t launch_fp8_splitk_plan(const GemmArgs &args, int cus, hipStream_t stream, bool masked) {
     TileSplit p = plan_splitk_fp8(args.M, args.N, args.K, cus);
-    if (p.splits < 2) return masked ? launch_tile_fp8_masked(args, cus, stream) : launch_tile_fp8(args, cus, stream);
+    if (p.splits < 2) return masked ? launch_tile_fp8_mfma32_masked(args, cus, stream) : launch_tile_fp8(args, cus, stream);
     uint32_t *unused = nullptr;
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     hipError_t err = get_workspace(stream, 0, (size_t)p.splits * (size_t)p.pstride, &unused, &p.P);
@@ -548,8 +548,8 @@ static int choose_kernel_fp8(int64_t M, int64_t N, int64_t K, const void *A, int
                        aligned16(C);
     if (force && !std::strcmp(force, kKindNames[kFp8Masked])) return kFp8Masked;
     if (force && !std::strcmp(force, kKindNames[kFp8])) return exact ? kFp8 : kFp8Masked;
-    if (force && !std::strcmp(force, kKindNames[kFp8Mfma32Masked])) return kFp8Mfma32Masked;
-    if (force && !std::strcmp(force, kKindNames[kFp8Mfma32])) return exact ? kFp8Mfma32 : kFp8Mfma32Masked;
+    if (force && !std::strcmp(force, kKindNames[kFp8Mfma16Masked])) return kFp8Mfma16Masked;
+    if (force && !std::strcmp(force, kKindNames[kFp8Mfma32])) return exact ? kFp8Mfma32 : kFp8Masked;
     // small grids: split K (the reduction needs C aligned and ldc % 8, both
     // implied; it writes a chunk that straddles M element by element)
     const bool can_split = plan_splitk_fp8(M, N, K, device_cu_count()).splits >= 2;
@@ -697,9 +697,9 @@ int gemm_fp8(int64_t M, int64_t N, int64_t K, const gemm_fp8_t *A, int64_t lda, 
     case kFp8: err = launch_tile_fp8(args, cus, stream); break;
     case kFp8SplitK: err = launch_fp8_splitk_plan(args, cus, stream, false); break;
     case kFp8SplitKMasked: err = launch_fp8_splitk_plan(args, cus, stream, true); break;
-    case kFp8Masked: err = launch_tile_fp8_masked(args, cus, stream); break;
+    case kFp8Masked: err = launch_tile_fp8_mfma32_masked(args, cus, stream); break;
     case kFp8Mfma32: err = launch_tile_fp8_mfma32(args, cus, stream); break;
-    case kFp8Mfma32Masked: err = launch_tile_fp8_mfma32_masked(args, cus, stream); break;
+    case kFp8Mfma16Masked: err = launch_tile_fp8_mfma16_masked(args, cus, stream); break;
     case kGemvFp8: err = launch_gemv(args, stream, true); break;
     case kSkinnyFp8: err = launch_skinny_plan(args, cus, stream, true); break;
     default: err = launch_generic(args, cus, stream, true); break;

@@ -283,6 +283,16 @@ gemm_fp8_ring16_kernel(const GemmArgs args, const TileSchedule sched) {
         RingEpiInputs epi_in;
         const auto mid = [&] { ring_epi_load<kFlags, kMasked, true>(epi_in, args, m0, n0, wm, wn, lane, 0); };
         RK::template slice<K::kLast>(smem, nk - 1, sa, Ln, rA, rB, fa, fb, acc, mid);
+        // With beta or masking, every MFMA of the tile completes here: the
+        // compiler may not sink the last slice's MFMAs into the epilogue,
+        // where their fragments would stay live beside the C loads and the
+        // masked stores and spill.  (The plain epilogue is better without.)
+        if constexpr (kMasked || (kFlags & kEpiBeta) != 0) {
+#pragma unroll
+            for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+                for (int q = 0; q < Cfg::FN; ++q) asm volatile("" : "+a"(acc[i][q]));
+        }
         // The out-of-range loads of the last full slices write zeros into
         // free slots: they land before the epilogue stages its values there.
         wait_vmcnt<0>();

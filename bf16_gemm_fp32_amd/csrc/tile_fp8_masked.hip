@@ -1,6 +1,6 @@
 // tile_fp8_masked.hip -- instances of the 256x256 FP8 (E4M3) tile kernel on
 // 32x32x64 MFMAs for shapes with tails (zero-filled out-of-range loads,
-// masked epilogue): whole-K (chosen only when forced) and split-K.
+// masked epilogue): whole-K (the default for FP8 tails) and split-K.
 #include "configs.h"
 #include "kernel_fp8.h"
 

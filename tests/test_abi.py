@@ -134,14 +134,16 @@ def test_fp8_argument_errors_and_names():
     assert name(1, 4096, 4040, P, 4048, P, 4048, P, 1) == "generic64x64x32"          # K % 16 != 0
 
 
-def test_fp8_forced_mfma32_names(monkeypatch):
-    # the 32x32x64 FP8 tiles run only when forced (their split mode serves split-K)
+def test_fp8_forced_mfma_form_names(monkeypatch):
+    # exact FP8 tiles run on 16x16x128 and tails on 32x32x64 MFMAs; the other
+    # form of each runs only when forced
     name = gb.gemm_fp8_kernel_name
     monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", "fp8_256x256x128_mfma32")
     assert name(4096, 4096, 4096, P, 4096, P, 4096, P, 4096) == "fp8_256x256x128_mfma32"
-    assert name(4000, 4096, 4096, P, 4096, P, 4096, P, 4000) == "fp8_256x256x128_mfma32_masked"
-    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", "fp8_256x256x128_mfma32_masked")
-    assert name(4096, 4096, 4096, P, 4096, P, 4096, P, 4096) == "fp8_256x256x128_mfma32_masked"
+    assert name(4000, 4096, 4096, P, 4096, P, 4096, P, 4000) == "fp8_256x256x128_masked"
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", "fp8_256x256x128_mfma16_masked")
+    assert name(4096, 4096, 4096, P, 4096, P, 4096, P, 4096) == "fp8_256x256x128_mfma16_masked"
+    assert name(4000, 4096, 4096, P, 4096, P, 4096, P, 4000) == "fp8_256x256x128_mfma16_masked"
     monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", "fp8_256x256x128")
     assert name(1024, 1024, 4096, P, 4096, P, 4096, P, 1024) == "fp8_256x256x128"  # unsplit when forced
 

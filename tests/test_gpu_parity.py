@@ -797,12 +797,13 @@ def test_fp8_splitk_deterministic():
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2]), "fp8 split-K results vary"
 
 
-# The FP8 tile kernel on 32x32x64 MFMAs (forced; its split mode serves
-# split-K): 1 to 10 K-slices, two tiles per CU, epilogue combinations with
-# scales on and off, padded leading dimensions, and its masked instance on
-# tails.
+# The FP8 tile kernel on 32x32x64 MFMAs forced onto exact tiles (its masked
+# instance is the default for tails, its split mode serves split-K): 1 to
+# 10 K-slices, two tiles per CU, epilogue combinations with scales on and
+# off, padded leading dimensions; and the masked instance of the 16x16x128
+# kernel (forced) on tails.
 FP8R32 = "fp8_256x256x128_mfma32"
-FP8R32M = "fp8_256x256x128_mfma32_masked"
+FP8R16M = "fp8_256x256x128_mfma16_masked"
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 256, 128), (512, 256, 256), (512, 512, 384), (256, 512, 512),
@@ -836,19 +837,19 @@ def test_fp8_mfma32_padded_leading_dims(monkeypatch):
     (520, 264, 4048, 4064, 4048, 528),   # 31 full slices and a 80-wide K tail
     (1001, 777, 400, 400, 416, 1003),    # ldc % 8 != 0: element-wise C
 ])
-def test_fp8_mfma32_masked_tails(M, N, K, lda, ldb, ldc, monkeypatch):
-    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", FP8R32M)
-    check_fp8(f"fp8 mfma32 masked {M}x{N}x{K}", M, N, K, lda=lda, ldb=ldb, ldc=ldc, beta=0.5, use_bias=True,
-              epilogue="relu", seed=M + N + K + 540, expect_kernel=FP8R32M)
+def test_fp8_mfma16_masked_tails(M, N, K, lda, ldb, ldc, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", FP8R16M)
+    check_fp8(f"fp8 mfma16 masked {M}x{N}x{K}", M, N, K, lda=lda, ldb=ldb, ldc=ldc, beta=0.5, use_bias=True,
+              epilogue="relu", seed=M + N + K + 540, expect_kernel=FP8R16M)
 
 
 @pytest.mark.parametrize("beta,use_bias,epi,scales", [(0.0, False, "none", True), (-0.75, True, "gelu_tanh", False),
                                                       (0.5, False, "relu", True), (0.0, True, "none", False)])
-def test_fp8_mfma32_masked_epilogue_combinations(beta, use_bias, epi, scales, monkeypatch):
-    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", FP8R32M)
-    check_fp8(f"fp8 mfma32 masked beta={beta} bias={use_bias} {epi} scales={scales}", 777, 300, 208, ldc=784,
+def test_fp8_mfma16_masked_epilogue_combinations(beta, use_bias, epi, scales, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", FP8R16M)
+    check_fp8(f"fp8 mfma16 masked beta={beta} bias={use_bias} {epi} scales={scales}", 777, 300, 208, ldc=784,
               alpha=1.25, beta=beta, use_bias=use_bias, epilogue=epi, scales=scales,
-              seed=560 + int(abs(beta) * 4) + 2 * use_bias + len(epi) + 7 * scales, expect_kernel=FP8R32M)
+              seed=560 + int(abs(beta) * 4) + 2 * use_bias + len(epi) + 7 * scales, expect_kernel=FP8R16M)
 
 
 # The masked FP8 instance: M and N tails of every size class, K tails down
