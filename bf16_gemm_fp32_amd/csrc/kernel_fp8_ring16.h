@@ -21,8 +21,9 @@
 // columns 4-7 (both row by row).  Every fragment then has one register set,
 // 128 VGPRs in all: A_0..3 are dead after the second quadrant and B_0..3
 // after the third, so the next slice's A_0..3 and B_0..3 are read in the
-// third and fourth quadrants; A_4..7 and B_4..7 are first needed in the
-// second and third quadrants, so each slice reads its own in the first two.
+// third and fourth quadrants; B_4..7 are first needed in the second
+// quadrant and A_4..7 in the third, so each slice reads its own B_4..7 in
+// the first quadrant and its own A_4..7 in the second.
 // One 16-byte read follows every even MFMA:
 //   quadrant 0: B_4..B_7    1: A_4..A_7    2: A'_0..A'_3    3: B'_0..B'_3
 // (A', B': the next slice's).
