@@ -108,7 +108,7 @@ def check_full(tag, M, N, K, lda=None, ldb=None, ldc=None, alpha=1.0, beta=0.0, 
     # rows M..ldc-1 of every column are not part of C: untouched
     if ldc > M:
         assert np.array_equal(g2[:, M:], C_init.reshape(N, ldc)[:, M:]), f"{tag}: padding written"
-    say(f"[parity] {tag}: ok max_ulp={rep['max_ulp']:.2f} mean_ulp={rep['mean_ulp']:.4f} "
+    say(f"[parity] {tag}: ok max_err/tol={rep['max_err_over_tol']:.3f} mean_err/tol={rep['mean_err_over_tol']:.4f} "
         f"exact={rep['exact']}/{rep['n']}")
     return rep
 
@@ -712,7 +712,7 @@ def check_fp8(tag, M, N, K, lda=None, ldb=None, ldc=None, alpha=1.0, beta=0.0, u
     rep = assert_within_tolerance(g2[:, :M], r2[:, :M], K, tag)
     if ldc > M:
         assert np.array_equal(g2[:, M:], C_init.reshape(N, ldc)[:, M:]), f"{tag}: padding written"
-    say(f"[parity-fp8] {tag}: ok max_ulp={rep['max_ulp']:.2f} mean_ulp={rep['mean_ulp']:.4f} "
+    say(f"[parity-fp8] {tag}: ok max_err/tol={rep['max_err_over_tol']:.3f} mean_err/tol={rep['mean_err_over_tol']:.4f} "
         f"exact={rep['exact']}/{rep['n']}")
     return rep
 
@@ -1024,8 +1024,8 @@ def test_workload_full_size_sampled(name):
         ref = oracle.gemm_elems(M, N, K, d["A"], K, d["B"], K, ms, ns, C0, M, w.alpha, w.beta, bias,
                                 w.epilogue, nthreads=_threads())
         rep = assert_within_tolerance(got[ms + ns * M], ref, K, name)
-    say(f"[parity] workload {name}: ok n={rep['n']} max_ulp={rep['max_ulp']:.2f} "
-        f"mean_ulp={rep['mean_ulp']:.4f} exact={rep['exact']}")
+    say(f"[parity] workload {name}: ok n={rep['n']} max_err/tol={rep['max_err_over_tol']:.3f} "
+        f"mean_err/tol={rep['mean_err_over_tol']:.4f} exact={rep['exact']}")
 
 
 def _workload_q8_sampled(w, d):
@@ -1065,4 +1065,4 @@ def _workload_fp8_sampled(w, d):
     ref_bits = oracle.gemm_fp8_elems(M, N, K, d["A"], K, d["B"], K, ms, ns, scale_a=d["scale_a"],
                                      scale_b=d["scale_b"], epilogue=w.epilogue, nthreads=_threads())
     rep = assert_within_tolerance(got[ms + ns * M], ref_bits, K, w.name)
-    say(f"[parity-fp8] workload {w.name}: ok n={rep['n']} max_ulp={rep['max_ulp']:.2f} exact={rep['exact']}")
+    say(f"[parity-fp8] workload {w.name}: ok n={rep['n']} max_err/tol={rep['max_err_over_tol']:.3f} exact={rep['exact']}")
