@@ -172,6 +172,16 @@ static bool gemv_path_ok(int64_t M, int64_t N, int64_t K, const void *A, int64_t
     return true;
 }
 
+// Split-K scratch.  Every split path stores fp32 partials, and the
+// streaming kernel also keeps one uint32 arrival counter per strip; both
+// live in one buffer laid out as [counters | partials].  Its size is fixed:
+// kScratchCounters counters and kScratchFloatsPerCu floats (one 128x128
+// fp32 tile) per compute unit.  The plans below never split further than
+// that holds, so no call ever needs more.
+constexpr size_t kScratchCounters = 16384;
+constexpr size_t kScratchCounterBytes = kScratchCounters * 4;
+constexpr size_t kScratchFloatsPerCu = 128 * 128;
+
 // How the streaming kernel covers a short product: its row block (32 or
 // 64), strip width, and the K split.  32-column strips measured fastest at
 // every size tried (the wider ones exist for experiments).  K is split only
@@ -179,12 +189,15 @@ static bool gemv_path_ok(int64_t M, int64_t N, int64_t K, const void *A, int64_t
 // idle: then up to one unit per compute unit, each split keeping at least 4
 // K-slices so the rings have something to overlap.  (At 64 x 1024 x 16384 a
 // split of 8 runs 2.3x faster than none; at 64 x 4096 x 4096, with 128
-// strips, a split of 2 is 10% slower than none.)
+// strips, a split of 2 is 10% slower than none.)  cap_floats bounds the
+// partials (strips x splits x rows x columns floats) and the strips must fit
+// the counters.
 struct SkinnyPlan {
     int rows, cols, strips, splits, spp;
 };
 
-static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int cus, bool fp8 = false, bool q8 = false) {
+static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int cus, size_t cap_floats, bool fp8 = false,
+                              bool q8 = false) {
     SkinnyPlan p{};
     p.rows = M <= 32 ? 32 : 64;
     int width = 32;
@@ -196,68 +209,86 @@ static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int cus, bool fp8
     p.cols = width;
     const int ks = fp8 ? ShapeSkinny::KS_FP8 : (width == 32 ? ShapeSkinny::KS_N32 : ShapeSkinny::KS_WIDE);
     const int64_t nk = (K + ks - 1) / ks;
-    p.strips = (int)((N + width - 1) / width);
-    int64_t splits = p.strips * 2 >= cus ? 1 : cus / p.strips;
+    const int64_t strips = (N + width - 1) / width;
+    p.strips = (int)strips;
+    int64_t splits = strips * 2 >= cus ? 1 : cus / strips;
     if (const char *env = std::getenv("GEMM_BF16_SKINNY_SPLITS")) {  // tuning knob
         const int s = std::atoi(env);
         if (s >= 1) splits = s;
     }
     const int64_t max_splits = nk / 4 > 1 ? nk / 4 : 1;
     if (splits > max_splits) splits = max_splits;
+    const int64_t per_split = strips * (int64_t)p.cols * p.rows;
+    if (splits > 1 && (strips > (int64_t)kScratchCounters || splits * per_split > (int64_t)cap_floats))
+        splits = strips > (int64_t)kScratchCounters ? 1 : (int64_t)cap_floats / per_split;
     if (splits < 1) splits = 1;
     p.spp = (int)((nk + splits - 1) / splits);
     p.splits = (int)((nk + p.spp - 1) / p.spp);  // no empty split
     return p;
 }
 
-// Per-(device, stream) workspace of the split-K reductions: one uint32
-// counter per strip (zero at allocation; the last unit of a strip resets its
-// counter) followed by the fp32 partials.  Calls on one stream are ordered,
-// so they can share it; a call on another stream gets its own.  It grows on
-// demand (after draining the stream, whose work may still use the old one)
-// and lives until the process ends.  The caller holds g_ws_mutex from the
-// lookup until its kernels are enqueued, so a growth started by another
-// thread on the same stream cannot free the buffer in between.
-struct Workspace {
-    char *base = nullptr;
-    size_t counter_bytes = 0, partial_bytes = 0;
+// Where a call's split-K scratch comes from.
+//  * gemm_bf16 and the other allocating entry points: one buffer per
+//    (device, stream), allocated by the first call on that stream that
+//    splits, at its fixed size (counters + CUs x 64 KiB), with the counters
+//    zeroed by a fill kernel on that stream; it is never grown, freed or
+//    synchronized on afterwards and lives until the process ends.  Calls on
+//    one stream are ordered, so they share it safely; calls on other streams
+//    get their own.  (A stream handle that is destroyed and handed out again
+//    by the runtime finds the old buffer: work on the destroyed stream must
+//    have finished by then, as for any memory it used.)
+struct Scratch {
+    char *fixed = nullptr;   // a caller-independent buffer to use instead (none yet)
+    size_t cap_floats = 0;   // partial floats the buffer holds
 };
-static std::mutex g_ws_mutex;
-static std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
-static hipError_t get_workspace(hipStream_t stream, size_t counters, size_t partial_floats, uint32_t **cnt,
-                                float **partials) {
-    int dev = 0;
-    hipError_t err = hipGetDevice(&dev);
-    if (err != hipSuccess) return err;
-    const size_t need_c = (counters * 4 + 255) / 256 * 256, need_p = partial_floats * 4;
-    Workspace &w = g_ws[std::make_pair(dev, stream)];
-    if (w.base == nullptr || w.counter_bytes < need_c || w.partial_bytes < need_p) {
-        const size_t nc = need_c > w.counter_bytes ? need_c : w.counter_bytes;
-        const size_t np = need_p > w.partial_bytes ? need_p : w.partial_bytes;
-        if (w.base != nullptr) {
-            if ((err = hipStreamSynchronize(stream)) != hipSuccess) return err;
-            if ((err = hipFree(w.base)) != hipSuccess) return err;
-            w = Workspace{};
+static std::mutex g_ws_mutex;  // guards g_ws (a lookup, or one allocation per (device, stream))
+static std::map<std::pair<int, hipStream_t>, char *> g_ws;
+
+__global__ void zero_u32_kernel(uint32_t *p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+static hipError_t zero_counters(uint32_t *cnt, hipStream_t stream) {
+    const int n = (int)kScratchCounters;
+    hipLaunchKernelGGL(zero_u32_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, cnt, n);
+    return hipGetLastError();
+}
+
+static Scratch stream_scratch(int cus) {
+    Scratch s;
+    s.cap_floats = (size_t)cus * kScratchFloatsPerCu;
+    return s;
+}
+
+static hipError_t get_scratch(const Scratch &src, hipStream_t stream, uint32_t **cnt, float **partials) {
+    char *base = src.fixed;
+    if (base == nullptr) {
+        int dev = 0;
+        hipError_t err = hipGetDevice(&dev);
+        if (err != hipSuccess) return err;
+        std::lock_guard<std::mutex> lock(g_ws_mutex);
+        auto it = g_ws.find(std::make_pair(dev, stream));
+        if (it != g_ws.end()) {
+            base = it->second;
+        } else {
+            if ((err = hipMalloc(&base, kScratchCounterBytes + src.cap_floats * 4)) != hipSuccess) return err;
+            if ((err = zero_counters(reinterpret_cast<uint32_t *>(base), stream)) != hipSuccess) {
+                (void)hipFree(base);
+                return err;
+            }
+            g_ws.emplace(std::make_pair(dev, stream), base);
         }
-        char *p = nullptr;
-        if ((err = hipMalloc(&p, nc + np)) != hipSuccess) return err;
-        if ((err = hipMemsetAsync(p, 0, nc, stream)) != hipSuccess) {
-            (void)hipFree(p);
-            return err;
-        }
-        w.base = p;
-        w.counter_bytes = nc;
-        w.partial_bytes = np;
     }
-    *cnt = reinterpret_cast<uint32_t *>(w.base);
-    *partials = reinterpret_cast<float *>(w.base + w.counter_bytes);
+    *cnt = reinterpret_cast<uint32_t *>(base);
+    *partials = reinterpret_cast<float *>(base + kScratchCounterBytes);
     return hipSuccess;
 }
 
-static hipError_t launch_skinny_plan(const GemmArgs &args, int cus, hipStream_t stream, bool fp8 = false,
-                                     bool q8 = false) {
-    const SkinnyPlan p = plan_skinny(args.M, args.N, args.K, cus, fp8, q8);
+static hipError_t launch_skinny_plan(const GemmArgs &args, int cus, const Scratch &scr, hipStream_t stream,
+                                     bool fp8 = false, bool q8 = false) {
+    const SkinnyPlan p = plan_skinny(args.M, args.N, args.K, cus, scr.cap_floats, fp8, q8);
     SkinnyWork work{};
     work.num_strips = p.strips;
     work.splits = p.splits;
@@ -266,8 +297,8 @@ static hipError_t launch_skinny_plan(const GemmArgs &args, int cus, hipStream_t 
     work.q_vector = q8 && (reinterpret_cast<uintptr_t>(args.Q) & 7u) == 0 && args.ldq % 8 == 0;
     if (p.splits > 1) {
         const size_t floats = (size_t)p.strips * p.splits * p.cols * p.rows;
-        std::lock_guard<std::mutex> lock(g_ws_mutex);
-        hipError_t err = get_workspace(stream, (size_t)p.strips, floats, &work.counters, &work.partials);
+        if (floats > scr.cap_floats || (size_t)p.strips > kScratchCounters) return hipErrorInvalidValue;
+        hipError_t err = get_scratch(scr, stream, &work.counters, &work.partials);
         if (err != hipSuccess) return err;
         if (q8) return launch_skinny_q8(p.rows, args, work, cus, stream);
         return fp8 ? launch_skinny_fp8(p.rows, args, work, cus, stream)
@@ -281,12 +312,13 @@ static hipError_t launch_skinny_plan(const GemmArgs &args, int cus, hipStream_t 
 // Split-K on the 128x128 tiles: used when those tiles alone would leave more
 // than half of the compute units idle.  The K-slices (64 wide) are cut into
 // up to CUs / tiles ranges of at least kMinSlices slices each, so every
-// range still runs a pipelined loop; partials take splits * M * N floats of
-// workspace (at most 4M floats: splits * tiles <= CUs and a tile is 16K
-// elements).  Returns 1 when no split applies.
+// range still runs a pipelined loop; partials take splits x (M x N padded to
+// tiles) floats of scratch (at most CUs x 16K floats: splits * tiles <= CUs
+// and a tile is 16K elements; forced split counts are capped by cap_floats).
+// Returns 1 when no split applies.
 constexpr int kSplitMinSlices = 8;
 
-static TileSplit plan_splitk(int64_t M, int64_t N, int64_t K, int cus) {
+static TileSplit plan_splitk(int64_t M, int64_t N, int64_t K, int cus, size_t cap_floats) {
     TileSplit p{};
     p.splits = 1;
     // tiles and slices rounded up: shapes with tails run the masked kernel
@@ -300,12 +332,15 @@ static TileSplit plan_splitk(int64_t M, int64_t N, int64_t K, int cus) {
     }
     const int64_t max_splits = nk / kSplitMinSlices;
     if (splits > max_splits) splits = max_splits;
+    // whole tiles are stored: the scratch is padded to tile multiples
+    const int64_t ldp = (M + ShapeM::BM - 1) / ShapeM::BM * ShapeM::BM;
+    const int64_t pstride = ldp * ((N + ShapeM::BN - 1) / ShapeM::BN * ShapeM::BN);
+    if (splits > (int64_t)cap_floats / pstride) splits = (int64_t)cap_floats / pstride;
     if (splits < 2) return p;
     p.kper = (int)((nk + splits - 1) / splits);
     p.splits = (int)((nk + p.kper - 1) / p.kper);  // no empty range
-    // whole tiles are stored: the workspace is padded to tile multiples
-    p.ldp = (M + ShapeM::BM - 1) / ShapeM::BM * ShapeM::BM;
-    p.pstride = p.ldp * ((N + ShapeM::BN - 1) / ShapeM::BN * ShapeM::BN);
+    p.ldp = ldp;
+    p.pstride = pstride;
     return p;
 }
 
@@ -326,7 +361,7 @@ static bool splitk_pays(int64_t M, int64_t N, int64_t K) {
 // Split-K for the FP8 tiles on small grids (the fp8 path has no smaller
 // tile): when the 256x256 tiles fill less than half of the compute units,
 // up to CUs / tiles ranges of at least 4 slices of 128, at most 8, and at
-// most 4M floats of partials (16 MiB).  Returns 1 when no split applies.
+// most cap_floats floats of partials.  Returns 1 when no split applies.
 // Whether splitting K over the 256x256 FP8 tiles beats the unsplit kernel:
 // measured on gfx950, the split (tile kernel, then the reduction) wins from
 // about 15 slices of 128 at 8 tiles, 24 at 16 tiles and 33 at 32 tiles
@@ -339,7 +374,7 @@ static bool fp8_splitk_pays(int64_t M, int64_t N, int64_t K) {
     return 8 * nk >= 88 + 5 * tiles;
 }
 
-static TileSplit plan_splitk_fp8(int64_t M, int64_t N, int64_t K, int cus) {
+static TileSplit plan_splitk_fp8(int64_t M, int64_t N, int64_t K, int cus, size_t cap_floats) {
     TileSplit p{};
     p.splits = 1;
     // tiles and slices rounded up (shapes with tails run the masked kernel,
@@ -356,7 +391,7 @@ static TileSplit plan_splitk_fp8(int64_t M, int64_t N, int64_t K, int cus) {
     }
     if (splits > nk / 4) splits = nk / 4;
     if (splits > 8) splits = 8;
-    const int64_t cap = ((int64_t)4 << 20) / (mp * np);
+    const int64_t cap = (int64_t)cap_floats / (mp * np);
     if (splits > cap) splits = cap;
     if (splits < 2) return p;
     p.kper = (int)((nk + splits - 1) / splits);
@@ -366,28 +401,29 @@ static TileSplit plan_splitk_fp8(int64_t M, int64_t N, int64_t K, int cus) {
     return p;
 }
 
-static hipError_t launch_fp8_splitk_plan(const GemmArgs &args, int cus, hipStream_t stream, bool masked) {
-    TileSplit p = plan_splitk_fp8(args.M, args.N, args.K, cus);
+static hipError_t launch_fp8_splitk_plan(const GemmArgs &args, int cus, const Scratch &scr, hipStream_t stream,
+                                         bool masked) {
+    TileSplit p = plan_splitk_fp8(args.M, args.N, args.K, cus, scr.cap_floats);
     if (p.splits < 2) return masked ? launch_tile_fp8_mfma32_masked(args, cus, stream) : launch_tile_fp8(args, cus, stream);
+    if ((size_t)p.splits * (size_t)p.pstride > scr.cap_floats) return hipErrorInvalidValue;
     uint32_t *unused = nullptr;
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    hipError_t err = get_workspace(stream, 0, (size_t)p.splits * (size_t)p.pstride, &unused, &p.P);
+    hipError_t err = get_scratch(scr, stream, &unused, &p.P);
     if (err != hipSuccess) return err;
     return masked ? launch_tile_fp8_splitk_masked(args, p, cus, stream) : launch_tile_fp8_splitk(args, p, cus, stream);
 }
 
 // kQ8: the quantizing output (the host chose this path only when the plan
 // splits).
-static hipError_t launch_splitk_plan(const GemmArgs &args, int cus, hipStream_t stream, bool q8 = false,
-                                     bool masked = false) {
-    TileSplit p = plan_splitk(args.M, args.N, args.K, cus);
+static hipError_t launch_splitk_plan(const GemmArgs &args, int cus, const Scratch &scr, hipStream_t stream,
+                                     bool q8 = false, bool masked = false) {
+    TileSplit p = plan_splitk(args.M, args.N, args.K, cus, scr.cap_floats);
     if (p.splits < 2) {
         if (q8) return hipErrorInvalidValue;
         return masked ? launch_tile_medium_masked(args, cus, stream) : launch_tile_medium(args, cus, stream);
     }
+    if ((size_t)p.splits * (size_t)p.pstride > scr.cap_floats) return hipErrorInvalidValue;
     uint32_t *unused = nullptr;
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    hipError_t err = get_workspace(stream, 0, (size_t)p.splits * (size_t)p.pstride, &unused, &p.P);
+    hipError_t err = get_scratch(scr, stream, &unused, &p.P);
     if (err != hipSuccess) return err;
     if (q8) return launch_tile_medium_splitk_q8(args, p, cus, stream);
     return masked ? launch_tile_medium_splitk_masked(args, p, cus, stream)
@@ -398,7 +434,7 @@ static hipError_t launch_splitk_plan(const GemmArgs &args, int cus, hipStream_t 
 // overrides the choice when that kernel can run the shape; it exists for
 // testing and benchmarking the alternatives.
 static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
-                         int64_t ldb, const void *C, int64_t ldc, int cus) {
+                         int64_t ldb, const void *C, int64_t ldc, int cus, size_t cap_floats) {
     if (M == 0 || N == 0) return kNone;
     const bool okL = tile_path_ok<ShapeL>(M, N, K, A, lda, B, ldb, C, ldc);
     const bool okM = tile_path_ok<ShapeM>(M, N, K, A, lda, B, ldb, C, ldc);
@@ -409,12 +445,12 @@ static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t
     const bool okMM = medium_masked_ok(M, N, K, A, lda, B, ldb, C, ldc);
     if (const char *force = std::getenv("GEMM_BF16_FORCE_KERNEL")) {
         if (!std::strcmp(force, kKindNames[kMediumMasked]) && okMM) return kMediumMasked;
-        if (!std::strcmp(force, kKindNames[kSplitKMasked]) && okMM && plan_splitk(M, N, K, cus).splits >= 2)
+        if (!std::strcmp(force, kKindNames[kSplitKMasked]) && okMM && plan_splitk(M, N, K, cus, cap_floats).splits >= 2)
             return kSplitKMasked;
         if (!std::strcmp(force, kKindNames[kGeneric])) return kGeneric;
         if (!std::strcmp(force, kKindNames[kLarge]) && okL) return kLarge;
         if (!std::strcmp(force, kKindNames[kMedium]) && okM) return kMedium;
-        if (!std::strcmp(force, kKindNames[kSplitK]) && okM && plan_splitk(M, N, K, cus).splits >= 2)
+        if (!std::strcmp(force, kKindNames[kSplitK]) && okM && plan_splitk(M, N, K, cus, cap_floats).splits >= 2)
             return kSplitK;
         if (!std::strcmp(force, kKindNames[kRing32]) && okR) return kRing32;
         if (!std::strcmp(force, kKindNames[kRing]) && okR) return kRing;
@@ -448,12 +484,12 @@ static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t
         const int64_t tiles = (M / ShapeL::BM) * (N / ShapeL::BN);
         if (tiles * 2 >= cus || !okM) return kLarge;
     }
-    if (okM) return plan_splitk(M, N, K, cus).splits >= 2 && splitk_pays(M, N, K) ? kSplitK : kMedium;
+    if (okM) return plan_splitk(M, N, K, cus, cap_floats).splits >= 2 && splitk_pays(M, N, K) ? kSplitK : kMedium;
     // Tails on small and mid-sized grids (and unaligned C or ldc % 8 != 0):
     // the masked 128x128 kernel, split by the same rule.  1000 x 1000 x 1000
     // runs in 11.5 us (1024^3 unmasked: 9.6 us; the bounds-checked kernel
     // 18.4 us), 1000 x 1000 x 4096 split in 21.8 us (bounds-checked 67 us).
-    if (okMM) return plan_splitk(M, N, K, cus).splits >= 2 && splitk_pays(M, N, K) ? kSplitKMasked : kMediumMasked;
+    if (okMM) return plan_splitk(M, N, K, cus, cap_floats).splits >= 2 && splitk_pays(M, N, K) ? kSplitKMasked : kMediumMasked;
     return kGeneric;
 }
 
@@ -463,7 +499,7 @@ static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t
 // shape allows it (its reduction quantizes); else the bounds-checked kernel.
 static int choose_kernel_q8(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
                             int64_t ldb, const void *C, int64_t ldc, float beta, const void *Q, int64_t ldq,
-                            const void *scale, int cus) {
+                            const void *scale, int cus, size_t cap_floats) {
     if (M == 0 || N == 0) return kNone;
     // At most 64 rows: the streaming kernel with the int8 epilogue (any ldc
     // and ldq; 8-row chunks of Q go out as one store when Q allows it).
@@ -490,7 +526,7 @@ static int choose_kernel_q8(int64_t M, int64_t N, int64_t K, const void *A, int6
         const bool forced = force && !std::strcmp(force, kKindNames[kRingQ8]);
         if (tiles * 2 >= cus || forced) return exact ? kRingQ8 : kRingQ8Masked;
         if (tile_path_ok<ShapeM>(M, N, K, A, lda, B, ldb, c_probe, ldc_probe) &&
-            plan_splitk(M, N, K, cus).splits >= 2)
+            plan_splitk(M, N, K, cus, cap_floats).splits >= 2)
             return kSplitKQ8;
     }
     return kGeneric;
@@ -519,7 +555,7 @@ static hipError_t launch_generic(const GemmArgs &args, int cus, hipStream_t stre
 // else the bounds-checked kernel (which converts the bytes to bf16 on their
 // way into LDS).
 static int choose_kernel_fp8(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
-                             int64_t ldb, const void *C, int64_t ldc) {
+                             int64_t ldb, const void *C, int64_t ldc, int cus, size_t cap_floats) {
     if (M == 0 || N == 0) return kNone;
     const char *force = std::getenv("GEMM_BF16_FORCE_KERNEL");
     if (force && !std::strcmp(force, kKindNames[kGeneric])) return kGeneric;
@@ -552,7 +588,7 @@ static int choose_kernel_fp8(int64_t M, int64_t N, int64_t K, const void *A, int
     if (force && !std::strcmp(force, kKindNames[kFp8Mfma32])) return exact ? kFp8Mfma32 : kFp8Masked;
     // small grids: split K (the reduction needs C aligned and ldc % 8, both
     // implied; it writes a chunk that straddles M element by element)
-    const bool can_split = plan_splitk_fp8(M, N, K, device_cu_count()).splits >= 2;
+    const bool can_split = plan_splitk_fp8(M, N, K, cus, cap_floats).splits >= 2;
     if (force && can_split &&
         (!std::strcmp(force, kKindNames[kFp8SplitK]) || !std::strcmp(force, kKindNames[kFp8SplitKMasked])))
         return exact ? kFp8SplitK : kFp8SplitKMasked;
@@ -560,18 +596,11 @@ static int choose_kernel_fp8(int64_t M, int64_t N, int64_t K, const void *A, int
     return exact ? kFp8 : kFp8Masked;
 }
 
-}  // namespace gb
-
-extern "C" {
-
-int gemm_bf16(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t lda, const gemm_bf16_t *B,
-              int64_t ldb, gemm_bf16_t *C, int64_t ldc, float alpha, float beta, const gemm_bf16_t *bias,
-              int epilogue, hipStream_t stream) {
-    using namespace gb;
-    const int st = validate(M, N, K, A, lda, B, ldb, C, ldc, epilogue);
-    if (st != GEMM_OK) return st;
-    if (M == 0 || N == 0) return GEMM_OK;
-
+// The bf16 product behind gemm_bf16 (arguments already validated, M, N >
+// 0); scr says where split-K partials go.
+static int run_bf16(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t lda, const gemm_bf16_t *B,
+                    int64_t ldb, gemm_bf16_t *C, int64_t ldc, float alpha, float beta, const gemm_bf16_t *bias,
+                    int epilogue, const Scratch &scr, int cus, hipStream_t stream) {
     GemmArgs args{};
     args.M = M;
     args.N = N;
@@ -591,19 +620,18 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t lda
     args.scale = nullptr;
     args.zp = 0.f;
 
-    const int cus = device_cu_count();
     hipError_t err = hipSuccess;
-    switch (choose_kernel(M, N, K, A, lda, B, ldb, C, ldc, cus)) {
+    switch (choose_kernel(M, N, K, A, lda, B, ldb, C, ldc, cus, scr.cap_floats)) {
     case kLarge: err = launch_tile_large(args, cus, stream); break;
     case kMedium: err = launch_tile_medium(args, cus, stream); break;
-    case kSplitK: err = launch_splitk_plan(args, cus, stream); break;
+    case kSplitK: err = launch_splitk_plan(args, cus, scr, stream); break;
     case kMediumMasked: err = launch_tile_medium_masked(args, cus, stream); break;
-    case kSplitKMasked: err = launch_splitk_plan(args, cus, stream, false, true); break;
+    case kSplitKMasked: err = launch_splitk_plan(args, cus, scr, stream, false, true); break;
     case kGemv: err = launch_gemv(args, stream); break;
     case kRing32: err = launch_tile_ring_mfma32(args, cus, stream); break;
     case kRing: err = launch_tile_ring(args, cus, stream); break;
     case kRingMasked: err = launch_tile_ring_masked(args, cus, stream); break;
-    case kSkinny: err = launch_skinny_plan(args, cus, stream); break;
+    case kSkinny: err = launch_skinny_plan(args, cus, scr, stream); break;
     default: err = launch_generic(args, cus, stream); break;
     }
     if (err != hipSuccess) {
@@ -611,6 +639,22 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t lda
         return GEMM_ERR_HIP;
     }
     return GEMM_OK;
+}
+
+}  // namespace gb
+
+extern "C" {
+
+int gemm_bf16(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t lda, const gemm_bf16_t *B,
+              int64_t ldb, gemm_bf16_t *C, int64_t ldc, float alpha, float beta, const gemm_bf16_t *bias,
+              int epilogue, hipStream_t stream) {
+    using namespace gb;
+    const int st = validate(M, N, K, A, lda, B, ldb, C, ldc, epilogue);
+    if (st != GEMM_OK) return st;
+    if (M == 0 || N == 0) return GEMM_OK;
+    const int cus = device_cu_count();
+    return run_bf16(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, bias, epilogue, stream_scratch(cus), cus,
+                    stream);
 }
 
 int gemm_bf16_q8(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t lda, const gemm_bf16_t *B,
@@ -642,12 +686,13 @@ int gemm_bf16_q8(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t 
     args.zp = (float)zero_point;
 
     const int cus = device_cu_count();
+    const Scratch scr = stream_scratch(cus);
     hipError_t err = hipSuccess;
-    switch (choose_kernel_q8(M, N, K, A, lda, B, ldb, C, ldc, beta, Q, ldq, scale, cus)) {
+    switch (choose_kernel_q8(M, N, K, A, lda, B, ldb, C, ldc, beta, Q, ldq, scale, cus, scr.cap_floats)) {
     case kRingQ8: err = launch_tile_ring_q8(args, cus, stream); break;
     case kRingQ8Masked: err = launch_tile_ring_q8_masked(args, cus, stream); break;
-    case kSkinnyQ8: err = launch_skinny_plan(args, cus, stream, false, true); break;
-    case kSplitKQ8: err = launch_splitk_plan(args, cus, stream, true); break;
+    case kSkinnyQ8: err = launch_skinny_plan(args, cus, scr, stream, false, true); break;
+    case kSplitKQ8: err = launch_splitk_plan(args, cus, scr, stream, true); break;
     default: err = launch_generic(args, cus, stream); break;
     }
     if (err != hipSuccess) {
@@ -663,7 +708,8 @@ const char *gemm_bf16_q8_kernel_name(int64_t M, int64_t N, int64_t K, const gemm
                                      int epilogue) {
     if (gb::validate_q8(M, N, K, A, lda, B, ldb, C, ldc, Q, ldq, beta, scale, epilogue) != GEMM_OK) return "none";
     return gb::kind_name(
-        gb::choose_kernel_q8(M, N, K, A, lda, B, ldb, C, ldc, beta, Q, ldq, scale, gb::device_cu_count()));
+        gb::choose_kernel_q8(M, N, K, A, lda, B, ldb, C, ldc, beta, Q, ldq, scale, gb::device_cu_count(),
+                             gb::stream_scratch(gb::device_cu_count()).cap_floats));
 }
 
 int gemm_fp8(int64_t M, int64_t N, int64_t K, const gemm_fp8_t *A, int64_t lda, const gemm_fp8_t *B,
@@ -692,16 +738,17 @@ int gemm_fp8(int64_t M, int64_t N, int64_t K, const gemm_fp8_t *A, int64_t lda, 
     args.scale_b = scale_b;
 
     const int cus = device_cu_count();
+    const Scratch scr = stream_scratch(cus);
     hipError_t err = hipSuccess;
-    switch (choose_kernel_fp8(M, N, K, A, lda, B, ldb, C, ldc)) {
+    switch (choose_kernel_fp8(M, N, K, A, lda, B, ldb, C, ldc, cus, scr.cap_floats)) {
     case kFp8: err = launch_tile_fp8(args, cus, stream); break;
-    case kFp8SplitK: err = launch_fp8_splitk_plan(args, cus, stream, false); break;
-    case kFp8SplitKMasked: err = launch_fp8_splitk_plan(args, cus, stream, true); break;
+    case kFp8SplitK: err = launch_fp8_splitk_plan(args, cus, scr, stream, false); break;
+    case kFp8SplitKMasked: err = launch_fp8_splitk_plan(args, cus, scr, stream, true); break;
     case kFp8Masked: err = launch_tile_fp8_mfma32_masked(args, cus, stream); break;
     case kFp8Mfma32: err = launch_tile_fp8_mfma32(args, cus, stream); break;
     case kFp8Mfma16Masked: err = launch_tile_fp8_mfma16_masked(args, cus, stream); break;
     case kGemvFp8: err = launch_gemv(args, stream, true); break;
-    case kSkinnyFp8: err = launch_skinny_plan(args, cus, stream, true); break;
+    case kSkinnyFp8: err = launch_skinny_plan(args, cus, scr, stream, true); break;
     default: err = launch_generic(args, cus, stream, true); break;
     }
     if (err != hipSuccess) {
@@ -715,7 +762,9 @@ const char *gemm_fp8_kernel_name(int64_t M, int64_t N, int64_t K, const gemm_fp8
                                  const gemm_fp8_t *B, int64_t ldb, const gemm_bf16_t *C, int64_t ldc,
                                  int epilogue) {
     if (gb::validate(M, N, K, A, lda, B, ldb, C, ldc, epilogue) != GEMM_OK) return "none";
-    return gb::kind_name(gb::choose_kernel_fp8(M, N, K, A, lda, B, ldb, C, ldc));
+    const int cus = gb::device_cu_count();
+    return gb::kind_name(
+        gb::choose_kernel_fp8(M, N, K, A, lda, B, ldb, C, ldc, cus, gb::stream_scratch(cus).cap_floats));
 }
 
 const char *gemm_bf16_status_string(int status) {
@@ -738,7 +787,8 @@ const char *gemm_bf16_kernel_name(int64_t M, int64_t N, int64_t K, const gemm_bf
     (void)beta;
     (void)bias;
     if (gb::validate(M, N, K, A, lda, B, ldb, C, ldc, epilogue) != GEMM_OK) return "none";
-    return gb::kind_name(gb::choose_kernel(M, N, K, A, lda, B, ldb, C, ldc, gb::device_cu_count()));
+    const int cus = gb::device_cu_count();
+    return gb::kind_name(gb::choose_kernel(M, N, K, A, lda, B, ldb, C, ldc, cus, gb::stream_scratch(cus).cap_floats));
 }
 
 }  // extern "C"

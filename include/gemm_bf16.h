@@ -19,16 +19,19 @@
  *
  * Every function is thread-safe.  The library keeps no pointer to caller
  * buffers after a call returns.  Its one device allocation is the split-K
- * workspace (fp32 partial sums, and counters for the short-product kernel)
- * used by three kinds of shape: 3 <= M <= 64 with few columns, products
- * whose 128x128 tiles would leave most compute units idle (for example
- * 1024 x 1024 x 4096; with tails the partials are padded to whole tiles),
- * and FP8 products whose 256x256 tiles would.  It is one buffer per (device, stream), allocated
- * with hipMalloc and its counters zeroed with hipMemsetAsync on the first
- * call that needs it, grown (after synchronising that stream) when a later
- * call needs more, and kept until the process ends; it holds at most about
- * 16 MiB on a 256-CU device.  Calls whose shape needs no split allocate
- * nothing.
+ * workspace (fp32 partial sums, and arrival counters for the short-product
+ * kernel) used by three kinds of shape: 3 <= M <= 64 with few columns,
+ * products whose 128x128 tiles would leave most compute units idle (for
+ * example 1024 x 1024 x 4096; with tails the partials are padded to whole
+ * tiles), and FP8 products whose 256x256 tiles would.  It is one buffer per
+ * (device, stream) of a fixed size -- 64 KiB of counters plus 64 KiB per
+ * compute unit (16 MiB + 64 KiB on a 256-CU device) -- allocated with
+ * hipMalloc by the first call on that stream that splits K (its counters
+ * zeroed by a fill kernel on the stream), never grown or freed, and kept
+ * until the process ends; no split plan needs more, so no later call
+ * allocates, frees or synchronises.  Calls whose shape needs no split
+ * allocate nothing.  A first split call made under HIP graph capture fails
+ * with GEMM_ERR_HIP when the runtime refuses hipMalloc during capture.
  */
 #ifndef GEMM_BF16_H
 #define GEMM_BF16_H
@@ -176,8 +179,8 @@ int gemm_bf16_q8(int64_t M, int64_t N, int64_t K,
  * multiples with C 16-byte aligned and ldc % 8 == 0 run unmasked, anything
  * else accesses C element by element where it must).  When those tiles
  * would fill less than half of the compute units, K is split over up to
- * eight ranges (fp32 partial tiles in the split-K workspace, at most 16 MiB,
- * then an ordered reduction that applies the scales and the epilogue).
+ * eight ranges (fp32 partial tiles in the split-K workspace, then an
+ * ordered reduction that applies the scales and the epilogue).
  * Other inputs take the bounds-checked path (same result).
  */
 int gemm_fp8(int64_t M, int64_t N, int64_t K,
