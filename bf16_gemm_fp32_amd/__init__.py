@@ -14,7 +14,7 @@ import ctypes
 import os
 
 __all__ = [
-    "EPILOGUES", "GemmError", "LIB_PATH", "gemm", "gemm_bf16", "gemm_bf16_kernel_name",
+    "EPILOGUES", "GemmError", "LIB_PATH", "gemm", "gemm_bf16", "gemm_bf16_kernel_name", "gemm_bf16_noalloc",
     "gemm_bf16_last_hip_error", "gemm_bf16_q8", "gemm_bf16_q8_kernel_name", "gemm_bf16_status_string",
     "gemm_fp8", "gemm_fp8_kernel_name", "gemm_q8", "library",
 ]
@@ -46,6 +46,8 @@ def library() -> ctypes.CDLL:
     i64, vp, f32, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
     lib.gemm_bf16.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, f32, f32, vp, i32, vp]
     lib.gemm_bf16.restype = i32
+    lib.gemm_bf16_noalloc.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, f32, f32, vp, i32, vp]
+    lib.gemm_bf16_noalloc.restype = i32
     lib.gemm_bf16_status_string.argtypes = [i32]
     lib.gemm_bf16_status_string.restype = ctypes.c_char_p
     lib.gemm_bf16_last_hip_error.argtypes = []
@@ -69,6 +71,13 @@ def gemm_bf16(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, bias, epilogue, stre
     """Raw C-ABI call; pointers and the stream are integers (0 / None = NULL)."""
     return library().gemm_bf16(M, N, K, A or None, lda, B or None, ldb, C or None, ldc,
                                alpha, beta, bias or None, epilogue, stream or None)
+
+
+def gemm_bf16_noalloc(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, bias, epilogue, stream) -> int:
+    """Raw C-ABI call of the entry point that allocates nothing (split-K
+    scratch in the library's static device array; see the header)."""
+    return library().gemm_bf16_noalloc(M, N, K, A or None, lda, B or None, ldb, C or None, ldc,
+                                       alpha, beta, bias or None, epilogue, stream or None)
 
 
 def gemm_bf16_q8(M, N, K, A, lda, B, ldb, C, ldc, Q, ldq, alpha, beta, bias, epilogue, scale,

@@ -237,8 +237,10 @@ static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int cus, size_t c
 //    get their own.  (A stream handle that is destroyed and handed out again
 //    by the runtime finds the old buffer: work on the destroyed stream must
 //    have finished by then, as for any memory it used.)
+//  * gemm_bf16_noalloc: the library's static device array (below), shared
+//    by every such call on the device.
 struct Scratch {
-    char *fixed = nullptr;   // a caller-independent buffer to use instead (none yet)
+    char *fixed = nullptr;   // the static array's device address (no-allocation entry point)
     size_t cap_floats = 0;   // partial floats the buffer holds
 };
 
@@ -596,8 +598,45 @@ static int choose_kernel_fp8(int64_t M, int64_t N, int64_t K, const void *A, int
     return exact ? kFp8 : kFp8Masked;
 }
 
-// The bf16 product behind gemm_bf16 (arguments already validated, M, N >
-// 0); scr says where split-K partials go.
+// The no-allocation entry point's scratch: a file-scope device array of
+// the fixed split-K layout sized for 256 compute units (64 KiB of counters
+// and 16 MiB of partials).  Each GPU the library runs on holds its own copy
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// so its device address is looked up once per device (noalloc_scratch) and
+// only that address is handed to kernels.
+constexpr size_t kNoAllocCus = 256;
+constexpr size_t kNoAllocFloats = kNoAllocCus * kScratchFloatsPerCu;
+constexpr size_t kNoAllocBytes = kScratchCounterBytes + kNoAllocFloats * 4;
+static __device__ __align__(256) char scratch[kNoAllocBytes];
+
+static std::mutex g_noalloc_mutex;
+static char *g_noalloc_ptr[64];  // device address of `scratch`, per device, after set-up
+
+// Set-up on a device's first no-allocation call (with that device
+// current): look up the array's device address and zero its counters with
+// a fill kernel on the caller's stream.  The streaming kernel's last unit
+// of each strip resets that strip's counter, so they stay zero between
+// calls.
+static hipError_t noalloc_scratch(hipStream_t stream, Scratch *out) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_noalloc_mutex);
+    if (g_noalloc_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if ((err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return err;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        if ((err = zero_counters(reinterpret_cast<uint32_t *>(p), stream)) != hipSuccess) return err;
+        g_noalloc_ptr[dev] = static_cast<char *>(p);
+    }
+    out->fixed = g_noalloc_ptr[dev];
+    out->cap_floats = kNoAllocFloats;
+    return hipSuccess;
+}
+
+// The bf16 product behind gemm_bf16 and gemm_bf16_noalloc (arguments
+// already validated, M, N > 0); scr says where split-K partials go.
 static int run_bf16(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t lda, const gemm_bf16_t *B,
                     int64_t ldb, gemm_bf16_t *C, int64_t ldc, float alpha, float beta, const gemm_bf16_t *bias,
                     int epilogue, const Scratch &scr, int cus, hipStream_t stream) {
@@ -655,6 +694,22 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t lda
     const int cus = device_cu_count();
     return run_bf16(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, bias, epilogue, stream_scratch(cus), cus,
                     stream);
+}
+
+int gemm_bf16_noalloc(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t lda, const gemm_bf16_t *B,
+                      int64_t ldb, gemm_bf16_t *C, int64_t ldc, float alpha, float beta, const gemm_bf16_t *bias,
+                      int epilogue, hipStream_t stream) {
+    using namespace gb;
+    const int st = validate(M, N, K, A, lda, B, ldb, C, ldc, epilogue);
+    if (st != GEMM_OK) return st;
+    if (M == 0 || N == 0) return GEMM_OK;
+    Scratch scr;
+    const hipError_t err = noalloc_scratch(stream, &scr);
+    if (err != hipSuccess) {
+        t_last_hip_error = (int)err;
+        return GEMM_ERR_HIP;
+    }
+    return run_bf16(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, bias, epilogue, scr, device_cu_count(), stream);
 }
 
 int gemm_bf16_q8(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t lda, const gemm_bf16_t *B,

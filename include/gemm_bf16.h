@@ -31,7 +31,8 @@
  * until the process ends; no split plan needs more, so no later call
  * allocates, frees or synchronises.  Calls whose shape needs no split
  * allocate nothing.  A first split call made under HIP graph capture fails
- * with GEMM_ERR_HIP when the runtime refuses hipMalloc during capture.
+ * with GEMM_ERR_HIP when the runtime refuses hipMalloc during capture:
+ * callers that capture use gemm_bf16_noalloc.
  */
 #ifndef GEMM_BF16_H
 #define GEMM_BF16_H
@@ -111,6 +112,35 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K,
               float alpha, float beta,
               const gemm_bf16_t *bias,
               int epilogue, hipStream_t stream);
+
+/*
+ * gemm_bf16_noalloc -- gemm_bf16 for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, result, kernels and errors as
+ * gemm_bf16; it never calls hipMalloc, hipFree or any allocating routine.
+ *
+ * Its split-K scratch is a static device array inside the library (64 KiB
+ * of counters and 16 MiB of fp32 partials, sized for 256 compute units),
+ * one copy per GPU, held until the process ends.  Split plans are capped to
+ * fit it (on a device with more than 256 compute units a shape may split
+ * less than under gemm_bf16); a plan that would not fit is refused with
+ * GEMM_ERR_HIP (hipErrorInvalidValue) before anything is enqueued -- by
+ * construction no shape reaches that.  The first call on a device looks up
+ * the array and enqueues one small kernel that zeroes its counters; every
+ * later call enqueues only the product's kernels.
+ *
+ * All gemm_bf16_noalloc calls on one GPU share that one array, and it
+ * keeps the last call's contents: calls that may overlap on one GPU (on
+ * different streams, or from several threads without ordering) race on it
+ * and give undefined results.  Calls ordered on one stream are safe.
+ */
+int gemm_bf16_noalloc(int64_t M, int64_t N, int64_t K,
+                      const gemm_bf16_t *A, int64_t lda,
+                      const gemm_bf16_t *B, int64_t ldb,
+                      gemm_bf16_t *C, int64_t ldc,
+                      float alpha, float beta,
+                      const gemm_bf16_t *bias,
+                      int epilogue, hipStream_t stream);
 
 /*
  * gemm_bf16_q8 -- enqueue the same product and epilogue with an int8 output

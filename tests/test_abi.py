@@ -58,6 +58,29 @@ def test_argument_errors(args, want):
     assert call(*args) == want
 
 
+def call_noalloc(M, N, K, A=P, lda=None, B=P, ldb=None, C=P, ldc=None, alpha=1.0, beta=0.0, bias=0, epi=0):
+    lda = max(K, 1) if lda is None else lda
+    ldb = max(K, 1) if ldb is None else ldb
+    ldc = max(M, 1) if ldc is None else ldc
+    return gb.gemm_bf16_noalloc(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, bias, epi, 0)
+
+
+@pytest.mark.parametrize("args,want", [
+    ((-1, 4, 4), ERR_DIM), ((4, 4, 4, P, 3), ERR_LD), ((4, 4, 4, P, 4, P, 4, P, 3), ERR_LD),
+    ((4, 4, 4, 0), ERR_NULL), ((4, 4, 4, P, 4, P, 4, 0), ERR_NULL),
+    ((0, 4, 4), OK), ((4, 0, 4), OK),
+])
+def test_noalloc_argument_errors(args, want):
+    """The entry point that allocates nothing validates exactly as gemm_bf16,
+    before it touches its scratch (so these run without a GPU)."""
+    assert call_noalloc(*args) == want
+    assert call(*args) == want
+
+
+def test_noalloc_bad_epilogue():
+    assert call_noalloc(4, 4, 4, epi=7) == ERR_EPI
+
+
 def call_q8(M, N, K, A=P, lda=None, B=P, ldb=None, C=0, ldc=None, Q=P, ldq=None, alpha=1.0, beta=0.0,
             bias=0, epi=0, scale=P, zp=0):
     lda = max(K, 1) if lda is None else lda
