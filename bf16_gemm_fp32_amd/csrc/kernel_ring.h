@@ -73,7 +73,8 @@ struct RingConfig {
     static_assert(KSTEPS == 2 && FM == 8 && FN == 8 && kUnitLoads == 8,
                   "the slice schedule below is written for 2 k-steps of 64 MFMAs and 8 loads per unit");
     static_assert(kLdsBytes <= 160 * 1024, "gfx950 has 160 KiB of LDS per compute unit");
-    static_assert(kWaves * kEpiWaveBytes <= kLdsBytes, "epilogue staging reuses the ring");
+    static_assert(kWaves * kEpiWaveBytes <= 3 * kUnitBytes,
+                  "epilogue staging fits in slots 0-2, leaving slots 3-4 for the next tile's A(0), B(0)");
 };
 
 __device__ __forceinline__ int ring_swizzle(int row) { return (row >> 1) & 7; }
@@ -419,38 +420,63 @@ gemm_ring_kernel(const GemmArgs args, const TileSchedule sched) {
     const int nk = (int)((args.K + Cfg::BK - 1) / Cfg::BK);
     const int num_tiles = sched.num_tiles();
 
-    for (int t = sched.slot(blockIdx.x); t < num_tiles; t += sched.grid) {
+    // The tile a workgroup works on: its origin and operand buffers (and,
+    // masked, its valid rows and columns).
+    struct TileRef {
+        int64_t m0, n0;
+        __amdgpu_buffer_rsrc_t rA, rB;
+    };
+    auto tile_ref = [&](int t) {
         int tm, tn;
         sched.tile(t, tm, tn);
-        const int64_t m0 = (int64_t)tm * Cfg::BM;
-        const int64_t n0 = (int64_t)tn * Cfg::BN;
+        TileRef r;
+        r.m0 = (int64_t)tm * Cfg::BM;
+        r.n0 = (int64_t)tn * Cfg::BN;
+        r.rA = make_rsrc(args.A + r.m0 * args.lda, (uint32_t)(((Cfg::BM - 1) * args.lda + args.K) * 2));
+        r.rB = make_rsrc(args.B + r.n0 * args.ldb, (uint32_t)(((Cfg::BN - 1) * args.ldb + args.K) * 2));
         if constexpr (kMasked) {
-            Ln.rowsA = (int)(args.M - m0 < Cfg::BM ? args.M - m0 : Cfg::BM);
-            Ln.rowsB = (int)(args.N - n0 < Cfg::BN ? args.N - n0 : Cfg::BN);
+            Ln.rowsA = (int)(args.M - r.m0 < Cfg::BM ? args.M - r.m0 : Cfg::BM);
+            Ln.rowsB = (int)(args.N - r.n0 < Cfg::BN ? args.N - r.n0 : Cfg::BN);
         }
-        const __amdgpu_buffer_rsrc_t rA =
-            make_rsrc(args.A + m0 * args.lda, (uint32_t)(((Cfg::BM - 1) * args.lda + args.K) * 2));
-        const __amdgpu_buffer_rsrc_t rB =
-            make_rsrc(args.B + n0 * args.ldb, (uint32_t)(((Cfg::BN - 1) * args.ldb + args.K) * 2));
+        return r;
+    };
+    // A(0) and B(0) of a tile into ring slots s0 and s0 + 1.
+    auto load_first = [&](const TileRef &r, int s0) {
+#pragma unroll
+        for (int l = 0; l < Cfg::kUnitLoads; ++l) RK::template load<true>(smem, s0, 0, l, Ln, r.rA);
+#pragma unroll
+        for (int l = 0; l < Cfg::kUnitLoads; ++l) RK::template load<false>(smem, ring_slot(s0 + 1), 0, l, Ln, r.rB);
+    };
 
+    int t = sched.slot(blockIdx.x);
+    if (t >= num_tiles) return;  // the host launches at most one workgroup per tile
+    TileRef cur = tile_ref(t);
+    // The first tile's ring starts at slot 0; every later tile's A(0) and
+    // B(0) are loaded into slots 3 and 4 while the previous tile's epilogue
+    // stages its results in the low slots (the persistent kernel's store of
+    // tile i overlapping the loads of tile i+1, "Outperforming cuBLAS on H100:
+    // a worklog", Kernel 6), so its ring starts at slot 3.
+    int s0 = 0;
+    load_first(cur, s0);
+
+    for (;;) {
         f32x4 acc[Cfg::FM][Cfg::FN];
 #pragma unroll
         for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
             for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        // The previous tile's epilogue is done with LDS.
-        lds_barrier();
-        // Prologue: A(0) -> slot 0, B(0) -> 1, A(1) -> 2, B(1) -> 3.
-#pragma unroll
-        for (int l = 0; l < Cfg::kUnitLoads; ++l) RK::template load<true>(smem, 0, 0, l, Ln, rA);
-#pragma unroll
-        for (int l = 0; l < Cfg::kUnitLoads; ++l) RK::template load<false>(smem, 1, 0, l, Ln, rB);
+        // Prologue: A(1), B(1) behind A(0), B(0).  Vector memory operations
+        // complete in issue order, so once at most A(1) and B(1) are
+        // outstanding, A(0) and B(0) -- and everything the previous
+        // epilogue stored -- have landed.
         if (nk >= 2) {
 #pragma unroll
-            for (int l = 0; l < Cfg::kUnitLoads; ++l) RK::template load<true>(smem, 2, 1, l, Ln, rA);
+            for (int l = 0; l < Cfg::kUnitLoads; ++l)
+                RK::template load<true>(smem, ring_slot(s0 + 2), 1, l, Ln, cur.rA);
 #pragma unroll
-            for (int l = 0; l < Cfg::kUnitLoads; ++l) RK::template load<false>(smem, 3, 1, l, Ln, rB);
+            for (int l = 0; l < Cfg::kUnitLoads; ++l)
+                RK::template load<false>(smem, ring_slot(s0 + 3), 1, l, Ln, cur.rB);
             wait_vmcnt<2 * Cfg::kUnitLoads>();
         } else {
             wait_vmcnt<0>();
@@ -458,8 +484,8 @@ gemm_ring_kernel(const GemmArgs args, const TileSchedule sched) {
         lds_barrier();
         bf16x8 fa[2][Cfg::FM], fb[2][Cfg::FN];
         {
-            const char *sA = smem;
-            const char *sB = smem + Cfg::kUnitBytes;
+            const char *sA = smem + s0 * Cfg::kUnitBytes;
+            const char *sB = smem + ring_slot(s0 + 1) * Cfg::kUnitBytes;
 #pragma unroll
             for (int i = 0; i < Cfg::FM; ++i)
                 fa[0][i] = *(const GB_LDS bf16x8 *)(sA + Ln.aRow + i * 16 * Cfg::kRowBytes + Ln.chunk_off[0]);
@@ -471,27 +497,42 @@ gemm_ring_kernel(const GemmArgs args, const TileSchedule sched) {
         // compiler sees), so the loop's LDS-read waits stay exact.
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
 
-        int j = 0, sa = 0;
+        int j = 0, sa = s0;
         for (; j + 2 < nk; ++j) {
-            RK::template slice<0>(smem, j, sa, Ln, rA, rB, fa, fb, acc, [] {});
+            RK::template slice<0>(smem, j, sa, Ln, cur.rA, cur.rB, fa, fb, acc, [] {});
             sa = ring_slot(sa + 2);
         }
         if (j + 1 < nk) {
-            RK::template slice<1>(smem, j, sa, Ln, rA, rB, fa, fb, acc, [] {});
+            RK::template slice<1>(smem, j, sa, Ln, cur.rA, cur.rB, fa, fb, acc, [] {});
             ++j;
             sa = ring_slot(sa + 2);
         }
         // The epilogue's first C / bias values load during the last k-step.
         RingEpiInputs epi_in;
-        RK::template slice<2>(smem, j, sa, Ln, rA, rB, fa, fb, acc, [&] {
+        RK::template slice<2>(smem, j, sa, Ln, cur.rA, cur.rB, fa, fb, acc, [&] {
             if constexpr ((kFlags & (kEpiBeta | kEpiBias)) != 0)
-                ring_epi_load<kFlags, kMasked>(epi_in, args, m0, n0, wm, wn, lane, 0);
+                ring_epi_load<kFlags, kMasked>(epi_in, args, cur.m0, cur.n0, wm, wn, lane, 0);
         });
 
         // Every wave is done reading the ring (all loads landed at the last
-        // wait): its memory now stages the epilogue.
+        // wait): its low slots now stage the epilogue, and the next tile's
+        // first units go into slots 3 and 4, which the staging leaves free.
         lds_barrier();
-        ring_epilogue<kFlags, kMasked, kQ8>(smem, args, m0, n0, wm, wn, lane, Ln.wave, acc, epi_in);
+        const int t_next = t + sched.grid;
+        const bool more = t_next < num_tiles;
+        TileRef next = cur;
+        if (more) {
+            next = tile_ref(t_next);
+            load_first(next, 3);
+        }
+        ring_epilogue<kFlags, kMasked, kQ8>(smem, args, cur.m0, cur.n0, wm, wn, lane, Ln.wave, acc, epi_in);
+        if (!more) break;
+        // The staging slots are free again before the next prologue loads
+        // into them.
+        lds_barrier();
+        t = t_next;
+        cur = next;
+        s0 = 3;
     }
 }
 
