@@ -133,13 +133,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // GELU, tanh form: 0.5 y (1 + tanh(u)), u = sqrt(2/pi) (y + 0.044715 y^3).
 // Uses the identity 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)), evaluated with
-// the hardware base-2 exponential and reciprocal.  Both limits are exact:
-// exp -> inf gives y * 0 (large negative y), exp -> 0 gives y.
+// the hardware base-2 exponential and reciprocal, and folds the constants
+// so that -2u log2(e) = y (c1 + c3 y^2): one multiply, one fused multiply-add
+// and one multiply before the exponential.  Both limits are exact: exp ->
+// inf gives y * 0 (large negative y), exp -> 0 gives y.
 __device__ __forceinline__ float gelu_tanh_f32(float y) {
-    const float kSqrt2OverPi = 0.7978845608028654f;
-    const float kLog2e = 1.4426950408889634f;
-    float u = kSqrt2OverPi * (y + 0.044715f * y * y * y);
-    float e = __builtin_amdgcn_exp2f(-2.0f * kLog2e * u);
+    // c1 = -2 log2(e) sqrt(2/pi), c3 = 0.044715 c1
+    const float kC1 = -2.30220819814432500f;
+    const float kC3 = -0.10294323958002350f;
+    const float y2 = y * y;
+    const float e = __builtin_amdgcn_exp2f(y * __builtin_fmaf(kC3, y2, kC1));
     return y * __builtin_amdgcn_rcpf(1.0f + e);
 }
 

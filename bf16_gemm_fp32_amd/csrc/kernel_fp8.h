@@ -415,8 +415,6 @@ hipError_t launch_fp8_ring(const GemmArgs &args, int cus, hipStream_t stream) {
     s.tiles_m = (int)((args.M + Fp8Config::BM - 1) / Fp8Config::BM);
     s.tiles_n = (int)((args.N + Fp8Config::BN - 1) / Fp8Config::BN);
     s.group_m = 4;
-    s.order = kOrderGrouped;
-    s.hilbert_log2 = 0;
     const int tiles = s.num_tiles();
     s.grid = tiles < cus ? tiles : cus;
     const dim3 grid(s.grid), block(Fp8Config::kThreads);
@@ -439,8 +437,6 @@ hipError_t launch_fp8_splitk(const GemmArgs &args, const TileSplit &split, int c
     s.tiles_m = (int)((args.M + Fp8Config::BM - 1) / Fp8Config::BM);
     s.tiles_n = (int)((args.N + Fp8Config::BN - 1) / Fp8Config::BN);
     s.group_m = 4;
-    s.order = kOrderGrouped;
-    s.hilbert_log2 = 0;
     const int units = s.num_tiles() * split.splits;
     s.grid = units < cus ? units : cus;
     hipLaunchKernelGGL((gemm_fp8_kernel<0u, kMasked, true>), dim3(s.grid), dim3(Fp8Config::kThreads), 0, stream,

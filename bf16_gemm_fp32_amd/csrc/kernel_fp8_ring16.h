@@ -313,8 +313,6 @@ hipError_t launch_fp8_ring16(const GemmArgs &args, int cus, hipStream_t stream) 
     s.tiles_m = (int)((args.M + Fp8Ring16Config::BM - 1) / Fp8Ring16Config::BM);
     s.tiles_n = (int)((args.N + Fp8Ring16Config::BN - 1) / Fp8Ring16Config::BN);
     s.group_m = 4;
-    s.order = kOrderGrouped;
-    s.hilbert_log2 = 0;
     const int tiles = s.num_tiles();
     s.grid = tiles < cus ? tiles : cus;
     const dim3 grid(s.grid), block(Fp8Ring16Config::kThreads);

@@ -553,8 +553,6 @@ inline TileSchedule ring_schedule(const GemmArgs &args, int cus) {
     s.tiles_m = (int)((args.M + RingConfig::BM - 1) / RingConfig::BM);
     s.tiles_n = (int)((args.N + RingConfig::BN - 1) / RingConfig::BN);
     s.group_m = 4;
-    s.order = kOrderGrouped;
-    s.hilbert_log2 = 0;
     const int tiles = s.num_tiles();
     s.grid = tiles < cus ? tiles : cus;
     return s;

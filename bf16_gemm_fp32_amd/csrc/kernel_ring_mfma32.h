@@ -265,8 +265,6 @@ inline hipError_t launch_ring32(const GemmArgs &args, int cus, hipStream_t strea
     s.tiles_m = (int)(args.M / Ring32Config::BM);
     s.tiles_n = (int)(args.N / Ring32Config::BN);
     s.group_m = 4;
-    s.order = kOrderGrouped;
-    s.hilbert_log2 = 0;
     const int tiles = s.num_tiles();
     s.grid = tiles < cus ? tiles : cus;
     const dim3 grid(s.grid), block(Ring32Config::kThreads);

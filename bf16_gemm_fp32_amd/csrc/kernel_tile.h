@@ -592,8 +592,6 @@ hipError_t launch_tile(const GemmArgs &args, int cus, hipStream_t stream) {
     s.tiles_m = (int)((args.M + Cfg::BM - 1) / Cfg::BM);
     s.tiles_n = (int)((args.N + Cfg::BN - 1) / Cfg::BN);
     s.group_m = 4;
-    s.order = kOrderGrouped;
-    s.hilbert_log2 = 0;
     const int tiles = s.num_tiles();
     s.grid = tiles < cus ? tiles : cus;
     const dim3 grid(s.grid), block(Cfg::kThreads);
@@ -618,8 +616,6 @@ hipError_t launch_tile_splitk(const GemmArgs &args, const TileSplit &split, int 
     s.tiles_m = (int)((args.M + Cfg::BM - 1) / Cfg::BM);
     s.tiles_n = (int)((args.N + Cfg::BN - 1) / Cfg::BN);
     s.group_m = 4;
-    s.order = kOrderGrouped;
-    s.hilbert_log2 = 0;
     const int units = s.num_tiles() * split.splits;
     s.grid = units < cus ? units : cus;
     hipLaunchKernelGGL((gemm_tile_kernel<Cfg, 0u, true, kMasked>), dim3(s.grid), dim3(Cfg::kThreads), 0, stream, args,

@@ -1,7 +1,6 @@
 // Host check of tile_schedule.h: for many (tiles_m, tiles_n, group_m, grid)
-// the persistent schedule must visit every tile exactly once, the XCD slot
-// map must be a bijection, and the Hilbert walk must visit every in-grid
-// cell once.  Prints one line per failure and "OK" at the end.
+// the persistent schedule must visit every tile exactly once and the XCD
+// slot map must be a bijection.  Prints one line per failure and "OK" at the end.
 // Also prints, for the 4096^3 launch (16x16 tiles of 256, grid 256), how
 // many distinct tile-rows and tile-columns each XCD touches in round 0.
 #include <cstdio>
@@ -20,7 +19,6 @@ static void check(int tm_, int tn_, int gm, int grid) {
     s.tiles_n = tn_;
     s.group_m = gm;
     s.grid = grid;
-    s.order = gb::kOrderGrouped;
     std::vector<int> slot_seen(grid, 0);
     for (int w = 0; w < grid; ++w) {
         int sl = s.slot(w);
@@ -48,22 +46,6 @@ static void check(int tm_, int tn_, int gm, int grid) {
             ++failures;
             return;
         }
-    // Hilbert walk over the same grid
-    gb::HilbertWalker hw{-1, gb::ceil_log2(tm_ > tn_ ? tm_ : tn_), tm_, tn_};
-    std::vector<int> hseen(tm_ * tn_, 0);
-    int a, b, count = 0;
-    while (hw.advance(1, a, b)) {
-        if (hseen[a * tn_ + b]++) {
-            std::printf("hilbert visits twice: %dx%d (%d,%d)\n", tm_, tn_, a, b);
-            ++failures;
-            return;
-        }
-        ++count;
-    }
-    if (count != tm_ * tn_) {
-        std::printf("hilbert misses cells: %dx%d got %d\n", tm_, tn_, count);
-        ++failures;
-    }
 }
 
 int main() {
@@ -78,7 +60,7 @@ int main() {
                     check(a, b, g, grid < tiles ? grid : tiles);
                 }
     // locality of the 4096^3 launch
-    TileSchedule s{16, 16, 4, 256, gb::kOrderGrouped, 0};
+    TileSchedule s{16, 16, 4, 256};
     for (int x = 0; x < gb::kNumXcds; ++x) {
         std::set<int> rows, cols;
         for (int w = x; w < 256; w += gb::kNumXcds) {

@@ -1,6 +1,6 @@
 """Host build of the tile scheduler header (the same file the kernels use):
 bijection of the XCD slot map, every tile visited exactly once for many grid
-shapes, Hilbert walk coverage, and XCD locality of the 4096^3 launch."""
+shapes, and XCD locality of the 4096^3 launch."""
 import os
 import subprocess
 
