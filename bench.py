@@ -57,11 +57,17 @@ def log(msg):
 
 
 def cpu_threads():
+    """Host threads for the CPU oracle: every core in this process's affinity
+    mask, capped by the host's allotment for this GPU when one is set
+    (OMP_NUM_THREADS; 16 cores per GPU on the MI355X boxes)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
         n = os.cpu_count() or 1
-    return max(1, min(16, n))
+    allot = os.environ.get("OMP_NUM_THREADS", "")
+    if allot.isdigit() and int(allot) > 0:
+        n = min(n, int(allot))
+    return max(1, n)
 
 
 def cpu_model():
@@ -109,9 +115,10 @@ def cpu_baseline(w, d, budget_cols=None):
     }
 
 
-def measured_traffic(workload, kernel):
-    """HBM bytes per launch from the recorded counter passes, or None when no
-    record matches this kernel, workload and source digest."""
+def measured_record(workload, kernel):
+    """The recorded counter passes for this kernel and workload (HBM bytes
+    per launch, achieved clock, MFMA busy, ...), or None when no record
+    matches this kernel, workload and library source digest."""
     from bf16_gemm_fp32_amd.build import source_digest
     try:
         with open(TRAFFIC_FILE) as f:
@@ -121,8 +128,26 @@ def measured_traffic(workload, kernel):
     digest = source_digest()
     for e in rec.get("entries", []):
         if e.get("workload") == workload and e.get("kernel") == kernel and e.get("source_digest") == digest:
-            return e.get("hbm_bytes_per_launch")
+            return e
     return None
+
+
+def device_info(torch):
+    """Compute units and clocks of device 0 (HIP device attributes)."""
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "cus": p.multi_processor_count,
+            "max_sclk_mhz": None}
+    try:
+        import ctypes
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        # hipDeviceAttributeClockRate (kHz)
+        attr = 5
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, 0) == 0 and v.value > 0:
+            info["max_sclk_mhz"] = v.value / 1000.0
+    except OSError:
+        pass
+    return info
 
 
 def run_workload(w, steps, warmup, cold, with_cpu):
@@ -224,7 +249,8 @@ def run_workload(w, steps, warmup, cold, with_cpu):
     log(f"[bench] per-launch event pairs ms: mean {statistics.fmean(per):.4f} min {min(per):.4f} "
         f"median {statistics.median(per):.4f} max {max(per):.4f}")
 
-    traffic = measured_traffic(w.name, kname)
+    rec = measured_record(w.name, kname)
+    traffic = rec.get("hbm_bytes_per_launch") if rec else None
     if w.bound == "hbm":
         roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                 "traffic": traffic}
@@ -260,6 +286,15 @@ def run_workload(w, steps, warmup, cold, with_cpu):
         "timed_region_wall_ms": wall * 1e3,
         "timed_region_event_ms": region_ms,
         "roofline": roof,
+        "device": device_info(torch),
+        # from the recorded counter passes of this kernel and workload at this
+        # library build (null when none match): the achieved clock between
+        # SQ_BUSY_CYCLES per shader engine and GRBM_GUI_ACTIVE per XCD over the
+        # kernel time, MFMA busy cycles over the SIMD cycles, L2 hit rate and
+        # LDS bank-conflict cycles per LDS instruction
+        "profiled": ({k: rec.get(k) for k in ("sclk_mhz_lower", "sclk_mhz_upper", "mfma_busy", "mfma_busy_upper",
+                                              "l2_hit", "lds_bank_conflict_per_lds_inst", "summary")}
+                     if rec else None),
         "cpu_baseline": None,
     }
     if with_cpu:
