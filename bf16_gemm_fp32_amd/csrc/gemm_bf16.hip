@@ -588,8 +588,9 @@ static int choose_kernel_fp8(int64_t M, int64_t N, int64_t K, const void *A, int
     if (force && !std::strcmp(force, kKindNames[kFp8])) return exact ? kFp8 : kFp8Masked;
     if (force && !std::strcmp(force, kKindNames[kFp8Mfma16Masked])) return kFp8Mfma16Masked;
     if (force && !std::strcmp(force, kKindNames[kFp8Mfma32])) return exact ? kFp8Mfma32 : kFp8Masked;
-    // small grids: split K (the reduction needs C aligned and ldc % 8, both
-    // implied; it writes a chunk that straddles M element by element)
+    // small grids: split K (the reduction takes any C: it reads and writes a
+    // chunk element by element where ldc % 8 != 0, C is unaligned or the
+    // chunk straddles M)
     const bool can_split = plan_splitk_fp8(M, N, K, cus, cap_floats).splits >= 2;
     if (force && can_split &&
         (!std::strcmp(force, kKindNames[kFp8SplitK]) || !std::strcmp(force, kKindNames[kFp8SplitKMasked])))

@@ -99,7 +99,12 @@ struct Fp8Ring16Kernel {
 
     // DMA load number l (0..7) of this wave for one operand unit: rows
     // 8q .. 8q+7 of the tile, q = 8 * wave + l, K-slice kt, into the slot.
-    // A slice past the end of K (kt >= nk) gets the out-of-range offset.
+    // A slice past the end of K (kt >= nk) is loaded from the out-of-range
+    // offset, which the buffer unit turns into zeros without touching
+    // memory.  That offset goes into the per-lane voffset, which the range
+    // check covers; the scalar offset stays the in-range row offset (its
+    // sum with the out-of-range voffset stays below 2^32, so nothing wraps
+    // back into range).
     template <bool kIsA>
     __device__ __forceinline__ static void load(char *smem, int slot, int kt, int l, const Lane &L,
                                                 __amdgpu_buffer_rsrc_t rsrc) {
@@ -111,9 +116,10 @@ struct Fp8Ring16Kernel {
             const int k = kt * Cfg::BK + L.lchunk[q & 1] * 16;
             if (!(row < (kIsA ? L.rowsA : L.rowsB) && k < L.kmax)) voff = kOobOffset;
         }
-        const uint32_t koff = kt < L.nk ? (uint32_t)kt * Cfg::kRowBytes : kOobOffset;
+        const bool in_k = kt < L.nk;
+        if (!in_k) voff = kOobOffset;
         buffer_load_lds16(rsrc, (GB_LDS void *)(smem + slot * Cfg::kUnitBytes + q * 1024), voff,
-                          (uint32_t)(q * Cfg::kRowsPerLoad) * ld + koff);
+                          (uint32_t)(q * Cfg::kRowsPerLoad) * ld + (in_k ? (uint32_t)kt * Cfg::kRowBytes : 0u));
     }
 
     // One 16-byte half of fragment f (16-row block f of the wave's rows).
