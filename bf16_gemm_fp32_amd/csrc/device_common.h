@@ -48,11 +48,14 @@ struct GemmArgs {
 
 // The K split of the tile kernel: `splits` ranges of `kper` K-slices (the
 // last may be shorter, none is empty); partial s of the element (m, n) is
-// P[s * pstride + n * ldp + m].
+// P[s * pstride + n * ldp + m].  tile_major: work unit u is tile u / splits,
+// range u % splits (a tile's ranges in consecutive units, so on one XCD);
+// otherwise range u / tiles, tile u % tiles.
 struct TileSplit {
     float *P;
     int64_t ldp, pstride;
     int splits, kper;
+    int tile_major;
 };
 
 // Call f(std::integral_constant<uint32_t, flags>) for the run-time flag word,

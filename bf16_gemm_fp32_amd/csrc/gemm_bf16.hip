@@ -343,6 +343,13 @@ static TileSplit plan_splitk(int64_t M, int64_t N, int64_t K, int cus, size_t ca
     p.splits = (int)((nk + p.kper - 1) / p.kper);  // no empty range
     p.ldp = ldp;
     p.pstride = pstride;
+    // A tile's ranges on one XCD when every unit has its own workgroup and
+    // each XCD's share of them is whole tiles: the reduction then reads a
+    // tile's partials on the XCD that wrote them.
+    p.tile_major = tiles * p.splits <= cus && tiles % kNumXcds == 0;
+    if (const char *env = std::getenv("GEMM_BF16_SPLITK_COLOCATE")) {  // tuning knob: 0 = range-major units
+        if (env[0] == '0') p.tile_major = 0;
+    }
     return p;
 }
 

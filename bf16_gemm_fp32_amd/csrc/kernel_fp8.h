@@ -439,6 +439,7 @@ hipError_t launch_fp8_splitk(const GemmArgs &args, const TileSplit &split, int c
     s.group_m = 4;
     const int units = s.num_tiles() * split.splits;
     s.grid = units < cus ? units : cus;
+    // the FP8 units are range-major (split.tile_major is 0 on this path)
     hipLaunchKernelGGL((gemm_fp8_kernel<0u, kMasked, true>), dim3(s.grid), dim3(Fp8Config::kThreads), 0, stream,
                        args, s, split);
     hipError_t err = hipGetLastError();
@@ -448,8 +449,8 @@ hipError_t launch_fp8_splitk(const GemmArgs &args, const TileSplit &split, int c
     const int64_t cap = (int64_t)cus * 8;
     const dim3 rgrid((unsigned)(blocks < cap ? blocks : cap));
     dispatch_flags(args.flags, [&](auto f) {
-        hipLaunchKernelGGL((splitk_reduce_kernel<decltype(f)::value, false>), rgrid, dim3(256), 0, stream, args,
-                           split);
+        hipLaunchKernelGGL((splitk_reduce_kernel<decltype(f)::value, false, Fp8Config::BM, Fp8Config::BN>), rgrid,
+                           dim3(256), 0, stream, args, split, s);
     });
     return hipGetLastError();
 }

@@ -416,8 +416,13 @@ gemm_tile_kernel(const GemmArgs args, const TileSchedule sched, const TileSplit 
     for (int u = sched.slot(blockIdx.x); u < num_units; u += sched.grid) {
         int t = u, s = 0, nk = nk_all;
         if constexpr (kSplit) {
-            s = u / num_tiles;
-            t = u - s * num_tiles;
+            if (split.tile_major) {
+                t = u / split.splits;
+                s = u - t * split.splits;
+            } else {
+                s = u / num_tiles;
+                t = u - s * num_tiles;
+            }
             const int rest = nk_all - s * split.kper;
             nk = rest < split.kper ? rest : split.kper;
         }
@@ -494,13 +499,47 @@ gemm_tile_kernel(const GemmArgs args, const TileSchedule sched, const TileSplit 
 // int8 Q.  Requires M % 8 == 0, C 16-byte aligned and ldc % 8 == 0 (when C
 // is read or written), and for kQ8 Q and scale 16-byte aligned and
 // ldq % 8 == 0 (checked on the host).
-template <uint32_t kFlags, bool kQ8 = false>
-__global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs args, const TileSplit split) {
+//
+// Which thread takes which chunk.  Without tile_major, chunk idx of the
+// column-major chunk order (grid-stride).  With tile_major (kTileM x kTileN
+// tiles, the split units of a tile consecutive, so on one XCD: the host
+// launched one tile kernel workgroup per unit, a multiple of 8 of them, each
+// XCD's share holding whole tiles), block b reduces part of a tile of the
+// units on XCD b mod 8 -- the same XCD under the round-robin dispatch of
+// workgroups to XCDs, so its partials are read from that XCD's L2 where they
+// are still held.  Both mappings give the same sums in the same order.
+template <uint32_t kFlags, bool kQ8 = false, int kTileM = 128, int kTileN = 128>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs args, const TileSplit split,
+                                                            const TileSchedule sched) {
+    constexpr int kTileChunks = kTileM / 8 * kTileN;  // 8-row chunks of a tile
+    constexpr int kBlocksPerTile = kTileChunks / 256;
+    static_assert(kTileChunks % 256 == 0, "whole blocks per tile");
     const int64_t chunks_m = (args.M + 7) / 8;
-    const int64_t total = chunks_m * args.N;
-    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
-        const int64_t n = idx / chunks_m;
-        const int64_t m = (idx - n * chunks_m) * 8;
+    int64_t total = chunks_m * args.N, step = (int64_t)gridDim.x * 256;
+    int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    int64_t tm0 = 0, tn0 = 0;
+    if (split.tile_major) {
+        const int x = blockIdx.x % kNumXcds, j = blockIdx.x / kNumXcds;
+        const int tiles_per_xcd = sched.grid / kNumXcds / split.splits;
+        const int t = x * tiles_per_xcd + j / kBlocksPerTile;
+        int tm, tn;
+        sched.tile(t, tm, tn);
+        tm0 = (int64_t)tm * kTileM;
+        tn0 = (int64_t)tn * kTileN;
+        idx = (int64_t)(j % kBlocksPerTile) * 256 + threadIdx.x;  // chunk within the tile
+        total = idx + 1;  // one chunk per thread
+        step = 1;
+    }
+    for (; idx < total; idx += step) {
+        int64_t n, m;
+        if (split.tile_major) {
+            n = tn0 + idx / (kTileM / 8);
+            m = tm0 + (idx % (kTileM / 8)) * 8;
+            if (n >= args.N || m >= args.M) break;  // past the matrix in a tail tile
+        } else {
+            n = idx / chunks_m;
+            m = (idx - n * chunks_m) * 8;
+        }
         // Loads of four ranges go out before their sums, so the memory
         // latency is paid once per four ranges; the adds keep range order.
         const float *p = split.P + n * split.ldp + m;
@@ -625,10 +664,12 @@ hipError_t launch_tile_splitk(const GemmArgs &args, const TileSplit &split, int 
     const int64_t threads = (args.M + 7) / 8 * args.N;
     const int64_t blocks = (threads + 255) / 256;
     const int64_t cap = (int64_t)cus * 8;
-    const dim3 rgrid((unsigned)(blocks < cap ? blocks : cap));
+    // tile_major: one block per 256 chunks of every tile, in XCD order
+    const int64_t tile_blocks = (int64_t)s.num_tiles() * (Cfg::BM / 8 * Cfg::BN / 256);
+    const dim3 rgrid((unsigned)(split.tile_major ? tile_blocks : (blocks < cap ? blocks : cap)));
     dispatch_flags(args.flags, [&](auto f) {
-        hipLaunchKernelGGL((splitk_reduce_kernel<decltype(f)::value, kQ8>), rgrid, dim3(256), 0, stream, args,
-                           split);
+        hipLaunchKernelGGL((splitk_reduce_kernel<decltype(f)::value, kQ8, Cfg::BM, Cfg::BN>), rgrid, dim3(256), 0,
+                           stream, args, split, s);
     });
     return hipGetLastError();
 }
