@@ -46,6 +46,8 @@
 // article (section 3.2), redone for this row width and lane-to-phase map.
 #pragma once
 
+#include <cstdlib>
+
 #include "device_common.h"
 #include "tile_schedule.h"
 
@@ -548,11 +550,20 @@ hipError_t launch_ring_t(const GemmArgs &args, const TileSchedule &s, hipStream_
     return hipGetLastError();
 }
 
+// The ring's schedule: grouped order with GROUP_M = 4 and the XCD slot
+// remap.  GEMM_BF16_GROUP_M (1 .. 64) and GEMM_BF16_XCD_REMAP=0 override them;
+// they exist to measure those two choices (the results stay correct under
+// any order).
 inline TileSchedule ring_schedule(const GemmArgs &args, int cus) {
     TileSchedule s{};
     s.tiles_m = (int)((args.M + RingConfig::BM - 1) / RingConfig::BM);
     s.tiles_n = (int)((args.N + RingConfig::BN - 1) / RingConfig::BN);
     s.group_m = 4;
+    if (const char *env = std::getenv("GEMM_BF16_GROUP_M")) {
+        const int g = std::atoi(env);
+        if (g >= 1 && g <= 64) s.group_m = g;
+    }
+    if (const char *env = std::getenv("GEMM_BF16_XCD_REMAP")) s.no_xcd_remap = env[0] == '0';
     const int tiles = s.num_tiles();
     s.grid = tiles < cus ? tiles : cus;
     return s;

@@ -49,14 +49,17 @@
 // Split-K.  When the tiles alone would leave most compute units idle (a
 // 1024 x 1024 output is 64 tiles of 128x128 for 256 compute units), the
 // K-slices are cut into `splits` contiguous ranges and a work unit is one
-// (range, tile) pair: unit u = s * tiles + t, so the units of one range run
-// side by side and the compute units of one XCD share their A rows and B
-// columns in L2.  A unit stores its fp32 partial tile to a workspace instead
-// of running the epilogue; splitk_reduce_kernel then adds the partials of
-// each element in range order (the same order on every run, so results are
-// deterministic) and applies the fused epilogue.  The partials cross XCDs,
-// whose L2s are not coherent with each other, so the reduction is a second
-// kernel on the same stream: the kernel boundary makes the partials visible.
+// (range, tile) pair.  When every unit has its own workgroup and each XCD's
+// share of them is whole tiles, units are tile-major (u = t * splits + s):
+// a tile's ranges then run on one XCD, and the reduction reads them there.
+// Otherwise they are range-major (u = s * tiles + t), so the units of one
+// range run side by side and share their A rows and B columns in L2.  A
+// unit stores its fp32 partial tile to a workspace instead of running the
+// epilogue; splitk_reduce_kernel then adds the partials of each element in
+// range order (the same order on every run, so results are deterministic)
+// and applies the fused epilogue.  It is a second kernel on the same stream:
+// the kernel boundary makes the partials visible whichever XCDs wrote them
+// (the XCDs' L2s are not coherent with each other).
 #pragma once
 
 #include "device_common.h"

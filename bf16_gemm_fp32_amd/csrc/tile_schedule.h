@@ -45,13 +45,14 @@ struct TileSchedule {
     int tiles_n;   // ceil(N / BN)
     int group_m;   // tile-rows per group (grouped order)
     int grid;      // number of persistent workgroups
+    int no_xcd_remap;  // nonzero: slot = workgroup id (for measuring the remap)
 
     GB_HD int num_tiles() const { return tiles_m * tiles_n; }
 
     // Slot of workgroup w under round-robin XCD dispatch.
     GB_HD int slot(int w) const {
         int per = grid / kNumXcds;
-        if (w >= per * kNumXcds) return w;
+        if (no_xcd_remap || w >= per * kNumXcds) return w;
         return (w % kNumXcds) * per + w / kNumXcds;
     }
 
