@@ -46,6 +46,8 @@ hipError_t launch_tile_medium_splitk_masked(const GemmArgs &args, const TileSpli
                                             hipStream_t stream);
 hipError_t launch_tile_ring_mfma32(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_ring(const GemmArgs &args, int cus, hipStream_t stream);
+// the same tiles on eight waves of 128x64, two per SIMD (chosen only when forced)
+hipError_t launch_tile_ring_w8(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_ring_masked(const GemmArgs &args, int cus, hipStream_t stream);
 // int8 output: exact tile multiples, and shapes with tails (masked)
 hipError_t launch_tile_ring_q8(const GemmArgs &args, int cus, hipStream_t stream);

@@ -20,7 +20,7 @@
 namespace gb {
 
 enum KernelKind {
-    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8Mfma32, kSplitK, kGemv, kSplitKQ8, kFp8Masked, kGemvFp8, kSkinnyFp8, kFp8SplitK, kRingQ8Masked, kSkinnyQ8, kMediumMasked, kSplitKMasked, kFp8SplitKMasked, kFp8, kFp8Mfma16Masked, kNumKinds
+    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8Mfma32, kSplitK, kGemv, kSplitKQ8, kFp8Masked, kGemvFp8, kSkinnyFp8, kFp8SplitK, kRingQ8Masked, kSkinnyQ8, kMediumMasked, kSplitKMasked, kFp8SplitKMasked, kFp8, kFp8Mfma16Masked, kRingW8, kNumKinds
 };
 
 static const char *const kKindNames[kNumKinds] = {"none",            "tile256x256x32_s5", "tile128x128x64_s4",
@@ -33,7 +33,8 @@ static const char *const kKindNames[kNumKinds] = {"none",            "tile256x25
                                                   "splitk_fp8_256x256x128", "ring256x256x64_q8_masked",
                                                   "skinny_q8", "tile128x128x64_s4_masked",
                                                   "splitk128x128x64_masked", "splitk_fp8_256x256x128_masked",
-                                                  "fp8_256x256x128", "fp8_256x256x128_mfma16_masked"};
+                                                  "fp8_256x256x128", "fp8_256x256x128_mfma16_masked",
+                                                  "ring256x256x64_w8"};
 
 static const char *kind_name(int k) { return (k >= 0 && k < kNumKinds) ? kKindNames[k] : "none"; }
 
@@ -463,6 +464,7 @@ static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t
             return kSplitK;
         if (!std::strcmp(force, kKindNames[kRing32]) && okR) return kRing32;
         if (!std::strcmp(force, kKindNames[kRing]) && okR) return kRing;
+        if (!std::strcmp(force, kKindNames[kRingW8]) && okR) return kRingW8;
         if (!std::strcmp(force, kKindNames[kRingMasked]) && okRM) return kRingMasked;
         if (!std::strcmp(force, kKindNames[kSkinny]) && okS) return kSkinny;
         if (!std::strcmp(force, kKindNames[kGemv]) && okV) return kGemv;
@@ -677,6 +679,7 @@ static int run_bf16(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64
     case kGemv: err = launch_gemv(args, stream); break;
     case kRing32: err = launch_tile_ring_mfma32(args, cus, stream); break;
     case kRing: err = launch_tile_ring(args, cus, stream); break;
+    case kRingW8: err = launch_tile_ring_w8(args, cus, stream); break;
     case kRingMasked: err = launch_tile_ring_masked(args, cus, stream); break;
     case kSkinny: err = launch_skinny_plan(args, cus, scr, stream); break;
     default: err = launch_generic(args, cus, stream); break;

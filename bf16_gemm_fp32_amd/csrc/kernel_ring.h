@@ -54,30 +54,50 @@
 namespace gb {
 
 
-struct RingConfig {
+// kWavesN: waves across the tile's columns (two down its rows).  2 gives
+// four waves of 128x128, one per SIMD, 256 accumulators each; 4 gives eight
+// waves of 128x64, two per SIMD, 128 accumulators each, so one wave's
+// fragment reads, DMA issue and barrier waits can run under the other's
+// MFMAs, at 1.5x the LDS fragment reads per slice.
+template <int kWavesN>
+struct RingConfigT {
     static constexpr int BM = 256, BN = 256, BK = 64;
-    static constexpr int WAVES_M = 2, WAVES_N = 2;
+    static constexpr int WAVES_M = 2, WAVES_N = kWavesN;
     static constexpr int kWaves = WAVES_M * WAVES_N;
     static constexpr int kThreads = 64 * kWaves;
-    static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;  // 128 x 128 wave tile
+    static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;  // wave tile
     static constexpr int FM = WTM / 16, FN = WTN / 16;            // 16x16 MFMA blocks per wave
     static constexpr int KSTEPS = BK / 32;                        // MFMA k-steps per slice
+    static constexpr int kMfmas = FM * FN;                        // MFMAs per wave per k-step
+    static constexpr int kReads = FM + FN;                        // fragment reads per wave per k-step
     static constexpr int kRowBytes = BK * 2;                      // 128: one cache line
     static constexpr int kUnitBytes = BM * kRowBytes;             // one operand of one slice
     static constexpr int kSlots = 5;
     static constexpr int kLdsBytes = kSlots * kUnitBytes;
     static constexpr int kRowsPerLoad = 1024 / kRowBytes;         // rows one wave DMA fills
     static constexpr int kUnitLoads = BM / kRowsPerLoad / kWaves; // DMA loads per wave per unit
+    // The shadows (MFMA indices within a k-step) of a unit's DMA loads.
+    static constexpr int kLoadStart = kWaves == 4 ? 16 : kReads + 1;
+    static constexpr int kLoadStep = kWaves == 4 ? 6 : (kMfmas - kLoadStart) / kUnitLoads;
     static constexpr int kEpiColBytes = WTM * 4 + 16;
     static constexpr int kEpiWaveBytes = 32 * kEpiColBytes;
+    // Epilogue staging in slots 0-2 leaves slots 3-4 for the next tile's
+    // A(0), B(0); otherwise the staging takes the whole ring and the next
+    // tile's loads wait for it.
+    static constexpr bool kEpiInRing = kWaves * kEpiWaveBytes <= 3 * kUnitBytes;
 
     static_assert(BM == BN, "A and B units have the same size");
-    static_assert(KSTEPS == 2 && FM == 8 && FN == 8 && kUnitLoads == 8,
-                  "the slice schedule below is written for 2 k-steps of 64 MFMAs and 8 loads per unit");
+    static_assert(KSTEPS == 2, "the slice schedule below is written for 2 k-steps per slice");
+    static_assert(FN <= FM && kReads <= kMfmas, "one fragment read per MFMA shadow");
+    static_assert(kUnitLoads % 2 == 0 && kLoadStep >= 1 && kLoadStart >= kReads &&
+                      kLoadStart + (kUnitLoads - 1) * kLoadStep < kMfmas,
+                  "a unit's loads fit in the shadows after the reads, in row groups of both parities");
     static_assert(kLdsBytes <= 160 * 1024, "gfx950 has 160 KiB of LDS per compute unit");
-    static_assert(kWaves * kEpiWaveBytes <= 3 * kUnitBytes,
-                  "epilogue staging fits in slots 0-2, leaving slots 3-4 for the next tile's A(0), B(0)");
+    static_assert(kWaves * kEpiWaveBytes <= kLdsBytes, "epilogue staging fits in LDS");
 };
+using RingConfig = RingConfigT<2>;
+using RingConfigW8 = RingConfigT<4>;
+static_assert(RingConfig::kEpiInRing, "the four-wave ring stages its epilogue in slots 0-2");
 
 __device__ __forceinline__ int ring_swizzle(int row) { return (row >> 1) & 7; }
 
@@ -94,10 +114,8 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(const bf16x8 &a, const bf16x8 &b,
 // turns into zeros (the zero-fill of the DeepGEMM article, sections 4.2-4.3),
 // and the epilogue masks its loads and stores.  Unmasked instances carry no
 // such code.
-template <bool kMasked>
+template <bool kMasked, class Cfg = RingConfig>
 struct RingKernel {
-    using Cfg = RingConfig;
-
     struct Lane {
         uint32_t vA[2], vB[2];    // load voffsets by parity of the 8-row group
         uint32_t aRow, bRow;      // LDS offsets (within a unit) of this lane's fragment rows
@@ -110,8 +128,9 @@ struct RingKernel {
         int rowsA, rowsB, kmax;
     };
 
-    // DMA load number l (0..7) of this wave for one operand unit: rows
-    // 8q .. 8q+7 of the tile, q = 8 * wave + l, K-slice kt, into the slot.
+    // DMA load number l (0 .. kUnitLoads-1) of this wave for one operand
+    // unit: rows 8q .. 8q+7 of the tile, q = kUnitLoads * wave + l, K-slice
+    // kt, into the slot.
     template <bool kIsA>
     __device__ __forceinline__ static void load(char *smem, int slot, int kt, int l, const Lane &L,
                                                 __amdgpu_buffer_rsrc_t rsrc) {
@@ -129,16 +148,22 @@ struct RingKernel {
 
     enum : int { kNoLoad = 0, kLoadA = 1, kLoadB = 2 };
 
-    // Shadow schedule of a k-step: the fragment read (0..15, A0, B0, A1, B1,
-    // ...) and the DMA load (0..7) that follow MFMA s, or -1.
-    __host__ __device__ static constexpr int read_at(int s) { return s < 2 * Cfg::FM ? s : -1; }
+    // Shadow schedule of a k-step: the fragment read (A0, B0, A1, B1, ...,
+    // then the A fragments past the last B) and the DMA load (0 ..
+    // kUnitLoads-1) that follow MFMA s, or -1.
+    __host__ __device__ static constexpr int read_at(int s) { return s < Cfg::kReads ? s : -1; }
+    __host__ __device__ static constexpr bool read_is_a(int r) { return r < 2 * Cfg::FN ? (r & 1) == 0 : true; }
+    __host__ __device__ static constexpr int read_frag(int r) { return r < 2 * Cfg::FN ? r >> 1 : r - Cfg::FN; }
     __host__ __device__ static constexpr int load_at(int s) {
-        return (s >= 16 && (s - 16) % 6 == 0 && (s - 16) / 6 < Cfg::kUnitLoads) ? (s - 16) / 6 : -1;
+        return (s >= Cfg::kLoadStart && (s - Cfg::kLoadStart) % Cfg::kLoadStep == 0 &&
+                (s - Cfg::kLoadStart) / Cfg::kLoadStep < Cfg::kUnitLoads)
+                   ? (s - Cfg::kLoadStart) / Cfg::kLoadStep
+                   : -1;
     }
 
-    // One k-step: 64 MFMAs on (a, b), block (s / FN, s % FN) for MFMA s;
-    // (if kRead) the 16 fragment reads of k-step rks from slots (rsa, rsb)
-    // into (ra, rb) and (if kLoad) the 8 DMA loads of the unit (kLoad's
+    // One k-step: FM x FN MFMAs on (a, b), block (s / FN, s % FN) for MFMA s;
+    // (if kRead) the FM + FN fragment reads of k-step rks from slots (rsa, rsb)
+    // into (ra, rb) and (if kLoad) the DMA loads of the unit (kLoad's
     // operand) of slice lkt into slot lslot, each in the MFMA shadow that
     // read_at / load_at assign it.
     template <bool kRead, int kLoad>
@@ -149,14 +174,14 @@ struct RingKernel {
         const char *sA = smem + rsa * Cfg::kUnitBytes;
         const char *sB = smem + rsb * Cfg::kUnitBytes;
 #pragma unroll
-        for (int s = 0; s < Cfg::FM * Cfg::FN; ++s) {
+        for (int s = 0; s < Cfg::kMfmas; ++s) {
             const int p = s / Cfg::FN, q = s % Cfg::FN;
             acc[p][q] = mfma_16x16x32(a[p], b[q], acc[p][q]);
             __builtin_amdgcn_sched_barrier(0);
             const int r = read_at(s);
             if (kRead && r >= 0) {
-                const int f = r >> 1;
-                if ((r & 1) == 0)
+                const int f = read_frag(r);
+                if (read_is_a(r))
                     ra[f] = *(const GB_LDS bf16x8 *)(sA + L.aRow + f * 16 * Cfg::kRowBytes + L.chunk_off[rks]);
                 else
                     rb[f] = *(const GB_LDS bf16x8 *)(sB + L.bRow + f * 16 * Cfg::kRowBytes + L.chunk_off[rks]);
@@ -228,10 +253,9 @@ struct RingEpiInputs {
 // chunk that straddles M -- or every chunk, when ldc % 8 != 0 or C is not
 // 16-byte aligned -- is read and written element by element, and chunks
 // past M or columns past N are skipped.  kScaled: also the column scales.
-template <uint32_t kFlags, bool kMasked, bool kScaled = false>
+template <uint32_t kFlags, bool kMasked, bool kScaled = false, class Cfg = RingConfig>
 __device__ __forceinline__ void ring_epi_load(RingEpiInputs &in, const GemmArgs &args, int64_t m0, int64_t n0,
                                               int wm, int wn, int lane, int jj) {
-    using Cfg = RingConfig;
     constexpr int kColChunks = Cfg::WTM / 8;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -270,12 +294,10 @@ __device__ __forceinline__ void ring_epi_load(RingEpiInputs &in, const GemmArgs 
 // kScaled: the FP8 input scales -- the product is acc * scale_a[m] *
 // scale_b[n] (a missing scale is 1) before alpha, beta*C, bias and the
 // activation; the row scales likewise load once per tile.
-template <uint32_t kFlags, bool kMasked, bool kQ8, bool kScaled = false>
+template <uint32_t kFlags, bool kMasked, bool kQ8, bool kScaled = false, class Cfg = RingConfig>
 __device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, int64_t m0, int64_t n0, int wm,
-                                              int wn, int lane, int wave,
-                                              const f32x4 (&acc)[RingConfig::FM][RingConfig::FN],
+                                              int wn, int lane, int wave, const f32x4 (&acc)[Cfg::FM][Cfg::FN],
                                               RingEpiInputs &in) {
-    using Cfg = RingConfig;
     char *stage = smem + wave * Cfg::kEpiWaveBytes;
     constexpr int kColChunks = Cfg::WTM / 8;      // 8-row chunks per column
     constexpr int kIters = 32 * kColChunks / 64;  // per lane per 32 columns
@@ -307,7 +329,7 @@ __device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, 
     for (int jj = 0; jj < Cfg::FN / 2; ++jj) {
         RingEpiInputs next;
         if (jj + 1 < Cfg::FN / 2)
-            ring_epi_load<kFlags, kMasked, kScaled>(next, args, m0, n0, wm, wn, lane, jj + 1);
+            ring_epi_load<kFlags, kMasked, kScaled, Cfg>(next, args, m0, n0, wm, wn, lane, jj + 1);
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
@@ -383,11 +405,10 @@ __device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, 
 // lda/ldb (and unmasked ldc) multiples of 8, and 256*lda*2 + 2K,
 // 256*ldb*2 + 2K below 2^31; for kQ8 also Q and scale 16-byte aligned and
 // ldq a multiple of 8.
-template <uint32_t kFlags, bool kMasked, bool kQ8>
-__global__ void __launch_bounds__(RingConfig::kThreads)
+template <uint32_t kFlags, bool kMasked, bool kQ8, class Cfg = RingConfig>
+__global__ void __launch_bounds__(Cfg::kThreads)
 gemm_ring_kernel(const GemmArgs args, const TileSchedule sched) {
-    using Cfg = RingConfig;
-    using RK = RingKernel<kMasked>;
+    using RK = RingKernel<kMasked, Cfg>;
     __shared__ __attribute__((aligned(1024))) char smem[Cfg::kLdsBytes];
 
     const int lane = threadIdx.x & 63;
@@ -513,39 +534,47 @@ gemm_ring_kernel(const GemmArgs args, const TileSchedule sched) {
         RingEpiInputs epi_in;
         RK::template slice<2>(smem, j, sa, Ln, cur.rA, cur.rB, fa, fb, acc, [&] {
             if constexpr ((kFlags & (kEpiBeta | kEpiBias)) != 0)
-                ring_epi_load<kFlags, kMasked>(epi_in, args, cur.m0, cur.n0, wm, wn, lane, 0);
+                ring_epi_load<kFlags, kMasked, false, Cfg>(epi_in, args, cur.m0, cur.n0, wm, wn, lane, 0);
         });
 
         // Every wave is done reading the ring (all loads landed at the last
         // wait): its low slots now stage the epilogue, and the next tile's
-        // first units go into slots 3 and 4, which the staging leaves free.
+        // first units go into slots 3 and 4, which the staging leaves free
+        // (kEpiInRing; else they load once the staging is done).
         lds_barrier();
         const int t_next = t + sched.grid;
         const bool more = t_next < num_tiles;
         TileRef next = cur;
         if (more) {
             next = tile_ref(t_next);
-            load_first(next, 3);
+            if constexpr (Cfg::kEpiInRing) load_first(next, 3);
         }
-        ring_epilogue<kFlags, kMasked, kQ8>(smem, args, cur.m0, cur.n0, wm, wn, lane, Ln.wave, acc, epi_in);
+        ring_epilogue<kFlags, kMasked, kQ8, false, Cfg>(smem, args, cur.m0, cur.n0, wm, wn, lane, Ln.wave, acc,
+                                                        epi_in);
         if (!more) break;
         // The staging slots are free again before the next prologue loads
         // into them.
         lds_barrier();
         t = t_next;
         cur = next;
-        s0 = 3;
+        if constexpr (Cfg::kEpiInRing) {
+            s0 = 3;
+        } else {
+            s0 = 0;
+            load_first(next, 0);
+        }
     }
 }
 
 // Launch with the epilogue flags of args baked in; grid = min(tiles, CUs),
 // one persistent workgroup per compute unit.  The masked instances run when
 // the shape has tails.
-template <bool kMasked, bool kQ8 = false>
+template <bool kMasked, bool kQ8 = false, class Cfg = RingConfig>
 hipError_t launch_ring_t(const GemmArgs &args, const TileSchedule &s, hipStream_t stream) {
-    const dim3 grid(s.grid), block(RingConfig::kThreads);
+    const dim3 grid(s.grid), block(Cfg::kThreads);
     dispatch_flags(args.flags, [&](auto f) {
-        hipLaunchKernelGGL((gemm_ring_kernel<decltype(f)::value, kMasked, kQ8>), grid, block, 0, stream, args, s);
+        hipLaunchKernelGGL((gemm_ring_kernel<decltype(f)::value, kMasked, kQ8, Cfg>), grid, block, 0, stream, args,
+                           s);
     });
     return hipGetLastError();
 }

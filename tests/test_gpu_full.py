@@ -20,8 +20,8 @@ output element against the CPU oracle:
   oracle everywhere;
 * Inf and NaN operands and products that overflow bf16, on every kernel
   family;
-* two kernels with the same accumulation order (the ring and its masked
-  instance on exact tile multiples) must agree bit for bit.
+* kernels with the same accumulation order (the ring, its masked instance
+  on exact tile multiples, and the eight-wave ring) must agree bit for bit.
 
 Tolerance: |gpu - oracle| <= 2 ulp_bf16(oracle) + 1e-3 sqrt(K); infinities
 must match exactly and NaN only passes against NaN.
@@ -45,6 +45,7 @@ pytestmark = pytest.mark.gpu
 
 RING = "ring256x256x64"
 RINGM = "ring256x256x64_masked"
+RINGW8 = "ring256x256x64_w8"
 FP8 = "fp8_256x256x128"
 RQ8 = "ring256x256x64_q8"
 
@@ -116,16 +117,18 @@ def test_q8_ring_seven_tiles_per_cu_whole_q():
     say(f"[full-q8] ok exact={rep['exact']}/{rep['n']} near_boundary={rep['near_boundary']}")
 
 
-def test_ring_and_masked_ring_bit_identical_on_many_tiles(monkeypatch):
-    """The masked ring instance runs the same MFMA sequence in the same k
-    order as the unmasked one, so on exact tile multiples (where it loads no
-    zeros) the two must agree bit for bit -- on 512 tiles, two per CU, with
-    the full epilogue.  A race in either LDS ring would show up as a
-    difference."""
+def test_ring_variants_bit_identical_on_many_tiles(monkeypatch):
+    """The masked ring instance and the eight-wave ring run, for every output
+    element, the same MFMAs on the same operands in the same k order as the
+    unmasked four-wave ring, so on exact tile multiples (where the masked one
+    loads no zeros) all three must agree bit for bit -- on 512 tiles, two per
+    CU, with the full epilogue.  A race in any LDS ring, or in the eight-wave
+    kernel's hand-over from one tile's epilogue to the next tile's loads,
+    would show up as a difference."""
     M, N, K = 8192, 4096, 512
     case = inputs.random_case(906, M, N, K, with_c0=True, with_bias=True)
     outs = []
-    for kernel in (RING, RINGM):
+    for kernel in (RING, RINGM, RINGW8):
         monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", kernel)
         assert gb.gemm_bf16_kernel_name(M, N, K, 4096, K, 4096, K, 4096, M) == kernel
         say(f"[full] bit-identity {M}x{N}x{K} kernel={kernel}")
@@ -133,6 +136,7 @@ def test_ring_and_masked_ring_bit_identical_on_many_tiles(monkeypatch):
                             "gelu_tanh"))
     monkeypatch.delenv("GEMM_BF16_FORCE_KERNEL")
     assert np.array_equal(outs[0], outs[1]), "ring and masked ring differ on exact tile multiples"
+    assert np.array_equal(outs[0], outs[2]), "four-wave and eight-wave rings differ"
     idx = np.random.Generator(np.random.PCG64(906)).integers(0, M * N, 4096)
     ref = oracle.gemm_elems(M, N, K, case["A"], K, case["B"], K, idx % M, idx // M, case["C0"], M, 1.0, 0.5,
                             case["bias"], "gelu_tanh", nthreads=_threads())

@@ -207,8 +207,8 @@ def test_splitk_deterministic():
 # pipeline's prologue and tail cases (1 .. 10 slices, fewer and more slices
 # than LDS stages, odd and even counts).
 FORCEABLE = {"tile256x256x32_s5": 32, "tile128x128x64_s4": 64, "ring256x256x64": 64,
-             "ring256x256x64_mfma32": 64, "ring256x256x64_masked": 8, "generic64x64x32": 1,
-             "tile128x128x64_s4_masked": 8}
+             "ring256x256x64_mfma32": 64, "ring256x256x64_w8": 64, "ring256x256x64_masked": 8,
+             "generic64x64x32": 1, "tile128x128x64_s4_masked": 8}
 
 
 @pytest.mark.parametrize("kernel", list(FORCEABLE))
@@ -274,7 +274,8 @@ def test_masked_splitk_forced_split_counts(splits, monkeypatch):
 @pytest.mark.parametrize("kernel,M,N,K", [("tile256x256x32_s5", 2048, 1024, 160),
                                           ("tile128x128x64_s4", 512, 384, 192),
                                           ("ring256x256x64", 2048, 1024, 192),
-                                          ("ring256x256x64_mfma32", 2048, 1024, 192)])
+                                          ("ring256x256x64_mfma32", 2048, 1024, 192),
+                                          ("ring256x256x64_w8", 2048, 1024, 192)])
 @pytest.mark.parametrize("beta,use_bias,epi", [(b, u, e) for b in (0.0, -0.75) for u in (False, True)
                                                for e in ("none", "gelu_tanh", "relu")])
 def test_tile_epilogue_combinations(kernel, M, N, K, beta, use_bias, epi, monkeypatch):
