@@ -31,6 +31,9 @@ struct SkinnyWork;
 // FP8 (E4M3) operands: 256x256 output tiles, K-slices of 128 fp8 (one
 // 128-byte line per operand row).
 struct ShapeFp8 { static constexpr int BM = 256, BN = 256, BK = 128; };
+// FP8 on the 128x128 tiles for small and mid-sized grids: K-slices of 128
+// values (128-byte rows, the bytes of a bf16 slice of 64).
+struct ShapeFp8M { static constexpr int BM = 128, BN = 128, BK = 128; };
 
 hipError_t launch_tile_large(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_medium(const GemmArgs &args, int cus, hipStream_t stream);
@@ -60,6 +63,13 @@ hipError_t launch_tile_fp8_mfma16_masked(const GemmArgs &args, int cus, hipStrea
 // exact multiples (chosen only when forced)
 hipError_t launch_tile_fp8_mfma32_masked(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_fp8_mfma32(const GemmArgs &args, int cus, hipStream_t stream);
+// FP8 on the 128x128 tiles (32x32x64 MFMAs): whole K and split-K, exact
+// multiples and shapes with tails (split.P as for the bf16 128x128 split)
+hipError_t launch_tile_fp8_medium(const GemmArgs &args, int cus, hipStream_t stream);
+hipError_t launch_tile_fp8_medium_masked(const GemmArgs &args, int cus, hipStream_t stream);
+hipError_t launch_tile_fp8_medium_splitk(const GemmArgs &args, const TileSplit &split, int cus, hipStream_t stream);
+hipError_t launch_tile_fp8_medium_splitk_masked(const GemmArgs &args, const TileSplit &split, int cus,
+                                                hipStream_t stream);
 // split-K on the 32x32x64 FP8 tiles (split.P: splits * M * N floats of workspace)
 hipError_t launch_tile_fp8_splitk(const GemmArgs &args, const TileSplit &split, int cus, hipStream_t stream);
 hipError_t launch_tile_fp8_splitk_masked(const GemmArgs &args, const TileSplit &split, int cus,

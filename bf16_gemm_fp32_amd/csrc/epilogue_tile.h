@@ -1,7 +1,8 @@
 // epilogue_tile.h -- the fused epilogue of the 32x32-MFMA tile kernels:
 // accumulators -> alpha, beta*C, bias, activation in fp32 -> bf16 -> C.
-// Cfg supplies the wave tile (WTM x WTN as FM x FN blocks of 32x32) and the
-// per-wave LDS staging area (kEpiColBytes, kEpiWaveBytes).
+// Cfg supplies the wave tile (WTM x WTN as FM x FN blocks of 32x32), the
+// per-wave LDS staging area (kEpiColBytes, kEpiWaveBytes) and whether the
+// inputs were FP8 (kFp8: the sums are scaled by scale_a[m] * scale_b[n]).
 #pragma once
 
 #include "device_common.h"
@@ -68,7 +69,20 @@ __device__ __forceinline__ void tile_epilogue(char *smem, const GemmArgs &args, 
                     for (int e = 0; e < 8 && m + e < args.M; ++e) cin[e] = bf16_bits_to_f32(p[e]);
                 }
             }
-            const float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            if constexpr (Cfg::kFp8) {
+                // FP8 inputs: the sum times scale_a[m] and scale_b[n] (a
+                // missing scale is 1; rows past M are never stored)
+                if (args.scale_a) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = x[e] * (!kMasked || m + e < args.M ? args.scale_a[m + e] : 0.f);
+                }
+                if (args.scale_b) {
+                    const float sb = args.scale_b[n];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = x[e] * sb;
+                }
+            }
             u32x4 out;
 #pragma unroll
             for (int e = 0; e < 4; ++e)

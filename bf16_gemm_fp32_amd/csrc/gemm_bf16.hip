@@ -20,7 +20,7 @@
 namespace gb {
 
 enum KernelKind {
-    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8Mfma32, kSplitK, kGemv, kSplitKQ8, kFp8Masked, kGemvFp8, kSkinnyFp8, kFp8SplitK, kRingQ8Masked, kSkinnyQ8, kMediumMasked, kSplitKMasked, kFp8SplitKMasked, kFp8, kFp8Mfma16Masked, kRingW8, kNumKinds
+    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8Mfma32, kSplitK, kGemv, kSplitKQ8, kFp8Masked, kGemvFp8, kSkinnyFp8, kFp8SplitK, kRingQ8Masked, kSkinnyQ8, kMediumMasked, kSplitKMasked, kFp8SplitKMasked, kFp8, kFp8Mfma16Masked, kRingW8, kFp8Medium, kFp8MediumMasked, kFp8SplitKMedium, kFp8SplitKMediumMasked, kNumKinds
 };
 
 static const char *const kKindNames[kNumKinds] = {"none",            "tile256x256x32_s5", "tile128x128x64_s4",
@@ -34,7 +34,9 @@ static const char *const kKindNames[kNumKinds] = {"none",            "tile256x25
                                                   "skinny_q8", "tile128x128x64_s4_masked",
                                                   "splitk128x128x64_masked", "splitk_fp8_256x256x128_masked",
                                                   "fp8_256x256x128", "fp8_256x256x128_mfma16_masked",
-                                                  "ring256x256x64_w8"};
+                                                  "ring256x256x64_w8", "fp8_128x128x128",
+                                                  "fp8_128x128x128_masked", "splitk_fp8_128x128x128",
+                                                  "splitk_fp8_128x128x128_masked"};
 
 static const char *kind_name(int k) { return (k >= 0 && k < kNumKinds) ? kKindNames[k] : "none"; }
 
@@ -321,12 +323,15 @@ static hipError_t launch_skinny_plan(const GemmArgs &args, int cus, const Scratc
 // Returns 1 when no split applies.
 constexpr int kSplitMinSlices = 8;
 
+// Shape: the 128x128 tiles' K-slice (ShapeM, 64 bf16 values; ShapeFp8M, 128
+// FP8 values: the same 128-byte rows and MFMA time per slice).
+template <class Shape = ShapeM>
 static TileSplit plan_splitk(int64_t M, int64_t N, int64_t K, int cus, size_t cap_floats) {
     TileSplit p{};
     p.splits = 1;
     // tiles and slices rounded up: shapes with tails run the masked kernel
-    const int64_t tiles = ((M + ShapeM::BM - 1) / ShapeM::BM) * ((N + ShapeM::BN - 1) / ShapeM::BN);
-    const int64_t nk = (K + ShapeM::BK - 1) / ShapeM::BK;
+    const int64_t tiles = ((M + Shape::BM - 1) / Shape::BM) * ((N + Shape::BN - 1) / Shape::BN);
+    const int64_t nk = (K + Shape::BK - 1) / Shape::BK;
     if (tiles <= 0 || tiles * 2 >= cus) return p;
     int64_t splits = cus / tiles;
     if (const char *env = std::getenv("GEMM_BF16_SPLITK_SPLITS")) {  // tuning knob
@@ -336,8 +341,8 @@ static TileSplit plan_splitk(int64_t M, int64_t N, int64_t K, int cus, size_t ca
     const int64_t max_splits = nk / kSplitMinSlices;
     if (splits > max_splits) splits = max_splits;
     // whole tiles are stored: the scratch is padded to tile multiples
-    const int64_t ldp = (M + ShapeM::BM - 1) / ShapeM::BM * ShapeM::BM;
-    const int64_t pstride = ldp * ((N + ShapeM::BN - 1) / ShapeM::BN * ShapeM::BN);
+    const int64_t ldp = (M + Shape::BM - 1) / Shape::BM * Shape::BM;
+    const int64_t pstride = ldp * ((N + Shape::BN - 1) / Shape::BN * Shape::BN);
     if (splits > (int64_t)cap_floats / pstride) splits = (int64_t)cap_floats / pstride;
     if (splits < 2) return p;
     p.kper = (int)((nk + splits - 1) / splits);
@@ -362,28 +367,19 @@ static TileSplit plan_splitk(int64_t M, int64_t N, int64_t K, int cus, size_t ca
 // 1024: 15.2 us split against 9.4 us unsplit; 1024 x 1024 x 4096: 23.4 us
 // against 25.0 us).  The quantizing output has no unsplit small-grid kernel
 // and splits whenever the plan allows.
-static bool splitk_pays(int64_t M, int64_t N, int64_t K) {
-    const int64_t tiles = ((M + ShapeM::BM - 1) / ShapeM::BM) * ((N + ShapeM::BN - 1) / ShapeM::BN);
-    const int64_t nk = (K + ShapeM::BK - 1) / ShapeM::BK;
+template <class Shape>
+static bool splitk_pays_t(int64_t M, int64_t N, int64_t K) {
+    const int64_t tiles = ((M + Shape::BM - 1) / Shape::BM) * ((N + Shape::BN - 1) / Shape::BN);
+    const int64_t nk = (K + Shape::BK - 1) / Shape::BK;
     return 5 * nk >= 100 + 2 * tiles;
 }
+static bool splitk_pays(int64_t M, int64_t N, int64_t K) { return splitk_pays_t<ShapeM>(M, N, K); }
 
-// Split-K for the FP8 tiles on small grids (the fp8 path has no smaller
-// tile): when the 256x256 tiles fill less than half of the compute units,
-// up to CUs / tiles ranges of at least 4 slices of 128, at most 8, and at
-// most cap_floats floats of partials.  Returns 1 when no split applies.
-// Whether splitting K over the 256x256 FP8 tiles beats the unsplit kernel:
-// measured on gfx950, the split (tile kernel, then the reduction) wins from
-// about 15 slices of 128 at 8 tiles, 24 at 16 tiles and 33 at 32 tiles
-// (16 tiles: 16 slices unsplit 23.1 us against 28.0 split, 32 slices 37.6
-// against 31.7; 32 tiles: 24 slices 30.8 against 35.5, 40 slices 46.5
-// against 40.1).
-static bool fp8_splitk_pays(int64_t M, int64_t N, int64_t K) {
-    const int64_t tiles = ((M + ShapeFp8::BM - 1) / ShapeFp8::BM) * ((N + ShapeFp8::BN - 1) / ShapeFp8::BN);
-    const int64_t nk = (K + ShapeFp8::BK - 1) / ShapeFp8::BK;
-    return 8 * nk >= 88 + 5 * tiles;
-}
-
+// Split-K over the 256x256 FP8 tiles, reached by GEMM_BF16_FORCE_KERNEL
+// only (on the small grids where it applies the 128x128 tiles are faster):
+// when those tiles fill less than half of the compute units, up to CUs /
+// tiles ranges of at least 4 slices of 128, at most 8, and at most
+// cap_floats floats of partials.  Returns 1 when no split applies.
 static TileSplit plan_splitk_fp8(int64_t M, int64_t N, int64_t K, int cus, size_t cap_floats) {
     TileSplit p{};
     p.splits = 1;
@@ -420,6 +416,20 @@ static hipError_t launch_fp8_splitk_plan(const GemmArgs &args, int cus, const Sc
     hipError_t err = get_scratch(scr, stream, &unused, &p.P);
     if (err != hipSuccess) return err;
     return masked ? launch_tile_fp8_splitk_masked(args, p, cus, stream) : launch_tile_fp8_splitk(args, p, cus, stream);
+}
+
+// FP8 split-K on the 128x128 tiles (unsplit when the plan does not split).
+static hipError_t launch_fp8_medium_splitk_plan(const GemmArgs &args, int cus, const Scratch &scr,
+                                                hipStream_t stream, bool masked) {
+    TileSplit p = plan_splitk<ShapeFp8M>(args.M, args.N, args.K, cus, scr.cap_floats);
+    if (p.splits < 2)
+        return masked ? launch_tile_fp8_medium_masked(args, cus, stream) : launch_tile_fp8_medium(args, cus, stream);
+    if ((size_t)p.splits * (size_t)p.pstride > scr.cap_floats) return hipErrorInvalidValue;
+    uint32_t *unused = nullptr;
+    hipError_t err = get_scratch(scr, stream, &unused, &p.P);
+    if (err != hipSuccess) return err;
+    return masked ? launch_tile_fp8_medium_splitk_masked(args, p, cus, stream)
+                  : launch_tile_fp8_medium_splitk(args, p, cus, stream);
 }
 
 // kQ8: the quantizing output (the host chose this path only when the plan
@@ -597,14 +607,36 @@ static int choose_kernel_fp8(int64_t M, int64_t N, int64_t K, const void *A, int
     if (force && !std::strcmp(force, kKindNames[kFp8])) return exact ? kFp8 : kFp8Masked;
     if (force && !std::strcmp(force, kKindNames[kFp8Mfma16Masked])) return kFp8Mfma16Masked;
     if (force && !std::strcmp(force, kKindNames[kFp8Mfma32])) return exact ? kFp8Mfma32 : kFp8Masked;
-    // small grids: split K (the reduction takes any C: it reads and writes a
-    // chunk element by element where ldc % 8 != 0, C is unaligned or the
-    // chunk straddles M)
+    // the 128x128 tiles: exact multiples of 128 (and C's alignment), or masked
+    const bool ok128 = ((M + ShapeFp8M::BM - 1) / ShapeFp8M::BM) * ((N + ShapeFp8M::BN - 1) / ShapeFp8M::BN) < lim / 64;
+    const bool exact128 = M % ShapeFp8M::BM == 0 && N % ShapeFp8M::BN == 0 && K % ShapeFp8M::BK == 0 &&
+                          ldc % 8 == 0 && aligned16(C);
+    const bool can_split128 = ok128 && plan_splitk<ShapeFp8M>(M, N, K, cus, cap_floats).splits >= 2;
+    if (force && ok128 && !std::strcmp(force, kKindNames[kFp8MediumMasked])) return kFp8MediumMasked;
+    if (force && ok128 && !std::strcmp(force, kKindNames[kFp8Medium])) return exact128 ? kFp8Medium : kFp8MediumMasked;
+    if (force && can_split128 &&
+        (!std::strcmp(force, kKindNames[kFp8SplitKMedium]) || !std::strcmp(force, kKindNames[kFp8SplitKMediumMasked])))
+        return exact128 ? kFp8SplitKMedium : kFp8SplitKMediumMasked;
     const bool can_split = plan_splitk_fp8(M, N, K, cus, cap_floats).splits >= 2;
     if (force && can_split &&
         (!std::strcmp(force, kKindNames[kFp8SplitK]) || !std::strcmp(force, kKindNames[kFp8SplitKMasked])))
         return exact ? kFp8SplitK : kFp8SplitKMasked;
-    if (can_split && fp8_splitk_pays(M, N, K)) return exact ? kFp8SplitK : kFp8SplitKMasked;
+    // Small and mid-sized grids (the 256x256 tiles fill less than half of
+    // the compute units): the 128x128 tiles, splitting K by the bf16 128x128
+    // kernel's rule (an FP8 slice of 128 has its bytes and MFMA time).  The
+    // reduction takes any C: it reads and writes a chunk element by element
+    // where ldc % 8 != 0, C is unaligned or the chunk straddles M.
+    // Measured against the 256x256 paths (split where they split): 1024 x
+    // 1024 x 4096 16.4 us against 32.5, 512 x 512 x 8192 (split) 14.8 against
+    // 26.8, 2048 x 2048 x 2048 13.0 against 24.8, 1000 x 1000 x 4096 22.1
+    // against 31.6; at 144 tiles of 256x256 (3072 x 3072 x 2048) the large
+    // tiles win, 27.4 against 34.8.
+    const int64_t tiles256 = ((M + ShapeFp8::BM - 1) / ShapeFp8::BM) * ((N + ShapeFp8::BN - 1) / ShapeFp8::BN);
+    if (ok128 && tiles256 * 2 < cus) {
+        if (can_split128 && splitk_pays_t<ShapeFp8M>(M, N, K))
+            return exact128 ? kFp8SplitKMedium : kFp8SplitKMediumMasked;
+        return exact128 ? kFp8Medium : kFp8MediumMasked;
+    }
     return exact ? kFp8 : kFp8Masked;
 }
 
@@ -813,6 +845,10 @@ int gemm_fp8(int64_t M, int64_t N, int64_t K, const gemm_fp8_t *A, int64_t lda, 
     case kFp8Masked: err = launch_tile_fp8_mfma32_masked(args, cus, stream); break;
     case kFp8Mfma32: err = launch_tile_fp8_mfma32(args, cus, stream); break;
     case kFp8Mfma16Masked: err = launch_tile_fp8_mfma16_masked(args, cus, stream); break;
+    case kFp8Medium: err = launch_tile_fp8_medium(args, cus, stream); break;
+    case kFp8MediumMasked: err = launch_tile_fp8_medium_masked(args, cus, stream); break;
+    case kFp8SplitKMedium: err = launch_fp8_medium_splitk_plan(args, cus, scr, stream, false); break;
+    case kFp8SplitKMediumMasked: err = launch_fp8_medium_splitk_plan(args, cus, scr, stream, true); break;
     case kGemvFp8: err = launch_gemv(args, stream, true); break;
     case kSkinnyFp8: err = launch_skinny_plan(args, cus, scr, stream, true); break;
     default: err = launch_generic(args, cus, stream, true); break;

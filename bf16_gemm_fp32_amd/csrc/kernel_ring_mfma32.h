@@ -23,6 +23,7 @@ namespace gb {
 
 struct Ring32Config {
     static constexpr int BM = 256, BN = 256, BK = 64;
+    static constexpr bool kFp8 = false;
     static constexpr int WAVES_M = 2, WAVES_N = 2;
     static constexpr int kWaves = WAVES_M * WAVES_N;
     static constexpr int kThreads = 64 * kWaves;

@@ -68,19 +68,33 @@
 
 namespace gb {
 
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_>
+// ELEM_: bytes per operand element, 2 (bf16 on v_mfma_f32_32x32x16_bf16) or
+// 1 (FP8 E4M3 on v_mfma_scale_f32_32x32x64_f8f6f4).  BK counts elements, so
+// an FP8 slice of 128 has the bytes, loads and LDS layout of a bf16 slice
+// of 64 and twice its k.
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_, int ELEM_ = 2>
 struct TileConfig {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, STAGES = STAGES_;
+    static constexpr int kElem = ELEM_;
+    static constexpr bool kFp8 = ELEM_ == 1;
+    using Frag = std::conditional_t<kFp8, i32x8, bf16x8>;  // one lane's MFMA operand
     static constexpr int kWaves = WAVES_M * WAVES_N;
     static constexpr int kThreads = 64 * kWaves;
     static constexpr int WTM = BM / WAVES_M;  // wave tile
     static constexpr int WTN = BN / WAVES_N;
     static constexpr int FM = WTM / 32;       // 32x32 MFMA blocks per wave
     static constexpr int FN = WTN / 32;
-    static constexpr int KSTEPS = BK / 16;    // MFMA k-steps per slice
-    static constexpr int kRowBytes = BK * 2;
-    static constexpr int kChunks = BK / 8;                 // 16-byte chunks per row
+    static constexpr int KSTEPS = BK / (kFp8 ? 64 : 16);  // MFMA k-steps per slice
+    static constexpr int kRowBytes = BK * kElem;
+    static constexpr int kSwzBK = kRowBytes / 2;           // the LDS swizzle is keyed on the row's bytes
+    static constexpr int kChunks = kRowBytes / 16;         // 16-byte chunks per row
+    static constexpr int kElemsPerChunk = 16 / kElem;
+    static constexpr int kChunkSteps = kRowBytes / 32;     // 32-byte k groups of a row (chunk offsets)
+    // ds_read_b128 per k-step: one per bf16 fragment, two per FP8 fragment
+    static constexpr int kReadOps = (FM + FN) * (kFp8 ? 2 : 1);
+    static constexpr int kReadsPerShadow = kReadOps <= FM * FN ? 1 : 2;
+    static constexpr int kReadShadows = (kReadOps + kReadsPerShadow - 1) / kReadsPerShadow;
     static constexpr int kRowsPerLoad = 64 / kChunks;      // rows one 1 KiB wave load fills
     static constexpr int kABytes = BM * kRowBytes;
     static constexpr int kBBytes = BN * kRowBytes;
@@ -94,7 +108,7 @@ struct TileConfig {
     static constexpr int kEpiColBytes = WTM * 4 + 16;
     static constexpr int kEpiWaveBytes = 32 * kEpiColBytes;
 
-    static_assert(BK == 32 || BK == 64, "swizzles exist for 64- and 128-byte rows");
+    static_assert(kRowBytes == 64 || kRowBytes == 128, "swizzles exist for 64- and 128-byte rows");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must hold whole 32x32 blocks");
     static_assert(BM % (kRowsPerLoad * kWaves) == 0 && BN % (kRowsPerLoad * kWaves) == 0,
                   "tile rows must split evenly over the waves' loads");
@@ -104,7 +118,7 @@ struct TileConfig {
     static_assert(kLdsBytes <= 160 * 1024, "gfx950 has 160 KiB of LDS per compute unit");
     static_assert(kWaves * kEpiWaveBytes <= kLdsBytes, "epilogue staging reuses the ring");
     static_assert(KSTEPS % 2 == 0, "fragment double-buffering alternates per k-step");
-    static_assert(FM * FN >= FM + FN && FM * FN >= kHalf, "MFMA count paces the reads and loads");
+    static_assert(kReadShadows <= FM * FN && FM * FN >= kHalf, "MFMA count paces the reads and loads");
 };
 
 template <int BK>
@@ -142,7 +156,7 @@ struct TileKernel {
     struct Lane {
         uint32_t vA[2], vB[2];            // load voffsets by parity of the row group
         uint32_t aRow, bRow;              // LDS row offsets of this lane's fragments
-        uint32_t chunk_off[Cfg::KSTEPS];  // swizzled chunk offset per k-step
+        uint32_t chunk_off[Cfg::kChunkSteps];  // swizzled chunk offset per 32-byte k group
         uint32_t lda_bytes, ldb_bytes;
         int wave;
         // masking only: this lane's row within a load's rows, its logical
@@ -159,7 +173,7 @@ struct TileKernel {
         uint32_t v = kIsA ? L.vA[q & 1] : L.vB[q & 1];
         if constexpr (kMasked) {
             const int row = q * Cfg::kRowsPerLoad + L.lrow;
-            const int k = kt * Cfg::BK + L.lchunk[q & 1] * 8;
+            const int k = kt * Cfg::BK + L.lchunk[q & 1] * Cfg::kElemsPerChunk;
             if (!(row < (kIsA ? L.rowsA : L.rowsB) && k < L.kmax)) v = kOobOffset;
         }
         return v;
@@ -172,7 +186,7 @@ struct TileKernel {
                                                  __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rB) {
         char *sA = smem + buf * Cfg::kStageBytes;
         char *sB = sA + Cfg::kABytes;
-        const uint32_t kbytes = (uint32_t)kt * Cfg::BK * 2;
+        const uint32_t kbytes = (uint32_t)kt * Cfg::kRowBytes;
 #pragma unroll
         for (int idx = LO; idx < HI; ++idx) {
             if (idx < Cfg::kALoads) {
@@ -187,26 +201,49 @@ struct TileKernel {
         }
     }
 
-    // Fragments of MFMA k-step kk (16 k values) of the slice in ring buffer
-    // buf: FM A blocks and FN B blocks, one ds_read_b128 each.
+    using Frag = typename Cfg::Frag;
+
+    __device__ __forceinline__ static f32x16 mfma(const Frag &a, const Frag &b, const f32x16 &c) {
+        if constexpr (Cfg::kFp8)
+            return mfma_fp8_32x32x64(a, b, c);
+        else
+            return mfma_32x32x16(a, b, c);
+    }
+
+    // Fragment read op r (0 .. kReadOps-1) of MFMA k-step kk of the slice at
+    // (sA, sB).  A bf16 fragment (16 k) is one ds_read_b128: lane l takes
+    // row l % 32 of its 32-row block and logical chunk 2kk + l/32.  An FP8
+    // fragment (64 k) is two: its low 16 bytes from chunk 4kk + l/32 and its
+    // high 16 bytes from chunk 4kk + 2 + l/32, the operand layout of the
+    // 32x32x64 MFMA -- i.e. the chunks of bf16 k-steps 2kk and 2kk + 1.
+    // Fragments go A0, B0, A1, B1, ... while both remain, then the rest of A.
+    __device__ __forceinline__ static void read_op(const char *sA, const char *sB, int kk, int r, const Lane &L,
+                                                   Frag (&a)[Cfg::FM], Frag (&b)[Cfg::FN]) {
+        constexpr int kHalves = Cfg::kFp8 ? 2 : 1;
+        const int fr = r / kHalves, half = r % kHalves;
+        const bool is_a = fr < 2 * Cfg::FN ? (fr & 1) == 0 : true;
+        const int f = fr < 2 * Cfg::FN ? fr >> 1 : fr - Cfg::FN;
+        const uint32_t off = L.chunk_off[kHalves * kk + half];
+        const char *src = is_a ? sA + L.aRow : sB + L.bRow;
+        Frag &dst = is_a ? a[f] : b[f];
+        if constexpr (Cfg::kFp8) {
+            const i32x4 v = *(const GB_LDS i32x4 *)(src + f * 32 * Cfg::kRowBytes + off);
+            if (half)
+                dst.hi = v;
+            else
+                dst.lo = v;
+        } else {
+            dst = *(const GB_LDS bf16x8 *)(src + f * 32 * Cfg::kRowBytes + off);
+        }
+    }
+
+    // All fragments of MFMA k-step kk of the slice in ring buffer buf.
     __device__ __forceinline__ static void read_frags(const char *smem, int buf, int kk, const Lane &L,
-                                                      bf16x8 (&a)[Cfg::FM], bf16x8 (&b)[Cfg::FN]) {
+                                                      Frag (&a)[Cfg::FM], Frag (&b)[Cfg::FN]) {
         const char *sA = smem + buf * Cfg::kStageBytes;
         const char *sB = sA + Cfg::kABytes;
 #pragma unroll
-        for (int i = 0; i < Cfg::FM; ++i)
-            a[i] = *(const GB_LDS bf16x8 *)(sA + L.aRow + i * 32 * Cfg::kRowBytes + L.chunk_off[kk]);
-#pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j)
-            b[j] = *(const GB_LDS bf16x8 *)(sB + L.bRow + j * 32 * Cfg::kRowBytes + L.chunk_off[kk]);
-    }
-
-    __device__ __forceinline__ static void mfma_block(const bf16x8 (&a)[Cfg::FM], const bf16x8 (&b)[Cfg::FN],
-                                                      f32x16 (&acc)[Cfg::FM][Cfg::FN]) {
-#pragma unroll
-        for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-            for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = mfma_32x32x16(a[i], b[j], acc[i][j]);
+        for (int r = 0; r < Cfg::kReadOps; ++r) read_op(sA, sB, kk, r, L, a, b);
     }
 
     // One k-step: the FM x FN MFMAs on (a, b), issued one at a time, with the
@@ -221,44 +258,33 @@ struct TileKernel {
     // one read or one load per shadow stays under that.  Hard scheduling
     // fences keep this order.
     template <bool kRead, bool kLoad, int LO>
-    __device__ __forceinline__ static void kstep(char *smem, const bf16x8 (&a)[Cfg::FM], const bf16x8 (&b)[Cfg::FN],
+    __device__ __forceinline__ static void kstep(char *smem, const Frag (&a)[Cfg::FM], const Frag (&b)[Cfg::FN],
                                                  f32x16 (&acc)[Cfg::FM][Cfg::FN], int rbuf, int rkk,
-                                                 bf16x8 (&ra)[Cfg::FM], bf16x8 (&rb)[Cfg::FN], int lbuf, int lkt,
+                                                 Frag (&ra)[Cfg::FM], Frag (&rb)[Cfg::FN], int lbuf, int lkt,
                                                  const Lane &L, __amdgpu_buffer_rsrc_t rA,
                                                  __amdgpu_buffer_rsrc_t rB) {
         constexpr int kMf = Cfg::FM * Cfg::FN;
-        constexpr int kReads = Cfg::FM + Cfg::FN;
         constexpr int kLoadsHere = Cfg::kHalf;
-        static_assert(kReads <= kMf, "one fragment read per MFMA shadow");
+        constexpr int kRps = Cfg::kReadsPerShadow;
         // first shadow of load l: after the reads if they leave room, else shared with them
-        constexpr int kFree = kMf - kReads;
+        constexpr int kFree = kMf - Cfg::kReadShadows;
         const char *sA = smem + rbuf * Cfg::kStageBytes;
         const char *sB = sA + Cfg::kABytes;
 #pragma unroll
         for (int s = 0; s < kMf; ++s) {
             const int p = s / Cfg::FN, j = s % Cfg::FN;
-            acc[p][j] = mfma_32x32x16(a[p], b[j], acc[p][j]);
+            acc[p][j] = mfma(a[p], b[j], acc[p][j]);
             __builtin_amdgcn_sched_barrier(0);
-            if (kRead && s < kReads) {
-                // reads alternate A, B while both remain, then the rest of A
-                const int r = s;
-                const int nb = Cfg::FN;
-                if (r < 2 * nb) {
-                    if ((r & 1) == 0)
-                        ra[r >> 1] = *(const GB_LDS bf16x8 *)(sA + L.aRow + (r >> 1) * 32 * Cfg::kRowBytes +
-                                                             L.chunk_off[rkk]);
-                    else
-                        rb[r >> 1] = *(const GB_LDS bf16x8 *)(sB + L.bRow + (r >> 1) * 32 * Cfg::kRowBytes +
-                                                             L.chunk_off[rkk]);
-                } else {
-                    const int ia = r - nb;
-                    ra[ia] = *(const GB_LDS bf16x8 *)(sA + L.aRow + ia * 32 * Cfg::kRowBytes + L.chunk_off[rkk]);
-                }
+            if (kRead) {
+#pragma unroll
+                for (int u = 0; u < kRps; ++u)
+                    if (s * kRps + u < Cfg::kReadOps) read_op(sA, sB, rkk, s * kRps + u, L, ra, rb);
             }
             if (kLoad) {
 #pragma unroll
                 for (int l = 0; l < kLoadsHere; ++l) {
-                    const int slot = (kFree >= kLoadsHere) ? kReads + l * kFree / kLoadsHere : l * kMf / kLoadsHere;
+                    const int slot = (kFree >= kLoadsHere) ? Cfg::kReadShadows + l * kFree / kLoadsHere
+                                                           : l * kMf / kLoadsHere;
                     if (slot == s) issue_range<LO>(smem, lbuf, lkt, L, rA, rB, l, 1);
                 }
             }
@@ -274,7 +300,7 @@ struct TileKernel {
                                                        int first, int count) {
         char *sA = smem + buf * Cfg::kStageBytes;
         char *sB = sA + Cfg::kABytes;
-        const uint32_t kbytes = (uint32_t)kt * Cfg::BK * 2;
+        const uint32_t kbytes = (uint32_t)kt * Cfg::kRowBytes;
 #pragma unroll
         for (int r = 0; r < count; ++r) {
             const int idx = LO + first + r;
@@ -308,8 +334,8 @@ struct TileKernel {
     template <bool kSteady, bool kNext>
     __device__ __forceinline__ static void slice(char *smem, int kt, int cur, bool first, bool second, int ahead,
                                                  const Lane &L, __amdgpu_buffer_rsrc_t rA,
-                                                 __amdgpu_buffer_rsrc_t rB, bf16x8 (&fa)[2][Cfg::FM],
-                                                 bf16x8 (&fb)[2][Cfg::FN], f32x16 (&acc)[Cfg::FM][Cfg::FN]) {
+                                                 __amdgpu_buffer_rsrc_t rB, Frag (&fa)[2][Cfg::FM],
+                                                 Frag (&fb)[2][Cfg::FN], f32x16 (&acc)[Cfg::FM][Cfg::FN]) {
         const int prev = (cur == 0) ? S - 1 : cur - 1;
         const int next = (cur + 1 == S) ? 0 : cur + 1;
         if (!kSteady && second) issue<Cfg::kHalf, Cfg::kLoads>(smem, prev, kt + S - 1, L, rA, rB);
@@ -387,8 +413,8 @@ gemm_tile_kernel(const GemmArgs args, const TileSchedule sched, const TileSplit 
     Ln.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = Ln.wave / Cfg::WAVES_N;
     const int wn = Ln.wave % Cfg::WAVES_N;
-    Ln.lda_bytes = (uint32_t)args.lda * 2u;
-    Ln.ldb_bytes = (uint32_t)args.ldb * 2u;
+    Ln.lda_bytes = (uint32_t)(args.lda * Cfg::kElem);
+    Ln.ldb_bytes = (uint32_t)(args.ldb * Cfg::kElem);
 
     // Load side: in row group q, lane i covers row q*kRowsPerLoad + i/kChunks
     // and LDS position i%kChunks, which holds logical chunk (i%kChunks) ^
@@ -397,20 +423,21 @@ gemm_tile_kernel(const GemmArgs args, const TileSchedule sched, const TileSplit 
     const int lrow = lane / Cfg::kChunks, lpos = lane % Cfg::kChunks;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-        const int c = lpos ^ lds_swizzle<Cfg::BK>(p * Cfg::kRowsPerLoad + lrow);
+        const int c = lpos ^ lds_swizzle<Cfg::kSwzBK>(p * Cfg::kRowsPerLoad + lrow);
         Ln.vA[p] = lrow * Ln.lda_bytes + (uint32_t)(c << 4);
         Ln.vB[p] = lrow * Ln.ldb_bytes + (uint32_t)(c << 4);
         Ln.lchunk[p] = c;
     }
     Ln.lrow = lrow;
     Ln.rowsA = Ln.rowsB = Ln.kmax = 0;
-    // Read side: MFMA operand lane l takes row l % 32 of its 32-row block and
-    // 8 consecutive k from logical chunk 2*kk + l/32.
+    // Read side: MFMA operand lane l takes row l % 32 of its 32-row block;
+    // in 32-byte k group kk its 16 bytes are logical chunk 2*kk + l/32
+    // (read_op: one group per bf16 k-step, two per FP8 k-step).
     Ln.aRow = (uint32_t)(wm * Cfg::WTM + (lane & 31)) * Cfg::kRowBytes;
     Ln.bRow = (uint32_t)(wn * Cfg::WTN + (lane & 31)) * Cfg::kRowBytes;
 #pragma unroll
-    for (int kk = 0; kk < Cfg::KSTEPS; ++kk)
-        Ln.chunk_off[kk] = (uint32_t)(((2 * kk + (lane >> 5)) ^ lds_swizzle<Cfg::BK>(lane & 31)) << 4);
+    for (int kk = 0; kk < Cfg::kChunkSteps; ++kk)
+        Ln.chunk_off[kk] = (uint32_t)(((2 * kk + (lane >> 5)) ^ lds_swizzle<Cfg::kSwzBK>(lane & 31)) << 4);
 
     const int nk_all = (int)((args.K + Cfg::BK - 1) / Cfg::BK);
     const int num_tiles = sched.num_tiles();
@@ -440,10 +467,12 @@ gemm_tile_kernel(const GemmArgs args, const TileSchedule sched, const TileSplit 
             Ln.rowsB = (int)(args.N - n0 < Cfg::BN ? args.N - n0 : Cfg::BN);
             Ln.kmax = (int)(args.K - k0);  // the unit's K: chunks at or past it are zeros
         }
-        const __amdgpu_buffer_rsrc_t rA =
-            make_rsrc(args.A + m0 * args.lda + k0, (uint32_t)(((Cfg::BM - 1) * args.lda + kn) * 2));
-        const __amdgpu_buffer_rsrc_t rB =
-            make_rsrc(args.B + n0 * args.ldb + k0, (uint32_t)(((Cfg::BN - 1) * args.ldb + kn) * 2));
+        const char *A = reinterpret_cast<const char *>(args.A);
+        const char *B = reinterpret_cast<const char *>(args.B);
+        const __amdgpu_buffer_rsrc_t rA = make_rsrc(A + (m0 * args.lda + k0) * Cfg::kElem,
+                                                    (uint32_t)(((Cfg::BM - 1) * args.lda + kn) * Cfg::kElem));
+        const __amdgpu_buffer_rsrc_t rB = make_rsrc(B + (n0 * args.ldb + k0) * Cfg::kElem,
+                                                    (uint32_t)(((Cfg::BN - 1) * args.ldb + kn) * Cfg::kElem));
 
         f32x16 acc[Cfg::FM][Cfg::FN];
 #pragma unroll
@@ -456,7 +485,7 @@ gemm_tile_kernel(const GemmArgs args, const TileSchedule sched, const TileSplit 
         // Prologue: slices 0 .. S-2 and the first half of slice S-1 in
         // flight; once slice 0 has landed everywhere its first fragments are
         // read.
-        bf16x8 fa[2][Cfg::FM], fb[2][Cfg::FN];
+        typename Cfg::Frag fa[2][Cfg::FM], fb[2][Cfg::FN];
 #pragma unroll
         for (int s = 0; s < S - 1; ++s)
             if (s < nk) TK::template issue<0, L>(smem, s, s, Ln, rA, rB);

@@ -109,6 +109,9 @@ WORKLOADS = {
         # the memory-bound case with FP8 operands: B (64 MiB) streamed once
         Workload("fp8_skinny_64x8192x8192", 10, 64, 8192, 8192, inp="fp8", bound="hbm",
                  notes="C = sa[m] sb[n] (A*B), E4M3 operands, 64 rows"),
+        # FP8 on the small grid of the DeepGEMM article's shapes (section 5.1)
+        Workload("fp8_mid_1024x1024x4096", 11, 1024, 1024, 4096, inp="fp8",
+                 notes="64 tiles of 128x128 for 256 compute units, E4M3 operands"),
     ]
 }
 

@@ -136,24 +136,27 @@ def test_fp8_argument_errors_and_names():
     assert name(2, 8192, 8192, P, 8192, P, 8192, P, 2) == "gemv_fp8"
     assert name(3, 8192, 8192, P, 8192, P, 8192, P, 3) == "skinny_fp8"   # large B: A shared per strip
     assert name(4, 16384, 4096, P, 4096, P, 4096, P, 4) == "skinny_fp8"
-    # small grids of exact FP8 tiles split K; larger grids and short K do not
-    assert name(1024, 1024, 4096, P, 4096, P, 4096, P, 1024) == "splitk_fp8_256x256x128"
-    assert name(512, 512, 8192, P, 8192, P, 8192, P, 512) == "splitk_fp8_256x256x128"
-    assert name(1024, 1024, 384, P, 384, P, 384, P, 1024) == "fp8_256x256x128"     # 3 slices
-    assert name(1000, 1000, 4096, P, 4096, P, 4096, P, 1000) == "splitk_fp8_256x256x128_masked"
-    assert name(1000, 1000, 208, P, 208, P, 208, P, 1000) == "fp8_256x256x128_masked"
-    assert name(2048, 4096, 4096, P, 4096, P, 4096, P, 2048) == "fp8_256x256x128"  # 128 tiles
-    assert name(2048, 2048, 4096, P, 4096, P, 4096, P, 2048) == "fp8_256x256x128"  # 4M outputs: partials capped
+    # grids where the 256x256 tiles fill less than half the CUs take the
+    # 128x128 tiles, splitting K by the bf16 rule (5 nk >= 100 + 2 tiles)
+    assert name(1024, 1024, 4096, P, 4096, P, 4096, P, 1024) == "fp8_128x128x128"         # 64 tiles, 32 slices
+    assert name(512, 512, 8192, P, 8192, P, 8192, P, 512) == "splitk_fp8_128x128x128"     # 16 tiles, 64 slices
+    assert name(256, 256, 8192, P, 8192, P, 8192, P, 256) == "splitk_fp8_128x128x128"     # 4 tiles
+    assert name(1024, 1024, 384, P, 384, P, 384, P, 1024) == "fp8_128x128x128"           # 3 slices
+    assert name(1000, 1000, 4096, P, 4096, P, 4096, P, 1000) == "fp8_128x128x128_masked"
+    assert name(1000, 1000, 208, P, 208, P, 208, P, 1000) == "fp8_128x128x128_masked"    # K tail
+    assert name(500, 500, 8192, P, 8192, P, 8192, P, 504) == "splitk_fp8_128x128x128_masked"
+    assert name(2048, 4096, 4096, P, 4096, P, 4096, P, 2048) == "fp8_256x256x128"  # 128 tiles of 256x256
+    assert name(2048, 2048, 4096, P, 4096, P, 4096, P, 2048) == "fp8_128x128x128"  # 256 tiles of 128x128
+    assert name(3072, 3072, 2048, P, 2048, P, 2048, P, 3072) == "fp8_256x256x128"  # 144 tiles of 256x256
     assert name(4, 4096, 4096, P, 4096, P, 4096, P + 2, 5) == "gemv_fp8"
     assert name(5, 4096, 4096, P, 4096, P, 4096, P, 8) == "skinny_fp8"
     assert name(64, 8192, 8192, P, 8192, P, 8192, P, 64) == "skinny_fp8"
-    assert name(65, 4096, 4096, P, 4096, P, 4096, P, 72) == "splitk_fp8_256x256x128_masked"  # 16 tiles: split
-    # the split must pay for its reduction: few slices on 16 or more tiles run unsplit
-    assert name(1024, 1024, 2048, P, 2048, P, 2048, P, 1024) == "fp8_256x256x128"      # 16 tiles, 16 slices
-    assert name(1024, 1024, 3072, P, 3072, P, 3072, P, 1024) == "splitk_fp8_256x256x128"  # 16 tiles, 24 slices
-    assert name(2048, 1024, 3072, P, 3072, P, 3072, P, 2048) == "fp8_256x256x128"      # 32 tiles, 24 slices
-    assert name(2048, 1024, 4096, P, 4096, P, 4096, P, 2048) == "splitk_fp8_256x256x128"  # 32 tiles, 32 slices
-    assert name(512, 512, 2048, P, 2048, P, 2048, P, 512) == "splitk_fp8_256x256x128"  # 4 tiles, 16 slices
+    assert name(65, 4096, 4096, P, 4096, P, 4096, P, 72) == "fp8_128x128x128_masked"  # 32 tiles, 32 slices
+    assert name(65, 4096, 16384, P, 16384, P, 16384, P, 72) == "splitk_fp8_128x128x128_masked"
+    assert name(1024, 1024, 2048, P, 2048, P, 2048, P, 1024) == "fp8_128x128x128"
+    assert name(2048, 1024, 4096, P, 4096, P, 4096, P, 2048) == "fp8_128x128x128"  # 128 tiles: no split
+    assert name(512, 512, 4096, P, 4096, P, 4096, P, 512) == "splitk_fp8_128x128x128"  # 16 tiles, 32 slices
+    assert name(512, 512, 2048, P, 2048, P, 2048, P, 512) == "fp8_128x128x128"         # 16 tiles, 16 slices
     assert name(1, 4096, 4040, P, 4048, P, 4048, P, 1) == "generic64x64x32"          # K % 16 != 0
 
 
@@ -169,6 +172,15 @@ def test_fp8_forced_mfma_form_names(monkeypatch):
     assert name(4000, 4096, 4096, P, 4096, P, 4096, P, 4000) == "fp8_256x256x128_mfma16_masked"
     monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", "fp8_256x256x128")
     assert name(1024, 1024, 4096, P, 4096, P, 4096, P, 1024) == "fp8_256x256x128"  # unsplit when forced
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", "splitk_fp8_256x256x128")
+    assert name(1024, 1024, 4096, P, 4096, P, 4096, P, 1024) == "splitk_fp8_256x256x128"
+    assert name(1000, 1000, 4096, P, 4096, P, 4096, P, 1000) == "splitk_fp8_256x256x128_masked"
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", "fp8_128x128x128")
+    assert name(4096, 4096, 4096, P, 4096, P, 4096, P, 4096) == "fp8_128x128x128"
+    assert name(4000, 4096, 4096, P, 4096, P, 4096, P, 4000) == "fp8_128x128x128_masked"
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", "splitk_fp8_128x128x128")
+    assert name(1024, 1024, 4096, P, 4096, P, 4096, P, 1024) == "splitk_fp8_128x128x128"
+    assert name(4096, 4096, 4096, P, 4096, P, 4096, P, 4096) == "fp8_256x256x128"  # no split on 1024 tiles
 
 
 def test_relu_is_accepted():

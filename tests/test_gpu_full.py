@@ -168,8 +168,9 @@ def test_workload_every_element(name):
     say(f"[full] workload {name}: ok n={rep['n']} max_err/tol={rep['max_err_over_tol']:.3f} exact={rep['exact']}")
 
 
-def test_fp8_workload_every_element():
-    w = inputs.WORKLOADS["fp8_4096"]
+@pytest.mark.parametrize("name", ["fp8_4096", "fp8_mid_1024x1024x4096"])
+def test_fp8_workload_every_element(name):
+    w = inputs.WORKLOADS[name]
     d = inputs.make_inputs(w)
     M, N, K = w.M, w.N, w.K
     kname = gb.gemm_fp8_kernel_name(M, N, K, 4096, K, 4096, K, 4096, M, EPI[w.epilogue])

@@ -676,13 +676,21 @@ def to_dev_u8(bits: np.ndarray, offset: int = 0):
     return full, full.data_ptr() + offset
 
 
+FP8_NAN = 0x7F  # E4M3: S.1111.111
+
+
 def check_fp8(tag, M, N, K, lda=None, ldb=None, ldc=None, alpha=1.0, beta=0.0, use_bias=False,
-              epilogue="none", scales=True, offsets=(0, 0, 0), seed=0, expect_kernel=None):
+              epilogue="none", scales=True, offsets=(0, 0, 0), seed=0, expect_kernel=None, poison_pad=False):
     lda = max(K, 1) if lda is None else lda
     ldb = max(K, 1) if ldb is None else ldb
     ldc = max(M, 1) if ldc is None else ldc
     A = inputs.normal_fp8(seed + 1, M * lda)
     B = inputs.normal_fp8(seed + 2, N * ldb)
+    if poison_pad:
+        # operand padding (k >= K) is NaN: a kernel that reads it produces NaN
+        for X, ld, rows in ((A, lda, M), (B, ldb, N)):
+            if ld > K:
+                X.reshape(rows, ld)[:, K:] = FP8_NAN
     C0 = inputs.normal_bf16(seed + 3, N * ldc)
     bias = inputs.normal_bf16(seed + 4, N, scale=0.1) if use_bias else None
     sa = inputs.uniform_f32(seed + 6, M, 0.5, 2.0) if scales else None
@@ -719,20 +727,23 @@ def check_fp8(tag, M, N, K, lda=None, ldb=None, ldc=None, alpha=1.0, beta=0.0, u
 
 
 @pytest.mark.parametrize("M,N,K", [(512, 512, 128), (512, 256, 256), (1024, 512, 640), (4096, 2048, 1280)])
-def test_fp8_ring_slice_counts(M, N, K):
+def test_fp8_ring_slice_counts(M, N, K, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", FP8R)  # small grids default to the 128x128 tiles
     check_fp8(f"fp8 ring {M}x{N}x{K}", M, N, K, seed=M + N + K, expect_kernel=FP8R)
 
 
 @pytest.mark.parametrize("beta,use_bias,epi,scales", [(b, u, e, sc) for b in (0.0, -0.75) for u in (False, True)
                                                       for e in ("none", "gelu_tanh", "relu") for sc in (True, False)
                                                       if not (u and not sc and e == "relu")])
-def test_fp8_ring_epilogue_combinations(beta, use_bias, epi, scales):
+def test_fp8_ring_epilogue_combinations(beta, use_bias, epi, scales, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", FP8R)
     check_fp8(f"fp8 ring beta={beta} bias={use_bias} {epi} scales={scales}", 1024, 512, 384, alpha=1.25,
               beta=beta, use_bias=use_bias, epilogue=epi, scales=scales,
               seed=int(abs(beta) * 4) + 2 * use_bias + len(epi) + 7 * scales, expect_kernel=FP8R)
 
 
-def test_fp8_ring_padded_leading_dims():
+def test_fp8_ring_padded_leading_dims(monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", FP8R)
     check_fp8("fp8 ring padded", 512, 768, 512, lda=528, ldb=640, ldc=520, beta=0.5, use_bias=True, seed=95,
               expect_kernel=FP8R)
 
@@ -743,10 +754,16 @@ def test_fp8_three_and_four_rows_on_large_b_take_the_streaming_kernel(M, N, K, l
               seed=M * 11 + 5, expect_kernel="skinny_fp8")
 
 
-# Split-K on the FP8 tiles for small grids: ranges of unequal length, the
-# scales applied by the reduction, every epilogue combination, forced range
-# counts, run-to-run bit equality.
+# Split-K on the 256x256 FP8 tiles (forced: on small grids the 128x128 tiles
+# are the default): ranges of unequal length, the scales applied by the
+# reduction, every epilogue combination, forced range counts, run-to-run
+# bit equality.
 FP8S = "splitk_fp8_256x256x128"
+
+
+@pytest.fixture
+def force_fp8_split256(monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", FP8S)
 
 
 @pytest.mark.parametrize("M,N,K", [
@@ -755,7 +772,7 @@ FP8S = "splitk_fp8_256x256x128"
     (256, 768, 1664),     # 3 tiles, 13 slices: ranges of 5, 5, 3
     (512, 256, 2048),     # 2 tiles, 16 slices: 4 ranges
 ])
-def test_fp8_splitk_shapes(M, N, K):
+def test_fp8_splitk_shapes(M, N, K, force_fp8_split256):
     check_fp8(f"fp8 splitk {M}x{N}x{K}", M, N, K, beta=0.5, use_bias=True, epilogue="gelu_tanh",
               seed=M + 2 * N + K, expect_kernel=FP8S)
 
@@ -763,30 +780,32 @@ def test_fp8_splitk_shapes(M, N, K):
 @pytest.mark.parametrize("beta,use_bias,epi,scales", [(b, u, e, sc) for b in (0.0, -0.75) for u in (False, True)
                                                       for e in ("none", "gelu_tanh", "relu") for sc in (True, False)
                                                       if not (u and not sc and e == "relu")])
-def test_fp8_splitk_epilogue_combinations(beta, use_bias, epi, scales):
+def test_fp8_splitk_epilogue_combinations(beta, use_bias, epi, scales, force_fp8_split256):
     check_fp8(f"fp8 splitk beta={beta} bias={use_bias} {epi} scales={scales}", 512, 256, 2048, alpha=1.25,
               beta=beta, use_bias=use_bias, epilogue=epi, scales=scales,
               seed=100 + int(abs(beta) * 4) + 2 * use_bias + len(epi) + 7 * scales, expect_kernel=FP8S)
 
 
-def test_fp8_splitk_padded_leading_dims():
+def test_fp8_splitk_padded_leading_dims(force_fp8_split256):
     check_fp8("fp8 splitk padded", 512, 512, 2048, lda=2064, ldb=2080, ldc=520, beta=0.5, use_bias=True,
               seed=131, expect_kernel=FP8S)
 
 
 @pytest.mark.parametrize("splits", ["2", "3", "5"])
-def test_fp8_splitk_forced_range_counts(splits, monkeypatch):
+def test_fp8_splitk_forced_range_counts(splits, monkeypatch, force_fp8_split256):
     monkeypatch.setenv("GEMM_BF16_FP8_SPLITS", splits)
     check_fp8(f"fp8 splitk {splits} ranges", 256, 512, 2560, beta=0.25, use_bias=True, seed=140 + int(splits),
               expect_kernel=FP8S)
 
 
-def test_fp8_splitk_deterministic():
+@pytest.mark.parametrize("kernel", [FP8S, "splitk_fp8_128x128x128"])
+def test_fp8_splitk_deterministic(kernel, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", kernel)
     M, N, K = 512, 512, 4096
     A, B = inputs.normal_fp8(150, M * K), inputs.normal_fp8(151, N * K)
     a_t, a_p = to_dev_u8(A)
     b_t, b_p = to_dev_u8(B)
-    assert gb.gemm_fp8_kernel_name(M, N, K, a_p, K, b_p, K, a_p, M) == FP8S
+    assert gb.gemm_fp8_kernel_name(M, N, K, a_p, K, b_p, K, a_p, M) == kernel
     outs = []
     for _ in range(3):
         c = torch.full((M * N,), -1, dtype=torch.int16, device="cuda")
@@ -796,6 +815,93 @@ def test_fp8_splitk_deterministic():
         torch.cuda.synchronize()
         outs.append(c.cpu().numpy())
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2]), "fp8 split-K results vary"
+
+
+# FP8 on the 128x128 tiles (32x32x64 MFMAs, K-slices of 128 values, the
+# bf16 128x128 kernel's rows and ring): whole K over 1 to 10 slices, split-K
+# (ranges of unequal length, the reduction applying the scales), tails of
+# every kind with NaN operand padding, every epilogue combination with
+# scales on and off.
+F8T128 = "fp8_128x128x128"
+F8T128M = "fp8_128x128x128_masked"
+F8T128S = "splitk_fp8_128x128x128"
+F8T128SM = "splitk_fp8_128x128x128_masked"
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 128, 128), (256, 128, 256), (512, 384, 384), (384, 512, 512),
+                                   (1024, 512, 640), (256, 768, 1152), (2048, 2048, 1280), (4096, 2048, 768)])
+def test_fp8_medium_slice_counts(M, N, K, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", F8T128)
+    check_fp8(f"fp8 128x128 {M}x{N}x{K}", M, N, K, seed=M + N + K + 600, expect_kernel=F8T128)
+
+
+@pytest.mark.parametrize("beta,use_bias,epi,scales", [(b, u, e, sc) for b in (0.0, -0.75) for u in (False, True)
+                                                      for e in ("none", "gelu_tanh", "relu") for sc in (True, False)
+                                                      if not (u and not sc and e == "relu")])
+@pytest.mark.parametrize("kernel", [F8T128, F8T128S])
+def test_fp8_medium_epilogue_combinations(kernel, beta, use_bias, epi, scales, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", kernel)
+    K = 384 if kernel == F8T128 else 2048
+    check_fp8(f"{kernel} beta={beta} bias={use_bias} {epi} scales={scales}", 512, 384, K, alpha=1.25,
+              beta=beta, use_bias=use_bias, epilogue=epi, scales=scales,
+              seed=610 + int(abs(beta) * 4) + 2 * use_bias + len(epi) + 7 * scales, expect_kernel=kernel)
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1024, 1024, 4096),  # 64 tiles, 32 slices: 4 ranges
+    (512, 512, 8192),    # 16 tiles, 64 slices: 8 ranges of 8
+    (256, 384, 2048),    # 6 tiles, 16 slices: 2 ranges
+    (128, 128, 16384),   # 1 tile, 128 slices: 16 ranges
+    (384, 256, 3200),    # 6 tiles, 25 slices: 3 ranges of 9, 9, 7
+])
+def test_fp8_medium_splitk_shapes(M, N, K, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", F8T128S)
+    check_fp8(f"fp8 128x128 splitk {M}x{N}x{K}", M, N, K, beta=0.5, use_bias=True, epilogue="gelu_tanh",
+              seed=M + 2 * N + K + 620, expect_kernel=F8T128S)
+
+
+@pytest.mark.parametrize("splits", ["2", "3", "5"])
+def test_fp8_medium_splitk_forced_range_counts(splits, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", F8T128S)
+    monkeypatch.setenv("GEMM_BF16_SPLITK_SPLITS", splits)
+    check_fp8(f"fp8 128x128 splitk {splits} ranges", 256, 384, 5120, beta=0.25, use_bias=True,
+              seed=630 + int(splits), expect_kernel=F8T128S)
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc,kernel", [
+    (1000, 1000, 1008, 1008, 1024, 1000, F8T128M),   # M, N tails; K tail of 112 in the last slice
+    (130, 70, 528, 544, 528, 136, F8T128M),          # one row / one column past a tile
+    (1001, 777, 400, 416, 400, 1003, F8T128M),       # M % 8 == 1, ldc % 8 != 0: element-wise C
+    (100, 300, 16, 16, 32, 104, F8T128M),            # a single 16-value K chunk
+    (1000, 1000, 4096, 4096, 4112, 1000, F8T128SM),  # split K with M, N tails
+    (1001, 520, 8208, 8224, 8208, 1008, F8T128SM),   # M % 8 == 1 in the reduction, K tail
+    (250, 130, 3008, 3008, 3024, 256, F8T128SM),     # 4 tiles, a K tail in the last range
+])
+def test_fp8_medium_masked_shapes(M, N, K, lda, ldb, ldc, kernel, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", kernel)
+    check_fp8(f"{kernel} {M}x{N}x{K}", M, N, K, lda=lda, ldb=ldb, ldc=ldc, beta=0.5, use_bias=True,
+              epilogue="gelu_tanh", seed=M + N + K + 640, expect_kernel=kernel, poison_pad=True)
+
+
+@pytest.mark.parametrize("M,N,K,ldc,kernel", [
+    (1024, 1024, 4096, 1024, F8T128),     # 64 tiles, 32 slices: unsplit
+    (512, 512, 8192, 512, F8T128S),      # 16 tiles, 64 slices: split
+    (1000, 1000, 4096, 1000, F8T128M),
+    (500, 500, 8192, 504, F8T128SM),
+])
+def test_fp8_small_grid_defaults(M, N, K, ldc, kernel):
+    """Without forcing, small FP8 grids take the 128x128 tiles."""
+    check_fp8(f"fp8 default {M}x{N}x{K}", M, N, K, ldc=ldc, beta=0.5, use_bias=True, epilogue="gelu_tanh",
+              seed=M + N + K + 660, expect_kernel=kernel)
+
+
+def test_fp8_medium_masked_unaligned_c(monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", F8T128M)
+    check_fp8("fp8 128x128 masked unaligned C", 520, 300, 640, ldc=521, offsets=(0, 0, 3), beta=0.5,
+              use_bias=True, epilogue="relu", seed=650, expect_kernel=F8T128M)
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", F8T128SM)
+    check_fp8("fp8 128x128 splitk masked unaligned C", 520, 300, 4000, ldc=523, offsets=(0, 0, 5), beta=-0.5,
+              use_bias=True, epilogue="gelu_tanh", seed=651, expect_kernel=F8T128SM)
 
 
 # The FP8 tile kernel on 32x32x64 MFMAs forced onto exact tiles (its masked
@@ -853,13 +959,15 @@ def test_fp8_mfma16_masked_epilogue_combinations(beta, use_bias, epi, scales, mo
               seed=560 + int(abs(beta) * 4) + 2 * use_bias + len(epi) + 7 * scales, expect_kernel=FP8R16M)
 
 
-# The masked FP8 instance: M and N tails of every size class, K tails down
-# to a single 16-byte chunk, padded leading dimensions, epilogue
-# combinations, and exact tile multiples forced through it.
+# The masked 256x256 FP8 instance (forced: small grids take the 128x128
+# tiles): M and N tails of every size class, K tails down to a single
+# 16-byte chunk, padded leading dimensions, epilogue combinations, and exact
+# tile multiples forced through it.
 FP8M = "fp8_256x256x128_masked"
 
 
-def test_fp8_masked_odd_ldc():
+def test_fp8_masked_odd_ldc(monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", FP8M)
     check_fp8("fp8 masked odd ldc", 1001, 777, 208, lda=224, ldb=208, ldc=1003, beta=0.5, use_bias=True,
               epilogue="relu", seed=420, expect_kernel=FP8M)
     check_fp8("fp8 masked unaligned C", 512, 512, 256, ldc=520, offsets=(0, 0, 3), beta=-0.5, seed=421,
@@ -880,7 +988,7 @@ def test_fp8_masked_tails(M, N, K, lda, ldb, ldc, monkeypatch):
               expect_kernel=FP8M)
 
 
-# Split-K on the masked FP8 kernel (tails on small grids): whole tiles into a
+# Split-K on the masked 256x256 FP8 kernel (forced): whole tiles into a
 # padded workspace, K tails in the last range, M % 8 != 0 in the reduction.
 FP8SM = "splitk_fp8_256x256x128_masked"
 
@@ -891,7 +999,8 @@ FP8SM = "splitk_fp8_256x256x128_masked"
     (300, 260, 2064, 2064, 2064, 304),   # 4 tiles, 17 slices: 4 ranges, a 16-wide K tail
     (1001, 777, 4000, 4000, 4000, 1001), # ldc % 8 != 0: element-wise C in the reduction
 ])
-def test_fp8_masked_splitk_shapes(M, N, K, lda, ldb, ldc):
+def test_fp8_masked_splitk_shapes(M, N, K, lda, ldb, ldc, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", FP8SM)
     check_fp8(f"fp8 masked splitk {M}x{N}x{K}", M, N, K, lda=lda, ldb=ldb, ldc=ldc, beta=0.5, use_bias=True,
               epilogue="gelu_tanh", seed=M + N + K + 400, expect_kernel=FP8SM)
 
@@ -899,7 +1008,8 @@ def test_fp8_masked_splitk_shapes(M, N, K, lda, ldb, ldc):
 @pytest.mark.parametrize("beta,use_bias,epi,scales", [(b, u, e, sc) for b in (0.0, -0.75) for u in (False, True)
                                                       for e in ("none", "gelu_tanh", "relu") for sc in (True, False)
                                                       if not (u and not sc and e == "relu")])
-def test_fp8_masked_splitk_epilogue_combinations(beta, use_bias, epi, scales):
+def test_fp8_masked_splitk_epilogue_combinations(beta, use_bias, epi, scales, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", FP8SM)
     check_fp8(f"fp8 masked splitk beta={beta} bias={use_bias} {epi} scales={scales}", 777, 300, 2000, ldc=784,
               alpha=1.25, beta=beta, use_bias=use_bias, epilogue=epi, scales=scales,
               seed=410 + int(abs(beta) * 4) + 2 * use_bias + len(epi) + 7 * scales, expect_kernel=FP8SM)
@@ -907,7 +1017,8 @@ def test_fp8_masked_splitk_epilogue_combinations(beta, use_bias, epi, scales):
 
 @pytest.mark.parametrize("beta,use_bias,epi", [(b, u, e) for b in (0.0, -0.75) for u in (False, True)
                                                for e in ("none", "gelu_tanh", "relu")])
-def test_fp8_masked_epilogue_combinations(beta, use_bias, epi):
+def test_fp8_masked_epilogue_combinations(beta, use_bias, epi, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", FP8M)
     check_fp8(f"fp8 masked beta={beta} bias={use_bias} {epi}", 777, 300, 208, ldc=784, alpha=1.25, beta=beta,
               use_bias=use_bias, epilogue=epi, seed=17 + int(abs(beta) * 4) + 2 * use_bias + len(epi),
               expect_kernel=FP8M)
