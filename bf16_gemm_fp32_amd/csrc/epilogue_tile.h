@@ -66,7 +66,8 @@ __device__ __forceinline__ void tile_epilogue(char *smem, const GemmArgs &args, 
                         cin[2 * e + 1] = bf16_bits_to_f32(raw[e] >> 16);
                     }
                 } else {
-                    for (int e = 0; e < 8 && m + e < args.M; ++e) cin[e] = bf16_bits_to_f32(p[e]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) if (m + e < args.M) cin[e] = bf16_bits_to_f32(p[e]);
                 }
             }
             float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -92,7 +93,8 @@ __device__ __forceinline__ void tile_epilogue(char *smem, const GemmArgs &args, 
             if (full) {
                 __builtin_nontemporal_store(out, (u32x4 *)p);
             } else {
-                for (int e = 0; e < 8 && m + e < args.M; ++e) p[e] = (uint16_t)(out[e >> 1] >> ((e & 1) * 16));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) if (m + e < args.M) p[e] = (uint16_t)(out[e >> 1] >> ((e & 1) * 16));
             }
         }
     }

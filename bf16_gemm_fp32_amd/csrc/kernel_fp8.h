@@ -81,23 +81,56 @@ struct Fp8Kernel {
         uint32_t lda_bytes, ldb_bytes;
         int wave;
         // masking only: this lane's row within a load's 8 rows, its logical
-        // chunk by parity of the row group, and the tile's valid extents
+        // chunk by parity of the row group, and the tile's valid extents;
+        // per tile, the voffset of each of this wave's loads of a unit with
+        // rows past M or N already out of range (vAr, vBr); the last slice
+        // (klast) and, by parity, the out-of-range bit of this lane's chunk
+        // in that slice (kx: 0 or kOobOffset)
         int lrow, lchunk[2];
         int rowsA, rowsB, kmax;
+        uint32_t vAr[kMasked ? Cfg::kUnitLoads : 1], vBr[kMasked ? Cfg::kUnitLoads : 1], kx[2];
+        int klast;
     };
+
+    // Masking state (kMasked): the K tail (per launch, or per unit when K
+    // is split) and the rows (per tile).  Only the last slice can hold
+    // chunks at or past K, so a load's voffset in the K loop is its
+    // row-masked one, with kx or-ed in when kt is that slice.
+    __device__ __forceinline__ static void mask_k(Lane &L, int nk) {
+        L.klast = __builtin_amdgcn_readfirstlane(nk - 1);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) L.kx[p] = (nk - 1) * Cfg::BK + L.lchunk[p] * 16 < L.kmax ? 0u : kOobOffset;
+    }
+    __device__ __forceinline__ static void mask_rows(Lane &L) {
+#pragma unroll
+        for (int l = 0; l < Cfg::kUnitLoads; ++l) {
+            const int q = L.wave * Cfg::kUnitLoads + l;
+            const int row = q * Cfg::kRowsPerLoad + L.lrow;
+            L.vAr[l] = row < L.rowsA ? L.vA[q & 1] : kOobOffset;
+            L.vBr[l] = row < L.rowsB ? L.vB[q & 1] : kOobOffset;
+        }
+    }
 
     // DMA load number l (0..7) of this wave for one operand unit: rows
     // 8q .. 8q+7 of the tile, q = 8 * wave + l, K-slice kt, into the slot.
-    template <bool kIsA>
+    // kK (masked instances): whether kt is the unit's last slice -- kKAny:
+    // decided at run time; kKBefore: known to come before it (rows masked
+    // only); kKLast: known to be it.
+    enum : int { kKAny = 0, kKBefore = 1, kKLast = 2 };
+    template <bool kIsA, int kK = kKAny>
     __device__ __forceinline__ static void load(char *smem, int slot, int kt, int l, const Lane &L,
                                                 __amdgpu_buffer_rsrc_t rsrc) {
         const int q = L.wave * Cfg::kUnitLoads + l;
         const uint32_t ld = kIsA ? L.lda_bytes : L.ldb_bytes;
         uint32_t voff = kIsA ? L.vA[q & 1] : L.vB[q & 1];
         if constexpr (kMasked) {
-            const int row = q * Cfg::kRowsPerLoad + L.lrow;
-            const int k = kt * Cfg::BK + L.lchunk[q & 1] * 16;
-            if (!(row < (kIsA ? L.rowsA : L.rowsB) && k < L.kmax)) voff = kOobOffset;
+            const uint32_t rows = kIsA ? L.vAr[l] : L.vBr[l];
+            if constexpr (kK == kKBefore)
+                voff = rows;
+            else if constexpr (kK == kKLast)
+                voff = L.kx[q & 1] | rows;
+            else
+                voff = (L.kx[q & 1] & (kt == L.klast ? 0xFFFFFFFFu : 0u)) | rows;
         }
         buffer_load_lds16(rsrc, (GB_LDS void *)(smem + slot * Cfg::kUnitBytes + q * 1024), voff,
                           (uint32_t)(q * Cfg::kRowsPerLoad) * ld + (uint32_t)kt * Cfg::kRowBytes);
@@ -109,7 +142,7 @@ struct Fp8Kernel {
     // (if kRead) after MFMA s one 16-byte half of a fragment of k-step rks
     // from slots (rsa, rsb) into (ra, rb); (if kLoad) after MFMA 2l+1 the
     // DMA load l of the unit (kLoad's operand) of slice lkt into slot lslot.
-    template <bool kRead, int kLoad>
+    template <bool kRead, int kLoad, int kK = kKAny>
     __device__ __forceinline__ static void kstep(char *smem, const i32x8 (&a)[Cfg::FM], const i32x8 (&b)[Cfg::FN],
                                                  f32x16 (&acc)[Cfg::FM][Cfg::FN], int rsa, int rsb, int rks,
                                                  i32x8 (&ra)[Cfg::FM], i32x8 (&rb)[Cfg::FN], int lslot, int lkt,
@@ -143,9 +176,9 @@ struct Fp8Kernel {
             if (kLoad != kNoLoad && (s & 1) == 1) {
                 const int l = s >> 1;
                 if (kLoad == kLoadA)
-                    load<true>(smem, lslot, lkt, l, L, rA);
+                    load<true, kK>(smem, lslot, lkt, l, L, rA);
                 else
-                    load<false>(smem, lslot, lkt, l, L, rB);
+                    load<false, kK>(smem, lslot, lkt, l, L, rB);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -158,7 +191,7 @@ struct Fp8Kernel {
     //   wait for A(j+1), B(j+1); barrier   (modes 0, 1)
     //   k-step 1: reads slice j+1's k-step 0 (modes 0, 1);
     //             loads B(j+2) into A(j)'s slot (mode 0)
-    template <int kMode>
+    template <int kMode, int kK = kKAny>
     __device__ __forceinline__ static void slice(char *smem, int j, int sa, const Lane &L,
                                                  __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rB,
                                                  i32x8 (&fa)[2][Cfg::FM], i32x8 (&fb)[2][Cfg::FN],
@@ -169,7 +202,7 @@ struct Fp8Kernel {
         const int sa2 = fp8_slot(sa + 4);  // A(j+2)
         constexpr int kL0 = kMode == 0 ? kLoadA : kNoLoad;
         constexpr int kL1 = kMode == 0 ? kLoadB : kNoLoad;
-        kstep<true, kL0>(smem, fa[0], fb[0], acc, sa, sb, 1, fa[1], fb[1], sa2, j + 2, L, rA, rB);
+        kstep<true, kL0, kK>(smem, fa[0], fb[0], acc, sa, sb, 1, fa[1], fb[1], sa2, j + 2, L, rA, rB);
         if constexpr (kMode <= 1) {
             if constexpr (kMode == 0)
                 wait_vmcnt<Cfg::kUnitLoads>();
@@ -177,7 +210,7 @@ struct Fp8Kernel {
                 wait_vmcnt<0>();
             lds_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            kstep<true, kL1>(smem, fa[1], fb[1], acc, san, sbn, 0, fa[0], fb[0], sa, j + 2, L, rA, rB);
+            kstep<true, kL1, kK>(smem, fa[1], fb[1], acc, san, sbn, 0, fa[0], fb[0], sa, j + 2, L, rA, rB);
         } else {
             kstep<false, kNoLoad>(smem, fa[1], fb[1], acc, 0, 0, 0, fa[0], fb[0], 0, 0, L, rA, rB);
         }
@@ -243,7 +276,8 @@ __device__ __forceinline__ void fp8_epilogue(char *smem, const GemmArgs &args, i
                         cin[2 * e + 1] = bf16_bits_to_f32(raw[e] >> 16);
                     }
                 } else {
-                    for (int e = 0; e < 8 && m + e < args.M; ++e) cin[e] = bf16_bits_to_f32(p[e]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) if (m + e < args.M) cin[e] = bf16_bits_to_f32(p[e]);
                 }
             }
             const float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -257,7 +291,8 @@ __device__ __forceinline__ void fp8_epilogue(char *smem, const GemmArgs &args, i
             if (full) {
                 __builtin_nontemporal_store(out, (u32x4 *)p);
             } else {
-                for (int e = 0; e < 8 && m + e < args.M; ++e) p[e] = (uint16_t)(out[e >> 1] >> ((e & 1) * 16));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) if (m + e < args.M) p[e] = (uint16_t)(out[e >> 1] >> ((e & 1) * 16));
             }
         }
     }
@@ -337,6 +372,8 @@ gemm_fp8_kernel(const GemmArgs args, const TileSchedule sched, const TileSplit s
         if constexpr (kMasked) {
             Ln.rowsA = (int)(args.M - m0 < Cfg::BM ? args.M - m0 : Cfg::BM);
             Ln.rowsB = (int)(args.N - n0 < Cfg::BN ? args.N - n0 : Cfg::BN);
+            RK::mask_rows(Ln);
+            RK::mask_k(Ln, nk);
         }
         const __amdgpu_buffer_rsrc_t rA =
             make_rsrc(A8 + m0 * args.lda + k0, (uint32_t)((Cfg::BM - 1) * args.lda + kn));
@@ -386,9 +423,23 @@ gemm_fp8_kernel(const GemmArgs args, const TileSchedule sched, const TileSplit s
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
 
         int j = 0, sa = 0;
-        for (; j + 2 < nk; ++j) {
-            RK::template slice<0>(smem, j, sa, Ln, rA, rB, fa, fb, acc);
-            sa = fp8_slot(sa + 2);
+        if constexpr (kMasked) {
+            // the slices that load A(j+2), B(j+2) before the unit's last
+            // one, then the one that loads the last
+            for (; j + 3 < nk; ++j) {
+                RK::template slice<0, RK::kKBefore>(smem, j, sa, Ln, rA, rB, fa, fb, acc);
+                sa = fp8_slot(sa + 2);
+            }
+            if (j + 2 < nk) {
+                RK::template slice<0, RK::kKLast>(smem, j, sa, Ln, rA, rB, fa, fb, acc);
+                ++j;
+                sa = fp8_slot(sa + 2);
+            }
+        } else {
+            for (; j + 2 < nk; ++j) {
+                RK::template slice<0>(smem, j, sa, Ln, rA, rB, fa, fb, acc);
+                sa = fp8_slot(sa + 2);
+            }
         }
         if (j + 1 < nk) {
             RK::template slice<1>(smem, j, sa, Ln, rA, rB, fa, fb, acc);

@@ -92,10 +92,35 @@ struct Fp8Ring16Kernel {
         uint32_t lda_bytes, ldb_bytes;
         int wave, nk;
         // masking only: this lane's row within a load's 8 rows, its logical
-        // chunk by parity of the row group, and the tile's valid extents
+        // chunk by parity of the row group, and the tile's valid extents;
+        // per tile, the voffset of each of this wave's loads of a unit with
+        // rows past M or N already out of range (vAr, vBr); the last slice
+        // (klast) and, by parity, the out-of-range bit of this lane's chunk
+        // in that slice (kx: 0 or kOobOffset)
         int lrow, lchunk[2];
         int rowsA, rowsB, kmax;
+        uint32_t vAr[kMasked ? Cfg::kUnitLoads : 1], vBr[kMasked ? Cfg::kUnitLoads : 1], kx[2];
+        int klast;
     };
+
+    // Masking state (kMasked): the K tail (per launch, or per unit when K
+    // is split) and the rows (per tile).  Only the last slice can hold
+    // chunks at or past K, so a load's voffset in the K loop is its
+    // row-masked one, with kx or-ed in when kt is that slice.
+    __device__ __forceinline__ static void mask_k(Lane &L, int nk) {
+        L.klast = __builtin_amdgcn_readfirstlane(nk - 1);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) L.kx[p] = (nk - 1) * Cfg::BK + L.lchunk[p] * 16 < L.kmax ? 0u : kOobOffset;
+    }
+    __device__ __forceinline__ static void mask_rows(Lane &L) {
+#pragma unroll
+        for (int l = 0; l < Cfg::kUnitLoads; ++l) {
+            const int q = L.wave * Cfg::kUnitLoads + l;
+            const int row = q * Cfg::kRowsPerLoad + L.lrow;
+            L.vAr[l] = row < L.rowsA ? L.vA[q & 1] : kOobOffset;
+            L.vBr[l] = row < L.rowsB ? L.vB[q & 1] : kOobOffset;
+        }
+    }
 
     // DMA load number l (0..7) of this wave for one operand unit: rows
     // 8q .. 8q+7 of the tile, q = 8 * wave + l, K-slice kt, into the slot.
@@ -105,18 +130,27 @@ struct Fp8Ring16Kernel {
     // check covers; the scalar offset stays the in-range row offset (its
     // sum with the out-of-range voffset stays below 2^32, so nothing wraps
     // back into range).
-    template <bool kIsA>
+    //
+    // kK: where kt lies -- kKAny: decided at run time (a slice past the end,
+    // the last slice or one before it); kKBefore: known to come before the
+    // last slice (no K test; rows masked only); kKLast: known to be it.
+    enum : int { kKAny = 0, kKBefore = 1, kKLast = 2 };
+    template <bool kIsA, int kK = kKAny>
     __device__ __forceinline__ static void load(char *smem, int slot, int kt, int l, const Lane &L,
                                                 __amdgpu_buffer_rsrc_t rsrc) {
         const int q = L.wave * Cfg::kUnitLoads + l;
         const uint32_t ld = kIsA ? L.lda_bytes : L.ldb_bytes;
         uint32_t voff = kIsA ? L.vA[q & 1] : L.vB[q & 1];
         if constexpr (kMasked) {
-            const int row = q * Cfg::kRowsPerLoad + L.lrow;
-            const int k = kt * Cfg::BK + L.lchunk[q & 1] * 16;
-            if (!(row < (kIsA ? L.rowsA : L.rowsB) && k < L.kmax)) voff = kOobOffset;
+            const uint32_t rows = kIsA ? L.vAr[l] : L.vBr[l];
+            if constexpr (kK == kKBefore)
+                voff = rows;
+            else if constexpr (kK == kKLast)
+                voff = L.kx[q & 1] | rows;
+            else
+                voff = (L.kx[q & 1] & (kt == L.klast ? 0xFFFFFFFFu : 0u)) | rows;
         }
-        const bool in_k = kt < L.nk;
+        const bool in_k = kK != kKAny || kt < L.nk;
         if (!in_k) voff = kOobOffset;
         buffer_load_lds16(rsrc, (GB_LDS void *)(smem + slot * Cfg::kUnitBytes + q * 1024), voff,
                           (uint32_t)(q * Cfg::kRowsPerLoad) * ld + (in_k ? (uint32_t)kt * Cfg::kRowBytes : 0u));
@@ -140,7 +174,7 @@ struct Fp8Ring16Kernel {
         return (((s >> 4) & 1) ? 4 : 0) + ((s >> 4) < 2 ? ((s & 15) >> 2) : (s & 3));
     }
 
-    template <int kMode, class Mid>
+    template <int kMode, int kK, class Mid>
     __device__ __forceinline__ static void slice(char *smem, int j, int sa, const Lane &L,
                                                  __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rB,
                                                  i32x8 (&fa)[Cfg::FM], i32x8 (&fb)[Cfg::FN],
@@ -181,9 +215,9 @@ struct Fp8Ring16Kernel {
             if (kMode == kFull && (s & 3) == 1) {
                 const int l = s >> 2;  // 0..15
                 if (l < Cfg::kUnitLoads)
-                    load<true>(smem, slotA2, j + 2, l, L, rA);
+                    load<true, kK>(smem, slotA2, j + 2, l, L, rA);
                 else
-                    load<false>(smem, slotB2, j + 2, l - Cfg::kUnitLoads, L, rB);
+                    load<false, kK>(smem, slotB2, j + 2, l - Cfg::kUnitLoads, L, rB);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -233,6 +267,7 @@ gemm_fp8_ring16_kernel(const GemmArgs args, const TileSchedule sched) {
     Ln.hi_off = (uint32_t)(((4 + (lane >> 4)) ^ ring_swizzle(lane & 15)) << 4);
 
     const int nk = Ln.nk;
+    if constexpr (kMasked) RK::mask_k(Ln, nk);
     const int num_tiles = sched.num_tiles();
 
     for (int t = sched.slot(blockIdx.x); t < num_tiles; t += sched.grid) {
@@ -243,6 +278,7 @@ gemm_fp8_ring16_kernel(const GemmArgs args, const TileSchedule sched) {
         if constexpr (kMasked) {
             Ln.rowsA = (int)(args.M - m0 < Cfg::BM ? args.M - m0 : Cfg::BM);
             Ln.rowsB = (int)(args.N - n0 < Cfg::BN ? args.N - n0 : Cfg::BN);
+            RK::mask_rows(Ln);
         }
         const __amdgpu_buffer_rsrc_t rA = make_rsrc(A8 + m0 * args.lda, (uint32_t)((Cfg::BM - 1) * args.lda + args.K));
         const __amdgpu_buffer_rsrc_t rB = make_rsrc(B8 + n0 * args.ldb, (uint32_t)((Cfg::BN - 1) * args.ldb + args.K));
@@ -281,15 +317,29 @@ gemm_fp8_ring16_kernel(const GemmArgs args, const TileSchedule sched) {
 
         using K = RK;
         const auto none = [] {};
-        int sa = 0;
-        for (int j = 0; j + 1 < nk; ++j) {
-            RK::template slice<K::kFull>(smem, j, sa, Ln, rA, rB, fa, fb, acc, none);
+        // Slice j loads slice j + 2.  Masked: before the last one while
+        // j + 3 < nk, then the last one, then (j = nk - 2) one past the end;
+        // unmasked, one loop that tests for slices past the end.
+        int sa = 0, j = 0;
+        if constexpr (kMasked) {
+            for (; j + 3 < nk; ++j) {
+                RK::template slice<K::kFull, K::kKBefore>(smem, j, sa, Ln, rA, rB, fa, fb, acc, none);
+                sa = ring_slot(sa + 2);
+            }
+            if (j + 2 < nk) {
+                RK::template slice<K::kFull, K::kKLast>(smem, j, sa, Ln, rA, rB, fa, fb, acc, none);
+                ++j;
+                sa = ring_slot(sa + 2);
+            }
+        }
+        for (; j + 1 < nk; ++j) {
+            RK::template slice<K::kFull, K::kKAny>(smem, j, sa, Ln, rA, rB, fa, fb, acc, none);
             sa = ring_slot(sa + 2);
         }
         // The epilogue's first C / bias / scale values load during the last slice.
         RingEpiInputs epi_in;
         const auto mid = [&] { ring_epi_load<kFlags, kMasked, true>(epi_in, args, m0, n0, wm, wn, lane, 0); };
-        RK::template slice<K::kLast>(smem, nk - 1, sa, Ln, rA, rB, fa, fb, acc, mid);
+        RK::template slice<K::kLast, K::kKAny>(smem, nk - 1, sa, Ln, rA, rB, fa, fb, acc, mid);
         // With beta or masking, every MFMA of the tile completes here: the
         // compiler may not sink the last slice's MFMAs into the epilogue,
         // where their fragments would stay live beside the C loads and the

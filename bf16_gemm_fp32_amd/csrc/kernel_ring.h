@@ -123,24 +123,57 @@ struct RingKernel {
         uint32_t lda_bytes, ldb_bytes;
         int wave;
         // masking only: this lane's row within a load's 8 rows, its logical
-        // chunk by parity of the row group, and the tile's valid extents
+        // chunk by parity of the row group, and the tile's valid extents;
+        // per tile, the voffset of each of this wave's loads of a unit with
+        // rows past M or N already out of range (vAr, vBr); the last slice
+        // (klast) and, by parity, the out-of-range bit of this lane's chunk
+        // in that slice (kx: 0 or kOobOffset)
         int lrow, lchunk[2];
         int rowsA, rowsB, kmax;
+        uint32_t vAr[kMasked ? Cfg::kUnitLoads : 1], vBr[kMasked ? Cfg::kUnitLoads : 1], kx[2];
+        int klast;
     };
+
+    // Masking state (kMasked): the K tail once per launch, the rows once per
+    // tile.  Only the last slice can hold chunks at or past K, so a load's
+    // voffset in the K loop is its row-masked one, with kx or-ed in when kt
+    // is that slice: one vector instruction per load.
+    __device__ __forceinline__ static void mask_k(Lane &L, int nk) {
+        L.klast = __builtin_amdgcn_readfirstlane(nk - 1);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) L.kx[p] = (nk - 1) * Cfg::BK + L.lchunk[p] * 8 < L.kmax ? 0u : kOobOffset;
+    }
+    __device__ __forceinline__ static void mask_rows(Lane &L) {
+#pragma unroll
+        for (int l = 0; l < Cfg::kUnitLoads; ++l) {
+            const int q = L.wave * Cfg::kUnitLoads + l;
+            const int row = q * Cfg::kRowsPerLoad + L.lrow;
+            L.vAr[l] = row < L.rowsA ? L.vA[q & 1] : kOobOffset;
+            L.vBr[l] = row < L.rowsB ? L.vB[q & 1] : kOobOffset;
+        }
+    }
 
     // DMA load number l (0 .. kUnitLoads-1) of this wave for one operand
     // unit: rows 8q .. 8q+7 of the tile, q = kUnitLoads * wave + l, K-slice
     // kt, into the slot.
-    template <bool kIsA>
+    // kK (masked instances): whether kt is the last slice -- kKAny: decided
+    // at run time; kKBefore: known to come before it (rows masked only, no
+    // vector instruction); kKLast: known to be it.
+    enum : int { kKAny = 0, kKBefore = 1, kKLast = 2 };
+    template <bool kIsA, int kK = kKAny>
     __device__ __forceinline__ static void load(char *smem, int slot, int kt, int l, const Lane &L,
                                                 __amdgpu_buffer_rsrc_t rsrc) {
         const int q = L.wave * Cfg::kUnitLoads + l;
         const uint32_t ld = kIsA ? L.lda_bytes : L.ldb_bytes;
         uint32_t voff = kIsA ? L.vA[q & 1] : L.vB[q & 1];
         if constexpr (kMasked) {
-            const int row = q * Cfg::kRowsPerLoad + L.lrow;
-            const int k = kt * Cfg::BK + L.lchunk[q & 1] * 8;
-            if (!(row < (kIsA ? L.rowsA : L.rowsB) && k < L.kmax)) voff = kOobOffset;
+            const uint32_t rows = kIsA ? L.vAr[l] : L.vBr[l];
+            if constexpr (kK == kKBefore)
+                voff = rows;
+            else if constexpr (kK == kKLast)
+                voff = L.kx[q & 1] | rows;
+            else
+                voff = (L.kx[q & 1] & (kt == L.klast ? 0xFFFFFFFFu : 0u)) | rows;
         }
         buffer_load_lds16(rsrc, (GB_LDS void *)(smem + slot * Cfg::kUnitBytes + q * 1024), voff,
                           (uint32_t)(q * Cfg::kRowsPerLoad) * ld + (uint32_t)kt * Cfg::kRowBytes);
@@ -166,7 +199,7 @@ struct RingKernel {
     // into (ra, rb) and (if kLoad) the DMA loads of the unit (kLoad's
     // operand) of slice lkt into slot lslot, each in the MFMA shadow that
     // read_at / load_at assign it.
-    template <bool kRead, int kLoad>
+    template <bool kRead, int kLoad, int kK = kKAny>
     __device__ __forceinline__ static void kstep(char *smem, const bf16x8 (&a)[Cfg::FM], const bf16x8 (&b)[Cfg::FN],
                                                  f32x4 (&acc)[Cfg::FM][Cfg::FN], int rsa, int rsb, int rks,
                                                  bf16x8 (&ra)[Cfg::FM], bf16x8 (&rb)[Cfg::FN], int lslot, int lkt,
@@ -189,9 +222,9 @@ struct RingKernel {
             const int l = load_at(s);
             if (kLoad != kNoLoad && l >= 0) {
                 if (kLoad == kLoadA)
-                    load<true>(smem, lslot, lkt, l, L, rA);
+                    load<true, kK>(smem, lslot, lkt, l, L, rA);
                 else
-                    load<false>(smem, lslot, lkt, l, L, rB);
+                    load<false, kK>(smem, lslot, lkt, l, L, rB);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -205,7 +238,7 @@ struct RingKernel {
     //   wait for A(j+1), B(j+1); barrier   (modes 0, 1)
     //   k-step 1: reads slice j+1's k-step 0 (modes 0, 1);
     //             loads B(j+2) into A(j)'s slot (mode 0)
-    template <int kMode, class Mid>
+    template <int kMode, int kK = kKAny, class Mid>
     __device__ __forceinline__ static void slice(char *smem, int j, int sa, const Lane &L,
                                                  __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rB,
                                                  bf16x8 (&fa)[2][Cfg::FM], bf16x8 (&fb)[2][Cfg::FN],
@@ -216,7 +249,7 @@ struct RingKernel {
         const int sa2 = ring_slot(sa + 4);  // A(j+2)
         constexpr int kL0 = kMode == 0 ? kLoadA : kNoLoad;
         constexpr int kL1 = kMode == 0 ? kLoadB : kNoLoad;
-        kstep<true, kL0>(smem, fa[0], fb[0], acc, sa, sb, 1, fa[1], fb[1], sa2, j + 2, L, rA, rB);
+        kstep<true, kL0, kK>(smem, fa[0], fb[0], acc, sa, sb, 1, fa[1], fb[1], sa2, j + 2, L, rA, rB);
         if constexpr (kMode <= 1) {
             if constexpr (kMode == 0)
                 wait_vmcnt<Cfg::kUnitLoads>();
@@ -224,7 +257,7 @@ struct RingKernel {
                 wait_vmcnt<0>();
             lds_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            kstep<true, kL1>(smem, fa[1], fb[1], acc, san, sbn, 0, fa[0], fb[0], sa, j + 2, L, rA, rB);
+            kstep<true, kL1, kK>(smem, fa[1], fb[1], acc, san, sbn, 0, fa[0], fb[0], sa, j + 2, L, rA, rB);
         } else {
             // k-step 0's fragments are dead: their registers take mid()'s loads
             mid();
@@ -277,7 +310,8 @@ __device__ __forceinline__ void ring_epi_load(RingEpiInputs &in, const GemmArgs 
                     in.c[t] = *(const u32x4 *)p;
                 } else if (m < args.M) {
                     uint32_t w[4] = {0u, 0u, 0u, 0u};
-                    for (int e = 0; e < 8 && m + e < args.M; ++e) w[e >> 1] |= (uint32_t)p[e] << ((e & 1) * 16);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) if (m + e < args.M) w[e >> 1] |= (uint32_t)p[e] << ((e & 1) * 16);
                     in.c[t] = u32x4{w[0], w[1], w[2], w[3]};
                 }
             }
@@ -313,7 +347,8 @@ __device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, 
             sc[0] = lo.x; sc[1] = lo.y; sc[2] = lo.z; sc[3] = lo.w;
             sc[4] = hi.x; sc[5] = hi.y; sc[6] = hi.z; sc[7] = hi.w;
         } else {
-            for (int e = 0; e < 8 && m + e < args.M; ++e) sc[e] = args.scale[m + e];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) if (m + e < args.M) sc[e] = args.scale[m + e];
         }
     }
     float sa[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
@@ -325,11 +360,16 @@ __device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, 
                 if (!kMasked || m + e < args.M) sa[e] = args.scale_a[m + e];
         }
     }
+    // The masked instances load a group's inputs at its start instead of
+    // one group ahead: with their per-tile masks live, a second set of
+    // inputs would not fit in the registers.
+    constexpr bool kAhead = !kMasked;
 #pragma unroll
     for (int jj = 0; jj < Cfg::FN / 2; ++jj) {
         RingEpiInputs next;
-        if (jj + 1 < Cfg::FN / 2)
+        if (kAhead && jj + 1 < Cfg::FN / 2)
             ring_epi_load<kFlags, kMasked, kScaled, Cfg>(next, args, m0, n0, wm, wn, lane, jj + 1);
+        if (!kAhead && jj > 0) ring_epi_load<kFlags, kMasked, kScaled, Cfg>(in, args, m0, n0, wm, wn, lane, jj);
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
@@ -371,7 +411,8 @@ __device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, 
                 if (!kMasked || (n < args.N && m + 8 <= args.M)) {
                     __builtin_nontemporal_store(qw, (u32x2 *)qp);
                 } else if (n < args.N) {
-                    for (int e = 0; e < 8 && m + e < args.M; ++e) qp[e] = (int8_t)(qw[e >> 2] >> ((e & 3) * 8));
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) if (m + e < args.M) qp[e] = (int8_t)(qw[e >> 2] >> ((e & 3) * 8));
                 }
                 continue;
             }
@@ -387,7 +428,8 @@ __device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, 
                     if (m + 8 <= args.M && (args.ldc & 7) == 0 && (reinterpret_cast<uintptr_t>(args.C) & 15) == 0) {
                         __builtin_nontemporal_store(out, (u32x4 *)p);
                     } else {
-                        for (int e = 0; e < 8 && m + e < args.M; ++e)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) if (m + e < args.M)
                             p[e] = (uint16_t)(out[e >> 1] >> ((e & 1) * 16));
                     }
                 }
@@ -395,7 +437,7 @@ __device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, 
                 __builtin_nontemporal_store(out, (u32x4 *)p);
             }
         }
-        if (jj + 1 < Cfg::FN / 2) in = next;
+        if (kAhead && jj + 1 < Cfg::FN / 2) in = next;
     }
 }
 
@@ -441,6 +483,7 @@ gemm_ring_kernel(const GemmArgs args, const TileSchedule sched) {
         Ln.chunk_off[ks] = (uint32_t)(((4 * ks + (lane >> 4)) ^ ring_swizzle(lane & 15)) << 4);
 
     const int nk = (int)((args.K + Cfg::BK - 1) / Cfg::BK);
+    if constexpr (kMasked) RK::mask_k(Ln, nk);
     const int num_tiles = sched.num_tiles();
 
     // The tile a workgroup works on: its origin and operand buffers (and,
@@ -460,6 +503,7 @@ gemm_ring_kernel(const GemmArgs args, const TileSchedule sched) {
         if constexpr (kMasked) {
             Ln.rowsA = (int)(args.M - r.m0 < Cfg::BM ? args.M - r.m0 : Cfg::BM);
             Ln.rowsB = (int)(args.N - r.n0 < Cfg::BN ? args.N - r.n0 : Cfg::BN);
+            RK::mask_rows(Ln);
         }
         return r;
     };
@@ -521,9 +565,23 @@ gemm_ring_kernel(const GemmArgs args, const TileSchedule sched) {
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
 
         int j = 0, sa = s0;
-        for (; j + 2 < nk; ++j) {
-            RK::template slice<0>(smem, j, sa, Ln, cur.rA, cur.rB, fa, fb, acc, [] {});
-            sa = ring_slot(sa + 2);
+        if constexpr (kMasked) {
+            // the slices that load A(j+2), B(j+2) before the last one, then
+            // the one that loads the last
+            for (; j + 3 < nk; ++j) {
+                RK::template slice<0, RK::kKBefore>(smem, j, sa, Ln, cur.rA, cur.rB, fa, fb, acc, [] {});
+                sa = ring_slot(sa + 2);
+            }
+            if (j + 2 < nk) {
+                RK::template slice<0, RK::kKLast>(smem, j, sa, Ln, cur.rA, cur.rB, fa, fb, acc, [] {});
+                ++j;
+                sa = ring_slot(sa + 2);
+            }
+        } else {
+            for (; j + 2 < nk; ++j) {
+                RK::template slice<0>(smem, j, sa, Ln, cur.rA, cur.rB, fa, fb, acc, [] {});
+                sa = ring_slot(sa + 2);
+            }
         }
         if (j + 1 < nk) {
             RK::template slice<1>(smem, j, sa, Ln, cur.rA, cur.rB, fa, fb, acc, [] {});

@@ -364,7 +364,8 @@ gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
                         cin[2 * e + 1] = bf16_bits_to_f32(raw[e] >> 16);
                     }
                 } else {
-                    for (int e = 0; e < 8 && m + e < args.M; ++e) cin[e] = bf16_bits_to_f32(cp[e]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) if (m + e < args.M) cin[e] = bf16_bits_to_f32(cp[e]);
                 }
             }
             if constexpr (kQ8) {
@@ -380,7 +381,8 @@ gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
                 if (m + 8 <= args.M && work.q_vector) {
                     __builtin_nontemporal_store(qw, (u32x2 *)qp);
                 } else {
-                    for (int e = 0; e < 8 && m + e < args.M; ++e) qp[e] = (int8_t)(qw[e >> 2] >> ((e & 3) * 8));
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) if (m + e < args.M) qp[e] = (int8_t)(qw[e >> 2] >> ((e & 3) * 8));
                 }
                 return;
             }
@@ -393,7 +395,8 @@ gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
             if (full) {
                 __builtin_nontemporal_store(out, (u32x4 *)cp);
             } else {
-                for (int e = 0; e < 8 && m + e < args.M; ++e) cp[e] = (uint16_t)(out[e >> 1] >> ((e & 1) * 16));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) if (m + e < args.M) cp[e] = (uint16_t)(out[e >> 1] >> ((e & 1) * 16));
             }
         };
 

@@ -161,27 +161,64 @@ struct TileKernel {
         int wave;
         // masking only: this lane's row within a load's rows, its logical
         // chunk by parity of the row group, the tile's valid rows of A and
-        // B and the unit's K
+        // B and the unit's K; per unit, the voffset of each of this wave's
+        // loads with rows past M or N already out of range (vAr, vBr), the
+        // unit's last slice (klast) and, by parity, the out-of-range bit of
+        // this lane's chunk in that slice (kx: 0 or kOobOffset)
         int lrow, lchunk[2];
         int rowsA, rowsB, kmax;
+        uint32_t vAr[kMasked ? Cfg::kALoads : 1], vBr[kMasked ? Cfg::kBLoads : 1], kx[2];
+        int klast;
     };
 
-    // The voffset of this lane's chunk in load q (row group q) of slice kt:
-    // the precomputed one, or the out-of-range offset outside the matrix.
-    template <bool kIsA>
-    __device__ __forceinline__ static uint32_t voff(int q, int kt, const Lane &L) {
-        uint32_t v = kIsA ? L.vA[q & 1] : L.vB[q & 1];
-        if constexpr (kMasked) {
-            const int row = q * Cfg::kRowsPerLoad + L.lrow;
-            const int k = kt * Cfg::BK + L.lchunk[q & 1] * Cfg::kElemsPerChunk;
-            if (!(row < (kIsA ? L.rowsA : L.rowsB) && k < L.kmax)) v = kOobOffset;
+    // Per-unit masking state (kMasked): rows and the K tail.  Only the last
+    // slice of a unit can hold chunks at or past its K, so a load's voffset
+    // in the K loop is its row-masked one, with kx or-ed in when kt is that
+    // slice: one vector instruction per load.
+    __device__ __forceinline__ static void mask_unit(Lane &L, int nk) {
+#pragma unroll
+        for (int i = 0; i < Cfg::kALoads; ++i) {
+            const int q = L.wave * Cfg::kALoads + i;
+            L.vAr[i] = q * Cfg::kRowsPerLoad + L.lrow < L.rowsA ? L.vA[q & 1] : kOobOffset;
         }
-        return v;
+#pragma unroll
+        for (int i = 0; i < Cfg::kBLoads; ++i) {
+            const int q = L.wave * Cfg::kBLoads + i;
+            L.vBr[i] = q * Cfg::kRowsPerLoad + L.lrow < L.rowsB ? L.vB[q & 1] : kOobOffset;
+        }
+        L.klast = __builtin_amdgcn_readfirstlane(nk - 1);
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+            L.kx[p] = (nk - 1) * Cfg::BK + L.lchunk[p] * Cfg::kElemsPerChunk < L.kmax ? 0u : kOobOffset;
+    }
+
+    // The voffset of this lane's chunk in load i of its operand (row group
+    // q of the tile) in slice kt: the precomputed one, or (kMasked) an
+    // out-of-range offset for rows past the matrix and chunks past the
+    // unit's K.
+    //
+    // kK (masked instances): whether kt is the unit's last slice -- kKAny:
+    // decided at run time; kKBefore: known to come before it (rows masked
+    // only); kKLast: known to be it.
+    enum : int { kKAny = 0, kKBefore = 1, kKLast = 2 };
+    template <bool kIsA, int kK = kKAny>
+    __device__ __forceinline__ static uint32_t voff(int i, int q, int kt, const Lane &L) {
+        if constexpr (kMasked) {
+            const uint32_t rows = kIsA ? L.vAr[i] : L.vBr[i];
+            if constexpr (kK == kKBefore)
+                return rows;
+            else if constexpr (kK == kKLast)
+                return L.kx[q & 1] | rows;
+            else
+                return (L.kx[q & 1] & (kt == L.klast ? 0xFFFFFFFFu : 0u)) | rows;
+        } else {
+            return kIsA ? L.vA[q & 1] : L.vB[q & 1];
+        }
     }
 
     // Loads number LO .. HI-1 of K-slice kt into ring buffer buf.  Loads
     // 0 .. kALoads-1 fill this wave's row groups of A, the rest those of B.
-    template <int LO, int HI>
+    template <int LO, int HI, int kK = kKAny>
     __device__ __forceinline__ static void issue(char *smem, int buf, int kt, const Lane &L,
                                                  __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rB) {
         char *sA = smem + buf * Cfg::kStageBytes;
@@ -191,11 +228,11 @@ struct TileKernel {
         for (int idx = LO; idx < HI; ++idx) {
             if (idx < Cfg::kALoads) {
                 const int q = L.wave * Cfg::kALoads + idx;  // row group of the tile
-                buffer_load_lds16(rA, (GB_LDS void *)(sA + q * 1024), voff<true>(q, kt, L),
+                buffer_load_lds16(rA, (GB_LDS void *)(sA + q * 1024), voff<true, kK>(idx, q, kt, L),
                                   (uint32_t)(q * Cfg::kRowsPerLoad) * L.lda_bytes + kbytes);
             } else {
                 const int q = L.wave * Cfg::kBLoads + (idx - Cfg::kALoads);
-                buffer_load_lds16(rB, (GB_LDS void *)(sB + q * 1024), voff<false>(q, kt, L),
+                buffer_load_lds16(rB, (GB_LDS void *)(sB + q * 1024), voff<false, kK>(idx - Cfg::kALoads, q, kt, L),
                                   (uint32_t)(q * Cfg::kRowsPerLoad) * L.ldb_bytes + kbytes);
             }
         }
@@ -257,7 +294,7 @@ struct TileKernel {
     // issue work than the MFMA's own 32 cycles leaves the matrix core idle;
     // one read or one load per shadow stays under that.  Hard scheduling
     // fences keep this order.
-    template <bool kRead, bool kLoad, int LO>
+    template <bool kRead, bool kLoad, int LO, int kK = kKAny>
     __device__ __forceinline__ static void kstep(char *smem, const Frag (&a)[Cfg::FM], const Frag (&b)[Cfg::FN],
                                                  f32x16 (&acc)[Cfg::FM][Cfg::FN], int rbuf, int rkk,
                                                  Frag (&ra)[Cfg::FM], Frag (&rb)[Cfg::FN], int lbuf, int lkt,
@@ -285,7 +322,7 @@ struct TileKernel {
                 for (int l = 0; l < kLoadsHere; ++l) {
                     const int slot = (kFree >= kLoadsHere) ? Cfg::kReadShadows + l * kFree / kLoadsHere
                                                            : l * kMf / kLoadsHere;
-                    if (slot == s) issue_range<LO>(smem, lbuf, lkt, L, rA, rB, l, 1);
+                    if (slot == s) issue_range<LO, kK>(smem, lbuf, lkt, L, rA, rB, l, 1);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -294,7 +331,7 @@ struct TileKernel {
 
     // kCount loads starting at number LO + first (first is a compile-time
     // constant after unrolling).
-    template <int LO>
+    template <int LO, int kK = kKAny>
     __device__ __forceinline__ static void issue_range(char *smem, int buf, int kt, const Lane &L,
                                                        __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rB,
                                                        int first, int count) {
@@ -306,11 +343,11 @@ struct TileKernel {
             const int idx = LO + first + r;
             if (idx < Cfg::kALoads) {
                 const int q = L.wave * Cfg::kALoads + idx;
-                buffer_load_lds16(rA, (GB_LDS void *)(sA + q * 1024), voff<true>(q, kt, L),
+                buffer_load_lds16(rA, (GB_LDS void *)(sA + q * 1024), voff<true, kK>(idx, q, kt, L),
                                   (uint32_t)(q * Cfg::kRowsPerLoad) * L.lda_bytes + kbytes);
             } else {
                 const int q = L.wave * Cfg::kBLoads + (idx - Cfg::kALoads);
-                buffer_load_lds16(rB, (GB_LDS void *)(sB + q * 1024), voff<false>(q, kt, L),
+                buffer_load_lds16(rB, (GB_LDS void *)(sB + q * 1024), voff<false, kK>(idx - Cfg::kALoads, q, kt, L),
                                   (uint32_t)(q * Cfg::kRowsPerLoad) * L.ldb_bytes + kbytes);
             }
         }
@@ -331,7 +368,7 @@ struct TileKernel {
     // Before the last k-step every wave waits for slice kt+1, passes the
     // barrier (all waves have then finished reading slice kt) and reads
     // slice kt+1's first fragments during the last k-step's MFMAs.
-    template <bool kSteady, bool kNext>
+    template <bool kSteady, bool kNext, int kK1 = kKAny, int kK2 = kKAny>
     __device__ __forceinline__ static void slice(char *smem, int kt, int cur, bool first, bool second, int ahead,
                                                  const Lane &L, __amdgpu_buffer_rsrc_t rA,
                                                  __amdgpu_buffer_rsrc_t rB, Frag (&fa)[2][Cfg::FM],
@@ -342,7 +379,7 @@ struct TileKernel {
 #pragma unroll
         for (int kk = 0; kk < Cfg::KSTEPS - 1; ++kk) {
             if (kSteady && kk == 0)
-                kstep<true, true, Cfg::kHalf>(smem, fa[0], fb[0], acc, cur, kk + 1, fa[1], fb[1], prev,
+                kstep<true, true, Cfg::kHalf, kK2>(smem, fa[0], fb[0], acc, cur, kk + 1, fa[1], fb[1], prev,
                                                kt + S - 1, L, rA, rB);
             else
                 kstep<true, false, 0>(smem, fa[kk & 1], fb[kk & 1], acc, cur, kk + 1, fa[(kk + 1) & 1],
@@ -357,7 +394,7 @@ struct TileKernel {
             lds_barrier();
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (kSteady) {
-                kstep<true, true, 0>(smem, fa[kLast], fb[kLast], acc, next, 0, fa[0], fb[0], cur, kt + S, L, rA,
+                kstep<true, true, 0, kK1>(smem, fa[kLast], fb[kLast], acc, next, 0, fa[0], fb[0], cur, kt + S, L, rA,
                                      rB);
             } else {
                 if (first) issue<0, Cfg::kHalf>(smem, cur, kt + S, L, rA, rB);
@@ -466,6 +503,7 @@ gemm_tile_kernel(const GemmArgs args, const TileSchedule sched, const TileSplit 
             Ln.rowsA = (int)(args.M - m0 < Cfg::BM ? args.M - m0 : Cfg::BM);
             Ln.rowsB = (int)(args.N - n0 < Cfg::BN ? args.N - n0 : Cfg::BN);
             Ln.kmax = (int)(args.K - k0);  // the unit's K: chunks at or past it are zeros
+            TK::mask_unit(Ln, nk);
         }
         const char *A = reinterpret_cast<const char *>(args.A);
         const char *B = reinterpret_cast<const char *>(args.B);
@@ -499,9 +537,26 @@ gemm_tile_kernel(const GemmArgs args, const TileSchedule sched, const TileSplit 
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
 
         int kt = 0, cur = 0;
-        for (; kt + S < nk; ++kt) {
-            TK::template slice<true, true>(smem, kt, cur, true, true, 0, Ln, rA, rB, fa, fb, acc);
-            cur = (cur + 1 == S) ? 0 : cur + 1;
+        if constexpr (kMasked) {
+            // Steady slices load slice kt + S (first half) and kt + S - 1
+            // (second half): before the unit's last slice while
+            // kt + S + 1 < nk, then one that loads the last one's first half.
+            for (; kt + S + 1 < nk; ++kt) {
+                TK::template slice<true, true, TK::kKBefore, TK::kKBefore>(smem, kt, cur, true, true, 0, Ln, rA,
+                                                                            rB, fa, fb, acc);
+                cur = (cur + 1 == S) ? 0 : cur + 1;
+            }
+            if (kt + S < nk) {
+                TK::template slice<true, true, TK::kKLast, TK::kKBefore>(smem, kt, cur, true, true, 0, Ln, rA, rB,
+                                                                          fa, fb, acc);
+                ++kt;
+                cur = (cur + 1 == S) ? 0 : cur + 1;
+            }
+        } else {
+            for (; kt + S < nk; ++kt) {
+                TK::template slice<true, true>(smem, kt, cur, true, true, 0, Ln, rA, rB, fa, fb, acc);
+                cur = (cur + 1 == S) ? 0 : cur + 1;
+            }
         }
         for (; kt + 1 < nk; ++kt) {
             // loads issued after slice kt+1's: slices kt+2 .. min(kt+S-1, nk-1)
@@ -611,7 +666,8 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs args,
                     cin[2 * e + 1] = bf16_bits_to_f32(raw[e] >> 16);
                 }
             } else {
-                for (int e = 0; e < 8 && m + e < args.M; ++e) cin[e] = bf16_bits_to_f32(c[e]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) if (m + e < args.M) cin[e] = bf16_bits_to_f32(c[e]);
             }
         }
         float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -648,7 +704,8 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs args,
             if (full) {
                 __builtin_nontemporal_store(out, (u32x4 *)c);
             } else {
-                for (int e = 0; e < 8 && m + e < args.M; ++e) c[e] = (uint16_t)(out[e >> 1] >> ((e & 1) * 16));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) if (m + e < args.M) c[e] = (uint16_t)(out[e >> 1] >> ((e & 1) * 16));
             }
         }
     }
