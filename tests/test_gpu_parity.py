@@ -868,6 +868,19 @@ def test_fp8_medium_splitk_forced_range_counts(splits, monkeypatch):
               seed=630 + int(splits), expect_kernel=F8T128S)
 
 
+# The masked kernels load the last K-slice through a peeled iteration: walk
+# the slice count through 1 .. 7 with a K tail in the last slice, on both
+# masked FP8 tile kernels (the bf16 ones are walked by the forced-kernel
+# slice counts above).
+@pytest.mark.parametrize("kernel", ["fp8_256x256x128_masked", "fp8_256x256x128_mfma16_masked", F8T128M])
+@pytest.mark.parametrize("nk", [1, 2, 3, 4, 5, 7])
+def test_fp8_masked_slice_counts_with_k_tail(kernel, nk, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", kernel)
+    K = 128 * nk - 48
+    check_fp8(f"{kernel} nk={nk}", 520, 264, K, lda=K + 16, ldb=K + 32, ldc=528, beta=0.5, use_bias=True,
+              seed=700 + nk, expect_kernel=kernel, poison_pad=True)
+
+
 @pytest.mark.parametrize("M,N,K,lda,ldb,ldc,kernel", [
     (1000, 1000, 1008, 1008, 1024, 1000, F8T128M),   # M, N tails; K tail of 112 in the last slice
     (130, 70, 528, 544, 528, 136, F8T128M),          # one row / one column past a tile
