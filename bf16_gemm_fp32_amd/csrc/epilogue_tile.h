@@ -75,8 +75,18 @@ __device__ __forceinline__ void tile_epilogue(char *smem, const GemmArgs &args, 
                 // FP8 inputs: the sum times scale_a[m] and scale_b[n] (a
                 // missing scale is 1; rows past M are never stored)
                 if (args.scale_a) {
+                    // a whole chunk's 8 scales as two 16-byte loads; a chunk
+                    // that straddles M element by element
+                    float sa[8];
+                    if (!kMasked || m + 8 <= args.M) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] = x[e] * (!kMasked || m + e < args.M ? args.scale_a[m + e] : 0.f);
+                        for (int e = 0; e < 8; ++e) sa[e] = args.scale_a[m + e];
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) sa[e] = m + e < args.M ? args.scale_a[m + e] : 0.f;
+                    }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = x[e] * sa[e];
                 }
                 if (args.scale_b) {
                     const float sb = args.scale_b[n];

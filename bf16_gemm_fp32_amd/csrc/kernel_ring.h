@@ -355,9 +355,14 @@ __device__ __forceinline__ void ring_epilogue(char *smem, const GemmArgs &args, 
     if constexpr (kScaled) {
         const int64_t m = m0 + wm * Cfg::WTM + (lane % kColChunks) * 8;
         if (args.scale_a) {
+            if (!kMasked || m + 8 <= args.M) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (!kMasked || m + e < args.M) sa[e] = args.scale_a[m + e];
+                for (int e = 0; e < 8; ++e) sa[e] = args.scale_a[m + e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (m + e < args.M) sa[e] = args.scale_a[m + e];
+            }
         }
     }
     // The masked instances load a group's inputs at its start instead of
