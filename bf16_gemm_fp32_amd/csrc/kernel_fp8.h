@@ -476,9 +476,9 @@ hipError_t launch_fp8_ring(const GemmArgs &args, int cus, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Split-K on small grids: the tile kernel over (range, tile) units into the
-// workspace split.P, then the reduction (which applies the scales and the
-// epilogue).  The host has checked the tile requirements (exact multiples,
+// Split-K over these tiles (forced only; small grids take the 128x128 FP8
+// tiles): the tile kernel over (range, tile) units into the workspace
+// split.P, then the reduction (which applies the scales and the epilogue).  The host has checked the tile requirements (exact multiples,
 // or the masked ones), split.splits >= 2, every range non-empty, and that
 // split.P holds splits * pstride floats (ldp = M rounded up to 256, pstride
 // = ldp times N rounded up to 256).

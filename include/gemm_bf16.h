@@ -21,9 +21,10 @@
  * buffers after a call returns.  Its one device allocation is the split-K
  * workspace (fp32 partial sums, and arrival counters for the short-product
  * kernel) used by three kinds of shape: 3 <= M <= 64 with few columns,
- * products whose 128x128 tiles would leave most compute units idle (for
- * example 1024 x 1024 x 4096; with tails the partials are padded to whole
- * tiles), and FP8 products whose 256x256 tiles would.  It is one buffer per
+ * and products, bf16 or FP8, whose 128x128 tiles would leave most compute
+ * units idle and whose K is long enough to pay for the split (for example
+ * 512 x 512 x 8192; with tails the partials are padded to whole tiles).
+ * It is one buffer per
  * (device, stream) of a fixed size -- 64 KiB of counters plus 64 KiB per
  * compute unit (16 MiB + 64 KiB on a 256-CU device) -- allocated with
  * hipMalloc by the first call on that stream that splits K (its counters
@@ -204,14 +205,15 @@ int gemm_bf16_q8(int64_t M, int64_t N, int64_t K,
  * Errors and quick returns as gemm_bf16.  With K, lda and ldb multiples of
  * 16 and A, B 16-byte aligned: 1 <= M <= 2 (and 3 <= M <= 4 when
  * N * K < 2^26) takes a matrix-vector kernel and the other M <= 64 a
- * streaming FP8 MFMA kernel (any ldc); larger M the
- * 256x256 FP8 MFMA kernel (any M and N: tails are masked; exact tile
+ * streaming FP8 MFMA kernel (any ldc); larger M the 256x256 FP8 MFMA
+ * kernel, or where its tiles would fill less than half of the compute
+ * units the 128x128 one (any M and N: tails are masked; exact tile
  * multiples with C 16-byte aligned and ldc % 8 == 0 run unmasked, anything
- * else accesses C element by element where it must).  When those tiles
- * would fill less than half of the compute units, K is split over up to
- * eight ranges (fp32 partial tiles in the split-K workspace, then an
- * ordered reduction that applies the scales and the epilogue).
- * Other inputs take the bounds-checked path (same result).
+ * else accesses C element by element where it must).  On those small grids
+ * K is split over several ranges when it is long enough (fp32 partial tiles
+ * in the split-K workspace, then an ordered reduction that applies the
+ * scales and the epilogue).  Other inputs take the bounds-checked path
+ * (same result).
  */
 int gemm_fp8(int64_t M, int64_t N, int64_t K,
              const gemm_fp8_t *A, int64_t lda,
