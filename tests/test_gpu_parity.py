@@ -500,12 +500,37 @@ def test_repeat_launches_bit_identical_and_paths_agree():
     r1 = run_gpu(M, N, K, case["A"], K, case["B"], K, C_init, M, 1.0, 0.0, None, "none")
     r2 = run_gpu(M, N, K, case["A"], K, case["B"], K, C_init, M, 1.0, 0.0, None, "none")
     assert np.array_equal(r1, r2)
-    os.environ["GEMM_BF16_FORCE_KERNEL"] = "generic"
+    os.environ["GEMM_BF16_FORCE_KERNEL"] = "generic64x64x32"
     try:
+        assert gb.gemm_bf16_kernel_name(M, N, K, 4096, K, 4096, K, 4096, M) == "generic64x64x32"
         r3 = run_gpu(M, N, K, case["A"], K, case["B"], K, C_init, M, 1.0, 0.0, None, "none")
     finally:
         del os.environ["GEMM_BF16_FORCE_KERNEL"]
     assert_within_tolerance(r3, r1, K, "generic vs tile")
+
+
+def test_kernels_with_one_accumulation_order_agree_bit_for_bit(monkeypatch):
+    """Every kernel built on v_mfma_f32_32x32x16_bf16 that walks K in order
+    gives each output element the same MFMAs on the same operands in the same
+    order, whatever its tile, its ring (a five-slot unit ring, five and four
+    stages, a plain double buffer) and its epilogue staging -- so their
+    results must agree bit for bit.  A race in any of those pipelines would
+    show up as a difference.  The epilogue is alpha * sum alone (one
+    rounding), so the compiler's contraction of longer epilogues cannot make
+    the kernels differ."""
+    M, N, K = 1024, 512, 640
+    case = inputs.random_case(32, M, N, K, with_c0=False, with_bias=False)
+    C_init = np.full(N * M, NAN_BF16, np.uint16)
+    outs = {}
+    for kernel in ("ring256x256x64_mfma32", "tile256x256x32_s5", "tile128x128x64_s4", "generic64x64x32"):
+        monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", kernel)
+        assert gb.gemm_bf16_kernel_name(M, N, K, 4096, K, 4096, K, 4096, M) == kernel
+        outs[kernel] = run_gpu(M, N, K, case["A"], K, case["B"], K, C_init, M, 1.25, 0.0, None, "none")
+    ref = outs.pop("ring256x256x64_mfma32")
+    for kernel, got in outs.items():
+        assert np.array_equal(got, ref), f"{kernel} differs from ring256x256x64_mfma32"
+    exp = oracle.gemm(M, N, K, case["A"], K, case["B"], K, None, M, 1.25, 0.0, None, "none", nthreads=_threads())
+    assert_within_tolerance(ref, exp, K, "32x32x16 kernels vs oracle")
 
 
 # ------------------------------------------------------- int8 output ---
