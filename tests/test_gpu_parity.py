@@ -942,6 +942,36 @@ def test_fp8_medium_masked_unaligned_c(monkeypatch):
               use_bias=True, epilogue="gelu_tanh", seed=651, expect_kernel=F8T128SM)
 
 
+def test_fp8_kernels_with_one_accumulation_order_agree_bit_for_bit(monkeypatch):
+    """The FP8 kernels on 32x32x64 MFMAs (256x256 tiles exact and masked,
+    128x128 tiles exact and masked) give each output element the same MFMAs
+    on the same operand bytes in the same k order, and scale and round it
+    the same way (the sum times scale_a[m], times scale_b[n], times alpha:
+    no additions to contract), so on exact tile multiples they must agree
+    bit for bit."""
+    M, N, K = 1024, 512, 640
+    A, B = inputs.normal_fp8(720, M * K), inputs.normal_fp8(721, N * K)
+    sa, sb = inputs.uniform_f32(722, M, 0.5, 2.0), inputs.uniform_f32(723, N, 0.5, 2.0)
+    a_t, a_p = to_dev_u8(A)
+    b_t, b_p = to_dev_u8(B)
+    sa_t, sb_t = torch.from_numpy(sa).cuda(), torch.from_numpy(sb).cuda()
+    outs = {}
+    for kernel in ("fp8_256x256x128_mfma32", "fp8_256x256x128_masked", F8T128, F8T128M):
+        monkeypatch.setenv("GEMM_BF16_FORCE_KERNEL", kernel)
+        assert gb.gemm_fp8_kernel_name(M, N, K, a_p, K, b_p, K, a_p, M) == kernel
+        c = torch.full((M * N,), -1, dtype=torch.int16, device="cuda")
+        st = gb.gemm_fp8(M, N, K, a_p, K, b_p, K, c.data_ptr(), M, 1.25, 0.0, sa_t.data_ptr(), sb_t.data_ptr(), 0,
+                         0, torch.cuda.current_stream().cuda_stream)
+        assert st == 0, gb.gemm_bf16_status_string(st)
+        torch.cuda.synchronize()
+        outs[kernel] = c.cpu().numpy().view(np.uint16)
+    ref = outs.pop("fp8_256x256x128_mfma32")
+    for kernel, got in outs.items():
+        assert np.array_equal(got, ref), f"{kernel} differs from fp8_256x256x128_mfma32"
+    exp = oracle.gemm_fp8(M, N, K, A, K, B, K, None, M, 1.25, 0.0, sa, sb, None, "none", nthreads=_threads())
+    assert_within_tolerance(ref, exp, K, "32x32x64 FP8 kernels vs oracle")
+
+
 # The FP8 tile kernel on 32x32x64 MFMAs forced onto exact tiles (its masked
 # instance is the default for tails, its split mode serves split-K): 1 to
 # 10 K-slices, two tiles per CU, epilogue combinations with scales on and
