@@ -569,12 +569,12 @@ static hipError_t launch_generic(const GemmArgs &args, int cus, hipStream_t stre
 }
 
 // The fp8 product: one to four rows on the matrix-vector kernel, up to 64
-// on the streaming kernel; else the
-// 256x256 FP8 tile kernel with 16-byte aligned rows
-// (lda, ldb % 16, K % 16, ldc % 8) -- its unmasked instance for exact tile
-// multiples (M, N % 256, K % 128), the masked one for shapes with tails --
-// else the bounds-checked kernel (which converts the bytes to bf16 on their
-// way into LDS).
+// on the streaming kernel; else, with 16-byte aligned rows (lda, ldb % 16,
+// K % 16), the 256x256 FP8 tile kernel, or the 128x128 one (whole K or
+// split) where the 256x256 tiles would fill less than half of the compute
+// units -- each unmasked for exact tile multiples (and ldc % 8, aligned C),
+// masked for anything else; else the bounds-checked kernel (which converts
+// the bytes to bf16 on their way into LDS).
 static int choose_kernel_fp8(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
                              int64_t ldb, const void *C, int64_t ldc, int cus, size_t cap_floats) {
     if (M == 0 || N == 0) return kNone;

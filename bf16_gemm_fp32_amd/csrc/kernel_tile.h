@@ -5,10 +5,13 @@
 //
 //   HBM/L2 --(buffer_load ... lds, 16 B per lane, coalesced)--> LDS ring of
 //   STAGES buffers (XOR-swizzled rows) --(ds_read_b128)--> VGPR fragments
-//   --(v_mfma_f32_32x32x16_bf16)--> fp32 accumulators in AGPRs
+//   --(v_mfma_f32_32x32x16_bf16, or for FP8 E4M3 operands
+//      v_mfma_scale_f32_32x32x64_f8f6f4)--> fp32 accumulators in AGPRs
 //
 // and then the fused epilogue stages the accumulators through LDS and writes
-// bf16 C with 16-byte, column-contiguous stores.
+// bf16 C with 16-byte, column-contiguous stores.  FP8 operands (TileConfig's
+// ELEM_ = 1) keep the byte layout: a slice of BK values is BK bytes per row,
+// so a 128-value FP8 slice has the 128-byte rows of a 64-value bf16 slice.
 //
 // The decomposition into tiles, K-slices staged through on-chip memory and
 // register accumulators is the one of "Outperforming cuBLAS on H100: a
@@ -31,10 +34,10 @@
 //
 // Operand layout in LDS.  A (row-major) and B (column-major, i.e. rows of K
 // per output column) are both K-contiguous, so both tiles are stored the
-// same way: one row of BK bf16 (2*BK bytes) per M (or N) index, split into
-// 16-byte chunks.  Chunk c of row r is stored at position c ^ swz(r):
-//   BK = 64 (8 chunks, 128-byte rows): swz(r) = (r & 7) ^ ((r >> 3) & 1)
-//   BK = 32 (4 chunks,  64-byte rows): swz(r) = (r >> 2) & 3
+// same way: one row of BK values (kRowBytes bytes) per M (or N) index, split
+// into 16-byte chunks.  Chunk c of row r is stored at position c ^ swz(r):
+//   128-byte rows (8 chunks): swz(r) = (r & 7) ^ ((r >> 3) & 1)
+//    64-byte rows (4 chunks): swz(r) = (r >> 2) & 3
 // On gfx950 LDS has 64 four-byte banks and a ds_read_b128 is served in four
 // phases of 16 lanes; lanes 0-31 fall into two phases by the parity of lane
 // bits 2..4 ({0-3, 12-15, 20-27} and {4-11, 16-19, 28-31}), lanes 32-63 the
@@ -42,9 +45,10 @@
 // (32 consecutive rows, one logical chunk per half-wave) then touches 16
 // distinct 16-byte bank groups in every phase -- the XOR swizzle the DeepGEMM
 // article (section 3.2) uses against shared-memory bank conflicts, redone for
-// these row widths and this lane-to-phase map.  The direct-to-LDS load writes a wave's 64 lanes to 1 KiB of
-// consecutive LDS bytes, so the swizzle is applied on the global side: lane
-// i fetches the chunk that belongs at its LDS position.
+// these row widths and this lane-to-phase map.  The direct-to-LDS load
+// writes a wave's 64 lanes to 1 KiB of consecutive LDS bytes, so the swizzle
+// is applied on the global side: lane i fetches the chunk that belongs at
+// its LDS position.
 //
 // Split-K.  When the tiles alone would leave most compute units idle (a
 // 1024 x 1024 output is 64 tiles of 128x128 for 256 compute units), the
