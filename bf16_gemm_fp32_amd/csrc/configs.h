@@ -22,9 +22,9 @@ struct ShapeRing { static constexpr int BM = 256, BN = 256, BK = 64; };
 
 // Short-and-wide products (at most 64 rows): one workgroup per strip of 32,
 // 64 or 128 columns and range of K (split-K) streams B once; K-slices of 256
-// for 32-column strips, 128 for the wider ones, 512 FP8 values (the same
-// 512 bytes) for FP8 operands.
-struct ShapeSkinny { static constexpr int KS_N32 = 256, KS_WIDE = 128, KS_FP8 = 512; };
+// for 32- and 64-column strips, 128 for 128-column ones, 512 FP8 values (the
+// same 512 bytes) for FP8 operands.
+struct ShapeSkinny { static constexpr int KS_N32 = 256, KS_N64 = 256, KS_N128 = 128, KS_FP8 = 512; };
 
 struct SkinnyWork;
 

@@ -186,35 +186,43 @@ constexpr size_t kScratchCounterBytes = kScratchCounters * 4;
 constexpr size_t kScratchFloatsPerCu = 128 * 128;
 
 // How the streaming kernel covers a short product: its row block (32 or
-// 64), strip width, and the K split.  32-column strips measured fastest at
-// every size tried (the wider ones exist for experiments).  K is split only
-// when the strips alone would leave more than half of the compute units
-// idle: then up to one unit per compute unit, each split keeping at least 4
-// K-slices so the rings have something to overlap.  (At 64 x 1024 x 16384 a
-// split of 8 runs 2.3x faster than none; at 64 x 4096 x 4096, with 128
-// strips, a split of 2 is 10% slower than none.)  cap_floats bounds the
-// partials (strips x splits x rows x columns floats) and the strips must fit
-// the counters.
+// 64), strip width, and the K split.
+//  * 32-column strips by default.  K is split only when the strips alone
+//    would leave more than half of the compute units idle: then up to one
+//    unit per compute unit, each split keeping at least 4 K-slices so the
+//    rings have something to overlap.  The split colocates (handoff.h) when
+//    the strips are a multiple of 8 and every unit has its own workgroup;
+//    else the partials cross XCDs through device-wide atomics.  Colocated
+//    against crossing, interleaved in one process (cold B): 64 x 2048 x 4096
+//    11.8 against 16.7 us, 64 x 1024 x 16384 18.3 against 21.3 us,
+//    64 x 512 x 16384 17.7 against 24.2 us.
+//  * Where 32-column strips would leave compute units idle without a split
+//    (N from 4096 to 8191 on 256 CUs) and the N / 64 strips of 64 columns
+//    are a multiple of 8, bf16 products take 64-column strips with K split
+//    (at least 8 slices of 256) so that the units fill the CUs, colocated:
+//    64 x 4096 x 8192 21.1 against 28.6 us, 64 x 6144 x 8192 27.1 against
+//    29.3 us, 32 x 4096 x 8192 19.2 against 22.4 us.  Where the 32-column
+//    strips split or fill the CUs, 64-column strips are slower (their rings
+//    keep fewer B slices in flight): 64 x 8192 x 8192 unsplit 39.1 against
+//    29.2 us, split in two 35.2 us.
+// cap_floats bounds the partials (strips x splits x rows x columns floats)
+// and the strips must fit the counters (records, when colocated).
 struct SkinnyPlan {
-    int rows, cols, strips, splits, spp;
+    int rows, cols, strips, splits, spp, colocate;
 };
 
-static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int cus, size_t cap_floats, bool fp8 = false,
-                              bool q8 = false) {
+static SkinnyPlan plan_skinny_width(int64_t M, int64_t N, int64_t K, int cus, size_t cap_floats, bool fp8,
+                                    int width, bool coloc_ok) {
     SkinnyPlan p{};
     p.rows = M <= 32 ? 32 : 64;
-    int width = 32;
-    if (const char *env = std::getenv("GEMM_BF16_SKINNY_COLS")) {  // tuning knob: 32, 64 or 128
-        const int w = std::atoi(env);
-        if (w == 32 || w == 64 || w == 128) width = w;
-    }
-    if (fp8 || q8) width = 32;  // the FP8 and int8-output instances are built for 32-column strips
     p.cols = width;
-    const int ks = fp8 ? ShapeSkinny::KS_FP8 : (width == 32 ? ShapeSkinny::KS_N32 : ShapeSkinny::KS_WIDE);
+    const int ks = fp8 ? ShapeSkinny::KS_FP8
+                       : (width == 32 ? ShapeSkinny::KS_N32 : width == 64 ? ShapeSkinny::KS_N64 : ShapeSkinny::KS_N128);
     const int64_t nk = (K + ks - 1) / ks;
     const int64_t strips = (N + width - 1) / width;
     p.strips = (int)strips;
-    int64_t splits = strips * 2 >= cus ? 1 : cus / strips;
+    const bool split = width == 64 ? strips * 2 <= cus : strips * 2 < cus;
+    int64_t splits = split ? cus / strips : 1;
     if (const char *env = std::getenv("GEMM_BF16_SKINNY_SPLITS")) {  // tuning knob
         const int s = std::atoi(env);
         if (s >= 1) splits = s;
@@ -227,7 +235,28 @@ static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int cus, size_t c
     if (splits < 1) splits = 1;
     p.spp = (int)((nk + splits - 1) / splits);
     p.splits = (int)((nk + p.spp - 1) / p.spp);  // no empty split
+    p.colocate = coloc_ok && p.splits > 1 && p.splits < 256 && strips % kNumXcds == 0 &&
+                 strips * p.splits <= cus && (size_t)strips * sizeof(HandoffRecord) <= kScratchCounterBytes;
     return p;
+}
+
+static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int cus, size_t cap_floats, bool fp8 = false,
+                              bool q8 = false) {
+    bool coloc_ok = true;
+    if (const char *env = std::getenv("GEMM_BF16_SKINNY_COLOCATE"))  // tuning knob: 0 = partials cross XCDs
+        coloc_ok = env[0] != '0';
+    if (fp8 || q8)  // the FP8 and int8-output instances are built for 32-column strips
+        return plan_skinny_width(M, N, K, cus, cap_floats, fp8, 32, coloc_ok);
+    if (const char *env = std::getenv("GEMM_BF16_SKINNY_COLS")) {  // tuning knob: 32, 64 or 128
+        const int w = std::atoi(env);
+        if (w == 32 || w == 64 || w == 128) return plan_skinny_width(M, N, K, cus, cap_floats, false, w, coloc_ok);
+    }
+    const int64_t strips32 = (N + 31) / 32, strips64 = (N + 63) / 64;
+    if (coloc_ok && strips32 < cus && strips32 * 2 >= cus && strips64 % kNumXcds == 0 && strips64 * 2 <= cus) {
+        const SkinnyPlan p = plan_skinny_width(M, N, K, cus, cap_floats, false, 64, coloc_ok);
+        if (p.colocate) return p;
+    }
+    return plan_skinny_width(M, N, K, cus, cap_floats, false, 32, coloc_ok);
 }
 
 // Where a call's split-K scratch comes from.
@@ -300,11 +329,13 @@ static hipError_t launch_skinny_plan(const GemmArgs &args, int cus, const Scratc
     work.spp = p.spp;
     work.c_vector = aligned16(args.C) && args.ldc % 8 == 0;
     work.q_vector = q8 && (reinterpret_cast<uintptr_t>(args.Q) & 7u) == 0 && args.ldq % 8 == 0;
+    work.colocate = p.colocate;
     if (p.splits > 1) {
         const size_t floats = (size_t)p.strips * p.splits * p.cols * p.rows;
         if (floats > scr.cap_floats || (size_t)p.strips > kScratchCounters) return hipErrorInvalidValue;
         hipError_t err = get_scratch(scr, stream, &work.counters, &work.partials);
         if (err != hipSuccess) return err;
+        work.records = reinterpret_cast<HandoffRecord *>(work.counters);
         if (q8) return launch_skinny_q8(p.rows, args, work, cus, stream);
         return fp8 ? launch_skinny_fp8(p.rows, args, work, cus, stream)
                    : launch_skinny(p.rows, p.cols, args, work, cus, stream);

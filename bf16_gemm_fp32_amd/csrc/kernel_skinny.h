@@ -20,7 +20,10 @@
 // otherwise the unit's fp32 partial goes to a workspace and the last unit of
 // the strip to arrive (an atomic counter per strip) adds the partials in
 // split order -- the same order whichever unit is last, so the result is
-// deterministic -- and runs the epilogue.
+// deterministic -- and runs the epilogue.  When the host places a strip's
+// splits on one XCD (colocate) the partials are plain stores that the last
+// unit reads back through that XCD's L2 (handoff.h); otherwise they cross
+// XCDs as device-wide atomics.
 //
 // Why split K.  Every unit reads all M rows of A for its K range, so without
 // a split each of 256 compute units pulls the whole of A through its load
@@ -53,6 +56,7 @@
 #pragma once
 
 #include "device_common.h"
+#include "handoff.h"
 #include "tile_schedule.h"
 
 namespace gb {
@@ -93,16 +97,22 @@ struct SkinnyConfig {
 };
 
 // The unit decomposition and the split-K workspace (unused with splits == 1):
-// partials[unit * BN * BMr + col * BMr + row] in fp32 (unit = strip * splits
-// + split) and one uint32 counter per strip, zero between calls.
+// partials[unit * BN * BMr + chunk * 8 + row % 8] in fp32 (unit = strip *
+// splits + split, chunk = col * BMr / 8 + row / 8) and, per strip, one
+// uint32 counter or (colocate) one handoff record, zero between calls.
+// colocate: the grid is exactly one workgroup per unit, a multiple of 8 of
+// them, and each XCD's run of slots holds whole strips; a strip's splits
+// then hand their partials over within one XCD (handoff.h).
 struct SkinnyWork {
     int num_strips;
     int splits;
     int spp;       // K-slices per split (the last split may have fewer)
     int c_vector;  // C 16-byte aligned and ldc % 8 == 0: 8-row chunks move as one 16-byte access
     int q_vector;  // int8 output: Q 8-byte aligned and ldq % 8 == 0 (8-row chunks as one 8-byte store)
+    int colocate;
     float *partials;
     uint32_t *counters;
+    HandoffRecord *records;  // the same memory as counters, for colocate
 };
 
 // Requirements checked by the host: 1 <= M <= BMr, N >= 1, K a multiple of
@@ -163,7 +173,10 @@ gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
     const char *B8 = reinterpret_cast<const char *>(args.B);
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(A8, (uint32_t)(((rowsA - 1) * args.lda + args.K) * kElem));
 
-    for (int unit = blockIdx.x; unit < num_units; unit += gridDim.x) {
+    const bool coloc = work.colocate != 0;
+    const int xcd = coloc ? xcd_id() : 0;
+    for (int w = blockIdx.x; w < num_units; w += gridDim.x) {
+        const int unit = coloc ? handoff_slot(w, gridDim.x) : w;
         const int strip = unit / work.splits;
         const int split = unit % work.splits;
         const int64_t n0 = (int64_t)strip * Cfg::BN;
@@ -176,13 +189,15 @@ gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
         // Slice j of this unit's order into its ring buffer.  Slices are
         // issued in order (A and B each), walking the unit's K range from a
         // rotated start (strip index within its XCD, so the workgroups
-        // sharing an L2 do not all request the same A lines at once).  A
+        // sharing an L2 do not all request the same A lines at once; a
+        // colocated XCD holds a contiguous run of strips).  A
         // chunk outside the matrix (row past M or N, k past K) is loaded from
         // the out-of-range offset; slices of full strips take a branch-free
         // path.
         const bool allA = rowsA == Cfg::BMr, allB = colsB == Cfg::BN;
         const int s_end = s0 + ns;
-        int ksA = s0 + (strip / kNumXcds) % ns, ksB = ksA;
+        const int xcd_strip = coloc ? strip % (work.num_strips / kNumXcds) : strip / kNumXcds;
+        int ksA = s0 + xcd_strip % ns, ksB = ksA;
         auto issueA = [&](int j) {
             char *dst = ringA + (j % Cfg::SA) * Cfg::kABytes;
             const int ks = ksA;
@@ -226,6 +241,7 @@ gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
 #pragma unroll
             for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = f32x16{};
 
+        if (coloc && threadIdx.x == 0) handoff_register(work.records + strip, xcd);
         // Previous unit's partial-sum reduction is done with LDS.
         lds_barrier();
         // Prologue: the steady state issues A(j + SA-1), then B(j + SB-1), at
@@ -409,10 +425,76 @@ gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
             continue;
         }
 
-        // Split K: publish this unit's partial, then count arrivals per
-        // strip.  The XCDs' L2 caches are not coherent with each other, and a
-        // cache-wide write-back / invalidate (an agent-scope fence) costs
-        // tens of microseconds when every unit issues one.  The partials are
+        if (coloc) {
+            // Split K within one XCD: plain stores of this unit's partial,
+            // then the handoff; the last unit adds the partials in split
+            // order (the same sum whichever unit is last), loading two
+            // splits of every chunk it owns at a time.
+            float *mine = work.partials + (int64_t)unit * (Cfg::BN * Cfg::BMr);
+            for (int idx = threadIdx.x; idx < kChunks; idx += Cfg::kThreads) {
+                float x[8];
+                wave_sum(idx, x);
+                *(f32x4 *)(mine + idx * 8) = f32x4{x[0], x[1], x[2], x[3]};
+                *(f32x4 *)(mine + idx * 8 + 4) = f32x4{x[4], x[5], x[6], x[7]};
+            }
+            uint32_t *flag = (uint32_t *)(smem + Cfg::kFlagOffset);
+            if (!handoff_arrive(work.records + strip, work.splits, xcd, flag)) continue;
+            constexpr int kCpt = (kChunks + Cfg::kThreads - 1) / Cfg::kThreads;
+            constexpr int64_t kUnitFloats = Cfg::BN * Cfg::BMr;
+            const float *base = work.partials + (int64_t)strip * work.splits * kUnitFloats;
+            float x[kCpt][8];
+#pragma unroll
+            for (int c = 0; c < kCpt; ++c)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[c][e] = 0.f;
+            auto add = [&](const f32x4 &lo, const f32x4 &hi, float (&y)[8]) {
+                y[0] += lo.x; y[1] += lo.y; y[2] += lo.z; y[3] += lo.w;
+                y[4] += hi.x; y[5] += hi.y; y[6] += hi.z; y[7] += hi.w;
+            };
+            int sp = 0;
+            for (; sp + 2 <= work.splits; sp += 2) {
+                f32x4 v[kCpt][4];
+#pragma unroll
+                for (int c = 0; c < kCpt; ++c) {
+                    const int idx = threadIdx.x + c * Cfg::kThreads;
+                    if (kChunks % Cfg::kThreads == 0 || idx < kChunks) {
+                        const float *p = base + sp * kUnitFloats + idx * 8;
+                        v[c][0] = *(const f32x4 *)p;
+                        v[c][1] = *(const f32x4 *)(p + 4);
+                        v[c][2] = *(const f32x4 *)(p + kUnitFloats);
+                        v[c][3] = *(const f32x4 *)(p + kUnitFloats + 4);
+                    }
+                }
+#pragma unroll
+                for (int c = 0; c < kCpt; ++c) {
+                    add(v[c][0], v[c][1], x[c]);
+                    add(v[c][2], v[c][3], x[c]);
+                }
+            }
+            if (sp < work.splits) {
+#pragma unroll
+                for (int c = 0; c < kCpt; ++c) {
+                    const int idx = threadIdx.x + c * Cfg::kThreads;
+                    if (kChunks % Cfg::kThreads == 0 || idx < kChunks) {
+                        const float *p = base + sp * kUnitFloats + idx * 8;
+                        add(*(const f32x4 *)p, *(const f32x4 *)(p + 4), x[c]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < kCpt; ++c) {
+                const int idx = threadIdx.x + c * Cfg::kThreads;
+                if (kChunks % Cfg::kThreads == 0 || idx < kChunks) finish(idx, x[c]);
+            }
+            if (threadIdx.x == 0) handoff_reset(work.records + strip);
+            continue;
+        }
+
+        // Split K across XCDs: publish this unit's partial, then count
+        // arrivals per strip.  The XCDs' L2 caches are not coherent with
+        // each other, and a cache-wide write-back / invalidate (an
+        // agent-scope fence) costs tens of microseconds when every unit
+        // issues one.  The partials are
         // small, so they move through agent-scope atomic read-modify-writes
         // instead, which the hardware performs coherently for the whole
         // device (as it does the arrival counter): each unit swaps its values

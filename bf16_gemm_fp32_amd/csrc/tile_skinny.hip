@@ -1,19 +1,20 @@
 // tile_skinny.hip -- instances of the streaming kernel for at most 64 rows:
-// 32-column strips with K-slices of 256 in A/B rings of 3/4 slices, and 64-
-// or 128-column strips (for split-K) with K-slices of 128.
+// 32-column strips with K-slices of 256 in A/B rings of 3/4 slices, 64-column
+// strips (split K within an XCD) with K-slices of 256 in rings of 2/3 (2/4
+// for 32 rows), and 128-column strips with K-slices of 128.
 #include "configs.h"
 #include "kernel_skinny.h"
 
 namespace gb {
 
-using SkinnyM64N64 = SkinnyConfig<2, 2, 128, 3, 7>;
+using SkinnyM64N64 = SkinnyConfig<2, 2, 256, 2, 3>;
 using SkinnyM64N128 = SkinnyConfig<2, 4, 128, 2, 4>;
-using SkinnyM32N64 = SkinnyConfig<1, 2, 128, 3, 8>;
+using SkinnyM32N64 = SkinnyConfig<1, 2, 256, 2, 4>;
 using SkinnyM32N128 = SkinnyConfig<1, 4, 128, 2, 4>;
 
-static_assert(SkinnyM64N32::KS == ShapeSkinny::KS_N32 && SkinnyM64N64::KS == ShapeSkinny::KS_WIDE &&
-                  SkinnyM64N128::KS == ShapeSkinny::KS_WIDE && SkinnyM32N32::KS == ShapeSkinny::KS_N32 &&
-                  SkinnyM32N64::KS == ShapeSkinny::KS_WIDE && SkinnyM32N128::KS == ShapeSkinny::KS_WIDE,
+static_assert(SkinnyM64N32::KS == ShapeSkinny::KS_N32 && SkinnyM64N64::KS == ShapeSkinny::KS_N64 &&
+                  SkinnyM64N128::KS == ShapeSkinny::KS_N128 && SkinnyM32N32::KS == ShapeSkinny::KS_N32 &&
+                  SkinnyM32N64::KS == ShapeSkinny::KS_N64 && SkinnyM32N128::KS == ShapeSkinny::KS_N128,
               "the host plans splits with these slice lengths");
 
 hipError_t launch_skinny(int rows, int cols, const GemmArgs &args, const SkinnyWork &work, int cus,

@@ -454,6 +454,57 @@ def test_skinny_split_k_is_deterministic_across_launches(monkeypatch):
     assert_within_tolerance(runs[0], ref, K, "split vs oracle")
 
 
+# Split K within one XCD: when a strip's splits share an XCD (the strips a
+# multiple of 8, one workgroup per unit) the partials are plain stores read
+# back through that XCD's L2; otherwise (GEMM_BF16_SKINNY_COLOCATE=0) they
+# cross XCDs as device-wide atomics.  (The two place strips differently, so
+# each unit walks its K range from a different rotated start: their sums
+# round differently and both are checked against the oracle.)  Three
+# colocated calls in a row must agree bit for bit: the handoff records
+# return to zero after every call.
+@pytest.mark.parametrize("M,N,K,ldc,cols", [
+    (64, 2048, 4096, 64, "32"),    # 64 strips of 32 columns, 4 splits
+    (64, 4096, 8192, 64, "64"),    # 64 strips of 64 columns, 4 splits (the default there)
+    (40, 1000, 4096, 41, "32"),    # N tail, odd ldc, 32 strips, 4 splits
+    (17, 2048, 8192, 17, "32"),    # 32-row block, 64 strips, 4 splits
+    (64, 512, 16384, 64, "32"),    # 16 strips, 16 splits
+])
+def test_skinny_colocated_and_crossing_splits(M, N, K, ldc, cols, monkeypatch):
+    case = inputs.random_case(M + N + K, M, N, K, ldc=ldc, with_c0=True, with_bias=True)
+    monkeypatch.setenv("GEMM_BF16_SKINNY_COLS", cols)
+    assert gb.gemm_bf16_kernel_name(M, N, K, 4096, K, 4096, K, 4096, ldc) == SK
+    say(f"[skinny-colocated] {M}x{N}x{K} ldc={ldc} cols={cols}")
+    run = lambda: run_gpu(M, N, K, case["A"], K, case["B"], K, case["C0"], ldc, 1.25, -0.5, case["bias"], "relu")
+    coloc = [run() for _ in range(3)]
+    for r in coloc[1:]:
+        assert np.array_equal(coloc[0], r), "colocated skinny split varies between calls"
+    monkeypatch.setenv("GEMM_BF16_SKINNY_COLOCATE", "0")
+    cross = run()
+    ref = oracle.gemm(M, N, K, case["A"], K, case["B"], K, case["C0"], ldc, 1.25, -0.5, case["bias"], "relu",
+                      nthreads=_threads())
+    r2 = ref.reshape(N, ldc)
+    for tag, got in (("colocated", coloc[0]), ("crossing", cross)):
+        g2 = got.reshape(N, ldc)
+        assert_within_tolerance(g2[:, :M], r2[:, :M], K, f"{tag} skinny split vs oracle")
+        assert np.array_equal(g2[:, M:], case["C0"].reshape(N, ldc)[:, M:]), f"{tag}: padding rows of C written"
+
+
+@pytest.mark.parametrize("M,N,K,ldq", [(40, 512, 4096, 48), (64, 1024, 8192, 64)])
+def test_skinny_colocated_split_int8_output(M, N, K, ldq):
+    """The int8-output instance takes the same colocated handoff (16 or 32
+    strips of 32 columns, 4 or 8 splits)."""
+    check_q8(f"q8 skinny colocated {M}x{N}x{K}", M, N, K, ldq=ldq, alpha=1.25, beta=0.5, use_bias=True,
+             epilogue="gelu_tanh", zp=2, seed=M + N, expect_kernel=SQ8K)
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 2048, 8192), (40, 1024, 16384)])
+def test_skinny_colocated_split_fp8(M, N, K):
+    """The FP8 instance takes the same colocated handoff (64 or 32 strips,
+    4 or 8 splits of 512-value slices)."""
+    check_fp8(f"fp8 skinny colocated {M}x{N}x{K}", M, N, K, beta=-0.25, use_bias=True, epilogue="relu",
+              seed=M + K, expect_kernel=SKF)
+
+
 # ---------------------------------------------------- bounds-checked path ---
 
 @pytest.mark.parametrize("M,N,K", [
