@@ -19,12 +19,13 @@
  *
  * Every function is thread-safe.  The library keeps no pointer to caller
  * buffers after a call returns.  Its one device allocation is the split-K
- * workspace (fp32 partial sums, and arrival counters for the short-product
- * kernel) used by three kinds of shape: 3 <= M <= 64 with few columns,
- * and products, bf16 or FP8, whose 128x128 tiles would leave most compute
- * units idle and whose K is long enough to pay for the split (for example
- * 512 x 512 x 8192; with tails the partials are padded to whole tiles).
- * It is one buffer per
+ * workspace (fp32 partial sums, and per-strip arrival counters or handoff
+ * records for the short-product kernel, whose splits pass their partials
+ * within one XCD where the strips allow it), used by shapes of two kinds:
+ * 3 <= M <= 64 with few columns, and products, bf16 or FP8, whose 128x128
+ * tiles would leave most compute units idle and whose K is long enough to
+ * pay for the split (for example 512 x 512 x 8192; with tails the partials
+ * are padded to whole tiles).  It is one buffer per
  * (device, stream) of a fixed size -- 64 KiB of counters plus 64 KiB per
  * compute unit (16 MiB + 64 KiB on a 256-CU device) -- allocated with
  * hipMalloc by the first call on that stream that splits K (its counters
