@@ -12,8 +12,10 @@ on both sides); their mean is `value` and the roofline's achieved rate.  A
 second pass of K launches, each between its own event pair, gives the
 per-launch spread (min / median / max); a per-launch pair also times the
 command processor's dispatch of the kernel, a few microseconds that matter
-for the short memory-bound launch.  When beta != 0 C is in/out: every launch
-reads the previous launch's output as C0 (same bytes, same work).
+for the short memory-bound launch.  Then the pages' own protocol (one
+warm-up launch, the mean of 8 launches) is reported beside it.  When
+beta != 0 C is in/out: every launch reads the previous launch's output as C0
+(same bytes, same work).
 
 Prints ONE JSON line (rank 0, one GPU).  With --all it prints one line per
 workload instead.
@@ -249,6 +251,18 @@ def run_workload(w, steps, warmup, cold, with_cpu):
     log(f"[bench] per-launch event pairs ms: mean {statistics.fmean(per):.4f} min {min(per):.4f} "
         f"median {statistics.median(per):.4f} max {max(per):.4f}")
 
+    # The pages' own protocol, after the runs above: one warm-up launch, then
+    # the mean of 8 launches, each between its own event pair.
+    call(launch(warmup + 2 * steps))
+    ev8 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(8)]
+    for i in range(8):
+        j = launch(warmup + 2 * steps + 1 + i)
+        ev8[i][0].record(stream)
+        call(j)
+        ev8[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms8 = statistics.fmean(a.elapsed_time(b) for a, b in ev8)
+
     rec = measured_record(w.name, kname)
     traffic = rec.get("hbm_bytes_per_launch") if rec else None
     if w.bound == "hbm":
@@ -283,6 +297,9 @@ def run_workload(w, steps, warmup, cold, with_cpu):
         "per_launch_event_pairs_ms": {"mean": statistics.fmean(per), "min": min(per),
                                       "median": statistics.median(per), "max": max(per),
                                       "stdev": statistics.pstdev(per)},
+        "pages_protocol": {"warmup": 1, "runs": 8, "ms_mean": ms8, "tflops": w.flops / (ms8 * 1e-3) / 1e12,
+                           "note": "after the timed region: 1 warm-up launch, then the mean of 8 launches each "
+                                   "timed by its own event pair"},
         "timed_region_wall_ms": wall * 1e3,
         "timed_region_event_ms": region_ms,
         "roofline": roof,
