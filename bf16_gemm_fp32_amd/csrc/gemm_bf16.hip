@@ -212,7 +212,7 @@ struct SkinnyPlan {
 };
 
 static SkinnyPlan plan_skinny_width(int64_t M, int64_t N, int64_t K, int cus, size_t cap_floats, bool fp8,
-                                    int width, bool coloc_ok) {
+                                    int width, int coloc_ok) {
     SkinnyPlan p{};
     p.rows = M <= 32 ? 32 : 64;
     p.cols = width;
@@ -235,16 +235,20 @@ static SkinnyPlan plan_skinny_width(int64_t M, int64_t N, int64_t K, int cus, si
     if (splits < 1) splits = 1;
     p.spp = (int)((nk + splits - 1) / splits);
     p.splits = (int)((nk + p.spp - 1) / p.spp);  // no empty split
-    p.colocate = coloc_ok && p.splits > 1 && p.splits < 256 && strips % kNumXcds == 0 &&
-                 strips * p.splits <= cus && (size_t)strips * sizeof(HandoffRecord) <= kScratchCounterBytes;
+    const bool coloc = coloc_ok && p.splits > 1 && p.splits < 256 && strips % kNumXcds == 0 &&
+                       strips * p.splits <= cus && (size_t)strips * sizeof(HandoffRecord) <= kScratchCounterBytes;
+    p.colocate = coloc ? coloc_ok : 0;
     return p;
 }
 
 static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int cus, size_t cap_floats, bool fp8 = false,
                               bool q8 = false) {
-    bool coloc_ok = true;
-    if (const char *env = std::getenv("GEMM_BF16_SKINNY_COLOCATE"))  // tuning knob: 0 = partials cross XCDs
-        coloc_ok = env[0] != '0';
+    int coloc_ok = 1;
+    if (const char *env = std::getenv("GEMM_BF16_SKINNY_COLOCATE")) {
+        // tuning knob: 0 = partials cross XCDs; testing knob: "fence" = colocated, always the fenced path
+        if (env[0] == '0') coloc_ok = 0;
+        if (!std::strcmp(env, "fence")) coloc_ok = 2;
+    }
     if (fp8 || q8)  // the FP8 and int8-output instances are built for 32-column strips
         return plan_skinny_width(M, N, K, cus, cap_floats, fp8, 32, coloc_ok);
     if (const char *env = std::getenv("GEMM_BF16_SKINNY_COLS")) {  // tuning knob: 32, 64 or 128

@@ -19,8 +19,9 @@
 // started) it makes its stores visible device-wide with an agent-scope
 // release fence and says so when it arrives; a last part that sees such an
 // arrival performs an agent-scope acquire fence before it reads -- the
-// memory model's own synchronisation, much slower (it writes back and
-// invalidates whole caches) but correct wherever the parts run.  A part
+// memory model's own synchronisation, slower (it writes back and
+// invalidates whole caches: about 5 us per launch on the short products
+// measured) but correct wherever the parts run.  A part
 // that skipped its fence saw all parts on its XCD, the last one included,
 // so its partial is in the last part's L2.
 //
@@ -56,32 +57,23 @@ __device__ __forceinline__ void handoff_register(HandoffRecord *rec, int xcd) {
         __hip_atomic_fetch_add(&rec->start, 1ull << (8 * xcd), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Thread 0, once every wave's stores have completed at its L2: the
-// placement check, the release fence when it fails, and the arrival.
-// Returns the arrive word before this part's arrival.
-__device__ __forceinline__ unsigned long long handoff_publish(HandoffRecord *rec, int parts, int xcd, bool &local) {
-    const unsigned long long start = __hip_atomic_load(&rec->start, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    local = xcd < 8 && start == ((unsigned long long)parts << (8 * xcd));
-    if (!local) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    return __hip_atomic_fetch_add(&rec->arrive, local ? 1ull : 0x101ull, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ int handoff_arrived(unsigned long long w) { return (int)(w & 0xFFu); }
-__device__ __forceinline__ bool handoff_fenced(unsigned long long w) { return ((w >> 8) & 0xFFu) != 0u; }
-
 // Every thread of the part, after it has issued the stores of its partial.
 // Returns true in the last part to arrive, whose loads then see every
-// partner's partial.  flag: a 4-byte LDS word, free until the next barrier
-// of the caller.
-__device__ __forceinline__ bool handoff_arrive(HandoffRecord *rec, int parts, int xcd, uint32_t *flag) {
+// partner's partial.  fence_always: take the fenced path even when the
+// placement check passes (for testing that path).  flag: a 4-byte LDS word,
+// free until the next barrier of the caller.
+__device__ __forceinline__ bool handoff_arrive(HandoffRecord *rec, int parts, int xcd, bool fence_always,
+                                               uint32_t *flag) {
     wait_vmcnt<0>();  // this wave's stores have completed at its L2
     __syncthreads();  // and every wave's
     if (threadIdx.x == 0) {
-        bool local;
-        const unsigned long long old = handoff_publish(rec, parts, xcd, local);
-        const bool last = handoff_arrived(old) + 1 == parts;
-        const bool fenced = handoff_fenced(old) || !local;
+        const unsigned long long start = __hip_atomic_load(&rec->start, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool local = !fence_always && xcd < 8 && start == ((unsigned long long)parts << (8 * xcd));
+        if (!local) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        const unsigned long long old = __hip_atomic_fetch_add(&rec->arrive, local ? 1ull : 0x101ull,
+                                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = (int)(old & 0xFFu) + 1 == parts;
+        const bool fenced = ((old >> 8) & 0xFFu) != 0u || !local;
         *flag = (last ? 1u : 0u) | (fenced ? 2u : 0u);
     }
     __syncthreads();

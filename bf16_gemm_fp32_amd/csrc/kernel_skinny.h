@@ -102,7 +102,8 @@ struct SkinnyConfig {
 // uint32 counter or (colocate) one handoff record, zero between calls.
 // colocate: the grid is exactly one workgroup per unit, a multiple of 8 of
 // them, and each XCD's run of slots holds whole strips; a strip's splits
-// then hand their partials over within one XCD (handoff.h).
+// then hand their partials over within one XCD (handoff.h) -- with 2, always
+// through the fenced path (for testing it).
 struct SkinnyWork {
     int num_strips;
     int splits;
@@ -438,7 +439,7 @@ gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
                 *(f32x4 *)(mine + idx * 8 + 4) = f32x4{x[4], x[5], x[6], x[7]};
             }
             uint32_t *flag = (uint32_t *)(smem + Cfg::kFlagOffset);
-            if (!handoff_arrive(work.records + strip, work.splits, xcd, flag)) continue;
+            if (!handoff_arrive(work.records + strip, work.splits, xcd, work.colocate == 2, flag)) continue;
             constexpr int kCpt = (kChunks + Cfg::kThreads - 1) / Cfg::kThreads;
             constexpr int64_t kUnitFloats = Cfg::BN * Cfg::BMr;
             const float *base = work.partials + (int64_t)strip * work.splits * kUnitFloats;

@@ -460,8 +460,10 @@ def test_skinny_split_k_is_deterministic_across_launches(monkeypatch):
 # cross XCDs as device-wide atomics.  (The two place strips differently, so
 # each unit walks its K range from a different rotated start: their sums
 # round differently and both are checked against the oracle.)  Three
-# colocated calls in a row must agree bit for bit: the handoff records
-# return to zero after every call.
+# colocated calls in a row must agree bit for bit -- the handoff records
+# return to zero after every call -- and so must a call that takes the
+# handoff's fallback, the agent-scope release/acquire fences, although the
+# placement check passes (GEMM_BF16_SKINNY_COLOCATE=fence).
 @pytest.mark.parametrize("M,N,K,ldc,cols", [
     (64, 2048, 4096, 64, "32"),    # 64 strips of 32 columns, 4 splits
     (64, 4096, 8192, 64, "64"),    # 64 strips of 64 columns, 4 splits (the default there)
@@ -478,6 +480,8 @@ def test_skinny_colocated_and_crossing_splits(M, N, K, ldc, cols, monkeypatch):
     coloc = [run() for _ in range(3)]
     for r in coloc[1:]:
         assert np.array_equal(coloc[0], r), "colocated skinny split varies between calls"
+    monkeypatch.setenv("GEMM_BF16_SKINNY_COLOCATE", "fence")
+    assert np.array_equal(coloc[0], run()), "the fenced handoff differs from the L2 handoff"
     monkeypatch.setenv("GEMM_BF16_SKINNY_COLOCATE", "0")
     cross = run()
     ref = oracle.gemm(M, N, K, case["A"], K, case["B"], K, case["C0"], ldc, 1.25, -0.5, case["bias"], "relu",
