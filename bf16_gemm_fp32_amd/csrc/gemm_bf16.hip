@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cmath>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -351,11 +352,21 @@ static hipError_t launch_skinny_plan(const GemmArgs &args, int cus, const Scratc
 
 // Split-K on the 128x128 tiles: used when those tiles alone would leave more
 // than half of the compute units idle.  The K-slices (64 wide) are cut into
-// up to CUs / tiles ranges of at least kMinSlices slices each, so every
-// range still runs a pipelined loop; partials take splits x (M x N padded to
-// tiles) floats of scratch (at most CUs x 16K floats: splits * tiles <= CUs
-// and a tile is 16K elements; forced split counts are capped by cap_floats).
-// Returns 1 when no split applies.
+// ranges of at least kMinSlices slices each, so every range still runs a
+// pipelined loop, and at most CUs / tiles of them.  How many: a split trades
+// each unit's K loop (slices / splits) against the fp32 partials written and
+// read back (splits x tiles whole tiles), and the count that balances the
+// two is close to 3 sqrt(slices / tiles); it is raised to the count that
+// gives at least half of the compute units a unit.  Measured interleaved in
+// one process (the count that fills every compute unit in parentheses):
+// 1024 x 1024 x 4096 3 ranges 18.8 us (4: 19.5 us; 24.2 against 20.6 us on
+// a slower box), 1024 x 512 x 4096 4 ranges 15.7 us (8: 18.1 us),
+// 512 x 512 x 8192 8 ranges 16.7 us (16: 18.4 us), 768 x 768 x 4096 4 ranges
+// 18.1 us (7: 18.2 us; 3 ranges 17.3 us), 512 x 512 x 4096 8 ranges 12.9 us
+// (the square-root rule alone would take 6, 13.7 us).  Partials take
+// splits x (M x N padded to tiles) floats of scratch (at most CUs x 16K
+// floats: splits * tiles <= CUs and a tile is 16K elements; forced split
+// counts are capped by cap_floats).  Returns 1 when no split applies.
 constexpr int kSplitMinSlices = 8;
 
 // Shape: the 128x128 tiles' K-slice (ShapeM, 64 bf16 values; ShapeFp8M, 128
@@ -368,7 +379,10 @@ static TileSplit plan_splitk(int64_t M, int64_t N, int64_t K, int cus, size_t ca
     const int64_t tiles = ((M + Shape::BM - 1) / Shape::BM) * ((N + Shape::BN - 1) / Shape::BN);
     const int64_t nk = (K + Shape::BK - 1) / Shape::BK;
     if (tiles <= 0 || tiles * 2 >= cus) return p;
-    int64_t splits = cus / tiles;
+    int64_t splits = std::llround(3.0 * std::sqrt((double)nk / (double)tiles));
+    const int64_t half = (cus / 2 + tiles - 1) / tiles;
+    if (splits < half) splits = half;
+    if (splits > cus / tiles) splits = cus / tiles;
     if (const char *env = std::getenv("GEMM_BF16_SPLITK_SPLITS")) {  // tuning knob
         const int v = std::atoi(env);
         if (v >= 1) splits = v;
@@ -397,16 +411,19 @@ static TileSplit plan_splitk(int64_t M, int64_t N, int64_t K, int cus, size_t ca
 // Whether splitting K beats the unsplit 128x128 kernel on a small grid.
 // Measured: the unsplit kernel takes about 4.3 us plus 0.31 us per 64-wide
 // K-slice whatever the tile count (up to 64 tiles), while the split pays a
-// reduction kernel and runs more, busier compute units; it wins from about
-// 26 slices at 16 tiles, 33 at 32 tiles and 46 at 64 tiles (1024 x 1024 x
-// 1024: 15.2 us split against 9.4 us unsplit; 1024 x 1024 x 4096: 23.4 us
-// against 25.0 us).  The quantizing output has no unsplit small-grid kernel
-// and splits whenever the plan allows.
+// reduction kernel and runs more, busier compute units; with the range
+// counts of plan_splitk it wins from about 26 slices at 16 tiles, 32 at 32
+// tiles and 45 at 64 tiles (interleaved: 1024 x 512 x 2048 12.7 us split
+// against 14.6 us unsplit, FP8 1024 x 512 x 4096 13.1 against 15.5 us;
+// 1024 x 1024 x 2048 14.9 against 14.8 us; 768 x 768 x 2048, 36 tiles,
+// 15.9 against 14.6 us; 1024 x 1024 x 4096 20.1 against 25.6 us).  The
+// quantizing output has no unsplit small-grid kernel and splits whenever
+// the plan allows.
 template <class Shape>
 static bool splitk_pays_t(int64_t M, int64_t N, int64_t K) {
     const int64_t tiles = ((M + Shape::BM - 1) / Shape::BM) * ((N + Shape::BN - 1) / Shape::BN);
     const int64_t nk = (K + Shape::BK - 1) / Shape::BK;
-    return 5 * nk >= 100 + 2 * tiles;
+    return 5 * nk >= 96 + 2 * tiles;
 }
 static bool splitk_pays(int64_t M, int64_t N, int64_t K) { return splitk_pays_t<ShapeM>(M, N, K); }
 

@@ -137,7 +137,7 @@ def test_fp8_argument_errors_and_names():
     assert name(3, 8192, 8192, P, 8192, P, 8192, P, 3) == "skinny_fp8"   # large B: A shared per strip
     assert name(4, 16384, 4096, P, 4096, P, 4096, P, 4) == "skinny_fp8"
     # grids where the 256x256 tiles fill less than half the CUs take the
-    # 128x128 tiles, splitting K by the bf16 rule (5 nk >= 100 + 2 tiles)
+    # 128x128 tiles, splitting K by the bf16 rule (5 nk >= 96 + 2 tiles)
     assert name(1024, 1024, 4096, P, 4096, P, 4096, P, 1024) == "fp8_128x128x128"         # 64 tiles, 32 slices
     assert name(512, 512, 8192, P, 8192, P, 8192, P, 512) == "splitk_fp8_128x128x128"     # 16 tiles, 64 slices
     assert name(256, 256, 8192, P, 8192, P, 8192, P, 256) == "splitk_fp8_128x128x128"     # 4 tiles
@@ -151,7 +151,9 @@ def test_fp8_argument_errors_and_names():
     assert name(4, 4096, 4096, P, 4096, P, 4096, P + 2, 5) == "gemv_fp8"
     assert name(5, 4096, 4096, P, 4096, P, 4096, P, 8) == "skinny_fp8"
     assert name(64, 8192, 8192, P, 8192, P, 8192, P, 64) == "skinny_fp8"
-    assert name(65, 4096, 4096, P, 4096, P, 4096, P, 72) == "fp8_128x128x128_masked"  # 32 tiles, 32 slices
+    assert name(65, 4096, 4096, P, 4096, P, 4096, P, 72) == "splitk_fp8_128x128x128_masked"  # 32 tiles, 32 slices
+    assert name(1024, 512, 4096, P, 4096, P, 4096, P, 1024) == "splitk_fp8_128x128x128"  # 32 tiles, 32 slices
+    assert name(768, 768, 4096, P, 4096, P, 4096, P, 768) == "fp8_128x128x128"  # 36 tiles, 32 slices
     assert name(65, 4096, 16384, P, 16384, P, 16384, P, 72) == "splitk_fp8_128x128x128_masked"
     assert name(1024, 1024, 2048, P, 2048, P, 2048, P, 1024) == "fp8_128x128x128"
     assert name(2048, 1024, 4096, P, 4096, P, 4096, P, 2048) == "fp8_128x128x128"  # 128 tiles: no split
@@ -227,6 +229,8 @@ def test_kernel_selection_names():
     assert name(512, 512, 8192, P, 8192, P, 8192, P, 512) == "splitk128x128x64"
     assert name(512, 512, 2048, P, 2048, P, 2048, P, 512) == "splitk128x128x64"     # 16 tiles, 32 slices
     assert name(1024, 1024, 2048, P, 2048, P, 2048, P, 1024) == "tile128x128x64_s4"  # 64 tiles: K too short to split
+    assert name(1024, 512, 2048, P, 2048, P, 2048, P, 1024) == "splitk128x128x64"     # 32 tiles, 32 slices
+    assert name(768, 768, 2048, P, 2048, P, 2048, P, 768) == "tile128x128x64_s4"     # 36 tiles, 32 slices
     assert name(1024, 1024, 1024, P, 1024, P, 1024, P, 1024) == "tile128x128x64_s4"
     assert name(512, 512, 512, P, 512, P, 512, P, 512) == "tile128x128x64_s4"   # 8 slices: no split
     assert name(2048, 2048, 4096, P, 4096, P, 4096, P, 2048) == "tile128x128x64_s4"  # 256 tiles
