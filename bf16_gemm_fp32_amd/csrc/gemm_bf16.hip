@@ -190,8 +190,12 @@ constexpr size_t kScratchFloatsPerCu = 128 * 128;
 // 64), strip width, and the K split.
 //  * 32-column strips by default.  K is split only when the strips alone
 //    would leave more than half of the compute units idle: then up to one
-//    unit per compute unit, each split keeping at least 4 K-slices so the
-//    rings have something to overlap.  The split colocates (handoff.h) when
+//    unit per compute unit, each split keeping at least 8 K-slices (4 where
+//    K is too short for 4 such splits) so the rings have something to
+//    overlap: interleaved, cold B, 64 x 512 x 16384 takes 15.5 us in 8
+//    splits against 18.2 us in 16, 32 x 1024 x 8192 11.3 us in 4 against
+//    12.4 us in 8, while 64 x 2048 x 4096 keeps 4 splits of 4 slices
+//    (11.9 us; 2 splits 12.7 us).  The split colocates (handoff.h) when
 //    the strips are a multiple of 8 and every unit has its own workgroup;
 //    else the partials cross XCDs through device-wide atomics.  Colocated
 //    against crossing, interleaved in one process (cold B): 64 x 2048 x 4096
@@ -228,7 +232,11 @@ static SkinnyPlan plan_skinny_width(int64_t M, int64_t N, int64_t K, int cus, si
         const int s = std::atoi(env);
         if (s >= 1) splits = s;
     }
-    const int64_t max_splits = nk / 4 > 1 ? nk / 4 : 1;
+    // At least 8 K-slices per split, so the rings (3 and 4 slices deep) have
+    // a loop to overlap, or 4 where K is too short for 4 such splits.
+    int64_t max_splits = nk / 8;
+    if (max_splits < 4) max_splits = nk / 4 < 4 ? nk / 4 : 4;
+    if (max_splits < 1) max_splits = 1;
     if (splits > max_splits) splits = max_splits;
     const int64_t per_split = strips * (int64_t)p.cols * p.rows;
     if (splits > 1 && (strips > (int64_t)kScratchCounters || splits * per_split > (int64_t)cap_floats))

@@ -439,7 +439,7 @@ def test_skinny_split_k_is_deterministic_across_launches(monkeypatch):
     unit arrives last, and resets the strip counters -- repeated launches on
     one stream are bit-identical and match the unsplit kernel within the
     tolerance."""
-    M, N, K = 64, 2048, 8192
+    M, N, K = 64, 2048, 16384  # 32 strips of 64 columns, 8 splits of 8 slices
     case = inputs.random_case(91, M, N, K)
     C_init = np.zeros(M * N, np.uint16)
     monkeypatch.setenv("GEMM_BF16_SKINNY_COLS", "64")
@@ -469,7 +469,7 @@ def test_skinny_split_k_is_deterministic_across_launches(monkeypatch):
     (64, 4096, 8192, 64, "64"),    # 64 strips of 64 columns, 4 splits (the default there)
     (40, 1000, 4096, 41, "32"),    # N tail, odd ldc, 32 strips, 4 splits
     (17, 2048, 8192, 17, "32"),    # 32-row block, 64 strips, 4 splits
-    (64, 512, 16384, 64, "32"),    # 16 strips, 16 splits
+    (64, 512, 16384, 64, "32"),    # 16 strips, 8 splits
 ])
 def test_skinny_colocated_and_crossing_splits(M, N, K, ldc, cols, monkeypatch):
     case = inputs.random_case(M + N + K, M, N, K, ldc=ldc, with_c0=True, with_bias=True)
@@ -496,7 +496,7 @@ def test_skinny_colocated_and_crossing_splits(M, N, K, ldc, cols, monkeypatch):
 @pytest.mark.parametrize("M,N,K,ldq", [(40, 512, 4096, 48), (64, 1024, 8192, 64)])
 def test_skinny_colocated_split_int8_output(M, N, K, ldq):
     """The int8-output instance takes the same colocated handoff (16 or 32
-    strips of 32 columns, 4 or 8 splits)."""
+    strips of 32 columns, 4 splits)."""
     check_q8(f"q8 skinny colocated {M}x{N}x{K}", M, N, K, ldq=ldq, alpha=1.25, beta=0.5, use_bias=True,
              epilogue="gelu_tanh", zp=2, seed=M + N, expect_kernel=SQ8K)
 
@@ -504,7 +504,7 @@ def test_skinny_colocated_split_int8_output(M, N, K, ldq):
 @pytest.mark.parametrize("M,N,K", [(16, 2048, 8192), (40, 1024, 16384)])
 def test_skinny_colocated_split_fp8(M, N, K):
     """The FP8 instance takes the same colocated handoff (64 or 32 strips,
-    4 or 8 splits of 512-value slices)."""
+    4 splits of 512-value slices)."""
     check_fp8(f"fp8 skinny colocated {M}x{N}x{K}", M, N, K, beta=-0.25, use_bias=True, epilogue="relu",
               seed=M + K, expect_kernel=SKF)
 
