@@ -681,18 +681,21 @@ static int choose_kernel_fp8(int64_t M, int64_t N, int64_t K, const void *A, int
     if (force && can_split &&
         (!std::strcmp(force, kKindNames[kFp8SplitK]) || !std::strcmp(force, kKindNames[kFp8SplitKMasked])))
         return exact ? kFp8SplitK : kFp8SplitKMasked;
-    // Small and mid-sized grids (the 256x256 tiles fill less than half of
-    // the compute units): the 128x128 tiles, splitting K by the bf16 128x128
+    // Small and mid-sized grids (the 256x256 tiles fill at most half of the
+    // compute units): the 128x128 tiles, splitting K by the bf16 128x128
     // kernel's rule (an FP8 slice of 128 has its bytes and MFMA time).  The
     // reduction takes any C: it reads and writes a chunk element by element
     // where ldc % 8 != 0, C is unaligned or the chunk straddles M.
     // Measured against the 256x256 paths (split where they split): 1024 x
     // 1024 x 4096 16.4 us against 32.5, 512 x 512 x 8192 (split) 14.8 against
     // 26.8, 2048 x 2048 x 2048 13.0 against 24.8, 1000 x 1000 x 4096 22.1
-    // against 31.6; at 144 tiles of 256x256 (3072 x 3072 x 2048) the large
-    // tiles win, 27.4 against 34.8.
+    // against 31.6.  At exactly half (128 tiles of 256x256) the 128x128
+    // tiles still win, as for bf16: 2048 x 4096 x 4096 35.3 against 39.0 us,
+    // 2048 x 4096 x 8192 60.9 against 69.8 us; at 144 tiles of 256x256 the
+    // large tiles do (3072 x 3072 x 2048 27.4 against 34.8 us, 3072 x 3072 x
+    // 4096 39.0 against 50.2 us).
     const int64_t tiles256 = ((M + ShapeFp8::BM - 1) / ShapeFp8::BM) * ((N + ShapeFp8::BN - 1) / ShapeFp8::BN);
-    if (ok128 && tiles256 * 2 < cus) {
+    if (ok128 && tiles256 * 2 <= cus) {
         if (can_split128 && splitk_pays_t<ShapeFp8M>(M, N, K))
             return exact128 ? kFp8SplitKMedium : kFp8SplitKMediumMasked;
         return exact128 ? kFp8Medium : kFp8MediumMasked;

@@ -145,7 +145,8 @@ def test_fp8_argument_errors_and_names():
     assert name(1000, 1000, 4096, P, 4096, P, 4096, P, 1000) == "fp8_128x128x128_masked"
     assert name(1000, 1000, 208, P, 208, P, 208, P, 1000) == "fp8_128x128x128_masked"    # K tail
     assert name(500, 500, 8192, P, 8192, P, 8192, P, 504) == "splitk_fp8_128x128x128_masked"
-    assert name(2048, 4096, 4096, P, 4096, P, 4096, P, 2048) == "fp8_256x256x128"  # 128 tiles of 256x256
+    assert name(2048, 4096, 4096, P, 4096, P, 4096, P, 2048) == "fp8_128x128x128"  # 128 tiles of 256x256: half
+    assert name(2304, 4096, 4096, P, 4096, P, 4096, P, 2304) == "fp8_256x256x128"  # 144 tiles of 256x256
     assert name(2048, 2048, 4096, P, 4096, P, 4096, P, 2048) == "fp8_128x128x128"  # 256 tiles of 128x128
     assert name(3072, 3072, 2048, P, 2048, P, 2048, P, 3072) == "fp8_256x256x128"  # 144 tiles of 256x256
     assert name(4, 4096, 4096, P, 4096, P, 4096, P + 2, 5) == "gemv_fp8"
