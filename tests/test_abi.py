@@ -223,7 +223,8 @@ def test_kernel_selection_names():
     assert name(4000, 4000, 4000, P, 4000, P, 4000, P, 4000) == "ring256x256x64_masked"
     assert name(2048, 4096, 4096, P, 4096, P, 4096, P, 2048) == "tile128x128x64_s4"  # 128 ring tiles: half the CUs
     assert name(2304, 4096, 4096, P, 4096, P, 4096, P, 2304) == "ring256x256x64"     # 144 ring tiles
-    assert name(4000, 2000, 1000, P, 1000, P, 1000, P, 4000) == "ring256x256x64_masked"
+    assert name(4000, 2000, 1000, P, 1000, P, 1000, P, 4000) == "tile128x128x64_s4_masked"  # 128 ring tiles: half
+    assert name(4000, 2100, 1000, P, 1000, P, 1000, P, 4000) == "ring256x256x64_masked"     # 144 ring tiles
     assert name(256, 256, 256, P, 256, P, 256, P, 256) == "tile128x128x64_s4"
     # small grids of 128-tiles with enough K-slices: split-K
     assert name(1024, 1024, 4096, P, 4096, P, 4096, P, 1024) == "splitk128x128x64"

@@ -122,8 +122,9 @@ def check_full(tag, M, N, K, lda=None, ldb=None, ldc=None, alpha=1.0, beta=0.0, 
     (4608, 2048, 320, "ring256x256x64"),      # 144 tiles of 256, 5 slices of 64
     (4608, 2048, 64, "ring256x256x64"),       # a single K-slice
     (4096, 2048, 320, "tile128x128x64_s4"),   # 128 ring tiles, half the CUs: 128x128 tiles, two per CU
-    (4096, 2048, 352, "ring256x256x64_masked"),  # K % 64 == 32: a half-empty last slice
-    (4096, 2048, 32, "ring256x256x64_masked"),   # a single half-empty K-slice
+    (4608, 2048, 352, "ring256x256x64_masked"),  # K % 64 == 32: a half-empty last slice
+    (4608, 2048, 32, "ring256x256x64_masked"),   # a single half-empty K-slice
+    (4096, 2048, 352, "tile128x128x64_s4_masked"),  # half the CUs in ring tiles, with a K tail: 128x128 masked
 ])
 def test_tile_paths_full(M, N, K, kernel):
     check_full(f"tile {M}x{N}x{K}", M, N, K, seed=M + N + K, expect_kernel=kernel)
@@ -132,7 +133,7 @@ def test_tile_paths_full(M, N, K, kernel):
 def test_tile_path_epilogue_full():
     check_full("ring256 epilogue", 4608, 2048, 192, alpha=1.0, beta=0.5, use_bias=True,
                epilogue="gelu_tanh", seed=11, expect_kernel="ring256x256x64")
-    check_full("masked ring epilogue", 4096, 2048, 160, alpha=1.0, beta=0.5, use_bias=True,
+    check_full("masked ring epilogue", 4608, 2048, 160, alpha=1.0, beta=0.5, use_bias=True,
                epilogue="gelu_tanh", seed=16, expect_kernel="ring256x256x64_masked")
     check_full("tile128 epilogue", 512, 512, 128, alpha=-0.75, beta=-1.5, use_bias=True,
                epilogue="none", seed=12, expect_kernel="tile128x128x64_s4")
@@ -145,7 +146,7 @@ def test_tile_path_padded_leading_dims():
                seed=14, expect_kernel="tile128x128x64_s4")
     check_full("ring256 padded ld", 4608, 2048, 128, lda=136, ldb=192, ldc=4616, seed=15,
                expect_kernel="ring256x256x64")
-    check_full("masked ring padded ld", 4096, 2048, 96, lda=104, ldb=136, ldc=4112, seed=17,
+    check_full("masked ring padded ld", 4608, 2048, 96, lda=104, ldb=136, ldc=4616, seed=17,
                expect_kernel="ring256x256x64_masked")
 
 
@@ -318,7 +319,7 @@ def test_masked_ring_epilogue_combinations(beta, use_bias, epi, monkeypatch):
 
 
 def test_masked_ring_any_ldc_and_c_alignment():
-    check_full("masked ring odd ldc", 4000, 2000, 320, ldc=4001, beta=0.5, use_bias=True, epilogue="gelu_tanh",
+    check_full("masked ring odd ldc", 4500, 2000, 320, ldc=4501, beta=0.5, use_bias=True, epilogue="gelu_tanh",
                seed=350, expect_kernel="ring256x256x64_masked")
     check_full("masked ring unaligned C", 4096, 2304, 256, ldc=4104, offsets=(0, 0, 3), beta=-0.5, seed=351,
                expect_kernel="ring256x256x64_masked")
@@ -330,7 +331,7 @@ def test_q8_exact_ring_unaligned_c0_takes_the_masked_instance():
 
 
 def test_masked_ring_is_the_default_for_large_ragged_shapes():
-    check_full("ragged default", 4000, 2000, 1000, beta=0.5, use_bias=True, epilogue="gelu_tanh", seed=51,
+    check_full("ragged default", 4500, 2000, 1000, beta=0.5, use_bias=True, epilogue="gelu_tanh", seed=51,
                expect_kernel=MASKED)
 
 
