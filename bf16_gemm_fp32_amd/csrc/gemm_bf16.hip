@@ -558,10 +558,19 @@ static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t
     // third round).  The same with tails, masked: 2000 x 4000 x 4000 71.2
     // against 78.3 us, 2000 x 4000 x 2000 43.9 against 47.8 us; at 144 ring
     // tiles (2100 x 4000 x 4096) the masked ring, 85.8 against 99.9 us.
+    // Just over one round (more ring tiles than compute units, at most 5/4
+    // as many), the ring's second round leaves most compute units idle and
+    // the 128x128 tiles balance better: 4096 x 4608 x 4096 (288 ring tiles)
+    // 153.6 against 162.1 us, 5120 x 4096 x 4096 (320) 158.2 against
+    // 177.0 us, 4096 x 4608 x 1024 46.2 against 51.2 us; from 352 ring tiles
+    // (4096 x 5632 x 4096, 176.2 against 183.1 us) the ring is faster.  With
+    // tails the masked ring stays faster (4000 x 4500 x 4000 173.4 against
+    // 178.4 us).
     if (okRM) {
         const int64_t tiles = ((M + ShapeRing::BM - 1) / ShapeRing::BM) * ((N + ShapeRing::BN - 1) / ShapeRing::BN);
         if (tiles * 2 == cus && okM) return kMedium;
         if (tiles * 2 == cus && okMM) return kMediumMasked;
+        if (tiles > cus && tiles * 4 <= (int64_t)cus * 5 && okM) return kMedium;
         if (tiles * 2 >= cus || (!okM && okR)) return okR ? kRing : kRingMasked;
     }
     if (okL) {

@@ -125,6 +125,7 @@ def check_full(tag, M, N, K, lda=None, ldb=None, ldc=None, alpha=1.0, beta=0.0, 
     (4608, 2048, 352, "ring256x256x64_masked"),  # K % 64 == 32: a half-empty last slice
     (4608, 2048, 32, "ring256x256x64_masked"),   # a single half-empty K-slice
     (4096, 2048, 352, "tile128x128x64_s4_masked"),  # half the CUs in ring tiles, with a K tail: 128x128 masked
+    (4096, 4608, 256, "tile128x128x64_s4"),   # 288 ring tiles, just over one round: 1152 128x128 tiles, 4.5 per CU
 ])
 def test_tile_paths_full(M, N, K, kernel):
     check_full(f"tile {M}x{N}x{K}", M, N, K, seed=M + N + K, expect_kernel=kernel)
