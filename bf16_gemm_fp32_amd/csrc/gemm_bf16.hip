@@ -189,8 +189,8 @@ constexpr size_t kScratchFloatsPerCu = 128 * 128;
 // How the streaming kernel covers a short product: its row block (32 or
 // 64), strip width, and the K split.
 //  * 32-column strips by default.  K is split only when the strips alone
-//    would leave more than half of the compute units idle: then up to one
-//    unit per compute unit, each split keeping at least 8 K-slices (4 where
+//    would leave more than half of the compute units idle, or exactly half
+//    when the split colocates: then up to one unit per compute unit, each split keeping at least 8 K-slices (4 where
 //    K is too short for 4 such splits) so the rings have something to
 //    overlap: interleaved, cold B, 64 x 512 x 16384 takes 15.5 us in 8
 //    splits against 18.2 us in 16, 32 x 1024 x 8192 11.3 us in 4 against
@@ -226,7 +226,14 @@ static SkinnyPlan plan_skinny_width(int64_t M, int64_t N, int64_t K, int cus, si
     const int64_t nk = (K + ks - 1) / ks;
     const int64_t strips = (N + width - 1) / width;
     p.strips = (int)strips;
-    const bool split = width == 64 ? strips * 2 <= cus : strips * 2 < cus;
+    // 32-column strips filling exactly half of the compute units split in
+    // two when the halves colocate and keep 8 slices each: int8 output
+    // 64 x 4096 x 8192 21.1 against 28.7 us unsplit, FP8 64 x 4096 x 16384
+    // 20.1 against 25.1 us (FP8 32 x 4096 x 4096, 4 slices a half: 9.6
+    // against 8.5 us, so it stays whole).
+    const bool split = width == 64 ? strips * 2 <= cus
+                                   : strips * 2 < cus ||
+                                         (strips * 2 == cus && coloc_ok && strips % kNumXcds == 0 && nk >= 16);
     int64_t splits = split ? cus / strips : 1;
     if (const char *env = std::getenv("GEMM_BF16_SKINNY_SPLITS")) {  // tuning knob
         const int s = std::atoi(env);
