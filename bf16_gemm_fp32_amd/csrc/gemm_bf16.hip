@@ -190,9 +190,10 @@ constexpr size_t kScratchFloatsPerCu = 128 * 128;
 // 64), strip width, and the K split.
 //  * 32-column strips by default.  K is split only when the strips alone
 //    would leave more than half of the compute units idle, or exactly half
-//    when the split colocates: then up to one unit per compute unit, each split keeping at least 8 K-slices (4 where
-//    K is too short for 4 such splits) so the rings have something to
-//    overlap: interleaved, cold B, 64 x 512 x 16384 takes 15.5 us in 8
+//    when the split colocates: then up to one unit per compute unit, each
+//    split keeping at least 8 K-slices (4 where K is too short for 4 such
+//    splits) so the rings have something to overlap: interleaved, cold B,
+//    64 x 512 x 16384 takes 15.5 us in 8
 //    splits against 18.2 us in 16, 32 x 1024 x 8192 11.3 us in 4 against
 //    12.4 us in 8, while 64 x 2048 x 4096 keeps 4 splits of 4 slices
 //    (11.9 us; 2 splits 12.7 us).  The split colocates (handoff.h) when
@@ -628,6 +629,15 @@ static int choose_kernel_q8(int64_t M, int64_t N, int64_t K, const void *A, int6
         if (tile_path_ok<ShapeM>(M, N, K, A, lda, B, ldb, c_probe, ldc_probe) &&
             plan_splitk(M, N, K, cus, cap_floats).splits >= 2)
             return kSplitKQ8;
+        // Grids too large to split on 128x128 tiles and too small to fill
+        // half of the compute units with ring tiles: from more than an
+        // eighth of the compute units in ring tiles the ring, with idle
+        // compute units, beats the bounds-checked kernel (2048 x 2048 x 4096,
+        // 64 ring tiles: 76.7 against 95.7 us; 3072 x 2048 x 4096 79.8
+        // against 121.4 us; 1536 x 1536 x 4096, 36 tiles, 76.2 against
+        // 82.5 us); at 32 ring tiles or fewer it does not (2048 x 1024 x 4096
+        // 76.5 against 74.9 us, 1000 x 1000 x 4096 84.5 against 67.4 us).
+        if (tiles * 8 > cus && force == nullptr) return exact ? kRingQ8 : kRingQ8Masked;
     }
     return kGeneric;
 }

@@ -663,6 +663,16 @@ def test_q8_ring_is_the_default_for_large_shapes():
              expect_kernel=RQ8)
 
 
+@pytest.mark.parametrize("M,N,K,ldq,kernel", [
+    (2048, 2048, 256, 2048, RQ8),                # 64 ring tiles, 256 128x128 tiles: too many to split
+    (1500, 1500, 320, 1504, RQ8M),               # 36 ring tiles, with tails
+    (2048, 1024, 256, 2048, "generic64x64x32"),  # 32 ring tiles: the bounds-checked kernel is faster
+])
+def test_q8_mid_sized_grids(M, N, K, ldq, kernel):
+    check_q8(f"q8 mid {M}x{N}x{K}", M, N, K, ldq=ldq, ldc=ldq, beta=0.5, use_bias=True, epilogue="gelu_tanh", zp=5,
+             seed=M + N + K, expect_kernel=kernel)
+
+
 @pytest.mark.parametrize("M,N,K,ldq", [
     (1001, 777, 200, 1008), (257, 513, 8, 264), (1, 255, 64, 8), (300, 260, 72, 304), (512, 512, 256, 512),
 ])
