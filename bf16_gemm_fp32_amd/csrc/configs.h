@@ -47,6 +47,8 @@ hipError_t launch_tile_medium_splitk_q8(const GemmArgs &args, const TileSplit &s
 hipError_t launch_tile_medium_masked(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_medium_splitk_masked(const GemmArgs &args, const TileSplit &split, int cus,
                                             hipStream_t stream);
+hipError_t launch_tile_medium_splitk_q8_masked(const GemmArgs &args, const TileSplit &split, int cus,
+                                               hipStream_t stream);
 hipError_t launch_tile_ring_mfma32(const GemmArgs &args, int cus, hipStream_t stream);
 hipError_t launch_tile_ring(const GemmArgs &args, int cus, hipStream_t stream);
 // the same tiles on eight waves of 128x64, two per SIMD (chosen only when forced)

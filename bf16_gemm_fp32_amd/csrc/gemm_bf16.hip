@@ -21,7 +21,7 @@
 namespace gb {
 
 enum KernelKind {
-    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8Mfma32, kSplitK, kGemv, kSplitKQ8, kFp8Masked, kGemvFp8, kSkinnyFp8, kFp8SplitK, kRingQ8Masked, kSkinnyQ8, kMediumMasked, kSplitKMasked, kFp8SplitKMasked, kFp8, kFp8Mfma16Masked, kRingW8, kFp8Medium, kFp8MediumMasked, kFp8SplitKMedium, kFp8SplitKMediumMasked, kNumKinds
+    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8Mfma32, kSplitK, kGemv, kSplitKQ8, kFp8Masked, kGemvFp8, kSkinnyFp8, kFp8SplitK, kRingQ8Masked, kSkinnyQ8, kMediumMasked, kSplitKMasked, kFp8SplitKMasked, kFp8, kFp8Mfma16Masked, kRingW8, kFp8Medium, kFp8MediumMasked, kFp8SplitKMedium, kFp8SplitKMediumMasked, kSplitKQ8Masked, kNumKinds
 };
 
 static const char *const kKindNames[kNumKinds] = {"none",            "tile256x256x32_s5", "tile128x128x64_s4",
@@ -37,7 +37,7 @@ static const char *const kKindNames[kNumKinds] = {"none",            "tile256x25
                                                   "fp8_256x256x128", "fp8_256x256x128_mfma16_masked",
                                                   "ring256x256x64_w8", "fp8_128x128x128",
                                                   "fp8_128x128x128_masked", "splitk_fp8_128x128x128",
-                                                  "splitk_fp8_128x128x128_masked"};
+                                                  "splitk_fp8_128x128x128_masked", "splitk128x128x64_q8_masked"};
 
 static const char *kind_name(int k) { return (k >= 0 && k < kNumKinds) ? kKindNames[k] : "none"; }
 
@@ -513,7 +513,8 @@ static hipError_t launch_splitk_plan(const GemmArgs &args, int cus, const Scratc
     uint32_t *unused = nullptr;
     hipError_t err = get_scratch(scr, stream, &unused, &p.P);
     if (err != hipSuccess) return err;
-    if (q8) return launch_tile_medium_splitk_q8(args, p, cus, stream);
+    if (q8) return masked ? launch_tile_medium_splitk_q8_masked(args, p, cus, stream)
+                          : launch_tile_medium_splitk_q8(args, p, cus, stream);
     return masked ? launch_tile_medium_splitk_masked(args, p, cus, stream)
                   : launch_tile_medium_splitk(args, p, cus, stream);
 }
@@ -610,6 +611,7 @@ static int choose_kernel_q8(int64_t M, int64_t N, int64_t K, const void *A, int6
                                             !std::strcmp(force, kKindNames[kRingQ8]) ||
                                             !std::strcmp(force, kKindNames[kRingQ8Masked]));
         if (!forced_other && skinny_path_ok(M, N, K, A, lda, B, ldb, C, ldc)) return kSkinnyQ8;
+        if (force && !std::strcmp(force, kKindNames[kGeneric])) return kGeneric;
     }
     const void *c_probe = beta != 0.0f ? C : A;  // C is not read when beta == 0
     const int64_t ldc_probe = beta != 0.0f ? ldc : 8;
@@ -626,9 +628,12 @@ static int choose_kernel_q8(int64_t M, int64_t N, int64_t K, const void *A, int6
         if (force && !std::strcmp(force, kKindNames[kRingQ8Masked])) return kRingQ8Masked;
         const bool forced = force && !std::strcmp(force, kKindNames[kRingQ8]);
         if (tiles * 2 >= cus || forced) return exact ? kRingQ8 : kRingQ8Masked;
-        if (tile_path_ok<ShapeM>(M, N, K, A, lda, B, ldb, c_probe, ldc_probe) &&
-            plan_splitk(M, N, K, cus, cap_floats).splits >= 2)
-            return kSplitKQ8;
+        const bool can_split = plan_splitk(M, N, K, cus, cap_floats).splits >= 2;
+        if (tile_path_ok<ShapeM>(M, N, K, A, lda, B, ldb, c_probe, ldc_probe) && can_split) return kSplitKQ8;
+        // with tails: the masked split (1000 x 1000 x 4096 in 20.3 us against
+        // 66.0 us on the bounds-checked kernel, 504 x 504 x 8192 18.1 against
+        // 125.2 us, 1000 x 1000 x 1000 13.3 against 20.4 us)
+        if (medium_masked_ok(M, N, K, A, lda, B, ldb, c_probe, ldc_probe) && can_split) return kSplitKQ8Masked;
         // Grids too large to split on 128x128 tiles and too small to fill
         // half of the compute units with ring tiles: from more than an
         // eighth of the compute units in ring tiles the ring, with idle
@@ -883,6 +888,7 @@ int gemm_bf16_q8(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t 
     case kRingQ8Masked: err = launch_tile_ring_q8_masked(args, cus, stream); break;
     case kSkinnyQ8: err = launch_skinny_plan(args, cus, scr, stream, false, true); break;
     case kSplitKQ8: err = launch_splitk_plan(args, cus, scr, stream, true); break;
+    case kSplitKQ8Masked: err = launch_splitk_plan(args, cus, scr, stream, true, true); break;
     default: err = launch_generic(args, cus, stream); break;
     }
     if (err != hipSuccess) {

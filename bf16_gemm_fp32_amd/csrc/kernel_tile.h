@@ -588,8 +588,8 @@ gemm_tile_kernel(const GemmArgs args, const TileSchedule sched, const TileSplit 
 // the activation in fp32 and writes one 16-byte run of bf16 C -- or, with
 // kQ8, quantizes the 8 values with their rows' scales and writes 8 bytes of
 // int8 Q.  Requires M % 8 == 0, C 16-byte aligned and ldc % 8 == 0 (when C
-// is read or written), and for kQ8 Q and scale 16-byte aligned and
-// ldq % 8 == 0 (checked on the host).
+// is read or written), and for kQ8 the scale 16-byte aligned (checked on
+// the host) -- except that masked splits handle any M, C, ldc, Q and ldq.
 //
 // Which thread takes which chunk.  Without tile_major, chunk idx of the
 // column-major chunk order (grid-stride).  With tile_major (kTileM x kTileN
@@ -687,17 +687,33 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs args,
             for (int e = 0; e < 8; ++e) x[e] = x[e] * sb;
         }
         if constexpr (kQ8) {
-            // the quantizing reduction runs on exact tile multiples only
-            const f32x4 s_lo = *(const f32x4 *)(args.scale + m);
-            const f32x4 s_hi = *(const f32x4 *)(args.scale + m + 4);
-            const float sc[8] = {s_lo.x, s_lo.y, s_lo.z, s_lo.w, s_hi.x, s_hi.y, s_hi.z, s_hi.w};
+            // A chunk that straddles M (masked splits only) loads its rows'
+            // scales one by one, 0 past M, and stores its bytes one by one,
+            // as does every chunk when ldq % 8 != 0 or Q is not 8-byte
+            // aligned; whole chunks load their 8 scales as two 16-byte loads.
+            float sc[8];
+            if (m + 8 <= args.M) {
+                const f32x4 s_lo = *(const f32x4 *)(args.scale + m);
+                const f32x4 s_hi = *(const f32x4 *)(args.scale + m + 4);
+                sc[0] = s_lo.x; sc[1] = s_lo.y; sc[2] = s_lo.z; sc[3] = s_lo.w;
+                sc[4] = s_hi.x; sc[5] = s_hi.y; sc[6] = s_hi.z; sc[7] = s_hi.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sc[e] = m + e < args.M ? args.scale[m + e] : 0.f;
+            }
             u32x2 qw = {0u, 0u};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float v = epilogue_value<kFlags>(x[e], cin[e], bias_v, args.alpha, args.beta);
                 qw[e >> 2] |= ((uint32_t)quantize_i8(v, sc[e], args.zp) & 0xFFu) << ((e & 3) * 8);
             }
-            __builtin_nontemporal_store(qw, (u32x2 *)(args.Q + n * args.ldq + m));
+            int8_t *q = args.Q + n * args.ldq + m;
+            if (m + 8 <= args.M && (args.ldq & 7) == 0 && (reinterpret_cast<uintptr_t>(args.Q) & 7) == 0) {
+                __builtin_nontemporal_store(qw, (u32x2 *)q);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) if (m + e < args.M) q[e] = (int8_t)(qw[e >> 2] >> ((e & 3) * 8));
+            }
         } else {
             u32x4 out;
 #pragma unroll
@@ -743,7 +759,6 @@ hipError_t launch_tile(const GemmArgs &args, int cus, hipStream_t stream) {
 // rounded up to BN; exact shapes: M and M * N).
 template <class Cfg, bool kQ8 = false, bool kMasked = false>
 hipError_t launch_tile_splitk(const GemmArgs &args, const TileSplit &split, int cus, hipStream_t stream) {
-    static_assert(!(kQ8 && kMasked), "the quantizing reduction runs on exact tile multiples");
     TileSchedule s{};
     s.tiles_m = (int)((args.M + Cfg::BM - 1) / Cfg::BM);
     s.tiles_n = (int)((args.N + Cfg::BN - 1) / Cfg::BN);

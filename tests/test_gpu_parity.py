@@ -673,6 +673,21 @@ def test_q8_mid_sized_grids(M, N, K, ldq, kernel):
              seed=M + N + K, expect_kernel=kernel)
 
 
+SQ8M = "splitk128x128x64_q8_masked"
+
+
+# Small grids with tails: split-K on the masked 128x128 tiles, the reduction
+# quantizing 8-row chunks (element by element where a chunk straddles M).
+@pytest.mark.parametrize("M,N,K,ldq,beta,use_bias,epi,zp", [
+    (1000, 1000, 4096, 1000, 0.5, True, "relu", -7),      # 64 tiles, 3 ranges
+    (1001, 777, 2048, 1008, 0.0, True, "gelu_tanh", 3),    # M % 8 == 1: the last chunk straddles M
+    (1000, 1000, 1000, 1000, -0.75, False, "none", 0),     # 16 slices in 2 ranges
+])
+def test_q8_masked_splitk(M, N, K, ldq, beta, use_bias, epi, zp):
+    check_q8(f"q8 masked splitk {M}x{N}x{K}", M, N, K, ldq=ldq, ldc=ldq, alpha=1.25, beta=beta,
+             use_bias=use_bias, epilogue=epi, zp=zp, seed=M + N + K, expect_kernel=SQ8M)
+
+
 @pytest.mark.parametrize("M,N,K,ldq", [
     (1001, 777, 200, 1008), (257, 513, 8, 264), (1, 255, 64, 8), (300, 260, 72, 304), (512, 512, 256, 512),
 ])
