@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libgemm_bf16.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["gemm_bf16.hip", "tile_large.hip", "tile_medium.hip", "tile_medium_masked.hip", "tile_ring.hip", "tile_ring_w8.hip", "tile_ring_masked.hip", "tile_ring_q8.hip", "tile_ring_q8_exact.hip", "tile_fp8.hip", "tile_fp8_masked.hip", "tile_fp8_medium.hip", "tile_fp8_ring16.hip", "tile_ring_mfma32.hip", "tile_skinny.hip", "tile_skinny_fp8.hip", "tile_skinny_q8.hip", "tile_gemv.hip"]
+SOURCES = ["gemm_bf16.hip", "tile_large.hip", "tile_medium.hip", "tile_medium_masked.hip", "tile_ring.hip", "tile_ring_w8.hip", "tile_ring_masked.hip", "tile_ring_q8.hip", "tile_ring_q8_exact.hip", "tile_fp8.hip", "tile_fp8_masked.hip", "tile_fp8_medium.hip", "tile_fp8_ring16.hip", "tile_ring_mfma32.hip", "tile_skinny.hip", "tile_skinny_t.hip", "tile_skinny_fp8.hip", "tile_skinny_q8.hip", "tile_gemv.hip"]
 
 # Packed-fp32 VALU forms are disabled: the kernels write plain float code.
 HIP_FLAGS = [

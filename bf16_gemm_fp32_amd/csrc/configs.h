@@ -81,6 +81,10 @@ hipError_t launch_gemv(const GemmArgs &args, hipStream_t stream, bool fp8 = fals
 // rows: 32 or 64 (the kernel's row block, M <= rows); cols: strip width
 hipError_t launch_skinny(int rows, int cols, const GemmArgs &args, const SkinnyWork &work, int cus,
                          hipStream_t stream);
+// the same on a transposed product (args already transposed: M' = N <= 64),
+// writing C' transposed into C
+hipError_t launch_skinny_t(int rows, int cols, const GemmArgs &args, const SkinnyWork &work, int cus,
+                           hipStream_t stream);
 // int8 output (per-row scale, zero point), 32-column strips
 hipError_t launch_skinny_q8(int rows, const GemmArgs &args, const SkinnyWork &work, int cus, hipStream_t stream);
 // FP8 (E4M3) operands, 32-column strips with slices of KS_FP8 values

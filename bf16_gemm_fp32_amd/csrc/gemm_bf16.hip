@@ -21,7 +21,7 @@
 namespace gb {
 
 enum KernelKind {
-    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8Mfma32, kSplitK, kGemv, kSplitKQ8, kFp8Masked, kGemvFp8, kSkinnyFp8, kFp8SplitK, kRingQ8Masked, kSkinnyQ8, kMediumMasked, kSplitKMasked, kFp8SplitKMasked, kFp8, kFp8Mfma16Masked, kRingW8, kFp8Medium, kFp8MediumMasked, kFp8SplitKMedium, kFp8SplitKMediumMasked, kSplitKQ8Masked, kNumKinds
+    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8Mfma32, kSplitK, kGemv, kSplitKQ8, kFp8Masked, kGemvFp8, kSkinnyFp8, kFp8SplitK, kRingQ8Masked, kSkinnyQ8, kMediumMasked, kSplitKMasked, kFp8SplitKMasked, kFp8, kFp8Mfma16Masked, kRingW8, kFp8Medium, kFp8MediumMasked, kFp8SplitKMedium, kFp8SplitKMediumMasked, kSplitKQ8Masked, kSkinnyT, kNumKinds
 };
 
 static const char *const kKindNames[kNumKinds] = {"none",            "tile256x256x32_s5", "tile128x128x64_s4",
@@ -37,7 +37,8 @@ static const char *const kKindNames[kNumKinds] = {"none",            "tile256x25
                                                   "fp8_256x256x128", "fp8_256x256x128_mfma16_masked",
                                                   "ring256x256x64_w8", "fp8_128x128x128",
                                                   "fp8_128x128x128_masked", "splitk_fp8_128x128x128",
-                                                  "splitk_fp8_128x128x128_masked", "splitk128x128x64_q8_masked"};
+                                                  "splitk_fp8_128x128x128_masked", "splitk128x128x64_q8_masked",
+                                                  "skinny_t"};
 
 static const char *kind_name(int k) { return (k >= 0 && k < kNumKinds) ? kKindNames[k] : "none"; }
 
@@ -342,7 +343,7 @@ static hipError_t get_scratch(const Scratch &src, hipStream_t stream, uint32_t *
 }
 
 static hipError_t launch_skinny_plan(const GemmArgs &args, int cus, const Scratch &scr, hipStream_t stream,
-                                     bool fp8 = false, bool q8 = false) {
+                                     bool fp8 = false, bool q8 = false, bool trans = false) {
     const SkinnyPlan p = plan_skinny(args.M, args.N, args.K, cus, scr.cap_floats, fp8, q8);
     SkinnyWork work{};
     work.num_strips = p.strips;
@@ -357,13 +358,11 @@ static hipError_t launch_skinny_plan(const GemmArgs &args, int cus, const Scratc
         hipError_t err = get_scratch(scr, stream, &work.counters, &work.partials);
         if (err != hipSuccess) return err;
         work.records = reinterpret_cast<HandoffRecord *>(work.counters);
-        if (q8) return launch_skinny_q8(p.rows, args, work, cus, stream);
-        return fp8 ? launch_skinny_fp8(p.rows, args, work, cus, stream)
-                   : launch_skinny(p.rows, p.cols, args, work, cus, stream);
     }
     if (q8) return launch_skinny_q8(p.rows, args, work, cus, stream);
-    return fp8 ? launch_skinny_fp8(p.rows, args, work, cus, stream)
-               : launch_skinny(p.rows, p.cols, args, work, cus, stream);
+    if (fp8) return launch_skinny_fp8(p.rows, args, work, cus, stream);
+    return trans ? launch_skinny_t(p.rows, p.cols, args, work, cus, stream)
+                 : launch_skinny(p.rows, p.cols, args, work, cus, stream);
 }
 
 // Split-K on the 128x128 tiles: used when those tiles alone would leave more
@@ -530,6 +529,8 @@ static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t
     const bool okR = tile_path_ok<ShapeRing>(M, N, K, A, lda, B, ldb, C, ldc);
     const bool okRM = ring_masked_ok(M, N, K, A, lda, B, ldb, C, ldc);
     const bool okS = skinny_path_ok(M, N, K, A, lda, B, ldb, C, ldc);
+    // the transposed product (N' = M, M' = N <= 64, A' = B^T, B' = A^T)
+    const bool okST = skinny_path_ok(N, M, K, B, ldb, A, lda, C, ldc);
     const bool okV = gemv_path_ok(M, N, K, A, lda, B, ldb);
     const bool okMM = medium_masked_ok(M, N, K, A, lda, B, ldb, C, ldc);
     if (const char *force = std::getenv("GEMM_BF16_FORCE_KERNEL")) {
@@ -546,6 +547,7 @@ static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t
         if (!std::strcmp(force, kKindNames[kRingW8]) && okR) return kRingW8;
         if (!std::strcmp(force, kKindNames[kRingMasked]) && okRM) return kRingMasked;
         if (!std::strcmp(force, kKindNames[kSkinny]) && okS) return kSkinny;
+        if (!std::strcmp(force, kKindNames[kSkinnyT]) && okST) return kSkinnyT;
         if (!std::strcmp(force, kKindNames[kGemv]) && okV) return kGemv;
     }
     // One to four rows: the matrix-vector kernel.  Each of its waves reads
@@ -554,9 +556,17 @@ static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t
     // 32-column strip, is faster (8192 x 8192: 25.0 us against 27.8 us at
     // three rows and 29.2 us at four).
     if (okV && (M <= 2 || N * K < ((int64_t)1 << 26) || !okS)) return kGemv;
-    // At most 64 rows: the streaming kernel (a 256- or 128-row tile would be
-    // mostly empty).
-    if (okS) return kSkinny;
+    // At most 64 rows: the streaming kernel (a 256-row tile would be mostly
+    // empty) -- except where its 32-column strips outnumber the compute
+    // units over a short K (fewer than 8 slices of 256): each unit then
+    // fills and drains its rings, and the masked 128x128 tiles, which
+    // overlap one another's loads, are faster (64 x 65536 x 512: 19.1 us
+    // against 29.7 us; 28.6 us on the 256x256 ring).
+    if (okS) return ((N + 31) / 32 <= cus || K >= 2048 || !okMM) ? kSkinny : kMediumMasked;
+    // At most 64 columns: the streaming kernel on the transposed product,
+    // writing C transposed (A, row-major, is then the streamed operand),
+    // with the same exception over M's strips.
+    if (okST) return ((M + 31) / 32 <= cus || K >= 2048 || !okMM) ? kSkinnyT : kMediumMasked;
     // 256x256 tiles when they give at least half the compute units a tile:
     // exact multiples take the unmasked ring kernel, shapes with tails the
     // masked one.
@@ -811,6 +821,20 @@ static int run_bf16(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64
     case kRingW8: err = launch_tile_ring_w8(args, cus, stream); break;
     case kRingMasked: err = launch_tile_ring_masked(args, cus, stream); break;
     case kSkinny: err = launch_skinny_plan(args, cus, scr, stream); break;
+    case kSkinnyT: {
+        // C' = C^T: M' = N, N' = M, A' = B^T (row-major, lda' = ldb),
+        // B' = A^T (column-major, ldb' = lda); the kernel writes C' back
+        // transposed and takes the bias of C's columns per row of C'
+        GemmArgs t = args;
+        t.M = args.N;
+        t.N = args.M;
+        t.A = args.B;
+        t.lda = args.ldb;
+        t.B = args.A;
+        t.ldb = args.lda;
+        err = launch_skinny_plan(t, cus, scr, stream, false, false, true);
+        break;
+    }
     default: err = launch_generic(args, cus, stream); break;
     }
     if (err != hipSuccess) {

@@ -125,10 +125,16 @@ struct SkinnyWork {
 // kQ8: the int8 output of the quantizing entry point -- the epilogue value
 // of row m becomes sat8(rne(fma(v, scale[m], zp))) in Q (C is then only
 // read, when beta != 0).
-template <class Cfg, uint32_t kFlags, bool kFp8 = false, bool kQ8 = false>
+// kTrans: the kernel computes the transposed product C' = A' B' of a
+// product with at most 64 columns (the host passes A' = B^T, B' = A^T,
+// M' = N, N' = M, and the bias of C's columns as bias[m']) and writes C'
+// transposed: element (m', n') of C' goes to C[n' + m' * ldc], so each
+// output chunk is 8 consecutive n' of one row m', contiguous in C.
+template <class Cfg, uint32_t kFlags, bool kFp8 = false, bool kQ8 = false, bool kTrans = false>
 __global__ void __launch_bounds__(Cfg::kThreads)
 gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
     static_assert(!(kFp8 && kQ8), "int8 output is built for bf16 inputs");
+    static_assert(!(kTrans && (kFp8 || kQ8)), "the transposed output is built for bf16");
     __shared__ __attribute__((aligned(1024))) char smem[Cfg::kLdsBytes];
     char *const ringA = smem;
     char *const ringB = smem + Cfg::SA * Cfg::kABytes;
@@ -334,12 +340,24 @@ gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
         lds_barrier();
         constexpr int kChunksPerCol = Cfg::BMr / 8;
         constexpr int kChunks = Cfg::BN * kChunksPerCol;  // 8-row pieces of the strip
+        constexpr int kChunksPerRow = Cfg::BN / 8;          // kTrans: 8-column pieces of a row
 
-        // The four waves' sum of one 8-row chunk (column idx / kChunksPerCol).
+        // The four waves' sum of one 8-row chunk (column idx / kChunksPerCol)
+        // -- with kTrans, of one 8-column chunk (row idx / kChunksPerRow).
         auto wave_sum = [&](int idx, float (&x)[8]) {
-            const int col = idx / kChunksPerCol, q = idx % kChunksPerCol;
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = 0.f;
+            if constexpr (kTrans) {
+                const int r = idx / kChunksPerRow, c8 = (idx % kChunksPerRow) * 8;
+#pragma unroll
+                for (int w = 0; w < Cfg::kWaves; ++w)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        x[e] += *(const GB_LDS float *)(smem + w * Cfg::kPartBytes + (c8 + e) * Cfg::kColBytes +
+                                                        r * 4);
+                return;
+            }
+            const int col = idx / kChunksPerCol, q = idx % kChunksPerCol;
 #pragma unroll
             for (int w = 0; w < Cfg::kWaves; ++w) {
                 const char *p = smem + w * Cfg::kPartBytes + col * Cfg::kColBytes + q * 32;
@@ -352,6 +370,45 @@ gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
         // The fused epilogue on one 8-row chunk of the strip's sum x: bf16 C
         // with a 16-byte store, element by element where the chunk straddles M.
         auto finish = [&](int idx, const float (&x)[8]) {
+            if constexpr (kTrans) {
+                // row m' of C', columns n0 + c8 .. + 7: C[n' + m' * ldc],
+                // the bias of C's column m'
+                const int r = idx / kChunksPerRow, c8 = (idx % kChunksPerRow) * 8;
+                const int64_t n = n0 + c8;
+                if (r >= args.M || n >= args.N) return;
+                uint16_t *cp = args.C + (int64_t)r * args.ldc + n;
+                const bool full = n + 8 <= args.N && work.c_vector;
+                float bias_v = 0.f;
+                if constexpr ((kFlags & kEpiBias) != 0) bias_v = bf16_bits_to_f32(args.bias[r]);
+                float cin[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                if constexpr ((kFlags & kEpiBeta) != 0) {
+                    if (full) {
+                        const u32x4 raw = *(const u32x4 *)cp;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            cin[2 * e] = bf16_bits_to_f32(raw[e] & 0xFFFFu);
+                            cin[2 * e + 1] = bf16_bits_to_f32(raw[e] >> 16);
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) if (n + e < args.N) cin[e] = bf16_bits_to_f32(cp[e]);
+                    }
+                }
+                u32x4 out;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    out[e] = pack_bf16x2(epilogue_value<kFlags>(x[2 * e], cin[2 * e], bias_v, args.alpha, args.beta),
+                                         epilogue_value<kFlags>(x[2 * e + 1], cin[2 * e + 1], bias_v, args.alpha,
+                                                                args.beta));
+                if (full) {
+                    __builtin_nontemporal_store(out, (u32x4 *)cp);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (n + e < args.N) cp[e] = (uint16_t)(out[e >> 1] >> ((e & 1) * 16));
+                }
+                return;
+            }
             const int col = idx / kChunksPerCol, q = idx % kChunksPerCol;
             const int64_t n = n0 + col;
             const int64_t m = (int64_t)q * 8;
@@ -543,20 +600,26 @@ gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
 }
 
 // One workgroup per compute unit (at most one per work unit).
-template <class Cfg, bool kFp8 = false, bool kQ8 = false>
+template <class Cfg, bool kFp8 = false, bool kQ8 = false, bool kTrans = false>
 hipError_t launch_skinny(const GemmArgs &args, const SkinnyWork &work, int cus, hipStream_t stream) {
     const int units = work.num_strips * work.splits;
     const dim3 grid(units < cus ? units : cus), block(Cfg::kThreads);
     dispatch_flags(args.flags, [&](auto f) {
-        hipLaunchKernelGGL((gemm_skinny_kernel<Cfg, decltype(f)::value, kFp8, kQ8>), grid, block, 0, stream, args,
-                           work);
+        hipLaunchKernelGGL((gemm_skinny_kernel<Cfg, decltype(f)::value, kFp8, kQ8, kTrans>), grid, block, 0, stream,
+                           args, work);
     });
     return hipGetLastError();
 }
 
-// The 32-column configurations the host plans with: rows of 64 (or 32),
-// K-slices of 256 in A/B rings of 3 and 4 (6 for 32 rows) slices.
+// The configurations the host plans with: 32-column strips of 64 (or 32)
+// rows, K-slices of 256 in A/B rings of 3 and 4 (6 for 32 rows) slices;
+// 64-column strips (split K within an XCD), K-slices of 256 in rings of 2/3
+// (2/4 for 32 rows); 128-column strips, K-slices of 128.
 using SkinnyM64N32 = SkinnyConfig<2, 1, 256, 3, 4>;
 using SkinnyM32N32 = SkinnyConfig<1, 1, 256, 3, 6>;
+using SkinnyM64N64 = SkinnyConfig<2, 2, 256, 2, 3>;
+using SkinnyM64N128 = SkinnyConfig<2, 4, 128, 2, 4>;
+using SkinnyM32N64 = SkinnyConfig<1, 2, 256, 2, 4>;
+using SkinnyM32N128 = SkinnyConfig<1, 4, 128, 2, 4>;
 
 }  // namespace gb

@@ -7,11 +7,6 @@
 
 namespace gb {
 
-using SkinnyM64N64 = SkinnyConfig<2, 2, 256, 2, 3>;
-using SkinnyM64N128 = SkinnyConfig<2, 4, 128, 2, 4>;
-using SkinnyM32N64 = SkinnyConfig<1, 2, 256, 2, 4>;
-using SkinnyM32N128 = SkinnyConfig<1, 4, 128, 2, 4>;
-
 static_assert(SkinnyM64N32::KS == ShapeSkinny::KS_N32 && SkinnyM64N64::KS == ShapeSkinny::KS_N64 &&
                   SkinnyM64N128::KS == ShapeSkinny::KS_N128 && SkinnyM32N32::KS == ShapeSkinny::KS_N32 &&
                   SkinnyM32N64::KS == ShapeSkinny::KS_N64 && SkinnyM32N128::KS == ShapeSkinny::KS_N128,

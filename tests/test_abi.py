@@ -258,6 +258,23 @@ def test_kernel_selection_names():
     assert name(1, 4096, 4100, P, 4100, P, 4100, P, 1) == "generic64x64x32"   # K % 8 != 0
     assert name(48, 4096, 1020, P, 1020, P, 1020, P, 48) == "generic64x64x32"
     assert name(65, 4096, 1024, P, 1024, P, 1024, P, 72) != "skinny"
+    # at most 64 columns: the streaming kernel on the transposed product
+    assert name(8192, 64, 8192, P, 8192, P, 8192, P, 8192) == "skinny_t"
+    assert name(8192, 1, 8192, P, 8192, P, 8192, P, 8192) == "skinny_t"
+    assert name(1000, 17, 3000, P, 3000, P, 3000, P, 1001) == "skinny_t"
+    assert name(64, 64, 4096, P, 4096, P, 4096, P, 64) == "skinny"       # both small: the direct kernel
+    assert name(8192, 65, 8192, P, 8192, P, 8192, P, 8192) != "skinny_t"
+    assert name(8192, 48, 1020, P, 1020, P, 1020, P, 8192) == "generic64x64x32"   # K % 8 != 0
+    assert name(8192, 48, 1024, P + 2, 1024, P, 1024, P, 8192) != "skinny_t"     # A not 16-byte aligned
+    # more 32-wide strips than compute units over fewer than 8 slices of 256:
+    # the masked 128x128 tiles
+    assert name(64, 65536, 512, P, 512, P, 512, P, 64) == "tile128x128x64_s4_masked"
+    assert name(65536, 64, 1024, P, 1024, P, 1024, P, 65536) == "tile128x128x64_s4_masked"
+    assert name(65536, 1, 512, P, 512, P, 512, P, 65536) == "tile128x128x64_s4_masked"
+    assert name(65536, 64, 2048, P, 2048, P, 2048, P, 65536) == "skinny_t"
+    assert name(64, 65536, 2048, P, 2048, P, 2048, P, 64) == "skinny"
+    assert name(64, 8192, 256, P, 256, P, 256, P, 64) == "skinny"       # one strip per compute unit
+    assert name(8192, 64, 256, P, 256, P, 256, P, 8192) == "skinny_t"
     assert name(4096, 4096, 4096, P + 2, 4096, P, 4096, P, 4096) == "generic64x64x32"
     assert name(4096, 4096, 4100, P, 4100, P, 4100, P, 4096) == "generic64x64x32"
     assert name(4096, 4096, 0, P, 1, P, 1, P, 4096) == "generic64x64x32"
@@ -270,6 +287,8 @@ def test_kernel_selection_names():
     assert name(4096, 4096, 4096, P, 2 * big, P, 4096, P, 4096) == "generic64x64x32"
     assert name(64, 8192, 8192, P, big * 2, P, 8192, P, 64) == "skinny"      # 64 rows: 2^30 bytes
     assert name(64, 8192, 8192, P, big * 4, P, 8192, P, 64) == "generic64x64x32"
+    assert name(8192, 64, 8192, P, 8192, P, big * 2, P, 8192) == "skinny_t"  # 64 columns of B: 2^30 bytes
+    assert name(8192, 64, 8192, P, 8192, P, big * 4, P, 8192) != "skinny_t"
     assert name(1, 4096, 4096, P, 4096, P, big * 32, P, 1) == "gemv"          # 4 columns: 2^30 bytes
     assert name(1, 4096, 4096, P, 4096, P, big * 64, P, 1) == "generic64x64x32"
     assert name(-1, 4096, 4096, P, 4096, P, 4096, P, 1) == "none"

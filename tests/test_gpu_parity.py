@@ -511,6 +511,88 @@ def test_skinny_colocated_split_fp8(M, N, K):
               seed=M + K, expect_kernel=SKF)
 
 
+# At most 64 columns (and more than 64 rows): the streaming kernel runs on
+# the transposed product C^T = B^T A^T, whose rows are C's columns, and
+# writes each 8-wide chunk of a row of C^T as 8 consecutive rows of one
+# column of C.  The bias belongs to C's columns, i.e. to the rows of C^T.
+SKT = "skinny_t"
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc", [
+    (8192, 64, 1024, 1024, 1024, 8192),  # 64 columns: 256 strips of 32 rows of C
+    (4096, 1, 2048, 2048, 2048, 4096),   # a single column
+    (1000, 17, 3000, 3000, 3000, 1001),  # M tail inside a chunk, odd ldc: element-wise stores
+    (777, 33, 1032, 1040, 1032, 784),    # 33 columns: the 64-row block; padded A
+    (130, 5, 520, 528, 536, 131),        # a few strips, padded A and B
+    (65, 64, 1024, 1024, 1024, 72),      # one row past the streaming kernel's own limit
+    (2048, 32, 16384, 16384, 16384, 2048),  # long K: split within an XCD
+])
+def test_skinny_transposed_shapes(M, N, K, lda, ldb, ldc):
+    check_full(f"skinny_t {M}x{N}x{K}", M, N, K, lda=lda, ldb=ldb, ldc=ldc, beta=0.0, seed=M + 3 * N + K,
+               expect_kernel=SKT, poison_pad=True)
+
+
+@pytest.mark.parametrize("beta,use_bias,epi", [(0.5, True, "gelu_tanh"), (0.0, True, "none"),
+                                               (-1.0, False, "gelu_tanh"), (0.25, True, "relu")])
+@pytest.mark.parametrize("splits", ["1", "4"])
+def test_skinny_transposed_epilogues(beta, use_bias, epi, splits, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_SKINNY_SPLITS", splits)
+    check_full(f"skinny_t epilogue beta={beta} bias={use_bias} {epi}", 3000, 48, 2048, ldc=3000, alpha=0.5,
+               beta=beta, use_bias=use_bias, epilogue=epi, seed=43, expect_kernel=SKT)
+    check_full("skinny_t unaligned C", 999, 40, 1024, ldc=1003, alpha=1.5, beta=beta, use_bias=use_bias,
+               epilogue=epi, offsets=(0, 0, 3), seed=44, expect_kernel=SKT)
+
+
+@pytest.mark.parametrize("cols", ["32", "64", "128"])
+@pytest.mark.parametrize("splits", ["1", "3", "7"])
+def test_skinny_transposed_widths_and_splits(cols, splits, monkeypatch):
+    monkeypatch.setenv("GEMM_BF16_SKINNY_COLS", cols)
+    monkeypatch.setenv("GEMM_BF16_SKINNY_SPLITS", splits)
+    check_full(f"skinny_t cols={cols} splits={splits}", 1024, 64, 4096, beta=0.5, use_bias=True,
+               epilogue="gelu_tanh", seed=5 * int(cols) + int(splits), expect_kernel=SKT)
+    check_full(f"skinny_t N=20 cols={cols} splits={splits}", 520, 20, 2048, ldc=528,
+               seed=7 * int(cols) + int(splits), expect_kernel=SKT)
+
+
+@pytest.mark.parametrize("M,N,K,cols", [(2048, 64, 8192, "32"), (4096, 64, 8192, "64"), (1000, 40, 4096, "32")])
+def test_skinny_transposed_equals_the_direct_kernel_on_swapped_operands(M, N, K, cols, monkeypatch):
+    """C^T = B^T A^T: the direct streaming kernel on the swapped operands
+    (N x M x K, A' = B read row-major, B' = A read column-major) computes
+    the same sums in the same order, so without bias the two outputs are
+    bit-identical transposes (colocated split, fenced handoff and crossing
+    split alike); both also match the oracle."""
+    monkeypatch.setenv("GEMM_BF16_SKINNY_COLS", cols)
+    case = inputs.random_case(M + N + K, M, N, K, with_c0=True)
+    assert gb.gemm_bf16_kernel_name(M, N, K, 4096, K, 4096, K, 4096, M) == SKT
+    assert gb.gemm_bf16_kernel_name(N, M, K, 4096, K, 4096, K, 4096, N) == SK
+    say(f"[skinny_t] {M}x{N}x{K} cols={cols} vs direct {N}x{M}x{K}")
+    trans = [run_gpu(M, N, K, case["A"], K, case["B"], K, case["C0"], M, 1.25, -0.5, None, "relu")
+             for _ in range(2)]
+    assert np.array_equal(trans[0], trans[1]), "transposed skinny varies between calls"
+    C0_t = np.ascontiguousarray(case["C0"].reshape(N, M).T).reshape(-1)
+    direct = run_gpu(N, M, K, case["B"], K, case["A"], K, C0_t, N, 1.25, -0.5, None, "relu")
+    assert np.array_equal(trans[0].reshape(N, M), direct.reshape(M, N).T), "transposed != direct kernel"
+    for mode in ("fence", "0"):
+        monkeypatch.setenv("GEMM_BF16_SKINNY_COLOCATE", mode)
+        other = run_gpu(M, N, K, case["A"], K, case["B"], K, case["C0"], M, 1.25, -0.5, None, "relu")
+        if mode == "fence":
+            assert np.array_equal(trans[0], other), "the fenced handoff differs from the L2 handoff"
+        ref = oracle.gemm(M, N, K, case["A"], K, case["B"], K, case["C0"], M, 1.25, -0.5, None, "relu",
+                          nthreads=_threads())
+        assert_within_tolerance(other, ref, K, f"skinny_t colocate={mode} vs oracle")
+    ref = oracle.gemm(M, N, K, case["A"], K, case["B"], K, case["C0"], M, 1.25, -0.5, None, "relu",
+                      nthreads=_threads())
+    assert_within_tolerance(trans[0], ref, K, "skinny_t vs oracle")
+
+
+@pytest.mark.parametrize("M,N,K,ldc", [(40, 10000, 512, 41), (9000, 24, 1024, 9000)])
+def test_many_strips_over_a_short_k_take_the_masked_tiles(M, N, K, ldc):
+    """More 32-wide strips than compute units over a short K: the masked
+    128x128 tiles, their rows (or columns) mostly past the matrix."""
+    check_full(f"many strips short K {M}x{N}x{K}", M, N, K, ldc=ldc, beta=0.5, use_bias=True,
+               epilogue="gelu_tanh", seed=M + N + K, expect_kernel="tile128x128x64_s4_masked")
+
+
 # ---------------------------------------------------- bounds-checked path ---
 
 @pytest.mark.parametrize("M,N,K", [
