@@ -89,5 +89,10 @@ hipError_t launch_skinny_t(int rows, int cols, const GemmArgs &args, const Skinn
 hipError_t launch_skinny_q8(int rows, const GemmArgs &args, const SkinnyWork &work, int cus, hipStream_t stream);
 // FP8 (E4M3) operands, 32-column strips with slices of KS_FP8 values
 hipError_t launch_skinny_fp8(int rows, const GemmArgs &args, const SkinnyWork &work, int cus, hipStream_t stream);
+// the int8-output and FP8 instances on a transposed product (args already
+// transposed, FP8 scales swapped), writing C' (and Q') transposed
+hipError_t launch_skinny_q8_t(int rows, const GemmArgs &args, const SkinnyWork &work, int cus, hipStream_t stream);
+hipError_t launch_skinny_fp8_t(int rows, const GemmArgs &args, const SkinnyWork &work, int cus,
+                               hipStream_t stream);
 
 }  // namespace gb

@@ -21,7 +21,7 @@
 namespace gb {
 
 enum KernelKind {
-    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8Mfma32, kSplitK, kGemv, kSplitKQ8, kFp8Masked, kGemvFp8, kSkinnyFp8, kFp8SplitK, kRingQ8Masked, kSkinnyQ8, kMediumMasked, kSplitKMasked, kFp8SplitKMasked, kFp8, kFp8Mfma16Masked, kRingW8, kFp8Medium, kFp8MediumMasked, kFp8SplitKMedium, kFp8SplitKMediumMasked, kSplitKQ8Masked, kSkinnyT, kNumKinds
+    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8Mfma32, kSplitK, kGemv, kSplitKQ8, kFp8Masked, kGemvFp8, kSkinnyFp8, kFp8SplitK, kRingQ8Masked, kSkinnyQ8, kMediumMasked, kSplitKMasked, kFp8SplitKMasked, kFp8, kFp8Mfma16Masked, kRingW8, kFp8Medium, kFp8MediumMasked, kFp8SplitKMedium, kFp8SplitKMediumMasked, kSplitKQ8Masked, kSkinnyT, kSkinnyQ8T, kSkinnyFp8T, kNumKinds
 };
 
 static const char *const kKindNames[kNumKinds] = {"none",            "tile256x256x32_s5", "tile128x128x64_s4",
@@ -38,7 +38,7 @@ static const char *const kKindNames[kNumKinds] = {"none",            "tile256x25
                                                   "ring256x256x64_w8", "fp8_128x128x128",
                                                   "fp8_128x128x128_masked", "splitk_fp8_128x128x128",
                                                   "splitk_fp8_128x128x128_masked", "splitk128x128x64_q8_masked",
-                                                  "skinny_t"};
+                                                  "skinny_t", "skinny_q8_t", "skinny_fp8_t"};
 
 static const char *kind_name(int k) { return (k >= 0 && k < kNumKinds) ? kKindNames[k] : "none"; }
 
@@ -342,6 +342,24 @@ static hipError_t get_scratch(const Scratch &src, hipStream_t stream, uint32_t *
     return hipSuccess;
 }
 
+// The transposed product C' = C^T for the streaming kernel's transposed
+// output: M' = N, N' = M, A' = B^T (row-major, lda' = ldb), B' = A^T
+// (column-major, ldb' = lda), the FP8 scales swapped (scale_a' indexes the
+// rows of C', i.e. C's columns).  C, Q, bias and the int8 scales keep C's
+// indexing; the kernel writes C' (and Q') back transposed.
+static GemmArgs transposed(const GemmArgs &args) {
+    GemmArgs t = args;
+    t.M = args.N;
+    t.N = args.M;
+    t.A = args.B;
+    t.lda = args.ldb;
+    t.B = args.A;
+    t.ldb = args.lda;
+    t.scale_a = args.scale_b;
+    t.scale_b = args.scale_a;
+    return t;
+}
+
 static hipError_t launch_skinny_plan(const GemmArgs &args, int cus, const Scratch &scr, hipStream_t stream,
                                      bool fp8 = false, bool q8 = false, bool trans = false) {
     const SkinnyPlan p = plan_skinny(args.M, args.N, args.K, cus, scr.cap_floats, fp8, q8);
@@ -359,8 +377,12 @@ static hipError_t launch_skinny_plan(const GemmArgs &args, int cus, const Scratc
         if (err != hipSuccess) return err;
         work.records = reinterpret_cast<HandoffRecord *>(work.counters);
     }
-    if (q8) return launch_skinny_q8(p.rows, args, work, cus, stream);
-    if (fp8) return launch_skinny_fp8(p.rows, args, work, cus, stream);
+    if (q8)
+        return trans ? launch_skinny_q8_t(p.rows, args, work, cus, stream)
+                     : launch_skinny_q8(p.rows, args, work, cus, stream);
+    if (fp8)
+        return trans ? launch_skinny_fp8_t(p.rows, args, work, cus, stream)
+                     : launch_skinny_fp8(p.rows, args, work, cus, stream);
     return trans ? launch_skinny_t(p.rows, p.cols, args, work, cus, stream)
                  : launch_skinny(p.rows, p.cols, args, work, cus, stream);
 }
@@ -555,14 +577,21 @@ static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t
     // large B (N * K >= 2^26) the streaming kernel, which shares A across a
     // 32-column strip, is faster (8192 x 8192: 25.0 us against 27.8 us at
     // three rows and 29.2 us at four).
-    if (okV && (M <= 2 || N * K < ((int64_t)1 << 26) || !okS)) return kGemv;
+    // Where the streaming kernel's 32-column strips outnumber the compute
+    // units, each unit fills and drains its rings: then the matrix-vector
+    // kernel keeps three and four rows unless K is long (3 x 65536 x 2048:
+    // 45.9 us against 57.2 us streaming, 4 x 32768 x 4096 49.0 against
+    // 51.1 us; 4 x 16384 x 8192 52.3 against 47.8 us).
+    const bool many_strips = (N + 31) / 32 > cus;
+    if (okV && (M <= 2 || N * K < ((int64_t)1 << 26) || !okS || (many_strips && K >= 2048 && K < 8192)))
+        return kGemv;
     // At most 64 rows: the streaming kernel (a 256-row tile would be mostly
-    // empty) -- except where its 32-column strips outnumber the compute
-    // units over a short K (fewer than 8 slices of 256): each unit then
-    // fills and drains its rings, and the masked 128x128 tiles, which
+    // empty) -- except with more strips than compute units over a short K
+    // (fewer than 8 slices of 256), where the masked 128x128 tiles, which
     // overlap one another's loads, are faster (64 x 65536 x 512: 19.1 us
-    // against 29.7 us; 28.6 us on the 256x256 ring).
-    if (okS) return ((N + 31) / 32 <= cus || K >= 2048 || !okMM) ? kSkinny : kMediumMasked;
+    // against 29.7 us, 28.6 us on the 256x256 ring; 4 x 65536 x 1024 30.8
+    // against 39.2 us, 35.1 us on the matrix-vector kernel).
+    if (okS) return (!many_strips || K >= 2048 || !okMM) ? kSkinny : kMediumMasked;
     // At most 64 columns: the streaming kernel on the transposed product,
     // writing C transposed (A, row-major, is then the streamed operand),
     // with the same exception over M's strips.
@@ -622,6 +651,12 @@ static int choose_kernel_q8(int64_t M, int64_t N, int64_t K, const void *A, int6
                                             !std::strcmp(force, kKindNames[kRingQ8Masked]));
         if (!forced_other && skinny_path_ok(M, N, K, A, lda, B, ldb, C, ldc)) return kSkinnyQ8;
         if (force && !std::strcmp(force, kKindNames[kGeneric])) return kGeneric;
+        // At most 64 columns: the same on the transposed product (Q and C
+        // transposed back), except, as for bf16, where its strips outnumber
+        // the compute units over fewer than 8 slices of 256.
+        const bool okST = skinny_path_ok(N, M, K, B, ldb, A, lda, C, ldc);
+        if (force && !std::strcmp(force, kKindNames[kSkinnyQ8T]) && okST) return kSkinnyQ8T;
+        if (!forced_other && okST && ((M + 31) / 32 <= cus || K >= 2048)) return kSkinnyQ8T;
     }
     const void *c_probe = beta != 0.0f ? C : A;  // C is not read when beta == 0
     const int64_t ldc_probe = beta != 0.0f ? ldc : 8;
@@ -693,15 +728,31 @@ static int choose_kernel_fp8(int64_t M, int64_t N, int64_t K, const void *A, int
                      aligned16(B) && 64 * lda + K + ShapeSkinny::KS_FP8 < lim &&
                      128 * ldb + K + ShapeSkinny::KS_FP8 < lim && N / 32 + 1 < lim / 64;
     if (force && !std::strcmp(force, kKindNames[kSkinnyFp8]) && okS) return kSkinnyFp8;
+    // Up to 64 columns (more than 64 rows): the same on the transposed
+    // product, B's columns as its rows.
+    const bool okST = M > 64 && N <= 64 && K > 0 && K % 16 == 0 && lda % 16 == 0 && ldb % 16 == 0 &&
+                      aligned16(A) && aligned16(B) && 64 * ldb + K + ShapeSkinny::KS_FP8 < lim &&
+                      128 * lda + K + ShapeSkinny::KS_FP8 < lim && M / 32 + 1 < lim / 64;
+    if (force && !std::strcmp(force, kKindNames[kSkinnyFp8T]) && okST) return kSkinnyFp8T;
     // As for bf16: at three and four rows on a large B the streaming kernel,
     // sharing A across a strip, is faster (8192 x 8192: 15.9 us against
     // 18.7 us at three rows, 15.8 against 19.3 at four).
     if (okV && (M <= 2 || N * K < ((int64_t)1 << 26) || !okS)) return kGemvFp8;
-    if (okS) return kSkinnyFp8;
     bool ok = K > 0 && K % 16 == 0;
     ok = ok && lda % 16 == 0 && ldb % 16 == 0 && aligned16(A) && aligned16(B);
     ok = ok && ShapeFp8::BM * lda + K + ShapeFp8::BK < lim && ShapeFp8::BN * ldb + K + ShapeFp8::BK < lim;
     ok = ok && ((M + 255) / 256) * ((N + 255) / 256) < lim;
+    const bool ok128 = ((M + ShapeFp8M::BM - 1) / ShapeFp8M::BM) * ((N + ShapeFp8M::BN - 1) / ShapeFp8M::BN) < lim / 64;
+    // As for bf16, more than two 32-wide strips per compute unit over a
+    // short K (fewer than 8 slices of 512) run faster on the masked 128x128
+    // tiles (65536 x 64 x 1024: 20.5 us against 29.9 us streaming; 32 x
+    // 32768 x 2048 16.3 against 20.0 us; at two strips per compute unit the
+    // streaming kernel is still faster: 64 x 16384 x 2048 12.6 against
+    // 13.9 us).
+    const bool tiles_pay = ok && ok128 && K < 8 * ShapeSkinny::KS_FP8;
+    if (okS) return ((N + 31) / 32 > 2 * cus && tiles_pay) ? kFp8MediumMasked : kSkinnyFp8;
+    if (okST && force == nullptr)  // (a forced tile kernel takes such shapes too)
+        return ((M + 31) / 32 > 2 * cus && tiles_pay) ? kFp8MediumMasked : kSkinnyFp8T;
     if (!ok) return kGeneric;
     // the unmasked instance stores C in 16-byte runs; the masked one takes any
     // C (element by element where ldc % 8 != 0 or C is unaligned)
@@ -712,7 +763,6 @@ static int choose_kernel_fp8(int64_t M, int64_t N, int64_t K, const void *A, int
     if (force && !std::strcmp(force, kKindNames[kFp8Mfma16Masked])) return kFp8Mfma16Masked;
     if (force && !std::strcmp(force, kKindNames[kFp8Mfma32])) return exact ? kFp8Mfma32 : kFp8Masked;
     // the 128x128 tiles: exact multiples of 128 (and C's alignment), or masked
-    const bool ok128 = ((M + ShapeFp8M::BM - 1) / ShapeFp8M::BM) * ((N + ShapeFp8M::BN - 1) / ShapeFp8M::BN) < lim / 64;
     const bool exact128 = M % ShapeFp8M::BM == 0 && N % ShapeFp8M::BN == 0 && K % ShapeFp8M::BK == 0 &&
                           ldc % 8 == 0 && aligned16(C);
     const bool can_split128 = ok128 && plan_splitk<ShapeFp8M>(M, N, K, cus, cap_floats).splits >= 2;
@@ -821,20 +871,7 @@ static int run_bf16(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64
     case kRingW8: err = launch_tile_ring_w8(args, cus, stream); break;
     case kRingMasked: err = launch_tile_ring_masked(args, cus, stream); break;
     case kSkinny: err = launch_skinny_plan(args, cus, scr, stream); break;
-    case kSkinnyT: {
-        // C' = C^T: M' = N, N' = M, A' = B^T (row-major, lda' = ldb),
-        // B' = A^T (column-major, ldb' = lda); the kernel writes C' back
-        // transposed and takes the bias of C's columns per row of C'
-        GemmArgs t = args;
-        t.M = args.N;
-        t.N = args.M;
-        t.A = args.B;
-        t.lda = args.ldb;
-        t.B = args.A;
-        t.ldb = args.lda;
-        err = launch_skinny_plan(t, cus, scr, stream, false, false, true);
-        break;
-    }
+    case kSkinnyT: err = launch_skinny_plan(transposed(args), cus, scr, stream, false, false, true); break;
     default: err = launch_generic(args, cus, stream); break;
     }
     if (err != hipSuccess) {
@@ -911,6 +948,7 @@ int gemm_bf16_q8(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t 
     case kRingQ8: err = launch_tile_ring_q8(args, cus, stream); break;
     case kRingQ8Masked: err = launch_tile_ring_q8_masked(args, cus, stream); break;
     case kSkinnyQ8: err = launch_skinny_plan(args, cus, scr, stream, false, true); break;
+    case kSkinnyQ8T: err = launch_skinny_plan(transposed(args), cus, scr, stream, false, true, true); break;
     case kSplitKQ8: err = launch_splitk_plan(args, cus, scr, stream, true); break;
     case kSplitKQ8Masked: err = launch_splitk_plan(args, cus, scr, stream, true, true); break;
     default: err = launch_generic(args, cus, stream); break;
@@ -973,6 +1011,7 @@ int gemm_fp8(int64_t M, int64_t N, int64_t K, const gemm_fp8_t *A, int64_t lda, 
     case kFp8SplitKMediumMasked: err = launch_fp8_medium_splitk_plan(args, cus, scr, stream, true); break;
     case kGemvFp8: err = launch_gemv(args, stream, true); break;
     case kSkinnyFp8: err = launch_skinny_plan(args, cus, scr, stream, true); break;
+    case kSkinnyFp8T: err = launch_skinny_plan(transposed(args), cus, scr, stream, true, false, true); break;
     default: err = launch_generic(args, cus, stream, true); break;
     }
     if (err != hipSuccess) {

@@ -129,12 +129,14 @@ struct SkinnyWork {
 // product with at most 64 columns (the host passes A' = B^T, B' = A^T,
 // M' = N, N' = M, and the bias of C's columns as bias[m']) and writes C'
 // transposed: element (m', n') of C' goes to C[n' + m' * ldc], so each
-// output chunk is 8 consecutive n' of one row m', contiguous in C.
+// output chunk is 8 consecutive n' of one row m', contiguous in C.  With
+// kFp8 the host also swaps the scales (scale_a[m'] is C's column scale,
+// scale_b[n'] its row scale); with kQ8, scale[n'] is the quantization
+// scale of C's row n' and Q is written transposed like C.
 template <class Cfg, uint32_t kFlags, bool kFp8 = false, bool kQ8 = false, bool kTrans = false>
 __global__ void __launch_bounds__(Cfg::kThreads)
 gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
     static_assert(!(kFp8 && kQ8), "int8 output is built for bf16 inputs");
-    static_assert(!(kTrans && (kFp8 || kQ8)), "the transposed output is built for bf16");
     __shared__ __attribute__((aligned(1024))) char smem[Cfg::kLdsBytes];
     char *const ringA = smem;
     char *const ringB = smem + Cfg::SA * Cfg::kABytes;
@@ -378,6 +380,18 @@ gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
                 if (r >= args.M || n >= args.N) return;
                 uint16_t *cp = args.C + (int64_t)r * args.ldc + n;
                 const bool full = n + 8 <= args.N && work.c_vector;
+                float xs[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) xs[e] = x[e];
+                if constexpr (kFp8) {
+                    // C's row scale, then its column scale, as the direct kernel multiplies
+                    const float sc = args.scale_a ? args.scale_a[r] : 1.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float sr = (args.scale_b && n + e < args.N) ? args.scale_b[n + e] : 1.f;
+                        xs[e] = x[e] * sr * sc;
+                    }
+                }
                 float bias_v = 0.f;
                 if constexpr ((kFlags & kEpiBias) != 0) bias_v = bf16_bits_to_f32(args.bias[r]);
                 float cin[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -394,11 +408,30 @@ gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
                         for (int e = 0; e < 8; ++e) if (n + e < args.N) cin[e] = bf16_bits_to_f32(cp[e]);
                     }
                 }
+                if constexpr (kQ8) {
+                    // columns past N' get scale 0 and are never stored
+                    u32x2 qw = {0u, 0u};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float v = epilogue_value<kFlags>(xs[e], cin[e], bias_v, args.alpha, args.beta);
+                        const float sc = n + e < args.N ? args.scale[n + e] : 0.f;
+                        qw[e >> 2] |= ((uint32_t)quantize_i8(v, sc, args.zp) & 0xFFu) << ((e & 3) * 8);
+                    }
+                    int8_t *qp = args.Q + (int64_t)r * args.ldq + n;
+                    if (n + 8 <= args.N && work.q_vector) {
+                        __builtin_nontemporal_store(qw, (u32x2 *)qp);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (n + e < args.N) qp[e] = (int8_t)(qw[e >> 2] >> ((e & 3) * 8));
+                    }
+                    return;
+                }
                 u32x4 out;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    out[e] = pack_bf16x2(epilogue_value<kFlags>(x[2 * e], cin[2 * e], bias_v, args.alpha, args.beta),
-                                         epilogue_value<kFlags>(x[2 * e + 1], cin[2 * e + 1], bias_v, args.alpha,
+                    out[e] = pack_bf16x2(epilogue_value<kFlags>(xs[2 * e], cin[2 * e], bias_v, args.alpha, args.beta),
+                                         epilogue_value<kFlags>(xs[2 * e + 1], cin[2 * e + 1], bias_v, args.alpha,
                                                                 args.beta));
                 if (full) {
                     __builtin_nontemporal_store(out, (u32x4 *)cp);

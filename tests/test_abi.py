@@ -105,6 +105,9 @@ def test_q8_argument_errors():
     assert name(4000, 4000, 1000, P, 1000, P, 1000, P, 4000, P, 4000, 0.5, P, 1) == "ring256x256x64_q8_masked"
     assert name(1, 4096, 4096, P, 4096, P, 4096, 0, 1, P + 3, 1, 0.0, P, 2) == "skinny_q8"    # any Q alignment
     assert name(64, 8192, 8192, P, 8192, P, 8192, 0, 64, P, 64, 0.0, P, 0) == "skinny_q8"
+    assert name(8192, 64, 8192, P, 8192, P, 8192, 0, 8192, P, 8192, 0.0, P, 0) == "skinny_q8_t"
+    assert name(1000, 17, 3000, P, 3000, P, 3000, 0, 1000, P + 3, 1001, 0.0, P, 0) == "skinny_q8_t"
+    assert name(65536, 64, 1024, P, 1024, P, 1024, 0, 65536, P, 65536, 0.0, P, 0) != "skinny_q8_t"  # short K
     assert name(65, 8192, 8192, P, 8192, P, 8192, 0, 72, P, 72, 0.0, P, 0) != "skinny_q8"
     assert name(4096, 4096, 4096, P, 4096, P, 4096, 0, 1, P + 8, 4096, 0.0, P, 0) == "generic64x64x32"
     assert name(4096, 4096, 4096, P, 4096, P, 4096, 0, 1, P, 4100, 0.0, P, 0) == "generic64x64x32"
@@ -158,6 +161,14 @@ def test_fp8_argument_errors_and_names():
     assert name(4, 4096, 4096, P, 4096, P, 4096, P + 2, 5) == "gemv_fp8"
     assert name(5, 4096, 4096, P, 4096, P, 4096, P, 8) == "skinny_fp8"
     assert name(64, 8192, 8192, P, 8192, P, 8192, P, 64) == "skinny_fp8"
+    assert name(8192, 64, 8192, P, 8192, P, 8192, P, 8192) == "skinny_fp8_t"
+    assert name(8192, 1, 4096, P, 4096, P, 4096, P, 8192) == "skinny_fp8_t"
+    assert name(8192, 64, 4104, P, 4104, P, 4104, P, 8192) != "skinny_fp8_t"   # K % 16 != 0
+    # more than two strips per compute unit over fewer than 8 slices of 512
+    assert name(64, 65536, 1024, P, 1024, P, 1024, P, 64) == "fp8_128x128x128_masked"
+    assert name(65536, 64, 2048, P, 2048, P, 2048, P, 65536) == "fp8_128x128x128_masked"
+    assert name(64, 16384, 2048, P, 2048, P, 2048, P, 64) == "skinny_fp8"
+    assert name(64, 65536, 4096, P, 4096, P, 4096, P, 64) == "skinny_fp8"
     assert name(65, 4096, 4096, P, 4096, P, 4096, P, 72) == "splitk_fp8_128x128x128_masked"  # 32 tiles, 32 slices
     assert name(1024, 512, 4096, P, 4096, P, 4096, P, 1024) == "splitk_fp8_128x128x128"  # 32 tiles, 32 slices
     assert name(768, 768, 4096, P, 4096, P, 4096, P, 768) == "fp8_128x128x128"  # 36 tiles, 32 slices
@@ -252,7 +263,12 @@ def test_kernel_selection_names():
     assert name(4, 4096, 4096, P, 4096, P, 4096, P, 4) == "gemv"
     assert name(2, 8192, 8192, P, 8192, P, 8192, P, 2) == "gemv"
     assert name(3, 8192, 8192, P, 8192, P, 8192, P, 3) == "skinny"   # large B: A shared per strip
-    assert name(4, 16384, 4096, P, 4096, P, 4096, P, 4) == "skinny"
+    assert name(4, 16384, 8192, P, 8192, P, 8192, P, 4) == "skinny"
+    # more strips than compute units: the matrix-vector kernel over a K of
+    # 2048 to 8191, the masked 128x128 tiles below that
+    assert name(4, 16384, 4096, P, 4096, P, 4096, P, 4) == "gemv"
+    assert name(3, 65536, 2048, P, 2048, P, 2048, P, 3) == "gemv"
+    assert name(3, 65536, 1024, P, 1024, P, 1024, P, 3) == "tile128x128x64_s4_masked"
     assert name(4, 4096, 16376, P, 16376, P, 16376, P, 4) == "gemv"    # N * K just below 2^26
     assert name(5, 4096, 4096, P, 4096, P, 4096, P, 8) == "skinny"
     assert name(1, 4096, 4100, P, 4100, P, 4100, P, 1) == "generic64x64x32"   # K % 8 != 0

@@ -409,7 +409,7 @@ def test_gemv_epilogue_combinations(beta, use_bias, epi):
                expect_kernel=GV)
 
 
-@pytest.mark.parametrize("M,N,K,ldc", [(3, 8192, 8192, 3), (4, 16384, 4096, 8)])
+@pytest.mark.parametrize("M,N,K,ldc", [(3, 8192, 8192, 3), (4, 16384, 8192, 8)])
 def test_three_and_four_rows_on_large_b_take_the_streaming_kernel(M, N, K, ldc):
     check_full(f"rows {M} large B", M, N, K, ldc=ldc, beta=0.5, use_bias=True, epilogue="gelu_tanh",
                seed=M * 7 + 3, expect_kernel="skinny")
@@ -585,12 +585,48 @@ def test_skinny_transposed_equals_the_direct_kernel_on_swapped_operands(M, N, K,
     assert_within_tolerance(trans[0], ref, K, "skinny_t vs oracle")
 
 
+@pytest.mark.parametrize("M,N,K,ldq,q_offset", [
+    (8192, 64, 2048, 8192, 0),     # 64 columns: 256 strips of 32 rows of Q, 8-byte stores
+    (1000, 17, 3000, 1001, 0),     # row tail inside a chunk, odd ldq: element-wise stores
+    (4096, 1, 2048, 4096, 0),      # a single column
+    (999, 40, 1024, 1000, 1),      # Q not 8-byte aligned
+    (2048, 32, 16384, 2048, 0),    # long K: split within an XCD
+])
+def test_skinny_transposed_int8_output(M, N, K, ldq, q_offset):
+    """The int8-output instance on the transposed product: the scale of C's
+    row m quantizes column m of C^T, and Q is written back transposed."""
+    check_q8(f"q8 skinny_t {M}x{N}x{K}", M, N, K, ldq=ldq, ldc=ldq, alpha=1.25, beta=0.5, use_bias=True,
+             epilogue="gelu_tanh", zp=3, q_offset=q_offset, seed=M + 2 * N + K, expect_kernel="skinny_q8_t")
+    check_q8(f"q8 skinny_t beta=0 {M}x{N}x{K}", M, N, K, ldq=ldq, epilogue="relu", zp=-7, q_offset=q_offset,
+             seed=M + 3 * N + K, expect_kernel="skinny_q8_t")
+
+
+@pytest.mark.parametrize("M,N,K,ldc,scales", [
+    (8192, 64, 1024, 8192, True),   # 64 columns: 256 strips
+    (1000, 17, 3008, 1001, True),   # row tail, odd ldc
+    (4096, 1, 2048, 4096, True),    # a single column
+    (2048, 32, 16384, 2048, True),  # long K: split within an XCD
+    (777, 33, 1024, 784, False),    # no scales
+])
+def test_skinny_transposed_fp8(M, N, K, ldc, scales):
+    """The FP8 instance on the transposed product: the row and column scales
+    trade places with the operands."""
+    check_fp8(f"fp8 skinny_t {M}x{N}x{K}", M, N, K, ldc=ldc, alpha=0.75, beta=-0.25, use_bias=True,
+              epilogue="relu", scales=scales, seed=M + N + K, expect_kernel="skinny_fp8_t")
+
+
 @pytest.mark.parametrize("M,N,K,ldc", [(40, 10000, 512, 41), (9000, 24, 1024, 9000)])
 def test_many_strips_over_a_short_k_take_the_masked_tiles(M, N, K, ldc):
     """More 32-wide strips than compute units over a short K: the masked
     128x128 tiles, their rows (or columns) mostly past the matrix."""
     check_full(f"many strips short K {M}x{N}x{K}", M, N, K, ldc=ldc, beta=0.5, use_bias=True,
                epilogue="gelu_tanh", seed=M + N + K, expect_kernel="tile128x128x64_s4_masked")
+
+
+@pytest.mark.parametrize("M,N,K,ldc", [(40, 20000, 1024, 41), (20000, 24, 512, 20000)])
+def test_fp8_many_strips_over_a_short_k_take_the_masked_tiles(M, N, K, ldc):
+    check_fp8(f"fp8 many strips short K {M}x{N}x{K}", M, N, K, ldc=ldc, beta=0.5, use_bias=True,
+              epilogue="gelu_tanh", seed=M + N + K, expect_kernel="fp8_128x128x128_masked")
 
 
 # ---------------------------------------------------- bounds-checked path ---
