@@ -56,10 +56,13 @@ SEQUENCES = [
      (48, 512, 8192, -0.5, "relu", "skinny")],
     [(1000, 1000, 4096, 0.5, "gelu_tanh", "splitk128x128x64_masked"),
      (520, 300, 4000, 0.0, "none", "splitk128x128x64_masked")],
+    [(2048, 32, 16384, 0.0, "none", "skinny_t"),                 # the transposed product, split in K
+     (1000, 40, 8192, 0.5, "relu", "skinny_t")],
 ]
 
 
-@pytest.mark.parametrize("seq", SEQUENCES, ids=["tile-split", "streaming-split", "masked-split"])
+@pytest.mark.parametrize("seq", SEQUENCES, ids=["tile-split", "streaming-split", "masked-split",
+                                                "transposed-split"])
 def test_noalloc_matches_gemm_bf16_twice(seq):
     for i, (M, N, K, beta, epi, kernel) in enumerate(seq):
         kname = gb.gemm_bf16_kernel_name(M, N, K, 4096, K, 4096, K, 4096, M)
