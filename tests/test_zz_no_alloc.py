@@ -77,3 +77,47 @@ def test_noalloc_matches_gemm_bf16_twice(seq):
         # the static array keeps this call's contents; a repeat must not see them
         again = _run(gb.gemm_bf16_noalloc, M, N, K, case, beta, epi)
         assert np.array_equal(again, got), "a repeated gemm_bf16_noalloc call differs"
+
+
+@pytest.mark.parametrize("M,N,K,kernel", [
+    (1024, 1024, 4096, "splitk128x128x64"),
+    (64, 1024, 16384, "skinny"),
+    (2048, 32, 16384, "skinny_t"),
+    (1000, 1000, 4096, "splitk128x128x64_masked"),
+    (4608, 2048, 320, "ring256x256x64"),
+])
+def test_noalloc_replays_from_a_captured_graph(M, N, K, kernel):
+    """A gemm_bf16_noalloc call captured into a HIP graph (stream capture
+    through torch.cuda.graph) replays to the eager call's result bit for bit,
+    replay after replay, with eager work and a synchronisation between
+    replays: the split paths clear what they count in-kernel, so nothing in
+    the graph depends on state a previous replay left behind."""
+    assert gb.gemm_bf16_kernel_name(M, N, K, 4096, K, 4096, K, 4096, M) == kernel
+    case = inputs.random_case(9100 + M + N, M, N, K, with_c0=True, with_bias=True)
+    A, B, bias, C0 = _dev(case["A"]), _dev(case["B"]), _dev(case["bias"]), _dev(case["C0"])
+    C = C0.clone()
+
+    def call():
+        st = gb.gemm_bf16_noalloc(M, N, K, A.data_ptr(), K, B.data_ptr(), K, C.data_ptr(), M, 1.25, 0.5,
+                                  bias.data_ptr(), gb.EPILOGUES["gelu_tanh"], torch.cuda.current_stream().cuda_stream)
+        assert st == 0, gb.gemm_bf16_status_string(st)
+
+    print(f"[noalloc-graph] {M}x{N}x{K} kernel={kernel}", flush=True)
+    call()  # eager: the reference, and the device's one-time set-up outside the capture
+    torch.cuda.synchronize()
+    want = C.cpu().numpy().view(np.uint16).copy()
+    ref = oracle.gemm(M, N, K, case["A"], K, case["B"], K, case["C0"], M, 1.25, 0.5, case["bias"], "gelu_tanh")
+    assert_within_tolerance(want, ref, K, f"eager {M}x{N}x{K}")
+    C.copy_(C0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for r in range(3):
+        C.copy_(C0)  # beta != 0: every replay starts from C0 again
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = C.cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, want), f"replay {r} differs from the eager call"
