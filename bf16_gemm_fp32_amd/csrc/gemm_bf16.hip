@@ -21,7 +21,7 @@
 namespace gb {
 
 enum KernelKind {
-    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8Mfma32, kSplitK, kGemv, kSplitKQ8, kFp8Masked, kGemvFp8, kSkinnyFp8, kFp8SplitK, kRingQ8Masked, kSkinnyQ8, kMediumMasked, kSplitKMasked, kFp8SplitKMasked, kFp8, kFp8Mfma16Masked, kRingW8, kFp8Medium, kFp8MediumMasked, kFp8SplitKMedium, kFp8SplitKMediumMasked, kSplitKQ8Masked, kSkinnyT, kSkinnyQ8T, kSkinnyFp8T, kNumKinds
+    kNone = 0, kLarge, kMedium, kSkinny, kGeneric, kRing32, kRing, kRingMasked, kRingQ8, kFp8Mfma32, kSplitK, kGemv, kSplitKQ8, kFp8Masked, kGemvFp8, kSkinnyFp8, kFp8SplitK, kRingQ8Masked, kSkinnyQ8, kMediumMasked, kSplitKMasked, kFp8SplitKMasked, kFp8, kFp8Mfma16Masked, kRingW8, kFp8Medium, kFp8MediumMasked, kFp8SplitKMedium, kFp8SplitKMediumMasked, kSplitKQ8Masked, kSkinnyT, kSkinnyQ8T, kSkinnyFp8T, kTileQ8, kTileQ8Masked, kNumKinds
 };
 
 static const char *const kKindNames[kNumKinds] = {"none",            "tile256x256x32_s5", "tile128x128x64_s4",
@@ -38,7 +38,8 @@ static const char *const kKindNames[kNumKinds] = {"none",            "tile256x25
                                                   "ring256x256x64_w8", "fp8_128x128x128",
                                                   "fp8_128x128x128_masked", "splitk_fp8_128x128x128",
                                                   "splitk_fp8_128x128x128_masked", "splitk128x128x64_q8_masked",
-                                                  "skinny_t", "skinny_q8_t", "skinny_fp8_t"};
+                                                  "skinny_t", "skinny_q8_t", "skinny_fp8_t",
+                                                  "tile128x128x64_q8", "tile128x128x64_q8_masked"};
 
 static const char *kind_name(int k) { return (k >= 0 && k < kNumKinds) ? kKindNames[k] : "none"; }
 
@@ -540,6 +541,32 @@ static hipError_t launch_splitk_plan(const GemmArgs &args, int cus, const Scratc
                   : launch_tile_medium_splitk(args, p, cus, stream);
 }
 
+// The int8 output on 128x128 tiles over the whole of K: the split kernels
+// with a single K range -- the tile kernel stores each tile's fp32 sum to
+// the workspace and the ordered reduction kernel runs the epilogue and
+// quantizes (the unsplit tile kernel's epilogue writes bf16 only).  The
+// workspace holds M x N floats rounded up to whole tiles.
+static TileSplit plan_tile_q8(int64_t M, int64_t N, int64_t K) {
+    TileSplit p{};
+    p.splits = 1;
+    p.kper = (int)((K + ShapeM::BK - 1) / ShapeM::BK);
+    p.ldp = (M + ShapeM::BM - 1) / ShapeM::BM * ShapeM::BM;
+    p.pstride = p.ldp * ((N + ShapeM::BN - 1) / ShapeM::BN * ShapeM::BN);
+    p.tile_major = 0;
+    return p;
+}
+
+static hipError_t launch_tile_q8_plan(const GemmArgs &args, int cus, const Scratch &scr, hipStream_t stream,
+                                      bool masked) {
+    TileSplit p = plan_tile_q8(args.M, args.N, args.K);
+    if ((size_t)p.pstride > scr.cap_floats) return hipErrorInvalidValue;
+    uint32_t *unused = nullptr;
+    hipError_t err = get_scratch(scr, stream, &unused, &p.P);
+    if (err != hipSuccess) return err;
+    return masked ? launch_tile_medium_splitk_q8_masked(args, p, cus, stream)
+                  : launch_tile_medium_splitk_q8(args, p, cus, stream);
+}
+
 // Kernel for a shape.  GEMM_BF16_FORCE_KERNEL=<name> (a kKindNames entry)
 // overrides the choice when that kernel can run the shape; it exists for
 // testing and benchmarking the alternatives.
@@ -637,7 +664,9 @@ static int choose_kernel(int64_t M, int64_t N, int64_t K, const void *A, int64_t
 // The quantizing path: the masked ring kernel when its requirements hold
 // (also for Q, scale and ldq) and its 256x256 tiles give at least half the
 // compute units a tile; on smaller grids split-K on 128x128 tiles when the
-// shape allows it (its reduction quantizes); else the bounds-checked kernel.
+// shape allows it (its reduction quantizes), else whole-K 128x128 tiles
+// through the same reduction when the workspace holds every tile; else the
+// ring with idle compute units or the bounds-checked kernel.
 static int choose_kernel_q8(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
                             int64_t ldb, const void *C, int64_t ldc, float beta, const void *Q, int64_t ldq,
                             const void *scale, int cus, size_t cap_floats) {
@@ -679,6 +708,22 @@ static int choose_kernel_q8(int64_t M, int64_t N, int64_t K, const void *A, int6
         // 66.0 us on the bounds-checked kernel, 504 x 504 x 8192 18.1 against
         // 125.2 us, 1000 x 1000 x 1000 13.3 against 20.4 us)
         if (medium_masked_ok(M, N, K, A, lda, B, ldb, c_probe, ldc_probe) && can_split) return kSplitKQ8Masked;
+        // whole K on 128x128 tiles, the workspace holding every tile
+        const bool fits = (size_t)plan_tile_q8(M, N, K).pstride <= cap_floats;
+        const bool exact128 = tile_path_ok<ShapeM>(M, N, K, A, lda, B, ldb, c_probe, ldc_probe);
+        const bool masked128 = medium_masked_ok(M, N, K, A, lda, B, ldb, c_probe, ldc_probe);
+        if (force && !std::strcmp(force, kKindNames[kTileQ8]) && fits && exact128) return kTileQ8;
+        if (force && !std::strcmp(force, kKindNames[kTileQ8Masked]) && fits && masked128) return kTileQ8Masked;
+        // From 8 slices of K the fp32 round trip pays for itself against the
+        // ring with idle compute units or the bounds-checked kernel (2048 x
+        // 2048 x 4096: 47.8 us against 82.2 us on the ring; 2048 x 1024 x
+        // 4096 42.8 against 87.2 us generic; 1504 x 1504 x 320, masked, 16.6
+        // against 27.8 us); at 4 slices it does not (2048 x 2048 x 256: 20.6
+        // against 18.3 us on the ring).
+        if (fits && K >= 8 * ShapeM::BK && force == nullptr) {
+            if (exact128) return kTileQ8;
+            if (masked128) return kTileQ8Masked;
+        }
         // Grids too large to split on 128x128 tiles and too small to fill
         // half of the compute units with ring tiles: from more than an
         // eighth of the compute units in ring tiles the ring, with idle
@@ -951,6 +996,8 @@ int gemm_bf16_q8(int64_t M, int64_t N, int64_t K, const gemm_bf16_t *A, int64_t 
     case kSkinnyQ8T: err = launch_skinny_plan(transposed(args), cus, scr, stream, false, true, true); break;
     case kSplitKQ8: err = launch_splitk_plan(args, cus, scr, stream, true); break;
     case kSplitKQ8Masked: err = launch_splitk_plan(args, cus, scr, stream, true, true); break;
+    case kTileQ8: err = launch_tile_q8_plan(args, cus, scr, stream, false); break;
+    case kTileQ8Masked: err = launch_tile_q8_plan(args, cus, scr, stream, true); break;
     default: err = launch_generic(args, cus, stream); break;
     }
     if (err != hipSuccess) {

@@ -754,7 +754,9 @@ hipError_t launch_tile(const GemmArgs &args, int cus, hipStream_t stream) {
 // Split-K launch: the tile kernel over (range, tile) units into the
 // workspace split.P, then the reduction with the epilogue flags baked in
 // (kQ8: writing int8 Q).  The host has checked the tile-path requirements,
-// split.splits >= 2, every range non-empty, and that split.P holds
+// split.splits >= 1 (one range: the int8 output over the whole of K, the
+// reduction only running the epilogue), every range non-empty, and that
+// split.P holds
 // splits * pstride floats (ldp = M rounded up to BM, pstride = ldp times N
 // rounded up to BN; exact shapes: M and M * N).
 template <class Cfg, bool kQ8 = false, bool kMasked = false>

@@ -115,13 +115,21 @@ def test_q8_argument_errors():
     # small grids of 128-tiles with enough K-slices: split-K, the reduction quantizing
     assert name(1024, 1024, 4096, P, 4096, P, 4096, 0, 1, P, 1024, 0.0, P, 2) == "splitk128x128x64_q8"
     assert name(1024, 1024, 4096, P, 4096, P, 4096, 0, 1, P, 1028, 0.0, P, 2) == "generic64x64x32"
-    assert name(1024, 1024, 512, P, 512, P, 512, 0, 1, P, 1024, 0.0, P, 2) == "generic64x64x32"  # 8 slices
+    # too few slices to split: whole K on 128x128 tiles through the same reduction
+    assert name(1024, 1024, 512, P, 512, P, 512, 0, 1, P, 1024, 0.0, P, 2) == "tile128x128x64_q8"  # 8 slices
+    assert name(2048, 2048, 4096, P, 4096, P, 4096, 0, 1, P, 2048, 0.0, P, 2) == "tile128x128x64_q8"
+    assert name(1504, 1504, 512, P, 512, P, 512, 0, 1, P, 1504, 0.0, P, 2) == "tile128x128x64_q8_masked"
+    assert name(2048, 2048, 256, P, 256, P, 256, 0, 1, P, 2048, 0.0, P, 2) == "ring256x256x64_q8"  # 4 slices
+    assert name(3072, 2048, 4096, P, 4096, P, 4096, 0, 1, P, 3072, 0.0, P, 2) == "ring256x256x64_q8"  # too big
     # with tails: the masked split
     assert name(1000, 1000, 4096, P, 4096, P, 4096, 0, 1, P, 1000, 0.0, P, 2) == "splitk128x128x64_q8_masked"
     assert name(1001, 777, 2048, P, 2048, P, 2048, 0, 1, P, 1008, 0.0, P, 2) == "splitk128x128x64_q8_masked"
-    # mid-sized grids too large to split: the ring from more than 32 ring tiles
-    assert name(2048, 2048, 4096, P, 4096, P, 4096, 0, 1, P, 2048, 0.0, P, 2) == "ring256x256x64_q8"
-    assert name(2048, 1024, 4096, P, 4096, P, 4096, 0, 1, P, 2048, 0.0, P, 2) == "generic64x64x32"
+    # mid-sized grids too large to split: whole K on 128x128 tiles while the
+    # workspace holds every tile, then the ring from more than 32 ring tiles
+    assert name(2048, 1024, 4096, P, 4096, P, 4096, 0, 1, P, 2048, 0.0, P, 2) == "tile128x128x64_q8"
+    assert name(4096, 1536, 4096, P, 4096, P, 4096, 0, 1, P, 4096, 0.0, P, 2) == "ring256x256x64_q8"
+    assert name(2304, 2048, 256, P, 256, P, 256, 0, 1, P, 2304, 0.0, P, 2) == "ring256x256x64_q8"
+    assert name(2048, 1024, 256, P, 256, P, 256, 0, 1, P, 2048, 0.0, P, 2) == "generic64x64x32"
 
 
 def test_fp8_argument_errors_and_names():

@@ -781,6 +781,20 @@ def test_q8_ring_is_the_default_for_large_shapes():
              expect_kernel=RQ8)
 
 
+# Grids too large to split but whose 128x128 tiles all fit the workspace:
+# whole K through the split kernels with one range, the reduction running
+# the epilogue and quantizing.
+@pytest.mark.parametrize("M,N,K,ldq,beta,use_bias,epi,zp,kernel", [
+    (2048, 1024, 1024, 2048, 0.5, True, "gelu_tanh", 3, "tile128x128x64_q8"),     # 128 tiles
+    (2048, 2048, 512, 2056, 0.0, False, "relu", -9, "tile128x128x64_q8"),         # 256 tiles, padded ldq
+    (1500, 1400, 1024, 1504, -0.75, True, "none", 0, "tile128x128x64_q8_masked"),  # tails in M and N
+    (1504, 1504, 600, 1504, 0.5, True, "relu", 5, "tile128x128x64_q8_masked"),    # K tail
+])
+def test_q8_whole_k_tiles(M, N, K, ldq, beta, use_bias, epi, zp, kernel):
+    check_q8(f"q8 whole-K tiles {M}x{N}x{K}", M, N, K, ldq=ldq, ldc=ldq, alpha=1.25, beta=beta, use_bias=use_bias,
+             epilogue=epi, zp=zp, seed=M + N + K + 7, expect_kernel=kernel)
+
+
 @pytest.mark.parametrize("M,N,K,ldq,kernel", [
     (2048, 2048, 256, 2048, RQ8),                # 64 ring tiles, 256 128x128 tiles: too many to split
     (1500, 1500, 320, 1504, RQ8M),               # 36 ring tiles, with tails
