@@ -112,6 +112,10 @@ WORKLOADS = {
         # FP8 on the small grid of the DeepGEMM article's shapes (section 5.1)
         Workload("fp8_mid_1024x1024x4096", 11, 1024, 1024, 4096, inp="fp8",
                  notes="64 tiles of 128x128 for 256 compute units, E4M3 operands"),
+        # the memory-bound case transposed: 64 columns, so A (128 MiB) is
+        # the operand streamed once
+        Workload("tall_8192x64x8192", 12, 8192, 64, 8192, bound="hbm",
+                 notes="N = 64: A (128 MiB) streamed once"),
     ]
 }
 
