@@ -355,7 +355,7 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on exactly one GPU: this build is a single-GPU kernel library "
+        print("bench.py runs on exactly one GPU: gemm_bf16 is a single-GPU kernel library "
               "(multi-GPU sharding is described in the design notes, not implemented).", file=sys.stderr)
         sys.exit(2)
 
