@@ -343,6 +343,7 @@ gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
         constexpr int kChunksPerCol = Cfg::BMr / 8;
         constexpr int kChunks = Cfg::BN * kChunksPerCol;  // 8-row pieces of the strip
         constexpr int kChunksPerRow = Cfg::BN / 8;          // kTrans: 8-column pieces of a row
+        static_assert(16 % kChunksPerRow == 0, "strips of 32, 64 or 128 columns");
 
         // The four waves' sum of one 8-row chunk (column idx / kChunksPerCol)
         // -- with kTrans, of one 8-column chunk (row idx / kChunksPerRow).
@@ -350,13 +351,31 @@ gemm_skinny_kernel(const GemmArgs args, const SkinnyWork work) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = 0.f;
             if constexpr (kTrans) {
-                const int r = idx / kChunksPerRow, c8 = (idx % kChunksPerRow) * 8;
+                // One float per column at the column stride: the 64 lanes of a
+                // wave cover 64 / kChunksPerRow rows of kChunksPerRow chunks,
+                // and chunks two apart would meet on the same banks, so lane
+                // reads its 8 columns in the order e ^ rot (rot spreads the
+                // chunks over the banks), then undoes the permutation with
+                // conditional swaps of register pairs.
+                const int r = idx / kChunksPerRow, q = idx % kChunksPerRow, c8 = q * 8;
+                const int rot = ((q >> 1) * (16 / kChunksPerRow)) & 7;
 #pragma unroll
                 for (int w = 0; w < Cfg::kWaves; ++w)
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
-                        x[e] += *(const GB_LDS float *)(smem + w * Cfg::kPartBytes + (c8 + e) * Cfg::kColBytes +
-                                                        r * 4);
+                        x[e] += *(const GB_LDS float *)(smem + w * Cfg::kPartBytes +
+                                                        (c8 + (e ^ rot)) * Cfg::kColBytes + r * 4);
+#pragma unroll
+                for (int b = 1; b < 8; b <<= 1) {
+                    const bool swap = (rot & b) != 0;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if ((e & b) == 0) {
+                            const float lo = x[e], hi = x[e | b];
+                            x[e] = swap ? hi : lo;
+                            x[e | b] = swap ? lo : hi;
+                        }
+                }
                 return;
             }
             const int col = idx / kChunksPerCol, q = idx % kChunksPerCol;
